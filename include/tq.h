@@ -1,0 +1,243 @@
+/*
+ * tq.h -- C ABI of libtq: SRHT KV-cache compression and decode attention over
+ * the packed cache, for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (sources are the pages' titles and sections):
+ *  - Encode: each 128-dim head vector x of a key or value is rotated by the
+ *    randomized Walsh-Hadamard transform R = D H D / sqrt(d) ("TurboQuant-MLX
+ *    v2.0", What's New > Walsh-Hadamard Rotation; How It Works > Pipeline),
+ *    its L2 norm n is stored, and every coordinate of u = sqrt(d) R x / n is
+ *    scalar-quantised against a Lloyd-Max Gaussian codebook or a symmetric
+ *    uniform grid ("TurboMOQ", Architecture) at a per-page bit width of 1-8
+ *    ("TurboMOQ", Architecture: per-head adaptive bit width), then bit-packed.
+ *    Keys may carry a 1-bit QJL residual sign sketch with a per-vector scale
+ *    ("TurboMOQ", QJL residual correction; "TurboQuant-MLX v2.0", Pipeline).
+ *  - Decode attention: one query per session attends over every cached token:
+ *    softmax(q . k / sqrt(d)) . v, reading packed pages directly (scores in the
+ *    rotated domain, value accumulation in the rotated domain and one inverse
+ *    rotation at the end, which factors the Walsh-Hadamard transform out of the
+ *    V accumulation as the MLX TurboQuant skill page describes for its Metal
+ *    kernels, Path A > Optimisations Metal) and fp16 pages
+ *    for the attention sink and other uncompressed tokens ("TurboQuant-MLX
+ *    v2.0", What's New > FP16 Attention Sinks).
+ *
+ * Conventions shared by every call:
+ *  - head_dim d = 128, page = 64 tokens of one (session, KV head), JL dim m = 128.
+ *  - Device pointers are HIP device addresses owned by the caller.  The library
+ *    never allocates, frees or synchronises device memory; calls that take a
+ *    stream enqueue work on it (a hipStream_t passed as void*; NULL = default
+ *    stream) and return after the enqueue.
+ *  - Every call validates its arguments on the host before any HIP call; on a
+ *    validation failure it returns a negative status, writes nothing and
+ *    records a message readable with tq_last_error() (per thread).
+ *  - TQ_ERR_DEVICE reports a failed kernel launch (hipGetLastError after the
+ *    launch); faults during execution surface at the caller's next
+ *    synchronisation, as for any HIP kernel.
+ *
+ * Rotation: R = D H D / sqrt(d), H the Sylvester Hadamard matrix in natural
+ * order, D = diag(+-1) from the layer's sign mask.  R is symmetric and its own
+ * inverse.
+ *
+ * Quantisation: code_j = #{k : t_k <= u_j} over the ascending float32
+ * boundaries t of the page's bit width (ties round up; code 0 is the most
+ * negative centroid).  Dequantisation: xhat = (n / sqrt(d)) R c[code].
+ *
+ * QJL (keys): r = x - xhat, z_i = [(S r)_i >= 0], gamma = ||r||;
+ * rhat = sqrt(pi/2)/m * gamma * S^T (2z - 1); the attended key is xhat + rhat.
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status */
+enum {
+  TQ_OK = 0,
+  TQ_ERR_INVALID_ARG = -1, /* null pointer, bad size/range/kind             */
+  TQ_ERR_UNSUPPORTED = -2, /* head_dim != 128, bits outside 1..8, jl != 128, GQA group not 1/2/4/8 */
+  TQ_ERR_ALIGNMENT = -3,   /* pointer or stride not 16-byte aligned          */
+  TQ_ERR_WORKSPACE = -4,   /* workspace smaller than tq_decode_workspace_bytes */
+  TQ_ERR_DEVICE = -5       /* HIP reported an error when launching           */
+};
+
+enum { TQ_CODEBOOK_LLOYD_MAX = 0, TQ_CODEBOOK_UNIFORM = 1 };
+enum { TQ_DTYPE_F32 = 0, TQ_DTYPE_F16 = 1 };
+
+#define TQ_HEAD_DIM 128
+#define TQ_PAGE_TOKENS 64
+#define TQ_JL_DIM 128
+/* floats in one codebook table (all bit widths of one kind), see tq_codebook_table */
+#define TQ_CODEBOOK_TABLE_FLOATS 1024
+
+/* ------------------------------------------------------- page descriptors
+ * A cache is a caller-owned byte pool plus a page table of uint64
+ * descriptors, one per (session, KV head, page):
+ *   bits  0..47  byte offset of the page in the pool (multiple of 256)
+ *   bits 48..51  k_bits (1..8); 0 marks an fp16 page
+ *   bits 52..55  v_bits (1..8); 0 for an fp16 page
+ *   bit  56      the page carries a QJL residual for its keys
+ *   bit  63      present
+ * Packed page layout (bytes, in order):
+ *   K codes   1024*k_bits : 64 streams of 128 codes; stream t = token t's
+ *             codes of coordinates 0..127; a stream is its codes LSB-first
+ *             (code n at bits n*b..n*b+b-1), i.e. b little-endian 128-bit
+ *             words, and word w of stream s is at byte (w*64 + s)*16.
+ *   K norms   64 x float32
+ *   [QJL]     64 x 16 B sign words (bit i of token t's word = z_i), then
+ *             64 x float32 gamma
+ *   V codes   1024*v_bits : 64 streams as above, but stream s = 16q+i holds,
+ *             for k = 0..15 and e = 0..7, the code of token 4k+q,
+ *             coordinate 8i+e at stream position 8k+e
+ *   V norms   64 x float32
+ * fp16 page: 64 rows of K then 64 rows of V, fp16, 128 values per row.
+ * These layouts are a convention of this library (the pages name bit packing
+ * only as a utility module); tq_page_bytes() gives the sizes.              */
+#define TQ_PAGE_PRESENT (1ull << 63)
+#define TQ_PAGE_QJL (1ull << 56)
+#define TQ_PAGE_OFFSET_MASK ((1ull << 48) - 1)
+
+/* Bytes of one page: k_bits = 0 (and v_bits = 0, qjl = 0) for an fp16 page.
+ * Returns 0 for an invalid combination. */
+size_t tq_page_bytes(int k_bits, int v_bits, int qjl);
+
+/* Builds a page descriptor; returns 0 for an invalid combination or an offset
+ * that is not a multiple of 256 or does not fit 48 bits. */
+uint64_t tq_page_descriptor(uint64_t offset, int k_bits, int v_bits, int qjl);
+
+/* ------------------------------------------------------------ descriptors */
+typedef struct tq_layer {
+  int32_t head_dim;          /* must be 128                                      */
+  int32_t k_codebook;        /* TQ_CODEBOOK_* used by every packed K block       */
+  int32_t v_codebook;        /* TQ_CODEBOOK_* used by every packed V block       */
+  int32_t jl_dim;            /* 128; read only by pages with the QJL bit         */
+  const uint32_t* sign_mask; /* device, 4 words: bit j set <=> D_j = -1          */
+  const float* k_table;      /* device, TQ_CODEBOOK_TABLE_FLOATS floats from
+                                tq_codebook_table(k_codebook)                    */
+  const float* v_table;      /* device, same for v_codebook                      */
+  const float* qjl_s;        /* device, S as 128 x 128 float32 row-major, or
+                                NULL when no page of the cache uses QJL          */
+} tq_layer;
+
+typedef struct tq_cache {
+  int32_t n_sessions;        /* B                                                */
+  int32_t n_kv_heads;        /* H_kv                                             */
+  int32_t max_pages;         /* row length of the page table                     */
+  int32_t reserved;          /* 0                                                */
+  const int32_t* n_tokens;   /* device [B]: tokens cached per session; decode
+                                attends to tokens [0, n_tokens[b]) and needs
+                                n_tokens[b] <= 64 * max_pages                    */
+  const uint64_t* pages;     /* device [B][H_kv][max_pages] descriptors          */
+  void* pool;                /* device byte pool, 256-byte aligned               */
+  uint64_t pool_bytes;       /* pool size; pages outside it are never touched    */
+} tq_cache;
+
+typedef struct tq_kv_input {
+  const void* k;             /* device: element (b, h, t, j) of the call's keys at
+                                k + ((b*stride_b + h*stride_h + t*stride_t) + j)
+                                elements, t = 0..ntok-1 for cache token tok0+t   */
+  const void* v;             /* device, same shape and strides as k              */
+  int32_t dtype;             /* TQ_DTYPE_F16 or TQ_DTYPE_F32                     */
+  int32_t tok0;              /* first cache token written; multiple of 64        */
+  int32_t ntok;              /* tokens in this call (>= 1)                       */
+  int32_t reserved;          /* 0                                                */
+  int64_t stride_b, stride_h, stride_t;  /* in elements; rows 16-byte aligned   */
+  int32_t* error_flags;      /* device int or NULL: kernels OR in
+                                1 = a packed page only partly covered by the call
+                                    (left untouched),
+                                2 = a page descriptor in range not present,
+                                4 = a page outside the pool (left untouched)     */
+} tq_kv_input;
+
+typedef struct tq_query {
+  const void* q;             /* device: element (b, h, j) at
+                                q + b*stride_b + h*stride_h + j elements         */
+  int32_t dtype;             /* TQ_DTYPE_F16 or TQ_DTYPE_F32                     */
+  int32_t n_q_heads;         /* H_q = G * H_kv, G in {1, 2, 4, 8}; query head h
+                                reads KV head h / G                              */
+  int64_t stride_b, stride_h;
+  float softmax_scale;       /* 0 selects 1/sqrt(128)                            */
+  int32_t reserved;          /* 0                                                */
+} tq_query;
+
+/* --------------------------------------------------------- host-only calls */
+
+/* Codebook for one bit width ("TurboMOQ", Architecture: Lloyd-Max codebook;
+ * Limitations: without calibration data the method uses a symmetric grid).
+ * kind = TQ_CODEBOOK_LLOYD_MAX: the MSE-optimal 2^bits-level quantiser of
+ *   N(0,1) (the unique fixed point of the centroid and midpoint conditions);
+ * kind = TQ_CODEBOOK_UNIFORM: levels (k - (L-1)/2) * delta with the
+ *   MSE-optimal delta for N(0,1), boundaries at midpoints.
+ * Writes 2^bits ascending centroids and 2^bits - 1 boundaries (caller-owned
+ * host arrays), each the float32 nearest the exact value.  Pure, deterministic
+ * and thread-safe; bits in 1..8. */
+int tq_build_codebook(int bits, int kind, float* centroids, float* boundaries);
+
+/* The table kernels read: for every bits = 1..8 the centroids at float offset
+ * 2^bits - 2 and the boundaries at 510 + 2^bits - bits - 1; the tail is zero.
+ * Writes TQ_CODEBOOK_TABLE_FLOATS floats to a host array (copy it to the
+ * device for tq_layer). */
+int tq_codebook_table(int kind, float* table);
+
+/* Layer randomness from a seed ("TurboQuant-MLX v2.0", What's New: seed 42;
+ * MLX TurboQuant skill page, Standalone Benchmark: one cache per layer seeded
+ * 42 + layer).  Stream = counter-based SplitMix64 seeded with seed + layer.
+ * Outputs 1..head_dim give signs[j] = -1 if the top bit is set, else +1; when
+ * qjl_s is not NULL the following outputs, as uniforms (z >> 11) * 2^-53
+ * taken in pairs through Box-Muller (cos then sin), fill S (jl_dim x
+ * head_dim, row-major float32).  Host arrays; head_dim = jl_dim = 128. */
+int tq_layer_params(uint64_t seed, int layer, int head_dim, int jl_dim,
+                    int8_t* signs, float* qjl_s);
+
+/* Packs 128 signs (+1 / -1) into the 4-word mask tq_layer.sign_mask expects. */
+int tq_sign_mask(const int8_t* signs, int head_dim, uint32_t* mask);
+
+/* Workspace tq_decode_attention needs for this cache and query-head count. */
+size_t tq_decode_workspace_bytes(const tq_cache* cache, int n_q_heads);
+
+/* Bytes of a cache: the sum of tq_page_bytes over the given descriptors
+ * (a host copy of the page table, n entries; absent pages count zero). */
+size_t tq_cache_bytes(const uint64_t* host_pages, size_t n);
+
+const char* tq_status_string(int status);
+const char* tq_last_error(void);
+
+/* ----------------------------------------------------------- device calls */
+
+/* Encodes tokens [tok0, tok0 + ntok) of every (session, KV head) into the
+ * pages the page table names ("TurboQuant-MLX v2.0", What's New > Dynamic
+ * Chunk Buffering: compression fires on whole 64-token chunks).  A packed
+ * page is written only when the call covers all 64 of its tokens; an fp16
+ * page receives the covered rows (rounded to fp16 when the input is fp32).
+ * Pages are independent: calls over disjoint token ranges may be issued in any
+ * order.  Keys of QJL pages also get their sign sketch and gamma. */
+int tq_encode_kv(const tq_layer* layer, const tq_cache* cache,
+                 const tq_kv_input* in, void* stream);
+
+/* out[b][h][0..127] (device float32, row stride 128, B x H_q rows) =
+ * softmax_t(scale * q_bh . k_t) . v_t over t in [0, n_tokens[b]), where k_t,
+ * v_t are the fp16 values of fp16 pages and the dequantised vectors (keys plus
+ * the QJL residual where present) of packed pages.  Needs a device workspace of
+ * tq_decode_workspace_bytes(cache, n_q_heads) bytes (16-byte aligned; contents
+ * on entry are ignored).  Launches three kernels on the stream: query
+ * rotation, split-K over pages, and the combine. */
+int tq_decode_attention(const tq_layer* layer, const tq_cache* cache,
+                        const tq_query* query, float* out, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Dense reconstruction of tokens [tok0, tok0 + ntok) of every (session,
+ * KV head): out[b][h][t][0..127] float32 (device, contiguous).  which = 0 keys,
+ * 1 values; add_qjl adds the QJL residual on keys of QJL pages.  fp16 pages
+ * give their stored values.  For checking the codec; not on the decode path. */
+int tq_dequantize(const tq_layer* layer, const tq_cache* cache, int which,
+                  int add_qjl, int tok0, int ntok, float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H_ */

@@ -1,0 +1,325 @@
+// Host-only part of libtq: codebooks, layer randomness, sizes, validation,
+// status strings.  No HIP calls here, so every function works without a GPU.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "tq_internal.h"
+
+namespace tq {
+
+static thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return TQ_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Gaussian helpers in long double (64-bit mantissa on x86-64).
+// ---------------------------------------------------------------------------
+typedef long double ld;
+static const ld kInvSqrt2Pi = 0.398942280401432677939946059934381868L;
+static const ld kInvSqrt2 = 0.707106781186547524400844362104849039L;
+
+static ld pdf(ld x) { return isinf(x) ? 0.0L : kInvSqrt2Pi * expl(-0.5L * x * x); }
+// Upper tail P(Z >= x), accurate for large positive x.
+static ld upper(ld x) { return isinf(x) ? (x > 0 ? 0.0L : 1.0L) : 0.5L * erfcl(x * kInvSqrt2); }
+
+// Lloyd-Max quantiser of N(0,1) with L = 2^bits levels.  By symmetry only the
+// positive centroids c[0..h-1] (h = L/2) are unknowns; cell i of the positive
+// half is [a_i, b_i) with a_0 = 0, a_i = (c[i-1] + c[i]) / 2, b_i = a_{i+1},
+// b_{h-1} = +inf, and the conditions are c[i] = E[Z | a_i <= Z < b_i].
+// Solved by a few Lloyd sweeps followed by Newton's method with the exact
+// tridiagonal Jacobian (Thomas algorithm), all in long double.
+static void lloyd_max(int bits, std::vector<ld>& cpos) {
+  const int h = 1 << (bits - 1);
+  cpos.assign(h, 0.0L);
+  // Start: centroids of equal-probability cells of N(0, 3) (companding shape).
+  for (int i = 0; i < h; ++i) {
+    // bisection for the quantile of (h + i + 0.5) / (2h) of N(0, 3)
+    ld p = (ld)(h + i) + 0.5L;
+    p /= (ld)(2 * h);
+    ld lo = 0.0L, hi = 20.0L;
+    for (int it = 0; it < 200; ++it) {
+      ld mid = 0.5L * (lo + hi);
+      if (1.0L - upper(mid / sqrtl(3.0L)) < p) lo = mid; else hi = mid;
+    }
+    cpos[i] = 0.5L * (lo + hi);
+  }
+  auto cond_means = [&](const std::vector<ld>& c, std::vector<ld>& m,
+                        std::vector<ld>* dm_da, std::vector<ld>* dm_db) {
+    for (int i = 0; i < h; ++i) {
+      ld a = i == 0 ? 0.0L : 0.5L * (c[i - 1] + c[i]);
+      ld b = i == h - 1 ? INFINITY : 0.5L * (c[i] + c[i + 1]);
+      ld P = upper(a) - upper(b);
+      ld mean = (pdf(a) - pdf(b)) / P;
+      m[i] = mean;
+      if (dm_da) (*dm_da)[i] = pdf(a) * (mean - a) / P;
+      if (dm_db) (*dm_db)[i] = isinf(b) ? 0.0L : pdf(b) * (b - mean) / P;
+    }
+  };
+  std::vector<ld> m(h), da(h), db(h);
+  for (int it = 0; it < 300; ++it) {
+    cond_means(cpos, m, nullptr, nullptr);
+    cpos = m;
+  }
+  // Newton on F(c) = c - m(c).
+  std::vector<ld> lower(h), diag(h), upperd(h), rhs(h);
+  for (int it = 0; it < 100; ++it) {
+    cond_means(cpos, m, &da, &db);
+    ld maxstep = 0.0L;
+    for (int i = 0; i < h; ++i) {
+      rhs[i] = -(cpos[i] - m[i]);
+      // m_i depends on a_i (through c[i-1], c[i]) for i > 0 and on b_i
+      // (through c[i], c[i+1]) for i < h-1; each edge is a midpoint.
+      ld dii = 0.0L;
+      if (i > 0) dii += 0.5L * da[i];
+      if (i < h - 1) dii += 0.5L * db[i];
+      diag[i] = 1.0L - dii;
+      lower[i] = i > 0 ? -0.5L * da[i] : 0.0L;
+      upperd[i] = i < h - 1 ? -0.5L * db[i] : 0.0L;
+    }
+    // Thomas algorithm.
+    for (int i = 1; i < h; ++i) {
+      ld w = lower[i] / diag[i - 1];
+      diag[i] -= w * upperd[i - 1];
+      rhs[i] -= w * rhs[i - 1];
+    }
+    std::vector<ld> step(h);
+    step[h - 1] = rhs[h - 1] / diag[h - 1];
+    for (int i = h - 2; i >= 0; --i) step[i] = (rhs[i] - upperd[i] * step[i + 1]) / diag[i];
+    for (int i = 0; i < h; ++i) {
+      cpos[i] += step[i];
+      maxstep = std::max(maxstep, fabsl(step[i]));
+    }
+    if (maxstep < 1e-18L) break;
+  }
+}
+
+// Mid-rise uniform grid with the MSE-optimal step for N(0,1): the step solves
+// g(delta) = delta * sum m_k^2 P_k - sum m_k (pdf(a_k) - pdf(b_k)) = 0, i.e.
+// d MSE / d delta = 0, summed over the positive half (the negative half adds
+// the same terms).  g < 0 below the optimum and > 0 above; found by bisection.
+static ld uniform_step(int bits) {
+  const int L = 1 << bits, h = L / 2;
+  auto g = [&](ld delta) {
+    ld num = 0.0L, den = 0.0L;
+    for (int i = 0; i < h; ++i) {
+      ld mk = (ld)i + 0.5L;
+      ld a = (ld)i * delta;
+      ld b = i == h - 1 ? INFINITY : (ld)(i + 1) * delta;
+      num += mk * (pdf(a) - pdf(b));
+      den += mk * mk * (upper(a) - upper(b));
+    }
+    return delta * den - num;
+  };
+  ld lo = 0.01L * 8.0L / L, hi = 8.0L * 8.0L / L;
+  for (int it = 0; it < 200; ++it) {
+    ld mid = 0.5L * (lo + hi);
+    if (g(mid) < 0.0L) lo = mid; else hi = mid;
+    if (hi - lo <= 1e-21L * hi) break;
+  }
+  return 0.5L * (lo + hi);
+}
+
+}  // namespace tq
+
+using namespace tq;
+
+extern "C" {
+
+const char* tq_last_error(void) { return g_last_error; }
+
+const char* tq_status_string(int status) {
+  switch (status) {
+    case TQ_OK: return "ok";
+    case TQ_ERR_INVALID_ARG: return "invalid argument";
+    case TQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case TQ_ERR_ALIGNMENT: return "misaligned pointer or stride";
+    case TQ_ERR_WORKSPACE: return "workspace too small";
+    case TQ_ERR_DEVICE: return "device error";
+    default: return "unknown status";
+  }
+}
+
+size_t tq_page_bytes(int k_bits, int v_bits, int qjl) {
+  if (k_bits == 0) {
+    if (v_bits != 0 || qjl) return 0;
+    return (size_t)2 * TQ_PAGE_TOKENS * TQ_HEAD_DIM * 2;
+  }
+  if (k_bits < 1 || k_bits > 8 || v_bits < 1 || v_bits > 8) return 0;
+  return (size_t)1024 * (k_bits + v_bits) + 512 + (qjl ? 1280 : 0);
+}
+
+uint64_t tq_page_descriptor(uint64_t offset, int k_bits, int v_bits, int qjl) {
+  if (tq_page_bytes(k_bits, v_bits, qjl) == 0) return 0;
+  if ((offset & 255) || offset > TQ_PAGE_OFFSET_MASK) return 0;
+  return offset | ((uint64_t)k_bits << 48) | ((uint64_t)v_bits << 52) |
+         (qjl ? TQ_PAGE_QJL : 0) | TQ_PAGE_PRESENT;
+}
+
+int tq_build_codebook(int bits, int kind, float* centroids, float* boundaries) {
+  if (bits < 1 || bits > 8) return fail(TQ_ERR_UNSUPPORTED, "bits must be in 1..8 (got %d)", bits);
+  if (!centroids || !boundaries) return fail(TQ_ERR_INVALID_ARG, "null output array");
+  const int L = 1 << bits, h = L / 2;
+  std::vector<ld> c(L);
+  if (kind == TQ_CODEBOOK_LLOYD_MAX) {
+    std::vector<ld> cpos;
+    lloyd_max(bits, cpos);
+    for (int i = 0; i < h; ++i) {
+      c[h + i] = cpos[i];
+      c[h - 1 - i] = -cpos[i];
+    }
+  } else if (kind == TQ_CODEBOOK_UNIFORM) {
+    ld delta = uniform_step(bits);
+    for (int k = 0; k < L; ++k) c[k] = ((ld)k - 0.5L * (ld)(L - 1)) * delta;
+  } else {
+    return fail(TQ_ERR_INVALID_ARG, "unknown codebook kind %d", kind);
+  }
+  for (int k = 0; k < L; ++k) centroids[k] = (float)c[k];
+  for (int k = 0; k + 1 < L; ++k) boundaries[k] = (float)(0.5L * (c[k] + c[k + 1]));
+  return ok();
+}
+
+int tq_codebook_table(int kind, float* table) {
+  if (!table) return fail(TQ_ERR_INVALID_ARG, "null table");
+  memset(table, 0, sizeof(float) * TQ_CODEBOOK_TABLE_FLOATS);
+  for (int b = 1; b <= 8; ++b) {
+    int st = tq_build_codebook(b, kind, table + centroid_offset(b), table + boundary_offset(b));
+    if (st != TQ_OK) return st;
+  }
+  return ok();
+}
+
+static uint64_t splitmix64_at(uint64_t seed, uint64_t index) {
+  // Output `index` (1-based) of SplitMix64 seeded with `seed`.
+  uint64_t z = seed + index * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+int tq_layer_params(uint64_t seed, int layer, int head_dim, int jl_dim, int8_t* signs,
+                    float* qjl_s) {
+  if (head_dim != TQ_HEAD_DIM) return fail(TQ_ERR_UNSUPPORTED, "head_dim must be 128");
+  if (qjl_s && jl_dim != TQ_JL_DIM) return fail(TQ_ERR_UNSUPPORTED, "jl_dim must be 128");
+  if (!signs) return fail(TQ_ERR_INVALID_ARG, "null signs");
+  const uint64_t s = seed + (uint64_t)(int64_t)layer;
+  for (int j = 0; j < head_dim; ++j) signs[j] = (splitmix64_at(s, j + 1) >> 63) ? -1 : 1;
+  if (qjl_s) {
+    const int n = jl_dim * head_dim;
+    const double two_pi = 2.0 * M_PI;
+    uint64_t idx = head_dim + 1;
+    for (int i = 0; i < n; i += 2) {
+      double u1 = (double)(splitmix64_at(s, idx++) >> 11) * (1.0 / 9007199254740992.0);
+      double u2 = (double)(splitmix64_at(s, idx++) >> 11) * (1.0 / 9007199254740992.0);
+      double r = sqrt(-2.0 * log(1.0 - u1));
+      double a = two_pi * u2;
+      qjl_s[i] = (float)(r * cos(a));
+      if (i + 1 < n) qjl_s[i + 1] = (float)(r * sin(a));
+    }
+  }
+  return ok();
+}
+
+int tq_sign_mask(const int8_t* signs, int head_dim, uint32_t* mask) {
+  if (!signs || !mask) return fail(TQ_ERR_INVALID_ARG, "null pointer");
+  if (head_dim != TQ_HEAD_DIM) return fail(TQ_ERR_UNSUPPORTED, "head_dim must be 128");
+  for (int w = 0; w < 4; ++w) mask[w] = 0;
+  for (int j = 0; j < head_dim; ++j) {
+    if (signs[j] != 1 && signs[j] != -1) return fail(TQ_ERR_INVALID_ARG, "sign %d is not +-1", j);
+    if (signs[j] < 0) mask[j >> 5] |= 1u << (j & 31);
+  }
+  return ok();
+}
+
+size_t tq_cache_bytes(const uint64_t* host_pages, size_t n) {
+  if (!host_pages) return 0;
+  size_t total = 0;
+  for (size_t i = 0; i < n; ++i) {
+    uint64_t d = host_pages[i];
+    if (!(d & TQ_PAGE_PRESENT)) continue;
+    total += tq_page_bytes((int)((d >> 48) & 15), (int)((d >> 52) & 15), (d & TQ_PAGE_QJL) ? 1 : 0);
+  }
+  return total;
+}
+
+size_t tq_decode_workspace_bytes(const tq_cache* cache, int n_q_heads) {
+  if (!cache || cache->n_sessions <= 0 || cache->n_kv_heads <= 0 || cache->max_pages <= 0 ||
+      n_q_heads <= 0)
+    return 0;
+  SplitPlan sp = split_plan(cache->n_sessions, cache->n_kv_heads, cache->max_pages);
+  return decode_workspace_bytes(cache->n_sessions, n_q_heads, sp.n_splits);
+}
+
+}  // extern "C"
+
+namespace tq {
+
+SplitPlan split_plan(int n_sessions, int n_kv_heads, int max_pages) {
+  // Enough workgroups to fill the GPU several times over, each with at least
+  // one page per wave.
+  const int64_t units = (int64_t)n_sessions * n_kv_heads;
+  int64_t total_pages = units * max_pages;
+  int64_t pps = (total_pages + kTargetSplitGroups - 1) / kTargetSplitGroups;
+  if (pps < kDecodeWaves) pps = kDecodeWaves;
+  if (pps > max_pages) pps = max_pages;
+  SplitPlan sp;
+  sp.pages_per_split = (int)pps;
+  sp.n_splits = (int)((max_pages + pps - 1) / pps);
+  return sp;
+}
+
+size_t decode_workspace_bytes(int n_sessions, int n_q_heads, int n_splits) {
+  const size_t rows = (size_t)n_sessions * n_q_heads;
+  return sizeof(float) * rows * (kQPrepFloats + (size_t)n_splits * kPartialFloats);
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+int check_layer(const tq_layer* L) {
+  if (!L) return fail(TQ_ERR_INVALID_ARG, "null layer descriptor");
+  if (L->head_dim != TQ_HEAD_DIM) return fail(TQ_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", L->head_dim);
+  if (L->k_codebook != TQ_CODEBOOK_LLOYD_MAX && L->k_codebook != TQ_CODEBOOK_UNIFORM)
+    return fail(TQ_ERR_INVALID_ARG, "unknown k_codebook %d", L->k_codebook);
+  if (L->v_codebook != TQ_CODEBOOK_LLOYD_MAX && L->v_codebook != TQ_CODEBOOK_UNIFORM)
+    return fail(TQ_ERR_INVALID_ARG, "unknown v_codebook %d", L->v_codebook);
+  if (!L->sign_mask || !L->k_table || !L->v_table) return fail(TQ_ERR_INVALID_ARG, "null layer table");
+  if (!aligned16(L->sign_mask) || !aligned16(L->k_table) || !aligned16(L->v_table))
+    return fail(TQ_ERR_ALIGNMENT, "layer tables must be 16-byte aligned");
+  if (L->qjl_s) {
+    if (L->jl_dim != TQ_JL_DIM) return fail(TQ_ERR_UNSUPPORTED, "jl_dim must be 128 (got %d)", L->jl_dim);
+    if (!aligned16(L->qjl_s)) return fail(TQ_ERR_ALIGNMENT, "qjl_s must be 16-byte aligned");
+  }
+  return TQ_OK;
+}
+
+int check_cache(const tq_cache* C) {
+  if (!C) return fail(TQ_ERR_INVALID_ARG, "null cache descriptor");
+  if (C->n_sessions <= 0 || C->n_kv_heads <= 0 || C->max_pages <= 0)
+    return fail(TQ_ERR_INVALID_ARG, "cache sizes must be positive (B=%d H_kv=%d max_pages=%d)",
+                C->n_sessions, C->n_kv_heads, C->max_pages);
+  if ((int64_t)C->max_pages * TQ_PAGE_TOKENS > (int64_t)0x7fffffff)
+    return fail(TQ_ERR_INVALID_ARG, "max_pages too large");
+  if (!C->n_tokens || !C->pages || !C->pool) return fail(TQ_ERR_INVALID_ARG, "null cache pointer");
+  if (((uintptr_t)C->pool & 255) != 0) return fail(TQ_ERR_ALIGNMENT, "pool must be 256-byte aligned");
+  if (((uintptr_t)C->pages & 7) != 0 || ((uintptr_t)C->n_tokens & 3) != 0)
+    return fail(TQ_ERR_ALIGNMENT, "page table / token counts misaligned");
+  if (C->pool_bytes == 0) return fail(TQ_ERR_INVALID_ARG, "empty pool");
+  return TQ_OK;
+}
+
+}  // namespace tq

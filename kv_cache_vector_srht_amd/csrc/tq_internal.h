@@ -1,0 +1,39 @@
+// Internal declarations shared by the host and device translation units of libtq.
+#ifndef TQ_INTERNAL_H_
+#define TQ_INTERNAL_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "tq.h"
+
+namespace tq {
+
+// Records a message for tq_last_error() and returns `status`.
+int fail(int status, const char* fmt, ...);
+int ok();
+
+// Float offsets into a codebook table (all bit widths of one kind).
+constexpr int centroid_offset(int bits) { return (1 << bits) - 2; }
+constexpr int boundary_offset(int bits) { return 510 + (1 << bits) - bits - 1; }
+
+// Decode split-K geometry.
+constexpr int kDecodeWaves = 4;             // waves per split workgroup
+constexpr int kTargetSplitGroups = 1024;    // workgroups the split grid aims for
+constexpr int kQPrepFloats = 3 * 128;       // rotated q, plain q, S q (all pre-scaled)
+constexpr int kPartialFloats = 4 + 2 * 128; // m_r, l_r, m_o, l_o, acc_r[128], acc_o[128]
+
+struct SplitPlan {
+  int n_splits;
+  int pages_per_split;
+};
+SplitPlan split_plan(int n_sessions, int n_kv_heads, int max_pages);
+size_t decode_workspace_bytes(int n_sessions, int n_q_heads, int n_splits);
+
+// Validation shared by the device entry points (host only, before any HIP call).
+int check_layer(const tq_layer* layer);
+int check_cache(const tq_cache* cache);
+
+}  // namespace tq
+
+#endif  // TQ_INTERNAL_H_

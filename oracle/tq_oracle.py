@@ -1,0 +1,548 @@
+"""CPU oracle for the SRHT KV-cache codec and compressed-domain decode attention.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call anything here.  The
+product path (the HIP library and its Python binding) never does, and this
+module imports nothing from it: the only code both sides share is the seeded
+input generator module ``workloads``.
+
+Everything is plain numpy in float64 (scipy/mpmath only as root finders), written
+to be read against the source pages:
+
+* "TurboQuant-MLX v2.0", What's New > Walsh-Hadamard Rotation and
+  How It Works > Pipeline: the randomized rotation is the SRHT ``D @ H @ D``
+  (sign diagonal, Walsh-Hadamard, the same sign diagonal), O(n log n),
+  orthogonal and invertible; the norm of each vector is kept and no per-block
+  constants are stored; QJL corrects keys only with ``sign(S . residual)``.
+* "TurboMOQ", Architecture and Full Feature Set: Lloyd-Max codebooks,
+  symmetric/grid quantisation, per-head bit widths 1-8; QJL residual
+  correction section: 1-bit sign-encoded JL projection with a per-vector scale.
+* "TurboQuant-MLX v2.0", What's New > FP16 Attention Sinks and Dynamic Chunk
+  Buffering: the first 128 tokens stay fp16, compression fires on 64-token chunks.
+
+Readings where the pages are silent (each also listed in the design notes):
+  R1 one sign diagonal D on both sides of H, so R = D H D / sqrt(d) is symmetric
+     and its own inverse; H in Sylvester (natural) order.
+  R2 the scalar quantiser sees u = sqrt(d) R x / ||x||, which is ~N(0,1) per
+     coordinate; the norm is stored as float32.
+  R3 code = #{k : t_k <= u} with t the float32 boundaries (ties round up) and the
+     decision taken in float32 on both sides: u is rounded to float32 first.
+  R4 code 0 is the most negative centroid; codes are packed LSB-first in
+     128-code streams (layout below).
+  R5 QJL: r = x - xhat in the original domain, z = sign(S r) with sign(0) = +1,
+     gamma = ||r|| (float32), rhat = sqrt(pi/2)/m * gamma * S^T z.
+  R6 attention: scores q.k / sqrt(d), softmax over every cached token of the
+     session, query head h reads KV head floor(h / G).
+
+Parity pins live in ``tests/test_oracle_pins.py``.  The packing layout itself is
+a convention (the pages name bit packing only as a utility module); it is pinned by
+the bijection/round-trip/footprint checks there.
+"""
+from __future__ import annotations
+
+import math
+from functools import lru_cache
+from typing import Dict, List, Sequence, Tuple
+
+import numpy as np
+from scipy import optimize
+from scipy.special import ndtr
+
+HEAD_DIM = 128
+PAGE_TOKENS = 64
+STREAM_CODES = 128
+LLOYD_MAX = 0
+UNIFORM = 1
+
+
+# ----------------------------------------------------------------------------
+# Rotation ("TurboQuant-MLX v2.0", What's New > Walsh-Hadamard Rotation).
+# ----------------------------------------------------------------------------
+def sylvester_hadamard(d: int) -> np.ndarray:
+    """Sylvester Hadamard matrix: H_1 = [1], H_2n = [[H, H], [H, -H]] (int64)."""
+    assert d >= 1 and (d & (d - 1)) == 0
+    H = np.ones((1, 1), dtype=np.int64)
+    while H.shape[0] < d:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+def rotation_matrix(signs: Sequence[int]) -> np.ndarray:
+    """R = D H D / sqrt(d) with D = diag(signs) (reading R1), float64."""
+    return _rotation_cached(tuple(int(v) for v in np.asarray(signs).ravel())).copy()
+
+
+@lru_cache(maxsize=64)
+def _rotation_cached(signs: Tuple[int, ...]) -> np.ndarray:
+    s = np.asarray(signs, dtype=np.float64)
+    d = s.shape[0]
+    Dm = np.diag(s)
+    return Dm @ sylvester_hadamard(d).astype(np.float64) @ Dm / math.sqrt(d)
+
+
+# ----------------------------------------------------------------------------
+# Codebooks ("TurboMOQ", Architecture: Lloyd-Max codebook; symmetric grid).
+# ----------------------------------------------------------------------------
+def _phi(x):
+    with np.errstate(over="ignore"):
+        return np.exp(-0.5 * np.square(x)) / math.sqrt(2.0 * math.pi)
+
+
+def _mass(a, b):
+    """P(a <= Z < b) for Z ~ N(0,1), evaluated on the tail side (no cancellation)."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return np.where(a >= 0, ndtr(-a) - ndtr(-b), ndtr(b) - ndtr(a))
+
+
+def _centroids_of_cells(edges):
+    """E[Z | edges_k <= Z < edges_k+1] for every cell."""
+    return (_phi(edges[:-1]) - _phi(edges[1:])) / _mass(edges[:-1], edges[1:])
+
+
+def _lloyd_map(cpos: np.ndarray) -> np.ndarray:
+    """One Lloyd-Max update of the positive half of a symmetric codebook.
+
+    Boundaries are midpoints of neighbouring centroids; centroids are the
+    conditional means of N(0,1) over their cells.
+    """
+    c = np.concatenate((-cpos[::-1], cpos))
+    t = 0.5 * (c[:-1] + c[1:])
+    edges = np.concatenate(([-np.inf], t, [np.inf]))
+    return _centroids_of_cells(edges)[cpos.size:]
+
+
+@lru_cache(maxsize=None)
+def lloyd_max_gaussian(bits: int) -> Tuple[np.ndarray, np.ndarray]:
+    """MSE-optimal 2^bits-level scalar quantiser for N(0,1) (Lloyd-Max).
+
+    The quantiser is the unique fixed point (N(0,1) is log-concave) of the two
+    Lloyd-Max conditions; it is symmetric, so only the positive half is solved.
+    Steps: Lloyd iterations from a spread start, a library root finder on the
+    conditions in float64, then Newton steps in 40-digit arithmetic (the fixed
+    point is ill-conditioned at 8 bits: the Lloyd map contracts by 0.99985).
+
+    Returns (centroids, boundaries) in float64, ascending; boundaries are the
+    midpoints of neighbouring centroids.
+    """
+    import mpmath as mp
+    L = 1 << bits
+    h = L // 2
+    k = np.arange(h)
+    cpos = math.sqrt(3.0) * np.sqrt(2.0) * np.array(
+        [float(mp.erfinv((2 * (h + i) + 1) / L - 1)) for i in k])
+    for _ in range(200):
+        cpos = _lloyd_map(cpos)
+    sol = optimize.root(lambda c: c - _lloyd_map(c), cpos, method="hybr", tol=1e-15)
+    cpos = np.sort(sol.x)
+
+    with mp.workdps(40):
+        def cond_mean(a, b):
+            pa = mp.npdf(a) if a != -mp.inf else mp.mpf(0)
+            pb = mp.npdf(b) if b != mp.inf else mp.mpf(0)
+            if a >= 0:
+                m = mp.ncdf(-a) - mp.ncdf(-b)
+            else:
+                m = mp.ncdf(b) - mp.ncdf(a)
+            return (pa - pb) / m
+
+        def F(*cp):
+            c = [-x for x in reversed(cp)] + list(cp)
+            t = [(c[i] + c[i + 1]) / 2 for i in range(len(c) - 1)]
+            e = [-mp.inf] + t + [mp.inf]
+            return [cp[i] - cond_mean(e[h + i], e[h + i + 1]) for i in range(h)]
+
+        x0 = [mp.mpf(float(v)) for v in cpos]
+        if h == 1:
+            root = [mp.findroot(lambda x: F(x)[0], x0[0])]
+        else:
+            root = mp.findroot(F, x0, tol=mp.mpf(10) ** -30)
+            root = [root[i] for i in range(h)]
+        root = [+r for r in root]   # round to the working precision first
+        cfull = [-x for x in reversed(root)] + list(root)
+        tfull = [(cfull[i] + cfull[i + 1]) / 2 for i in range(L - 1)]
+        c = np.array([float(x) for x in cfull])
+        t = np.array([float(x) for x in tfull])
+        # float32 rounding taken from the high-precision values
+        c32 = np.array([_round_f32(x) for x in cfull], dtype=np.float32)
+        t32 = np.array([_round_f32(x) for x in tfull], dtype=np.float32)
+    _F32_TABLES[(bits, LLOYD_MAX)] = (c32, t32)
+    return c, t
+
+
+def _round_f32(x) -> np.float32:
+    """float32 nearest to the mpmath number x (checked against both neighbours)."""
+    import mpmath as mp
+    f = np.float32(float(x))
+    cands = (np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf)))
+    return min(cands, key=lambda c: abs(mp.mpf(float(c)) - x))
+
+
+_F32_TABLES: Dict[Tuple[int, int], Tuple[np.ndarray, np.ndarray]] = {}
+
+
+@lru_cache(maxsize=None)
+def uniform_gaussian(bits: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Symmetric mid-rise uniform grid with the MSE-optimal step for N(0,1).
+
+    Levels c_k = (k - (L-1)/2) * delta, boundaries at their midpoints
+    (k - L/2) * delta.  delta solves d MSE / d delta = 0, i.e.
+    delta * sum_k m_k^2 P_k = sum_k m_k (phi(a_k) - phi(b_k)) with m_k the
+    level multipliers and [a_k, b_k) the cells (the cell edges move with delta,
+    but the squared error is continuous across them, so no edge terms appear).
+    """
+    import mpmath as mp
+    L = 1 << bits
+    m = [mp.mpf(2 * k - (L - 1)) / 2 for k in range(L)]
+
+    with mp.workdps(40):
+        def g(delta):
+            num = mp.mpf(0)
+            den = mp.mpf(0)
+            for k in range(L):
+                a = -mp.inf if k == 0 else (k - mp.mpf(L) / 2) * delta
+                b = mp.inf if k == L - 1 else (k + 1 - mp.mpf(L) / 2) * delta
+                pa = mp.mpf(0) if a == -mp.inf else mp.npdf(a)
+                pb = mp.mpf(0) if b == mp.inf else mp.npdf(b)
+                P = mp.ncdf(b) - mp.ncdf(a) if (a == -mp.inf or a < 0) else mp.ncdf(-a) - mp.ncdf(-b)
+                num += m[k] * (pa - pb)
+                den += m[k] ** 2 * P
+            return delta * den - num
+
+        # bracket from the 1-bit closed form downward
+        delta = mp.findroot(g, (mp.mpf(0.5) * 4 / L, mp.mpf(4.0) * 4 / L), solver="anderson")
+        cfull = [mk * delta for mk in m]
+        tfull = [(k + 1 - mp.mpf(L) / 2) * delta for k in range(L - 1)]
+        c = np.array([float(x) for x in cfull])
+        t = np.array([float(x) for x in tfull])
+        _F32_TABLES[(bits, UNIFORM)] = (
+            np.array([_round_f32(x) for x in cfull], dtype=np.float32),
+            np.array([_round_f32(x) for x in tfull], dtype=np.float32))
+        _UNIFORM_DELTA[bits] = float(delta)
+    return c, t
+
+
+_UNIFORM_DELTA: Dict[int, float] = {}
+
+
+def uniform_step(bits: int) -> float:
+    uniform_gaussian(bits)
+    return _UNIFORM_DELTA[bits]
+
+
+def codebook(bits: int, kind: int = LLOYD_MAX) -> Tuple[np.ndarray, np.ndarray]:
+    """(centroids, boundaries) as float32 arrays, the values both sides compare with."""
+    if kind == LLOYD_MAX:
+        lloyd_max_gaussian(bits)
+    elif kind == UNIFORM:
+        uniform_gaussian(bits)
+    else:
+        raise ValueError(kind)
+    return _F32_TABLES[(bits, kind)]
+
+
+def gaussian_mse(centroids, boundaries) -> float:
+    """E[(Z - Q(Z))^2] for Z ~ N(0,1) of a scalar quantiser (float64 closed form).
+
+    Over a cell [a, b) with level c: E[(Z-c)^2 1_cell] =
+    P (1 + c^2) + (a phi(a) - b phi(b)) - 2 c (phi(a) - phi(b)).
+    """
+    c = np.asarray(centroids, dtype=np.float64)
+    e = np.concatenate(([-np.inf], np.asarray(boundaries, dtype=np.float64), [np.inf]))
+    a, b = e[:-1], e[1:]
+    P = _mass(a, b)
+    aphi = np.where(np.isinf(a), 0.0, np.nan_to_num(a) * _phi(np.nan_to_num(a)))
+    bphi = np.where(np.isinf(b), 0.0, np.nan_to_num(b) * _phi(np.nan_to_num(b)))
+    dphi = _phi(a) - _phi(b)
+    return float(np.sum(P * (1 + c * c) + (aphi - bphi) - 2 * c * dphi))
+
+
+# ----------------------------------------------------------------------------
+# Encode / dequantise one batch of head vectors.
+# ----------------------------------------------------------------------------
+def encode(X: np.ndarray, signs, bits: int, kind: int = LLOYD_MAX,
+           boundary_eps: float = 1e-6) -> Dict[str, np.ndarray]:
+    """Encode rows of X (values as stored, upcast to float64).
+
+    n = ||x||_2 (stored float32); u = sqrt(d) R x / n (u = 0 when n = 0);
+    code_j = #{k : t_k <= float32(u_j)} (readings R2, R3).
+    ``near`` flags coordinates whose float64 u lies within ``boundary_eps`` of
+    a boundary: there the float32 decision may legitimately differ by one level.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    d = X.shape[-1]
+    R = rotation_matrix(signs)
+    n = np.sqrt(np.sum(X * X, axis=-1))
+    Y = X @ R.T
+    safe = np.where(n > 0, n, 1.0)
+    U = np.where(n[:, None] > 0, math.sqrt(d) * Y / safe[:, None], 0.0)
+    c32, t32 = codebook(bits, kind)
+    U32 = U.astype(np.float32)
+    # the number of boundaries <= u (t32 is ascending)
+    codes = np.searchsorted(t32, U32, side="right").astype(np.int64)
+    t64 = t32.astype(np.float64)
+    below = np.abs(U - t64[np.clip(codes - 1, 0, t64.size - 1)])
+    above = np.abs(U - t64[np.clip(codes, 0, t64.size - 1)])
+    near = np.minimum(below, above) < boundary_eps
+    return {"norm": n.astype(np.float32), "u": U, "codes": codes, "near": near}
+
+
+def dequantize(norm32: np.ndarray, codes: np.ndarray, signs, bits: int,
+               kind: int = LLOYD_MAX) -> np.ndarray:
+    """xhat = (n / sqrt(d)) R^T c[code], from the stored float32 values."""
+    c32, _ = codebook(bits, kind)
+    R = rotation_matrix(signs)
+    d = R.shape[0]
+    C = c32.astype(np.float64)[codes]
+    return (np.asarray(norm32, dtype=np.float64)[:, None] / math.sqrt(d)) * (C @ R)
+
+
+def qjl_encode(X: np.ndarray, Xhat: np.ndarray, S: np.ndarray,
+               sign_eps: float = 1e-5) -> Dict[str, np.ndarray]:
+    """QJL residual sketch of keys ("TurboMOQ", QJL residual correction).
+
+    r = x - xhat; z_i = +1 if (S r)_i >= 0 else -1; gamma = ||r|| (float32).
+    ``near`` flags projections with |(S r)_i| < sign_eps * ||S_i|| ||r||, where
+    float32 evaluation may flip the sign.
+    """
+    r = np.asarray(X, dtype=np.float64) - np.asarray(Xhat, dtype=np.float64)
+    S = np.asarray(S, dtype=np.float64)
+    P = r @ S.T
+    z = P >= 0
+    g = np.sqrt(np.sum(r * r, axis=-1))
+    bound = np.sqrt(np.sum(S * S, axis=-1))[None, :] * g[:, None]
+    return {"z": z, "gamma": g.astype(np.float32), "near": np.abs(P) < sign_eps * bound,
+            "residual": r}
+
+
+def qjl_reconstruct(z: np.ndarray, gamma32: np.ndarray, S: np.ndarray) -> np.ndarray:
+    """rhat = sqrt(pi/2) / m * gamma * S^T z, z in {-1, +1}."""
+    S = np.asarray(S, dtype=np.float64)
+    m = S.shape[0]
+    zs = np.where(z, 1.0, -1.0)
+    return math.sqrt(math.pi / 2.0) / m * np.asarray(gamma32, dtype=np.float64)[:, None] * (zs @ S)
+
+
+# ----------------------------------------------------------------------------
+# Packed page layout (reading R4).
+#
+# A page holds 64 tokens of one (session, KV head).  Each b-bit code block is
+# 64 streams of 128 codes; a stream is its codes LSB-first (code n at bits
+# n*b .. n*b+b-1), i.e. b little-endian 128-bit words, and word w of stream s
+# sits at byte (w*64 + s)*16 of the block.
+#   K block: stream t = token t, codes of coordinates 0..127 in order.
+#   V block: stream s = 16q + i holds, for k = 0..15 and e = 0..7, the code of
+#            token 4k+q, coordinate 8i+e at stream position 8k+e.
+# Page = K block (1024 bK B) | K norms (64 x f32) | [QJL signs 64 x 16 B,
+#        bit i of token t's 128-bit word = z_i, | QJL gamma 64 x f32] |
+#        V block (1024 bV B) | V norms (64 x f32).
+# An fp16 page is the 64 K rows then the 64 V rows, fp16, 128 per row.
+# ----------------------------------------------------------------------------
+def k_stream_codes(codes: np.ndarray) -> np.ndarray:
+    """[64 tokens][128 coords] -> [64 streams][128 codes] for a K block."""
+    assert codes.shape == (PAGE_TOKENS, HEAD_DIM)
+    return np.array(codes, copy=True)
+
+
+def v_stream_codes(codes: np.ndarray) -> np.ndarray:
+    """[64 tokens][128 coords] -> [64 streams][128 codes] for a V block.
+
+    Token 4k+q, coordinate 8i+e goes to stream 16q+i, position 8k+e: view the
+    codes as [k][q][i][e] and reorder the axes to [q][i][k][e].
+    """
+    assert codes.shape == (PAGE_TOKENS, HEAD_DIM)
+    return np.asarray(codes).reshape(16, 4, 16, 8).transpose(1, 2, 0, 3).reshape(64, 128)
+
+
+def v_codes_from_streams(streams: np.ndarray) -> np.ndarray:
+    """Inverse of v_stream_codes."""
+    return np.asarray(streams).reshape(4, 16, 16, 8).transpose(2, 0, 1, 3).reshape(64, 128)
+
+
+def pack_block(streams: np.ndarray, bits: int) -> bytes:
+    """64 streams of 128 codes -> 1024*bits bytes (layout above).
+
+    Bit n*bits+k of a stream is bit k of its code n; the stream's bits are
+    gathered into little-endian bytes, cut into 16-byte words, and word w of
+    stream s is written at byte (w*64 + s)*16.
+    """
+    streams = np.asarray(streams, dtype=np.int64)
+    assert streams.shape == (64, STREAM_CODES)
+    assert streams.min() >= 0 and streams.max() < (1 << bits)
+    k = np.arange(bits)
+    stream_bits = ((streams[:, :, None] >> k[None, None, :]) & 1).astype(np.uint8)  # [s][n][k]
+    stream_bytes = np.packbits(stream_bits.reshape(64, STREAM_CODES * bits), axis=1,
+                               bitorder="little")                                   # [s][16*bits]
+    words = stream_bytes.reshape(64, bits, 16).transpose(1, 0, 2)                      # [w][s][16]
+    return words.tobytes()
+
+
+def unpack_block(block: bytes, bits: int) -> np.ndarray:
+    """Inverse of pack_block: 1024*bits bytes -> [64 streams][128 codes]."""
+    assert len(block) == 1024 * bits
+    words = np.frombuffer(block, dtype=np.uint8).reshape(bits, 64, 16).transpose(1, 0, 2)
+    stream_bits = np.unpackbits(words.reshape(64, 16 * bits), axis=1, bitorder="little")
+    stream_bits = stream_bits.reshape(64, STREAM_CODES, bits).astype(np.int64)
+    return np.sum(stream_bits << np.arange(bits)[None, None, :], axis=2)
+
+
+def pack_signs(z: np.ndarray) -> bytes:
+    """[T][128] booleans -> T x 16 bytes; bit i of token t's word is z[t, i]."""
+    z = np.asarray(z, dtype=np.uint8)
+    return np.packbits(z, axis=1, bitorder="little").tobytes()
+
+
+def unpack_signs(raw: bytes) -> np.ndarray:
+    b = np.frombuffer(raw, dtype=np.uint8).reshape(-1, 16)
+    return np.unpackbits(b, axis=1, bitorder="little").astype(bool)
+
+
+def page_bytes(fmt) -> int:
+    """Bytes one page of this format occupies."""
+    kb, vb, qjl = fmt
+    if kb == 0:
+        return 2 * PAGE_TOKENS * HEAD_DIM * 2
+    return 1024 * (kb + vb) + 2 * 256 + (1024 + 256 if qjl else 0)
+
+
+def page_sections(fmt) -> Dict[str, Tuple[int, int]]:
+    kb, vb, qjl = fmt
+    off = 0
+    sec = {}
+    for name, size in (("k_codes", 1024 * kb), ("k_norm", 256),
+                       ("qjl_signs", 1024 if qjl else 0), ("qjl_gamma", 256 if qjl else 0),
+                       ("v_codes", 1024 * vb), ("v_norm", 256)):
+        sec[name] = (off, size)
+        off += size
+    return sec
+
+
+def encode_page(K64: np.ndarray, V64: np.ndarray, fmt, signs, S=None,
+                k_kind: int = LLOYD_MAX, v_kind: int = LLOYD_MAX) -> Dict:
+    """Encode one full packed page; returns the page bytes and the pieces."""
+    kb, vb, qjl = fmt
+    assert kb > 0 and K64.shape == (PAGE_TOKENS, HEAD_DIM)
+    ek = encode(K64, signs, kb, k_kind)
+    ev = encode(V64, signs, vb, v_kind)
+    sec = page_sections(fmt)
+    buf = bytearray(page_bytes(fmt))
+
+    def put(name, data):
+        o, n = sec[name]
+        assert len(data) == n
+        buf[o:o + n] = data
+
+    put("k_codes", pack_block(k_stream_codes(ek["codes"]), kb))
+    put("k_norm", ek["norm"].astype("<f4").tobytes())
+    res = {"k": ek, "v": ev}
+    if qjl:
+        khat = dequantize(ek["norm"], ek["codes"], signs, kb, k_kind)
+        qj = qjl_encode(K64, khat, S)
+        put("qjl_signs", pack_signs(qj["z"]))
+        put("qjl_gamma", qj["gamma"].astype("<f4").tobytes())
+        res["qjl"] = qj
+    put("v_codes", pack_block(v_stream_codes(ev["codes"]), vb))
+    put("v_norm", ev["norm"].astype("<f4").tobytes())
+    res["bytes"] = bytes(buf)
+    return res
+
+
+def fp16_page_bytes(K: np.ndarray, V: np.ndarray) -> bytes:
+    """An fp16 page: 64 K rows then 64 V rows (tokens past the end stay zero)."""
+    buf = np.zeros((2, PAGE_TOKENS, HEAD_DIM), dtype="<f2")
+    buf[0, :K.shape[0]] = np.asarray(K, dtype=np.float16)
+    buf[1, :V.shape[0]] = np.asarray(V, dtype=np.float16)
+    return buf.tobytes()
+
+
+def decode_page(raw: bytes, fmt, signs, S=None, k_kind: int = LLOYD_MAX,
+                v_kind: int = LLOYD_MAX, add_qjl: bool = True):
+    """Reconstructed (keys, values) float64 [64, 128] of one page's bytes."""
+    kb, vb, qjl = fmt
+    if kb == 0:
+        a = np.frombuffer(raw, dtype="<f2").reshape(2, PAGE_TOKENS, HEAD_DIM).astype(np.float64)
+        return a[0], a[1]
+    sec = page_sections(fmt)
+
+    def get(name):
+        o, n = sec[name]
+        return raw[o:o + n]
+    kc = unpack_block(get("k_codes"), kb)
+    kn = np.frombuffer(get("k_norm"), dtype="<f4")
+    vc = v_codes_from_streams(unpack_block(get("v_codes"), vb))
+    vn = np.frombuffer(get("v_norm"), dtype="<f4")
+    K = dequantize(kn, kc, signs, kb, k_kind)
+    if qjl and add_qjl:
+        z = unpack_signs(get("qjl_signs"))
+        g = np.frombuffer(get("qjl_gamma"), dtype="<f4")
+        K = K + qjl_reconstruct(z, g, S)
+    V = dequantize(vn, vc, signs, vb, v_kind)
+    return K, V
+
+
+# ----------------------------------------------------------------------------
+# Attention over the reconstructed cache (reading R6).
+# ----------------------------------------------------------------------------
+def attention(q: np.ndarray, keys: np.ndarray, values: np.ndarray,
+              scale: float | None = None) -> np.ndarray:
+    """softmax(keys q * scale) . values for one query vector (float64)."""
+    q = np.asarray(q, dtype=np.float64)
+    keys = np.asarray(keys, dtype=np.float64)
+    values = np.asarray(values, dtype=np.float64)
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    s = keys @ q * scale
+    p = np.exp(s - np.max(s))
+    return (p[:, None] * values).sum(axis=0) / p.sum()
+
+
+def reconstruct_unit(K: np.ndarray, V: np.ndarray, formats, signs, S=None,
+                     k_kind: int = LLOYD_MAX, v_kind: int = LLOYD_MAX):
+    """Keys/values as decode attention sees them for one (session, KV head).
+
+    K, V: the stored input rows [T, 128] of this unit; formats: page formats.
+    fp16 pages keep the fp16 values; packed pages are encoded then dequantised
+    (keys plus the QJL residual when the page carries one).  Pages of one
+    format are encoded together (rows are independent).
+    """
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    T = K.shape[0]
+    Kh = np.zeros((T, HEAD_DIM))
+    Vh = np.zeros((T, HEAD_DIM))
+    groups: Dict[Tuple, List[int]] = {}
+    for p, fmt in enumerate(formats):
+        lo, hi = p * PAGE_TOKENS, min(T, (p + 1) * PAGE_TOKENS)
+        if lo >= T:
+            break
+        if fmt[0] == 0:
+            Kh[lo:hi] = K[lo:hi].astype(np.float16).astype(np.float64)
+            Vh[lo:hi] = V[lo:hi].astype(np.float16).astype(np.float64)
+        else:
+            assert hi - lo == PAGE_TOKENS, "a packed page must be full"
+            groups.setdefault(tuple(fmt), []).append(p)
+    for fmt, plist in groups.items():
+        kb, vb, qjl = fmt
+        rows = np.concatenate([np.arange(p * PAGE_TOKENS, (p + 1) * PAGE_TOKENS) for p in plist])
+        ek = encode(K[rows], signs, kb, k_kind)
+        ev = encode(V[rows], signs, vb, v_kind)
+        kh = dequantize(ek["norm"], ek["codes"], signs, kb, k_kind)
+        if qjl:
+            qj = qjl_encode(K[rows], kh, S)
+            kh = kh + qjl_reconstruct(qj["z"], qj["gamma"], S)
+        Kh[rows] = kh
+        Vh[rows] = dequantize(ev["norm"], ev["codes"], signs, vb, v_kind)
+    return Kh, Vh
+
+
+def decode_attention_unit(q_heads: np.ndarray, Kh: np.ndarray, Vh: np.ndarray) -> np.ndarray:
+    """Outputs [G, 128] for the G query heads that read one KV head."""
+    return np.stack([attention(q, Kh, Vh) for q in np.asarray(q_heads, dtype=np.float64)])
+
+
+# ----------------------------------------------------------------------------
+# Footprint.
+# ----------------------------------------------------------------------------
+def cache_bytes(formats_flat: Sequence) -> int:
+    """Bytes of a cache whose pages have these formats."""
+    return int(sum(page_bytes(f) for f in formats_flat))

@@ -1,0 +1,383 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test fixes a part of ``oracle/tq_oracle.py`` with a closed form, an
+invariant, a textbook table (tests/golden/max1960_gaussian.json), a figure the
+pages print (tests/golden/pages_figures.json), an independent numerical routine
+(quadrature) or a brute-force loop, chosen so that a plausible slip in the
+oracle (a dropped D, a transposed operand, a wrong constant, an off-by-one
+code) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy import integrate
+
+from oracle import tq_oracle as O
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _signs(seed=5):
+    return W.rotation_signs(seed, 0)
+
+
+# ----------------------------------------------------------------- rotation
+def test_hadamard_closed_form_and_orthogonality():
+    d = 128
+    H = O.sylvester_hadamard(d)
+    i = np.arange(d)
+    pop = np.vectorize(lambda v: bin(v).count("1"))(i[:, None] & i[None, :])
+    assert np.array_equal(H, np.where(pop % 2 == 0, 1, -1))
+    assert np.array_equal(H @ H.T, d * np.eye(d, dtype=np.int64))
+
+
+def test_rotation_two_by_two_by_hand():
+    # D = diag(1, -1): D H D = [[1, -1], [-1, -1]]
+    R = O.rotation_matrix([1, -1])
+    assert np.allclose(R, np.array([[1.0, -1.0], [-1.0, -1.0]]) / math.sqrt(2), atol=1e-15)
+
+
+def test_rotation_orthogonal_symmetric_involutory():
+    s = _signs()
+    R = O.rotation_matrix(s)
+    I = np.eye(128)
+    assert np.max(np.abs(R @ R.T - I)) < 1e-12
+    assert np.max(np.abs(R - R.T)) == 0.0
+    # one D on both sides: R is its own inverse (D H D D H D = D H H D = d I)
+    assert np.max(np.abs(R @ R - I)) < 1e-12
+    x = np.random.default_rng(1).standard_normal((16, 128))
+    assert np.allclose(np.linalg.norm(x @ R.T, axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)
+    assert np.allclose(np.abs(R[:, 0]), 1 / math.sqrt(128), atol=1e-15)
+    # all-plus signs reduce to the normalised Sylvester matrix
+    assert np.allclose(O.rotation_matrix(np.ones(128)), O.sylvester_hadamard(128) / math.sqrt(128))
+
+
+def test_rotation_gaussianises_outliers():
+    # TurboQuant-MLX v2.0, How It Works > Pipeline: the rotation brings heavy
+    # outlier channels to a near-Gaussian coordinate distribution (kurtosis ~3).
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((4000, 128))
+    x[:, [7, 31, 64, 100]] *= 20.0
+    k_before = np.mean(x ** 4) / np.mean(x ** 2) ** 2
+    u = x @ O.rotation_matrix(_signs()).T
+    k_after = np.mean(u ** 4) / np.mean(u ** 2) ** 2
+    assert k_before > 50 and 1.5 < k_after < 3.5
+
+
+# ----------------------------------------------------------------- codebooks
+def test_one_bit_lloyd_max_closed_form():
+    c, t = O.lloyd_max_gaussian(1)
+    assert abs(c[1] - math.sqrt(2 / math.pi)) < 1e-15 and c[0] == -c[1]
+    assert t[0] == 0.0
+    c32, _ = O.codebook(1)
+    assert c32[1] == np.float32(math.sqrt(2 / math.pi))
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_lloyd_max_matches_max_1960(bits):
+    g = _golden("max1960_gaussian.json")["lloyd_max"][str(bits)]
+    c, t = O.lloyd_max_gaussian(bits)
+    L = 1 << bits
+    assert np.allclose(c[L // 2:], g["levels"], atol=6e-4, rtol=0)
+    assert np.allclose(t[L // 2:], g["endpoints"], atol=6e-4, rtol=0)
+    assert abs(O.gaussian_mse(c, t) / g["mse"] - 1) < 1e-3
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_lloyd_max_conditions_by_quadrature(bits):
+    """Centroid condition re-derived by numerical integration (not the oracle's
+    closed-form phi differences), symmetric, strictly increasing."""
+    c, t = O.lloyd_max_gaussian(bits)
+    L = 1 << bits
+    assert np.all(np.diff(c) > 0) and np.allclose(c, -c[::-1], atol=0)
+    assert np.allclose(t, 0.5 * (c[:-1] + c[1:]), atol=0)
+    edges = np.concatenate(([-np.inf], t, [np.inf]))
+    pdf = lambda z: math.exp(-0.5 * z * z) / math.sqrt(2 * math.pi)
+    for k in range(L // 2, L):   # symmetric: check the positive half
+        a, b = edges[k], edges[k + 1]
+        num = integrate.quad(lambda z: z * pdf(z), a, b, epsabs=0, epsrel=1e-13, limit=200)[0]
+        den = integrate.quad(pdf, a, b, epsabs=0, epsrel=1e-13, limit=200)[0]
+        assert abs(num / den - c[k]) < 1e-8 * max(1.0, abs(c[k]))
+
+
+def test_lloyd_max_high_rate_panter_dite():
+    # D(b) ~ (pi sqrt(3) / 2) 4^-b for a Gaussian at high rate (Panter & Dite 1951).
+    c, t = O.lloyd_max_gaussian(8)
+    assert abs(O.gaussian_mse(c, t) / (math.pi * math.sqrt(3) / 2 * 4.0 ** -8) - 1) < 0.02
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_uniform_grid_matches_max_1960(bits):
+    g = _golden("max1960_gaussian.json")["uniform"][str(bits)]
+    c, t = O.uniform_gaussian(bits)
+    assert abs(O.uniform_step(bits) - g["step"]) < 6e-4
+    assert abs(O.gaussian_mse(c, t) / g["mse"] - 1) < 2e-3
+    assert np.allclose(np.diff(c), O.uniform_step(bits), rtol=1e-12)
+
+
+@pytest.mark.parametrize("bits", [2, 5, 8])
+def test_uniform_step_is_stationary(bits):
+    delta = O.uniform_step(bits)
+    L = 1 << bits
+
+    def mse(dl):
+        c = (np.arange(L) - (L - 1) / 2) * dl
+        return O.gaussian_mse(c, 0.5 * (c[:-1] + c[1:]))
+    h = delta * 1e-4
+    assert mse(delta) < mse(delta - h) and mse(delta) < mse(delta + h)
+
+
+def test_mse_formula_by_quadrature():
+    c, t = O.lloyd_max_gaussian(3)
+    edges = np.concatenate(([-np.inf], t, [np.inf]))
+    pdf = lambda z: math.exp(-0.5 * z * z) / math.sqrt(2 * math.pi)
+    q = sum(integrate.quad(lambda z, ck=ck: (z - ck) ** 2 * pdf(z), a, b, epsrel=1e-12)[0]
+            for a, b, ck in zip(edges[:-1], edges[1:], c))
+    assert abs(q - O.gaussian_mse(c, t)) < 1e-10
+
+
+# ------------------------------------------------------------------- encode
+@pytest.mark.parametrize("bits", [1, 3, 8])
+def test_encode_rotated_basis_vector(bits):
+    s = _signs()
+    R = O.rotation_matrix(s)
+    L = 1 << bits
+    x = 3.5 * R[:, 9]                      # R x = 3.5 e_9, so u = sqrt(d) e_9
+    e = O.encode(x[None, :], s, bits)
+    assert e["codes"][0, 9] == L - 1
+    # the other coordinates are 0 up to rounding: they sit on either side of
+    # the boundary t = 0 (exact ties are pinned by test_encode_zero_vector)
+    others = np.delete(e["codes"][0], 9)
+    assert np.all(np.abs(np.delete(e["u"][0], 9)) < 1e-12)
+    assert np.all((others == L // 2) | (others == L // 2 - 1))
+    assert abs(float(e["norm"][0]) - 3.5) < 1e-6
+
+
+def test_encode_zero_vector():
+    e = O.encode(np.zeros((1, 128)), _signs(), 3)
+    assert e["norm"][0] == 0 and np.all(e["codes"] == 4)
+    assert np.all(O.dequantize(e["norm"], e["codes"], _signs(), 3) == 0)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_cosine_matches_distortion(bits):
+    """For Gaussian rows the rotated coordinates are ~N(0,1), so with Lloyd-Max
+    levels E cos(x, xhat) ~ sqrt(1 - D_b), D_b the Gaussian distortion (Max 1960)."""
+    g = _golden("max1960_gaussian.json")["lloyd_max"][str(bits)]
+    x = W.gaussian_rows(11, 3000)
+    s = _signs()
+    e = O.encode(x, s, bits)
+    xh = O.dequantize(e["norm"], e["codes"], s, bits)
+    cos = np.sum(x * xh, 1) / np.linalg.norm(x, axis=1) / np.linalg.norm(xh, axis=1)
+    assert abs(cos.mean() - math.sqrt(1 - g["mse"])) < 0.005
+
+
+def test_one_bit_cosine_figure():
+    fig = _golden("pages_figures.json")["one_bit_cosine"]["cosine"]
+    x = W.gaussian_rows(12, 3000)
+    s = _signs()
+    e = O.encode(x, s, 1)
+    xh = O.dequantize(e["norm"], e["codes"], s, 1)
+    cos = np.sum(x * xh, 1) / np.linalg.norm(x, axis=1) / np.linalg.norm(xh, axis=1)
+    assert abs(cos.mean() - fig) < 0.01
+
+
+def test_tier_quality_figures():
+    s = _signs()
+    x = W.gaussian_rows(13, 2000)
+    for row in _golden("pages_figures.json")["tier_quality"]["rows"]:
+        cs = []
+        for b in (row["k_bits"], row["v_bits"]):
+            e = O.encode(x, s, b)
+            xh = O.dequantize(e["norm"], e["codes"], s, b)
+            cs.append(np.mean(np.sum(x * xh, 1) / np.linalg.norm(x, axis=1) / np.linalg.norm(xh, axis=1)))
+        assert abs(np.mean(cs) - row["cosine"]) < 0.03
+
+
+def test_eight_bit_is_near_lossless():
+    x = W.gaussian_rows(14, 200) * 3
+    s = _signs()
+    e = O.encode(x, s, 8)
+    xh = O.dequantize(e["norm"], e["codes"], s, 8)
+    rel = np.linalg.norm(x - xh, axis=1) / np.linalg.norm(x, axis=1)
+    # sqrt(D_8) = 0.0064 on average; overload of a rare |u| > 4.6 lifts the worst row
+    assert rel.mean() < 0.0075 and rel.max() < 0.04
+
+
+def test_boundary_flags():
+    s = _signs()
+    R = O.rotation_matrix(s)
+    _, t32 = O.codebook(2)
+    u = np.zeros(128)
+    u[3] = float(t32[2]) + 1e-9           # within 1e-6 of a boundary
+    u[4] = float(t32[2]) + 1e-3           # clear of it
+    rest = math.sqrt((128 - u[3] ** 2 - u[4] ** 2) / 126)
+    u[[j for j in range(128) if j not in (3, 4)]] = rest
+    x = R @ u                              # ||x|| = sqrt(d), so sqrt(d) R x / ||x|| = u
+    e = O.encode(x[None, :], s, 2)
+    assert abs(e["u"][0, 3] - u[3]) < 1e-12
+    assert e["near"][0, 3] and not e["near"][0, 4]
+    assert e["codes"][0, 4] == 3
+
+
+# ------------------------------------------------------------------ packing
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_pack_round_trip_and_bijection(bits):
+    rng = np.random.default_rng(bits)
+    codes = rng.integers(0, 1 << bits, size=(64, 128))
+    blk = O.pack_block(codes, bits)
+    assert len(blk) == 1024 * bits
+    assert np.array_equal(O.unpack_block(blk, bits), codes)
+    base = np.frombuffer(blk, dtype=np.uint8)
+    seen = set()
+    for _ in range(60):
+        s, n, k = rng.integers(64), rng.integers(128), rng.integers(bits)
+        c2 = codes.copy()
+        c2[s, n] ^= 1 << k
+        diff = np.unpackbits(np.frombuffer(O.pack_block(c2, bits), dtype=np.uint8) ^ base)
+        pos = np.nonzero(diff)[0]
+        assert pos.size == 1
+        seen.add((int(pos[0]), (int(s), int(n), int(k))))
+    # distinct code bits land on distinct storage bits
+    assert len({p for p, _ in seen}) == len({key for _, key in seen})
+    full = np.full((64, 128), (1 << bits) - 1)
+    assert O.pack_block(full, bits) == b"\xff" * (1024 * bits)
+
+
+def test_v_stream_order_is_a_permutation():
+    codes = np.arange(64 * 128).reshape(64, 128)
+    st = O.v_stream_codes(codes)
+    assert sorted(st.ravel().tolist()) == list(range(64 * 128))
+    assert np.array_equal(O.v_codes_from_streams(st), codes)
+    # stream 16q+i, position 8k+e holds token 4k+q, coordinate 8i+e
+    q, i, k, e = 2, 5, 7, 3
+    assert st[16 * q + i, 8 * k + e] == codes[4 * k + q, 8 * i + e]
+
+
+def test_sign_words_round_trip():
+    z = np.random.default_rng(3).random((64, 128)) < 0.5
+    raw = O.pack_signs(z)
+    assert len(raw) == 1024 and np.array_equal(O.unpack_signs(raw), z)
+
+
+def test_footprint_matches_pages_table():
+    fig = _golden("pages_figures.json")["footprint_fp16_vs_3bit"]
+    vpt = fig["values_per_token"]
+    vectors_per_token = vpt // 128
+    for row in fig["rows"]:
+        pages = row["tokens"] // 64
+        codes = pages * vectors_per_token * len(O.pack_block(np.zeros((64, 128), int), 3)) // 64 * 64
+        # one 3-bit code block holds 64 vectors: bytes per vector = 48
+        code_bytes = row["tokens"] * vectors_per_token * (1024 * 3 // 64)
+        fp16_bytes = row["tokens"] * vpt * 2
+        assert code_bytes == row["tq3_mb"] * 2 ** 20
+        assert fp16_bytes == row["fp16_mb"] * 2 ** 20
+        assert round(fp16_bytes / code_bytes, 1) == row["ratio"]
+
+
+def test_page_ratio_matches_pages_table():
+    fp16 = O.page_bytes((0, 0, False))
+    for row in _golden("pages_figures.json")["compression_by_bits"]["rows"]:
+        b = row["bits"]
+        assert round(fp16 / O.page_bytes((b, b, False)), 1) == row["ratio"]
+
+
+# ---------------------------------------------------------------------- QJL
+def test_qjl_estimator_unbiased_with_closed_form_variance():
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal(128)
+    r = rng.standard_normal(128) * 0.3
+    m, trials = 128, 3000
+    est = np.empty(trials)
+    for k in range(trials):
+        S = rng.standard_normal((m, 128))
+        z = (S @ r) >= 0
+        rhat = O.qjl_reconstruct(z[None, :], np.float32([np.linalg.norm(r)]), S)[0]
+        est[k] = q @ rhat
+    truth = q @ r
+    g32 = float(np.float32(np.linalg.norm(r)))
+    var = ((math.pi / 2) * (q @ q) * g32 ** 2 - truth ** 2 * (g32 / np.linalg.norm(r)) ** 2) / m
+    assert abs(est.mean() - truth * g32 / np.linalg.norm(r)) < 4 * math.sqrt(var / trials)
+    assert abs(est.var() / var - 1) < 0.15
+
+
+def test_qjl_encode_scale_and_signs():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((8, 128))
+    xh = x * 0.9
+    S = rng.standard_normal((128, 128))
+    qj = O.qjl_encode(x, xh, S)
+    assert np.allclose(qj["gamma"], np.linalg.norm(0.1 * x, axis=1), rtol=1e-6)
+    assert np.array_equal(qj["z"], (0.1 * x) @ S.T >= 0)
+
+
+# ---------------------------------------------------------------- attention
+def test_attention_special_cases():
+    rng = np.random.default_rng(6)
+    K = rng.standard_normal((9, 128))
+    V = rng.standard_normal((9, 128))
+    assert np.allclose(O.attention(rng.standard_normal(128), K[:1], V[:1]), V[0])
+    assert np.allclose(O.attention(np.zeros(128), K, V), V.mean(axis=0))
+    # two tokens, closed form
+    q = rng.standard_normal(128)
+    s1, s2 = K[0] @ q / math.sqrt(128), K[1] @ q / math.sqrt(128)
+    w1 = 1 / (1 + math.exp(s2 - s1))
+    assert np.allclose(O.attention(q, K[:2], V[:2]), w1 * V[0] + (1 - w1) * V[1])
+
+
+def test_attention_brute_force_loops():
+    rng = np.random.default_rng(7)
+    for n, d in ((1, 4), (5, 8), (8, 16)):
+        q = rng.standard_normal(d)
+        K = rng.standard_normal((n, d))
+        V = rng.standard_normal((n, d))
+        scores = []
+        for t in range(n):
+            acc = 0.0
+            for j in range(d):
+                acc += K[t][j] * q[j]
+            scores.append(acc / math.sqrt(d))
+        w = [math.exp(s) for s in scores]
+        tot = sum(w)
+        ref = [sum(w[t] * V[t][j] for t in range(n)) / tot for j in range(d)]
+        assert np.allclose(O.attention(q, K, V), ref, rtol=1e-12)
+
+
+def test_reconstruct_unit_fp16_sink_and_lossless_limit():
+    rng = np.random.default_rng(8)
+    T = 64 * 3 + 20
+    K = rng.standard_normal((T, 128)).astype(np.float16)
+    V = rng.standard_normal((T, 128)).astype(np.float16)
+    fmts = [W.FP16, (8, 8, False), (8, 8, False), W.FP16]
+    Kh, Vh = O.reconstruct_unit(K, V, fmts, _signs())
+    assert np.array_equal(Kh[:64], K[:64].astype(np.float64))
+    assert np.array_equal(Vh[192:], V[192:].astype(np.float64))
+    rel = np.linalg.norm(Kh[64:192] - K[64:192], axis=1) / np.linalg.norm(K[64:192].astype(float), axis=1)
+    assert rel.max() < 0.02
+    q = rng.standard_normal((4, 128))
+    out = O.decode_attention_unit(q, Kh, Vh)
+    exact = np.stack([O.attention(qq, K.astype(float), V.astype(float)) for qq in q])
+    assert np.max(np.abs(out - exact)) / np.max(np.abs(exact)) < 0.05
+
+
+def test_page_bytes_round_trip_through_decode_page():
+    rng = np.random.default_rng(9)
+    K = rng.standard_normal((64, 128))
+    V = rng.standard_normal((64, 128))
+    S = W.qjl_matrix(42, 0)
+    s = _signs()
+    fmt = (2, 3, True)
+    enc = O.encode_page(K, V, fmt, s, S)
+    assert len(enc["bytes"]) == O.page_bytes(fmt)
+    Kd, Vd = O.decode_page(enc["bytes"], fmt, s, S)
+    Kh, Vh = O.reconstruct_unit(K, V, [fmt], s, S)
+    assert np.allclose(Kd, Kh, atol=1e-12) and np.allclose(Vd, Vh, atol=1e-12)
