@@ -1,0 +1,287 @@
+"""Benchmark of the SRHT KV-cache hot path on one MI355X.
+
+One step = encode every layer's keys and values into packed pages, then one
+decode-attention query per session over every layer's cache (all rows of the
+hot path), on the Qwen3-8B-shaped workload: 36 layers x 8 KV heads x
+head_dim 128, 32K context, batch 4, fp16 inputs, base K3/V2 with per-head
+widths 1-8.  Inputs are synthetic, seeded, and resident in HBM before timing.
+
+Prints one JSON line.  ``value`` is decode-attention effective bandwidth
+(algorithmic bytes per decode step / decode time); the encode rate is in
+``encode_mtokens_per_s``.  The ``roofline`` object describes the kernel that
+dominates the step, timed with HIP events on the stream it runs on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn effective HBM GB/s (% of peak) + encode Mtokens/s at 32K ctx"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=3, help="workload index 1..5 (default 3)")
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
+    return ap.parse_args()
+
+
+def decode_bytes(w, formats, n_q_heads):
+    """Algorithmic bytes one decode step reads/writes for one layer: packed
+    pages (codes + norms [+ QJL]), fp16 pages, q and out."""
+    import kv_cache_vector_srht_amd as tq
+    total = 0
+    for row in formats:
+        for fm in row:
+            for p, f in enumerate(fm):
+                ntok = min(64, w.n_tokens - 64 * p)
+                if ntok <= 0:
+                    break
+                if f[0] == 0:
+                    total += ntok * 512
+                else:
+                    total += tq.page_bytes(f)
+    qbytes = 2 if w.dtype == "float16" else 4
+    total += w.batch * n_q_heads * 128 * (qbytes + 4)
+    return total
+
+
+def encode_bytes(w, formats):
+    """Algorithmic bytes of one layer's encode call: K and V inputs plus the
+    pages written."""
+    import kv_cache_vector_srht_amd as tq
+    ebytes = 2 if w.dtype == "float16" else 4
+    inp = 2 * w.batch * w.n_kv_heads * w.n_tokens * 128 * ebytes
+    out = 0
+    for row in formats:
+        for fm in row:
+            for p, f in enumerate(fm):
+                ntok = min(64, w.n_tokens - 64 * p)
+                if ntok <= 0:
+                    break
+                out += ntok * 512 if f[0] == 0 else tq.page_bytes(f)
+    return inp + out
+
+
+def traffic_record(kernel: str):
+    """Measured HBM traffic of `kernel` from profiles/, if taken on the current source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src = os.path.join(ROOT, "kv_cache_vector_srht_amd", "csrc", "tq_kernels.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, layers_data, seconds: float):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    whole (layer, session, KV head) units, encode then decode attention."""
+    import numpy as np
+    from oracle import tq_oracle as O
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    G = w.n_q_heads // w.n_kv_heads
+    enc_t = dec_t = 0.0
+    tokens = dec_bytes = 0
+    units = 0
+    t_start = time.perf_counter()
+    l = b = h = 0
+    while time.perf_counter() - t_start < seconds and units < 64:
+        k, v, q, signs, S = layers_data(l, b, h)
+        fm = w.formats[l][b][h]
+        t0 = time.perf_counter()
+        groups = {}
+        for p, f in enumerate(fm):
+            if f[0]:
+                groups.setdefault(tuple(f), []).append(p)
+        encs = {}
+        for f, plist in groups.items():
+            rows = np.concatenate([np.arange(64 * p, 64 * p + 64) for p in plist])
+            ek = O.encode(k[rows], signs, f[0], w.k_codebook)
+            ev = O.encode(v[rows], signs, f[1], w.v_codebook)
+            qj = None
+            if f[2]:
+                kh0 = O.dequantize(ek["norm"], ek["codes"], signs, f[0], w.k_codebook)
+                qj = O.qjl_encode(k[rows], kh0, S)
+            encs[f] = (rows, ek, ev, qj)
+        t1 = time.perf_counter()
+        Kh = np.zeros_like(k)
+        Vh = np.zeros_like(v)
+        for p, f in enumerate(fm):
+            if f[0] == 0:
+                Kh[64 * p:64 * p + 64] = k[64 * p:64 * p + 64].astype(np.float16)
+                Vh[64 * p:64 * p + 64] = v[64 * p:64 * p + 64].astype(np.float16)
+        for f, (rows, ek, ev, qj) in encs.items():
+            kh = O.dequantize(ek["norm"], ek["codes"], signs, f[0], w.k_codebook)
+            if qj is not None:
+                kh = kh + O.qjl_reconstruct(qj["z"], qj["gamma"], S)
+            Kh[rows] = kh
+            Vh[rows] = O.dequantize(ev["norm"], ev["codes"], signs, f[1], w.v_codebook)
+        O.decode_attention_unit(q[h * G:(h + 1) * G], Kh, Vh)
+        t2 = time.perf_counter()
+        enc_t += t1 - t0
+        dec_t += t2 - t1
+        tokens += w.n_tokens
+        one = type(w)(**{**w.__dict__})
+        one.batch, one.n_kv_heads, one.n_q_heads = 1, 1, G
+        dec_bytes += decode_bytes(one, [[fm]], G)
+        units += 1
+        h += 1
+        if h == w.n_kv_heads:
+            h, b = 0, b + 1
+            if b == w.batch:
+                b, l = 0, (l + 1) % w.n_layers
+    unit_count = w.n_layers * w.batch * w.n_kv_heads
+    return {
+        "value": dec_bytes / dec_t / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+        "sample": (f"{units} of {unit_count} (layer, session, KV head) units, "
+                   f"{w.n_tokens} tokens each: encode then decode attention for the "
+                   f"{G} query heads; numpy float64"),
+        # one whole-stack session-token = one vector per (layer, KV head)
+        "encode_mtokens_per_s": tokens / (w.n_layers * w.n_kv_heads) / enc_t / 1e6,
+        "seconds": enc_t + dec_t,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no "
+              "multi-GPU path; see the sharding notes in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import kv_cache_vector_srht_amd as tq
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    w = W.make_workload(args.workload)
+    if args.layers:
+        w.n_layers = args.layers
+        w.formats = w.formats[:args.layers]
+    G = w.n_q_heads // w.n_kv_heads
+    print(f"# bench: workload {w.index} ({w.name}), {w.n_layers} layers, B={w.batch}, "
+          f"T={w.n_tokens}", file=sys.stderr, flush=True)
+
+    layers, caches, inputs, queries, outs, wss = [], [], [], [], [], []
+    enc_bytes = dec_bytes = 0
+    for l in range(w.n_layers):
+        fm = w.formats[l]
+        has_qjl = any(f[2] for row in fm for r in row for f in r)
+        signs = W.rotation_signs(W.ROTATION_SEED, l)
+        S = W.qjl_matrix(W.ROTATION_SEED, l) if has_qjl else None
+        layers.append(tq.Layer(signs, dev, S, w.k_codebook, w.v_codebook))
+        caches.append(tq.Cache(fm, [w.n_tokens] * w.batch, dev))
+        inputs.append(W.make_kv(w, l, device=dev))
+        queries.append(W.make_query(w, l, device=dev))
+        outs.append(torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev))
+        wss.append(torch.empty(tq.workspace_bytes(caches[-1], w.n_q_heads), dtype=torch.uint8,
+                               device=dev))
+        enc_bytes += encode_bytes(w, fm)
+        dec_bytes += decode_bytes(w, fm, w.n_q_heads)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev_enc=None, ev_dec=None):
+        if ev_enc:
+            ev_enc[0].record(stream)
+        for l in range(w.n_layers):
+            k, v = inputs[l]
+            tq.encode_kv(layers[l], caches[l], k, v, tok0=0)
+        if ev_enc:
+            ev_enc[1].record(stream)
+        for l in range(w.n_layers):
+            tq.decode_attention(layers[l], caches[l], queries[l], out=outs[l], workspace=wss[l])
+        if ev_dec:
+            ev_dec[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        step((e[0], e[1]), (None, e[2]))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    enc_ms = np.array([a.elapsed_time(b) for a, b, _ in evs])
+    dec_ms = np.array([b.elapsed_time(c) for _, b, c in evs])
+    enc_s = float(np.mean(enc_ms)) / 1e3
+    dec_s = float(np.mean(dec_ms)) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+    dec_gbs = dec_bytes / dec_s / 1e9
+    enc_gbs = enc_bytes / enc_s / 1e9
+    enc_mtok = w.batch * w.n_tokens / enc_s / 1e6
+
+    # the kernel that dominates the step
+    if enc_s >= dec_s:
+        name, per_launch_bytes, per_launch_s, launches = ("encode_kv", enc_bytes / w.n_layers,
+                                                          enc_s / w.n_layers, w.n_layers)
+    else:
+        name, per_launch_bytes, per_launch_s, launches = ("decode_attention", dec_bytes / w.n_layers,
+                                                          dec_s / w.n_layers, w.n_layers)
+    achieved = per_launch_bytes / per_launch_s / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_record(name),
+            "kernel": name, "bytes_per_launch": int(per_launch_bytes),
+            "launch_us": round(per_launch_s * 1e6, 2)}
+    line = {
+        "metric": METRIC, "value": round(dec_gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.n_layers, "batch": w.batch,
+                   "kv_heads": w.n_kv_heads, "q_heads": w.n_q_heads, "head_dim": 128,
+                   "context": w.n_tokens, "input_dtype": w.dtype},
+        "decode_frac_of_peak": round(dec_gbs / HBM_PEAK_GBS, 4),
+        "decode_ms_per_step": round(dec_s * 1e3, 3),
+        "encode_mtokens_per_s": round(enc_mtok, 3),
+        "encode_gbs": round(enc_gbs, 1),
+        "encode_ms_per_step": round(enc_s * 1e3, 3),
+        "decode_bytes_per_step": int(dec_bytes), "encode_bytes_per_step": int(enc_bytes),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        kv_host = {}
+
+        def layer_unit(l, b, h):
+            if l not in kv_host:
+                k, v = inputs[l]
+                kv_host[l] = (k.cpu().numpy(), v.cpu().numpy(), queries[l].cpu().numpy())
+            k, v, q = kv_host[l]
+            signs = W.rotation_signs(W.ROTATION_SEED, l)
+            S = W.qjl_matrix(W.ROTATION_SEED, l) if any(f[2] for f in w.formats[l][b][h]) else None
+            return (k[b, h].astype(np.float64), v[b, h].astype(np.float64),
+                    q[b].astype(np.float64), signs, S)
+        cb = cpu_baseline(w, layer_unit, args.cpu_seconds)
+        line["cpu_baseline"] = {k2: (round(v2, 4) if isinstance(v2, float) else v2)
+                                for k2, v2 in cb.items()}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,299 @@
+"""Python binding of libtq (SRHT KV-cache compression + compressed decode attention).
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every step of encode, decode attention and dequantisation runs in
+the library's HIP kernels.  Importing this module does not touch the GPU; the
+first call loads ``lib/libtq.so`` and raises ``TQError`` if it is missing or a
+call fails.  There is no fallback path.
+
+Names follow ``include/tq.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import List, Optional, Sequence, Tuple
+
+HEAD_DIM = 128
+PAGE_TOKENS = 64
+JL_DIM = 128
+CODEBOOK_TABLE_FLOATS = 1024
+LLOYD_MAX = 0
+UNIFORM = 1
+DTYPE_F32 = 0
+DTYPE_F16 = 1
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libtq.so")
+EXPORTS = ("tq_page_bytes", "tq_page_descriptor", "tq_build_codebook", "tq_codebook_table",
+           "tq_layer_params", "tq_sign_mask", "tq_decode_workspace_bytes", "tq_cache_bytes",
+           "tq_status_string", "tq_last_error", "tq_encode_kv", "tq_decode_attention",
+           "tq_dequantize")
+
+
+class TQError(RuntimeError):
+    pass
+
+
+# ------------------------------------------------------------------ structs
+class tq_layer(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_int32), ("k_codebook", ctypes.c_int32),
+                ("v_codebook", ctypes.c_int32), ("jl_dim", ctypes.c_int32),
+                ("sign_mask", ctypes.c_void_p), ("k_table", ctypes.c_void_p),
+                ("v_table", ctypes.c_void_p), ("qjl_s", ctypes.c_void_p)]
+
+
+class tq_cache(ctypes.Structure):
+    _fields_ = [("n_sessions", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("n_tokens", ctypes.c_void_p), ("pages", ctypes.c_void_p),
+                ("pool", ctypes.c_void_p), ("pool_bytes", ctypes.c_uint64)]
+
+
+class tq_kv_input(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("tok0", ctypes.c_int32), ("ntok", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64),
+                ("stride_t", ctypes.c_int64), ("error_flags", ctypes.c_void_p)]
+
+
+class tq_query(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64),
+                ("softmax_scale", ctypes.c_float), ("reserved", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libtq (raises TQError when it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise TQError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "or python kv_cache_vector_srht_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        L.tq_page_bytes.restype = ctypes.c_size_t
+        L.tq_page_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        L.tq_page_descriptor.restype = ctypes.c_uint64
+        L.tq_page_descriptor.argtypes = [ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        L.tq_build_codebook.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        L.tq_codebook_table.argtypes = [ctypes.c_int, ctypes.c_void_p]
+        L.tq_layer_params.argtypes = [ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_void_p, ctypes.c_void_p]
+        L.tq_sign_mask.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+        L.tq_decode_workspace_bytes.restype = ctypes.c_size_t
+        L.tq_decode_workspace_bytes.argtypes = [ctypes.POINTER(tq_cache), ctypes.c_int]
+        L.tq_cache_bytes.restype = ctypes.c_size_t
+        L.tq_cache_bytes.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+        L.tq_status_string.restype = ctypes.c_char_p
+        L.tq_status_string.argtypes = [ctypes.c_int]
+        L.tq_last_error.restype = ctypes.c_char_p
+        L.tq_encode_kv.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
+                                   ctypes.POINTER(tq_kv_input), ctypes.c_void_p]
+        L.tq_decode_attention.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
+                                          ctypes.POINTER(tq_query), ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.tq_dequantize.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache), ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.c_void_p]
+        _lib = L
+    return _lib
+
+
+def check(status: int, what: str) -> None:
+    if status != 0:
+        L = lib()
+        raise TQError(f"{what}: {L.tq_status_string(status).decode()} ({status}): "
+                      f"{L.tq_last_error().decode()}")
+
+
+# ------------------------------------------------------------- host helpers
+def build_codebook(bits: int, kind: int = LLOYD_MAX):
+    """(centroids, boundaries) float32 numpy arrays from tq_build_codebook."""
+    import numpy as np
+    L = 1 << bits
+    c = np.zeros(L, np.float32)
+    t = np.zeros(max(L - 1, 1), np.float32)
+    check(lib().tq_build_codebook(bits, kind, c.ctypes.data, t.ctypes.data), "tq_build_codebook")
+    return c, t[:L - 1]
+
+
+def codebook_table(kind: int = LLOYD_MAX):
+    import numpy as np
+    tab = np.zeros(CODEBOOK_TABLE_FLOATS, np.float32)
+    check(lib().tq_codebook_table(kind, tab.ctypes.data), "tq_codebook_table")
+    return tab
+
+
+def layer_params(seed: int, layer: int, with_qjl: bool = True):
+    """(signs int8[128], S float32[128,128] or None) from tq_layer_params."""
+    import numpy as np
+    s = np.zeros(HEAD_DIM, np.int8)
+    S = np.zeros((JL_DIM, HEAD_DIM), np.float32) if with_qjl else None
+    check(lib().tq_layer_params(ctypes.c_uint64(seed), layer, HEAD_DIM, JL_DIM, s.ctypes.data,
+                                S.ctypes.data if S is not None else None), "tq_layer_params")
+    return s, S
+
+
+def sign_mask(signs):
+    import numpy as np
+    s = np.ascontiguousarray(np.asarray(signs, dtype=np.int8))
+    m = np.zeros(4, np.uint32)
+    check(lib().tq_sign_mask(s.ctypes.data, s.size, m.ctypes.data), "tq_sign_mask")
+    return m
+
+
+def page_bytes(fmt) -> int:
+    kb, vb, qjl = fmt
+    n = lib().tq_page_bytes(int(kb), int(vb), int(bool(qjl)))
+    if n == 0:
+        raise TQError(f"invalid page format {fmt}")
+    return int(n)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float16:
+        return DTYPE_F16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise TQError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(device) -> ctypes.c_void_p:
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+# ------------------------------------------------------------------- layer
+class Layer:
+    """Device-side constants of one layer: D, codebook tables, optional S."""
+
+    def __init__(self, signs, device, qjl_s=None, k_codebook: int = LLOYD_MAX,
+                 v_codebook: int = LLOYD_MAX):
+        import numpy as np
+        import torch
+        self.device = torch.device(device)
+        self.signs = np.asarray(signs, dtype=np.int8)
+        self.mask = torch.from_numpy(sign_mask(self.signs).view(np.int32).copy()).to(self.device)
+        self.k_table = torch.from_numpy(codebook_table(k_codebook)).to(self.device)
+        self.v_table = torch.from_numpy(codebook_table(v_codebook)).to(self.device)
+        self.qjl_s = None
+        if qjl_s is not None:
+            self.qjl_s = torch.from_numpy(np.ascontiguousarray(qjl_s, dtype=np.float32)).to(self.device)
+        self.k_codebook, self.v_codebook = k_codebook, v_codebook
+        self.struct = tq_layer(HEAD_DIM, k_codebook, v_codebook, JL_DIM, self.mask.data_ptr(),
+                               self.k_table.data_ptr(), self.v_table.data_ptr(),
+                               self.qjl_s.data_ptr() if self.qjl_s is not None else None)
+
+
+# ------------------------------------------------------------------- cache
+class Cache:
+    """Page pool + page table + token counts for B sessions x H_kv heads.
+
+    ``formats[b][h][p]`` is (0, 0, False) for an fp16 page or
+    (k_bits, v_bits, qjl) for a packed page.  Pages are laid out in the pool
+    in (session, head, page) order.
+    """
+
+    def __init__(self, formats, n_tokens: Sequence[int], device):
+        import numpy as np
+        import torch
+        self.device = torch.device(device)
+        B = len(formats)
+        H = len(formats[0])
+        P = max(len(formats[b][h]) for b in range(B) for h in range(H))
+        L = lib()
+        desc = np.zeros((B, H, P), dtype=np.uint64)
+        self.offsets = np.zeros((B, H, P), dtype=np.int64)
+        off = 0
+        for b in range(B):
+            for h in range(H):
+                for p, fmt in enumerate(formats[b][h]):
+                    kb, vb, q = fmt
+                    n = page_bytes(fmt)
+                    d = L.tq_page_descriptor(off, int(kb), int(vb), int(bool(q)))
+                    if d == 0:
+                        raise TQError(f"cannot describe page {fmt} at {off}")
+                    desc[b, h, p] = d
+                    self.offsets[b, h, p] = off
+                    off += (n + 255) // 256 * 256
+        self.formats = formats
+        self.n_sessions, self.n_kv_heads, self.max_pages = B, H, P
+        self.pool_bytes = max(off, 256)
+        self.pool = torch.zeros(self.pool_bytes, dtype=torch.uint8, device=self.device)
+        self.host_pages = desc
+        self.pages = torch.from_numpy(desc.view(np.int64)).to(self.device)
+        self.n_tokens = torch.tensor(list(n_tokens), dtype=torch.int32, device=self.device)
+        self.struct = tq_cache(B, H, P, 0, self.n_tokens.data_ptr(), self.pages.data_ptr(),
+                               self.pool.data_ptr(), self.pool_bytes)
+
+    def set_n_tokens(self, n_tokens: Sequence[int]) -> None:
+        self.n_tokens.copy_(self.n_tokens.new_tensor(list(n_tokens)))
+
+    def footprint(self) -> int:
+        """Bytes of the pages (tq_cache_bytes over the host page table)."""
+        import numpy as np
+        flat = np.ascontiguousarray(self.host_pages.reshape(-1))
+        return int(lib().tq_cache_bytes(flat.ctypes.data, flat.size))
+
+    def page_view(self, b: int, h: int, p: int):
+        """The bytes of one page (a uint8 tensor view of the pool)."""
+        off = int(self.offsets[b, h, p])
+        return self.pool[off:off + page_bytes(self.formats[b][h][p])]
+
+
+# ------------------------------------------------------------- device calls
+def encode_kv(layer: Layer, cache: Cache, k, v, tok0: int = 0, error_flags=None) -> None:
+    """tq_encode_kv over k, v of shape [B, H_kv, ntok, 128] (fp16 or fp32)."""
+    if k.shape != v.shape or k.dim() != 4 or k.shape[-1] != HEAD_DIM or k.dtype != v.dtype:
+        raise TQError(f"k and v must both be [B, H_kv, T, 128] of one dtype, got {tuple(k.shape)}, {tuple(v.shape)}")
+    if k.stride() != v.stride() or k.stride(-1) != 1:
+        raise TQError("k and v must share strides with a unit innermost stride")
+    if k.shape[0] != cache.n_sessions or k.shape[1] != cache.n_kv_heads:
+        raise TQError("k/v session or head count does not match the cache")
+    inp = tq_kv_input(k.data_ptr(), v.data_ptr(), _dtype_code(k), tok0, k.shape[2], 0,
+                      k.stride(0), k.stride(1), k.stride(2),
+                      error_flags.data_ptr() if error_flags is not None else None)
+    check(lib().tq_encode_kv(ctypes.byref(layer.struct), ctypes.byref(cache.struct),
+                             ctypes.byref(inp), _stream(k.device)), "tq_encode_kv")
+
+
+def workspace_bytes(cache: Cache, n_q_heads: int) -> int:
+    return int(lib().tq_decode_workspace_bytes(ctypes.byref(cache.struct), n_q_heads))
+
+
+def decode_attention(layer: Layer, cache: Cache, q, out=None, workspace=None,
+                     softmax_scale: float = 0.0):
+    """tq_decode_attention for q [B, H_q, 128]; returns out [B, H_q, 128] float32."""
+    import torch
+    if q.dim() != 3 or q.shape[0] != cache.n_sessions or q.shape[-1] != HEAD_DIM or q.stride(-1) != 1:
+        raise TQError(f"q must be [B, H_q, 128] with unit innermost stride, got {tuple(q.shape)}")
+    Hq = q.shape[1]
+    if out is None:
+        out = torch.empty((q.shape[0], Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    need = workspace_bytes(cache, Hq)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    qs = tq_query(q.data_ptr(), _dtype_code(q), Hq, q.stride(0), q.stride(1), softmax_scale, 0)
+    check(lib().tq_decode_attention(ctypes.byref(layer.struct), ctypes.byref(cache.struct),
+                                    ctypes.byref(qs), out.data_ptr(), workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(),
+                                    _stream(q.device)), "tq_decode_attention")
+    return out
+
+
+def dequantize(layer: Layer, cache: Cache, which: int, tok0: int, ntok: int, add_qjl: bool = True,
+               out=None):
+    """tq_dequantize: [B, H_kv, ntok, 128] float32 reconstruction (keys 0, values 1)."""
+    import torch
+    if out is None:
+        out = torch.empty((cache.n_sessions, cache.n_kv_heads, ntok, HEAD_DIM), dtype=torch.float32,
+                          device=cache.device)
+    check(lib().tq_dequantize(ctypes.byref(layer.struct), ctypes.byref(cache.struct), which,
+                              int(add_qjl), tok0, ntok, out.data_ptr(), _stream(cache.device)),
+          "tq_dequantize")
+    return out

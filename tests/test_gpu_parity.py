@@ -1,0 +1,170 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Sizes here span several pages, heads and sessions with
+ragged tails; tests/test_gpu_fullsize.py covers the full workload sizes on
+sampled units."""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import tq_oracle as O
+from tests.gpu_parity import Tally, compare_attention, compare_dequant, compare_unit_pages
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import kv_cache_vector_srht_amd as tq
+    tq.lib()
+    return torch.device("cuda:0")
+
+
+def _np(x):
+    return x.detach().cpu().numpy()
+
+
+def run_case(w, layers, dev, units=None, n_tokens=None, dequant=True, chunks=None, tally=None,
+             query_dtype=None):
+    """Encode + decode every listed layer of workload w on the GPU; compare the
+    listed units (all by default) with the oracle."""
+    import kv_cache_vector_srht_amd as tq
+    t = tally or Tally()
+    G = w.n_q_heads // w.n_kv_heads
+    for l in layers:
+        fm = w.formats[l]
+        has_qjl = any(f[2] for row in fm for r in row for f in r)
+        signs = W.rotation_signs(W.ROTATION_SEED, l)
+        S = W.qjl_matrix(W.ROTATION_SEED, l) if has_qjl else None
+        layer = tq.Layer(signs, dev, S, w.k_codebook, w.v_codebook)
+        ntoks = n_tokens or [w.n_tokens] * w.batch
+        cache = tq.Cache(fm, ntoks, dev)
+        k, v = W.make_kv(w, l, device=dev)
+        q = W.make_query(w, l, device=dev)
+        if query_dtype is not None:
+            q = q.to(query_dtype)
+        flags = torch.zeros(1, dtype=torch.int32, device=dev)
+        if chunks:
+            for t0, t1 in chunks:
+                tq.encode_kv(layer, cache, k[:, :, t0:t1], v[:, :, t0:t1], tok0=t0, error_flags=flags)
+        else:
+            tq.encode_kv(layer, cache, k, v, tok0=0, error_flags=flags)
+        out = _np(tq.decode_attention(layer, cache, q))
+        dk = _np(tq.dequantize(layer, cache, 0, 0, w.n_tokens)) if dequant else None
+        dv = _np(tq.dequantize(layer, cache, 1, 0, w.n_tokens)) if dequant else None
+        torch.cuda.synchronize()
+        assert int(flags.item()) == 0, f"encode error flags {int(flags.item())}"
+        kh, vh, qh = _np(k).astype(np.float64), _np(v).astype(np.float64), _np(q).astype(np.float64)
+        pool = _np(cache.pool)
+        for (b, h) in (units or [(b, h) for b in range(w.batch) for h in range(w.n_kv_heads)]):
+            T = ntoks[b]
+            k_ok, v_ok = compare_unit_pages(cache, b, h, kh[b, h], vh[b, h], fm[b][h], signs, S, t,
+                                            w.k_codebook, w.v_codebook, n_tokens=w.n_tokens,
+                                            pool_host=pool)
+            Kh, Vh = O.reconstruct_unit(kh[b, h, :T], vh[b, h, :T], fm[b][h], signs, S,
+                                        w.k_codebook, w.v_codebook)
+            rows = out[b, h * G:(h + 1) * G]
+            if T == 0:
+                assert np.all(rows == 0)
+            else:
+                compare_attention(rows, qh[b, h * G:(h + 1) * G], Kh, Vh, t)
+            if dequant and T > 0:
+                Kf, Vf = O.reconstruct_unit(kh[b, h], vh[b, h], fm[b][h], signs, S,
+                                            w.k_codebook, w.v_codebook)
+                compare_dequant(dk[b, h][k_ok], Kf[k_ok], t)
+                compare_dequant(dv[b, h][v_ok], Vf[v_ok], t)
+    t.check()
+    return t
+
+
+def test_workload1_single_head_fp32(dev):
+    run_case(W.make_workload(1), [0], dev)
+
+
+def test_workload2_llama_layer_chunked(dev):
+    w = W.make_workload(2)
+    chunks = [(0, 128)] + [(t0, t0 + 64) for t0 in range(128, 4096, 64)]
+    run_case(w, [0], dev, chunks=chunks)
+
+
+def test_workload3_per_head_bits_ragged(dev):
+    w = W.make_workload(3, {"n_tokens": 64 * 9 + 17, "batch": 2})
+    # layers whose heads cover hub (6-8), peripheral (1-2) and base (3/2) widths
+    run_case(w, [0, 1, 2], dev)
+
+
+def test_workload4_qjl_sink_ragged(dev):
+    w = W.make_workload(4, {"n_tokens": 64 * 6 + 5, "batch": 2})
+    run_case(w, [0], dev)
+
+
+def test_workload5_tiers_demotion(dev):
+    w = W.make_workload(5, {"n_tokens": 64 * 1100 + 33, "batch": 1})
+    fm = w.formats[0][0][0]
+    assert {f for f in fm if f[0]} >= {(2, 1, False)} and fm[-1] == W.FP16
+    run_case(w, [0], dev, units=[(0, h) for h in range(8)], dequant=False)
+
+
+def _all_bits_workload(G=4, dtype="float16", kind=O.LLOYD_MAX, pages=66, qjl=False):
+    w = W.make_workload(2, {"n_tokens": 64 * pages, "batch": 1, "n_kv_heads": 2,
+                            "n_q_heads": 2 * G, "sink_tokens": 0, "dtype": dtype})
+    combos = [(kb, vb) for kb in range(1, 9) for vb in range(1, 9)]
+    w.k_codebook = w.v_codebook = kind
+    w.formats = [[[[W.packed(*combos[(p + 7 * h) % 64], qjl) if p > 0 else W.FP16
+                    for p in range(pages)] for h in range(2)]]]
+    return w
+
+
+def test_every_bit_width_pair(dev):
+    run_case(_all_bits_workload(), [0], dev)
+
+
+def test_every_bit_width_with_qjl_uniform_codebook(dev):
+    run_case(_all_bits_workload(kind=O.UNIFORM, qjl=True), [0], dev)
+
+
+@pytest.mark.parametrize("G", [1, 2, 8])
+def test_gqa_groups(dev, G):
+    run_case(_all_bits_workload(G=G, pages=12), [0], dev, dequant=False)
+
+
+def test_fp32_inputs_and_fp32_query(dev):
+    run_case(_all_bits_workload(dtype="float32", pages=10), [0], dev, query_dtype=torch.float32)
+
+
+def test_short_and_empty_sessions(dev):
+    w = W.make_workload(2, {"n_tokens": 64 * 3, "batch": 3, "sink_tokens": 64})
+    # session 0: 1 token (partial fp16 page); session 1: none; session 2: all 192
+    run_case(w, [0], dev, n_tokens=[1, 0, 192], dequant=False)
+
+
+def test_partial_packed_page_is_flagged_and_untouched(dev):
+    import kv_cache_vector_srht_amd as tq
+    w = W.make_workload(2, {"n_tokens": 128, "batch": 1, "sink_tokens": 0})
+    layer = tq.Layer(W.rotation_signs(42, 0), dev)
+    cache = tq.Cache(w.formats[0], [128], dev)
+    k, v = W.make_kv(w, 0, device=dev)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    tq.encode_kv(layer, cache, k[:, :, :100], v[:, :, :100], tok0=0, error_flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 1
+    assert int(cache.page_view(0, 0, 1).to(torch.int32).sum()) == 0
+
+
+def test_deterministic(dev):
+    import kv_cache_vector_srht_amd as tq
+    w = W.make_workload(4, {"n_tokens": 64 * 8, "batch": 2})
+    S = W.qjl_matrix(42, 0)
+    layer = tq.Layer(W.rotation_signs(42, 0), dev, S)
+    k, v = W.make_kv(w, 0, device=dev)
+    q = W.make_query(w, 0, device=dev)
+    res = []
+    for _ in range(2):
+        cache = tq.Cache(w.formats[0], [w.n_tokens] * w.batch, dev)
+        tq.encode_kv(layer, cache, k, v)
+        out = tq.decode_attention(layer, cache, q)
+        torch.cuda.synchronize()
+        res.append((_np(cache.pool).copy(), _np(out).copy()))
+    assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])

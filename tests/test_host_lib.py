@@ -1,0 +1,179 @@
+"""libtq host-side behaviour, no GPU needed: exports, codebooks, layer
+randomness, sizes and argument validation (every device call here fails its
+host validation before any HIP call)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import kv_cache_vector_srht_amd as tq
+import workloads as W
+from oracle import tq_oracle as O
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "tq.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(tq.LIB_PATH):
+        from kv_cache_vector_srht_amd import build
+        build.build()
+    return tq.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    decl = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(tq_[a-z_0-9]+)\s*\(", open(HDR).read(), re.M)
+    assert set(decl) == set(tq.EXPORTS)
+    for name in decl:
+        assert hasattr(L, name)
+
+
+@pytest.mark.parametrize("kind", [tq.LLOYD_MAX, tq.UNIFORM])
+@pytest.mark.parametrize("bits", range(1, 9))
+def test_codebook_bit_equal_to_oracle(L, bits, kind):
+    c, t = tq.build_codebook(bits, kind)
+    oc, ot = O.codebook(bits, kind)
+    assert np.array_equal(c.view(np.uint32), oc.view(np.uint32))
+    assert np.array_equal(t.view(np.uint32), ot.view(np.uint32))
+
+
+def test_codebook_table_layout(L):
+    tab = tq.codebook_table(tq.LLOYD_MAX)
+    for b in range(1, 9):
+        c, t = O.codebook(b)
+        co, to = (1 << b) - 2, 510 + (1 << b) - b - 1
+        assert np.array_equal(tab[co:co + (1 << b)], c) and np.array_equal(tab[to:to + (1 << b) - 1], t)
+    assert np.all(tab[1012:] == 0)
+
+
+@pytest.mark.parametrize("layer", [0, 1, 35])
+def test_layer_params_match_generator(L, layer):
+    s, S = tq.layer_params(42, layer)
+    assert np.array_equal(s, W.rotation_signs(42, layer))
+    assert np.array_equal(S.view(np.uint32), W.qjl_matrix(42, layer).view(np.uint32))
+
+
+def test_sign_mask(L):
+    s = W.rotation_signs(42, 0)
+    m = tq.sign_mask(s)
+    for j in range(128):
+        assert ((int(m[j // 32]) >> (j % 32)) & 1) == (1 if s[j] < 0 else 0)
+    with pytest.raises(tq.TQError):
+        tq.sign_mask(np.zeros(128, np.int8))
+
+
+def test_page_sizes_match_oracle(L):
+    for fmt in [(0, 0, False), (1, 1, False), (3, 2, False), (2, 2, True), (8, 8, True), (4, 4, False)]:
+        assert tq.page_bytes(fmt) == O.page_bytes(fmt)
+    assert L.tq_page_bytes(9, 1, 0) == 0 and L.tq_page_bytes(0, 1, 0) == 0 and L.tq_page_bytes(2, 0, 0) == 0
+
+
+def test_page_descriptor_bits(L):
+    d = L.tq_page_descriptor(256 * 7, 3, 2, 1)
+    assert d == (256 * 7) | (3 << 48) | (2 << 52) | (1 << 56) | (1 << 63)
+    assert L.tq_page_descriptor(100, 3, 2, 0) == 0          # not 256-aligned
+    assert L.tq_page_descriptor(1 << 48, 3, 2, 0) == 0      # past 48 bits
+    assert L.tq_page_descriptor(0, 0, 0, 0) == 1 << 63      # fp16 page at offset 0
+
+
+def test_cache_bytes_and_workspace(L):
+    fm = [[[W.FP16, (3, 2, False), (2, 2, True)]]]
+    desc = np.array([L.tq_page_descriptor(0, 0, 0, 0), L.tq_page_descriptor(32768, 3, 2, 0),
+                     L.tq_page_descriptor(32768 + 5632, 2, 2, 1), 0], dtype=np.uint64)
+    assert L.tq_cache_bytes(desc.ctypes.data, 4) == O.cache_bytes(fm[0][0])
+    c = tq.tq_cache(4, 8, 512, 0, None, None, None, 0)
+    n = L.tq_decode_workspace_bytes(ctypes.byref(c), 32)
+    # 32 units x 512 pages over ~1024 groups: 16 pages per split, 32 splits
+    assert n == 4 * (4 * 32 * 384 + 4 * 32 * 32 * 260)
+    c0 = tq.tq_cache(0, 8, 512, 0, None, None, None, 0)
+    assert L.tq_decode_workspace_bytes(ctypes.byref(c0), 32) == 0
+
+
+def _fake_layer(**kw):
+    base = dict(head_dim=128, k_codebook=0, v_codebook=0, jl_dim=128, sign_mask=0x1000,
+                k_table=0x2000, v_table=0x3000, qjl_s=None)
+    base.update(kw)
+    return tq.tq_layer(**base)
+
+
+def _fake_cache(**kw):
+    base = dict(n_sessions=1, n_kv_heads=8, max_pages=4, reserved=0, n_tokens=0x4000,
+                pages=0x5000, pool=0x100000, pool_bytes=1 << 20)
+    base.update(kw)
+    return tq.tq_cache(**base)
+
+
+def _encode(L, layer, cache, **kw):
+    base = dict(k=0x10000, v=0x20000, dtype=1, tok0=0, ntok=64, reserved=0, stride_b=8 * 64 * 128,
+                stride_h=64 * 128, stride_t=128, error_flags=None)
+    base.update(kw)
+    inp = tq.tq_kv_input(**base)
+    return L.tq_encode_kv(ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(inp), None)
+
+
+def test_encode_validation(L):
+    bad = [
+        (dict(layer=_fake_layer(head_dim=64)), -2),
+        (dict(layer=_fake_layer(k_codebook=3)), -1),
+        (dict(layer=_fake_layer(sign_mask=0x1004)), -3),
+        (dict(layer=_fake_layer(qjl_s=0x6000, jl_dim=64)), -2),
+        (dict(cache=_fake_cache(n_sessions=0)), -1),
+        (dict(cache=_fake_cache(pool=0x100010)), -3),
+        (dict(cache=_fake_cache(pages=None)), -1),
+        (dict(inp=dict(tok0=32)), -1),
+        (dict(inp=dict(ntok=0)), -1),
+        (dict(inp=dict(ntok=4 * 64 + 1)), -1),
+        (dict(inp=dict(dtype=7)), -1),
+        (dict(inp=dict(k=0x10002)), -3),
+        (dict(inp=dict(stride_t=100)), -3),
+        (dict(inp=dict(stride_t=-128)), -1),
+        (dict(inp=dict(v=None)), -1),
+    ]
+    for case, want in bad:
+        layer = case.get("layer", _fake_layer())
+        cache = case.get("cache", _fake_cache())
+        st = _encode(L, layer, cache, **case.get("inp", {}))
+        assert st == want, (case, st, L.tq_last_error())
+        assert L.tq_last_error()
+    assert L.tq_encode_kv(None, None, None, None) == -1
+
+
+def _decode(L, layer, cache, ws_bytes=1 << 30, **kw):
+    base = dict(q=0x30000, dtype=1, n_q_heads=32, stride_b=32 * 128, stride_h=128, softmax_scale=0.0,
+                reserved=0)
+    base.update(kw)
+    qq = tq.tq_query(**base)
+    return L.tq_decode_attention(ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(qq),
+                                 ctypes.c_void_p(0x40000), ctypes.c_void_p(0x50000), ws_bytes, None)
+
+
+def test_decode_validation(L):
+    cases = [
+        (dict(kw=dict(n_q_heads=12)), -1),     # not a multiple of 8 KV heads
+        (dict(kw=dict(n_q_heads=8 * 16)), -2),  # group 16
+        (dict(kw=dict(dtype=5)), -1),
+        (dict(kw=dict(softmax_scale=float("nan"))), -1),
+        (dict(kw=dict(q=None)), -1),
+        (dict(ws=16), -4),
+        (dict(layer=_fake_layer(head_dim=256)), -2),
+    ]
+    for case, want in cases:
+        st = _decode(L, case.get("layer", _fake_layer()), _fake_cache(), case.get("ws", 1 << 30),
+                     **case.get("kw", {}))
+        assert st == want, (case, st, L.tq_last_error())
+
+
+def test_dequantize_validation(L):
+    out = ctypes.c_void_p(0x60000)
+    lay, cac = _fake_layer(), _fake_cache()
+    assert L.tq_dequantize(ctypes.byref(lay), ctypes.byref(cac), 2, 1, 0, 64, out, None) == -1
+    assert L.tq_dequantize(ctypes.byref(lay), ctypes.byref(cac), 0, 1, 0, 0, out, None) == -1
+    assert L.tq_dequantize(ctypes.byref(lay), ctypes.byref(cac), 0, 1, 0, 4 * 64 + 1, out, None) == -1
+    assert L.tq_dequantize(ctypes.byref(lay), ctypes.byref(cac), 0, 1, 0, 64, ctypes.c_void_p(0x60004), None) == -3
+    assert L.tq_dequantize(ctypes.byref(lay), ctypes.byref(cac), 0, 1, 0, 64, None, None) == -1
+
+
+def test_status_strings(L):
+    assert L.tq_status_string(0) == b"ok" and L.tq_status_string(-4) == b"workspace too small"
