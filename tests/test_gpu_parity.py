@@ -103,7 +103,8 @@ def test_workload4_qjl_sink_ragged(dev):
 def test_workload5_tiers_demotion(dev):
     w = W.make_workload(5, {"n_tokens": 64 * 1100 + 33, "batch": 1})
     fm = w.formats[0][0][0]
-    assert {f for f in fm if f[0]} >= {(2, 1, False)} and fm[-1] == W.FP16
+    # fp16 newest tier, three packed tiers (some pages demoted), ragged fp16 tail
+    assert len({f for f in fm if f[0]}) >= 3 and fm[-1] == W.FP16 and fm[-17] == W.FP16
     run_case(w, [0], dev, units=[(0, h) for h in range(8)], dequant=False)
 
 
