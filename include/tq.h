@@ -72,7 +72,7 @@ enum { TQ_DTYPE_F32 = 0, TQ_DTYPE_F16 = 1 };
 #define TQ_PAGE_TOKENS 64
 #define TQ_JL_DIM 128
 /* floats in one codebook table (all bit widths of one kind), see tq_codebook_table */
-#define TQ_CODEBOOK_TABLE_FLOATS 1024
+#define TQ_CODEBOOK_TABLE_FLOATS 8192
 
 /* ------------------------------------------------------- page descriptors
  * A cache is a caller-owned byte pool plus a page table of uint64
@@ -177,10 +177,15 @@ typedef struct tq_query {
  * and thread-safe; bits in 1..8. */
 int tq_build_codebook(int bits, int kind, float* centroids, float* boundaries);
 
-/* The table kernels read: for every bits = 1..8 the centroids at float offset
- * 2^bits - 2 and the boundaries at 510 + 2^bits - bits - 1; the tail is zero.
- * Writes TQ_CODEBOOK_TABLE_FLOATS floats to a host array (copy it to the
- * device for tq_layer). */
+/* The table kernels read, for every bits = 1..8: the centroids at float offset
+ * 2^bits - 2 and the boundaries at 510 + 2^bits - bits - 1; then, for the
+ * encoder, a lookup grid per width (header {S, O, n_bins, offset} at
+ * 1024 + 4 (bits - 1); n_bins entries {count of boundaries below the bin
+ * (u32), the one boundary inside the bin widened by a quarter bin each side
+ * (f32, or 3e38)} at `offset`), so that code(u) = count + [u >= boundary] at
+ * bin floor(u S + O) clamped to [0, n_bins).  The tail is zero.  Writes
+ * TQ_CODEBOOK_TABLE_FLOATS floats to a host array (copy it to the device for
+ * tq_layer). */
 int tq_codebook_table(int kind, float* table);
 
 /* Layer randomness from a seed ("TurboQuant-MLX v2.0", What's New: seed 42;

@@ -18,7 +18,7 @@ from typing import List, Optional, Sequence, Tuple
 HEAD_DIM = 128
 PAGE_TOKENS = 64
 JL_DIM = 128
-CODEBOOK_TABLE_FLOATS = 1024
+CODEBOOK_TABLE_FLOATS = 8192
 LLOYD_MAX = 0
 UNIFORM = 1
 DTYPE_F32 = 0

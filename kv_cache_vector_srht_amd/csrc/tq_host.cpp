@@ -197,9 +197,44 @@ int tq_build_codebook(int bits, int kind, float* centroids, float* boundaries) {
 int tq_codebook_table(int kind, float* table) {
   if (!table) return fail(TQ_ERR_INVALID_ARG, "null table");
   memset(table, 0, sizeof(float) * TQ_CODEBOOK_TABLE_FLOATS);
+  uint32_t* words = reinterpret_cast<uint32_t*>(table);
+  int next = kLutEntriesOffset;
   for (int b = 1; b <= 8; ++b) {
-    int st = tq_build_codebook(b, kind, table + centroid_offset(b), table + boundary_offset(b));
+    float* t = table + boundary_offset(b);
+    int st = tq_build_codebook(b, kind, table + centroid_offset(b), t);
     if (st != TQ_OK) return st;
+    // Quantiser lookup grid: bins of width h over [-T, T) with
+    // idx = floor(u * S + O), S = 1/h, O = T/h.  Bin i, widened by h/4 on each
+    // side, holds at most one boundary; base = boundaries below the widened bin.
+    const int nt = (1 << b) - 1;
+    double gap = 2.0, tmax = 0.0;
+    for (int k = 0; k + 1 < nt; ++k) gap = std::min(gap, (double)t[k + 1] - (double)t[k]);
+    for (int k = 0; k < nt; ++k) tmax = std::max(tmax, fabs((double)t[k]));
+    const double h = gap / 2.5, T = tmax + 2.0 * h;
+    const float S = (float)(1.0 / h), O = (float)(T / h);
+    const int nb = (int)ceil(2.0 * T / h) + 1;
+    if (next + 2 * nb > TQ_CODEBOOK_TABLE_FLOATS)
+      return fail(TQ_ERR_UNSUPPORTED, "codebook lookup grid does not fit the table");
+    float* hdr = table + kLutHeaderOffset + 4 * (b - 1);
+    hdr[0] = S;
+    hdr[1] = O;
+    reinterpret_cast<uint32_t*>(hdr)[2] = (uint32_t)nb;
+    reinterpret_cast<uint32_t*>(hdr)[3] = (uint32_t)next;
+    for (int i = 0; i < nb; ++i) {
+      const long double lo = ((long double)i - (long double)O) / (long double)S - 0.25L / (long double)S;
+      const long double hi = ((long double)i + 1.0L - (long double)O) / (long double)S + 0.25L / (long double)S;
+      uint32_t base = 0;
+      float thr = 3.0e38f;
+      int inside = 0;
+      for (int k = 0; k < nt; ++k) {
+        if ((long double)t[k] < lo) ++base;
+        else if ((long double)t[k] < hi) { thr = t[k]; ++inside; }
+      }
+      if (inside > 1) return fail(TQ_ERR_UNSUPPORTED, "lookup bin with two boundaries (bits %d)", b);
+      words[next + 2 * i] = base;
+      table[next + 2 * i + 1] = thr;
+    }
+    next += 2 * nb;
   }
   return ok();
 }

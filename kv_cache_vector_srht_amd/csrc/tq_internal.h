@@ -16,12 +16,17 @@ int ok();
 // Float offsets into a codebook table (all bit widths of one kind).
 constexpr int centroid_offset(int bits) { return (1 << bits) - 2; }
 constexpr int boundary_offset(int bits) { return 510 + (1 << bits) - bits - 1; }
+// Quantiser lookup grids: per bit width a header {S, O, n_bins, entry offset}
+// at kLutHeaderOffset + 4 (bits - 1); entries {base (u32), boundary (f32)}.
+constexpr int kLutHeaderOffset = 1024;
+constexpr int kLutEntriesOffset = 1056;
+constexpr int kLutMaxBins = 1400;
 
 // Decode split-K geometry.
 constexpr int kDecodeWaves = 4;             // waves per split workgroup
 constexpr int kTargetSplitGroups = 1024;    // workgroups the split grid aims for
 constexpr int kQPrepFloats = 3 * 128;       // rotated q, plain q, S q (all pre-scaled)
-constexpr int kPartialFloats = 4 + 2 * 128; // m_r, l_r, m_o, l_o, acc_r[128], acc_o[128]
+constexpr int kPartialFloats = 4 + 128;     // m, l, (pad), acc[128]
 
 struct SplitPlan {
   int n_splits;

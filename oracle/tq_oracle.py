@@ -261,13 +261,15 @@ def gaussian_mse(centroids, boundaries) -> float:
 # Encode / dequantise one batch of head vectors.
 # ----------------------------------------------------------------------------
 def encode(X: np.ndarray, signs, bits: int, kind: int = LLOYD_MAX,
-           boundary_eps: float = 1e-6) -> Dict[str, np.ndarray]:
+           boundary_eps: float = 1e-6, overrides=None) -> Dict[str, np.ndarray]:
     """Encode rows of X (values as stored, upcast to float64).
 
     n = ||x||_2 (stored float32); u = sqrt(d) R x / n (u = 0 when n = 0);
     code_j = #{k : t_k <= float32(u_j)} (readings R2, R3).
     ``near`` flags coordinates whose float64 u lies within ``boundary_eps`` of
     a boundary: there the float32 decision may legitimately differ by one level.
+    ``overrides`` = (rows, cols, codes) selects that other admissible level at
+    flagged coordinates (any other override raises ValueError).
     """
     X = np.asarray(X, dtype=np.float64)
     d = X.shape[-1]
@@ -284,6 +286,13 @@ def encode(X: np.ndarray, signs, bits: int, kind: int = LLOYD_MAX,
     below = np.abs(U - t64[np.clip(codes - 1, 0, t64.size - 1)])
     above = np.abs(U - t64[np.clip(codes, 0, t64.size - 1)])
     near = np.minimum(below, above) < boundary_eps
+    if overrides is not None:
+        rows, cols, alt = (np.asarray(v, dtype=np.int64) for v in overrides)
+        if rows.size:
+            if not np.all(near[rows, cols]) or not np.all(np.abs(alt - codes[rows, cols]) == 1):
+                raise ValueError("override outside the boundary allowance")
+            codes = codes.copy()
+            codes[rows, cols] = alt
     return {"norm": n.astype(np.float32), "u": U, "codes": codes, "near": near}
 
 
@@ -497,13 +506,16 @@ def attention(q: np.ndarray, keys: np.ndarray, values: np.ndarray,
 
 
 def reconstruct_unit(K: np.ndarray, V: np.ndarray, formats, signs, S=None,
-                     k_kind: int = LLOYD_MAX, v_kind: int = LLOYD_MAX):
+                     k_kind: int = LLOYD_MAX, v_kind: int = LLOYD_MAX,
+                     k_overrides=None, v_overrides=None):
     """Keys/values as decode attention sees them for one (session, KV head).
 
     K, V: the stored input rows [T, 128] of this unit; formats: page formats.
     fp16 pages keep the fp16 values; packed pages are encoded then dequantised
     (keys plus the QJL residual when the page carries one).  Pages of one
-    format are encoded together (rows are independent).
+    format are encoded together (rows are independent).  ``k_overrides`` /
+    ``v_overrides`` = (tokens, cols, codes) pick the other admissible level at
+    boundary coordinates (see ``encode``).
     """
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
@@ -521,11 +533,20 @@ def reconstruct_unit(K: np.ndarray, V: np.ndarray, formats, signs, S=None,
         else:
             assert hi - lo == PAGE_TOKENS, "a packed page must be full"
             groups.setdefault(tuple(fmt), []).append(p)
+    def local(ov, rows):
+        if ov is None:
+            return None
+        tok, col, code = (np.asarray(v, dtype=np.int64) for v in ov)
+        pos = np.full(T, -1, dtype=np.int64)
+        pos[rows] = np.arange(rows.size)
+        sel = pos[tok] >= 0 if tok.size else np.zeros(0, dtype=bool)
+        return pos[tok[sel]], col[sel], code[sel]
+
     for fmt, plist in groups.items():
         kb, vb, qjl = fmt
         rows = np.concatenate([np.arange(p * PAGE_TOKENS, (p + 1) * PAGE_TOKENS) for p in plist])
-        ek = encode(K[rows], signs, kb, k_kind)
-        ev = encode(V[rows], signs, vb, v_kind)
+        ek = encode(K[rows], signs, kb, k_kind, overrides=local(k_overrides, rows))
+        ev = encode(V[rows], signs, vb, v_kind, overrides=local(v_overrides, rows))
         kh = dequantize(ek["norm"], ek["codes"], signs, kb, k_kind)
         if qjl:
             qj = qjl_encode(K[rows], kh, S)

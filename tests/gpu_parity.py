@@ -50,7 +50,8 @@ class Tally:
         assert self.worst_cos >= COS_MIN, f"dequantised cosine {self.worst_cos:.9f}"
 
 
-def _cmp_codes(got: np.ndarray, exp: np.ndarray, near: np.ndarray, t: Tally, what: str):
+def _cmp_codes(got: np.ndarray, exp: np.ndarray, near: np.ndarray, t: Tally, what: str, lo: int,
+               alt: list):
     diff = got != exp
     t.coords += got.size
     if diff.any():
@@ -58,7 +59,15 @@ def _cmp_codes(got: np.ndarray, exp: np.ndarray, near: np.ndarray, t: Tally, wha
         assert not bad.any(), f"{what}: {int(bad.sum())} code mismatches away from a boundary " \
                               f"(first at {np.argwhere(bad)[0].tolist()}, got {got[bad][:4]}, want {exp[bad][:4]})"
         t.mismatches += int(diff.sum())
+        r, c = np.nonzero(diff)
+        alt.append((r + lo, c, got[r, c]))
     return ~diff.any(axis=1)   # rows (tokens) whose codes all match
+
+
+def _stack(alt):
+    if not alt:
+        return None
+    return tuple(np.concatenate([a[i] for a in alt]) for i in range(3))
 
 
 def compare_unit_pages(cache, b: int, h: int, K: np.ndarray, V: np.ndarray, formats, signs, S,
@@ -66,11 +75,14 @@ def compare_unit_pages(cache, b: int, h: int, K: np.ndarray, V: np.ndarray, form
                        pool_host: Optional[np.ndarray] = None):
     """Compare every page of unit (b, h) with the oracle's encoding of K, V.
 
-    Returns boolean arrays [T] marking tokens whose K (resp. V) codes all match.
+    Returns (k_ok, v_ok, k_alt, v_alt): boolean arrays [T] marking tokens whose
+    K (resp. V) codes all match, and the admissible boundary tie-breaks the GPU
+    took, as (tokens, coordinates, codes) for ``reconstruct_unit``.
     """
     T = K.shape[0] if n_tokens is None else n_tokens
     k_ok = np.ones(T, dtype=bool)
     v_ok = np.ones(T, dtype=bool)
+    k_alt, v_alt = [], []
     for p, fmt in enumerate(formats):
         lo, hi = p * 64, min(T, (p + 1) * 64)
         if lo >= T:
@@ -92,9 +104,11 @@ def compare_unit_pages(cache, b: int, h: int, K: np.ndarray, V: np.ndarray, form
             o, n = sec[name]
             return raw[o:o + n]
         kc = O.unpack_block(part("k_codes"), kb)
-        ok_rows = _cmp_codes(kc, enc["k"]["codes"], enc["k"]["near"], t, f"K page ({b},{h},{p}) fmt {fmt}")
+        ok_rows = _cmp_codes(kc, enc["k"]["codes"], enc["k"]["near"], t, f"K page ({b},{h},{p}) fmt {fmt}",
+                             lo, k_alt)
         vc = O.v_codes_from_streams(O.unpack_block(part("v_codes"), vb))
-        v_rows = _cmp_codes(vc, enc["v"]["codes"], enc["v"]["near"], t, f"V page ({b},{h},{p}) fmt {fmt}")
+        v_rows = _cmp_codes(vc, enc["v"]["codes"], enc["v"]["near"], t, f"V page ({b},{h},{p}) fmt {fmt}",
+                            lo, v_alt)
         k_ok[lo:hi] = ok_rows
         v_ok[lo:hi] = v_rows
         for name, ref in (("k_norm", enc["k"]["norm"]), ("v_norm", enc["v"]["norm"])):
@@ -112,7 +126,7 @@ def compare_unit_pages(cache, b: int, h: int, K: np.ndarray, V: np.ndarray, form
             assert np.allclose(g[rows], qj["gamma"][rows], rtol=NORM_RTOL, atol=1e-30), \
                 f"QJL gamma page ({b},{h},{p})"
             k_ok[lo + rows[dz.any(axis=1)]] = False
-    return k_ok, v_ok
+    return k_ok, v_ok, _stack(k_alt), _stack(v_alt)
 
 
 def compare_attention(out_rows: np.ndarray, q_rows: np.ndarray, Kh: np.ndarray, Vh: np.ndarray,

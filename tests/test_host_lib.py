@@ -45,7 +45,22 @@ def test_codebook_table_layout(L):
         c, t = O.codebook(b)
         co, to = (1 << b) - 2, 510 + (1 << b) - b - 1
         assert np.array_equal(tab[co:co + (1 << b)], c) and np.array_equal(tab[to:to + (1 << b) - 1], t)
-    assert np.all(tab[1012:] == 0)
+    assert np.all(tab[1012:1024] == 0)
+    # lookup grids: code(u) = base + [u >= boundary] at bin floor(u S + O)
+    words = tab.view(np.uint32)
+    rng = np.random.default_rng(0)
+    for b in range(1, 9):
+        gS, gO = tab[1024 + 4 * (b - 1)], tab[1024 + 4 * (b - 1) + 1]
+        nb, off = words[1024 + 4 * (b - 1) + 2], words[1024 + 4 * (b - 1) + 3]
+        ent = words[off:off + 2 * nb].reshape(nb, 2)
+        c, t = O.codebook(b)
+        u = np.concatenate([rng.standard_normal(20000).astype(np.float32) * 2,
+                            t, np.nextafter(t, np.float32(-np.inf)), np.nextafter(t, np.float32(np.inf)),
+                            np.float32([-50, 50, 0, -0.0])]).astype(np.float32)
+        bins = np.clip(np.trunc(u.astype(np.float64) * np.float64(gS) + np.float64(gO)).astype(np.int64), 0, nb - 1)
+        got = ent[bins, 0] + (u >= ent[bins, 1].view(np.float32))
+        want = np.searchsorted(t, u, side="right")
+        assert np.array_equal(got, want), b
 
 
 @pytest.mark.parametrize("layer", [0, 1, 35])
@@ -86,7 +101,7 @@ def test_cache_bytes_and_workspace(L):
     c = tq.tq_cache(4, 8, 512, 0, None, None, None, 0)
     n = L.tq_decode_workspace_bytes(ctypes.byref(c), 32)
     # 32 units x 512 pages over ~1024 groups: 16 pages per split, 32 splits
-    assert n == 4 * (4 * 32 * 384 + 4 * 32 * 32 * 260)
+    assert n == 4 * (4 * 32 * 384 + 4 * 32 * 32 * 132)
     c0 = tq.tq_cache(0, 8, 512, 0, None, None, None, 0)
     assert L.tq_decode_workspace_bytes(ctypes.byref(c0), 32) == 0
 

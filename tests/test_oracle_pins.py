@@ -381,3 +381,22 @@ def test_page_bytes_round_trip_through_decode_page():
     Kd, Vd = O.decode_page(enc["bytes"], fmt, s, S)
     Kh, Vh = O.reconstruct_unit(K, V, [fmt], s, S)
     assert np.allclose(Kd, Kh, atol=1e-12) and np.allclose(Vd, Vh, atol=1e-12)
+
+
+def test_overrides_only_within_the_boundary_allowance():
+    s = _signs()
+    R = O.rotation_matrix(s)
+    _, t32 = O.codebook(2)
+    u = np.zeros(128)
+    u[3] = float(t32[2]) + 1e-9
+    u[4] = float(t32[2]) + 1e-3
+    rest = math.sqrt((128 - u[3] ** 2 - u[4] ** 2) / 126)
+    u[[j for j in range(128) if j not in (3, 4)]] = rest
+    x = (R @ u)[None, :]
+    base = O.encode(x, s, 2)["codes"][0]
+    alt = O.encode(x, s, 2, overrides=([0], [3], [base[3] - 1]))["codes"][0]
+    assert alt[3] == base[3] - 1 and np.array_equal(np.delete(alt, 3), np.delete(base, 3))
+    with pytest.raises(ValueError):
+        O.encode(x, s, 2, overrides=([0], [4], [base[4] - 1]))   # not near a boundary
+    with pytest.raises(ValueError):
+        O.encode(x, s, 2, overrides=([0], [3], [base[3] - 2]))   # two levels away
