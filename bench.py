@@ -86,8 +86,10 @@ def traffic_record(kernel: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    src = os.path.join(ROOT, "kv_cache_vector_srht_amd", "csrc", "tq_kernels.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    sha = hashlib.sha256()
+    for f in rec.get("sources", []):
+        sha.update(open(os.path.join(ROOT, f), "rb").read())
+    sha = sha.hexdigest()
     if rec.get("source_sha256") != sha:
         return None
     return rec.get("bytes_per_launch")

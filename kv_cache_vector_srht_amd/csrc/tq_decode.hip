@@ -1,0 +1,679 @@
+// Decode-attention kernels of libtq for gfx950 (CDNA4, wave64) and
+// tq_decode_attention.
+//
+// (1) query prep rotates each query head (R q, and S q for QJL), pre-scaled
+// for exp2; (2) split-K: a 4-wave workgroup per (session, KV head, page
+// range); per page, lane = token for the key scores of the G query heads of
+// the KV head (codes looked up two at a time in LDS tables, query coordinates
+// read as wave-uniform scalars), an online softmax with wavefront reductions,
+// then lane = (token quarter, 8 coordinates) for the value accumulation in the
+// rotated domain; (3) combine: log-sum-exp merge of the splits and one inverse
+// rotation per query head (the Walsh-Hadamard transform factored out of the
+// value sum, as the MLX TurboQuant skill page reports for its Metal kernels,
+// Path A > Optimisations Metal).
+#include "tq_device.h"
+
+namespace tq {
+namespace dev {
+namespace {
+
+// ------------------------------------------------------------------ decode
+struct DecodeArgs {
+  const void* q;
+  int q_dtype;
+  int64_t q_sb, q_sh;
+  int n_q_heads, group;
+  float scale2;  // softmax scale * log2(e)
+  const int32_t* n_tokens;
+  int n_sessions, n_kv_heads, max_pages;
+  const char* pool;
+  uint64_t pool_bytes;
+  const uint32_t* sign_mask;
+  const float* k_table;
+  const float* v_table;
+  const float* qjl_s;
+  int n_splits, pages_per_split;            // common class
+  int n_splits_general, pages_per_split_general;
+  float* wsq;   // [B][H_q][384]: rotated q, plain q, S q (pre-scaled)
+  float* wsp;   // [B][H_q][n_splits][kPartialFloats]: m, l, -, -, acc[128]
+  float* out;
+};
+
+// (1) query prep: one 128-thread block per (session, query head).
+__global__ __launch_bounds__(128) void qprep_kernel(DecodeArgs a) {
+  __shared__ float buf[D];
+  __shared__ float qs[D];
+  const int j = threadIdx.x;
+  const int row = blockIdx.x;
+  const int b = row / a.n_q_heads, h = row - b * a.n_q_heads;
+  const float qj = load_elem(a.q, a.q_dtype, (size_t)b * a.q_sb + (size_t)h * a.q_sh + j);
+  const uint32_t neg = (a.sign_mask[j >> 5] >> (j & 31)) & 1u;
+  qs[j] = qj;
+  buf[j] = flip_if(qj, neg);
+  __syncthreads();
+#pragma clang loop unroll(full)
+  for (int hh = 1; hh < D; hh <<= 1) {
+    const float mine = buf[j], other = buf[j ^ hh];
+    __syncthreads();
+    buf[j] = (j & hh) ? other - mine : mine + other;
+    __syncthreads();
+  }
+  // Layout per (session, KV head): three sections of 128 x G floats (rotated q,
+  // plain q, S q), each ordered [coordinate / 4][query head in group][coordinate % 4]
+  // so that one 16-dword scalar load brings 4 coordinates of 4 heads.
+  const int G = a.group, g = h / G, hg = h - g * G;
+  float* w = a.wsq + ((size_t)b * a.n_kv_heads + g) * kQPrepFloats * G;
+  const size_t slot = ((size_t)(j >> 2) * G + hg) * 4 + (j & 3);
+  // R q = D H D q / sqrt(d); packed-page scores use (R q) * scale2 / sqrt(d).
+  w[slot] = flip_if(buf[j], neg) * (a.scale2 * (1.0f / D));
+  w[D * G + slot] = qj * a.scale2;
+  if (a.qjl_s) {
+    const float* srow = a.qjl_s + (size_t)j * D;
+    float p = 0.f;
+    for (int i = 0; i < D; ++i) p = fmaf(srow[i], qs[i], p);
+    w[2 * D * G + slot] = p * (a.scale2 * kSqrtHalfPi / TQ_JL_DIM);
+  } else {
+    w[2 * D * G + slot] = 0.f;
+  }
+}
+
+// Per-workgroup LDS of the split kernel.
+template <int G>
+struct SplitLds {
+  float2 kpair[340];          // pair tables for bits 1..4 (4 + 16 + 64 + 256 entries)
+  float2 vpair[340];
+  float kcent[512];           // centroid lists for every bit width (table layout)
+  float vcent[512];
+  float w[kDecodeWaves][PT * G];           // softmax weights of the current page
+  float red[kDecodeWaves][G * D];          // workgroup reduction
+  float stat[kDecodeWaves][2][G];          // m, l per wave
+};
+
+__device__ __forceinline__ int pair_offset(int b) {
+  return b == 1 ? 0 : b == 2 ? 4 : b == 3 ? 20 : 84;
+}
+
+// Key scores of one packed page, lane = token: s[h] = sum_j qr[h][j] c[code_j].
+// Query values are wave-uniform scalar loads; they share the LGKM counter with
+// the LDS codebook lookups and return out of order, so the loop is pipelined by
+// hand: for chunk n the first FMA waits for chunk n's data only, then chunk
+// n+1's scalar loads and lookups are issued, then the rest of chunk n runs.
+template <int B, int G>
+__device__ __forceinline__ void key_scores(const char* blk, int lane, const float* __restrict__ qr,
+                                           const float2* pair, const float* cent, float (&s)[G]) {
+  constexpr int CH = 4;                       // coordinates per chunk
+  uint32_t sw[4 * B];
+  const uint4* src = reinterpret_cast<const uint4*>(blk);
+#pragma clang loop unroll(full)
+  for (int w = 0; w < B; ++w) {
+    const uint4 v = src[w * 64 + lane];
+    sw[4 * w] = v.x; sw[4 * w + 1] = v.y; sw[4 * w + 2] = v.z; sw[4 * w + 3] = v.w;
+  }
+#pragma clang loop unroll(full)
+  for (int h = 0; h < G; ++h) s[h] = 0.f;
+  float qa[G][CH], qb[G][CH], ca[CH], cb[CH];
+  auto fetch = [&](int n, float (&qd)[G][CH], float (&cd)[CH]) {
+#pragma clang loop unroll(full)
+    for (int h = 0; h < G; ++h)
+#pragma clang loop unroll(full)
+      for (int e = 0; e < CH; ++e) qd[h][e] = qr[(n * G + h) * CH + e];
+    if constexpr (B <= 4) {
+      const float2* pt = pair + pair_offset(B);
+#pragma clang loop unroll(full)
+      for (int e = 0; e < CH; e += 2) {
+        const float2 c = pt[bits_at(sw, (n * CH + e) * B, 2 * B)];
+        cd[e] = c.x;
+        cd[e + 1] = c.y;
+      }
+    } else {
+      const float* ct = cent + centroid_offset(B);
+#pragma clang loop unroll(full)
+      for (int e = 0; e < CH; ++e) cd[e] = ct[bits_at(sw, (n * CH + e) * B, B)];
+    }
+  };
+  auto fmas = [&](const float (&qd)[G][CH], const float (&cd)[CH], int e0, int e1) {
+#pragma clang loop unroll(full)
+    for (int e = e0; e < e1; ++e)
+#pragma clang loop unroll(full)
+      for (int h = 0; h < G; ++h) s[h] = fmaf(qd[h][e], cd[e], s[h]);
+  };
+  fetch(0, qa, ca);
+#pragma clang loop unroll(full)
+  for (int n = 0; n < D / CH; n += 2) {
+    fmas(qa, ca, 0, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(n + 1, qb, cb);
+    __builtin_amdgcn_sched_barrier(0);
+    fmas(qa, ca, 1, CH);
+    fmas(qb, cb, 0, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (n + 2 < D / CH) fetch(n + 2, qa, ca);
+    __builtin_amdgcn_sched_barrier(0);
+    fmas(qb, cb, 1, CH);
+  }
+}
+
+// Key scores of an fp16 page, lane = token, with the unrotated query.
+template <int G>
+__device__ __forceinline__ void key_scores_fp16(const char* page, int lane, const float* __restrict__ qo,
+                                                float (&s)[G]) {
+  const __half* krow = reinterpret_cast<const __half*>(page) + (size_t)lane * D;
+#pragma clang loop unroll(full)
+  for (int h = 0; h < G; ++h) s[h] = 0.f;
+#pragma clang loop unroll(full)
+  for (int c = 0; c < D / 8; ++c) {
+    const uint4 kv = reinterpret_cast<const uint4*>(krow)[c];
+    const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma clang loop unroll(full)
+    for (int e = 0; e < 4; ++e) {
+      const float2 f = __half22float2(*reinterpret_cast<const __half2*>(&kw[e]));
+      const int j = 8 * c + 2 * e;
+#pragma clang loop unroll(full)
+      for (int h = 0; h < G; ++h) {
+        s[h] = fmaf(qo[((j >> 2) * G + h) * 4 + (j & 3)], f.x, s[h]);
+        s[h] = fmaf(qo[((j >> 2) * G + h) * 4 + (j & 3) + 1], f.y, s[h]);
+      }
+    }
+  }
+}
+
+// QJL term: sum_i qs[h][i] (2 z_i - 1) for lane = token.
+template <int G>
+__device__ __forceinline__ void qjl_scores(const char* qb, int lane, const float* __restrict__ qsv,
+                                           float (&t)[G]) {
+  const uint4 z4 = reinterpret_cast<const uint4*>(qb)[lane];
+  const uint32_t zw[4] = {z4.x, z4.y, z4.z, z4.w};
+#pragma clang loop unroll(full)
+  for (int h = 0; h < G; ++h) t[h] = 0.f;
+#pragma clang loop unroll(full)
+  for (int i = 0; i < TQ_JL_DIM; ++i) {
+    const float z = ((zw[i >> 5] >> (i & 31)) & 1u) ? 1.f : -1.f;
+#pragma clang loop unroll(full)
+    for (int h = 0; h < G; ++h) t[h] = fmaf(qsv[((i >> 2) * G + h) * 4 + (i & 3)], z, t[h]);
+  }
+}
+
+// Value accumulation of one packed page: lane (q, i) owns coordinates
+// 8i..8i+7 of tokens 4k+q; acc[h][e] += w[token][h] c[code].
+template <int B, int G>
+__device__ __forceinline__ void value_accum(const char* blk, int lane, const float* wv,
+                                            const float2* pair, const float* cent, float (&acc)[G][8]) {
+  uint32_t sw[4 * B];
+  const uint4* src = reinterpret_cast<const uint4*>(blk);
+#pragma clang loop unroll(full)
+  for (int w = 0; w < B; ++w) {
+    const uint4 v = src[w * 64 + lane];
+    sw[4 * w] = v.x; sw[4 * w + 1] = v.y; sw[4 * w + 2] = v.z; sw[4 * w + 3] = v.w;
+  }
+  const int q = lane >> 4;
+#pragma clang loop unroll(full)
+  for (int k = 0; k < 16; ++k) {
+    float wt[G];
+#pragma clang loop unroll(full)
+    for (int h = 0; h < G; ++h) wt[h] = wv[(4 * k + q) * G + h];
+    if constexpr (B <= 4) {
+      const float2* pt = pair + pair_offset(B);
+#pragma clang loop unroll(full)
+      for (int e = 0; e < 8; e += 2) {
+        const float2 c = pt[bits_at(sw, (8 * k + e) * B, 2 * B)];
+#pragma clang loop unroll(full)
+        for (int h = 0; h < G; ++h) {
+          acc[h][e] = fmaf(wt[h], c.x, acc[h][e]);
+          acc[h][e + 1] = fmaf(wt[h], c.y, acc[h][e + 1]);
+        }
+      }
+    } else {
+      const float* ct = cent + centroid_offset(B);
+#pragma clang loop unroll(full)
+      for (int e = 0; e < 8; ++e) {
+        const float c = ct[bits_at(sw, (8 * k + e) * B, B)];
+#pragma clang loop unroll(full)
+        for (int h = 0; h < G; ++h) acc[h][e] = fmaf(wt[h], c, acc[h][e]);
+      }
+    }
+  }
+}
+
+// Value accumulation of an fp16 page into the rotated-domain sums: each token's
+// row is rotated with the unnormalised D H D (the 16 lanes of a quarter hold
+// its 128 values, 8 each), so that D H D acc / d at the end returns sum p v.
+template <int G>
+__device__ __forceinline__ void value_accum_fp16(const char* page, int lane, const float* wv,
+                                                 const uint32_t (&dm)[8], float (&acc)[G][8]) {
+  const __half* vbase = reinterpret_cast<const __half*>(page + PT * D * 2);
+  const int q = lane >> 4, i = lane & 15;
+  for (int k = 0; k < 16; ++k) {
+    const int t = 4 * k + q;
+    const uint4 vv = reinterpret_cast<const uint4*>(vbase + (size_t)t * D + 8 * i)[0];
+    const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+    float x[8];
+#pragma clang loop unroll(full)
+    for (int e = 0; e < 4; ++e) {
+      const float2 f = __half22float2(*reinterpret_cast<const __half2*>(&vw[e]));
+      x[2 * e] = flip_if(f.x, dm[2 * e]);
+      x[2 * e + 1] = flip_if(f.y, dm[2 * e + 1]);
+    }
+    // coordinate bits 0..2: within the lane
+#pragma clang loop unroll(full)
+    for (int hh = 1; hh < 8; hh <<= 1)
+#pragma clang loop unroll(full)
+      for (int e = 0; e < 8; ++e)
+        if (!(e & hh)) {
+          const float a0 = x[e], b0 = x[e + hh];
+          x[e] = a0 + b0;
+          x[e + hh] = a0 - b0;
+        }
+    // coordinate bits 3..6: across the 16 lanes of the quarter
+#pragma clang loop unroll(full)
+    for (int m = 1; m < 16; m <<= 1) {
+      const float sg = (i & m) ? -1.f : 1.f;
+#pragma clang loop unroll(full)
+      for (int e = 0; e < 8; ++e) {
+        const float other = __shfl_xor(x[e], m, 64);
+        x[e] = fmaf(sg, x[e], other);
+      }
+    }
+    float wt[G];
+#pragma clang loop unroll(full)
+    for (int h = 0; h < G; ++h) wt[h] = wv[t * G + h];
+#pragma clang loop unroll(full)
+    for (int e = 0; e < 8; ++e) {
+      const float y = flip_if(x[e], dm[e]);
+#pragma clang loop unroll(full)
+      for (int h = 0; h < G; ++h) acc[h][e] = fmaf(wt[h], y, acc[h][e]);
+    }
+  }
+}
+
+// Online-softmax update of one page for G heads.  s: log2-domain scores of
+// this lane's token (-inf when masked); on return s holds p = 2^(s - m) and
+// alpha the rescale of the running sums.
+template <int G>
+__device__ __forceinline__ void softmax_update(float (&s)[G], float (&m)[G], float (&l)[G],
+                                               float (&alpha)[G]) {
+#pragma clang loop unroll(full)
+  for (int h = 0; h < G; ++h) {
+    const float mx = wave_max(s[h]);
+    const float mn = fmaxf(m[h], mx);
+    if (mn == -INFINITY) {
+      alpha[h] = 1.f;
+      s[h] = 0.f;
+    } else {
+      alpha[h] = exp2f(m[h] - mn);
+      s[h] = exp2f(s[h] - mn);
+    }
+    m[h] = mn;
+    l[h] = fmaf(l[h], alpha[h], s[h]);
+  }
+}
+
+// Page classes: the common packed formats (k_bits, v_bits <= 4, no QJL) run
+// in a kernel compiled for them alone (fewer registers, more waves in flight);
+// every other page (fp16, 5-8 bits, QJL) runs in the general kernel.  Each
+// writes its own partials; the combine merges both.
+__device__ __forceinline__ bool common_page(int kb, int vb, bool qjl) {
+  return kb >= 1 && kb <= 4 && vb >= 1 && vb <= 4 && !qjl;
+}
+
+template <int G, int CLASS>
+__global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
+                                                                  const float* __restrict__ wsq,
+                                                                  const uint64_t* __restrict__ pages,
+                                                                  float* __restrict__ wsp) {
+  __shared__ SplitLds<G> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+  const int hq0 = hkv * G;
+  // partials [B][H_q][n_splits common, then n_splits_general general]
+  const size_t head_stride = (size_t)(a.n_splits + a.n_splits_general) * kPartialFloats;
+  float* part = wsp + ((size_t)b * a.n_q_heads + hq0) * head_stride +
+                ((size_t)(CLASS == 0 ? 0 : a.n_splits) + split) * kPartialFloats;
+  const int pps = CLASS == 0 ? a.pages_per_split : a.pages_per_split_general;
+
+  const int ntok = max(0, a.n_tokens[b]);
+  const int npages = min(a.max_pages, (ntok + PT - 1) / PT);   // never past the table row
+  const int p_begin = split * pps;
+  const int p_end = min(npages, p_begin + pps);
+  const uint64_t* ptab = pages + ((size_t)b * a.n_kv_heads + hkv) * a.max_pages;
+  {
+    // nothing of this class in the range: an empty partial, no setup
+    bool any = false;
+    for (int p = p_begin; p < p_end && !any; ++p) {
+      const uint64_t desc = ptab[p];
+      const int kb = (int)((desc >> 48) & 15), vb = (int)((desc >> 52) & 15);
+      any = common_page(kb, vb, (desc & TQ_PAGE_QJL) != 0) == (CLASS == 0);
+    }
+    if (!any) {
+      if (tid < G) {
+        part[tid * head_stride] = -INFINITY;
+        part[tid * head_stride + 1] = 0.f;
+      }
+      return;
+    }
+  }
+
+  // Stage codebooks: pair tables for 1..4 bits and all centroid lists.
+  for (int i = tid; i < 510; i += blockDim.x) {
+    sm.kcent[i] = a.k_table[i];
+    sm.vcent[i] = a.v_table[i];
+  }
+  __syncthreads();
+  for (int i = tid; i < 340; i += blockDim.x) {
+    const int bb = i < 4 ? 1 : i < 20 ? 2 : i < 84 ? 3 : 4;
+    const int idx = i - pair_offset(bb), L = 1 << bb;
+    const int lo = idx & (L - 1), hi = idx >> bb;
+    sm.kpair[i] = make_float2(sm.kcent[centroid_offset(bb) + lo], sm.kcent[centroid_offset(bb) + hi]);
+    sm.vpair[i] = make_float2(sm.vcent[centroid_offset(bb) + lo], sm.vcent[centroid_offset(bb) + hi]);
+  }
+  __syncthreads();
+
+  const float* __restrict__ qrow = wsq + ((size_t)b * a.n_kv_heads + hkv) * kQPrepFloats * G;
+
+  float m[G], l[G], acc[G][8];
+#pragma clang loop unroll(full)
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma clang loop unroll(full)
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  }
+  float* wv = sm.w[wave];
+  const int q4 = lane >> 4, i16 = lane & 15;
+
+  for (int p = p_begin + wave; p < p_end; p += kDecodeWaves) {
+    const uint64_t desc = ptab[p];
+    const int kb = (int)((desc >> 48) & 15), vb = (int)((desc >> 52) & 15);
+    const bool qjl = (desc & TQ_PAGE_QJL) != 0;
+    const uint64_t off = desc & TQ_PAGE_OFFSET_MASK;
+    if (!(desc & TQ_PAGE_PRESENT) || off + page_size_dev(kb, vb, qjl) > a.pool_bytes) continue;
+    if (kb == 0 ? (vb != 0 || qjl) : (kb > 8 || vb < 1 || vb > 8)) continue;
+    if (qjl && a.qjl_s == nullptr) continue;
+    if (common_page(kb, vb, qjl) != (CLASS == 0)) continue;
+    const char* page = a.pool + off;
+    const int valid = min(PT, ntok - p * PT);
+    float s[G], alpha[G];
+    const char* vblk = page + 1024 * kb + 256;
+    float nv = 1.f;
+    if (CLASS == 1 && kb == 0) {
+      key_scores_fp16<G>(page, lane, qrow + D * G, s);
+    } else {
+      if constexpr (CLASS == 0) {
+        switch (kb) {
+          case 1: key_scores<1, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
+          case 2: key_scores<2, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
+          case 3: key_scores<3, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
+          default: key_scores<4, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
+        }
+      } else {
+        switch (kb) {
+          case 1: key_scores<1, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
+          case 2: key_scores<2, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
+          case 3: key_scores<3, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
+          case 4: key_scores<4, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
+          case 5: key_scores<5, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
+          case 6: key_scores<6, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
+          case 7: key_scores<7, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
+          default: key_scores<8, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
+        }
+      }
+      const float nk = reinterpret_cast<const float*>(page + 1024 * kb)[lane];
+#pragma clang loop unroll(full)
+      for (int h = 0; h < G; ++h) s[h] *= nk;
+      if (CLASS == 1 && qjl) {
+        float t[G];
+        qjl_scores<G>(vblk, lane, qrow + 2 * D * G, t);
+        const float gamma = reinterpret_cast<const float*>(vblk + 1024)[lane];
+#pragma clang loop unroll(full)
+        for (int h = 0; h < G; ++h) s[h] = fmaf(gamma, t[h], s[h]);
+        vblk += 1280;
+      }
+      nv = reinterpret_cast<const float*>(vblk + 1024 * vb)[lane];
+    }
+#pragma clang loop unroll(full)
+    for (int h = 0; h < G; ++h)
+      if (lane >= valid) s[h] = -INFINITY;
+    softmax_update<G>(s, m, l, alpha);
+#pragma clang loop unroll(full)
+    for (int h = 0; h < G; ++h) {
+#pragma clang loop unroll(full)
+      for (int e = 0; e < 8; ++e) acc[h][e] *= alpha[h];
+      wv[lane * G + h] = s[h] * nv;
+    }
+    wave_lds_sync();
+    if (CLASS == 1 && kb == 0) {
+      uint32_t dm[8];
+      const uint32_t dword = a.sign_mask[i16 >> 2];
+#pragma clang loop unroll(full)
+      for (int e = 0; e < 8; ++e) dm[e] = (dword >> (8 * (i16 & 3) + e)) & 1u;
+      value_accum_fp16<G>(page, lane, wv, dm, acc);
+    } else if constexpr (CLASS == 0) {
+      switch (vb) {
+        case 1: value_accum<1, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
+        case 2: value_accum<2, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
+        case 3: value_accum<3, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
+        default: value_accum<4, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
+      }
+    } else {
+      switch (vb) {
+        case 1: value_accum<1, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
+        case 2: value_accum<2, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
+        case 3: value_accum<3, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
+        case 4: value_accum<4, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
+        case 5: value_accum<5, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
+        case 6: value_accum<6, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
+        case 7: value_accum<7, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
+        default: value_accum<8, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
+      }
+    }
+    wave_lds_sync();
+  }
+
+  // ---- workgroup reduction: waves, then token quarters.
+#pragma clang loop unroll(full)
+  for (int h = 0; h < G; ++h) l[h] = wave_sum(l[h]);
+  if (lane == 0) {
+#pragma clang loop unroll(full)
+    for (int h = 0; h < G; ++h) {
+      sm.stat[wave][0][h] = m[h];
+      sm.stat[wave][1][h] = l[h];
+    }
+  }
+  __syncthreads();
+  float M[G];
+#pragma clang loop unroll(full)
+  for (int h = 0; h < G; ++h) {
+    M[h] = -INFINITY;
+    for (int w = 0; w < kDecodeWaves; ++w) M[h] = fmaxf(M[h], sm.stat[w][0][h]);
+  }
+  if (tid < G) {
+    const int h = tid;
+    float lsum = 0.f;
+    for (int w = 0; w < kDecodeWaves; ++w)
+      if (sm.stat[w][0][h] != -INFINITY) lsum += sm.stat[w][1][h] * exp2f(sm.stat[w][0][h] - M[h]);
+    float* ph = part + h * head_stride;
+    ph[0] = M[h];
+    ph[1] = lsum;
+  }
+#pragma clang loop unroll(full)
+  for (int h = 0; h < G; ++h) {
+    const float f = m[h] == -INFINITY ? 0.f : exp2f(m[h] - M[h]);
+#pragma clang loop unroll(full)
+    for (int e = 0; e < 8; ++e) {
+      float v = acc[h][e] * f;
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+      if (q4 == 0) sm.red[wave][h * D + 8 * i16 + e] = v;
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += blockDim.x) {
+    float v = 0.f;
+#pragma clang loop unroll(full)
+    for (int w = 0; w < kDecodeWaves; ++w) v += sm.red[w][idx];
+    const int h = idx / D, j = idx - h * D;
+    part[h * head_stride + 4 + j] = v;
+  }
+}
+
+// (3) combine: one 128-thread block per (session, query head).  The split
+// weights 2^(m_s - M) are computed once into LDS; the value sums then stream
+// with independent loads.
+__global__ __launch_bounds__(128) void combine_kernel(DecodeArgs a) {
+  __shared__ float buf[D];
+  __shared__ float wgt[kMaxPartials];
+  __shared__ float red[2];
+  const int j = threadIdx.x;
+  const int row = blockIdx.x;
+  const int b = row / a.n_q_heads;
+  const int ns = a.n_splits + a.n_splits_general;   // both page classes
+  const float* part = a.wsp + (size_t)row * ns * kPartialFloats;
+  float* o = a.out + (size_t)row * D;
+  // global max over splits
+  float mloc = -INFINITY;
+  for (int s = j; s < ns; s += D) mloc = fmaxf(mloc, part[(size_t)s * kPartialFloats]);
+  mloc = wave_max(mloc);
+  if ((j & 63) == 0) red[j >> 6] = mloc;
+  __syncthreads();
+  const float M = fmaxf(red[0], red[1]);
+  __syncthreads();
+  if (M == -INFINITY || a.n_tokens[b] <= 0) {
+    o[j] = 0.f;
+    return;
+  }
+  float lloc = 0.f;
+  for (int s = j; s < ns; s += D) {
+    const float ms = part[(size_t)s * kPartialFloats];
+    const float f = ms == -INFINITY ? 0.f : exp2f(ms - M);
+    wgt[s] = f;
+    lloc = fmaf(part[(size_t)s * kPartialFloats + 1], f, lloc);
+  }
+  lloc = wave_sum(lloc);
+  if ((j & 63) == 0) red[j >> 6] = lloc;
+  __syncthreads();
+  const float L = red[0] + red[1];
+  // value sums of the non-empty partials (an empty one may hold stale values,
+  // so its value is selected away, not multiplied by zero); eight independent
+  // loads in flight per thread
+  float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int s = 0;
+  for (; s + 8 <= ns; s += 8) {
+#pragma clang loop unroll(full)
+    for (int u = 0; u < 8; ++u) {
+      const float v = part[(size_t)(s + u) * kPartialFloats + 4 + j];
+      const float w = wgt[s + u];
+      acc8[u] = fmaf(w != 0.f ? v : 0.f, w, acc8[u]);
+    }
+  }
+  for (; s < ns; ++s) {
+    const float v = part[(size_t)s * kPartialFloats + 4 + j];
+    const float w = wgt[s];
+    acc8[0] = fmaf(w != 0.f ? v : 0.f, w, acc8[0]);
+  }
+  const float ar = ((acc8[0] + acc8[1]) + (acc8[2] + acc8[3])) + ((acc8[4] + acc8[5]) + (acc8[6] + acc8[7]));
+  const uint32_t neg = (a.sign_mask[j >> 5] >> (j & 31)) & 1u;
+  buf[j] = flip_if(ar, neg);
+  __syncthreads();
+#pragma clang loop unroll(full)
+  for (int hh = 1; hh < D; hh <<= 1) {
+    const float mine = buf[j], other = buf[j ^ hh];
+    __syncthreads();
+    buf[j] = (j & hh) ? other - mine : mine + other;
+    __syncthreads();
+  }
+  // o = D H D acc / d / L
+  o[j] = flip_if(buf[j], neg) * (1.0f / D) / L;
+}
+
+
+}  // namespace
+}  // namespace dev
+}  // namespace tq
+
+using namespace tq;
+using namespace tq::dev;
+
+extern "C" {
+
+int tq_decode_attention(const tq_layer* layer, const tq_cache* cache, const tq_query* query,
+                        float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_layer(layer);
+  if (st) return st;
+  if ((st = check_cache(cache))) return st;
+  if (!query || !query->q) return fail(TQ_ERR_INVALID_ARG, "null query");
+  if (query->dtype != TQ_DTYPE_F16 && query->dtype != TQ_DTYPE_F32)
+    return fail(TQ_ERR_INVALID_ARG, "unknown query dtype %d", query->dtype);
+  if (query->n_q_heads <= 0 || query->n_q_heads % cache->n_kv_heads)
+    return fail(TQ_ERR_INVALID_ARG, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)",
+                query->n_q_heads, cache->n_kv_heads);
+  const int G = query->n_q_heads / cache->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(TQ_ERR_UNSUPPORTED, "GQA group %d not in {1, 2, 4, 8}", G);
+  if (query->stride_b < 0 || query->stride_h < 0) return fail(TQ_ERR_INVALID_ARG, "negative stride");
+  if (!out || !workspace) return fail(TQ_ERR_INVALID_ARG, "null output or workspace");
+  if (!aligned16(out) || !aligned16(workspace)) return fail(TQ_ERR_ALIGNMENT, "out/workspace misaligned");
+  if (!(query->softmax_scale >= 0.f) || isinf(query->softmax_scale))
+    return fail(TQ_ERR_INVALID_ARG, "bad softmax scale");
+  const SplitPlan sp = split_plan(cache->n_sessions, cache->n_kv_heads, cache->max_pages);
+  if (sp.n_splits + sp.n_splits_general > kMaxPartials)   // the combine stages their weights in LDS
+    return fail(TQ_ERR_UNSUPPORTED, "%d partials per row exceed %d", sp.n_splits + sp.n_splits_general,
+                kMaxPartials);
+  const size_t need = decode_workspace_bytes(cache->n_sessions, query->n_q_heads, sp);
+  if (workspace_bytes < need)
+    return fail(TQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  DecodeArgs a;
+  a.q = query->q;
+  a.q_dtype = query->dtype;
+  a.q_sb = query->stride_b;
+  a.q_sh = query->stride_h;
+  a.n_q_heads = query->n_q_heads;
+  a.group = G;
+  const float scale = query->softmax_scale > 0.f ? query->softmax_scale : 0.08838834764831845f;
+  a.scale2 = scale * kLog2e;
+  a.n_tokens = cache->n_tokens;
+  a.n_sessions = cache->n_sessions;
+  a.n_kv_heads = cache->n_kv_heads;
+  a.max_pages = cache->max_pages;
+  a.pool = reinterpret_cast<const char*>(cache->pool);
+  a.pool_bytes = cache->pool_bytes;
+  a.sign_mask = layer->sign_mask;
+  a.k_table = layer->k_table;
+  a.v_table = layer->v_table;
+  a.qjl_s = layer->qjl_s;
+  a.n_splits = sp.n_splits;
+  a.pages_per_split = sp.pages_per_split;
+  a.n_splits_general = sp.n_splits_general;
+  a.pages_per_split_general = sp.pages_per_split_general;
+  a.wsq = reinterpret_cast<float*>(workspace);
+  a.wsp = a.wsq + (size_t)cache->n_sessions * query->n_q_heads * kQPrepFloats;
+  a.out = out;
+  hipStream_t s = (hipStream_t)stream;
+  const int rows = cache->n_sessions * query->n_q_heads;
+  hipLaunchKernelGGL(qprep_kernel, dim3(rows), dim3(128), 0, s, a);
+  if ((st = launch_status("query prep"))) return st;
+  const dim3 grid(sp.n_splits, cache->n_kv_heads, cache->n_sessions);
+  const dim3 ggrid(sp.n_splits_general, cache->n_kv_heads, cache->n_sessions);
+  const dim3 blk(64 * kDecodeWaves);
+  switch (G) {
+    case 1:
+      hipLaunchKernelGGL((split_kernel<1, 0>), grid, blk, 0, s, a, a.wsq, cache->pages, a.wsp);
+      hipLaunchKernelGGL((split_kernel<1, 1>), ggrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp);
+      break;
+    case 2:
+      hipLaunchKernelGGL((split_kernel<2, 0>), grid, blk, 0, s, a, a.wsq, cache->pages, a.wsp);
+      hipLaunchKernelGGL((split_kernel<2, 1>), ggrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp);
+      break;
+    case 4:
+      hipLaunchKernelGGL((split_kernel<4, 0>), grid, blk, 0, s, a, a.wsq, cache->pages, a.wsp);
+      hipLaunchKernelGGL((split_kernel<4, 1>), ggrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp);
+      break;
+    default:
+      hipLaunchKernelGGL((split_kernel<8, 0>), grid, blk, 0, s, a, a.wsq, cache->pages, a.wsp);
+      hipLaunchKernelGGL((split_kernel<8, 1>), ggrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp);
+      break;
+  }
+  if ((st = launch_status("split"))) return st;
+  hipLaunchKernelGGL(combine_kernel, dim3(rows), dim3(128), 0, s, a);
+  return launch_status("combine");
+}
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// Device helpers shared by the HIP translation units of libtq (gfx950, wave64).
+#ifndef TQ_DEVICE_H_
+#define TQ_DEVICE_H_
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "tq_internal.h"
+
+namespace tq {
+namespace dev {
+
+constexpr int D = TQ_HEAD_DIM;
+constexpr int PT = TQ_PAGE_TOKENS;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kSqrtHalfPi = 1.2533141373155003f;  // sqrt(pi / 2)
+constexpr int kEncodeRowBytes = 144;                 // LDS row of 128 code bytes + pad
+
+// ----------------------------------------------------------------- helpers
+__device__ __forceinline__ size_t page_size_dev(int kb, int vb, bool qjl) {
+  return kb == 0 ? (size_t)2 * PT * D * 2 : (size_t)1024 * (kb + vb) + 512 + (qjl ? 1280 : 0);
+}
+
+__device__ __forceinline__ float flip_if(float x, uint32_t neg) {
+  return __uint_as_float(__float_as_uint(x) ^ (neg << 31));
+}
+
+__device__ __forceinline__ uint32_t dsign(const uint32_t (&m)[4], int j) {
+  return (m[j >> 5] >> (j & 31)) & 1u;
+}
+
+// In-register Walsh-Hadamard transform (Sylvester order, unnormalised).
+__device__ __forceinline__ void fwht128(float (&x)[D]) {
+#pragma clang loop unroll(full)
+  for (int h = 1; h < D; h <<= 1) {
+#pragma clang loop unroll(full)
+    for (int i = 0; i < D; i += 2 * h) {
+#pragma clang loop unroll(full)
+      for (int j = i; j < i + h; ++j) {
+        const float a = x[j], b = x[j + h];
+        x[j] = a + b;
+        x[j + h] = a - b;
+      }
+    }
+  }
+}
+
+// `w` (<= 16) bits starting at bit `pos` of a little-endian dword array; with
+// the caller's loops unrolled, pos is a constant and this folds to one or two
+// instructions.
+template <int N>
+__device__ __forceinline__ uint32_t bits_at(const uint32_t (&s)[N], int pos, int w) {
+  const int wi = pos >> 5, sh = pos & 31;
+  uint32_t v = s[wi] >> sh;
+  if (sh + w > 32) v |= s[wi + 1] << (32 - sh);
+  return v & ((1u << w) - 1u);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma clang loop unroll(full)
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma clang loop unroll(full)
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Orders this wave's LDS writes before its later LDS reads.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float load_elem(const void* p, int dtype, size_t i) {
+  return dtype == TQ_DTYPE_F16 ? __half2float(reinterpret_cast<const __half*>(p)[i])
+                               : reinterpret_cast<const float*>(p)[i];
+}
+
+
+// Host helpers of the entry points.
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+inline int launch_status(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TQ_ERR_DEVICE, "%s launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace dev
+}  // namespace tq
+
+#endif  // TQ_DEVICE_H_

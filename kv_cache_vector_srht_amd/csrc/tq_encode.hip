@@ -1,0 +1,634 @@
+// Encode kernels of libtq for gfx950 (CDNA4, wave64) and tq_encode_kv.
+//
+// Encode ("TurboQuant-MLX v2.0", How It Works > Pipeline; "TurboMOQ",
+// Architecture): every 128-value head vector x is rotated by D H D, its norm is
+// stored, and each coordinate of u = D H D x / ||x|| is quantised and packed.
+// encode_pages_kernel (four lanes per vector, below) writes fp16 pages and the
+// packed keys and values of every page without a QJL residual.  encode_kernel
+// (one lane per vector) writes the keys of QJL pages: codes, norm, and the
+// signs of S r for r = x - xhat ("TurboMOQ", QJL residual correction).
+#include "tq_device.h"
+
+namespace tq {
+namespace dev {
+namespace {
+
+// ------------------------------------------------------------------ encode
+struct EncodeArgs {
+  const void* k;
+  const void* v;
+  int dtype;
+  int tok0, ntok, page0;
+  int64_t sb, sh, st;
+  int32_t* err;
+  const uint64_t* pages;
+  int n_kv_heads, max_pages;
+  char* pool;
+  uint64_t pool_bytes;
+  const uint32_t* sign_mask;
+  const float* k_table;
+  const float* v_table;
+  const float* qjl_s;
+};
+
+__device__ __forceinline__ void raise_flag(int32_t* err, int bit) {
+  if (err) atomicOr(err, bit);
+}
+
+// Loads one head vector (128 values) as float.
+__device__ __forceinline__ void load_row(const void* base, int dtype, size_t elem_off, float (&x)[D]) {
+  if (dtype == TQ_DTYPE_F16) {
+    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const __half*>(base) + elem_off);
+#pragma clang loop unroll(full)
+    for (int c = 0; c < D / 8; ++c) {
+      uint4 w = p[c];
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma clang loop unroll(full)
+      for (int e = 0; e < 4; ++e) {
+        __half2 h2 = *reinterpret_cast<const __half2*>(&ww[e]);
+        float2 f = __half22float2(h2);
+        x[8 * c + 2 * e] = f.x;
+        x[8 * c + 2 * e + 1] = f.y;
+      }
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + elem_off);
+#pragma clang loop unroll(full)
+    for (int c = 0; c < D / 4; ++c) {
+      float4 f = p[c];
+      x[4 * c] = f.x;
+      x[4 * c + 1] = f.y;
+      x[4 * c + 2] = f.z;
+      x[4 * c + 3] = f.w;
+    }
+  }
+}
+
+// Walsh-Hadamard transform of each 64-value half (stages 1..32); the last
+// stage (pairs j, j+64) is left to the caller so that it can consume outputs
+// as they are produced.
+__device__ __forceinline__ void fwht_halves(float (&x)[D]) {
+#pragma clang loop unroll(full)
+  for (int h = 1; h < D / 2; h <<= 1) {
+#pragma clang loop unroll(full)
+    for (int i = 0; i < D; i += 2 * h) {
+#pragma clang loop unroll(full)
+      for (int j = i; j < i + h; ++j) {
+        const float a = x[j], b = x[j + h];
+        x[j] = a + b;
+        x[j + h] = a - b;
+      }
+    }
+  }
+}
+
+template <int B>
+__device__ __forceinline__ uint32_t quantize(float u, const float* thr) {
+  uint32_t c = 0;
+#pragma clang loop unroll(full)
+  for (int s = 1 << (B - 1); s >= 1; s >>= 1) c += (u >= thr[c + s - 1]) ? (uint32_t)s : 0u;
+  return c;
+}
+
+// Norm, rotation and quantisation of one vector held by this lane:
+// u = D H D x / ||x||, code_j = #{k : t_k <= u_j} (binary search over the
+// boundaries in LDS).  Codes go to `emit(j, code)`; on return x holds the
+// rotated-domain residual u - c[code] (used by QJL).
+template <int B, class Emit>
+__device__ __forceinline__ float rotate_quantize(float (&x)[D], const uint32_t (&m)[4],
+                                                 const float* thr, const float* cent, Emit emit) {
+  float ss = 0.f;
+#pragma clang loop unroll(full)
+  for (int j = 0; j < D; ++j) ss = fmaf(x[j], x[j], ss);
+  const float n = sqrtf(ss);
+#pragma clang loop unroll(full)
+  for (int j = 0; j < D; ++j) x[j] = flip_if(x[j], dsign(m, j));
+  fwht_halves(x);
+  const float inv = n > 0.f ? 1.0f / n : 0.f;
+#pragma clang loop unroll(full)
+  for (int j = 0; j < D / 2; ++j) {
+    const float a = x[j], b = x[j + D / 2];
+    const float u0 = flip_if(a + b, dsign(m, j)) * inv;
+    const float u1 = flip_if(a - b, dsign(m, j + D / 2)) * inv;
+    const uint32_t c0 = quantize<B>(u0, thr);
+    const uint32_t c1 = quantize<B>(u1, thr);
+    emit(j, c0);
+    emit(j + D / 2, c1);
+    x[j] = u0 - cent[c0];
+    x[j + D / 2] = u1 - cent[c1];
+  }
+  return n;
+}
+
+template <int PART, int B>
+__device__ __forceinline__ void encode_packed(const float* __restrict__ qjl_s, char* page, bool qjl, int lane,
+                              float (&x)[D], const uint32_t (&m)[4], float* lds_thr,
+                              float* lds_cent, uint32_t* lds_rows) {
+  constexpr int kb = B;
+  if constexpr (PART == 0) {
+    uint32_t sw[4 * B];
+#pragma clang loop unroll(full)
+    for (int i = 0; i < 4 * B; ++i) sw[i] = 0;
+    const float n = rotate_quantize<B>(x, m, lds_thr, lds_cent, [&](int j, uint32_t c) {
+      const int pos = j * B, wi = pos >> 5, sh = pos & 31;
+      sw[wi] |= c << sh;
+      if (sh + B > 32) sw[wi + 1] |= c >> (32 - sh);
+    });
+    uint4* dst = reinterpret_cast<uint4*>(page);
+#pragma clang loop unroll(full)
+    for (int w = 0; w < B; ++w)
+      dst[w * 64 + lane] = make_uint4(sw[4 * w], sw[4 * w + 1], sw[4 * w + 2], sw[4 * w + 3]);
+    reinterpret_cast<float*>(page + 1024 * kb)[lane] = n;
+    if (qjl) {
+      // r = x - xhat = (n / d) D H D (u - c): one more butterfly in registers.
+      float e2 = 0.f;
+#pragma clang loop unroll(full)
+      for (int j = 0; j < D; ++j) {
+        e2 = fmaf(x[j], x[j], e2);
+        x[j] = flip_if(x[j], dsign(m, j));
+      }
+      fwht128(x);
+      const float sc = n * (1.0f / D);
+#pragma clang loop unroll(full)
+      for (int j = 0; j < D; ++j) x[j] = flip_if(x[j], dsign(m, j)) * sc;
+      const float gamma = n * sqrtf(e2) * 0.08838834764831845f;  // n ||u - c|| / sqrt(d)
+      uint32_t zw[4];
+#pragma clang loop unroll(full)
+      for (int w = 0; w < 4; ++w) {
+        uint32_t bitsw = 0;
+        for (int ii = 0; ii < 32; ++ii) {
+          const float* srow = qjl_s + (size_t)(32 * w + ii) * D;
+          float p = 0.f;
+#pragma clang loop unroll(full)
+          for (int j = 0; j < D; ++j) p = fmaf(srow[j], x[j], p);
+          bitsw |= (p >= 0.f ? 1u : 0u) << ii;
+        }
+        zw[w] = bitsw;
+      }
+      char* qbase = page + 1024 * kb + 256;
+      reinterpret_cast<uint4*>(qbase)[lane] = make_uint4(zw[0], zw[1], zw[2], zw[3]);
+      reinterpret_cast<float*>(qbase + 1024)[lane] = gamma;
+    }
+  } else {
+    // Codes as bytes into this lane's LDS row, then transpose into V streams.
+    uint32_t cb[D / 4];
+#pragma clang loop unroll(full)
+    for (int i = 0; i < D / 4; ++i) cb[i] = 0;
+    const float n = rotate_quantize<B>(x, m, lds_thr, lds_cent, [&](int j, uint32_t c) {
+      cb[j >> 2] |= c << (8 * (j & 3));
+    });
+    uint4* row = reinterpret_cast<uint4*>(reinterpret_cast<char*>(lds_rows) + lane * kEncodeRowBytes);
+#pragma clang loop unroll(full)
+    for (int i = 0; i < D / 16; ++i) row[i] = make_uint4(cb[4 * i], cb[4 * i + 1], cb[4 * i + 2], cb[4 * i + 3]);
+    __syncthreads();
+    const int q = lane >> 4, ii = lane & 15;
+    uint32_t sw[4 * B];
+#pragma clang loop unroll(full)
+    for (int i = 0; i < 4 * B; ++i) sw[i] = 0;
+#pragma clang loop unroll(full)
+    for (int k = 0; k < 16; ++k) {
+      const uint2 b8 = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(lds_rows) +
+                                                        (4 * k + q) * kEncodeRowBytes + 8 * ii);
+#pragma clang loop unroll(full)
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t c = ((e < 4 ? b8.x : b8.y) >> (8 * (e & 3))) & 0xffu;
+        const int pos = (8 * k + e) * B, wi = pos >> 5, sh = pos & 31;
+        sw[wi] |= c << sh;
+        if (sh + B > 32) sw[wi + 1] |= c >> (32 - sh);
+      }
+    }
+    uint4* dst = reinterpret_cast<uint4*>(page);
+#pragma clang loop unroll(full)
+    for (int w = 0; w < B; ++w)
+      dst[w * 64 + lane] = make_uint4(sw[4 * w], sw[4 * w + 1], sw[4 * w + 2], sw[4 * w + 3]);
+    reinterpret_cast<float*>(page + 1024 * B)[lane] = n;
+  }
+}
+
+// One wavefront per (page, KV head, session); PART 0 encodes keys, 1 values.
+template <int PART>
+__global__ __launch_bounds__(64) void encode_kernel(EncodeArgs a, const uint64_t* __restrict__ pages,
+                                                    const float* __restrict__ qjl_s) {
+  __shared__ float lds_thr[256];
+  __shared__ float lds_cent[256];
+  __shared__ uint32_t lds_rows[PT * kEncodeRowBytes / 4];
+  const int lane = threadIdx.x;
+  const int pg = a.page0 + blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  constexpr int part = PART;
+  const uint64_t desc = pages[((size_t)b * a.n_kv_heads + h) * a.max_pages + pg];
+  if (!(desc & TQ_PAGE_PRESENT)) {
+    if (lane == 0) raise_flag(a.err, 2);
+    return;
+  }
+  const int kb = (int)((desc >> 48) & 15), vb = (int)((desc >> 52) & 15);
+  const bool qjl = (desc & TQ_PAGE_QJL) != 0;
+  const uint64_t off = desc & TQ_PAGE_OFFSET_MASK;
+  const bool bad_fmt = kb == 0 ? (vb != 0 || qjl) : (kb > 8 || vb < 1 || vb > 8);
+  if (bad_fmt || off + page_size_dev(kb, vb, qjl) > a.pool_bytes) {
+    if (lane == 0) raise_flag(a.err, 4);
+    return;
+  }
+  char* page = a.pool + off;
+  const int t_first = pg * PT;
+  const int lo = max(t_first, a.tok0), hi = min(t_first + PT, a.tok0 + a.ntok);
+  const void* src = part == 0 ? a.k : a.v;
+  const size_t base = (size_t)b * a.sb + (size_t)h * a.sh;
+
+  if (kb == 0) {
+    // fp16 page: copy the covered rows of this part, 4 rows per pass.
+    __half* dst = reinterpret_cast<__half*>(page + part * PT * D * 2);
+    const int r = lane >> 4, c8 = (lane & 15) * 8;
+    for (int t = lo + r; t < hi; t += 4) {
+      const size_t e = base + (size_t)(t - a.tok0) * a.st + c8;
+      uint4 out;
+      if (a.dtype == TQ_DTYPE_F16) {
+        out = *reinterpret_cast<const uint4*>(reinterpret_cast<const __half*>(src) + e);
+      } else {
+        const float4 f0 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(src) + e);
+        const float4 f1 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(src) + e + 4);
+        __half2 h0 = __floats2half2_rn(f0.x, f0.y), h1 = __floats2half2_rn(f0.z, f0.w);
+        __half2 h2 = __floats2half2_rn(f1.x, f1.y), h3 = __floats2half2_rn(f1.z, f1.w);
+        out = make_uint4(*reinterpret_cast<uint32_t*>(&h0), *reinterpret_cast<uint32_t*>(&h1),
+                         *reinterpret_cast<uint32_t*>(&h2), *reinterpret_cast<uint32_t*>(&h3));
+      }
+      *reinterpret_cast<uint4*>(dst + (size_t)(t - t_first) * D + c8) = out;
+    }
+    return;
+  }
+  if (lo != t_first || hi != t_first + PT) {
+    if (lane == 0) raise_flag(a.err, 1);
+    return;
+  }
+  if (part == 0 && qjl && a.qjl_s == nullptr) {
+    if (lane == 0) raise_flag(a.err, 8);
+    return;
+  }
+  if (part == 0 && !qjl) return;   // non-QJL key pages are written by encode_pages_kernel
+  const int B = part == 0 ? kb : vb;
+  const float* table = part == 0 ? a.k_table : a.v_table;
+  const int L = 1 << B;
+  for (int i = lane; i < L; i += 64) {
+    lds_cent[i] = table[centroid_offset(B) + i];
+    if (i < L - 1) lds_thr[i] = table[boundary_offset(B) + i];
+  }
+  uint32_t m[4];
+#pragma clang loop unroll(full)
+  for (int w = 0; w < 4; ++w) m[w] = a.sign_mask[w];
+  float x[D];
+  load_row(src, a.dtype, base + (size_t)(t_first + lane - a.tok0) * a.st, x);
+  __syncthreads();
+  char* part_base = part == 0 ? page : page + 1024 * kb + 256 + (qjl ? 1280 : 0);
+  switch (B) {
+    case 1: encode_packed<PART, 1>(qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+    case 2: encode_packed<PART, 2>(qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+    case 3: encode_packed<PART, 3>(qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+    case 4: encode_packed<PART, 4>(qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+    case 5: encode_packed<PART, 5>(qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+    case 6: encode_packed<PART, 6>(qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+    case 7: encode_packed<PART, 7>(qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+    default: encode_packed<PART, 8>(qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+  }
+}
+
+// ------------------------------------------------------- encode (quad lanes)
+// One 256-thread block per (range of pages, KV head, session), keys and values.
+// A lane quad holds one token's vector, 32 values per lane: lane e of the quad
+// owns coordinates 32c + 8e + k (c = 0..3, k = 0..7), loaded as four 16-byte
+// chunks so that a wave's loads cover whole 64-byte row segments.  The
+// Walsh-Hadamard transform runs over coordinate bits {0,1,2,5,6} inside the
+// lane and over bits {3,4} across the quad (DPP quad permutations).
+//
+// Codes of u = H D x / ||x|| come from the width's lookup grid in LDS
+// (code = count below the bin + [u >= the bin's boundary]), so one code path
+// serves every width.  The outer D is applied afterwards as a code flip:
+// exact, because the float32 boundary sets are symmetric
+// (code(-u) = L-1-code(u) except at exact ties, which lie inside the boundary
+// allowance).  Codes go to an LDS byte matrix [token][coordinate]; each lane
+// then packs 32 consecutive codes of one stream (exactly b dwords) with a
+// streaming accumulator whose flush points are uniform.
+constexpr int kRowStride = 144;            // LDS byte-matrix row: 128 codes + pad
+constexpr int kEncodeBlock = 256;
+constexpr int kEncodePagesPerBlock = 8;
+
+__device__ __forceinline__ float quad_swap(float v, int m) {
+  // partner lane = lane ^ m inside the quad; m is a compile-time 1 or 2 after unrolling
+  return m == 1 ? __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false))
+                : __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+
+struct Lut {
+  float S, O;
+  int nb;
+};
+
+struct EncodeLane {
+  uint32_t hmask[16];   // D sign bits of the lane's value pairs, placed for an fp16x2 xor
+  uint32_t fmask[8];    // per code byte: 0xff when the outer D flips that coordinate
+  uint32_t dl;          // D bits of the lane's 32 slots
+};
+
+// Encodes this lane's quarter of one token into code bytes of its LDS matrix
+// row; returns the vector norm (the same in the four lanes of the quad).
+template <int DT>
+__device__ __forceinline__ float encode_quarter(const void* src, size_t row_off, int e,
+                                                const EncodeLane& el, int B, const Lut& lut,
+                                                const uint2* ent, uint32_t* mat_row) {
+  float x[32];
+  if constexpr (DT == TQ_DTYPE_F16) {
+    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const __half*>(src) + row_off);
+#pragma clang loop unroll(full)
+    for (int c = 0; c < 4; ++c) {
+      const uint4 w = p[4 * c + e];
+      const uint32_t ww[4] = {w.x ^ el.hmask[4 * c], w.y ^ el.hmask[4 * c + 1],
+                              w.z ^ el.hmask[4 * c + 2], w.w ^ el.hmask[4 * c + 3]};
+#pragma clang loop unroll(full)
+      for (int kk = 0; kk < 4; ++kk) {
+        const float2 f = __half22float2(*reinterpret_cast<const __half2*>(&ww[kk]));
+        x[8 * c + 2 * kk] = f.x;
+        x[8 * c + 2 * kk + 1] = f.y;
+      }
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(src) + row_off);
+#pragma clang loop unroll(full)
+    for (int c = 0; c < 4; ++c) {
+      const float4 f0 = p[2 * (4 * c + e)], f1 = p[2 * (4 * c + e) + 1];
+      const float v[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+#pragma clang loop unroll(full)
+      for (int k = 0; k < 8; ++k) x[8 * c + k] = flip_if(v[k], (el.dl >> (8 * c + k)) & 1u);
+    }
+  }
+  float ss = 0.f;
+#pragma clang loop unroll(full)
+  for (int s = 0; s < 32; ++s) ss = fmaf(x[s], x[s], ss);
+  ss += quad_swap(ss, 1);
+  ss += quad_swap(ss, 2);
+  // in-lane butterflies over slot bits 0..4 (coordinate bits 0,1,2,5,6)
+#pragma clang loop unroll(full)
+  for (int h = 1; h < 32; h <<= 1)
+#pragma clang loop unroll(full)
+    for (int s = 0; s < 32; ++s)
+      if (!(s & h)) {
+        const float a0 = x[s], b0 = x[s + h];
+        x[s] = a0 + b0;
+        x[s + h] = a0 - b0;
+      }
+  // across the quad: coordinate bits 3 (lane bit 0) and 4 (lane bit 1)
+#pragma clang loop unroll(full)
+  for (int m = 1; m <= 2; m <<= 1) {
+    const float sg = (e & m) ? -1.f : 1.f;
+#pragma clang loop unroll(full)
+    for (int s = 0; s < 32; ++s) x[s] = fmaf(x[s], sg, quad_swap(x[s], m));
+  }
+  const float n = sqrtf(ss);
+  const float inv = n > 0.f ? 1.0f / n : 0.f;
+  uint32_t cb[8];
+#pragma clang loop unroll(full)
+  for (int i = 0; i < 8; ++i) cb[i] = 0;
+#pragma clang loop unroll(full)
+  for (int s = 0; s < 32; ++s) {
+    const float u = x[s] * inv;
+    const int bin = min(max((int)fmaf(u, lut.S, lut.O), 0), lut.nb - 1);
+    const uint2 en = ent[bin];
+    const uint32_t c = en.x + (u >= __uint_as_float(en.y) ? 1u : 0u);
+    cb[s >> 2] |= c << (8 * (s & 3));
+  }
+  const uint32_t flip = ((1u << B) - 1u) * 0x01010101u;
+  // chunk c holds coordinates 32c + 8e .. +7: row bytes 32c + 8e
+#pragma clang loop unroll(full)
+  for (int c = 0; c < 4; ++c) {
+    const uint2 v = make_uint2(cb[2 * c] ^ (el.fmask[2 * c] & flip), cb[2 * c + 1] ^ (el.fmask[2 * c + 1] & flip));
+    *reinterpret_cast<uint2*>(reinterpret_cast<char*>(mat_row) + 32 * c + 8 * e) = v;
+  }
+  return n;
+}
+
+// Writes dwords [e*B, e*B + B) of stream s of a code block from its codes
+// 32e..32e+31 (bytes of c8), LSB-first.
+__device__ __forceinline__ void store_stream_part(int B, char* blk, int s, int e, const uint32_t (&c8)[8]) {
+  uint64_t acc = 0;
+  int nb = 0, d = e * B;
+#pragma clang loop unroll(full)
+  for (int n = 0; n < 32; ++n) {
+    acc |= (uint64_t)((c8[n >> 2] >> (8 * (n & 3))) & 0xffu) << nb;
+    nb += B;
+    if (nb >= 32) {
+      reinterpret_cast<uint32_t*>(blk + ((d >> 2) * 64 + s) * 16)[d & 3] = (uint32_t)acc;
+      acc >>= 32;
+      nb -= 32;
+      ++d;
+    }
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kEncodeBlock) void encode_pages_kernel(EncodeArgs a,
+                                                                    const uint64_t* __restrict__ pages) {
+  __shared__ uint2 entk[kLutMaxBins], entv[kLutMaxBins];
+  __shared__ uint32_t matk[PT * kRowStride / 4], matv[PT * kRowStride / 4];
+  __shared__ float normk[PT], normv[PT];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int e = lane & 3, t = wave * 16 + (lane >> 2);
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int pg0 = a.page0 + blockIdx.x * kEncodePagesPerBlock;
+  const int pg_last = (a.tok0 + a.ntok - 1) / PT;
+
+  EncodeLane el;
+  {
+    uint32_t m[4];
+#pragma clang loop unroll(full)
+    for (int w = 0; w < 4; ++w) m[w] = a.sign_mask[w];
+    el.dl = 0;
+#pragma clang loop unroll(full)
+    for (int c = 0; c < 4; ++c) el.dl |= ((m[c] >> (8 * e)) & 0xffu) << (8 * c);
+#pragma clang loop unroll(full)
+    for (int i = 0; i < 16; ++i)
+      el.hmask[i] = (((el.dl >> (2 * i)) & 1u) << 15) | (((el.dl >> (2 * i + 1)) & 1u) << 31);
+#pragma clang loop unroll(full)
+    for (int i = 0; i < 8; ++i) {
+      uint32_t f = 0;
+#pragma clang loop unroll(full)
+      for (int k = 0; k < 4; ++k) f |= ((el.dl >> (4 * i + k)) & 1u) ? (0xffu << (8 * k)) : 0u;
+      el.fmask[i] = f;
+    }
+  }
+  int cur_kb = -1, cur_vb = -1;
+  Lut lk{0.f, 0.f, 1}, lv{0.f, 0.f, 1};
+  const size_t base = (size_t)b * a.sb + (size_t)h * a.sh;
+  const uint64_t* prow = pages + ((size_t)b * a.n_kv_heads + h) * a.max_pages;
+
+  for (int pg = pg0; pg < pg0 + kEncodePagesPerBlock && pg <= pg_last; ++pg) {
+    const uint64_t desc = prow[pg];
+    if (!(desc & TQ_PAGE_PRESENT)) {
+      if (tid == 0) raise_flag(a.err, 2);
+      continue;
+    }
+    const int kb = (int)((desc >> 48) & 15), vb = (int)((desc >> 52) & 15);
+    const bool qjl = (desc & TQ_PAGE_QJL) != 0;
+    const uint64_t off = desc & TQ_PAGE_OFFSET_MASK;
+    const bool bad_fmt = kb == 0 ? (vb != 0 || qjl) : (kb > 8 || vb < 1 || vb > 8);
+    if (bad_fmt || off + page_size_dev(kb, vb, qjl) > a.pool_bytes) {
+      if (tid == 0) raise_flag(a.err, 4);
+      continue;
+    }
+    char* page = a.pool + off;
+    const int t_first = pg * PT;
+    const int lo = max(t_first, a.tok0), hi = min(t_first + PT, a.tok0 + a.ntok);
+    if (kb == 0) {
+      // fp16 page: copy the covered rows of K then V, 16 bytes per thread and pass
+      for (int idx = tid; idx < 2 * PT * 16; idx += kEncodeBlock) {
+        const int part = idx >> 10, r = (idx >> 4) & 63, c8 = (idx & 15) * 8;
+        const int tok = t_first + r;
+        if (tok < lo || tok >= hi) continue;
+        const void* src = part == 0 ? a.k : a.v;
+        const size_t ee = base + (size_t)(tok - a.tok0) * a.st + c8;
+        uint4 out;
+        if constexpr (DT == TQ_DTYPE_F16) {
+          out = *reinterpret_cast<const uint4*>(reinterpret_cast<const __half*>(src) + ee);
+        } else {
+          const float4 f0 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(src) + ee);
+          const float4 f1 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(src) + ee + 4);
+          __half2 h0 = __floats2half2_rn(f0.x, f0.y), h1 = __floats2half2_rn(f0.z, f0.w);
+          __half2 h2 = __floats2half2_rn(f1.x, f1.y), h3 = __floats2half2_rn(f1.z, f1.w);
+          out = make_uint4(*reinterpret_cast<uint32_t*>(&h0), *reinterpret_cast<uint32_t*>(&h1),
+                           *reinterpret_cast<uint32_t*>(&h2), *reinterpret_cast<uint32_t*>(&h3));
+        }
+        *reinterpret_cast<uint4*>(page + part * PT * D * 2 + ((size_t)r * D + c8) * 2) = out;
+      }
+      continue;
+    }
+    if (lo != t_first || hi != t_first + PT) {
+      if (tid == 0) raise_flag(a.err, 1);
+      continue;
+    }
+    // stage the lookup grids when the widths change (uniform branch)
+    if (kb != cur_kb || vb != cur_vb) {
+      __syncthreads();
+      const float* hk = a.k_table + kLutHeaderOffset + 4 * (kb - 1);
+      const float* hv = a.v_table + kLutHeaderOffset + 4 * (vb - 1);
+      lk = Lut{hk[0], hk[1], min((int)__float_as_uint(hk[2]), kLutMaxBins)};
+      lv = Lut{hv[0], hv[1], min((int)__float_as_uint(hv[2]), kLutMaxBins)};
+      const uint2* sk = reinterpret_cast<const uint2*>(a.k_table + __float_as_uint(hk[3]));
+      const uint2* sv = reinterpret_cast<const uint2*>(a.v_table + __float_as_uint(hv[3]));
+      for (int i = tid; i < lk.nb; i += kEncodeBlock) entk[i] = sk[i];
+      for (int i = tid; i < lv.nb; i += kEncodeBlock) entv[i] = sv[i];
+      cur_kb = kb;
+      cur_vb = vb;
+      __syncthreads();
+    }
+    const size_t row_off = base + (size_t)(t_first + t - a.tok0) * a.st;
+    uint32_t* rowk = matk + t * (kRowStride / 4);
+    uint32_t* rowv = matv + t * (kRowStride / 4);
+    // QJL key pages are written by the per-token kernel (codes + sketch)
+    const float nk = qjl ? 0.f : encode_quarter<DT>(a.k, row_off, e, el, kb, lk, entk, rowk);
+    const float nv = encode_quarter<DT>(a.v, row_off, e, el, vb, lv, entv, rowv);
+    if (e == 0) {
+      normk[t] = nk;
+      normv[t] = nv;
+    }
+    __syncthreads();
+    // pack: lane (stream s, part e) writes dwords [e*B, e*B+B) of stream s
+    char* vblk = page + 1024 * kb + 256 + (qjl ? 1280 : 0);
+    const int s = t;
+    if (!qjl) {
+      // K stream s = token s: codes 32e..32e+31 are bytes 32e.. of row s
+      const char* r = reinterpret_cast<const char*>(matk + s * (kRowStride / 4)) + 32 * e;
+      const uint4 c0 = *reinterpret_cast<const uint4*>(r);
+      const uint4 c1 = *reinterpret_cast<const uint4*>(r + 16);
+      const uint32_t c8[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      store_stream_part(kb, page, s, e, c8);
+    }
+    {
+      // V stream s = 16q + i: positions 8k + j (k = 4e..4e+3) = token 4k+q, coordinate 8i+j
+      const int q = s >> 4, i = s & 15;
+      uint32_t c8[8];
+#pragma clang loop unroll(full)
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint2 v = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(matv) +
+                                                        (4 * (4 * e + kk) + q) * kRowStride + 8 * i);
+        c8[2 * kk] = v.x;
+        c8[2 * kk + 1] = v.y;
+      }
+      store_stream_part(vb, vblk, s, e, c8);
+    }
+    if (e == 0) {
+      if (!qjl) reinterpret_cast<float*>(page + 1024 * kb)[s] = normk[s];
+      reinterpret_cast<float*>(vblk + 1024 * vb)[s] = normv[s];
+    }
+    __syncthreads();
+  }
+}
+
+
+}  // namespace
+}  // namespace dev
+}  // namespace tq
+
+using namespace tq;
+using namespace tq::dev;
+
+extern "C" {
+
+int tq_encode_kv(const tq_layer* layer, const tq_cache* cache, const tq_kv_input* in, void* stream) {
+  int st = check_layer(layer);
+  if (st) return st;
+  if ((st = check_cache(cache))) return st;
+  if (!in || !in->k || !in->v) return fail(TQ_ERR_INVALID_ARG, "null input");
+  if (in->dtype != TQ_DTYPE_F16 && in->dtype != TQ_DTYPE_F32)
+    return fail(TQ_ERR_INVALID_ARG, "unknown input dtype %d", in->dtype);
+  if (in->ntok < 1 || in->tok0 < 0) return fail(TQ_ERR_INVALID_ARG, "bad token range");
+  if (in->tok0 % TQ_PAGE_TOKENS) return fail(TQ_ERR_INVALID_ARG, "tok0 must be a multiple of 64");
+  if ((int64_t)in->tok0 + in->ntok > (int64_t)cache->max_pages * TQ_PAGE_TOKENS)
+    return fail(TQ_ERR_INVALID_ARG, "token range past the page table");
+  if (in->stride_b < 0 || in->stride_h < 0 || in->stride_t < 0)
+    return fail(TQ_ERR_INVALID_ARG, "negative stride");
+  const int esz = in->dtype == TQ_DTYPE_F16 ? 2 : 4;
+  if (!aligned16(in->k) || !aligned16(in->v) || (in->stride_b * esz) % 16 ||
+      (in->stride_h * esz) % 16 || (in->stride_t * esz) % 16)
+    return fail(TQ_ERR_ALIGNMENT, "input rows must be 16-byte aligned");
+  if (((uintptr_t)in->error_flags & 3) != 0) return fail(TQ_ERR_ALIGNMENT, "error_flags misaligned");
+  EncodeArgs a;
+  a.k = in->k;
+  a.v = in->v;
+  a.dtype = in->dtype;
+  a.tok0 = in->tok0;
+  a.ntok = in->ntok;
+  a.page0 = in->tok0 / TQ_PAGE_TOKENS;
+  a.sb = in->stride_b;
+  a.sh = in->stride_h;
+  a.st = in->stride_t;
+  a.err = in->error_flags;
+  a.pages = cache->pages;
+  a.n_kv_heads = cache->n_kv_heads;
+  a.max_pages = cache->max_pages;
+  a.pool = reinterpret_cast<char*>(cache->pool);
+  a.pool_bytes = cache->pool_bytes;
+  a.sign_mask = layer->sign_mask;
+  a.k_table = layer->k_table;
+  a.v_table = layer->v_table;
+  a.qjl_s = layer->qjl_s;
+  const int last_page = (in->tok0 + in->ntok - 1) / TQ_PAGE_TOKENS;
+  const int n_pages = last_page - a.page0 + 1;
+  dim3 grid((n_pages + kEncodePagesPerBlock - 1) / kEncodePagesPerBlock, cache->n_kv_heads,
+            cache->n_sessions);
+  if (a.dtype == TQ_DTYPE_F16)
+    hipLaunchKernelGGL(encode_pages_kernel<TQ_DTYPE_F16>, grid, dim3(kEncodeBlock), 0,
+                       (hipStream_t)stream, a, cache->pages);
+  else
+    hipLaunchKernelGGL(encode_pages_kernel<TQ_DTYPE_F32>, grid, dim3(kEncodeBlock), 0,
+                       (hipStream_t)stream, a, cache->pages);
+  int st2 = launch_status("encode");
+  if (st2) return st2;
+  if (layer->qjl_s) {
+    // keys of QJL pages: codes, norm and sign sketch, one wavefront per page
+    dim3 qgrid(n_pages, cache->n_kv_heads, cache->n_sessions);
+    hipLaunchKernelGGL(encode_kernel<0>, qgrid, dim3(64), 0, (hipStream_t)stream, a, cache->pages,
+                       layer->qjl_s);
+    st2 = launch_status("encode QJL keys");
+  }
+  return st2;
+}
+
+}  // extern "C"

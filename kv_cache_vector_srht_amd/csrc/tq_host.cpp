@@ -297,7 +297,7 @@ size_t tq_decode_workspace_bytes(const tq_cache* cache, int n_q_heads) {
       n_q_heads <= 0)
     return 0;
   SplitPlan sp = split_plan(cache->n_sessions, cache->n_kv_heads, cache->max_pages);
-  return decode_workspace_bytes(cache->n_sessions, n_q_heads, sp.n_splits);
+  return decode_workspace_bytes(cache->n_sessions, n_q_heads, sp);
 }
 
 }  // extern "C"
@@ -315,12 +315,16 @@ SplitPlan split_plan(int n_sessions, int n_kv_heads, int max_pages) {
   SplitPlan sp;
   sp.pages_per_split = (int)pps;
   sp.n_splits = (int)((max_pages + pps - 1) / pps);
+  sp.pages_per_split_general = (sp.pages_per_split + 3) / 4;
+  sp.n_splits_general = (max_pages + sp.pages_per_split_general - 1) / sp.pages_per_split_general;
   return sp;
 }
 
-size_t decode_workspace_bytes(int n_sessions, int n_q_heads, int n_splits) {
+size_t decode_workspace_bytes(int n_sessions, int n_q_heads, const SplitPlan& sp) {
   const size_t rows = (size_t)n_sessions * n_q_heads;
-  return sizeof(float) * rows * (kQPrepFloats + (size_t)n_splits * kPartialFloats);
+  // query prep, then the partials of both page classes
+  return sizeof(float) * rows *
+         (kQPrepFloats + (size_t)(sp.n_splits + sp.n_splits_general) * kPartialFloats);
 }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }

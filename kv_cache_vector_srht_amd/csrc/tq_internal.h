@@ -27,13 +27,19 @@ constexpr int kDecodeWaves = 4;             // waves per split workgroup
 constexpr int kTargetSplitGroups = 1024;    // workgroups the split grid aims for
 constexpr int kQPrepFloats = 3 * 128;       // rotated q, plain q, S q (all pre-scaled)
 constexpr int kPartialFloats = 4 + 128;     // m, l, (pad), acc[128]
+constexpr int kMaxPartials = 5120;          // partials per (session, query head), both classes
 
+// Split-K geometry: the common page class uses n_splits ranges of
+// pages_per_split pages; the general class (fp16, 5-8 bits, QJL; heavier per
+// page and usually rarer) uses ranges a quarter as long.
 struct SplitPlan {
   int n_splits;
   int pages_per_split;
+  int n_splits_general;
+  int pages_per_split_general;
 };
 SplitPlan split_plan(int n_sessions, int n_kv_heads, int max_pages);
-size_t decode_workspace_bytes(int n_sessions, int n_q_heads, int n_splits);
+size_t decode_workspace_bytes(int n_sessions, int n_q_heads, const SplitPlan& sp);
 
 // Validation shared by the device entry points (host only, before any HIP call).
 int check_layer(const tq_layer* layer);
