@@ -234,6 +234,121 @@ __device__ __forceinline__ void value_accum(const char* blk, int lane, const flo
   }
 }
 
+// Key scores of a packed page at 5-8 bits.  These widths are rare (a few
+// important heads), so the code is kept short instead of fully unrolled: four
+// passes over 32 coordinates each, whose codes fill exactly B dwords of the
+// lane's stream (dwords B n .. B n + B - 1).
+template <int B, int G>
+__device__ __forceinline__ void key_scores_wide(const char* blk, int lane, const float* __restrict__ qr,
+                                                const float* cent, float (&s)[G]) {
+  constexpr int CH = 4;                       // coordinates per chunk, pipelined as in key_scores
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(blk);
+  const float* ct = cent + centroid_offset(B);
+#pragma clang loop unroll(full)
+  for (int h = 0; h < G; ++h) s[h] = 0.f;
+  // pass n + 1's dwords are loaded while pass n computes (the last pass
+  // reloads its own, harmlessly)
+  uint32_t w[B], nx[B];
+  auto load = [&](int n, uint32_t (&d)[B]) {
+#pragma clang loop unroll(full)
+    for (int i = 0; i < B; ++i) {
+      const int dd = B * n + i;
+      d[i] = src[((dd >> 2) * 64 + lane) * 4 + (dd & 3)];
+    }
+  };
+  load(0, w);
+#pragma clang loop unroll(disable)
+  for (int n = 0; n < 4; ++n) {
+    load(min(n + 1, 3), nx);
+    const float* qn = qr + 32 * G * n;
+    float qa[G][CH], qb[G][CH], ca[CH], cb[CH];
+    auto fetch = [&](int c, float (&qd)[G][CH], float (&cd)[CH]) {
+#pragma clang loop unroll(full)
+      for (int h = 0; h < G; ++h)
+#pragma clang loop unroll(full)
+        for (int e = 0; e < CH; ++e) qd[h][e] = qn[(c * G + h) * CH + e];
+#pragma clang loop unroll(full)
+      for (int e = 0; e < CH; ++e) cd[e] = ct[bits_at(w, (c * CH + e) * B, B)];
+    };
+    auto fmas = [&](const float (&qd)[G][CH], const float (&cd)[CH], int e0, int e1) {
+#pragma clang loop unroll(full)
+      for (int e = e0; e < e1; ++e)
+#pragma clang loop unroll(full)
+        for (int h = 0; h < G; ++h) s[h] = fmaf(qd[h][e], cd[e], s[h]);
+    };
+    fetch(0, qa, ca);
+#pragma clang loop unroll(full)
+    for (int c = 0; c < 32 / CH; c += 2) {
+      fmas(qa, ca, 0, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      fetch(c + 1, qb, cb);
+      __builtin_amdgcn_sched_barrier(0);
+      fmas(qa, ca, 1, CH);
+      fmas(qb, cb, 0, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (c + 2 < 32 / CH) fetch(c + 2, qa, ca);
+      __builtin_amdgcn_sched_barrier(0);
+      fmas(qb, cb, 1, CH);
+    }
+#pragma clang loop unroll(full)
+    for (int i = 0; i < B; ++i) w[i] = nx[i];
+  }
+}
+
+// Value accumulation of a packed page at 5-8 bits, in the same four passes:
+// pass n holds tokens 4k + q for k = 4n .. 4n + 3.
+template <int B, int G>
+__device__ __forceinline__ void value_accum_wide(const char* blk, int lane, const float* wv,
+                                                 const float* cent, float (&acc)[G][8]) {
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(blk);
+  const float* ct = cent + centroid_offset(B);
+  const int q = lane >> 4;
+  uint32_t w[B], nx[B];
+  auto load = [&](int n, uint32_t (&d)[B]) {
+#pragma clang loop unroll(full)
+    for (int i = 0; i < B; ++i) {
+      const int dd = B * n + i;
+      d[i] = src[((dd >> 2) * 64 + lane) * 4 + (dd & 3)];
+    }
+  };
+  load(0, w);
+#pragma clang loop unroll(disable)
+  for (int n = 0; n < 4; ++n) {
+    load(min(n + 1, 3), nx);
+    // one token's weights and codes in flight while the previous one's FMAs run
+    float wa[G], wb[G], ca[8], cb[8];
+    auto fetch = [&](int kk, float (&wd)[G], float (&cd)[8]) {
+#pragma clang loop unroll(full)
+      for (int h = 0; h < G; ++h) wd[h] = wv[(4 * (4 * n + kk) + q) * G + h];
+#pragma clang loop unroll(full)
+      for (int e = 0; e < 8; ++e) cd[e] = ct[bits_at(w, (8 * kk + e) * B, B)];
+    };
+    auto fmas = [&](const float (&wd)[G], const float (&cd)[8]) {
+#pragma clang loop unroll(full)
+      for (int e = 0; e < 8; ++e)
+#pragma clang loop unroll(full)
+        for (int h = 0; h < G; ++h) acc[h][e] = fmaf(wd[h], cd[e], acc[h][e]);
+    };
+    fetch(0, wa, ca);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(1, wb, cb);
+    __builtin_amdgcn_sched_barrier(0);
+    fmas(wa, ca);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(2, wa, ca);
+    __builtin_amdgcn_sched_barrier(0);
+    fmas(wb, cb);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(3, wb, cb);
+    __builtin_amdgcn_sched_barrier(0);
+    fmas(wa, ca);
+    __builtin_amdgcn_sched_barrier(0);
+    fmas(wb, cb);
+#pragma clang loop unroll(full)
+    for (int i = 0; i < B; ++i) w[i] = nx[i];
+  }
+}
+
 // Value accumulation of an fp16 page into the rotated-domain sums: each token's
 // row is rotated with the unnormalised D H D (the 16 lanes of a quarter hold
 // its 128 values, 8 each), so that D H D acc / d at the end returns sum p v.
@@ -309,8 +424,8 @@ __device__ __forceinline__ void softmax_update(float (&s)[G], float (&m)[G], flo
 
 // Page classes: the common packed formats (k_bits, v_bits <= 4, no QJL) run
 // in a kernel compiled for them alone (fewer registers, more waves in flight);
-// every other page (fp16, 5-8 bits, QJL) runs in the general kernel.  Each
-// writes its own partials; the combine merges both.
+// the rest (fp16 pages, 5-8 bit codes, QJL keys) runs in the general kernel.
+// Each writes its own partials; the combine merges both.
 __device__ __forceinline__ bool common_page(int kb, int vb, bool qjl) {
   return kb >= 1 && kb <= 4 && vb >= 1 && vb <= 4 && !qjl;
 }
@@ -336,14 +451,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
   const int p_end = min(npages, p_begin + pps);
   const uint64_t* ptab = pages + ((size_t)b * a.n_kv_heads + hkv) * a.max_pages;
   {
-    // nothing of this class in the range: an empty partial, no setup
-    bool any = false;
-    for (int p = p_begin; p < p_end && !any; ++p) {
+    // nothing of this class in the range: an empty partial, no setup (the
+    // descriptors are read in parallel, one per thread)
+    bool mine = false;
+    for (int p = p_begin + tid; p < p_end; p += blockDim.x) {
       const uint64_t desc = ptab[p];
       const int kb = (int)((desc >> 48) & 15), vb = (int)((desc >> 52) & 15);
-      any = common_page(kb, vb, (desc & TQ_PAGE_QJL) != 0) == (CLASS == 0);
+      mine |= common_page(kb, vb, (desc & TQ_PAGE_QJL) != 0) == (CLASS == 0);
     }
-    if (!any) {
+    if (!__syncthreads_or(mine)) {
       if (tid < G) {
         part[tid * head_stride] = -INFINITY;
         part[tid * head_stride + 1] = 0.f;
@@ -410,10 +526,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
           case 2: key_scores<2, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
           case 3: key_scores<3, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
           case 4: key_scores<4, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
-          case 5: key_scores<5, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
-          case 6: key_scores<6, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
-          case 7: key_scores<7, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
-          default: key_scores<8, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
+          case 5: key_scores_wide<5, G>(page, lane, qrow, sm.kcent, s); break;
+          case 6: key_scores_wide<6, G>(page, lane, qrow, sm.kcent, s); break;
+          case 7: key_scores_wide<7, G>(page, lane, qrow, sm.kcent, s); break;
+          default: key_scores_wide<8, G>(page, lane, qrow, sm.kcent, s); break;
         }
       }
       const float nk = reinterpret_cast<const float*>(page + 1024 * kb)[lane];
@@ -459,10 +575,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
         case 2: value_accum<2, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
         case 3: value_accum<3, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
         case 4: value_accum<4, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
-        case 5: value_accum<5, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
-        case 6: value_accum<6, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
-        case 7: value_accum<7, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
-        default: value_accum<8, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
+        case 5: value_accum_wide<5, G>(vblk, lane, wv, sm.vcent, acc); break;
+        case 6: value_accum_wide<6, G>(vblk, lane, wv, sm.vcent, acc); break;
+        case 7: value_accum_wide<7, G>(vblk, lane, wv, sm.vcent, acc); break;
+        default: value_accum_wide<8, G>(vblk, lane, wv, sm.vcent, acc); break;
       }
     }
     wave_lds_sync();
@@ -518,70 +634,111 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
 // (3) combine: one 128-thread block per (session, query head).  The split
 // weights 2^(m_s - M) are computed once into LDS; the value sums then stream
 // with independent loads.
-__global__ __launch_bounds__(128) void combine_kernel(DecodeArgs a) {
-  __shared__ float buf[D];
+constexpr int kCombineGroups = 4;                  // 128-thread groups per row
+constexpr int kCombineWaves = kCombineGroups * 2;
+
+// Merges the partials of one (session, query head) row: log-sum-exp weights,
+// a compacted list of the non-empty partials (ascending, so the sum order is
+// fixed), their value sums split over four thread groups, then one FWHT.
+__global__ __launch_bounds__(128 * kCombineGroups) void combine_kernel(DecodeArgs a) {
   __shared__ float wgt[kMaxPartials];
-  __shared__ float red[2];
-  const int j = threadIdx.x;
+  __shared__ int list[kMaxPartials];
+  __shared__ float gsum[kCombineGroups][D];
+  __shared__ float red[kCombineWaves];
+  __shared__ int cnt[kCombineWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nthr = 128 * kCombineGroups;
   const int row = blockIdx.x;
   const int b = row / a.n_q_heads;
   const int ns = a.n_splits + a.n_splits_general;   // both page classes
   const float* part = a.wsp + (size_t)row * ns * kPartialFloats;
   float* o = a.out + (size_t)row * D;
-  // global max over splits
+  // global max over partials
   float mloc = -INFINITY;
-  for (int s = j; s < ns; s += D) mloc = fmaxf(mloc, part[(size_t)s * kPartialFloats]);
+  for (int s = tid; s < ns; s += nthr) mloc = fmaxf(mloc, part[(size_t)s * kPartialFloats]);
   mloc = wave_max(mloc);
-  if ((j & 63) == 0) red[j >> 6] = mloc;
+  if (lane == 0) red[wave] = mloc;
   __syncthreads();
-  const float M = fmaxf(red[0], red[1]);
-  __syncthreads();
+  float M = red[0];
+#pragma clang loop unroll(full)
+  for (int w = 1; w < kCombineWaves; ++w) M = fmaxf(M, red[w]);
   if (M == -INFINITY || a.n_tokens[b] <= 0) {
-    o[j] = 0.f;
+    if (tid < D) o[tid] = 0.f;
     return;
   }
+  // weights, the denominator and the list of non-empty partials
   float lloc = 0.f;
-  for (int s = j; s < ns; s += D) {
-    const float ms = part[(size_t)s * kPartialFloats];
-    const float f = ms == -INFINITY ? 0.f : exp2f(ms - M);
-    wgt[s] = f;
-    lloc = fmaf(part[(size_t)s * kPartialFloats + 1], f, lloc);
+  int total = 0;
+  for (int base = 0; base < ns; base += nthr) {
+    const int s = base + tid;
+    float f = 0.f;
+    if (s < ns) {
+      const float ms = part[(size_t)s * kPartialFloats];
+      f = ms == -INFINITY ? 0.f : exp2f(ms - M);
+      lloc = fmaf(part[(size_t)s * kPartialFloats + 1], f, lloc);
+      wgt[s] = f;
+    }
+    const uint64_t bal = __ballot(f != 0.f);
+    __syncthreads();                               // red / cnt free again
+    if (lane == 0) cnt[wave] = __popcll(bal);
+    __syncthreads();
+    int off = total, all = total;
+#pragma clang loop unroll(full)
+    for (int w = 0; w < kCombineWaves; ++w) {
+      off += w < wave ? cnt[w] : 0;
+      all += cnt[w];
+    }
+    if (f != 0.f) list[off + __popcll(bal & ((1ull << lane) - 1ull))] = s;
+    total = all;
   }
   lloc = wave_sum(lloc);
-  if ((j & 63) == 0) red[j >> 6] = lloc;
   __syncthreads();
-  const float L = red[0] + red[1];
-  // value sums of the non-empty partials (an empty one may hold stale values,
-  // so its value is selected away, not multiplied by zero); eight independent
-  // loads in flight per thread
-  float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  int s = 0;
-  for (; s + 8 <= ns; s += 8) {
+  if (lane == 0) red[wave] = lloc;
+  __syncthreads();
+  float L = 0.f;
 #pragma clang loop unroll(full)
-    for (int u = 0; u < 8; ++u) {
-      const float v = part[(size_t)(s + u) * kPartialFloats + 4 + j];
-      const float w = wgt[s + u];
-      acc8[u] = fmaf(w != 0.f ? v : 0.f, w, acc8[u]);
+  for (int w = 0; w < kCombineWaves; ++w) L += red[w];
+  // value sums: group g takes list entries g, g + 4, ...; four loads in flight
+  const int g = tid >> 7, j = tid & (D - 1);
+  float acc4[4] = {0.f, 0.f, 0.f, 0.f};
+  int k = g;
+  for (; k + 3 * kCombineGroups < total; k += 4 * kCombineGroups) {
+#pragma clang loop unroll(full)
+    for (int u = 0; u < 4; ++u) {
+      const int s = list[k + u * kCombineGroups];
+      acc4[u] = fmaf(part[(size_t)s * kPartialFloats + 4 + j], wgt[s], acc4[u]);
     }
   }
-  for (; s < ns; ++s) {
-    const float v = part[(size_t)s * kPartialFloats + 4 + j];
-    const float w = wgt[s];
-    acc8[0] = fmaf(w != 0.f ? v : 0.f, w, acc8[0]);
+  for (; k < total; k += kCombineGroups) {
+    const int s = list[k];
+    acc4[0] = fmaf(part[(size_t)s * kPartialFloats + 4 + j], wgt[s], acc4[0]);
   }
-  const float ar = ((acc8[0] + acc8[1]) + (acc8[2] + acc8[3])) + ((acc8[4] + acc8[5]) + (acc8[6] + acc8[7]));
-  const uint32_t neg = (a.sign_mask[j >> 5] >> (j & 31)) & 1u;
-  buf[j] = flip_if(ar, neg);
+  gsum[g][j] = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+  __syncthreads();
+  // o = D H D acc / d / L, the FWHT in place on gsum[0]
+  // (thread j alone reads column j of gsum and writes buf[j] = gsum[0][j])
+  float* buf = gsum[0];
+  uint32_t neg = 0;
+  if (tid < D) {
+    float ar = 0.f;
+#pragma clang loop unroll(full)
+    for (int q = 0; q < kCombineGroups; ++q) ar += gsum[q][j];
+    neg = (a.sign_mask[j >> 5] >> (j & 31)) & 1u;
+    buf[j] = flip_if(ar, neg);
+  }
   __syncthreads();
 #pragma clang loop unroll(full)
   for (int hh = 1; hh < D; hh <<= 1) {
-    const float mine = buf[j], other = buf[j ^ hh];
+    float mine = 0.f, other = 0.f;
+    if (tid < D) {
+      mine = buf[j];
+      other = buf[j ^ hh];
+    }
     __syncthreads();
-    buf[j] = (j & hh) ? other - mine : mine + other;
+    if (tid < D) buf[j] = (j & hh) ? other - mine : mine + other;
     __syncthreads();
   }
-  // o = D H D acc / d / L
-  o[j] = flip_if(buf[j], neg) * (1.0f / D) / L;
+  if (tid < D) o[j] = flip_if(buf[j], neg) * (1.0f / D) / L;
 }
 
 
@@ -672,7 +829,7 @@ int tq_decode_attention(const tq_layer* layer, const tq_cache* cache, const tq_q
       break;
   }
   if ((st = launch_status("split"))) return st;
-  hipLaunchKernelGGL(combine_kernel, dim3(rows), dim3(128), 0, s, a);
+  hipLaunchKernelGGL(combine_kernel, dim3(rows), dim3(128 * kCombineGroups), 0, s, a);
   return launch_status("combine");
 }
 

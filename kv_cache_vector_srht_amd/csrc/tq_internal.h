@@ -29,9 +29,9 @@ constexpr int kQPrepFloats = 3 * 128;       // rotated q, plain q, S q (all pre-
 constexpr int kPartialFloats = 4 + 128;     // m, l, (pad), acc[128]
 constexpr int kMaxPartials = 5120;          // partials per (session, query head), both classes
 
-// Split-K geometry: the common page class uses n_splits ranges of
-// pages_per_split pages; the general class (fp16, 5-8 bits, QJL; heavier per
-// page and usually rarer) uses ranges a quarter as long.
+// Split-K geometry: each page class (common: 1-4 bit codebook pages without
+// QJL; general: everything else) covers the page table in ranges of
+// pages_per_split pages.
 struct SplitPlan {
   int n_splits;
   int pages_per_split;
