@@ -172,8 +172,9 @@ def cpu_baseline(w, layers_data, seconds: float):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no "
-              "multi-GPU path; see the sharding notes in DESIGN.md", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library has no "
+              "multi-GPU path; a deployment shards sessions and KV heads across GPUs, each GPU "
+              "running this single-GPU path on its share", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
@@ -253,12 +254,14 @@ def main():
     enc_mtok = w.batch * w.n_tokens / enc_s / 1e6
 
     # the kernel that dominates the step
+    # (encode is one encode_pages_kernel launch per layer unless a layer has
+    # QJL keys; decode is four launches per layer, reported as one call)
     if enc_s >= dec_s:
-        name, per_launch_bytes, per_launch_s, launches = ("encode_kv", enc_bytes / w.n_layers,
-                                                          enc_s / w.n_layers, w.n_layers)
+        name, per_launch_bytes, per_launch_s = ("encode_pages_kernel", enc_bytes / w.n_layers,
+                                                enc_s / w.n_layers)
     else:
-        name, per_launch_bytes, per_launch_s, launches = ("decode_attention", dec_bytes / w.n_layers,
-                                                          dec_s / w.n_layers, w.n_layers)
+        name, per_launch_bytes, per_launch_s = ("decode_attention", dec_bytes / w.n_layers,
+                                                dec_s / w.n_layers)
     achieved = per_launch_bytes / per_launch_s / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_record(name),
