@@ -145,3 +145,68 @@ def compare_dequant(got: np.ndarray, ref: np.ndarray, t: Tally):
     if nz.any():
         t.worst_cos = min(t.worst_cos, float(np.min(num[nz] / den[nz])))
     assert np.all(np.linalg.norm(got[~nz], axis=1) == 0) and np.all(np.linalg.norm(ref[~nz], axis=1) == 0)
+
+
+def compare_unit_full(pool_host: np.ndarray, offsets: np.ndarray, b: int, h: int, K: np.ndarray,
+                      V: np.ndarray, formats, signs, S, t: Tally, k_kind=O.LLOYD_MAX,
+                      v_kind=O.LLOYD_MAX):
+    """Compare every page of unit (b, h) with the oracle, encoding the pages of
+    one format together (one oracle pass over the unit), and return the
+    oracle's reconstruction (Kh, Vh) under the admissible boundary tie-breaks
+    the GPU took: the same composition of oracle steps as
+    ``O.reconstruct_unit`` with overrides, without encoding twice."""
+    T = K.shape[0]
+    Kh = np.zeros((T, O.HEAD_DIM))
+    Vh = np.zeros((T, O.HEAD_DIM))
+    groups = {}
+    for p, fmt in enumerate(formats):
+        lo, hi = p * 64, min(T, (p + 1) * 64)
+        if lo >= T:
+            break
+        off = int(offsets[b, h, p])
+        if fmt[0] == 0:
+            raw = pool_host[off:off + O.page_bytes(fmt)].tobytes()
+            assert raw == O.fp16_page_bytes(K[lo:hi], V[lo:hi]), f"fp16 page ({b},{h},{p}) differs"
+            Kh[lo:hi] = K[lo:hi].astype(np.float16)
+            Vh[lo:hi] = V[lo:hi].astype(np.float16)
+        else:
+            assert hi - lo == 64, "a packed page must be full"
+            groups.setdefault(tuple(fmt), []).append(p)
+    for fmt, plist in groups.items():
+        kb, vb, qjl = fmt
+        sec = O.page_sections(fmt)
+        rows = np.concatenate([np.arange(p * 64, (p + 1) * 64) for p in plist])
+        raws = [pool_host[int(offsets[b, h, p]):int(offsets[b, h, p]) + O.page_bytes(fmt)] for p in plist]
+
+        def part(name):
+            o, n = sec[name]
+            return [r[o:o + n].tobytes() for r in raws]
+        gk = np.concatenate([O.unpack_block(x, kb) for x in part("k_codes")])
+        gv = np.concatenate([O.v_codes_from_streams(O.unpack_block(x, vb)) for x in part("v_codes")])
+        what = f"unit ({b},{h}) fmt {fmt}"
+        ek = O.encode(K[rows], signs, kb, k_kind)
+        ev = O.encode(V[rows], signs, vb, v_kind)
+        for name, e in (("k_norm", ek), ("v_norm", ev)):
+            got = np.frombuffer(b"".join(part(name)), dtype="<f4")
+            assert np.allclose(got, e["norm"], rtol=NORM_RTOL, atol=0), f"{name} {what}"
+        k_alt, v_alt = [], []
+        _cmp_codes(gk, ek["codes"], ek["near"], t, "K " + what, 0, k_alt)
+        _cmp_codes(gv, ev["codes"], ev["near"], t, "V " + what, 0, v_alt)
+        kc, vc = ek["codes"].copy(), ev["codes"].copy()
+        for codes, alt in ((kc, k_alt), (vc, v_alt)):
+            for r, c, code in alt:
+                codes[r, c] = code
+        kh = O.dequantize(ek["norm"], kc, signs, kb, k_kind)
+        if qjl:
+            qj = O.qjl_encode(K[rows], kh, S)
+            z = np.concatenate([O.unpack_signs(x) for x in part("qjl_signs")])
+            g = np.frombuffer(b"".join(part("qjl_gamma")), dtype="<f4")
+            dz = z != qj["z"]
+            assert not (dz & ~qj["near"]).any(), f"QJL signs {what}"
+            t.sign_bits += dz.size
+            t.sign_mismatches += int(dz.sum())
+            assert np.allclose(g, qj["gamma"], rtol=NORM_RTOL, atol=1e-30), f"QJL gamma {what}"
+            kh = kh + O.qjl_reconstruct(qj["z"], qj["gamma"], S)
+        Kh[rows] = kh
+        Vh[rows] = O.dequantize(ev["norm"], vc, signs, vb, v_kind)
+    return Kh, Vh
