@@ -318,14 +318,57 @@ __device__ __forceinline__ float quad_swap(float v, int m) {
                 : __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
 }
 
+// x[s] += sg * x[s] of the partner lane (quad permutation CTRL), for the 32
+// values, as v_fmac_f32 with a DPP source; the compiler does not fuse a DPP
+// move into a multiply-accumulate, so it is written out.  Each group opens with
+// two wait states (s_nop 1), which covers the DPP read-after-VALU-write hazard
+// for every register it reads.
+template <int CTRL>
+__device__ __forceinline__ void quad_butterfly(float (&x)[32], float sg) {
+  static_assert(CTRL == 0xB1 || CTRL == 0x4E, "quad permutations [1,0,3,2] and [2,3,0,1]");
+#define TQ_FMAC_DPP(PERM)                                                                          \
+  asm volatile("s_nop 1\n"                                                                        \
+               "v_fmac_f32_dpp %0, %0, %16 " PERM " row_mask:0xf bank_mask:0xf\n"                  \
+               "v_fmac_f32_dpp %1, %1, %16 " PERM " row_mask:0xf bank_mask:0xf\n"                  \
+               "v_fmac_f32_dpp %2, %2, %16 " PERM " row_mask:0xf bank_mask:0xf\n"                  \
+               "v_fmac_f32_dpp %3, %3, %16 " PERM " row_mask:0xf bank_mask:0xf\n"                  \
+               "v_fmac_f32_dpp %4, %4, %16 " PERM " row_mask:0xf bank_mask:0xf\n"                  \
+               "v_fmac_f32_dpp %5, %5, %16 " PERM " row_mask:0xf bank_mask:0xf\n"                  \
+               "v_fmac_f32_dpp %6, %6, %16 " PERM " row_mask:0xf bank_mask:0xf\n"                  \
+               "v_fmac_f32_dpp %7, %7, %16 " PERM " row_mask:0xf bank_mask:0xf\n"                  \
+               "v_fmac_f32_dpp %8, %8, %16 " PERM " row_mask:0xf bank_mask:0xf\n"                  \
+               "v_fmac_f32_dpp %9, %9, %16 " PERM " row_mask:0xf bank_mask:0xf\n"                  \
+               "v_fmac_f32_dpp %10, %10, %16 " PERM " row_mask:0xf bank_mask:0xf\n"                \
+               "v_fmac_f32_dpp %11, %11, %16 " PERM " row_mask:0xf bank_mask:0xf\n"                \
+               "v_fmac_f32_dpp %12, %12, %16 " PERM " row_mask:0xf bank_mask:0xf\n"                \
+               "v_fmac_f32_dpp %13, %13, %16 " PERM " row_mask:0xf bank_mask:0xf\n"                \
+               "v_fmac_f32_dpp %14, %14, %16 " PERM " row_mask:0xf bank_mask:0xf\n"                \
+               "v_fmac_f32_dpp %15, %15, %16 " PERM " row_mask:0xf bank_mask:0xf"                   \
+               : "+v"(x[g + 0]), "+v"(x[g + 1]), "+v"(x[g + 2]), "+v"(x[g + 3]), "+v"(x[g + 4]),        \
+                 "+v"(x[g + 5]), "+v"(x[g + 6]), "+v"(x[g + 7]), "+v"(x[g + 8]), "+v"(x[g + 9]),        \
+                 "+v"(x[g + 10]), "+v"(x[g + 11]), "+v"(x[g + 12]), "+v"(x[g + 13]), "+v"(x[g + 14]),   \
+                 "+v"(x[g + 15])                                                                   \
+               : "v"(sg))
+#pragma clang loop unroll(full)
+  for (int g = 0; g < 32; g += 16) {
+    if constexpr (CTRL == 0xB1) {
+      TQ_FMAC_DPP("quad_perm:[1,0,3,2]");
+    } else {
+      TQ_FMAC_DPP("quad_perm:[2,3,0,1]");
+    }
+  }
+#undef TQ_FMAC_DPP
+}
+
 struct Lut {
   float S, O;
   int nb;
+  float fmax;   // nb - 1 as a float
 };
 
 struct EncodeLane {
   uint32_t hmask[16];   // D sign bits of the lane's value pairs, placed for an fp16x2 xor
-  uint32_t fmask[8];    // per code byte: 0xff when the outer D flips that coordinate
+  uint32_t fmask[8];    // per code byte: 0xff when the code is flipped (outer D times the lane's sign)
   uint32_t dl;          // D bits of the lane's 32 slots
 };
 
@@ -336,7 +379,12 @@ __device__ __forceinline__ float encode_quarter(const void* src, size_t row_off,
                                                 const EncodeLane& el, int B, const Lut& lut,
                                                 const uint2* ent, uint32_t* mat_row) {
   float x[32];
+  float ss = 0.f;
   if constexpr (DT == TQ_DTYPE_F16) {
+    // slots 2i, 2i+1 are the two halves of one fp16 pair: the first butterfly
+    // (slot bit 0) reads them straight from the pair with mixed-precision
+    // multiply-adds (lo + 1.0 * hi, lo - 1.0 * hi), so no conversion is issued;
+    // the norm's squares are mixed-precision too
     const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const __half*>(src) + row_off);
 #pragma clang loop unroll(full)
     for (int c = 0; c < 4; ++c) {
@@ -346,8 +394,14 @@ __device__ __forceinline__ float encode_quarter(const void* src, size_t row_off,
 #pragma clang loop unroll(full)
       for (int kk = 0; kk < 4; ++kk) {
         const float2 f = __half22float2(*reinterpret_cast<const __half2*>(&ww[kk]));
-        x[8 * c + 2 * kk] = f.x;
-        x[8 * c + 2 * kk + 1] = f.y;
+        ss = fmaf(f.x, f.x, ss);
+        ss = fmaf(f.y, f.y, ss);
+        float sum, dif;
+        asm("v_fma_mix_f32 %0, %1, 1.0, %1 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(sum) : "v"(ww[kk]));
+        asm("v_fma_mix_f32 %0, %1, 1.0, -%1 op_sel:[0,0,1] op_sel_hi:[1,0,1]"
+            : "=v"(dif) : "v"(ww[kk]));
+        x[8 * c + 2 * kk] = sum;
+        x[8 * c + 2 * kk + 1] = dif;
       }
     }
   } else {
@@ -359,15 +413,20 @@ __device__ __forceinline__ float encode_quarter(const void* src, size_t row_off,
 #pragma clang loop unroll(full)
       for (int k = 0; k < 8; ++k) x[8 * c + k] = flip_if(v[k], (el.dl >> (8 * c + k)) & 1u);
     }
-  }
-  float ss = 0.f;
 #pragma clang loop unroll(full)
-  for (int s = 0; s < 32; ++s) ss = fmaf(x[s], x[s], ss);
+    for (int s = 0; s < 32; ++s) ss = fmaf(x[s], x[s], ss);
+#pragma clang loop unroll(full)
+    for (int s = 0; s < 32; s += 2) {
+      const float a0 = x[s], b0 = x[s + 1];
+      x[s] = a0 + b0;
+      x[s + 1] = a0 - b0;
+    }
+  }
   ss += quad_swap(ss, 1);
   ss += quad_swap(ss, 2);
-  // in-lane butterflies over slot bits 0..4 (coordinate bits 0,1,2,5,6)
+  // in-lane butterflies over slot bits 1..4 (coordinate bits 1,2,5,6); bit 0 is done
 #pragma clang loop unroll(full)
-  for (int h = 1; h < 32; h <<= 1)
+  for (int h = 2; h < 32; h <<= 1)
 #pragma clang loop unroll(full)
     for (int s = 0; s < 32; ++s)
       if (!(s & h)) {
@@ -375,13 +434,13 @@ __device__ __forceinline__ float encode_quarter(const void* src, size_t row_off,
         x[s] = a0 + b0;
         x[s + h] = a0 - b0;
       }
-  // across the quad: coordinate bits 3 (lane bit 0) and 4 (lane bit 1)
-#pragma clang loop unroll(full)
-  for (int m = 1; m <= 2; m <<= 1) {
-    const float sg = (e & m) ? -1.f : 1.f;
-#pragma clang loop unroll(full)
-    for (int s = 0; s < 32; ++s) x[s] = fmaf(x[s], sg, quad_swap(x[s], m));
-  }
+  // across the quad: coordinate bits 3 (lane bit 0) and 4 (lane bit 1).  Each
+  // lane computes mine + sg * partner (one multiply-add with the partner read
+  // through DPP), so an upper lane keeps the negated butterfly output; after
+  // both stages lane e holds rho_e times the transform, rho_e = -1 for e = 1, 2,
+  // which the code flip below undoes (the flip mask carries it).
+  quad_butterfly<0xB1>(x, (e & 1) ? -1.f : 1.f);
+  quad_butterfly<0x4E>(x, (e & 2) ? -1.f : 1.f);
   const float n = sqrtf(ss);
   const float inv = n > 0.f ? 1.0f / n : 0.f;
   uint32_t cb[8];
@@ -390,7 +449,8 @@ __device__ __forceinline__ float encode_quarter(const void* src, size_t row_off,
 #pragma clang loop unroll(full)
   for (int s = 0; s < 32; ++s) {
     const float u = x[s] * inv;
-    const int bin = min(max((int)fmaf(u, lut.S, lut.O), 0), lut.nb - 1);
+    // bin = clamp(floor(u S + O), 0, nb - 1), clamped in float (one med3)
+    const int bin = (int)__builtin_amdgcn_fmed3f(fmaf(u, lut.S, lut.O), 0.f, lut.fmax);
     const uint2 en = ent[bin];
     const uint32_t c = en.x + (u >= __uint_as_float(en.y) ? 1u : 0u);
     cb[s >> 2] |= c << (8 * (s & 3));
@@ -406,19 +466,51 @@ __device__ __forceinline__ float encode_quarter(const void* src, size_t row_off,
 }
 
 // Writes dwords [e*B, e*B + B) of stream s of a code block from its codes
-// 32e..32e+31 (bytes of c8), LSB-first.
+// 32e..32e+31 (one per byte of c8, each below 2^B), LSB-first: code n at bit
+// n B.  The width is uniform, so the branches below are too.  Up to 4 bits,
+// each dword of four codes is folded in two shift-or-mask steps (pairs, then a
+// 4B-bit quad) before entering the bit accumulator; 8-bit codes are already
+// packed; 5-7 bits enter code by code.
 __device__ __forceinline__ void store_stream_part(int B, char* blk, int s, int e, const uint32_t (&c8)[8]) {
-  uint64_t acc = 0;
-  int nb = 0, d = e * B;
+  uint32_t* const base = reinterpret_cast<uint32_t*>(blk + s * 16);   // dword d: base[(d >> 2) * 256 + (d & 3)]
+  int d = e * B;
+  auto emit = [&](uint32_t v) {
+    base[(d >> 2) * 256 + (d & 3)] = v;
+    ++d;
+  };
+  if (B == 8) {
 #pragma clang loop unroll(full)
-  for (int n = 0; n < 32; ++n) {
-    acc |= (uint64_t)((c8[n >> 2] >> (8 * (n & 3))) & 0xffu) << nb;
-    nb += B;
-    if (nb >= 32) {
-      reinterpret_cast<uint32_t*>(blk + ((d >> 2) * 64 + s) * 16)[d & 3] = (uint32_t)acc;
-      acc >>= 32;
-      nb -= 32;
-      ++d;
+    for (int i = 0; i < 8; ++i) emit(c8[i]);
+    return;
+  }
+  uint64_t acc = 0;
+  int nb = 0;
+  if (B <= 4) {
+    const int s1 = 8 - B, s2 = 16 - 2 * B, w4 = 4 * B;
+    const uint32_t m2 = ((1u << (2 * B)) - 1u) * 0x00010001u, m4 = (1u << w4) - 1u;
+#pragma clang loop unroll(full)
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t w = c8[k];
+      const uint32_t pr = (w | (w >> s1)) & m2;     // c0 | c1 << B, c2 | c3 << B
+      const uint32_t qd = (pr | (pr >> s2)) & m4;   // c0 | c1 << B | c2 << 2B | c3 << 3B
+      acc |= (uint64_t)qd << nb;
+      nb += w4;
+      if (nb >= 32) {
+        emit((uint32_t)acc);
+        acc >>= 32;
+        nb -= 32;
+      }
+    }
+  } else {
+#pragma clang loop unroll(full)
+    for (int n = 0; n < 32; ++n) {
+      acc |= (uint64_t)((c8[n >> 2] >> (8 * (n & 3))) & 0xffu) << nb;
+      nb += B;
+      if (nb >= 32) {
+        emit((uint32_t)acc);
+        acc >>= 32;
+        nb -= 32;
+      }
     }
   }
 }
@@ -451,11 +543,12 @@ __global__ __launch_bounds__(kEncodeBlock) void encode_pages_kernel(EncodeArgs a
       uint32_t f = 0;
 #pragma clang loop unroll(full)
       for (int k = 0; k < 4; ++k) f |= ((el.dl >> (4 * i + k)) & 1u) ? (0xffu << (8 * k)) : 0u;
-      el.fmask[i] = f;
+      // lanes 1 and 2 of the quad hold the negated transform (see encode_quarter)
+      el.fmask[i] = (e == 1 || e == 2) ? ~f : f;
     }
   }
   int cur_kb = -1, cur_vb = -1;
-  Lut lk{0.f, 0.f, 1}, lv{0.f, 0.f, 1};
+  Lut lk{0.f, 0.f, 1, 0.f}, lv{0.f, 0.f, 1, 0.f};
   const size_t base = (size_t)b * a.sb + (size_t)h * a.sh;
   const uint64_t* prow = pages + ((size_t)b * a.n_kv_heads + h) * a.max_pages;
 
@@ -508,8 +601,10 @@ __global__ __launch_bounds__(kEncodeBlock) void encode_pages_kernel(EncodeArgs a
       __syncthreads();
       const float* hk = a.k_table + kLutHeaderOffset + 4 * (kb - 1);
       const float* hv = a.v_table + kLutHeaderOffset + 4 * (vb - 1);
-      lk = Lut{hk[0], hk[1], min((int)__float_as_uint(hk[2]), kLutMaxBins)};
-      lv = Lut{hv[0], hv[1], min((int)__float_as_uint(hv[2]), kLutMaxBins)};
+      const int nbk = min((int)__float_as_uint(hk[2]), kLutMaxBins);
+      const int nbv = min((int)__float_as_uint(hv[2]), kLutMaxBins);
+      lk = Lut{hk[0], hk[1], nbk, (float)(nbk - 1)};
+      lv = Lut{hv[0], hv[1], nbv, (float)(nbv - 1)};
       const uint2* sk = reinterpret_cast<const uint2*>(a.k_table + __float_as_uint(hk[3]));
       const uint2* sv = reinterpret_cast<const uint2*>(a.v_table + __float_as_uint(hv[3]));
       for (int i = tid; i < lk.nb; i += kEncodeBlock) entk[i] = sk[i];
