@@ -46,7 +46,7 @@ class tq_layer(ctypes.Structure):
 
 class tq_cache(ctypes.Structure):
     _fields_ = [("n_sessions", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
-                ("max_pages", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32), ("page_classes", ctypes.c_int32),
                 ("n_tokens", ctypes.c_void_p), ("pages", ctypes.c_void_p),
                 ("pool", ctypes.c_void_p), ("pool_bytes", ctypes.c_uint64)]
 
@@ -191,6 +191,22 @@ class Layer:
 
 
 # ------------------------------------------------------------------- cache
+CACHE_COMMON_PAGES = 1
+CACHE_OTHER_PAGES = 2
+
+
+def page_classes(formats) -> int:
+    """The tq_cache.page_classes bits of a page table with these formats:
+    common = 1-4 bit K and V without QJL; other = fp16, 5-8 bit or QJL."""
+    bits = 0
+    for row in formats:
+        for fm in row:
+            for kb, vb, q in fm:
+                common = 1 <= kb <= 4 and 1 <= vb <= 4 and not q
+                bits |= CACHE_COMMON_PAGES if common else CACHE_OTHER_PAGES
+    return bits
+
+
 class Cache:
     """Page pool + page table + token counts for B sessions x H_kv heads.
 
@@ -228,8 +244,9 @@ class Cache:
         self.host_pages = desc
         self.pages = torch.from_numpy(desc.view(np.int64)).to(self.device)
         self.n_tokens = torch.tensor(list(n_tokens), dtype=torch.int32, device=self.device)
-        self.struct = tq_cache(B, H, P, 0, self.n_tokens.data_ptr(), self.pages.data_ptr(),
-                               self.pool.data_ptr(), self.pool_bytes)
+        self.page_classes = page_classes(formats)
+        self.struct = tq_cache(B, H, P, self.page_classes, self.n_tokens.data_ptr(),
+                               self.pages.data_ptr(), self.pool.data_ptr(), self.pool_bytes)
 
     def set_n_tokens(self, n_tokens: Sequence[int]) -> None:
         self.n_tokens.copy_(self.n_tokens.new_tensor(list(n_tokens)))

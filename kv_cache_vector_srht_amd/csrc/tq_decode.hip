@@ -770,7 +770,7 @@ int tq_decode_attention(const tq_layer* layer, const tq_cache* cache, const tq_q
   if (!aligned16(out) || !aligned16(workspace)) return fail(TQ_ERR_ALIGNMENT, "out/workspace misaligned");
   if (!(query->softmax_scale >= 0.f) || isinf(query->softmax_scale))
     return fail(TQ_ERR_INVALID_ARG, "bad softmax scale");
-  const SplitPlan sp = split_plan(cache->n_sessions, cache->n_kv_heads, cache->max_pages);
+  SplitPlan sp = split_plan(cache->n_sessions, cache->n_kv_heads, cache->max_pages);
   if (sp.n_splits + sp.n_splits_general > kMaxPartials)   // the combine stages their weights in LDS
     return fail(TQ_ERR_UNSUPPORTED, "%d partials per row exceed %d", sp.n_splits + sp.n_splits_general,
                 kMaxPartials);
@@ -796,6 +796,11 @@ int tq_decode_attention(const tq_layer* layer, const tq_cache* cache, const tq_q
   a.k_table = layer->k_table;
   a.v_table = layer->v_table;
   a.qjl_s = layer->qjl_s;
+  // A page class the host says is absent gets no launch and no partials.
+  const bool run_common = cache->page_classes == 0 || (cache->page_classes & TQ_CACHE_COMMON_PAGES);
+  const bool run_other = cache->page_classes == 0 || (cache->page_classes & TQ_CACHE_OTHER_PAGES);
+  if (!run_common) sp.n_splits = 0;
+  if (!run_other) sp.n_splits_general = 0;
   a.n_splits = sp.n_splits;
   a.pages_per_split = sp.pages_per_split;
   a.n_splits_general = sp.n_splits_general;
@@ -810,25 +815,24 @@ int tq_decode_attention(const tq_layer* layer, const tq_cache* cache, const tq_q
   const dim3 grid(sp.n_splits, cache->n_kv_heads, cache->n_sessions);
   const dim3 ggrid(sp.n_splits_general, cache->n_kv_heads, cache->n_sessions);
   const dim3 blk(64 * kDecodeWaves);
-  switch (G) {
-    case 1:
-      hipLaunchKernelGGL((split_kernel<1, 0>), grid, blk, 0, s, a, a.wsq, cache->pages, a.wsp);
-      hipLaunchKernelGGL((split_kernel<1, 1>), ggrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp);
-      break;
-    case 2:
-      hipLaunchKernelGGL((split_kernel<2, 0>), grid, blk, 0, s, a, a.wsq, cache->pages, a.wsp);
-      hipLaunchKernelGGL((split_kernel<2, 1>), ggrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp);
-      break;
-    case 4:
-      hipLaunchKernelGGL((split_kernel<4, 0>), grid, blk, 0, s, a, a.wsq, cache->pages, a.wsp);
-      hipLaunchKernelGGL((split_kernel<4, 1>), ggrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp);
-      break;
-    default:
-      hipLaunchKernelGGL((split_kernel<8, 0>), grid, blk, 0, s, a, a.wsq, cache->pages, a.wsp);
-      hipLaunchKernelGGL((split_kernel<8, 1>), ggrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp);
-      break;
+  if (run_common) {
+    switch (G) {
+      case 1: hipLaunchKernelGGL((split_kernel<1, 0>), grid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
+      case 2: hipLaunchKernelGGL((split_kernel<2, 0>), grid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
+      case 4: hipLaunchKernelGGL((split_kernel<4, 0>), grid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
+      default: hipLaunchKernelGGL((split_kernel<8, 0>), grid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
+    }
+    if ((st = launch_status("split (common pages)"))) return st;
   }
-  if ((st = launch_status("split"))) return st;
+  if (run_other) {
+    switch (G) {
+      case 1: hipLaunchKernelGGL((split_kernel<1, 1>), ggrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
+      case 2: hipLaunchKernelGGL((split_kernel<2, 1>), ggrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
+      case 4: hipLaunchKernelGGL((split_kernel<4, 1>), ggrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
+      default: hipLaunchKernelGGL((split_kernel<8, 1>), ggrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
+    }
+    if ((st = launch_status("split (other pages)"))) return st;
+  }
   hipLaunchKernelGGL(combine_kernel, dim3(rows), dim3(128 * kCombineGroups), 0, s, a);
   return launch_status("combine");
 }

@@ -57,16 +57,37 @@ __device__ __forceinline__ uint32_t bits_at(const uint32_t (&s)[N], int pos, int
   return v & ((1u << w) - 1u);
 }
 
+// Wavefront reductions (every lane active).  Inside each 16-lane row the
+// partner values come through DPP (quad permutations xor 1 and xor 2, then the
+// half-row and row mirrors), which keeps them in the VALU pipeline; the four
+// row results are then read as scalars.  Every lane returns the same value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma clang loop unroll(full)
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp_f<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror: the other quad of the 8
+  v = fmaxf(v, dpp_f<0x140>(v));   // row_mirror: the other 8 of the row
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma clang loop unroll(full)
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 // Orders this wave's LDS writes before its later LDS reads.

@@ -358,6 +358,8 @@ int check_cache(const tq_cache* C) {
   if (((uintptr_t)C->pages & 7) != 0 || ((uintptr_t)C->n_tokens & 3) != 0)
     return fail(TQ_ERR_ALIGNMENT, "page table / token counts misaligned");
   if (C->pool_bytes == 0) return fail(TQ_ERR_INVALID_ARG, "empty pool");
+  if (C->page_classes & ~(TQ_CACHE_COMMON_PAGES | TQ_CACHE_OTHER_PAGES))
+    return fail(TQ_ERR_INVALID_ARG, "unknown page_classes bits 0x%x", C->page_classes);
   return TQ_OK;
 }
 

@@ -170,3 +170,27 @@ def test_deterministic(dev):
         torch.cuda.synchronize()
         res.append((_np(cache.pool).copy(), _np(out).copy()))
     assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
+
+
+def test_page_class_hint(dev):
+    """Decode with the page-class bits the binding derives equals decode with
+    the bits cleared (0 = unknown: both classes run), bit for bit, for tables
+    with common pages only, other pages only, and both."""
+    import kv_cache_vector_srht_amd as tq
+    cases = [(W.make_workload(3, {"n_tokens": 64 * 5, "batch": 2}), l) for l in (0, 2)]
+    cases.append((W.make_workload(4, {"n_tokens": 64 * 4 + 9, "batch": 2}), 0))
+    seen = set()
+    for w, l in cases:
+        fm = w.formats[l]
+        S = W.qjl_matrix(42, l) if any(f[2] for row in fm for r in row for f in r) else None
+        layer = tq.Layer(W.rotation_signs(42, l), dev, S)
+        cache = tq.Cache(fm, [w.n_tokens] * w.batch, dev)
+        k, v = W.make_kv(w, l, device=dev)
+        q = W.make_query(w, l, device=dev)
+        tq.encode_kv(layer, cache, k, v)
+        hinted = _np(tq.decode_attention(layer, cache, q)).copy()
+        seen.add(cache.page_classes)
+        cache.struct.page_classes = 0
+        unknown = _np(tq.decode_attention(layer, cache, q))
+        assert np.array_equal(hinted, unknown)
+    assert seen == {1, 2, 3}

@@ -192,3 +192,13 @@ def test_dequantize_validation(L):
 
 def test_status_strings(L):
     assert L.tq_status_string(0) == b"ok" and L.tq_status_string(-4) == b"workspace too small"
+
+
+def test_page_classes_bits():
+    import kv_cache_vector_srht_amd as tq
+    assert tq.page_classes([[[W.packed(3, 2, False), W.packed(1, 1, False)]]]) == tq.CACHE_COMMON_PAGES
+    assert tq.page_classes([[[W.FP16, W.packed(2, 2, True)]]]) == tq.CACHE_OTHER_PAGES
+    assert tq.page_classes([[[W.packed(4, 4, False)], [W.packed(8, 8, False)]]]) == 3
+    w3 = W.make_workload(3, {"n_tokens": 128, "batch": 1})
+    assert tq.page_classes(w3.formats[0]) == tq.CACHE_COMMON_PAGES
+    assert tq.page_classes(w3.formats[2]) == 3
