@@ -549,12 +549,19 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
     for (int h = 0; h < G; ++h)
       if (lane >= valid) s[h] = -INFINITY;
     softmax_update<G>(s, m, l, alpha);
+    // the running sums need rescaling only when some head's maximum moved
+    // (alpha is wave-uniform, so is the branch)
+    bool moved = false;
 #pragma clang loop unroll(full)
-    for (int h = 0; h < G; ++h) {
+    for (int h = 0; h < G; ++h) moved |= alpha[h] != 1.f;
+    if (moved) {
 #pragma clang loop unroll(full)
-      for (int e = 0; e < 8; ++e) acc[h][e] *= alpha[h];
-      wv[lane * G + h] = s[h] * nv;
+      for (int h = 0; h < G; ++h)
+#pragma clang loop unroll(full)
+        for (int e = 0; e < 8; ++e) acc[h][e] *= alpha[h];
     }
+#pragma clang loop unroll(full)
+    for (int h = 0; h < G; ++h) wv[lane * G + h] = s[h] * nv;
     wave_lds_sync();
     if (CLASS == 1 && kb == 0) {
       uint32_t dm[8];

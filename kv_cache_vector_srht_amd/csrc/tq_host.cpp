@@ -315,7 +315,7 @@ SplitPlan split_plan(int n_sessions, int n_kv_heads, int max_pages) {
   SplitPlan sp;
   sp.pages_per_split = (int)pps;
   sp.n_splits = (int)((max_pages + pps - 1) / pps);
-  sp.pages_per_split_general = sp.pages_per_split;
+  sp.pages_per_split_general = (sp.pages_per_split + 1) / 2;
   sp.n_splits_general = (max_pages + sp.pages_per_split_general - 1) / sp.pages_per_split_general;
   return sp;
 }

@@ -29,9 +29,10 @@ constexpr int kQPrepFloats = 3 * 128;       // rotated q, plain q, S q (all pre-
 constexpr int kPartialFloats = 4 + 128;     // m, l, (pad), acc[128]
 constexpr int kMaxPartials = 5120;          // partials per (session, query head), both classes
 
-// Split-K geometry: each page class (common: 1-4 bit codebook pages without
-// QJL; general: everything else) covers the page table in ranges of
-// pages_per_split pages.
+// Split-K geometry: the common class (1-4 bit codebook pages without QJL)
+// covers the page table in ranges of pages_per_split pages; the general class
+// (fp16, 5-8 bit, QJL: heavier per page, and its blocks run fewer waves) in
+// ranges half as long.
 struct SplitPlan {
   int n_splits;
   int pages_per_split;
