@@ -192,7 +192,9 @@ int tq_build_codebook(int bits, int kind, float* centroids, float* boundaries);
  * 1024 + 4 (bits - 1); n_bins entries {count of boundaries below the bin
  * (u32), the one boundary inside the bin widened by a quarter bin each side
  * (f32, or 3e38)} at `offset`), so that code(u) = count + [u >= boundary] at
- * bin floor(u S + O) clamped to [0, n_bins).  The tail is zero.  Writes
+ * bin floor(u S + O) clamped to [0, n_bins); a grid of n_bins = 256 is instead
+ * indexed by u S + O rounded to the nearest integer (ties to even) and
+ * saturated to [0, 255].  The tail is zero.  Writes
  * TQ_CODEBOOK_TABLE_FLOATS floats to a host array (copy it to the device for
  * tq_layer). */
 int tq_codebook_table(int kind, float* table);

@@ -446,14 +446,27 @@ __device__ __forceinline__ float encode_quarter(const void* src, size_t row_off,
   uint32_t cb[8];
 #pragma clang loop unroll(full)
   for (int i = 0; i < 8; ++i) cb[i] = 0;
+  if (lut.nb == kLutByteBins) {
+    // 256-bin grid: the bin is u S + O (O carries the -1/2) rounded and
+    // saturated to a byte by one conversion
 #pragma clang loop unroll(full)
-  for (int s = 0; s < 32; ++s) {
-    const float u = x[s] * inv;
-    // bin = clamp(floor(u S + O), 0, nb - 1), clamped in float (one med3)
-    const int bin = (int)__builtin_amdgcn_fmed3f(fmaf(u, lut.S, lut.O), 0.f, lut.fmax);
-    const uint2 en = ent[bin];
-    const uint32_t c = en.x + (u >= __uint_as_float(en.y) ? 1u : 0u);
-    cb[s >> 2] |= c << (8 * (s & 3));
+    for (int s = 0; s < 32; ++s) {
+      const float u = x[s] * inv;
+      const uint32_t bin = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(u, lut.S, lut.O), 0, 0u);
+      const uint2 en = ent[bin];
+      const uint32_t c = en.x + (u >= __uint_as_float(en.y) ? 1u : 0u);
+      cb[s >> 2] |= c << (8 * (s & 3));
+    }
+  } else {
+#pragma clang loop unroll(full)
+    for (int s = 0; s < 32; ++s) {
+      const float u = x[s] * inv;
+      // bin = clamp(floor(u S + O), 0, nb - 1), clamped in float (one med3)
+      const int bin = (int)__builtin_amdgcn_fmed3f(fmaf(u, lut.S, lut.O), 0.f, lut.fmax);
+      const uint2 en = ent[bin];
+      const uint32_t c = en.x + (u >= __uint_as_float(en.y) ? 1u : 0u);
+      cb[s >> 2] |= c << (8 * (s & 3));
+    }
   }
   const uint32_t flip = ((1u << B) - 1u) * 0x01010101u;
   // chunk c holds coordinates 32c + 8e .. +7: row bytes 32c + 8e

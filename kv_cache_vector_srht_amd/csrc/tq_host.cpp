@@ -206,18 +206,24 @@ int tq_codebook_table(int kind, float* table) {
     // Quantiser lookup grid: bins of width h over [-T, T) with
     // idx = floor(u * S + O), S = 1/h, O = T/h.  Bin i, widened by h/4 on each
     // side, holds at most one boundary; base = boundaries below the widened bin.
+    // (The widening makes an index off by one at a bin edge harmless.)
     const int nt = (1 << b) - 1;
     double gap = 2.0, tmax = 0.0;
     for (int k = 0; k + 1 < nt; ++k) gap = std::min(gap, (double)t[k + 1] - (double)t[k]);
     for (int k = 0; k < nt; ++k) tmax = std::max(tmax, fabs((double)t[k]));
+    // A grid of at most 256 bins is stored as exactly 256 and indexed by the
+    // saturating round-to-nearest byte conversion of u S + O - 1/2 (bins past
+    // the grid's end hold the top code), which saves the clamp.
     const double h = gap / 2.5, T = tmax + 2.0 * h;
     const float S = (float)(1.0 / h), O = (float)(T / h);
-    const int nb = (int)ceil(2.0 * T / h) + 1;
+    int nb = (int)ceil(2.0 * T / h) + 1;
+    const bool byte_grid = nb <= kLutByteBins;
+    if (byte_grid) nb = kLutByteBins;
     if (next + 2 * nb > TQ_CODEBOOK_TABLE_FLOATS)
       return fail(TQ_ERR_UNSUPPORTED, "codebook lookup grid does not fit the table");
     float* hdr = table + kLutHeaderOffset + 4 * (b - 1);
     hdr[0] = S;
-    hdr[1] = O;
+    hdr[1] = byte_grid ? O - 0.5f : O;
     reinterpret_cast<uint32_t*>(hdr)[2] = (uint32_t)nb;
     reinterpret_cast<uint32_t*>(hdr)[3] = (uint32_t)next;
     for (int i = 0; i < nb; ++i) {

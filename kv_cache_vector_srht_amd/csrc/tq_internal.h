@@ -21,6 +21,7 @@ constexpr int boundary_offset(int bits) { return 510 + (1 << bits) - bits - 1; }
 constexpr int kLutHeaderOffset = 1024;
 constexpr int kLutEntriesOffset = 1056;
 constexpr int kLutMaxBins = 1400;
+constexpr int kLutByteBins = 256;   // grids this small are indexed by a saturating byte conversion
 
 // Decode split-K geometry.
 constexpr int kDecodeWaves = 4;             // waves per split workgroup

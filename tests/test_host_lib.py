@@ -39,25 +39,34 @@ def test_codebook_bit_equal_to_oracle(L, bits, kind):
     assert np.array_equal(t.view(np.uint32), ot.view(np.uint32))
 
 
-def test_codebook_table_layout(L):
-    tab = tq.codebook_table(tq.LLOYD_MAX)
+@pytest.mark.parametrize("kind", [tq.LLOYD_MAX, tq.UNIFORM])
+def test_codebook_table_layout(L, kind):
+    tab = tq.codebook_table(kind)
     for b in range(1, 9):
-        c, t = O.codebook(b)
+        c, t = O.codebook(b, kind)
         co, to = (1 << b) - 2, 510 + (1 << b) - b - 1
         assert np.array_equal(tab[co:co + (1 << b)], c) and np.array_equal(tab[to:to + (1 << b) - 1], t)
     assert np.all(tab[1012:1024] == 0)
-    # lookup grids: code(u) = base + [u >= boundary] at bin floor(u S + O)
+    # lookup grids: code(u) = base + [u >= boundary] at bin floor(u S + O), or
+    # at the nearest integer for 256-bin grids (their O carries the -1/2)
     words = tab.view(np.uint32)
     rng = np.random.default_rng(0)
     for b in range(1, 9):
         gS, gO = tab[1024 + 4 * (b - 1)], tab[1024 + 4 * (b - 1) + 1]
-        nb, off = words[1024 + 4 * (b - 1) + 2], words[1024 + 4 * (b - 1) + 3]
+        nb, off = int(words[1024 + 4 * (b - 1) + 2]), int(words[1024 + 4 * (b - 1) + 3])
         ent = words[off:off + 2 * nb].reshape(nb, 2)
-        c, t = O.codebook(b)
+        c, t = O.codebook(b, kind)
+        # bin edges of the grid (integer and half-integer index points) and their neighbours
+        edges = ((np.arange(-2, nb + 2, 0.5) - np.float64(gO)) / np.float64(gS)).astype(np.float32)
         u = np.concatenate([rng.standard_normal(20000).astype(np.float32) * 2,
                             t, np.nextafter(t, np.float32(-np.inf)), np.nextafter(t, np.float32(np.inf)),
-                            np.float32([-50, 50, 0, -0.0])]).astype(np.float32)
-        bins = np.clip(np.trunc(u.astype(np.float64) * np.float64(gS) + np.float64(gO)).astype(np.int64), 0, nb - 1)
+                            edges, np.nextafter(edges, np.float32(-np.inf)), np.nextafter(edges, np.float32(np.inf)),
+                            np.float32([-50, 50, 0, -0.0, -11.32, 11.32])]).astype(np.float32)
+        x = (u.astype(np.float64) * np.float64(gS) + np.float64(gO)).astype(np.float32).astype(np.float64)
+        if nb == 256:   # byte grid: round half to even, saturate to [0, 255]
+            bins = np.clip(np.rint(x), 0, 255).astype(np.int64)
+        else:
+            bins = np.clip(np.trunc(x).astype(np.int64), 0, nb - 1)
         got = ent[bins, 0] + (u >= ent[bins, 1].view(np.float32))
         want = np.searchsorted(t, u, side="right")
         assert np.array_equal(got, want), b
