@@ -81,6 +81,11 @@ enum { TQ_DTYPE_F32 = 0, TQ_DTYPE_F16 = 1 };
  *   bits 48..51  k_bits (1..8); 0 marks an fp16 page
  *   bits 52..55  v_bits (1..8); 0 for an fp16 page
  *   bit  56      the page carries a QJL residual for its keys
+ *   bit  57      pending: the page is still filling and is stored as an fp16
+ *                page (a 32 KiB slot) until tq_append_kv writes its 64th token
+ *                and encodes it in place into the packed format the other
+ *                bits name ("TurboQuant-MLX v2.0", What's New > Dynamic Chunk
+ *                Buffering: tokens are buffered until a chunk is complete)
  *   bit  63      present
  * Packed page layout (bytes, in order):
  *   K codes   1024*k_bits : 64 streams of 128 codes; stream t = token t's
@@ -101,6 +106,7 @@ enum { TQ_DTYPE_F32 = 0, TQ_DTYPE_F16 = 1 };
 #define TQ_CACHE_COMMON_PAGES 1
 #define TQ_CACHE_OTHER_PAGES 2
 #define TQ_PAGE_QJL (1ull << 56)
+#define TQ_PAGE_PENDING (1ull << 57)
 #define TQ_PAGE_OFFSET_MASK ((1ull << 48) - 1)
 
 /* Bytes of one page: k_bits = 0 (and v_bits = 0, qjl = 0) for an fp16 page.
@@ -162,6 +168,21 @@ typedef struct tq_kv_input {
                                 4 = a page outside the pool (left untouched)     */
 } tq_kv_input;
 
+typedef struct tq_token_input {
+  const void* k;             /* device: element (b, h, j) of the new keys at
+                                k + (b*stride_b + h*stride_h + j) elements       */
+  const void* v;             /* device, same shape and strides as k              */
+  int32_t dtype;             /* TQ_DTYPE_F16 or TQ_DTYPE_F32 (rounded to fp16)   */
+  int32_t reserved;          /* 0                                                */
+  int64_t stride_b, stride_h;  /* in elements; rows 16-byte aligned             */
+  int32_t* error_flags;      /* device int or NULL: kernels OR in
+                                2 = the page at the position is not present,
+                                4 = the page is outside the pool or its pending
+                                    format is invalid (left untouched),
+                                16 = the position is past the page table,
+                                32 = the page at the position is already packed */
+} tq_token_input;
+
 typedef struct tq_query {
   const void* q;             /* device: element (b, h, j) at
                                 q + b*stride_b + h*stride_h + j elements         */
@@ -216,7 +237,8 @@ int tq_sign_mask(const int8_t* signs, int head_dim, uint32_t* mask);
 size_t tq_decode_workspace_bytes(const tq_cache* cache, int n_q_heads);
 
 /* Bytes of a cache: the sum of tq_page_bytes over the given descriptors
- * (a host copy of the page table, n entries; absent pages count zero). */
+ * (a host copy of the page table, n entries; absent pages count zero, pending
+ * pages count as fp16 pages). */
 size_t tq_cache_bytes(const uint64_t* host_pages, size_t n);
 
 const char* tq_status_string(int status);
@@ -233,6 +255,21 @@ const char* tq_last_error(void);
  * order.  Keys of QJL pages also get their sign sketch and gamma. */
 int tq_encode_kv(const tq_layer* layer, const tq_cache* cache,
                  const tq_kv_input* in, void* stream);
+
+/* One step of a decode loop ("TurboQuant-MLX v2.0", What's New > FP16
+ * Attention Sinks and Dynamic Chunk Buffering: recent tokens stay fp16 until a
+ * 64-token chunk is complete, then the chunk is compressed).  For every
+ * session b and KV head h, writes the new key and value rows (fp16) as token
+ * n_tokens[b] of the cache: row n_tokens[b] mod 64 of the page that holds it,
+ * which must be an fp16 page or a pending page.  A pending page that receives
+ * its 64th token is encoded in place (same slot) into the packed format its
+ * descriptor names, exactly as tq_encode_kv would encode those 64 fp16 rows,
+ * and its pending bit is cleared.  Then n_tokens[b] += 1 for every session.
+ * Writes the pool, the page table (pending bits) and n_tokens, which must be
+ * device memory the call may modify.  Errors found on the device are OR-ed
+ * into in->error_flags; n_tokens advances regardless. */
+int tq_append_kv(const tq_layer* layer, const tq_cache* cache, const tq_token_input* in,
+                 void* stream);
 
 /* out[b][h][0..127] (device float32, row stride 128, B x H_q rows) =
  * softmax_t(scale * q_bh . k_t) . v_t over t in [0, n_tokens[b]), where k_t,

@@ -29,7 +29,7 @@ LIB_PATH = os.path.join(_PKG, "lib", "libtq.so")
 EXPORTS = ("tq_page_bytes", "tq_page_descriptor", "tq_build_codebook", "tq_codebook_table",
            "tq_layer_params", "tq_sign_mask", "tq_decode_workspace_bytes", "tq_cache_bytes",
            "tq_status_string", "tq_last_error", "tq_encode_kv", "tq_decode_attention",
-           "tq_dequantize")
+           "tq_dequantize", "tq_append_kv")
 
 
 class TQError(RuntimeError):
@@ -56,6 +56,12 @@ class tq_kv_input(ctypes.Structure):
                 ("tok0", ctypes.c_int32), ("ntok", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64),
                 ("stride_t", ctypes.c_int64), ("error_flags", ctypes.c_void_p)]
+
+
+class tq_token_input(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64),
+                ("error_flags", ctypes.c_void_p)]
 
 
 class tq_query(ctypes.Structure):
@@ -96,6 +102,8 @@ def lib() -> ctypes.CDLL:
         L.tq_decode_attention.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
                                           ctypes.POINTER(tq_query), ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.tq_append_kv.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
+                                   ctypes.POINTER(tq_token_input), ctypes.c_void_p]
         L.tq_dequantize.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache), ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                     ctypes.c_void_p]
@@ -146,8 +154,22 @@ def sign_mask(signs):
     return m
 
 
+PAGE_PENDING = 1 << 57
+
+
+def is_pending(fmt) -> bool:
+    """A format (k_bits, v_bits, qjl, pending) with pending set: the page fills
+    as fp16 and tq_append_kv packs it into (k_bits, v_bits, qjl) when full."""
+    return len(fmt) > 3 and bool(fmt[3])
+
+
 def page_bytes(fmt) -> int:
-    kb, vb, qjl = fmt
+    """Bytes of a page slot of this format (a pending page occupies an fp16 slot)."""
+    kb, vb, qjl = fmt[:3]
+    if is_pending(fmt):
+        if lib().tq_page_bytes(int(kb), int(vb), int(bool(qjl))) == 0 or kb == 0:
+            raise TQError(f"invalid pending page format {fmt}")
+        kb, vb, qjl = 0, 0, False
     n = lib().tq_page_bytes(int(kb), int(vb), int(bool(qjl)))
     if n == 0:
         raise TQError(f"invalid page format {fmt}")
@@ -197,20 +219,25 @@ CACHE_OTHER_PAGES = 2
 
 def page_classes(formats) -> int:
     """The tq_cache.page_classes bits of a page table with these formats:
-    common = 1-4 bit K and V without QJL; other = fp16, 5-8 bit or QJL."""
+    common = 1-4 bit K and V without QJL; other = fp16, 5-8 bit or QJL (a
+    pending page counts as fp16 and as its packed format)."""
     bits = 0
     for row in formats:
         for fm in row:
-            for kb, vb, q in fm:
+            for f in fm:
+                kb, vb, q = f[:3]
                 common = 1 <= kb <= 4 and 1 <= vb <= 4 and not q
                 bits |= CACHE_COMMON_PAGES if common else CACHE_OTHER_PAGES
+                if is_pending(f):
+                    bits |= CACHE_OTHER_PAGES   # fp16 until it is packed
     return bits
 
 
 class Cache:
     """Page pool + page table + token counts for B sessions x H_kv heads.
 
-    ``formats[b][h][p]`` is (0, 0, False) for an fp16 page or
+    ``formats[b][h][p]`` is (0, 0, False) for an fp16 page, (k_bits, v_bits,
+    qjl, True) for a pending page (see append_kv), or
     (k_bits, v_bits, qjl) for a packed page.  Pages are laid out in the pool
     in (session, head, page) order.
     """
@@ -229,11 +256,13 @@ class Cache:
         for b in range(B):
             for h in range(H):
                 for p, fmt in enumerate(formats[b][h]):
-                    kb, vb, q = fmt
+                    kb, vb, q = fmt[:3]
                     n = page_bytes(fmt)
                     d = L.tq_page_descriptor(off, int(kb), int(vb), int(bool(q)))
                     if d == 0:
                         raise TQError(f"cannot describe page {fmt} at {off}")
+                    if is_pending(fmt):
+                        d |= PAGE_PENDING
                     desc[b, h, p] = d
                     self.offsets[b, h, p] = off
                     off += (n + 255) // 256 * 256
@@ -301,6 +330,21 @@ def decode_attention(layer: Layer, cache: Cache, q, out=None, workspace=None,
                                     workspace.numel() * workspace.element_size(),
                                     _stream(q.device)), "tq_decode_attention")
     return out
+
+
+def append_kv(layer: Layer, cache: Cache, k, v, error_flags=None) -> None:
+    """tq_append_kv: one new token per session, k and v of shape [B, H_kv, 128]
+    (fp16 or fp32); advances cache.n_tokens on the device."""
+    if k.shape != v.shape or k.dim() != 3 or k.shape[-1] != HEAD_DIM or k.dtype != v.dtype:
+        raise TQError(f"k and v must both be [B, H_kv, 128] of one dtype, got {tuple(k.shape)}, {tuple(v.shape)}")
+    if k.stride() != v.stride() or k.stride(-1) != 1:
+        raise TQError("k and v must share strides with a unit innermost stride")
+    if k.shape[0] != cache.n_sessions or k.shape[1] != cache.n_kv_heads:
+        raise TQError("k/v session or head count does not match the cache")
+    inp = tq_token_input(k.data_ptr(), v.data_ptr(), _dtype_code(k), 0, k.stride(0), k.stride(1),
+                         error_flags.data_ptr() if error_flags is not None else None)
+    check(lib().tq_append_kv(ctypes.byref(layer.struct), ctypes.byref(cache.struct), ctypes.byref(inp),
+                             _stream(k.device)), "tq_append_kv")
 
 
 def dequantize(layer: Layer, cache: Cache, which: int, tok0: int, ntok: int, add_qjl: bool = True,

@@ -455,9 +455,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
     // descriptors are read in parallel, one per thread)
     bool mine = false;
     for (int p = p_begin + tid; p < p_end; p += blockDim.x) {
-      const uint64_t desc = ptab[p];
-      const int kb = (int)((desc >> 48) & 15), vb = (int)((desc >> 52) & 15);
-      mine |= common_page(kb, vb, (desc & TQ_PAGE_QJL) != 0) == (CLASS == 0);
+      const PageDesc pd = read_desc(ptab[p]);
+      mine |= common_page(pd.kb, pd.vb, pd.qjl) == (CLASS == 0);
     }
     if (!__syncthreads_or(mine)) {
       if (tid < G) {
@@ -497,11 +496,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
   const int q4 = lane >> 4, i16 = lane & 15;
 
   for (int p = p_begin + wave; p < p_end; p += kDecodeWaves) {
-    const uint64_t desc = ptab[p];
-    const int kb = (int)((desc >> 48) & 15), vb = (int)((desc >> 52) & 15);
-    const bool qjl = (desc & TQ_PAGE_QJL) != 0;
-    const uint64_t off = desc & TQ_PAGE_OFFSET_MASK;
-    if (!(desc & TQ_PAGE_PRESENT) || off + page_size_dev(kb, vb, qjl) > a.pool_bytes) continue;
+    const PageDesc pd = read_desc(ptab[p]);
+    const int kb = pd.kb, vb = pd.vb;
+    const bool qjl = pd.qjl;
+    const uint64_t off = pd.off;
+    if (!pd.present || off + page_size_dev(kb, vb, qjl) > a.pool_bytes) continue;
     if (kb == 0 ? (vb != 0 || qjl) : (kb > 8 || vb < 1 || vb > 8)) continue;
     if (qjl && a.qjl_s == nullptr) continue;
     if (common_page(kb, vb, qjl) != (CLASS == 0)) continue;

@@ -38,10 +38,11 @@ __global__ __launch_bounds__(64) void dequant_kernel(DequantArgs a, const float*
   const int t = pg * PT + lane;
   const bool in_range = t >= a.tok0 && t < a.tok0 + a.ntok;
   float* dst = a.out + (((size_t)b * a.n_kv_heads + h) * a.ntok + (size_t)(t - a.tok0)) * D;
-  const int kb = (int)((desc >> 48) & 15), vb = (int)((desc >> 52) & 15);
-  const bool qjl = (desc & TQ_PAGE_QJL) != 0;
-  const uint64_t off = desc & TQ_PAGE_OFFSET_MASK;
-  const bool bad = !(desc & TQ_PAGE_PRESENT) || off + page_size_dev(kb, vb, qjl) > a.pool_bytes ||
+  const PageDesc pd = read_desc(desc);
+  const int kb = pd.kb, vb = pd.vb;
+  const bool qjl = pd.qjl;
+  const uint64_t off = pd.off;
+  const bool bad = !pd.present || off + page_size_dev(kb, vb, qjl) > a.pool_bytes ||
                    (kb == 0 && (vb != 0 || qjl)) || kb > 8 || (kb > 0 && (vb < 1 || vb > 8));
   if (bad) {
     if (in_range)

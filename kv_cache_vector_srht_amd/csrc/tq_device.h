@@ -22,6 +22,24 @@ __device__ __forceinline__ size_t page_size_dev(int kb, int vb, bool qjl) {
   return kb == 0 ? (size_t)2 * PT * D * 2 : (size_t)1024 * (kb + vb) + 512 + (qjl ? 1280 : 0);
 }
 
+// A page descriptor as the kernels read it: a pending page is an fp16 page.
+struct PageDesc {
+  uint64_t off;
+  int kb, vb;
+  bool qjl, present;
+};
+
+__device__ __forceinline__ PageDesc read_desc(uint64_t d) {
+  PageDesc p;
+  p.off = d & TQ_PAGE_OFFSET_MASK;
+  p.present = (d & TQ_PAGE_PRESENT) != 0;
+  const bool pending = (d & TQ_PAGE_PENDING) != 0;
+  p.kb = pending ? 0 : (int)((d >> 48) & 15);
+  p.vb = pending ? 0 : (int)((d >> 52) & 15);
+  p.qjl = !pending && (d & TQ_PAGE_QJL) != 0;
+  return p;
+}
+
 __device__ __forceinline__ float flip_if(float x, uint32_t neg) {
   return __uint_as_float(__float_as_uint(x) ^ (neg << 31));
 }

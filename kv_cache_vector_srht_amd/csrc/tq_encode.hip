@@ -222,9 +222,10 @@ __global__ __launch_bounds__(64) void encode_kernel(EncodeArgs a, const uint64_t
     if (lane == 0) raise_flag(a.err, 2);
     return;
   }
-  const int kb = (int)((desc >> 48) & 15), vb = (int)((desc >> 52) & 15);
-  const bool qjl = (desc & TQ_PAGE_QJL) != 0;
-  const uint64_t off = desc & TQ_PAGE_OFFSET_MASK;
+  const PageDesc pd = read_desc(desc);
+  const int kb = pd.kb, vb = pd.vb;
+  const bool qjl = pd.qjl;
+  const uint64_t off = pd.off;
   const bool bad_fmt = kb == 0 ? (vb != 0 || qjl) : (kb > 8 || vb < 1 || vb > 8);
   if (bad_fmt || off + page_size_dev(kb, vb, qjl) > a.pool_bytes) {
     if (lane == 0) raise_flag(a.err, 4);
@@ -571,9 +572,10 @@ __global__ __launch_bounds__(kEncodeBlock) void encode_pages_kernel(EncodeArgs a
       if (tid == 0) raise_flag(a.err, 2);
       continue;
     }
-    const int kb = (int)((desc >> 48) & 15), vb = (int)((desc >> 52) & 15);
-    const bool qjl = (desc & TQ_PAGE_QJL) != 0;
-    const uint64_t off = desc & TQ_PAGE_OFFSET_MASK;
+    const PageDesc pd = read_desc(desc);
+    const int kb = pd.kb, vb = pd.vb;
+    const bool qjl = pd.qjl;
+    const uint64_t off = pd.off;
     const bool bad_fmt = kb == 0 ? (vb != 0 || qjl) : (kb > 8 || vb < 1 || vb > 8);
     if (bad_fmt || off + page_size_dev(kb, vb, qjl) > a.pool_bytes) {
       if (tid == 0) raise_flag(a.err, 4);
@@ -670,6 +672,130 @@ __global__ __launch_bounds__(kEncodeBlock) void encode_pages_kernel(EncodeArgs a
 }
 
 
+// ------------------------------------------------------- decode-loop append
+struct AppendArgs {
+  const void* k;
+  const void* v;
+  int dtype;
+  int64_t sb, sh;
+  int32_t* err;
+  uint64_t* pages;
+  int n_kv_heads, max_pages;
+  const int32_t* n_tokens;
+  char* pool;
+  uint64_t pool_bytes;
+  const uint32_t* sign_mask;
+  const float* k_table;
+  const float* v_table;
+  const float* qjl_s;
+};
+
+// One wavefront per (KV head, session): writes the new token's rows into its
+// fp16 or pending page; when a pending page receives its 64th token, encodes
+// the page in place with the per-token encoder (keys, then values; every lane
+// loads its row before any lane stores, and the key part ends below the value
+// rows) and clears the pending bit.
+__global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
+  __shared__ float lds_thr[256];
+  __shared__ float lds_cent[256];
+  __shared__ uint32_t lds_rows[PT * kEncodeRowBytes / 4];
+  const int lane = threadIdx.x, h = blockIdx.x, b = blockIdx.y;
+  const int t = a.n_tokens[b];
+  if (t < 0 || t >= a.max_pages * PT) {
+    if (lane == 0) raise_flag(a.err, 16);
+    return;
+  }
+  const int r = t & (PT - 1);
+  uint64_t* dp = a.pages + ((size_t)b * a.n_kv_heads + h) * a.max_pages + t / PT;
+  const uint64_t desc = *dp;
+  if (!(desc & TQ_PAGE_PRESENT)) {
+    if (lane == 0) raise_flag(a.err, 2);
+    return;
+  }
+  const bool pending = (desc & TQ_PAGE_PENDING) != 0;
+  const int kb = (int)((desc >> 48) & 15), vb = (int)((desc >> 52) & 15);
+  const bool qjl = (desc & TQ_PAGE_QJL) != 0;
+  const uint64_t off = desc & TQ_PAGE_OFFSET_MASK;
+  if (!pending && kb != 0) {
+    if (lane == 0) raise_flag(a.err, 32);
+    return;
+  }
+  const bool bad_target = pending && (kb < 1 || kb > 8 || vb < 1 || vb > 8 || (qjl && !a.qjl_s));
+  if (bad_target || off + page_size_dev(0, 0, false) > a.pool_bytes) {
+    if (lane == 0) raise_flag(a.err, 4);
+    return;
+  }
+  char* page = a.pool + off;
+  if (lane < 32) {
+    const int part = lane >> 4, c8 = (lane & 15) * 8;
+    const void* src = part == 0 ? a.k : a.v;
+    const size_t ee = (size_t)b * a.sb + (size_t)h * a.sh + c8;
+    uint4 out;
+    if (a.dtype == TQ_DTYPE_F16) {
+      out = *reinterpret_cast<const uint4*>(reinterpret_cast<const __half*>(src) + ee);
+    } else {
+      const float4 f0 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(src) + ee);
+      const float4 f1 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(src) + ee + 4);
+      __half2 h0 = __floats2half2_rn(f0.x, f0.y), h1 = __floats2half2_rn(f0.z, f0.w);
+      __half2 h2 = __floats2half2_rn(f1.x, f1.y), h3 = __floats2half2_rn(f1.z, f1.w);
+      out = make_uint4(*reinterpret_cast<uint32_t*>(&h0), *reinterpret_cast<uint32_t*>(&h1),
+                       *reinterpret_cast<uint32_t*>(&h2), *reinterpret_cast<uint32_t*>(&h3));
+    }
+    *reinterpret_cast<uint4*>(page + part * PT * D * 2 + ((size_t)r * D + c8) * 2) = out;
+  }
+  if (!pending || r != PT - 1) return;
+  // the page is complete: make the row just written visible to every lane
+  __threadfence();
+  __syncthreads();
+  uint32_t m[4];
+#pragma clang loop unroll(full)
+  for (int w = 0; w < 4; ++w) m[w] = a.sign_mask[w];
+  for (int part = 0; part < 2; ++part) {
+    const int B = part == 0 ? kb : vb;
+    const float* table = part == 0 ? a.k_table : a.v_table;
+    const int L = 1 << B;
+    for (int i = lane; i < L; i += 64) {
+      lds_cent[i] = table[centroid_offset(B) + i];
+      if (i < L - 1) lds_thr[i] = table[boundary_offset(B) + i];
+    }
+    float x[D];
+    load_row(page + part * PT * D * 2, TQ_DTYPE_F16, (size_t)lane * D, x);
+    __syncthreads();
+    char* part_base = part == 0 ? page : page + 1024 * kb + 256 + (qjl ? 1280 : 0);
+    if (part == 0) {
+      switch (B) {
+        case 1: encode_packed<0, 1>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+        case 2: encode_packed<0, 2>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+        case 3: encode_packed<0, 3>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+        case 4: encode_packed<0, 4>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+        case 5: encode_packed<0, 5>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+        case 6: encode_packed<0, 6>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+        case 7: encode_packed<0, 7>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+        default: encode_packed<0, 8>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+      }
+    } else {
+      switch (B) {
+        case 1: encode_packed<1, 1>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+        case 2: encode_packed<1, 2>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+        case 3: encode_packed<1, 3>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+        case 4: encode_packed<1, 4>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+        case 5: encode_packed<1, 5>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+        case 6: encode_packed<1, 6>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+        case 7: encode_packed<1, 7>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+        default: encode_packed<1, 8>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+      }
+    }
+    __syncthreads();
+  }
+  if (lane == 0) *dp = desc & ~TQ_PAGE_PENDING;
+}
+
+// n_tokens[b] += 1 for every session, after the append above.
+__global__ __launch_bounds__(256) void advance_kernel(int32_t* n_tokens, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) n_tokens[i] += 1;
+}
+
 }  // namespace
 }  // namespace dev
 }  // namespace tq
@@ -737,6 +863,43 @@ int tq_encode_kv(const tq_layer* layer, const tq_cache* cache, const tq_kv_input
     st2 = launch_status("encode QJL keys");
   }
   return st2;
+}
+
+int tq_append_kv(const tq_layer* layer, const tq_cache* cache, const tq_token_input* in, void* stream) {
+  int st = check_layer(layer);
+  if (st) return st;
+  if ((st = check_cache(cache))) return st;
+  if (!in || !in->k || !in->v) return fail(TQ_ERR_INVALID_ARG, "null input");
+  if (in->dtype != TQ_DTYPE_F16 && in->dtype != TQ_DTYPE_F32)
+    return fail(TQ_ERR_INVALID_ARG, "unknown input dtype %d", in->dtype);
+  if (in->stride_b < 0 || in->stride_h < 0) return fail(TQ_ERR_INVALID_ARG, "negative stride");
+  const int esz = in->dtype == TQ_DTYPE_F16 ? 2 : 4;
+  if (!aligned16(in->k) || !aligned16(in->v) || (in->stride_b * esz) % 16 || (in->stride_h * esz) % 16)
+    return fail(TQ_ERR_ALIGNMENT, "input rows must be 16-byte aligned");
+  if (((uintptr_t)in->error_flags & 3) != 0) return fail(TQ_ERR_ALIGNMENT, "error_flags misaligned");
+  AppendArgs a;
+  a.k = in->k;
+  a.v = in->v;
+  a.dtype = in->dtype;
+  a.sb = in->stride_b;
+  a.sh = in->stride_h;
+  a.err = in->error_flags;
+  a.pages = const_cast<uint64_t*>(cache->pages);
+  a.n_kv_heads = cache->n_kv_heads;
+  a.max_pages = cache->max_pages;
+  a.n_tokens = cache->n_tokens;
+  a.pool = reinterpret_cast<char*>(cache->pool);
+  a.pool_bytes = cache->pool_bytes;
+  a.sign_mask = layer->sign_mask;
+  a.k_table = layer->k_table;
+  a.v_table = layer->v_table;
+  a.qjl_s = layer->qjl_s;
+  hipStream_t s = (hipStream_t)stream;
+  hipLaunchKernelGGL(append_kernel, dim3(cache->n_kv_heads, cache->n_sessions), dim3(64), 0, s, a);
+  if ((st = launch_status("append"))) return st;
+  hipLaunchKernelGGL(advance_kernel, dim3((cache->n_sessions + 255) / 256), dim3(256), 0, s,
+                     const_cast<int32_t*>(cache->n_tokens), cache->n_sessions);
+  return launch_status("advance");
 }
 
 }  // extern "C"

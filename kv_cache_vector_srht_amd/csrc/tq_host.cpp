@@ -293,7 +293,9 @@ size_t tq_cache_bytes(const uint64_t* host_pages, size_t n) {
   for (size_t i = 0; i < n; ++i) {
     uint64_t d = host_pages[i];
     if (!(d & TQ_PAGE_PRESENT)) continue;
-    total += tq_page_bytes((int)((d >> 48) & 15), (int)((d >> 52) & 15), (d & TQ_PAGE_QJL) ? 1 : 0);
+    total += (d & TQ_PAGE_PENDING) ? tq_page_bytes(0, 0, 0)
+                                   : tq_page_bytes((int)((d >> 48) & 15), (int)((d >> 52) & 15),
+                                                   (d & TQ_PAGE_QJL) ? 1 : 0);
   }
   return total;
 }
