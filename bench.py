@@ -36,6 +36,9 @@ def parse():
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
+    ap.add_argument("--loop-steps", type=int, default=64,
+                    help="decode-loop steps (append one token per session + decode attention, "
+                         "every layer) measured after the main step; 0 skips")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (calibrates "
                          "the HBM byte counters) and exit")
@@ -169,6 +172,46 @@ def cpu_baseline(w, layers_data, seconds: float):
     }
 
 
+def decode_loop(w, layers, inputs, queries, outs, wss, steps, dev):
+    """The decode loop the cache serves: every step appends one token per
+    session to every layer (tq_append_kv into a pending fp16 tail page, packed
+    in place when its 64th token arrives) and runs decode attention over every
+    layer.  Each layer's cache is the workload's, prefilled by encode, plus one
+    pending tail page per (session, KV head) in the format of its last page."""
+    import torch
+    import kv_cache_vector_srht_amd as tq
+    caches, news = [], []
+    for l in range(w.n_layers):
+        fm = [[list(r) + [tuple(r[-1][:3]) + (True,)] for r in row] for row in w.formats[l]]
+        c = tq.Cache(fm, [w.n_tokens] * w.batch, dev)
+        k, v = inputs[l]
+        tq.encode_kv(layers[l], c, k, v, tok0=0)
+        caches.append(c)
+        g = torch.Generator(device=dev).manual_seed(7 + l)
+        news.append(torch.randn((steps, w.batch, w.n_kv_heads, 2, 128), generator=g, device=dev).to(k.dtype))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    t_append = t_decode = 0.0
+    for i in range(steps):
+        ev[0].record(stream)
+        for l in range(w.n_layers):
+            tq.append_kv(layers[l], caches[l], news[l][i, :, :, 0], news[l][i, :, :, 1])
+        ev[1].record(stream)
+        for l in range(w.n_layers):
+            tq.decode_attention(layers[l], caches[l], queries[l], out=outs[l], workspace=wss[l])
+        ev[2].record(stream)
+        ev[2].synchronize()
+        t_append += ev[0].elapsed_time(ev[1])
+        t_decode += ev[1].elapsed_time(ev[2])
+    ms = (t_append + t_decode) / steps
+    return {"steps": steps, "ms_per_step": round(ms, 3),
+            "append_us_per_layer": round(t_append / steps / w.n_layers * 1e3, 2),
+            "decode_us_per_layer": round(t_decode / steps / w.n_layers * 1e3, 2),
+            "tokens_per_s": round(w.batch / (ms / 1e3), 1),
+            "context": f"{w.n_tokens} + 1..{steps} tokens, every layer, one new token per session per step"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -283,6 +326,8 @@ def main():
         "decode_bytes_per_step": int(dec_bytes), "encode_bytes_per_step": int(enc_bytes),
         "roofline": roof,
     }
+    if args.loop_steps > 0:
+        line["decode_loop"] = decode_loop(w, layers, inputs, queries, outs, wss, args.loop_steps, dev)
     if not args.no_cpu_baseline:
         kv_host = {}
 
