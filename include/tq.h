@@ -105,6 +105,7 @@ enum { TQ_DTYPE_F32 = 0, TQ_DTYPE_F16 = 1 };
 #define TQ_PAGE_PRESENT (1ull << 63)
 #define TQ_CACHE_COMMON_PAGES 1
 #define TQ_CACHE_OTHER_PAGES 2
+#define TQ_CACHE_WIDE_PAGES 4
 #define TQ_PAGE_QJL (1ull << 56)
 #define TQ_PAGE_PENDING (1ull << 57)
 #define TQ_PAGE_OFFSET_MASK ((1ull << 48) - 1)
@@ -138,11 +139,14 @@ typedef struct tq_cache {
   int32_t page_classes;      /* which page classes the table holds, as the host
                                 that built it knows: TQ_CACHE_COMMON_PAGES (a
                                 1-4 bit K and V page without QJL) |
-                                TQ_CACHE_OTHER_PAGES (fp16, 5-8 bit or QJL);
-                                decode attention skips the work of a class whose
-                                bit is clear.  0 = unknown (both run).  A set
-                                that leaves out a class present in the table
-                                makes decode ignore those pages.                 */
+                                TQ_CACHE_WIDE_PAGES (5-8 bit K and V, no QJL) |
+                                TQ_CACHE_OTHER_PAGES (fp16, QJL or mixed
+                                widths; a pending page counts here and in the
+                                class of its packed format); decode attention
+                                skips the work of a class whose bit is clear.
+                                0 = unknown (all run).  A set that leaves out a
+                                class present in the table makes decode ignore
+                                those pages.                                     */
   const int32_t* n_tokens;   /* device [B]: tokens cached per session; decode
                                 attends to tokens [0, n_tokens[b]) and needs
                                 n_tokens[b] <= 64 * max_pages                    */

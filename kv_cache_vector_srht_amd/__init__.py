@@ -215,19 +215,25 @@ class Layer:
 # ------------------------------------------------------------------- cache
 CACHE_COMMON_PAGES = 1
 CACHE_OTHER_PAGES = 2
+CACHE_WIDE_PAGES = 4
 
 
 def page_classes(formats) -> int:
     """The tq_cache.page_classes bits of a page table with these formats:
-    common = 1-4 bit K and V without QJL; other = fp16, 5-8 bit or QJL (a
-    pending page counts as fp16 and as its packed format)."""
+    common = 1-4 bit K and V without QJL; wide = 5-8 bit K and V without QJL;
+    other = fp16, QJL or mixed widths (a pending page counts as fp16 and as its
+    packed format)."""
     bits = 0
     for row in formats:
         for fm in row:
             for f in fm:
                 kb, vb, q = f[:3]
-                common = 1 <= kb <= 4 and 1 <= vb <= 4 and not q
-                bits |= CACHE_COMMON_PAGES if common else CACHE_OTHER_PAGES
+                if 1 <= kb <= 4 and 1 <= vb <= 4 and not q:
+                    bits |= CACHE_COMMON_PAGES
+                elif kb >= 5 and vb >= 5 and not q:
+                    bits |= CACHE_WIDE_PAGES
+                else:
+                    bits |= CACHE_OTHER_PAGES
                 if is_pending(f):
                     bits |= CACHE_OTHER_PAGES   # fp16 until it is packed
     return bits

@@ -33,7 +33,8 @@ struct DecodeArgs {
   const float* v_table;
   const float* qjl_s;
   int n_splits, pages_per_split;            // common class
-  int n_splits_general, pages_per_split_general;
+  int n_splits_general, pages_per_split_general;   // wide and other classes
+  int part_base[3], n_partials;                     // first partial of each class, total
   float* wsq;   // [B][H_q][384]: rotated q, plain q, S q (pre-scaled)
   float* wsp;   // [B][H_q][n_splits][kPartialFloats]: m, l, -, -, acc[128]
   float* out;
@@ -422,12 +423,16 @@ __device__ __forceinline__ void softmax_update(float (&s)[G], float (&m)[G], flo
   }
 }
 
-// Page classes: the common packed formats (k_bits, v_bits <= 4, no QJL) run
-// in a kernel compiled for them alone (fewer registers, more waves in flight);
-// the rest (fp16 pages, 5-8 bit codes, QJL keys) runs in the general kernel.
-// Each writes its own partials; the combine merges both.
-__device__ __forceinline__ bool common_page(int kb, int vb, bool qjl) {
-  return kb >= 1 && kb <= 4 && vb >= 1 && vb <= 4 && !qjl;
+// Page classes, each run by a kernel instantiation compiled for its formats
+// alone (fewer code paths, fewer registers, more waves in flight):
+//   0 common: k_bits, v_bits <= 4, no QJL;
+//   1 wide:   k_bits, v_bits >= 5, no QJL (the few important heads);
+//   2 other:  fp16 pages, QJL keys and mixed widths.
+// Each writes its own partials; the combine merges them.
+__device__ __forceinline__ int page_class(int kb, int vb, bool qjl) {
+  if (kb >= 1 && kb <= 4 && vb >= 1 && vb <= 4 && !qjl) return 0;
+  if (kb >= 5 && vb >= 5 && !qjl) return 1;
+  return 2;
 }
 
 template <int G, int CLASS>
@@ -439,10 +444,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
   const int hq0 = hkv * G;
-  // partials [B][H_q][n_splits common, then n_splits_general general]
-  const size_t head_stride = (size_t)(a.n_splits + a.n_splits_general) * kPartialFloats;
+  // partials [B][H_q][n_partials]: the classes that run, in class order
+  const size_t head_stride = (size_t)a.n_partials * kPartialFloats;
   float* part = wsp + ((size_t)b * a.n_q_heads + hq0) * head_stride +
-                ((size_t)(CLASS == 0 ? 0 : a.n_splits) + split) * kPartialFloats;
+                ((size_t)a.part_base[CLASS] + split) * kPartialFloats;
   const int pps = CLASS == 0 ? a.pages_per_split : a.pages_per_split_general;
 
   const int ntok = max(0, a.n_tokens[b]);
@@ -456,7 +461,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
     bool mine = false;
     for (int p = p_begin + tid; p < p_end; p += blockDim.x) {
       const PageDesc pd = read_desc(ptab[p]);
-      mine |= common_page(pd.kb, pd.vb, pd.qjl) == (CLASS == 0);
+      mine |= page_class(pd.kb, pd.vb, pd.qjl) == CLASS;
     }
     if (!__syncthreads_or(mine)) {
       if (tid < G) {
@@ -503,13 +508,13 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
     if (!pd.present || off + page_size_dev(kb, vb, qjl) > a.pool_bytes) continue;
     if (kb == 0 ? (vb != 0 || qjl) : (kb > 8 || vb < 1 || vb > 8)) continue;
     if (qjl && a.qjl_s == nullptr) continue;
-    if (common_page(kb, vb, qjl) != (CLASS == 0)) continue;
+    if (page_class(kb, vb, qjl) != CLASS) continue;
     const char* page = a.pool + off;
     const int valid = min(PT, ntok - p * PT);
     float s[G], alpha[G];
     const char* vblk = page + 1024 * kb + 256;
     float nv = 1.f;
-    if (CLASS == 1 && kb == 0) {
+    if (CLASS == 2 && kb == 0) {
       key_scores_fp16<G>(page, lane, qrow + D * G, s);
     } else {
       if constexpr (CLASS == 0) {
@@ -518,6 +523,13 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
           case 2: key_scores<2, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
           case 3: key_scores<3, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
           default: key_scores<4, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
+        }
+      } else if constexpr (CLASS == 1) {
+        switch (kb) {
+          case 5: key_scores_wide<5, G>(page, lane, qrow, sm.kcent, s); break;
+          case 6: key_scores_wide<6, G>(page, lane, qrow, sm.kcent, s); break;
+          case 7: key_scores_wide<7, G>(page, lane, qrow, sm.kcent, s); break;
+          default: key_scores_wide<8, G>(page, lane, qrow, sm.kcent, s); break;
         }
       } else {
         switch (kb) {
@@ -534,7 +546,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
       const float nk = reinterpret_cast<const float*>(page + 1024 * kb)[lane];
 #pragma clang loop unroll(full)
       for (int h = 0; h < G; ++h) s[h] *= nk;
-      if (CLASS == 1 && qjl) {
+      if (CLASS == 2 && qjl) {
         float t[G];
         qjl_scores<G>(vblk, lane, qrow + 2 * D * G, t);
         const float gamma = reinterpret_cast<const float*>(vblk + 1024)[lane];
@@ -562,7 +574,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
 #pragma clang loop unroll(full)
     for (int h = 0; h < G; ++h) wv[lane * G + h] = s[h] * nv;
     wave_lds_sync();
-    if (CLASS == 1 && kb == 0) {
+    if (CLASS == 2 && kb == 0) {
       uint32_t dm[8];
       const uint32_t dword = a.sign_mask[i16 >> 2];
 #pragma clang loop unroll(full)
@@ -574,6 +586,13 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
         case 2: value_accum<2, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
         case 3: value_accum<3, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
         default: value_accum<4, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
+      }
+    } else if constexpr (CLASS == 1) {
+      switch (vb) {
+        case 5: value_accum_wide<5, G>(vblk, lane, wv, sm.vcent, acc); break;
+        case 6: value_accum_wide<6, G>(vblk, lane, wv, sm.vcent, acc); break;
+        case 7: value_accum_wide<7, G>(vblk, lane, wv, sm.vcent, acc); break;
+        default: value_accum_wide<8, G>(vblk, lane, wv, sm.vcent, acc); break;
       }
     } else {
       switch (vb) {
@@ -656,7 +675,7 @@ __global__ __launch_bounds__(128 * kCombineGroups) void combine_kernel(DecodeArg
   const int nthr = 128 * kCombineGroups;
   const int row = blockIdx.x;
   const int b = row / a.n_q_heads;
-  const int ns = a.n_splits + a.n_splits_general;   // both page classes
+  const int ns = a.n_partials;   // every class that ran
   const float* part = a.wsp + (size_t)row * ns * kPartialFloats;
   float* o = a.out + (size_t)row * D;
   // global max over partials
@@ -673,7 +692,6 @@ __global__ __launch_bounds__(128 * kCombineGroups) void combine_kernel(DecodeArg
     return;
   }
   // weights, the denominator and the list of non-empty partials
-  float lloc = 0.f;
   int total = 0;
   for (int base = 0; base < ns; base += nthr) {
     const int s = base + tid;
@@ -681,7 +699,6 @@ __global__ __launch_bounds__(128 * kCombineGroups) void combine_kernel(DecodeArg
     if (s < ns) {
       const float ms = part[(size_t)s * kPartialFloats];
       f = ms == -INFINITY ? 0.f : exp2f(ms - M);
-      lloc = fmaf(part[(size_t)s * kPartialFloats + 1], f, lloc);
       wgt[s] = f;
     }
     const uint64_t bal = __ballot(f != 0.f);
@@ -696,6 +713,14 @@ __global__ __launch_bounds__(128 * kCombineGroups) void combine_kernel(DecodeArg
     }
     if (f != 0.f) list[off + __popcll(bal & ((1ull << lane) - 1ull))] = s;
     total = all;
+  }
+  __syncthreads();
+  // the denominator, summed over the list in rank order, so that the result
+  // does not depend on where the partials sit (which classes ran)
+  float lloc = 0.f;
+  for (int k = tid; k < total; k += nthr) {
+    const int s = list[k];
+    lloc = fmaf(part[(size_t)s * kPartialFloats + 1], wgt[s], lloc);
   }
   lloc = wave_sum(lloc);
   __syncthreads();
@@ -777,8 +802,8 @@ int tq_decode_attention(const tq_layer* layer, const tq_cache* cache, const tq_q
   if (!(query->softmax_scale >= 0.f) || isinf(query->softmax_scale))
     return fail(TQ_ERR_INVALID_ARG, "bad softmax scale");
   SplitPlan sp = split_plan(cache->n_sessions, cache->n_kv_heads, cache->max_pages);
-  if (sp.n_splits + sp.n_splits_general > kMaxPartials)   // the combine stages their weights in LDS
-    return fail(TQ_ERR_UNSUPPORTED, "%d partials per row exceed %d", sp.n_splits + sp.n_splits_general,
+  if (sp.n_splits + 2 * sp.n_splits_general > kMaxPartials)   // the combine stages their weights in LDS
+    return fail(TQ_ERR_UNSUPPORTED, "%d partials per row exceed %d", sp.n_splits + 2 * sp.n_splits_general,
                 kMaxPartials);
   const size_t need = decode_workspace_bytes(cache->n_sessions, query->n_q_heads, sp);
   if (workspace_bytes < need)
@@ -803,10 +828,19 @@ int tq_decode_attention(const tq_layer* layer, const tq_cache* cache, const tq_q
   a.v_table = layer->v_table;
   a.qjl_s = layer->qjl_s;
   // A page class the host says is absent gets no launch and no partials.
-  const bool run_common = cache->page_classes == 0 || (cache->page_classes & TQ_CACHE_COMMON_PAGES);
-  const bool run_other = cache->page_classes == 0 || (cache->page_classes & TQ_CACHE_OTHER_PAGES);
-  if (!run_common) sp.n_splits = 0;
-  if (!run_other) sp.n_splits_general = 0;
+  const int cls = cache->page_classes == 0
+                      ? (TQ_CACHE_COMMON_PAGES | TQ_CACHE_WIDE_PAGES | TQ_CACHE_OTHER_PAGES)
+                      : cache->page_classes;
+  const bool run_common = (cls & TQ_CACHE_COMMON_PAGES) != 0;
+  const bool run_wide = (cls & TQ_CACHE_WIDE_PAGES) != 0;
+  const bool run_other = (cls & TQ_CACHE_OTHER_PAGES) != 0;
+  const int n_common = run_common ? sp.n_splits : 0;
+  const int n_wide = run_wide ? sp.n_splits_general : 0;
+  const int n_other = run_other ? sp.n_splits_general : 0;
+  a.part_base[0] = 0;
+  a.part_base[1] = n_common;
+  a.part_base[2] = n_common + n_wide;
+  a.n_partials = n_common + n_wide + n_other;
   a.n_splits = sp.n_splits;
   a.pages_per_split = sp.pages_per_split;
   a.n_splits_general = sp.n_splits_general;
@@ -830,12 +864,21 @@ int tq_decode_attention(const tq_layer* layer, const tq_cache* cache, const tq_q
     }
     if ((st = launch_status("split (common pages)"))) return st;
   }
-  if (run_other) {
+  if (run_wide) {
     switch (G) {
       case 1: hipLaunchKernelGGL((split_kernel<1, 1>), ggrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
       case 2: hipLaunchKernelGGL((split_kernel<2, 1>), ggrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
       case 4: hipLaunchKernelGGL((split_kernel<4, 1>), ggrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
       default: hipLaunchKernelGGL((split_kernel<8, 1>), ggrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
+    }
+    if ((st = launch_status("split (wide pages)"))) return st;
+  }
+  if (run_other) {
+    switch (G) {
+      case 1: hipLaunchKernelGGL((split_kernel<1, 2>), ggrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
+      case 2: hipLaunchKernelGGL((split_kernel<2, 2>), ggrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
+      case 4: hipLaunchKernelGGL((split_kernel<4, 2>), ggrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
+      default: hipLaunchKernelGGL((split_kernel<8, 2>), ggrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
     }
     if ((st = launch_status("split (other pages)"))) return st;
   }

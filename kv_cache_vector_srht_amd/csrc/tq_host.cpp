@@ -330,9 +330,9 @@ SplitPlan split_plan(int n_sessions, int n_kv_heads, int max_pages) {
 
 size_t decode_workspace_bytes(int n_sessions, int n_q_heads, const SplitPlan& sp) {
   const size_t rows = (size_t)n_sessions * n_q_heads;
-  // query prep, then the partials of both page classes
+  // query prep, then the partials of the three page classes
   return sizeof(float) * rows *
-         (kQPrepFloats + (size_t)(sp.n_splits + sp.n_splits_general) * kPartialFloats);
+         (kQPrepFloats + (size_t)(sp.n_splits + 2 * sp.n_splits_general) * kPartialFloats);
 }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
@@ -366,7 +366,7 @@ int check_cache(const tq_cache* C) {
   if (((uintptr_t)C->pages & 7) != 0 || ((uintptr_t)C->n_tokens & 3) != 0)
     return fail(TQ_ERR_ALIGNMENT, "page table / token counts misaligned");
   if (C->pool_bytes == 0) return fail(TQ_ERR_INVALID_ARG, "empty pool");
-  if (C->page_classes & ~(TQ_CACHE_COMMON_PAGES | TQ_CACHE_OTHER_PAGES))
+  if (C->page_classes & ~(TQ_CACHE_COMMON_PAGES | TQ_CACHE_OTHER_PAGES | TQ_CACHE_WIDE_PAGES))
     return fail(TQ_ERR_INVALID_ARG, "unknown page_classes bits 0x%x", C->page_classes);
   return TQ_OK;
 }

@@ -28,12 +28,12 @@ constexpr int kDecodeWaves = 4;             // waves per split workgroup
 constexpr int kTargetSplitGroups = 1024;    // workgroups the split grid aims for
 constexpr int kQPrepFloats = 3 * 128;       // rotated q, plain q, S q (all pre-scaled)
 constexpr int kPartialFloats = 4 + 128;     // m, l, (pad), acc[128]
-constexpr int kMaxPartials = 5120;          // partials per (session, query head), both classes
+constexpr int kMaxPartials = 5120;          // partials per (session, query head), all classes
 
 // Split-K geometry: the common class (1-4 bit codebook pages without QJL)
-// covers the page table in ranges of pages_per_split pages; the general class
-// (fp16, 5-8 bit, QJL: heavier per page, and its blocks run fewer waves) in
-// ranges half as long.
+// covers the page table in ranges of pages_per_split pages; the wide (5-8 bit)
+// and other (fp16, QJL, mixed) classes, heavier per page and run with fewer
+// waves per SIMD, in ranges half as long.
 struct SplitPlan {
   int n_splits;
   int pages_per_split;

@@ -174,8 +174,8 @@ def test_deterministic(dev):
 
 def test_page_class_hint(dev):
     """Decode with the page-class bits the binding derives equals decode with
-    the bits cleared (0 = unknown: both classes run), bit for bit, for tables
-    with common pages only, other pages only, and both."""
+    the bits cleared (0 = unknown: every class runs), bit for bit, for tables
+    with common pages only, other pages only, and common and wide pages."""
     import kv_cache_vector_srht_amd as tq
     cases = [(W.make_workload(3, {"n_tokens": 64 * 5, "batch": 2}), l) for l in (0, 2)]
     cases.append((W.make_workload(4, {"n_tokens": 64 * 4 + 9, "batch": 2}), 0))
@@ -193,4 +193,4 @@ def test_page_class_hint(dev):
         cache.struct.page_classes = 0
         unknown = _np(tq.decode_attention(layer, cache, q))
         assert np.array_equal(hinted, unknown)
-    assert seen == {1, 2, 3}
+    assert seen == {1, 2, 5}

@@ -110,7 +110,7 @@ def test_cache_bytes_and_workspace(L):
     c = tq.tq_cache(4, 8, 512, 0, None, None, None, 0)
     n = L.tq_decode_workspace_bytes(ctypes.byref(c), 32)
     # 32 units x 512 pages over ~1024 groups: 16 pages per split, 32 splits
-    assert n == 4 * (4 * 32 * 384 + 4 * 32 * (32 + 64) * 132)
+    assert n == 4 * (4 * 32 * 384 + 4 * 32 * (32 + 2 * 64) * 132)
     c0 = tq.tq_cache(0, 8, 512, 0, None, None, None, 0)
     assert L.tq_decode_workspace_bytes(ctypes.byref(c0), 32) == 0
 
@@ -207,7 +207,10 @@ def test_page_classes_bits():
     import kv_cache_vector_srht_amd as tq
     assert tq.page_classes([[[W.packed(3, 2, False), W.packed(1, 1, False)]]]) == tq.CACHE_COMMON_PAGES
     assert tq.page_classes([[[W.FP16, W.packed(2, 2, True)]]]) == tq.CACHE_OTHER_PAGES
-    assert tq.page_classes([[[W.packed(4, 4, False)], [W.packed(8, 8, False)]]]) == 3
+    assert tq.page_classes([[[W.packed(4, 4, False)], [W.packed(8, 8, False)]]]) == \
+        tq.CACHE_COMMON_PAGES | tq.CACHE_WIDE_PAGES
+    assert tq.page_classes([[[W.packed(4, 6, False), W.packed(6, 6, True)]]]) == tq.CACHE_OTHER_PAGES
+    assert tq.page_classes([[[(3, 2, False, True)]]]) == tq.CACHE_COMMON_PAGES | tq.CACHE_OTHER_PAGES
     w3 = W.make_workload(3, {"n_tokens": 128, "batch": 1})
     assert tq.page_classes(w3.formats[0]) == tq.CACHE_COMMON_PAGES
-    assert tq.page_classes(w3.formats[2]) == 3
+    assert tq.page_classes(w3.formats[2]) == tq.CACHE_COMMON_PAGES | tq.CACHE_WIDE_PAGES
