@@ -33,7 +33,8 @@ struct DecodeArgs {
   const float* v_table;
   const float* qjl_s;
   int n_splits, pages_per_split;            // common class
-  int n_splits_general, pages_per_split_general;   // wide and other classes
+  int n_splits_general, pages_per_split_general;   // other class
+  int n_splits_wide, pages_per_split_wide;         // wide class
   int part_base[3], n_partials;                     // first partial of each class, total
   float* wsq;   // [B][H_q][384]: rotated q, plain q, S q (pre-scaled)
   float* wsp;   // [B][H_q][n_splits][kPartialFloats]: m, l, -, -, acc[128]
@@ -448,7 +449,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
   const size_t head_stride = (size_t)a.n_partials * kPartialFloats;
   float* part = wsp + ((size_t)b * a.n_q_heads + hq0) * head_stride +
                 ((size_t)a.part_base[CLASS] + split) * kPartialFloats;
-  const int pps = CLASS == 0 ? a.pages_per_split : a.pages_per_split_general;
+  const int pps = CLASS == 0 ? a.pages_per_split : CLASS == 1 ? a.pages_per_split_wide : a.pages_per_split_general;
 
   const int ntok = max(0, a.n_tokens[b]);
   const int npages = min(a.max_pages, (ntok + PT - 1) / PT);   // never past the table row
@@ -802,9 +803,9 @@ int tq_decode_attention(const tq_layer* layer, const tq_cache* cache, const tq_q
   if (!(query->softmax_scale >= 0.f) || isinf(query->softmax_scale))
     return fail(TQ_ERR_INVALID_ARG, "bad softmax scale");
   SplitPlan sp = split_plan(cache->n_sessions, cache->n_kv_heads, cache->max_pages);
-  if (sp.n_splits + 2 * sp.n_splits_general > kMaxPartials)   // the combine stages their weights in LDS
-    return fail(TQ_ERR_UNSUPPORTED, "%d partials per row exceed %d", sp.n_splits + 2 * sp.n_splits_general,
-                kMaxPartials);
+  const int max_partials = sp.n_splits + sp.n_splits_wide + sp.n_splits_general;
+  if (max_partials > kMaxPartials)   // the combine stages their weights in LDS
+    return fail(TQ_ERR_UNSUPPORTED, "%d partials per row exceed %d", max_partials, kMaxPartials);
   const size_t need = decode_workspace_bytes(cache->n_sessions, query->n_q_heads, sp);
   if (workspace_bytes < need)
     return fail(TQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
@@ -835,7 +836,7 @@ int tq_decode_attention(const tq_layer* layer, const tq_cache* cache, const tq_q
   const bool run_wide = (cls & TQ_CACHE_WIDE_PAGES) != 0;
   const bool run_other = (cls & TQ_CACHE_OTHER_PAGES) != 0;
   const int n_common = run_common ? sp.n_splits : 0;
-  const int n_wide = run_wide ? sp.n_splits_general : 0;
+  const int n_wide = run_wide ? sp.n_splits_wide : 0;
   const int n_other = run_other ? sp.n_splits_general : 0;
   a.part_base[0] = 0;
   a.part_base[1] = n_common;
@@ -845,6 +846,8 @@ int tq_decode_attention(const tq_layer* layer, const tq_cache* cache, const tq_q
   a.pages_per_split = sp.pages_per_split;
   a.n_splits_general = sp.n_splits_general;
   a.pages_per_split_general = sp.pages_per_split_general;
+  a.n_splits_wide = sp.n_splits_wide;
+  a.pages_per_split_wide = sp.pages_per_split_wide;
   a.wsq = reinterpret_cast<float*>(workspace);
   a.wsp = a.wsq + (size_t)cache->n_sessions * query->n_q_heads * kQPrepFloats;
   a.out = out;
@@ -854,6 +857,7 @@ int tq_decode_attention(const tq_layer* layer, const tq_cache* cache, const tq_q
   if ((st = launch_status("query prep"))) return st;
   const dim3 grid(sp.n_splits, cache->n_kv_heads, cache->n_sessions);
   const dim3 ggrid(sp.n_splits_general, cache->n_kv_heads, cache->n_sessions);
+  const dim3 wgrid(sp.n_splits_wide, cache->n_kv_heads, cache->n_sessions);
   const dim3 blk(64 * kDecodeWaves);
   if (run_common) {
     switch (G) {
@@ -866,10 +870,10 @@ int tq_decode_attention(const tq_layer* layer, const tq_cache* cache, const tq_q
   }
   if (run_wide) {
     switch (G) {
-      case 1: hipLaunchKernelGGL((split_kernel<1, 1>), ggrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
-      case 2: hipLaunchKernelGGL((split_kernel<2, 1>), ggrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
-      case 4: hipLaunchKernelGGL((split_kernel<4, 1>), ggrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
-      default: hipLaunchKernelGGL((split_kernel<8, 1>), ggrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
+      case 1: hipLaunchKernelGGL((split_kernel<1, 1>), wgrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
+      case 2: hipLaunchKernelGGL((split_kernel<2, 1>), wgrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
+      case 4: hipLaunchKernelGGL((split_kernel<4, 1>), wgrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
+      default: hipLaunchKernelGGL((split_kernel<8, 1>), wgrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
     }
     if ((st = launch_status("split (wide pages)"))) return st;
   }

@@ -325,6 +325,8 @@ SplitPlan split_plan(int n_sessions, int n_kv_heads, int max_pages) {
   sp.n_splits = (int)((max_pages + pps - 1) / pps);
   sp.pages_per_split_general = (sp.pages_per_split + 1) / 2;
   sp.n_splits_general = (max_pages + sp.pages_per_split_general - 1) / sp.pages_per_split_general;
+  sp.pages_per_split_wide = (sp.pages_per_split + 3) / 4;
+  sp.n_splits_wide = (max_pages + sp.pages_per_split_wide - 1) / sp.pages_per_split_wide;
   return sp;
 }
 
@@ -332,7 +334,7 @@ size_t decode_workspace_bytes(int n_sessions, int n_q_heads, const SplitPlan& sp
   const size_t rows = (size_t)n_sessions * n_q_heads;
   // query prep, then the partials of the three page classes
   return sizeof(float) * rows *
-         (kQPrepFloats + (size_t)(sp.n_splits + 2 * sp.n_splits_general) * kPartialFloats);
+         (kQPrepFloats + (size_t)(sp.n_splits + sp.n_splits_wide + sp.n_splits_general) * kPartialFloats);
 }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }

@@ -28,17 +28,20 @@ constexpr int kDecodeWaves = 4;             // waves per split workgroup
 constexpr int kTargetSplitGroups = 1024;    // workgroups the split grid aims for
 constexpr int kQPrepFloats = 3 * 128;       // rotated q, plain q, S q (all pre-scaled)
 constexpr int kPartialFloats = 4 + 128;     // m, l, (pad), acc[128]
-constexpr int kMaxPartials = 5120;          // partials per (session, query head), all classes
+constexpr int kMaxPartials = 7168;          // partials per (session, query head), all classes (1024 + 4096 + 2048)
 
 // Split-K geometry: the common class (1-4 bit codebook pages without QJL)
-// covers the page table in ranges of pages_per_split pages; the wide (5-8 bit)
-// and other (fp16, QJL, mixed) classes, heavier per page and run with fewer
-// waves per SIMD, in ranges half as long.
+// covers the page table in ranges of pages_per_split pages; the other class
+// (fp16, QJL, mixed widths: heavier per page, two waves per SIMD) in ranges
+// half as long, and the wide class (5-8 bits) in ranges a quarter as long (one
+// page per wave: its pages are few, and latency-bound).
 struct SplitPlan {
   int n_splits;
   int pages_per_split;
-  int n_splits_general;
+  int n_splits_general;         // the other class (fp16, QJL, mixed widths)
   int pages_per_split_general;
+  int n_splits_wide;            // the wide class (5-8 bits)
+  int pages_per_split_wide;
 };
 SplitPlan split_plan(int n_sessions, int n_kv_heads, int max_pages);
 size_t decode_workspace_bytes(int n_sessions, int n_q_heads, const SplitPlan& sp);

@@ -110,7 +110,7 @@ def test_cache_bytes_and_workspace(L):
     c = tq.tq_cache(4, 8, 512, 0, None, None, None, 0)
     n = L.tq_decode_workspace_bytes(ctypes.byref(c), 32)
     # 32 units x 512 pages over ~1024 groups: 16 pages per split, 32 splits
-    assert n == 4 * (4 * 32 * 384 + 4 * 32 * (32 + 2 * 64) * 132)
+    assert n == 4 * (4 * 32 * 384 + 4 * 32 * (32 + 128 + 64) * 132)
     c0 = tq.tq_cache(0, 8, 512, 0, None, None, None, 0)
     assert L.tq_decode_workspace_bytes(ctypes.byref(c0), 32) == 0
 
