@@ -84,6 +84,8 @@ template <int G>
 struct SplitLds {
   float2 kpair[340];          // pair tables for bits 1..4 (4 + 16 + 64 + 256 entries)
   float2 vpair[340];
+  float4 kquad[272];          // quad tables for bits 1..2 (16 + 256 entries)
+  float4 vquad[272];
   float kcent[512];           // centroid lists for every bit width (table layout)
   float vcent[512];
   float w[kDecodeWaves][PT * G];           // softmax weights of the current page
@@ -95,6 +97,10 @@ __device__ __forceinline__ int pair_offset(int b) {
   return b == 1 ? 0 : b == 2 ? 4 : b == 3 ? 20 : 84;
 }
 
+// Up to 2 bits, four consecutive codes (4B bits, the first in the low bits)
+// index one table entry holding their four centroids.
+__device__ __forceinline__ int quad_offset(int b) { return b == 1 ? 0 : 16; }
+
 // Key scores of one packed page, lane = token: s[h] = sum_j qr[h][j] c[code_j].
 // Query values are wave-uniform scalar loads; they share the LGKM counter with
 // the LDS codebook lookups and return out of order, so the loop is pipelined by
@@ -102,7 +108,8 @@ __device__ __forceinline__ int pair_offset(int b) {
 // n+1's scalar loads and lookups are issued, then the rest of chunk n runs.
 template <int B, int G>
 __device__ __forceinline__ void key_scores(const char* blk, int lane, const float* __restrict__ qr,
-                                           const float2* pair, const float* cent, float (&s)[G]) {
+                                           const float2* pair, const float4* quad, const float* cent,
+                                           float (&s)[G]) {
   constexpr int CH = 4;                       // coordinates per chunk
   uint32_t sw[4 * B];
   const uint4* src = reinterpret_cast<const uint4*>(blk);
@@ -119,7 +126,13 @@ __device__ __forceinline__ void key_scores(const char* blk, int lane, const floa
     for (int h = 0; h < G; ++h)
 #pragma clang loop unroll(full)
       for (int e = 0; e < CH; ++e) qd[h][e] = qr[(n * G + h) * CH + e];
-    if constexpr (B <= 4) {
+    if constexpr (B <= 2) {
+      const float4 c = quad[quad_offset(B) + bits_at(sw, n * CH * B, 4 * B)];
+      cd[0] = c.x;
+      cd[1] = c.y;
+      cd[2] = c.z;
+      cd[3] = c.w;
+    } else if constexpr (B <= 4) {
       const float2* pt = pair + pair_offset(B);
 #pragma clang loop unroll(full)
       for (int e = 0; e < CH; e += 2) {
@@ -199,7 +212,8 @@ __device__ __forceinline__ void qjl_scores(const char* qb, int lane, const float
 // 8i..8i+7 of tokens 4k+q; acc[h][e] += w[token][h] c[code].
 template <int B, int G>
 __device__ __forceinline__ void value_accum(const char* blk, int lane, const float* wv,
-                                            const float2* pair, const float* cent, float (&acc)[G][8]) {
+                                            const float2* pair, const float4* quad, const float* cent,
+                                            float (&acc)[G][8]) {
   uint32_t sw[4 * B];
   const uint4* src = reinterpret_cast<const uint4*>(blk);
 #pragma clang loop unroll(full)
@@ -213,7 +227,19 @@ __device__ __forceinline__ void value_accum(const char* blk, int lane, const flo
     float wt[G];
 #pragma clang loop unroll(full)
     for (int h = 0; h < G; ++h) wt[h] = wv[(4 * k + q) * G + h];
-    if constexpr (B <= 4) {
+    if constexpr (B <= 2) {
+#pragma clang loop unroll(full)
+      for (int e = 0; e < 8; e += 4) {
+        const float4 c = quad[quad_offset(B) + bits_at(sw, (8 * k + e) * B, 4 * B)];
+#pragma clang loop unroll(full)
+        for (int h = 0; h < G; ++h) {
+          acc[h][e] = fmaf(wt[h], c.x, acc[h][e]);
+          acc[h][e + 1] = fmaf(wt[h], c.y, acc[h][e + 1]);
+          acc[h][e + 2] = fmaf(wt[h], c.z, acc[h][e + 2]);
+          acc[h][e + 3] = fmaf(wt[h], c.w, acc[h][e + 3]);
+        }
+      }
+    } else if constexpr (B <= 4) {
       const float2* pt = pair + pair_offset(B);
 #pragma clang loop unroll(full)
       for (int e = 0; e < 8; e += 2) {
@@ -473,7 +499,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
     }
   }
 
-  // Stage codebooks: pair tables for 1..4 bits and all centroid lists.
+  // Stage codebooks: pair tables for 1..4 bits, quad tables for 1..2 bits and
+  // all centroid lists.
   for (int i = tid; i < 510; i += blockDim.x) {
     sm.kcent[i] = a.k_table[i];
     sm.vcent[i] = a.v_table[i];
@@ -486,7 +513,17 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
     sm.kpair[i] = make_float2(sm.kcent[centroid_offset(bb) + lo], sm.kcent[centroid_offset(bb) + hi]);
     sm.vpair[i] = make_float2(sm.vcent[centroid_offset(bb) + lo], sm.vcent[centroid_offset(bb) + hi]);
   }
+  for (int i = tid; i < 272; i += blockDim.x) {
+    const int bb = i < 16 ? 1 : 2;
+    const int idx = i - quad_offset(bb), msk = (1 << bb) - 1, c0 = centroid_offset(bb);
+    const int q0 = idx & msk, q1 = (idx >> bb) & msk, q2 = (idx >> (2 * bb)) & msk, q3 = idx >> (3 * bb);
+    sm.kquad[i] = make_float4(sm.kcent[c0 + q0], sm.kcent[c0 + q1], sm.kcent[c0 + q2], sm.kcent[c0 + q3]);
+    sm.vquad[i] = make_float4(sm.vcent[c0 + q0], sm.vcent[c0 + q1], sm.vcent[c0 + q2], sm.vcent[c0 + q3]);
+  }
   __syncthreads();
+  // keep the scheduler from moving table work into the page loop (it otherwise
+  // inflates the loop's register use)
+  __builtin_amdgcn_sched_barrier(0);
 
   const float* __restrict__ qrow = wsq + ((size_t)b * a.n_kv_heads + hkv) * kQPrepFloats * G;
 
@@ -520,10 +557,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
     } else {
       if constexpr (CLASS == 0) {
         switch (kb) {
-          case 1: key_scores<1, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
-          case 2: key_scores<2, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
-          case 3: key_scores<3, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
-          default: key_scores<4, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
+          case 1: key_scores<1, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
+          case 2: key_scores<2, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
+          case 3: key_scores<3, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
+          default: key_scores<4, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
         }
       } else if constexpr (CLASS == 1) {
         switch (kb) {
@@ -534,10 +571,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
         }
       } else {
         switch (kb) {
-          case 1: key_scores<1, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
-          case 2: key_scores<2, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
-          case 3: key_scores<3, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
-          case 4: key_scores<4, G>(page, lane, qrow, sm.kpair, sm.kcent, s); break;
+          case 1: key_scores<1, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
+          case 2: key_scores<2, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
+          case 3: key_scores<3, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
+          case 4: key_scores<4, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
           case 5: key_scores_wide<5, G>(page, lane, qrow, sm.kcent, s); break;
           case 6: key_scores_wide<6, G>(page, lane, qrow, sm.kcent, s); break;
           case 7: key_scores_wide<7, G>(page, lane, qrow, sm.kcent, s); break;
@@ -583,10 +620,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
       value_accum_fp16<G>(page, lane, wv, dm, acc);
     } else if constexpr (CLASS == 0) {
       switch (vb) {
-        case 1: value_accum<1, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
-        case 2: value_accum<2, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
-        case 3: value_accum<3, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
-        default: value_accum<4, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
+        case 1: value_accum<1, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
+        case 2: value_accum<2, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
+        case 3: value_accum<3, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
+        default: value_accum<4, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
       }
     } else if constexpr (CLASS == 1) {
       switch (vb) {
@@ -597,10 +634,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
       }
     } else {
       switch (vb) {
-        case 1: value_accum<1, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
-        case 2: value_accum<2, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
-        case 3: value_accum<3, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
-        case 4: value_accum<4, G>(vblk, lane, wv, sm.vpair, sm.vcent, acc); break;
+        case 1: value_accum<1, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
+        case 2: value_accum<2, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
+        case 3: value_accum<3, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
+        case 4: value_accum<4, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
         case 5: value_accum_wide<5, G>(vblk, lane, wv, sm.vcent, acc); break;
         case 6: value_accum_wide<6, G>(vblk, lane, wv, sm.vcent, acc); break;
         case 7: value_accum_wide<7, G>(vblk, lane, wv, sm.vcent, acc); break;
