@@ -123,7 +123,7 @@ def _fake_layer(**kw):
 
 
 def _fake_cache(**kw):
-    base = dict(n_sessions=1, n_kv_heads=8, max_pages=4, reserved=0, n_tokens=0x4000,
+    base = dict(n_sessions=1, n_kv_heads=8, max_pages=4, page_classes=0, n_tokens=0x4000,
                 pages=0x5000, pool=0x100000, pool_bytes=1 << 20)
     base.update(kw)
     return tq.tq_cache(**base)
@@ -182,11 +182,45 @@ def test_decode_validation(L):
         (dict(kw=dict(q=None)), -1),
         (dict(ws=16), -4),
         (dict(layer=_fake_layer(head_dim=256)), -2),
+        (dict(cache=_fake_cache(page_classes=8)), -1),
     ]
     for case, want in cases:
-        st = _decode(L, case.get("layer", _fake_layer()), _fake_cache(), case.get("ws", 1 << 30),
-                     **case.get("kw", {}))
+        st = _decode(L, case.get("layer", _fake_layer()), case.get("cache", _fake_cache()),
+                     case.get("ws", 1 << 30), **case.get("kw", {}))
         assert st == want, (case, st, L.tq_last_error())
+
+
+def _append(L, layer, cache, **kw):
+    base = dict(k=0x10000, v=0x20000, dtype=1, reserved=0, stride_b=8 * 128, stride_h=128, error_flags=None)
+    base.update(kw)
+    inp = tq.tq_token_input(**base)
+    return L.tq_append_kv(ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(inp), None)
+
+
+def test_append_validation(L):
+    cases = [
+        (dict(kw=dict(dtype=3)), -1),
+        (dict(kw=dict(k=None)), -1),
+        (dict(kw=dict(v=0x20008)), -3),
+        (dict(kw=dict(stride_h=100)), -3),
+        (dict(kw=dict(stride_b=-128)), -1),
+        (dict(kw=dict(error_flags=0x70002)), -3),
+        (dict(layer=_fake_layer(head_dim=64)), -2),
+        (dict(cache=_fake_cache(pool=None)), -1),
+    ]
+    for case, want in cases:
+        st = _append(L, case.get("layer", _fake_layer()), case.get("cache", _fake_cache()), **case.get("kw", {}))
+        assert st == want, (case, st, L.tq_last_error())
+    assert L.tq_append_kv(None, None, None, None) == -1
+
+
+def test_pending_pages_in_the_footprint(L):
+    d = [L.tq_page_descriptor(0, 3, 2, 0), L.tq_page_descriptor(256 * 128, 3, 2, 0) | tq.PAGE_PENDING]
+    arr = np.array(d, dtype=np.uint64)
+    assert L.tq_cache_bytes(arr.ctypes.data, 2) == tq.page_bytes((3, 2, False)) + tq.page_bytes((0, 0, False))
+    assert tq.page_bytes((3, 2, False, True)) == tq.page_bytes((0, 0, False))
+    with pytest.raises(tq.TQError):
+        tq.page_bytes((0, 0, False, True))
 
 
 def test_dequantize_validation(L):
