@@ -551,7 +551,14 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
     const int valid = min(PT, ntok - p * PT);
     float s[G], alpha[G];
     const char* vblk = page + 1024 * kb + 256;
-    float nv = 1.f;
+    // the norms (and the QJL scale) are loaded with the codes, not after them
+    float nk = 1.f, nv = 1.f, gq = 0.f;
+    if (kb != 0) {
+      nk = reinterpret_cast<const float*>(page + 1024 * kb)[lane];
+      const char* vb0 = vblk + (qjl ? 1280 : 0);
+      nv = reinterpret_cast<const float*>(vb0 + 1024 * vb)[lane];
+      if (CLASS == 2 && qjl) gq = reinterpret_cast<const float*>(vblk + 1024)[lane];
+    }
     if (CLASS == 2 && kb == 0) {
       key_scores_fp16<G>(page, lane, qrow + D * G, s);
     } else {
@@ -581,18 +588,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
           default: key_scores_wide<8, G>(page, lane, qrow, sm.kcent, s); break;
         }
       }
-      const float nk = reinterpret_cast<const float*>(page + 1024 * kb)[lane];
 #pragma clang loop unroll(full)
       for (int h = 0; h < G; ++h) s[h] *= nk;
       if (CLASS == 2 && qjl) {
         float t[G];
         qjl_scores<G>(vblk, lane, qrow + 2 * D * G, t);
-        const float gamma = reinterpret_cast<const float*>(vblk + 1024)[lane];
 #pragma clang loop unroll(full)
-        for (int h = 0; h < G; ++h) s[h] = fmaf(gamma, t[h], s[h]);
+        for (int h = 0; h < G; ++h) s[h] = fmaf(gq, t[h], s[h]);
         vblk += 1280;
       }
-      nv = reinterpret_cast<const float*>(vblk + 1024 * vb)[lane];
     }
 #pragma clang loop unroll(full)
     for (int h = 0; h < G; ++h)
