@@ -490,6 +490,55 @@ def decode_page(raw: bytes, fmt, signs, S=None, k_kind: int = LLOYD_MAX,
 
 
 # ----------------------------------------------------------------------------
+# Re-tiering a page in place ("TurboMOQ", Progressive temporal tiering and
+# Attention-weighted tier demotion: a page moves to a tier with fewer bits).
+#
+# Reading: a packed page keeps its rotation and its norms; every stored code c
+# of width b becomes the code of its own centroid under the new width b':
+# code' = #{k : t'_k <= c_b[c]} (the same float32 decision as encode).  The
+# original vectors are gone, so this is the only information the page still
+# holds.  An fp16 page is encoded from its rows (as encode would).
+# ----------------------------------------------------------------------------
+def requantize_codes(codes: np.ndarray, bits: int, new_bits: int, kind: int = LLOYD_MAX) -> np.ndarray:
+    """Codes of width `bits` mapped to width `new_bits` through their centroids."""
+    c_old, _ = codebook(bits, kind)
+    _, t_new = codebook(new_bits, kind)
+    return np.searchsorted(t_new, c_old[np.asarray(codes, dtype=np.int64)], side="right").astype(np.int64)
+
+
+def retier_page(raw: bytes, fmt, new_fmt, signs, S=None, k_kind: int = LLOYD_MAX,
+                v_kind: int = LLOYD_MAX) -> bytes:
+    """The bytes of a page re-tiered from `fmt` to the packed `new_fmt`."""
+    nkb, nvb, nqjl = new_fmt
+    assert nkb > 0
+    kb, vb, qjl = fmt
+    if kb == 0:
+        a = np.frombuffer(raw, dtype="<f2").reshape(2, PAGE_TOKENS, HEAD_DIM).astype(np.float64)
+        return encode_page(a[0], a[1], new_fmt, signs, S, k_kind, v_kind)["bytes"]
+    assert not qjl and not nqjl, "a QJL residual cannot be recomputed without the original keys"
+    sec = page_sections(fmt)
+
+    def get(name):
+        o, n = sec[name]
+        return raw[o:o + n]
+    # stream order is kept: only the codes change width
+    ks = requantize_codes(unpack_block(get("k_codes"), kb), kb, nkb, k_kind)
+    vs = requantize_codes(unpack_block(get("v_codes"), vb), vb, nvb, v_kind)
+    out = bytearray(page_bytes(new_fmt))
+    nsec = page_sections(new_fmt)
+
+    def put(name, data):
+        o, n = nsec[name]
+        assert len(data) == n
+        out[o:o + n] = data
+    put("k_codes", pack_block(ks, nkb))
+    put("k_norm", get("k_norm"))
+    put("v_codes", pack_block(vs, nvb))
+    put("v_norm", get("v_norm"))
+    return bytes(out)
+
+
+# ----------------------------------------------------------------------------
 # Attention over the reconstructed cache (reading R6).
 # ----------------------------------------------------------------------------
 def attention(q: np.ndarray, keys: np.ndarray, values: np.ndarray,

@@ -400,3 +400,60 @@ def test_overrides_only_within_the_boundary_allowance():
         O.encode(x, s, 2, overrides=([0], [4], [base[4] - 1]))   # not near a boundary
     with pytest.raises(ValueError):
         O.encode(x, s, 2, overrides=([0], [3], [base[3] - 2]))   # two levels away
+
+
+# ---------------------------------------------------------------- re-tiering
+def test_requantize_codes_pins():
+    # same width: the identity (each centroid lies strictly inside its own cell)
+    for b in range(1, 9):
+        c = np.arange(1 << b)
+        assert np.array_equal(O.requantize_codes(c, b, b), c)
+    # to 1 bit: the sign of the centroid (boundary 0): the lower half of the levels -> 0
+    for b in range(2, 9):
+        c = np.arange(1 << b)
+        assert np.array_equal(O.requantize_codes(c, b, 1), (c >= (1 << (b - 1))).astype(np.int64))
+    # 2 -> 1 by hand with Max (1960): levels -1.5104, -0.4528, 0.4528, 1.5104 -> 0, 0, 1, 1
+    assert O.requantize_codes(np.array([0, 1, 2, 3]), 2, 1).tolist() == [0, 0, 1, 1]
+    # 3 -> 2: the 3-bit levels +-0.2451, +-0.7560, +-1.3439, +-2.1519 against the 2-bit
+    # boundaries 0, +-0.9816 (Max 1960, Table I)
+    assert O.requantize_codes(np.arange(8), 3, 2).tolist() == [0, 0, 1, 1, 2, 2, 3, 3]
+    # monotone and symmetric (code L-1-c maps to L'-1 minus the map of c) for every pair
+    # of widths; a demotion reaches both end levels
+    for b in range(1, 9):
+        for nb in range(1, 9):
+            m = O.requantize_codes(np.arange(1 << b), b, nb)
+            assert np.all(np.diff(m) >= 0)
+            assert np.array_equal(m[::-1], (1 << nb) - 1 - m)
+            if nb <= b:
+                assert m[0] == 0 and m[-1] == (1 << nb) - 1
+
+
+def test_retier_page_keeps_norms_and_reconstructs_nearest_levels():
+    rng = np.random.default_rng(3)
+    K = rng.standard_normal((64, 128))
+    V = rng.standard_normal((64, 128))
+    signs = W.rotation_signs(42, 1)
+    page = O.encode_page(K, V, (4, 4, False), signs)
+    new = O.retier_page(page["bytes"], (4, 4, False), (2, 1, False), signs)
+    assert len(new) == O.page_bytes((2, 1, False))
+    sec_o, sec_n = O.page_sections((4, 4, False)), O.page_sections((2, 1, False))
+    for name in ("k_norm", "v_norm"):
+        (oo, on), (no, nn) = sec_o[name], sec_n[name]
+        assert page["bytes"][oo:oo + on] == new[no:no + nn]
+    # the demoted codes are the encoder's codes of the old reconstruction's rotated
+    # coordinates (u = centroids), which requantize_codes states directly
+    kc = O.unpack_block(new[sec_n["k_codes"][0]:sec_n["k_codes"][0] + sec_n["k_codes"][1]], 2)
+    assert np.array_equal(kc, O.requantize_codes(page["k"]["codes"], 4, 2))
+    Kd, Vd = O.decode_page(new, (2, 1, False), signs)
+    K4, V4 = O.decode_page(page["bytes"], (4, 4, False), signs)
+    # re-encoding the 4-bit reconstruction at 2 bits gives the same codes (u = centroids
+    # up to rounding, never within 1e-6 of a 2-bit boundary here)
+    e2 = O.encode(K4, signs, 2)
+    assert not e2["near"].any() and np.array_equal(e2["codes"], kc)
+    assert np.corrcoef(Kd.ravel(), K.ravel())[0, 1] > 0.9
+    # an fp16 page is encoded from its rows
+    raw16 = O.fp16_page_bytes(K, V)
+    K16 = K.astype(np.float16).astype(np.float64)
+    V16 = V.astype(np.float16).astype(np.float64)
+    assert O.retier_page(raw16, W.FP16, (3, 2, False), signs) == \
+        O.encode_page(K16, V16, (3, 2, False), signs)["bytes"]
