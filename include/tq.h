@@ -275,6 +275,36 @@ int tq_encode_kv(const tq_layer* layer, const tq_cache* cache,
 int tq_append_kv(const tq_layer* layer, const tq_cache* cache, const tq_token_input* in,
                  void* stream);
 
+/* Re-tiers pages in place ("TurboMOQ", Progressive temporal tiering: older
+ * chunks move from fp16 to 4/4, 3/2 and 2/1 bits; Attention-weighted tier
+ * demotion: the tier of a chunk may also follow the attention it receives).
+ * For i in [0, n): the page at flat page-table position page_index[i]
+ * (= (b * n_kv_heads + h) * max_pages + p) takes descriptor new_desc[i], a
+ * present packed format (not pending):
+ *   - from an fp16 page: its 64 fp16 rows are encoded into the new format
+ *     (QJL allowed), exactly as tq_encode_kv would encode them;
+ *   - from a packed page without QJL: to k_bits' <= k_bits and
+ *     v_bits' <= v_bits without QJL, each code c of width b becomes the
+ *     width-b' code of centroid c_b[c] (the count of width-b' boundaries at
+ *     or below it) and the norms are kept: rotation and norm are unchanged,
+ *     so the page is re-coded without being decoded.
+ * The new slot (offset of new_desc[i]) is the old one or a range that does
+ * not overlap it; slots of different listed pages must not overlap, and
+ * no position may be listed twice.  page_index and new_desc are device
+ * arrays (8-byte aligned) of n entries; the call writes the pool and the page
+ * table.  Decode after the call needs tq_cache.page_classes to cover the new
+ * formats.  Errors found on the device are OR-ed into error_flags (device int
+ * or NULL), and the page is left untouched:
+ *   2 = the old or new descriptor is not present,
+ *   4 = invalid format, a slot outside the pool, or overlapping old and new
+ *       slots,
+ *   8 = a QJL target and layer->qjl_s is NULL,
+ *   16 = page_index[i] outside the page table,
+ *   64 = an unsupported change: a pending page, a QJL page as the source or
+ *       (from a packed page) as the target, or a packed width that grows.  */
+int tq_retier_pages(const tq_layer* layer, const tq_cache* cache, const int64_t* page_index,
+                    const uint64_t* new_desc, int n, int32_t* error_flags, void* stream);
+
 /* out[b][h][0..127] (device float32, row stride 128, B x H_q rows) =
  * softmax_t(scale * q_bh . k_t) . v_t over t in [0, n_tokens[b]), where k_t,
  * v_t are the fp16 values of fp16 pages and the dequantised vectors (keys plus

@@ -29,7 +29,7 @@ LIB_PATH = os.path.join(_PKG, "lib", "libtq.so")
 EXPORTS = ("tq_page_bytes", "tq_page_descriptor", "tq_build_codebook", "tq_codebook_table",
            "tq_layer_params", "tq_sign_mask", "tq_decode_workspace_bytes", "tq_cache_bytes",
            "tq_status_string", "tq_last_error", "tq_encode_kv", "tq_decode_attention",
-           "tq_dequantize", "tq_append_kv")
+           "tq_dequantize", "tq_append_kv", "tq_retier_pages")
 
 
 class TQError(RuntimeError):
@@ -104,6 +104,8 @@ def lib() -> ctypes.CDLL:
                                           ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.tq_append_kv.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
                                    ctypes.POINTER(tq_token_input), ctypes.c_void_p]
+        L.tq_retier_pages.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache), ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
         L.tq_dequantize.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache), ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                     ctypes.c_void_p]
@@ -245,10 +247,11 @@ class Cache:
     ``formats[b][h][p]`` is (0, 0, False) for an fp16 page, (k_bits, v_bits,
     qjl, True) for a pending page (see append_kv), or
     (k_bits, v_bits, qjl) for a packed page.  Pages are laid out in the pool
-    in (session, head, page) order.
+    in (session, head, page) order, followed by ``spare_bytes`` (rounded up
+    to 256) of free pool space, e.g. for pages that retier_pages moves.
     """
 
-    def __init__(self, formats, n_tokens: Sequence[int], device):
+    def __init__(self, formats, n_tokens: Sequence[int], device, spare_bytes: int = 0):
         import numpy as np
         import torch
         self.device = torch.device(device)
@@ -272,9 +275,10 @@ class Cache:
                     desc[b, h, p] = d
                     self.offsets[b, h, p] = off
                     off += (n + 255) // 256 * 256
-        self.formats = formats
+        self.formats = [[list(fm) for fm in row] for row in formats]
         self.n_sessions, self.n_kv_heads, self.max_pages = B, H, P
-        self.pool_bytes = max(off, 256)
+        self.spare_offset = off     # free pool space past the pages (spare_bytes of it)
+        self.pool_bytes = max(off + (int(spare_bytes) + 255) // 256 * 256, 256)
         self.pool = torch.zeros(self.pool_bytes, dtype=torch.uint8, device=self.device)
         self.host_pages = desc
         self.pages = torch.from_numpy(desc.view(np.int64)).to(self.device)
@@ -351,6 +355,52 @@ def append_kv(layer: Layer, cache: Cache, k, v, error_flags=None) -> None:
                          error_flags.data_ptr() if error_flags is not None else None)
     check(lib().tq_append_kv(ctypes.byref(layer.struct), ctypes.byref(cache.struct), ctypes.byref(inp),
                              _stream(k.device)), "tq_append_kv")
+
+
+def retier_pages(layer: Layer, cache: Cache, pages, new_formats, new_offsets=None,
+                 error_flags=None) -> None:
+    """tq_retier_pages: page (b, h, p) of ``pages`` takes the packed format
+    (k_bits, v_bits, qjl) of ``new_formats``, in its own slot or at the pool
+    byte offset of ``new_offsets`` (a slot clear of every other page).  Updates
+    the cache's record of formats, offsets and its page-class bits."""
+    import numpy as np
+    import torch
+    pages = [tuple(int(x) for x in p) for p in pages]
+    if len(pages) != len(new_formats):
+        raise TQError("one new format per listed page")
+    if len(set(pages)) != len(pages):
+        raise TQError("a page is listed twice")
+    if new_offsets is None:
+        new_offsets = [int(cache.offsets[p]) for p in pages]
+    if len(new_offsets) != len(pages):
+        raise TQError("one offset per listed page")
+    L = lib()
+    H, P = cache.n_kv_heads, cache.max_pages
+    idx = np.zeros(len(pages), dtype=np.int64)
+    desc = np.zeros(len(pages), dtype=np.uint64)
+    for i, ((b, h, p), fmt, off) in enumerate(zip(pages, new_formats, new_offsets)):
+        if not (0 <= b < cache.n_sessions and 0 <= h < H and 0 <= p < len(cache.formats[b][h])):
+            raise TQError(f"page {(b, h, p)} is not in the cache")
+        kb, vb, q = fmt[:3]
+        d = L.tq_page_descriptor(int(off), int(kb), int(vb), int(bool(q)))
+        if d == 0 or kb == 0 or is_pending(fmt):
+            raise TQError(f"invalid target format {fmt}")
+        idx[i] = (b * H + h) * P + p
+        desc[i] = d
+    if not pages:
+        return
+    idx_t = torch.from_numpy(idx).to(cache.device)
+    desc_t = torch.from_numpy(desc.view(np.int64)).to(cache.device)
+    check(L.tq_retier_pages(ctypes.byref(layer.struct), ctypes.byref(cache.struct), idx_t.data_ptr(),
+                            desc_t.data_ptr(), len(pages),
+                            error_flags.data_ptr() if error_flags is not None else None,
+                            _stream(cache.device)), "tq_retier_pages")
+    for (b, h, p), fmt, d, off in zip(pages, new_formats, desc, new_offsets):
+        cache.formats[b][h][p] = tuple(fmt[:3])
+        cache.host_pages[b, h, p] = d
+        cache.offsets[b, h, p] = int(off)
+    cache.page_classes = page_classes(cache.formats)
+    cache.struct.page_classes = cache.page_classes
 
 
 def dequantize(layer: Layer, cache: Cache, which: int, tok0: int, ntok: int, add_qjl: bool = True,

@@ -796,6 +796,231 @@ __global__ __launch_bounds__(256) void advance_kernel(int32_t* n_tokens, int n) 
   if (i < n) n_tokens[i] += 1;
 }
 
+// ------------------------------------------------------------- re-tiering
+struct RetierArgs {
+  const int64_t* index;
+  const uint64_t* new_desc;
+  int32_t* err;
+  uint64_t* pages;
+  int64_t n_entries;
+  char* pool;
+  uint64_t pool_bytes;
+  const uint32_t* sign_mask;
+  const float* k_table;
+  const float* v_table;
+  const float* qjl_s;
+};
+
+// Stream `lane` of a B-bit code block (word w at (w * 64 + lane) * 16),
+// unpacked and mapped through `map` into this lane's LDS row of 128 bytes.
+template <int B>
+__device__ __forceinline__ void unpack_mapped(const uint4* __restrict__ blk, int lane, const uint8_t* map,
+                                              uint4* row) {
+  uint32_t s[4 * B];
+#pragma clang loop unroll(full)
+  for (int i = 0; i < B; ++i) {
+    const uint4 w = blk[i * 64 + lane];
+    s[4 * i] = w.x;
+    s[4 * i + 1] = w.y;
+    s[4 * i + 2] = w.z;
+    s[4 * i + 3] = w.w;
+  }
+#pragma clang loop unroll(full)
+  for (int i = 0; i < D / 16; ++i) {
+    uint32_t o[4];
+#pragma clang loop unroll(full)
+    for (int k = 0; k < 4; ++k) {
+      uint32_t v = 0;
+#pragma clang loop unroll(full)
+      for (int e = 0; e < 4; ++e) v |= (uint32_t)map[bits_at(s, (16 * i + 4 * k + e) * B, B)] << (8 * e);
+      o[k] = v;
+    }
+    row[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// The inverse: this lane's row of byte codes (each < 2^B) packed into stream
+// `lane` of a B-bit block.
+template <int B>
+__device__ __forceinline__ void pack_row(const uint4* row, int lane, uint4* __restrict__ blk) {
+  uint32_t s[4 * B];
+#pragma clang loop unroll(full)
+  for (int i = 0; i < 4 * B; ++i) s[i] = 0;
+#pragma clang loop unroll(full)
+  for (int i = 0; i < D / 16; ++i) {
+    const uint4 r = row[i];
+    const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
+#pragma clang loop unroll(full)
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t c = (rw[e >> 2] >> (8 * (e & 3))) & 0xffu;
+      const int pos = (16 * i + e) * B, wi = pos >> 5, sh = pos & 31;
+      s[wi] |= c << sh;
+      if (sh + B > 32) s[wi + 1] |= c >> (32 - sh);
+    }
+  }
+#pragma clang loop unroll(full)
+  for (int i = 0; i < B; ++i) blk[i * 64 + lane] = make_uint4(s[4 * i], s[4 * i + 1], s[4 * i + 2], s[4 * i + 3]);
+}
+
+__device__ __forceinline__ void unpack_mapped_any(int b, const uint4* blk, int lane, const uint8_t* map,
+                                                  uint4* row) {
+  switch (b) {
+    case 1: unpack_mapped<1>(blk, lane, map, row); break;
+    case 2: unpack_mapped<2>(blk, lane, map, row); break;
+    case 3: unpack_mapped<3>(blk, lane, map, row); break;
+    case 4: unpack_mapped<4>(blk, lane, map, row); break;
+    case 5: unpack_mapped<5>(blk, lane, map, row); break;
+    case 6: unpack_mapped<6>(blk, lane, map, row); break;
+    case 7: unpack_mapped<7>(blk, lane, map, row); break;
+    default: unpack_mapped<8>(blk, lane, map, row); break;
+  }
+}
+
+__device__ __forceinline__ void pack_row_any(int b, const uint4* row, int lane, uint4* blk) {
+  switch (b) {
+    case 1: pack_row<1>(row, lane, blk); break;
+    case 2: pack_row<2>(row, lane, blk); break;
+    case 3: pack_row<3>(row, lane, blk); break;
+    case 4: pack_row<4>(row, lane, blk); break;
+    case 5: pack_row<5>(row, lane, blk); break;
+    case 6: pack_row<6>(row, lane, blk); break;
+    case 7: pack_row<7>(row, lane, blk); break;
+    default: pack_row<8>(row, lane, blk); break;
+  }
+}
+
+// map[c] = the new-width code of old centroid c: the number of new-width
+// boundaries at or below it (the quantiser's own rule, applied to the value
+// the old code stands for).
+__device__ __forceinline__ void build_code_map(const float* table, int ob, int nb, uint8_t* map, int lane) {
+  const int nt = (1 << nb) - 1;
+  for (int c = lane; c < (1 << ob); c += 64) {
+    const float u = table[centroid_offset(ob) + c];
+    int n = 0;
+    for (int j = 0; j < nt; ++j) n += table[boundary_offset(nb) + j] <= u ? 1 : 0;
+    map[c] = (uint8_t)n;
+  }
+}
+
+// The checks of one listed page: 0 when it can be re-tiered, else the error
+// flag it raises.
+__device__ __forceinline__ int retier_check(const RetierArgs& a, int64_t idx, uint64_t od, uint64_t nd) {
+  if (idx < 0 || idx >= a.n_entries) return 16;
+  if (!(od & TQ_PAGE_PRESENT) || !(nd & TQ_PAGE_PRESENT)) return 2;
+  const int kb = (int)((od >> 48) & 15), vb = (int)((od >> 52) & 15);
+  const int nkb = (int)((nd >> 48) & 15), nvb = (int)((nd >> 52) & 15);
+  const bool oq = (od & TQ_PAGE_QJL) != 0, nq = (nd & TQ_PAGE_QJL) != 0;
+  const uint64_t ooff = od & TQ_PAGE_OFFSET_MASK, noff = nd & TQ_PAGE_OFFSET_MASK;
+  const bool bad_old = kb == 0 ? (vb != 0 || oq) : (kb > 8 || vb < 1 || vb > 8);
+  const bool bad_new = nkb < 1 || nkb > 8 || nvb < 1 || nvb > 8;
+  const size_t osz = page_size_dev(kb, vb, oq), nsz = page_size_dev(nkb, nvb, nq);
+  if (bad_old || bad_new || ooff + osz > a.pool_bytes || noff + nsz > a.pool_bytes ||
+      (noff != ooff && noff < ooff + osz && ooff < noff + nsz))
+    return 4;
+  if (((od | nd) & TQ_PAGE_PENDING) || (kb != 0 && (oq || nq || nkb > kb || nvb > vb))) return 64;
+  if (nq && !a.qjl_s) return 8;
+  return 0;
+}
+
+// One wavefront per listed page; FROM_FP16 selects the pages of one source
+// kind, the other instance handles the rest.  The packed instance runs first
+// and raises the error flags of every listed page (the fp16 instance then
+// finds the same errors on the unchanged descriptors and skips them
+// silently).  A packed page (no QJL) is re-coded stream by stream to narrower
+// widths, keeping its norms; an fp16 page is encoded with the per-token
+// encoder.  Every lane loads the whole of its part of the old page before any
+// lane stores, so the new page may take the old slot.
+template <bool FROM_FP16>
+__global__ __launch_bounds__(64) void retier_kernel(RetierArgs a) {
+  __shared__ float lds_thr[FROM_FP16 ? 256 : 1];
+  __shared__ float lds_cent[FROM_FP16 ? 256 : 1];
+  __shared__ uint32_t lds_rows[(FROM_FP16 ? 1 : 2) * PT * kEncodeRowBytes / 4];
+  __shared__ uint8_t lds_map[2][256];
+  __shared__ float lds_norm[2][FROM_FP16 ? 1 : PT];
+  const int lane = threadIdx.x;
+  const int64_t idx = a.index[blockIdx.x];
+  const bool in_table = idx >= 0 && idx < a.n_entries;
+  uint64_t* dp = a.pages + (in_table ? idx : 0);
+  const uint64_t od = in_table ? *dp : 0, nd = a.new_desc[blockIdx.x];
+  const int e = retier_check(a, idx, od, nd);
+  if (e) {
+    if (!FROM_FP16 && lane == 0) raise_flag(a.err, e);
+    return;
+  }
+  const int kb = (int)((od >> 48) & 15), vb = (int)((od >> 52) & 15);
+  const int nkb = (int)((nd >> 48) & 15), nvb = (int)((nd >> 52) & 15);
+  const bool nq = (nd & TQ_PAGE_QJL) != 0;
+  if ((kb == 0) != FROM_FP16) return;
+  const char* src = a.pool + (od & TQ_PAGE_OFFSET_MASK);
+  char* dst = a.pool + (nd & TQ_PAGE_OFFSET_MASK);
+  if constexpr (FROM_FP16) {
+    uint32_t m[4];
+#pragma clang loop unroll(full)
+    for (int w = 0; w < 4; ++w) m[w] = a.sign_mask[w];
+    for (int part = 0; part < 2; ++part) {
+      const int B = part == 0 ? nkb : nvb;
+      const float* table = part == 0 ? a.k_table : a.v_table;
+      const int L = 1 << B;
+      for (int i = lane; i < L; i += 64) {
+        lds_cent[i] = table[centroid_offset(B) + i];
+        if (i < L - 1) lds_thr[i] = table[boundary_offset(B) + i];
+      }
+      float x[D];
+      load_row(src + part * PT * D * 2, TQ_DTYPE_F16, (size_t)lane * D, x);
+      // the key part ends below the value rows, so in place the values are
+      // still intact when they are loaded here
+      __syncthreads();
+      char* part_base = part == 0 ? dst : dst + 1024 * nkb + 256 + (nq ? 1280 : 0);
+      if (part == 0) {
+        switch (B) {
+          case 1: encode_packed<0, 1>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+          case 2: encode_packed<0, 2>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+          case 3: encode_packed<0, 3>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+          case 4: encode_packed<0, 4>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+          case 5: encode_packed<0, 5>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+          case 6: encode_packed<0, 6>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+          case 7: encode_packed<0, 7>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+          default: encode_packed<0, 8>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+        }
+      } else {
+        switch (B) {
+          case 1: encode_packed<1, 1>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+          case 2: encode_packed<1, 2>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+          case 3: encode_packed<1, 3>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+          case 4: encode_packed<1, 4>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+          case 5: encode_packed<1, 5>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+          case 6: encode_packed<1, 6>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+          case 7: encode_packed<1, 7>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+          default: encode_packed<1, 8>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+        }
+      }
+      __syncthreads();
+    }
+  } else {
+    build_code_map(a.k_table, kb, nkb, lds_map[0], lane);
+    build_code_map(a.v_table, vb, nvb, lds_map[1], lane);
+    __syncthreads();
+    // every load of the old page, then (after the barrier) every store
+    uint4* krow = reinterpret_cast<uint4*>(reinterpret_cast<char*>(lds_rows) + lane * kEncodeRowBytes);
+    uint4* vrow = reinterpret_cast<uint4*>(reinterpret_cast<char*>(lds_rows) + (PT + lane) * kEncodeRowBytes);
+    const char* ov = src + 1024 * kb + 256;
+    unpack_mapped_any(kb, reinterpret_cast<const uint4*>(src), lane, lds_map[0], krow);
+    unpack_mapped_any(vb, reinterpret_cast<const uint4*>(ov), lane, lds_map[1], vrow);
+    // the norms pass through LDS too, so that every load of the old page has
+    // returned before the first store (the barrier of a one-wave block does
+    // not wait for vector memory)
+    lds_norm[0][lane] = reinterpret_cast<const float*>(src + 1024 * kb)[lane];
+    lds_norm[1][lane] = reinterpret_cast<const float*>(ov + 1024 * vb)[lane];
+    __syncthreads();
+    char* nv = dst + 1024 * nkb + 256;
+    pack_row_any(nkb, krow, lane, reinterpret_cast<uint4*>(dst));
+    pack_row_any(nvb, vrow, lane, reinterpret_cast<uint4*>(nv));
+    reinterpret_cast<float*>(dst + 1024 * nkb)[lane] = lds_norm[0][lane];
+    reinterpret_cast<float*>(nv + 1024 * nvb)[lane] = lds_norm[1][lane];
+  }
+  if (lane == 0) *dp = nd;
+}
+
 }  // namespace
 }  // namespace dev
 }  // namespace tq
@@ -900,6 +1125,37 @@ int tq_append_kv(const tq_layer* layer, const tq_cache* cache, const tq_token_in
   hipLaunchKernelGGL(advance_kernel, dim3((cache->n_sessions + 255) / 256), dim3(256), 0, s,
                      const_cast<int32_t*>(cache->n_tokens), cache->n_sessions);
   return launch_status("advance");
+}
+
+int tq_retier_pages(const tq_layer* layer, const tq_cache* cache, const int64_t* page_index,
+                    const uint64_t* new_desc, int n, int32_t* error_flags, void* stream) {
+  int st = check_layer(layer);
+  if (st) return st;
+  if ((st = check_cache(cache))) return st;
+  if (n < 0) return fail(TQ_ERR_INVALID_ARG, "negative page count");
+  if (n == 0) return TQ_OK;
+  if (!page_index || !new_desc) return fail(TQ_ERR_INVALID_ARG, "null page list");
+  if (((uintptr_t)page_index & 7) || ((uintptr_t)new_desc & 7))
+    return fail(TQ_ERR_ALIGNMENT, "page lists must be 8-byte aligned");
+  if (((uintptr_t)error_flags & 3) != 0) return fail(TQ_ERR_ALIGNMENT, "error_flags misaligned");
+  RetierArgs a;
+  a.index = page_index;
+  a.new_desc = new_desc;
+  a.err = error_flags;
+  a.pages = const_cast<uint64_t*>(cache->pages);
+  a.n_entries = (int64_t)cache->n_sessions * cache->n_kv_heads * cache->max_pages;
+  a.pool = reinterpret_cast<char*>(cache->pool);
+  a.pool_bytes = cache->pool_bytes;
+  a.sign_mask = layer->sign_mask;
+  a.k_table = layer->k_table;
+  a.v_table = layer->v_table;
+  a.qjl_s = layer->qjl_s;
+  // packed sources first: that instance raises the error flags, and the pages
+  // it re-tiers no longer look like fp16 pages to the second launch
+  hipLaunchKernelGGL(retier_kernel<false>, dim3(n), dim3(64), 0, (hipStream_t)stream, a);
+  if ((st = launch_status("retier packed pages"))) return st;
+  hipLaunchKernelGGL(retier_kernel<true>, dim3(n), dim3(64), 0, (hipStream_t)stream, a);
+  return launch_status("retier fp16 pages");
 }
 
 }  // extern "C"

@@ -149,12 +149,13 @@ def compare_dequant(got: np.ndarray, ref: np.ndarray, t: Tally):
 
 def compare_unit_full(pool_host: np.ndarray, offsets: np.ndarray, b: int, h: int, K: np.ndarray,
                       V: np.ndarray, formats, signs, S, t: Tally, k_kind=O.LLOYD_MAX,
-                      v_kind=O.LLOYD_MAX):
+                      v_kind=O.LLOYD_MAX, skip=()):
     """Compare every page of unit (b, h) with the oracle, encoding the pages of
     one format together (one oracle pass over the unit), and return the
     oracle's reconstruction (Kh, Vh) under the admissible boundary tie-breaks
     the GPU took: the same composition of oracle steps as
-    ``O.reconstruct_unit`` with overrides, without encoding twice."""
+    ``O.reconstruct_unit`` with overrides, without encoding twice.  Pages in
+    ``skip`` are left to the caller (their rows of Kh, Vh stay zero)."""
     T = K.shape[0]
     Kh = np.zeros((T, O.HEAD_DIM))
     Vh = np.zeros((T, O.HEAD_DIM))
@@ -163,6 +164,8 @@ def compare_unit_full(pool_host: np.ndarray, offsets: np.ndarray, b: int, h: int
         lo, hi = p * 64, min(T, (p + 1) * 64)
         if lo >= T:
             break
+        if p in skip:
+            continue
         off = int(offsets[b, h, p])
         if fmt[0] == 0:
             # the rows the session holds (rows past its tokens are unspecified)

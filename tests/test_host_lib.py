@@ -214,6 +214,25 @@ def test_append_validation(L):
     assert L.tq_append_kv(None, None, None, None) == -1
 
 
+def test_retier_validation(L):
+    """tq_retier_pages: argument errors found on the host (no launch)."""
+    lay, cac = _fake_layer(), _fake_cache()
+    idx, desc = ctypes.c_void_p(0x70000), ctypes.c_void_p(0x71000)
+
+    def call(layer=lay, cache=cac, i=idx, d=desc, n=4, err=None):
+        return L.tq_retier_pages(ctypes.byref(layer) if layer is not None else None,
+                                 ctypes.byref(cache) if cache is not None else None, i, d, n, err, None)
+    assert call(n=-1) == -1
+    assert call(n=0) == 0                      # nothing to do, nothing launched
+    assert call(i=None) == -1 and call(d=None) == -1
+    assert call(i=ctypes.c_void_p(0x70004)) == -3
+    assert call(d=ctypes.c_void_p(0x71004)) == -3
+    assert call(err=ctypes.c_void_p(0x72002)) == -3
+    assert call(layer=_fake_layer(head_dim=64)) == -2
+    assert call(cache=_fake_cache(page_classes=16)) == -1
+    assert call(layer=None) == -1 and call(cache=None) == -1
+
+
 def test_pending_pages_in_the_footprint(L):
     d = [L.tq_page_descriptor(0, 3, 2, 0), L.tq_page_descriptor(256 * 128, 3, 2, 0) | tq.PAGE_PENDING]
     arr = np.array(d, dtype=np.uint64)
