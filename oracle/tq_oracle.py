@@ -610,6 +610,24 @@ def decode_attention_unit(q_heads: np.ndarray, Kh: np.ndarray, Vh: np.ndarray) -
     return np.stack([attention(q, Kh, Vh) for q in np.asarray(q_heads, dtype=np.float64)])
 
 
+def page_attention_mass(q_heads: np.ndarray, Kh: np.ndarray, scale: float | None = None) -> np.ndarray:
+    """[G, n_pages]: for each query head, the softmax weights of the keys Kh
+    ("TurboMOQ", Attention-weighted tier demotion: tiers follow the attention
+    tokens receive) summed over each 64-token page."""
+    Kh = np.asarray(Kh, dtype=np.float64)
+    T = Kh.shape[0]
+    n_pages = (T + PAGE_TOKENS - 1) // PAGE_TOKENS
+    out = np.zeros((len(q_heads), n_pages))
+    for g, q in enumerate(np.asarray(q_heads, dtype=np.float64)):
+        sc = 1.0 / math.sqrt(q.shape[-1]) if scale is None else scale
+        s = Kh @ q * sc
+        w = np.exp(s - np.max(s))
+        w /= w.sum()
+        for p in range(n_pages):
+            out[g, p] = w[p * PAGE_TOKENS:(p + 1) * PAGE_TOKENS].sum()
+    return out
+
+
 # ----------------------------------------------------------------------------
 # Footprint.
 # ----------------------------------------------------------------------------

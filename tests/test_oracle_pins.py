@@ -457,3 +457,33 @@ def test_retier_page_keeps_norms_and_reconstructs_nearest_levels():
     V16 = V.astype(np.float16).astype(np.float64)
     assert O.retier_page(raw16, W.FP16, (3, 2, False), signs) == \
         O.encode_page(K16, V16, (3, 2, False), signs)["bytes"]
+
+
+def test_page_attention_mass_pins():
+    rng = np.random.default_rng(3)
+    T = 150
+    K = rng.standard_normal((T, 128)) * 2
+    qs = rng.standard_normal((3, 128))
+    m = O.page_attention_mass(qs, K)
+    assert m.shape == (3, 3)
+    assert np.allclose(m.sum(axis=1), 1.0, atol=1e-12)
+    # the page masses are attention over values that indicate each token's page
+    ind = np.zeros((T, 3))
+    ind[np.arange(T), np.arange(T) // 64] = 1.0
+    for g in range(3):
+        assert np.allclose(m[g], O.attention(qs[g], K, ind), atol=1e-12)
+    # identical keys: mass in proportion to the tokens a page holds
+    same = np.tile(rng.standard_normal(128), (T, 1))
+    assert np.allclose(O.page_attention_mass(qs[:1], same)[0], [64 / T, 64 / T, 22 / T], atol=1e-12)
+    # closed form: page 0 scores 0, page 1 scores c
+    q = np.zeros(128)
+    q[0] = 1.0
+    K2 = np.zeros((128, 128))
+    K2[64:, 0] = 3.0
+    c = 3.0 / math.sqrt(128)
+    want1 = math.exp(c) / (1 + math.exp(c))
+    assert np.allclose(O.page_attention_mass(q[None], K2)[0], [1 - want1, want1], atol=1e-12)
+    # a key that dominates every other score takes all the mass
+    K3 = rng.standard_normal((T, 128)) * 0.01
+    K3[140] = 1e3 * qs[0] / np.linalg.norm(qs[0])
+    assert O.page_attention_mass(qs[:1], K3)[0, 2] > 1 - 1e-12
