@@ -316,6 +316,20 @@ int tq_decode_attention(const tq_layer* layer, const tq_cache* cache,
                         const tq_query* query, float* out, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* tq_decode_attention, also returning the attention mass of every page
+ * ("TurboMOQ", Attention-weighted tier demotion: a policy reassigns tiers from
+ * the attention weights of each decode step, and pins what stays important).
+ * page_mass[b][hq][p] (device float32, B x H_q x max_pages, contiguous, 4-byte
+ * aligned; every entry is written) = the sum over the tokens t < n_tokens[b]
+ * held by page p of the softmax weight query head hq gives t; 0 for pages
+ * past n_tokens[b] or that decode skips (absent, outside the pool, or of a
+ * class page_classes leaves out).  A row's masses sum to 1 up to rounding.
+ * Same workspace and errors as tq_decode_attention, plus TQ_ERR_INVALID_ARG
+ * for a null page_mass. */
+int tq_decode_attention_mass(const tq_layer* layer, const tq_cache* cache,
+                             const tq_query* query, float* out, float* page_mass,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Dense reconstruction of tokens [tok0, tok0 + ntok) of every (session,
  * KV head): out[b][h][t][0..127] float32 (device, contiguous).  which = 0 keys,
  * 1 values; add_qjl adds the QJL residual on keys of QJL pages.  fp16 pages

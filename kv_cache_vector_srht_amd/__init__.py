@@ -29,7 +29,7 @@ LIB_PATH = os.path.join(_PKG, "lib", "libtq.so")
 EXPORTS = ("tq_page_bytes", "tq_page_descriptor", "tq_build_codebook", "tq_codebook_table",
            "tq_layer_params", "tq_sign_mask", "tq_decode_workspace_bytes", "tq_cache_bytes",
            "tq_status_string", "tq_last_error", "tq_encode_kv", "tq_decode_attention",
-           "tq_dequantize", "tq_append_kv", "tq_retier_pages")
+           "tq_dequantize", "tq_append_kv", "tq_retier_pages", "tq_decode_attention_mass")
 
 
 class TQError(RuntimeError):
@@ -102,6 +102,9 @@ def lib() -> ctypes.CDLL:
         L.tq_decode_attention.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
                                           ctypes.POINTER(tq_query), ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.tq_decode_attention_mass.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
+                                               ctypes.POINTER(tq_query), ctypes.c_void_p, ctypes.c_void_p,
+                                               ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.tq_append_kv.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
                                    ctypes.POINTER(tq_token_input), ctypes.c_void_p]
         L.tq_retier_pages.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache), ctypes.c_void_p,
@@ -323,8 +326,10 @@ def workspace_bytes(cache: Cache, n_q_heads: int) -> int:
 
 
 def decode_attention(layer: Layer, cache: Cache, q, out=None, workspace=None,
-                     softmax_scale: float = 0.0):
-    """tq_decode_attention for q [B, H_q, 128]; returns out [B, H_q, 128] float32."""
+                     softmax_scale: float = 0.0, page_mass=None):
+    """tq_decode_attention for q [B, H_q, 128]; returns out [B, H_q, 128] float32.
+    With ``page_mass`` (float32 [B, H_q, max_pages]), tq_decode_attention_mass
+    also fills it with each page's attention mass."""
     import torch
     if q.dim() != 3 or q.shape[0] != cache.n_sessions or q.shape[-1] != HEAD_DIM or q.stride(-1) != 1:
         raise TQError(f"q must be [B, H_q, 128] with unit innermost stride, got {tuple(q.shape)}")
@@ -335,10 +340,19 @@ def decode_attention(layer: Layer, cache: Cache, q, out=None, workspace=None,
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     qs = tq_query(q.data_ptr(), _dtype_code(q), Hq, q.stride(0), q.stride(1), softmax_scale, 0)
-    check(lib().tq_decode_attention(ctypes.byref(layer.struct), ctypes.byref(cache.struct),
-                                    ctypes.byref(qs), out.data_ptr(), workspace.data_ptr(),
-                                    workspace.numel() * workspace.element_size(),
-                                    _stream(q.device)), "tq_decode_attention")
+    if page_mass is None:
+        check(lib().tq_decode_attention(ctypes.byref(layer.struct), ctypes.byref(cache.struct),
+                                        ctypes.byref(qs), out.data_ptr(), workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream(q.device)), "tq_decode_attention")
+        return out
+    if (page_mass.dtype != torch.float32 or not page_mass.is_contiguous()
+            or tuple(page_mass.shape) != (cache.n_sessions, Hq, cache.max_pages)):
+        raise TQError(f"page_mass must be a contiguous float32 [B, H_q, max_pages] tensor")
+    check(lib().tq_decode_attention_mass(ctypes.byref(layer.struct), ctypes.byref(cache.struct),
+                                         ctypes.byref(qs), out.data_ptr(), page_mass.data_ptr(),
+                                         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                         _stream(q.device)), "tq_decode_attention_mass")
     return out
 
 

@@ -39,6 +39,7 @@ struct DecodeArgs {
   float* wsq;   // [B][H_q][384]: rotated q, plain q, S q (pre-scaled)
   float* wsp;   // [B][H_q][n_splits][kPartialFloats]: m, l, -, -, acc[128]
   float* out;
+  float* mass;  // [B][H_q][max_pages] page attention mass, or null
 };
 
 // (1) query prep: one 128-thread block per (session, query head).
@@ -49,6 +50,11 @@ __global__ __launch_bounds__(128) void qprep_kernel(DecodeArgs a) {
   const int row = blockIdx.x;
   const int b = row / a.n_q_heads, h = row - b * a.n_q_heads;
   const float qj = load_elem(a.q, a.q_dtype, (size_t)b * a.q_sb + (size_t)h * a.q_sh + j);
+  if (a.mass) {
+    // pages no split kernel visits keep -inf (mass 0 after the combine)
+    float* mrow = a.mass + (size_t)row * a.max_pages;
+    for (int p = j; p < a.max_pages; p += 128) mrow[p] = -INFINITY;
+  }
   const uint32_t neg = (a.sign_mask[j >> 5] >> (j & 31)) & 1u;
   qs[j] = qj;
   buf[j] = flip_if(qj, neg);
@@ -462,7 +468,10 @@ __device__ __forceinline__ int page_class(int kb, int vb, bool qjl) {
   return 2;
 }
 
-template <int G, int CLASS>
+// MASS: also write, per page and query head, log2 of the page's share of the
+// softmax numerator (m + log2 of the page's sum of 2^(s - m)); the combine
+// turns it into the page's attention mass.
+template <int G, int CLASS, bool MASS>
 __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
                                                                   const float* __restrict__ wsq,
                                                                   const uint64_t* __restrict__ pages,
@@ -602,6 +611,14 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
     for (int h = 0; h < G; ++h)
       if (lane >= valid) s[h] = -INFINITY;
     softmax_update<G>(s, m, l, alpha);
+    if constexpr (MASS) {
+      float* mrow = a.mass + ((size_t)b * a.n_q_heads + hq0) * a.max_pages + p;
+#pragma clang loop unroll(full)
+      for (int h = 0; h < G; ++h) {
+        const float ps = wave_sum(s[h]);
+        if (lane == 0) mrow[(size_t)h * a.max_pages] = ps > 0.f ? m[h] + log2f(ps) : -INFINITY;
+      }
+    }
     // the running sums need rescaling only when some head's maximum moved
     // (alpha is wave-uniform, so is the branch)
     bool moved = false;
@@ -729,8 +746,11 @@ __global__ __launch_bounds__(128 * kCombineGroups) void combine_kernel(DecodeArg
   float M = red[0];
 #pragma clang loop unroll(full)
   for (int w = 1; w < kCombineWaves; ++w) M = fmaxf(M, red[w]);
+  float* mrow = a.mass ? a.mass + (size_t)row * a.max_pages : nullptr;
   if (M == -INFINITY || a.n_tokens[b] <= 0) {
     if (tid < D) o[tid] = 0.f;
+    if (mrow)
+      for (int p = tid; p < a.max_pages; p += nthr) mrow[p] = 0.f;
     return;
   }
   // weights, the denominator and the list of non-empty partials
@@ -771,6 +791,13 @@ __global__ __launch_bounds__(128 * kCombineGroups) void combine_kernel(DecodeArg
   float L = 0.f;
 #pragma clang loop unroll(full)
   for (int w = 0; w < kCombineWaves; ++w) L += red[w];
+  if (mrow) {
+    const float invL = 1.0f / L;
+    for (int p = tid; p < a.max_pages; p += nthr) {
+      const float v = mrow[p];
+      mrow[p] = v == -INFINITY ? 0.f : exp2f(v - M) * invL;
+    }
+  }
   // value sums: group g takes list entries g, g + 4, ...; four loads in flight
   const int g = tid >> 7, j = tid & (D - 1);
   float acc4[4] = {0.f, 0.f, 0.f, 0.f};
@@ -822,10 +849,29 @@ __global__ __launch_bounds__(128 * kCombineGroups) void combine_kernel(DecodeArg
 using namespace tq;
 using namespace tq::dev;
 
-extern "C" {
+namespace {
 
-int tq_decode_attention(const tq_layer* layer, const tq_cache* cache, const tq_query* query,
-                        float* out, void* workspace, size_t workspace_bytes, void* stream) {
+template <int CLASS, bool MASS>
+void launch_split(int G, dim3 grid, dim3 blk, hipStream_t s, const DecodeArgs& a, const uint64_t* pages) {
+  switch (G) {
+    case 1: hipLaunchKernelGGL((split_kernel<1, CLASS, MASS>), grid, blk, 0, s, a, a.wsq, pages, a.wsp); break;
+    case 2: hipLaunchKernelGGL((split_kernel<2, CLASS, MASS>), grid, blk, 0, s, a, a.wsq, pages, a.wsp); break;
+    case 4: hipLaunchKernelGGL((split_kernel<4, CLASS, MASS>), grid, blk, 0, s, a, a.wsq, pages, a.wsp); break;
+    default: hipLaunchKernelGGL((split_kernel<8, CLASS, MASS>), grid, blk, 0, s, a, a.wsq, pages, a.wsp); break;
+  }
+}
+
+template <int CLASS>
+void launch_split_any(bool mass, int G, dim3 grid, dim3 blk, hipStream_t s, const DecodeArgs& a,
+                      const uint64_t* pages) {
+  if (mass)
+    launch_split<CLASS, true>(G, grid, blk, s, a, pages);
+  else
+    launch_split<CLASS, false>(G, grid, blk, s, a, pages);
+}
+
+int decode_impl(const tq_layer* layer, const tq_cache* cache, const tq_query* query, float* out,
+                float* page_mass, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_layer(layer);
   if (st) return st;
   if ((st = check_cache(cache))) return st;
@@ -841,6 +887,7 @@ int tq_decode_attention(const tq_layer* layer, const tq_cache* cache, const tq_q
   if (query->stride_b < 0 || query->stride_h < 0) return fail(TQ_ERR_INVALID_ARG, "negative stride");
   if (!out || !workspace) return fail(TQ_ERR_INVALID_ARG, "null output or workspace");
   if (!aligned16(out) || !aligned16(workspace)) return fail(TQ_ERR_ALIGNMENT, "out/workspace misaligned");
+  if (((uintptr_t)page_mass & 3) != 0) return fail(TQ_ERR_ALIGNMENT, "page_mass misaligned");
   if (!(query->softmax_scale >= 0.f) || isinf(query->softmax_scale))
     return fail(TQ_ERR_INVALID_ARG, "bad softmax scale");
   SplitPlan sp = split_plan(cache->n_sessions, cache->n_kv_heads, cache->max_pages);
@@ -892,6 +939,8 @@ int tq_decode_attention(const tq_layer* layer, const tq_cache* cache, const tq_q
   a.wsq = reinterpret_cast<float*>(workspace);
   a.wsp = a.wsq + (size_t)cache->n_sessions * query->n_q_heads * kQPrepFloats;
   a.out = out;
+  a.mass = page_mass;
+  const bool mass = page_mass != nullptr;
   hipStream_t s = (hipStream_t)stream;
   const int rows = cache->n_sessions * query->n_q_heads;
   hipLaunchKernelGGL(qprep_kernel, dim3(rows), dim3(128), 0, s, a);
@@ -901,34 +950,35 @@ int tq_decode_attention(const tq_layer* layer, const tq_cache* cache, const tq_q
   const dim3 wgrid(sp.n_splits_wide, cache->n_kv_heads, cache->n_sessions);
   const dim3 blk(64 * kDecodeWaves);
   if (run_common) {
-    switch (G) {
-      case 1: hipLaunchKernelGGL((split_kernel<1, 0>), grid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
-      case 2: hipLaunchKernelGGL((split_kernel<2, 0>), grid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
-      case 4: hipLaunchKernelGGL((split_kernel<4, 0>), grid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
-      default: hipLaunchKernelGGL((split_kernel<8, 0>), grid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
-    }
+    launch_split_any<0>(mass, G, grid, blk, s, a, cache->pages);
     if ((st = launch_status("split (common pages)"))) return st;
   }
   if (run_wide) {
-    switch (G) {
-      case 1: hipLaunchKernelGGL((split_kernel<1, 1>), wgrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
-      case 2: hipLaunchKernelGGL((split_kernel<2, 1>), wgrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
-      case 4: hipLaunchKernelGGL((split_kernel<4, 1>), wgrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
-      default: hipLaunchKernelGGL((split_kernel<8, 1>), wgrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
-    }
+    launch_split_any<1>(mass, G, wgrid, blk, s, a, cache->pages);
     if ((st = launch_status("split (wide pages)"))) return st;
   }
   if (run_other) {
-    switch (G) {
-      case 1: hipLaunchKernelGGL((split_kernel<1, 2>), ggrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
-      case 2: hipLaunchKernelGGL((split_kernel<2, 2>), ggrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
-      case 4: hipLaunchKernelGGL((split_kernel<4, 2>), ggrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
-      default: hipLaunchKernelGGL((split_kernel<8, 2>), ggrid, blk, 0, s, a, a.wsq, cache->pages, a.wsp); break;
-    }
+    launch_split_any<2>(mass, G, ggrid, blk, s, a, cache->pages);
     if ((st = launch_status("split (other pages)"))) return st;
   }
   hipLaunchKernelGGL(combine_kernel, dim3(rows), dim3(128 * kCombineGroups), 0, s, a);
   return launch_status("combine");
+}
+
+}  // namespace
+
+extern "C" {
+
+int tq_decode_attention(const tq_layer* layer, const tq_cache* cache, const tq_query* query,
+                        float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(layer, cache, query, out, nullptr, workspace, workspace_bytes, stream);
+}
+
+int tq_decode_attention_mass(const tq_layer* layer, const tq_cache* cache, const tq_query* query,
+                             float* out, float* page_mass, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (!page_mass) return fail(TQ_ERR_INVALID_ARG, "null page_mass");
+  return decode_impl(layer, cache, query, out, page_mass, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

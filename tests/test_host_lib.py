@@ -190,6 +190,24 @@ def test_decode_validation(L):
         assert st == want, (case, st, L.tq_last_error())
 
 
+def test_decode_mass_validation(L):
+    """tq_decode_attention_mass: its own argument errors, then the decode ones."""
+    lay, cac = _fake_layer(), _fake_cache()
+    qq = tq.tq_query(q=0x30000, dtype=1, n_q_heads=32, stride_b=32 * 128, stride_h=128,
+                     softmax_scale=0.0, reserved=0)
+
+    def call(mass, ws_bytes=1 << 30, query=qq):
+        return L.tq_decode_attention_mass(ctypes.byref(lay), ctypes.byref(cac), ctypes.byref(query),
+                                          ctypes.c_void_p(0x40000), mass, ctypes.c_void_p(0x50000),
+                                          ws_bytes, None)
+    assert call(None) == -1
+    assert call(ctypes.c_void_p(0x60002)) == -3
+    assert call(ctypes.c_void_p(0x60000), ws_bytes=16) == -4
+    bad = tq.tq_query(q=0x30000, dtype=1, n_q_heads=12, stride_b=0, stride_h=128, softmax_scale=0.0,
+                      reserved=0)
+    assert call(ctypes.c_void_p(0x60000), query=bad) == -1
+
+
 def _append(L, layer, cache, **kw):
     base = dict(k=0x10000, v=0x20000, dtype=1, reserved=0, stride_b=8 * 128, stride_h=128, error_flags=None)
     base.update(kw)
