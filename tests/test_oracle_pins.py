@@ -487,3 +487,18 @@ def test_page_attention_mass_pins():
     K3 = rng.standard_normal((T, 128)) * 0.01
     K3[140] = 1e3 * qs[0] / np.linalg.norm(qs[0])
     assert O.page_attention_mass(qs[:1], K3)[0, 2] > 1 - 1e-12
+
+
+def test_requantize_decisions_are_far_from_ties():
+    """Every centroid sits at least 1e-4 from every boundary of a narrower or
+    equal width, so the map is the same whether it is decided in float32 or
+    float64."""
+    for kind in (O.LLOYD_MAX, O.UNIFORM):
+        for b in range(1, 9):
+            c, _ = O.codebook(b, kind)
+            for nb in range(1, b + 1):
+                _, t = O.codebook(nb, kind)
+                gap = np.abs(c[:, None] - t[None, :]).min()
+                assert gap > 1e-4, (kind, b, nb, gap)
+                m32 = np.searchsorted(t.astype(np.float32), c.astype(np.float32), side="right")
+                assert np.array_equal(m32, O.requantize_codes(np.arange(1 << b), b, nb, kind))
