@@ -539,6 +539,52 @@ def retier_page(raw: bytes, fmt, new_fmt, signs, S=None, k_kind: int = LLOYD_MAX
 
 
 # ----------------------------------------------------------------------------
+# Scoring a QJL-sketched key ("TurboQuant-MLX v2.0", RaBitQ vs QJL correction).
+# ----------------------------------------------------------------------------
+QJL_SCORE_UNBIASED = 0
+QJL_SCORE_SIGN = 1
+
+
+def qjl_score_term(q: np.ndarray, z: np.ndarray, gamma32: np.ndarray, S: np.ndarray,
+                   mode: int = QJL_SCORE_UNBIASED) -> np.ndarray:
+    """The sketch's share of q . k for keys with signs z [T, m] (True = +1, as
+    qjl_encode gives them) and scales gamma.
+
+    UNBIASED: the query stays real, sqrt(pi/2)/m gamma z . (S q), which is
+    q . rhat (the QJL estimator of q . r).
+    SIGN: the query is reduced to signs as well and the agreement is scaled by
+    pi/2 (the RaBitQ-style correction): pi/2 / m gamma ||q|| z . sign(S q),
+    sign(0) = +1; its mean over S is ||q|| ||r|| asin(cos(q, r)).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    z = np.where(np.asarray(z, dtype=bool), 1.0, -1.0)
+    g = np.asarray(gamma32, dtype=np.float64)
+    Sq = np.asarray(S, dtype=np.float64) @ q
+    m = Sq.size
+    if mode == QJL_SCORE_UNBIASED:
+        return math.sqrt(math.pi / 2) / m * g * (z @ Sq)
+    if mode == QJL_SCORE_SIGN:
+        sq = np.where(Sq >= 0, 1.0, -1.0)
+        return (math.pi / 2) / m * g * np.linalg.norm(q) * (z @ sq)
+    raise ValueError(mode)
+
+
+def decode_attention_unit_qjl(q_heads: np.ndarray, Kbase: np.ndarray, Vh: np.ndarray,
+                              z: np.ndarray, gamma32: np.ndarray, S: np.ndarray,
+                              mode: int = QJL_SCORE_UNBIASED) -> np.ndarray:
+    """Outputs [G, 128]: scores (q . kbase_t + the sketch term of token t) / sqrt(d),
+    softmax, values.  Tokens without a sketch have gamma = 0."""
+    Kbase = np.asarray(Kbase, dtype=np.float64)
+    Vh = np.asarray(Vh, dtype=np.float64)
+    out = []
+    for q in np.asarray(q_heads, dtype=np.float64):
+        s = (Kbase @ q + qjl_score_term(q, z, gamma32, S, mode)) / math.sqrt(q.size)
+        p = np.exp(s - np.max(s))
+        out.append((p[:, None] * Vh).sum(axis=0) / p.sum())
+    return np.stack(out)
+
+
+# ----------------------------------------------------------------------------
 # Attention over the reconstructed cache (reading R6).
 # ----------------------------------------------------------------------------
 def attention(q: np.ndarray, keys: np.ndarray, values: np.ndarray,

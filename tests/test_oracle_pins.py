@@ -502,3 +502,55 @@ def test_requantize_decisions_are_far_from_ties():
                 assert gap > 1e-4, (kind, b, nb, gap)
                 m32 = np.searchsorted(t.astype(np.float32), c.astype(np.float32), side="right")
                 assert np.array_equal(m32, O.requantize_codes(np.arange(1 << b), b, nb, kind))
+
+
+def test_qjl_sign_scoring_pins():
+    """The sign-agreement score of the sketch: exact at parallel and
+    antiparallel residuals, q . rhat in the unbiased mode, and a mean of
+    ||q|| ||r|| asin(rho) over draws of S (Grothendieck's identity
+    P[sign(g.x) = sign(g.y)] = 1 - angle / pi for Gaussian g)."""
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal(128)
+    S = rng.standard_normal((128, 128))
+    for sgn in (1.0, -1.0):
+        r = sgn * 0.4 * q
+        z = (S @ r >= 0)[None, :]
+        g = np.float32([np.linalg.norm(r)])
+        want = sgn * (math.pi / 2) * np.linalg.norm(q) * float(g[0])
+        assert np.isclose(O.qjl_score_term(q, z, g, S, O.QJL_SCORE_SIGN)[0], want, rtol=1e-12)
+    # unbiased mode is the score against the reconstructed residual
+    r = rng.standard_normal(128) * 0.2
+    z = (S @ r >= 0)[None, :]
+    g = np.float32([np.linalg.norm(r)])
+    assert np.isclose(O.qjl_score_term(q, z, g, S, O.QJL_SCORE_UNBIASED)[0],
+                      q @ O.qjl_reconstruct(z, g, S)[0], rtol=1e-12)
+    # mean over S: ||q|| ||r|| asin(rho), at an oblique and a small correlation
+    u = q / np.linalg.norm(q)
+    w = rng.standard_normal(128)
+    w -= (w @ u) * u
+    w /= np.linalg.norm(w)
+    for rho in (0.6, 0.1):
+        r = 0.3 * (rho * u + math.sqrt(1 - rho * rho) * w)
+        g = np.float32([np.linalg.norm(r)])
+        est = np.empty(2000)
+        for k in range(est.size):
+            Sk = rng.standard_normal((128, 128))
+            est[k] = O.qjl_score_term(q, (Sk @ r >= 0)[None, :], g, Sk, O.QJL_SCORE_SIGN)[0]
+        want = np.linalg.norm(q) * float(g[0]) * math.asin(rho)
+        assert abs(est.mean() - want) < 4 * est.std() / math.sqrt(est.size)
+
+
+def test_decode_attention_unit_qjl_matches_reconstruction_in_unbiased_mode():
+    rng = np.random.default_rng(22)
+    T = 70
+    Kb = rng.standard_normal((T, 128))
+    V = rng.standard_normal((T, 128))
+    S = rng.standard_normal((128, 128))
+    r = rng.standard_normal((T, 128)) * 0.3
+    qj = O.qjl_encode(Kb + r, Kb, S)
+    g = qj["gamma"].copy()
+    g[:10] = 0          # tokens without a sketch
+    qs = rng.standard_normal((4, 128))
+    got = O.decode_attention_unit_qjl(qs, Kb, V, qj["z"], g, S, O.QJL_SCORE_UNBIASED)
+    Kh = Kb + O.qjl_reconstruct(qj["z"], g, S)
+    assert np.allclose(got, O.decode_attention_unit(qs, Kh, V), rtol=1e-10, atol=1e-12)
