@@ -67,6 +67,7 @@ enum {
 
 enum { TQ_CODEBOOK_LLOYD_MAX = 0, TQ_CODEBOOK_UNIFORM = 1 };
 enum { TQ_DTYPE_F32 = 0, TQ_DTYPE_F16 = 1 };
+enum { TQ_QJL_SCORE_UNBIASED = 0, TQ_QJL_SCORE_SIGN = 1 };
 
 #define TQ_HEAD_DIM 128
 #define TQ_PAGE_TOKENS 64
@@ -195,7 +196,15 @@ typedef struct tq_query {
                                 reads KV head h / G                              */
   int64_t stride_b, stride_h;
   float softmax_scale;       /* 0 selects 1/sqrt(128)                            */
-  int32_t reserved;          /* 0                                                */
+  int32_t qjl_scoring;       /* how pages with a QJL sketch score it:
+                                TQ_QJL_SCORE_UNBIASED (0): gamma sqrt(pi/2)/m
+                                  z . (S q), the estimator of q . r;
+                                TQ_QJL_SCORE_SIGN (1): gamma (pi/2)/m ||q||
+                                  z . sign(S q), the sign-agreement form
+                                ("TurboQuant-MLX v2.0", RaBitQ vs QJL
+                                correction and Implementation Status: both
+                                sides as signs, scaled by pi/2), which
+                                estimates ||q|| ||r|| asin(cos(q, r))        */
 } tq_query;
 
 /* --------------------------------------------------------- host-only calls */

@@ -23,6 +23,8 @@ LLOYD_MAX = 0
 UNIFORM = 1
 DTYPE_F32 = 0
 DTYPE_F16 = 1
+QJL_SCORE_UNBIASED = 0
+QJL_SCORE_SIGN = 1
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "lib", "libtq.so")
@@ -67,7 +69,7 @@ class tq_token_input(ctypes.Structure):
 class tq_query(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
                 ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64),
-                ("softmax_scale", ctypes.c_float), ("reserved", ctypes.c_int32)]
+                ("softmax_scale", ctypes.c_float), ("qjl_scoring", ctypes.c_int32)]
 
 
 _lib = None
@@ -326,7 +328,7 @@ def workspace_bytes(cache: Cache, n_q_heads: int) -> int:
 
 
 def decode_attention(layer: Layer, cache: Cache, q, out=None, workspace=None,
-                     softmax_scale: float = 0.0, page_mass=None):
+                     softmax_scale: float = 0.0, page_mass=None, qjl_scoring: int = 0):
     """tq_decode_attention for q [B, H_q, 128]; returns out [B, H_q, 128] float32.
     With ``page_mass`` (float32 [B, H_q, max_pages]), tq_decode_attention_mass
     also fills it with each page's attention mass."""
@@ -339,7 +341,7 @@ def decode_attention(layer: Layer, cache: Cache, q, out=None, workspace=None,
     need = workspace_bytes(cache, Hq)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    qs = tq_query(q.data_ptr(), _dtype_code(q), Hq, q.stride(0), q.stride(1), softmax_scale, 0)
+    qs = tq_query(q.data_ptr(), _dtype_code(q), Hq, q.stride(0), q.stride(1), softmax_scale, qjl_scoring)
     if page_mass is None:
         check(lib().tq_decode_attention(ctypes.byref(layer.struct), ctypes.byref(cache.struct),
                                         ctypes.byref(qs), out.data_ptr(), workspace.data_ptr(),

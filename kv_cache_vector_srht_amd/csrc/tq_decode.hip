@@ -24,6 +24,7 @@ struct DecodeArgs {
   int64_t q_sb, q_sh;
   int n_q_heads, group;
   float scale2;  // softmax scale * log2(e)
+  int qjl_sign;  // TQ_QJL_SCORE_SIGN: the query side of the QJL term is sign(S q)
   const int32_t* n_tokens;
   int n_sessions, n_kv_heads, max_pages;
   const char* pool;
@@ -79,7 +80,15 @@ __global__ __launch_bounds__(128) void qprep_kernel(DecodeArgs a) {
     const float* srow = a.qjl_s + (size_t)j * D;
     float p = 0.f;
     for (int i = 0; i < D; ++i) p = fmaf(srow[i], qs[i], p);
-    w[2 * D * G + slot] = p * (a.scale2 * kSqrtHalfPi / TQ_JL_DIM);
+    if (a.qjl_sign) {
+      // sign agreement scaled by pi/2 ||q|| / m (every thread sums the same
+      // squares in the same order)
+      float qq = 0.f;
+      for (int i = 0; i < D; ++i) qq = fmaf(qs[i], qs[i], qq);
+      w[2 * D * G + slot] = (p >= 0.f ? 1.f : -1.f) * sqrtf(qq) * (a.scale2 * kHalfPi / TQ_JL_DIM);
+    } else {
+      w[2 * D * G + slot] = p * (a.scale2 * kSqrtHalfPi / TQ_JL_DIM);
+    }
   } else {
     w[2 * D * G + slot] = 0.f;
   }
@@ -890,6 +899,8 @@ int decode_impl(const tq_layer* layer, const tq_cache* cache, const tq_query* qu
   if (((uintptr_t)page_mass & 3) != 0) return fail(TQ_ERR_ALIGNMENT, "page_mass misaligned");
   if (!(query->softmax_scale >= 0.f) || isinf(query->softmax_scale))
     return fail(TQ_ERR_INVALID_ARG, "bad softmax scale");
+  if (query->qjl_scoring != TQ_QJL_SCORE_UNBIASED && query->qjl_scoring != TQ_QJL_SCORE_SIGN)
+    return fail(TQ_ERR_INVALID_ARG, "unknown qjl_scoring %d", query->qjl_scoring);
   SplitPlan sp = split_plan(cache->n_sessions, cache->n_kv_heads, cache->max_pages);
   const int max_partials = sp.n_splits + sp.n_splits_wide + sp.n_splits_general;
   if (max_partials > kMaxPartials)   // the combine stages their weights in LDS
@@ -906,6 +917,7 @@ int decode_impl(const tq_layer* layer, const tq_cache* cache, const tq_query* qu
   a.group = G;
   const float scale = query->softmax_scale > 0.f ? query->softmax_scale : 0.08838834764831845f;
   a.scale2 = scale * kLog2e;
+  a.qjl_sign = query->qjl_scoring == TQ_QJL_SCORE_SIGN;
   a.n_tokens = cache->n_tokens;
   a.n_sessions = cache->n_sessions;
   a.n_kv_heads = cache->n_kv_heads;

@@ -15,6 +15,7 @@ constexpr int D = TQ_HEAD_DIM;
 constexpr int PT = TQ_PAGE_TOKENS;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSqrtHalfPi = 1.2533141373155003f;  // sqrt(pi / 2)
+constexpr float kHalfPi = 1.5707963267948966f;       // pi / 2
 constexpr int kEncodeRowBytes = 144;                 // LDS row of 128 code bytes + pad
 
 // ----------------------------------------------------------------- helpers

@@ -149,16 +149,23 @@ def compare_dequant(got: np.ndarray, ref: np.ndarray, t: Tally):
 
 def compare_unit_full(pool_host: np.ndarray, offsets: np.ndarray, b: int, h: int, K: np.ndarray,
                       V: np.ndarray, formats, signs, S, t: Tally, k_kind=O.LLOYD_MAX,
-                      v_kind=O.LLOYD_MAX, skip=()):
+                      v_kind=O.LLOYD_MAX, skip=(), parts=None):
     """Compare every page of unit (b, h) with the oracle, encoding the pages of
     one format together (one oracle pass over the unit), and return the
     oracle's reconstruction (Kh, Vh) under the admissible boundary tie-breaks
     the GPU took: the same composition of oracle steps as
     ``O.reconstruct_unit`` with overrides, without encoding twice.  Pages in
-    ``skip`` are left to the caller (their rows of Kh, Vh stay zero)."""
+    ``skip`` are left to the caller (their rows of Kh, Vh stay zero).  With a
+    ``parts`` dict, also returns there the keys without their QJL term
+    ("kbase") and the oracle's sketch ("z" [T, 128] bool, "gamma" [T], zero
+    on rows without one)."""
     T = K.shape[0]
     Kh = np.zeros((T, O.HEAD_DIM))
     Vh = np.zeros((T, O.HEAD_DIM))
+    if parts is not None:
+        parts["kbase"] = np.zeros((T, O.HEAD_DIM))
+        parts["z"] = np.zeros((T, O.HEAD_DIM), dtype=bool)
+        parts["gamma"] = np.zeros(T, dtype=np.float32)
     groups = {}
     for p, fmt in enumerate(formats):
         lo, hi = p * 64, min(T, (p + 1) * 64)
@@ -177,6 +184,8 @@ def compare_unit_full(pool_host: np.ndarray, offsets: np.ndarray, b: int, h: int
                 np.array_equal(raw[half:half + n * 256], exp[half:half + n * 256]), f"fp16 page ({b},{h},{p}) differs"
             Kh[lo:hi] = K[lo:hi].astype(np.float16)
             Vh[lo:hi] = V[lo:hi].astype(np.float16)
+            if parts is not None:
+                parts["kbase"][lo:hi] = Kh[lo:hi]
         else:
             assert hi - lo == 64, "a packed page must be full"
             groups.setdefault(tuple(fmt), []).append(p)
@@ -205,6 +214,8 @@ def compare_unit_full(pool_host: np.ndarray, offsets: np.ndarray, b: int, h: int
             for r, c, code in alt:
                 codes[r, c] = code
         kh = O.dequantize(ek["norm"], kc, signs, kb, k_kind)
+        if parts is not None:
+            parts["kbase"][rows] = kh
         if qjl:
             qj = O.qjl_encode(K[rows], kh, S)
             z = np.concatenate([O.unpack_signs(x) for x in part("qjl_signs")])
@@ -215,6 +226,9 @@ def compare_unit_full(pool_host: np.ndarray, offsets: np.ndarray, b: int, h: int
             t.sign_mismatches += int(dz.sum())
             assert np.allclose(g, qj["gamma"], rtol=NORM_RTOL, atol=1e-30), f"QJL gamma {what}"
             kh = kh + O.qjl_reconstruct(qj["z"], qj["gamma"], S)
+            if parts is not None:
+                parts["z"][rows] = qj["z"]
+                parts["gamma"][rows] = qj["gamma"]
         Kh[rows] = kh
         Vh[rows] = O.dequantize(ev["norm"], vc, signs, vb, v_kind)
     return Kh, Vh

@@ -7,7 +7,7 @@ import pytest
 
 import workloads as W
 from oracle import tq_oracle as O
-from tests.gpu_parity import Tally, compare_attention, compare_dequant, compare_unit_pages
+from tests.gpu_parity import Tally, compare_attention, compare_dequant, compare_unit_full, compare_unit_pages
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -194,3 +194,46 @@ def test_page_class_hint(dev):
         unknown = _np(tq.decode_attention(layer, cache, q))
         assert np.array_equal(hinted, unknown)
     assert seen == {1, 2, 5}
+
+
+@pytest.mark.parametrize("mode", [O.QJL_SCORE_SIGN, O.QJL_SCORE_UNBIASED])
+def test_qjl_scoring_modes(dev, mode):
+    """Decode with either QJL score form against the oracle's scores: the keys
+    without their sketch plus ``O.qjl_score_term``.  Every width with QJL keys,
+    an fp16 first page, GQA 4, a full and a ragged session."""
+    import kv_cache_vector_srht_amd as tq
+    w = _all_bits_workload(pages=20, qjl=True)
+    n_tok = [w.n_tokens, 64 * 17 + 9]
+    w.batch = 2
+    fm = [w.formats[0][0], [[W.FP16 if p == 17 else f for p, f in enumerate(row)] for row in w.formats[0][0]]]
+    signs, S = W.rotation_signs(42, 0), W.qjl_matrix(42, 0)
+    layer = tq.Layer(signs, dev, S)
+    cache = tq.Cache(fm, n_tok, dev)
+    k, v = W.make_kv(w, 0, device=dev)
+    q = W.make_query(w, 0, device=dev)
+    qh = _np(q).astype(np.float64)
+    # the sign of S q is decided in float32 on the device: the seeded queries
+    # keep every projection clear of zero by far more than its rounding
+    qf = qh.reshape(-1, 128)
+    ratio = np.abs(qf @ S.astype(np.float64).T) / (np.linalg.norm(S, axis=1)[None, :] *
+                                                   np.linalg.norm(qf, axis=1)[:, None])
+    assert ratio.min() > 1e-5
+    tq.encode_kv(layer, cache, k, v)
+    print(f"decode, qjl_scoring {mode}", flush=True)
+    out = _np(tq.decode_attention(layer, cache, q, qjl_scoring=mode))
+    pool = _np(cache.pool)
+    kh, vh = _np(k).astype(np.float64), _np(v).astype(np.float64)
+    t = Tally()
+    G = w.n_q_heads // w.n_kv_heads
+    for b in range(2):
+        n = n_tok[b]
+        for h in range(w.n_kv_heads):
+            parts = {}
+            _, Vh = compare_unit_full(pool, cache.offsets, b, h, kh[b, h, :n], vh[b, h, :n], fm[b][h],
+                                      signs, S, t, parts=parts)
+            rows = slice(h * G, (h + 1) * G)
+            ref = O.decode_attention_unit_qjl(qh[b, rows], parts["kbase"], Vh, parts["z"], parts["gamma"],
+                                              S, mode)
+            err = np.abs(out[b, rows] - ref).max(axis=1) / np.abs(ref).max(axis=1)
+            t.worst_attn = max(t.worst_attn, float(err.max()))
+    t.check()

@@ -166,7 +166,7 @@ def test_encode_validation(L):
 
 def _decode(L, layer, cache, ws_bytes=1 << 30, **kw):
     base = dict(q=0x30000, dtype=1, n_q_heads=32, stride_b=32 * 128, stride_h=128, softmax_scale=0.0,
-                reserved=0)
+                qjl_scoring=0)
     base.update(kw)
     qq = tq.tq_query(**base)
     return L.tq_decode_attention(ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(qq),
@@ -179,6 +179,7 @@ def test_decode_validation(L):
         (dict(kw=dict(n_q_heads=8 * 16)), -2),  # group 16
         (dict(kw=dict(dtype=5)), -1),
         (dict(kw=dict(softmax_scale=float("nan"))), -1),
+        (dict(kw=dict(qjl_scoring=2)), -1),
         (dict(kw=dict(q=None)), -1),
         (dict(ws=16), -4),
         (dict(layer=_fake_layer(head_dim=256)), -2),
@@ -194,7 +195,7 @@ def test_decode_mass_validation(L):
     """tq_decode_attention_mass: its own argument errors, then the decode ones."""
     lay, cac = _fake_layer(), _fake_cache()
     qq = tq.tq_query(q=0x30000, dtype=1, n_q_heads=32, stride_b=32 * 128, stride_h=128,
-                     softmax_scale=0.0, reserved=0)
+                     softmax_scale=0.0, qjl_scoring=0)
 
     def call(mass, ws_bytes=1 << 30, query=qq):
         return L.tq_decode_attention_mass(ctypes.byref(lay), ctypes.byref(cac), ctypes.byref(query),
@@ -204,7 +205,7 @@ def test_decode_mass_validation(L):
     assert call(ctypes.c_void_p(0x60002)) == -3
     assert call(ctypes.c_void_p(0x60000), ws_bytes=16) == -4
     bad = tq.tq_query(q=0x30000, dtype=1, n_q_heads=12, stride_b=0, stride_h=128, softmax_scale=0.0,
-                      reserved=0)
+                      qjl_scoring=0)
     assert call(ctypes.c_void_p(0x60000), query=bad) == -1
 
 
