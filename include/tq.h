@@ -65,7 +65,7 @@ enum {
   TQ_ERR_DEVICE = -5       /* HIP reported an error when launching           */
 };
 
-enum { TQ_CODEBOOK_LLOYD_MAX = 0, TQ_CODEBOOK_UNIFORM = 1 };
+enum { TQ_CODEBOOK_LLOYD_MAX = 0, TQ_CODEBOOK_UNIFORM = 1, TQ_CODEBOOK_BETA = 2 };
 enum { TQ_DTYPE_F32 = 0, TQ_DTYPE_F16 = 1 };
 enum { TQ_QJL_SCORE_UNBIASED = 0, TQ_QJL_SCORE_SIGN = 1 };
 
@@ -214,7 +214,13 @@ typedef struct tq_query {
  * kind = TQ_CODEBOOK_LLOYD_MAX: the MSE-optimal 2^bits-level quantiser of
  *   N(0,1) (the unique fixed point of the centroid and midpoint conditions);
  * kind = TQ_CODEBOOK_UNIFORM: levels (k - (L-1)/2) * delta with the
- *   MSE-optimal delta for N(0,1), boundaries at midpoints.
+ *   MSE-optimal delta for N(0,1), boundaries at midpoints;
+ * kind = TQ_CODEBOOK_BETA: the MSE-optimal quantiser of one coordinate of
+ *   sqrt(128) times a uniformly random unit vector of R^128 (density
+ *   proportional to (1 - u^2/128)^(125/2); u^2/128 ~ Beta(1/2, 127/2)), the
+ *   exact law of a rotated, normalised coordinate when the direction is random
+ *   ("TurboMOQ", Head-to-Head Comparison and Project Structure: Beta-CDF,
+ *   Beta-distribution codebooks).
  * Writes 2^bits ascending centroids and 2^bits - 1 boundaries (caller-owned
  * host arrays), each the float32 nearest the exact value.  Pure, deterministic
  * and thread-safe; bits in 1..8. */

@@ -21,6 +21,7 @@ JL_DIM = 128
 CODEBOOK_TABLE_FLOATS = 8192
 LLOYD_MAX = 0
 UNIFORM = 1
+BETA = 2
 DTYPE_F32 = 0
 DTYPE_F16 = 1
 QJL_SCORE_UNBIASED = 0

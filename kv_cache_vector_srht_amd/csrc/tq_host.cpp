@@ -38,13 +38,83 @@ static ld pdf(ld x) { return isinf(x) ? 0.0L : kInvSqrt2Pi * expl(-0.5L * x * x)
 // Upper tail P(Z >= x), accurate for large positive x.
 static ld upper(ld x) { return isinf(x) ? (x > 0 ? 0.0L : 1.0L) : 0.5L * erfcl(x * kInvSqrt2); }
 
-// Lloyd-Max quantiser of N(0,1) with L = 2^bits levels.  By symmetry only the
-// positive centroids c[0..h-1] (h = L/2) are unknowns; cell i of the positive
-// half is [a_i, b_i) with a_0 = 0, a_i = (c[i-1] + c[i]) / 2, b_i = a_{i+1},
-// b_{h-1} = +inf, and the conditions are c[i] = E[Z | a_i <= Z < b_i].
-// Solved by a few Lloyd sweeps followed by Newton's method with the exact
-// tridiagonal Jacobian (Thomas algorithm), all in long double.
-static void lloyd_max(int bits, std::vector<ld>& cpos) {
+// Densities the Lloyd-Max quantiser is solved for.  Each gives, for x >= 0,
+// the density f(x), the upper tail P(X >= x), and the partial first moment
+// E[X; X >= x] (for N(0,1) this is f(x) itself); `end` is the top of the
+// support.
+struct GaussianModel {
+  ld end() const { return INFINITY; }
+  ld density(ld x) const { return pdf(x); }
+  ld tail(ld x) const { return upper(x); }
+  ld moment(ld x) const { return pdf(x); }
+};
+
+// Regularised incomplete beta I_x(a, b) from the continued fraction of
+// Abramowitz & Stegun 26.5.8,
+//   I_x(a, b) = x^a (1-x)^b / (a B(a, b)) * 1 / (1 + d1 / (1 + d2 / (1 + ...))),
+//   d(2m+1) = -(a+m)(a+b+m) x / ((a+2m)(a+2m+1)),  d(2m) = m(b-m) x / ((a+2m-1)(a+2m)),
+// evaluated front to back with the modified Lentz method, on the side of the
+// symmetry I_x(a, b) = 1 - I_{1-x}(b, a) where the fraction converges fast.
+static ld incomplete_beta(ld a, ld b, ld x) {
+  if (x <= 0.0L) return 0.0L;
+  if (x >= 1.0L) return 1.0L;
+  if (x > (a + 1.0L) / (a + b + 2.0L)) return 1.0L - incomplete_beta(b, a, 1.0L - x);
+  const ld tiny = 1e-4000L;
+  auto guard = [&](ld v) { return fabsl(v) < tiny ? tiny : v; };
+  // value = 1 / (1 + d1 / (1 + d2 / ...)): C_k, D_k of the Lentz recurrences
+  ld C = 1.0L;
+  ld Dk = 1.0L / guard(1.0L - (a + b) * x / (a + 1.0L));   // 1 + d1
+  ld value = Dk;
+  for (int m = 1; m < 5000; ++m) {
+    const ld even = (ld)m * (b - (ld)m) * x / ((a + 2 * m - 1) * (a + 2 * m));
+    Dk = 1.0L / guard(1.0L + even * Dk);
+    C = guard(1.0L + even / C);
+    value *= Dk * C;
+    const ld odd = -(a + m) * (a + b + m) * x / ((a + 2 * m) * (a + 2 * m + 1));
+    Dk = 1.0L / guard(1.0L + odd * Dk);
+    C = guard(1.0L + odd / C);
+    const ld step = Dk * C;
+    value *= step;
+    if (fabsl(step - 1.0L) < 1e-21L) break;
+  }
+  const ld lfront = a * logl(x) + b * log1pl(-x) - (lgammal(a) + lgammal(b) - lgammal(a + b)) - logl(a);
+  return expl(lfront) * value;
+}
+
+// One coordinate of sqrt(d) times a uniformly random unit vector of R^d (the
+// distribution a rotated, normalised head vector's coordinate has when its
+// direction is random): f(u) = c (1 - u^2/d)^((d-3)/2) on |u| < sqrt(d), with
+// c = Gamma(d/2) / (sqrt(pi d) Gamma((d-1)/2)); u^2/d ~ Beta(1/2, (d-1)/2).
+struct SphereModel {
+  ld d, c;
+  explicit SphereModel(int dim) : d((ld)dim) {
+    c = expl(lgammal(0.5L * d) - lgammal(0.5L * (d - 1.0L))) / sqrtl(3.14159265358979323846264338327950288L * d);
+  }
+  ld end() const { return sqrtl(d); }
+  ld density(ld x) const {
+    const ld y = 1.0L - x * x / d;
+    return y <= 0.0L ? 0.0L : c * powl(y, 0.5L * (d - 3.0L));
+  }
+  ld tail(ld x) const {
+    const ld y = 1.0L - x * x / d;
+    return y <= 0.0L ? 0.0L : 0.5L * incomplete_beta(0.5L * (d - 1.0L), 0.5L, y);
+  }
+  ld moment(ld x) const {
+    // integral of u f(u) from x to sqrt(d)
+    const ld y = 1.0L - x * x / d;
+    return y <= 0.0L ? 0.0L : c * d / (d - 1.0L) * powl(y, 0.5L * (d - 1.0L));
+  }
+};
+
+// Lloyd-Max quantiser of a symmetric density with L = 2^bits levels.  By
+// symmetry only the positive centroids c[0..h-1] (h = L/2) are unknowns; cell i
+// of the positive half is [a_i, b_i) with a_0 = 0, a_i = (c[i-1] + c[i]) / 2,
+// b_i = a_{i+1}, b_{h-1} = the end of the support, and the conditions are
+// c[i] = E[X | a_i <= X < b_i].  Solved by a few Lloyd sweeps followed by
+// Newton's method with the exact tridiagonal Jacobian (Thomas algorithm), all
+// in long double.
+template <class Model>
+static void lloyd_max(int bits, const Model& M, std::vector<ld>& cpos) {
   const int h = 1 << (bits - 1);
   cpos.assign(h, 0.0L);
   // Start: centroids of equal-probability cells of N(0, 3) (companding shape).
@@ -57,18 +127,18 @@ static void lloyd_max(int bits, std::vector<ld>& cpos) {
       ld mid = 0.5L * (lo + hi);
       if (1.0L - upper(mid / sqrtl(3.0L)) < p) lo = mid; else hi = mid;
     }
-    cpos[i] = 0.5L * (lo + hi);
+    cpos[i] = std::min(0.5L * (lo + hi), M.end() * (ld)(i + 1) / (ld)(h + 1));
   }
   auto cond_means = [&](const std::vector<ld>& c, std::vector<ld>& m,
                         std::vector<ld>* dm_da, std::vector<ld>* dm_db) {
     for (int i = 0; i < h; ++i) {
       ld a = i == 0 ? 0.0L : 0.5L * (c[i - 1] + c[i]);
-      ld b = i == h - 1 ? INFINITY : 0.5L * (c[i] + c[i + 1]);
-      ld P = upper(a) - upper(b);
-      ld mean = (pdf(a) - pdf(b)) / P;
+      ld b = i == h - 1 ? M.end() : 0.5L * (c[i] + c[i + 1]);
+      ld P = M.tail(a) - M.tail(b);
+      ld mean = (M.moment(a) - M.moment(b)) / P;
       m[i] = mean;
-      if (dm_da) (*dm_da)[i] = pdf(a) * (mean - a) / P;
-      if (dm_db) (*dm_db)[i] = isinf(b) ? 0.0L : pdf(b) * (b - mean) / P;
+      if (dm_da) (*dm_da)[i] = M.density(a) * (mean - a) / P;
+      if (dm_db) (*dm_db)[i] = i == h - 1 ? 0.0L : M.density(b) * (b - mean) / P;
     }
   };
   std::vector<ld> m(h), da(h), db(h);
@@ -176,9 +246,12 @@ int tq_build_codebook(int bits, int kind, float* centroids, float* boundaries) {
   if (!centroids || !boundaries) return fail(TQ_ERR_INVALID_ARG, "null output array");
   const int L = 1 << bits, h = L / 2;
   std::vector<ld> c(L);
-  if (kind == TQ_CODEBOOK_LLOYD_MAX) {
+  if (kind == TQ_CODEBOOK_LLOYD_MAX || kind == TQ_CODEBOOK_BETA) {
     std::vector<ld> cpos;
-    lloyd_max(bits, cpos);
+    if (kind == TQ_CODEBOOK_LLOYD_MAX)
+      lloyd_max(bits, GaussianModel(), cpos);
+    else
+      lloyd_max(bits, SphereModel(TQ_HEAD_DIM), cpos);
     for (int i = 0; i < h; ++i) {
       c[h + i] = cpos[i];
       c[h - 1 - i] = -cpos[i];
@@ -342,9 +415,9 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 int check_layer(const tq_layer* L) {
   if (!L) return fail(TQ_ERR_INVALID_ARG, "null layer descriptor");
   if (L->head_dim != TQ_HEAD_DIM) return fail(TQ_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", L->head_dim);
-  if (L->k_codebook != TQ_CODEBOOK_LLOYD_MAX && L->k_codebook != TQ_CODEBOOK_UNIFORM)
+  if (L->k_codebook < TQ_CODEBOOK_LLOYD_MAX || L->k_codebook > TQ_CODEBOOK_BETA)
     return fail(TQ_ERR_INVALID_ARG, "unknown k_codebook %d", L->k_codebook);
-  if (L->v_codebook != TQ_CODEBOOK_LLOYD_MAX && L->v_codebook != TQ_CODEBOOK_UNIFORM)
+  if (L->v_codebook < TQ_CODEBOOK_LLOYD_MAX || L->v_codebook > TQ_CODEBOOK_BETA)
     return fail(TQ_ERR_INVALID_ARG, "unknown v_codebook %d", L->v_codebook);
   if (!L->sign_mask || !L->k_table || !L->v_table) return fail(TQ_ERR_INVALID_ARG, "null layer table");
   if (!aligned16(L->sign_mask) || !aligned16(L->k_table) || !aligned16(L->v_table))

@@ -53,6 +53,7 @@ PAGE_TOKENS = 64
 STREAM_CODES = 128
 LLOYD_MAX = 0
 UNIFORM = 1
+BETA = 2
 
 
 # ----------------------------------------------------------------------------
@@ -225,6 +226,102 @@ def uniform_gaussian(bits: int) -> Tuple[np.ndarray, np.ndarray]:
 _UNIFORM_DELTA: Dict[int, float] = {}
 
 
+# The Beta codebook ("TurboMOQ", Head-to-Head Comparison: Beta-CDF; Project
+# Structure: Beta-distribution codebooks): Lloyd-Max for the law of one
+# coordinate of sqrt(d) times a uniformly random unit vector of R^d,
+#   f(u) = C (1 - u^2/d)^((d-3)/2) on |u| < sqrt(d),
+#   C = Gamma(d/2) / (sqrt(pi d) Gamma((d-1)/2)),
+# i.e. u^2/d ~ Beta(1/2, (d-1)/2).  For x >= 0 the upper tail is
+# (1/2) I_{1-x^2/d}((d-1)/2, 1/2) and the partial first moment
+# int_x^sqrt(d) u f(u) du = C d/(d-1) (1 - x^2/d)^((d-1)/2).
+def _sphere_c(d: int) -> float:
+    return math.exp(math.lgamma(d / 2) - math.lgamma((d - 1) / 2)) / math.sqrt(math.pi * d)
+
+
+def _sphere_lloyd_map(cpos: np.ndarray, d: int) -> np.ndarray:
+    """One Lloyd-Max update of the positive half under the sphere marginal."""
+    from scipy.special import betainc
+    C = _sphere_c(d)
+    c = np.concatenate((-cpos[::-1], cpos))
+    t = 0.5 * (c[:-1] + c[1:])
+    edges = np.concatenate(([0.0], t[cpos.size:], [math.sqrt(d)]))
+    y = np.clip(1.0 - edges * edges / d, 0.0, 1.0)
+    tail = 0.5 * betainc((d - 1) / 2, 0.5, y)
+    mom = C * d / (d - 1) * y ** ((d - 1) / 2)
+    return (mom[:-1] - mom[1:]) / (tail[:-1] - tail[1:])
+
+
+@lru_cache(maxsize=None)
+def lloyd_max_sphere(bits: int, d: int = HEAD_DIM) -> Tuple[np.ndarray, np.ndarray]:
+    """MSE-optimal 2^bits-level quantiser of the sphere marginal above.
+
+    Steps as for the Gaussian: Lloyd iterations from the Gaussian codebook, a
+    library root finder in float64, then Newton steps in 40-digit arithmetic
+    whose Jacobian is the tridiagonal one of the conditions
+    c_i = E[U | a_i <= U < b_i] with a_i, b_i the midpoints next to c_i:
+    d mean / d a = f(a) (mean - a) / P and d mean / d b = f(b) (b - mean) / P.
+    Returns (centroids, boundaries) in float64, ascending.
+    """
+    import mpmath as mp
+    L = 1 << bits
+    h = L // 2
+    cpos = lloyd_max_gaussian(bits)[0][h:].copy()
+    for _ in range(200):
+        cpos = _sphere_lloyd_map(cpos, d)
+    sol = optimize.root(lambda c: c - _sphere_lloyd_map(c, d), cpos, method="hybr", tol=1e-15)
+    cpos = np.sort(sol.x)
+    with mp.workdps(40):
+        D = mp.mpf(d)
+        C = mp.gamma(D / 2) / (mp.sqrt(mp.pi * D) * mp.gamma((D - 1) / 2))
+        end = mp.sqrt(D)
+
+        def dens(x):
+            y = 1 - x * x / D
+            return C * y ** ((D - 3) / 2) if y > 0 else mp.mpf(0)
+
+        def tail(x):
+            y = 1 - x * x / D
+            return mp.betainc((D - 1) / 2, mp.mpf(1) / 2, 0, y, regularized=True) / 2 if y > 0 else mp.mpf(0)
+
+        def mom(x):
+            y = 1 - x * x / D
+            return C * D / (D - 1) * y ** ((D - 1) / 2) if y > 0 else mp.mpf(0)
+
+        c = [mp.mpf(float(v)) for v in cpos]
+        for _ in range(30):
+            a = [mp.mpf(0)] + [(c[i - 1] + c[i]) / 2 for i in range(1, h)]
+            b = a[1:] + [end]
+            ta = [tail(x) for x in a] + [mp.mpf(0)]
+            ma = [mom(x) for x in a] + [mp.mpf(0)]
+            P = [ta[i] - ta[i + 1] for i in range(h)]
+            mean = [(ma[i] - ma[i + 1]) / P[i] for i in range(h)]
+            da = [dens(a[i]) * (mean[i] - a[i]) / P[i] for i in range(h)]
+            db = [dens(b[i]) * (b[i] - mean[i]) / P[i] if i < h - 1 else mp.mpf(0) for i in range(h)]
+            # J step = -F, J tridiagonal: lower -da_i/2, diagonal 1 - (da_i + db_i)/2, upper -db_i/2
+            rhs = [-(c[i] - mean[i]) for i in range(h)]
+            diag = [1 - (da[i] if i > 0 else 0) / 2 - db[i] / 2 for i in range(h)]
+            low = [-da[i] / 2 if i > 0 else mp.mpf(0) for i in range(h)]
+            up = [-db[i] / 2 for i in range(h)]
+            for i in range(1, h):
+                w = low[i] / diag[i - 1]
+                diag[i] -= w * up[i - 1]
+                rhs[i] -= w * rhs[i - 1]
+            step = [mp.mpf(0)] * h
+            step[h - 1] = rhs[h - 1] / diag[h - 1]
+            for i in range(h - 2, -1, -1):
+                step[i] = (rhs[i] - up[i] * step[i + 1]) / diag[i]
+            c = [c[i] + step[i] for i in range(h)]
+            if max(abs(x) for x in step) < mp.mpf(10) ** -34:
+                break
+        cfull = [-x for x in reversed(c)] + list(c)
+        tfull = [(cfull[i] + cfull[i + 1]) / 2 for i in range(L - 1)]
+        if d == HEAD_DIM:
+            _F32_TABLES[(bits, BETA)] = (
+                np.array([_round_f32(x) for x in cfull], dtype=np.float32),
+                np.array([_round_f32(x) for x in tfull], dtype=np.float32))
+        return np.array([float(x) for x in cfull]), np.array([float(x) for x in tfull])
+
+
 def uniform_step(bits: int) -> float:
     uniform_gaussian(bits)
     return _UNIFORM_DELTA[bits]
@@ -236,6 +333,8 @@ def codebook(bits: int, kind: int = LLOYD_MAX) -> Tuple[np.ndarray, np.ndarray]:
         lloyd_max_gaussian(bits)
     elif kind == UNIFORM:
         uniform_gaussian(bits)
+    elif kind == BETA:
+        lloyd_max_sphere(bits)
     else:
         raise ValueError(kind)
     return _F32_TABLES[(bits, kind)]

@@ -237,3 +237,13 @@ def test_qjl_scoring_modes(dev, mode):
             err = np.abs(out[b, rows] - ref).max(axis=1) / np.abs(ref).max(axis=1)
             t.worst_attn = max(t.worst_attn, float(err.max()))
     t.check()
+
+
+def test_every_bit_width_pair_beta_codebook(dev):
+    run_case(_all_bits_workload(kind=O.BETA, pages=40), [0], dev)
+
+
+def test_beta_keys_lloyd_max_values_with_qjl(dev):
+    w = _all_bits_workload(pages=24, qjl=True)
+    w.k_codebook, w.v_codebook = O.BETA, O.LLOYD_MAX
+    run_case(w, [0], dev)

@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol(L):
         assert hasattr(L, name)
 
 
-@pytest.mark.parametrize("kind", [tq.LLOYD_MAX, tq.UNIFORM])
+@pytest.mark.parametrize("kind", [tq.LLOYD_MAX, tq.UNIFORM, tq.BETA])
 @pytest.mark.parametrize("bits", range(1, 9))
 def test_codebook_bit_equal_to_oracle(L, bits, kind):
     c, t = tq.build_codebook(bits, kind)
@@ -39,7 +39,7 @@ def test_codebook_bit_equal_to_oracle(L, bits, kind):
     assert np.array_equal(t.view(np.uint32), ot.view(np.uint32))
 
 
-@pytest.mark.parametrize("kind", [tq.LLOYD_MAX, tq.UNIFORM])
+@pytest.mark.parametrize("kind", [tq.LLOYD_MAX, tq.UNIFORM, tq.BETA])
 def test_codebook_table_layout(L, kind):
     tab = tq.codebook_table(kind)
     for b in range(1, 9):

@@ -554,3 +554,60 @@ def test_decode_attention_unit_qjl_matches_reconstruction_in_unbiased_mode():
     got = O.decode_attention_unit_qjl(qs, Kb, V, qj["z"], g, S, O.QJL_SCORE_UNBIASED)
     Kh = Kb + O.qjl_reconstruct(qj["z"], g, S)
     assert np.allclose(got, O.decode_attention_unit(qs, Kh, V), rtol=1e-10, atol=1e-12)
+
+
+# ------------------------------------------------------------ Beta codebook
+def _sphere_density(u, d=128):
+    # written out directly from the law of sqrt(d) x_1, x uniform on the unit sphere
+    c = math.gamma(d / 2) / (math.sqrt(math.pi * d) * math.gamma((d - 1) / 2))
+    y = 1.0 - u * u / d
+    return c * y ** ((d - 3) / 2) if y > 0 else 0.0
+
+
+def test_beta_codebook_pins():
+    from scipy import integrate
+    d = 128
+    end = math.sqrt(d)
+    # the density is a probability law with unit variance
+    assert abs(integrate.quad(_sphere_density, -end, end, epsabs=1e-13)[0] - 1) < 1e-10
+    assert abs(integrate.quad(lambda u: u * u * _sphere_density(u), -end, end, epsabs=1e-13)[0] - 1) < 1e-10
+    # 1 bit: the centroid is E|U| = sqrt(d) Gamma(d/2) / (sqrt(pi) Gamma((d+1)/2))
+    c1, t1 = O.codebook(1, O.BETA)
+    want = math.sqrt(d) * math.exp(math.lgamma(d / 2) - math.lgamma((d + 1) / 2)) / math.sqrt(math.pi)
+    assert np.float32(want) == c1[1] and c1[0] == -c1[1] and t1[0] == 0
+    # centroid condition by quadrature, cell by cell
+    for bits in (2, 3, 4, 5):
+        c, t = O.codebook(bits, O.BETA)
+        edges = np.concatenate(([-end], t.astype(np.float64), [end]))
+        for k in range(c.size):
+            a, b = edges[k], edges[k + 1]
+            P = integrate.quad(_sphere_density, a, b, epsabs=1e-15, limit=200)[0]
+            M = integrate.quad(lambda u: u * _sphere_density(u), a, b, epsabs=1e-15, limit=200)[0]
+            assert abs(M / P - c[k]) < 2e-6 * max(1.0, abs(c[k])), (bits, k, M / P, c[k])
+        assert np.array_equal(c, -c[::-1])
+    # optimal for its law: a lower MSE under the sphere density than the
+    # Gaussian Lloyd-Max codebook of the same width
+    def mse(c, t):
+        edges = np.concatenate(([-end], t.astype(np.float64), [end]))
+        return sum(integrate.quad(lambda u: (u - c[k]) ** 2 * _sphere_density(u), edges[k], edges[k + 1],
+                                  epsabs=1e-15, limit=200)[0] for k in range(c.size))
+    for bits in (1, 2, 3, 4):
+        assert mse(*O.codebook(bits, O.BETA)) < mse(*O.codebook(bits, O.LLOYD_MAX))
+    # as d grows the law tends to N(0,1) and so does the codebook
+    for bits in (1, 2, 3):
+        big, _ = O.lloyd_max_sphere(bits, d=10 ** 7)
+        gauss, _ = O.lloyd_max_gaussian(bits)
+        assert np.allclose(big, gauss, atol=1e-6)
+
+
+def test_beta_codebook_law_matches_random_directions():
+    """The law the codebook is built for is that of rotated, normalised
+    coordinates of random directions: empirical tails of sqrt(d) x_1."""
+    from scipy import integrate
+    rng = np.random.default_rng(23)
+    X = rng.standard_normal((200000, 128))
+    u = math.sqrt(128) * X[:, 0] / np.linalg.norm(X, axis=1)
+    for t in (0.5, 1.0, 2.0):
+        p = integrate.quad(_sphere_density, t, math.sqrt(128), epsabs=1e-14)[0]
+        emp = np.mean(u >= t)
+        assert abs(emp - p) < 5 * math.sqrt(p * (1 - p) / u.size)
