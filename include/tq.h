@@ -65,7 +65,8 @@ enum {
   TQ_ERR_DEVICE = -5       /* HIP reported an error when launching           */
 };
 
-enum { TQ_CODEBOOK_LLOYD_MAX = 0, TQ_CODEBOOK_UNIFORM = 1, TQ_CODEBOOK_BETA = 2 };
+enum { TQ_CODEBOOK_LLOYD_MAX = 0, TQ_CODEBOOK_UNIFORM = 1, TQ_CODEBOOK_BETA = 2,
+       TQ_CODEBOOK_FITTED = 3 /* a table from tq_calibrated_table */ };
 enum { TQ_DTYPE_F32 = 0, TQ_DTYPE_F16 = 1 };
 enum { TQ_QJL_SCORE_UNBIASED = 0, TQ_QJL_SCORE_SIGN = 1 };
 
@@ -238,6 +239,28 @@ int tq_build_codebook(int bits, int kind, float* centroids, float* boundaries);
  * TQ_CODEBOOK_TABLE_FLOATS floats to a host array (copy it to the device for
  * tq_layer). */
 int tq_codebook_table(int kind, float* table);
+
+/* Codebook fitted to sample head vectors ("TurboMOQ", Quick Start: calibrate
+ * codebooks from sample data; Architecture: Lloyd-Max codebook (k-means);
+ * Limitations: Lloyd-Max codebooks need sample data).  The samples are the
+ * rotated, normalised coordinates u = sqrt(128) R x / ||x|| of the n nonzero
+ * vectors (host float32, n x 128, rotated with the layer's signs) together
+ * with their mirror images -u, so the codebook is symmetric as the encoder
+ * requires.  Lloyd's iteration (k-means in one dimension): levels start at the
+ * Gaussian Lloyd-Max ones; each sweep assigns every sample to the cell between
+ * the midpoints of neighbouring levels and moves each level to its cell's mean
+ * (a level whose cell is empty stays), until no sample changes cell or 200
+ * sweeps.  Writes 2^bits ascending centroids and their 2^bits - 1 midpoints
+ * (float32 of the double values).  Deterministic; host memory only. */
+int tq_fit_codebook(const float* vectors, size_t n, const int8_t* signs, int bits,
+                    float* centroids, float* boundaries);
+
+/* A codebook table (as tq_codebook_table writes) of the codebooks
+ * tq_fit_codebook fits at every width 1..8 from the same samples; use it as
+ * tq_layer.k_table or v_table with kind TQ_CODEBOOK_FITTED.
+ * TQ_ERR_UNSUPPORTED when a width's boundaries are too close together for the
+ * encoder's lookup grid (too few distinct samples). */
+int tq_calibrated_table(const float* vectors, size_t n, const int8_t* signs, float* table);
 
 /* Layer randomness from a seed ("TurboQuant-MLX v2.0", What's New: seed 42;
  * MLX TurboQuant skill page, Standalone Benchmark: one cache per layer seeded

@@ -22,6 +22,7 @@ CODEBOOK_TABLE_FLOATS = 8192
 LLOYD_MAX = 0
 UNIFORM = 1
 BETA = 2
+FITTED = 3
 DTYPE_F32 = 0
 DTYPE_F16 = 1
 QJL_SCORE_UNBIASED = 0
@@ -32,7 +33,8 @@ LIB_PATH = os.path.join(_PKG, "lib", "libtq.so")
 EXPORTS = ("tq_page_bytes", "tq_page_descriptor", "tq_build_codebook", "tq_codebook_table",
            "tq_layer_params", "tq_sign_mask", "tq_decode_workspace_bytes", "tq_cache_bytes",
            "tq_status_string", "tq_last_error", "tq_encode_kv", "tq_decode_attention",
-           "tq_dequantize", "tq_append_kv", "tq_retier_pages", "tq_decode_attention_mass")
+           "tq_dequantize", "tq_append_kv", "tq_retier_pages", "tq_decode_attention_mass",
+           "tq_fit_codebook", "tq_calibrated_table")
 
 
 class TQError(RuntimeError):
@@ -90,6 +92,9 @@ def lib() -> ctypes.CDLL:
         L.tq_page_descriptor.argtypes = [ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
         L.tq_build_codebook.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
         L.tq_codebook_table.argtypes = [ctypes.c_int, ctypes.c_void_p]
+        L.tq_fit_codebook.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                      ctypes.c_void_p, ctypes.c_void_p]
+        L.tq_calibrated_table.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
         L.tq_layer_params.argtypes = [ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_void_p, ctypes.c_void_p]
         L.tq_sign_mask.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
@@ -141,6 +146,37 @@ def codebook_table(kind: int = LLOYD_MAX):
     import numpy as np
     tab = np.zeros(CODEBOOK_TABLE_FLOATS, np.float32)
     check(lib().tq_codebook_table(kind, tab.ctypes.data), "tq_codebook_table")
+    return tab
+
+
+def _samples(vectors, signs):
+    import numpy as np
+    X = np.ascontiguousarray(np.asarray(vectors, dtype=np.float32).reshape(-1, HEAD_DIM))
+    sg = np.ascontiguousarray(np.asarray(signs, dtype=np.int8))
+    if sg.size != HEAD_DIM:
+        raise TQError("signs must hold 128 entries")
+    return X, sg
+
+
+def fit_codebook(vectors, signs, bits: int):
+    """tq_fit_codebook: (centroids, boundaries) fitted to sample vectors [n, 128]."""
+    import numpy as np
+    X, sg = _samples(vectors, signs)
+    L = 1 << bits
+    c = np.zeros(L, np.float32)
+    t = np.zeros(max(L - 1, 1), np.float32)
+    check(lib().tq_fit_codebook(X.ctypes.data, X.shape[0], sg.ctypes.data, bits, c.ctypes.data,
+                                t.ctypes.data), "tq_fit_codebook")
+    return c, t[:L - 1]
+
+
+def calibrated_table(vectors, signs):
+    """tq_calibrated_table: a codebook table fitted to sample vectors [n, 128]."""
+    import numpy as np
+    X, sg = _samples(vectors, signs)
+    tab = np.zeros(CODEBOOK_TABLE_FLOATS, np.float32)
+    check(lib().tq_calibrated_table(X.ctypes.data, X.shape[0], sg.ctypes.data, tab.ctypes.data),
+          "tq_calibrated_table")
     return tab
 
 
@@ -203,14 +239,20 @@ class Layer:
     """Device-side constants of one layer: D, codebook tables, optional S."""
 
     def __init__(self, signs, device, qjl_s=None, k_codebook: int = LLOYD_MAX,
-                 v_codebook: int = LLOYD_MAX):
+                 v_codebook: int = LLOYD_MAX, k_table=None, v_table=None):
+        """k_table / v_table: a table from calibrated_table (kind FITTED) in
+        place of the built-in codebook of that kind."""
         import numpy as np
         import torch
         self.device = torch.device(device)
         self.signs = np.asarray(signs, dtype=np.int8)
         self.mask = torch.from_numpy(sign_mask(self.signs).view(np.int32).copy()).to(self.device)
-        self.k_table = torch.from_numpy(codebook_table(k_codebook)).to(self.device)
-        self.v_table = torch.from_numpy(codebook_table(v_codebook)).to(self.device)
+        if (k_table is None) == (k_codebook == FITTED) or (v_table is None) == (v_codebook == FITTED):
+            raise TQError("a FITTED codebook comes with its table, and only a FITTED one does")
+        kt = codebook_table(k_codebook) if k_table is None else np.asarray(k_table, dtype=np.float32)
+        vt = codebook_table(v_codebook) if v_table is None else np.asarray(v_table, dtype=np.float32)
+        self.k_table = torch.from_numpy(np.ascontiguousarray(kt)).to(self.device)
+        self.v_table = torch.from_numpy(np.ascontiguousarray(vt)).to(self.device)
         self.qjl_s = None
         if qjl_s is not None:
             self.qjl_s = torch.from_numpy(np.ascontiguousarray(qjl_s, dtype=np.float32)).to(self.device)

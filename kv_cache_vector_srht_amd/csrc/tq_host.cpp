@@ -267,15 +267,17 @@ int tq_build_codebook(int bits, int kind, float* centroids, float* boundaries) {
   return ok();
 }
 
-int tq_codebook_table(int kind, float* table) {
-  if (!table) return fail(TQ_ERR_INVALID_ARG, "null table");
-  memset(table, 0, sizeof(float) * TQ_CODEBOOK_TABLE_FLOATS);
+}  // extern "C"
+
+namespace tq {
+
+// The encoder's lookup grids of a table whose centroids and boundaries are in
+// place (layout in tq_codebook_table's description).
+static int build_grids(float* table) {
   uint32_t* words = reinterpret_cast<uint32_t*>(table);
   int next = kLutEntriesOffset;
   for (int b = 1; b <= 8; ++b) {
     float* t = table + boundary_offset(b);
-    int st = tq_build_codebook(b, kind, table + centroid_offset(b), t);
-    if (st != TQ_OK) return st;
     // Quantiser lookup grid: bins of width h over [-T, T) with
     // idx = floor(u * S + O), S = 1/h, O = T/h.  Bin i, widened by h/4 on each
     // side, holds at most one boundary; base = boundaries below the widened bin.
@@ -287,6 +289,8 @@ int tq_codebook_table(int kind, float* table) {
     // A grid of at most 256 bins is stored as exactly 256 and indexed by the
     // saturating round-to-nearest byte conversion of u S + O - 1/2 (bins past
     // the grid's end hold the top code), which saves the clamp.
+    if (!(gap > 0.0) || 2.0 * (tmax / gap + 1.0) * 2.5 > TQ_CODEBOOK_TABLE_FLOATS)
+      return fail(TQ_ERR_UNSUPPORTED, "boundaries of width %d too close for the lookup grid", b);
     const double h = gap / 2.5, T = tmax + 2.0 * h;
     const float S = (float)(1.0 / h), O = (float)(T / h);
     int nb = (int)ceil(2.0 * T / h) + 1;
@@ -316,6 +320,116 @@ int tq_codebook_table(int kind, float* table) {
     next += 2 * nb;
   }
   return ok();
+}
+
+// Magnitudes |u| of the rotated, normalised coordinates
+// u = D H D x / ||x|| (= sqrt(d) R x / ||x||) of the nonzero sample vectors, in
+// double, sorted.
+static std::vector<double> sample_magnitudes(const float* vectors, size_t n, const int8_t* signs) {
+  const int d = TQ_HEAD_DIM;
+  std::vector<double> u;
+  u.reserve(n * d);
+  double y[TQ_HEAD_DIM];
+  for (size_t v = 0; v < n; ++v) {
+    const float* x = vectors + v * d;
+    double ss = 0.0;
+    for (int j = 0; j < d; ++j) ss += (double)x[j] * (double)x[j];
+    if (!(ss > 0.0)) continue;
+    const double inv = 1.0 / sqrt(ss);
+    for (int j = 0; j < d; ++j) y[j] = signs[j] * (double)x[j];
+    for (int h = 1; h < d; h <<= 1)
+      for (int i = 0; i < d; i += 2 * h)
+        for (int j = i; j < i + h; ++j) {
+          const double a = y[j], b = y[j + h];
+          y[j] = a + b;
+          y[j + h] = a - b;
+        }
+    for (int j = 0; j < d; ++j) u.push_back(fabs(y[j]) * inv);
+  }
+  std::sort(u.begin(), u.end());
+  return u;
+}
+
+// A symmetric codebook fitted to the samples and their mirror images (the
+// encoder relies on t_k = -t_{L-2-k}): Lloyd's iteration (k-means in one
+// dimension) on the positive half, over the sorted magnitudes.  The positive
+// cells are [0, t_1), [t_1, t_2), ..., [t_{h-1}, inf) with t_i the midpoints of
+// the current levels; each level moves to the mean of its cell (an empty cell
+// keeps its level) until no sample changes cell or kFitSweeps sweeps.  Starts
+// from the Gaussian Lloyd-Max levels.  Writes the 2^bits levels and their
+// midpoints.
+constexpr int kFitSweeps = 200;
+
+static int fit_levels(const std::vector<double>& u, int bits, float* centroids, float* boundaries) {
+  const int L = 1 << bits, h = L / 2;
+  std::vector<float> c0(L), t0(L);
+  int st = tq_build_codebook(bits, TQ_CODEBOOK_LLOYD_MAX, c0.data(), t0.data());
+  if (st != TQ_OK) return st;
+  std::vector<double> c(c0.begin() + h, c0.end());
+  std::vector<size_t> pos(h + 1), prev(h + 1, (size_t)-1);
+  for (int sweep = 0; sweep < kFitSweeps; ++sweep) {
+    pos[0] = 0;
+    pos[h] = u.size();
+    for (int k = 1; k < h; ++k)
+      pos[k] = (size_t)(std::lower_bound(u.begin(), u.end(), 0.5 * (c[k - 1] + c[k])) - u.begin());
+    if (pos == prev) break;
+    for (int k = 0; k < h; ++k) {
+      if (pos[k + 1] <= pos[k]) continue;
+      long double sum = 0.0L;
+      for (size_t i = pos[k]; i < pos[k + 1]; ++i) sum += u[i];
+      c[k] = (double)(sum / (long double)(pos[k + 1] - pos[k]));
+    }
+    prev = pos;
+  }
+  std::vector<double> full(L);
+  for (int i = 0; i < h; ++i) {
+    full[h + i] = c[i];
+    full[h - 1 - i] = -c[i];
+  }
+  for (int k = 0; k < L; ++k) centroids[k] = (float)full[k];
+  for (int k = 0; k + 1 < L; ++k) boundaries[k] = (float)(0.5 * (full[k] + full[k + 1]));
+  return TQ_OK;
+}
+
+}  // namespace tq
+
+extern "C" {
+
+int tq_codebook_table(int kind, float* table) {
+  if (!table) return fail(TQ_ERR_INVALID_ARG, "null table");
+  memset(table, 0, sizeof(float) * TQ_CODEBOOK_TABLE_FLOATS);
+  for (int b = 1; b <= 8; ++b) {
+    int st = tq_build_codebook(b, kind, table + centroid_offset(b), table + boundary_offset(b));
+    if (st != TQ_OK) return st;
+  }
+  return build_grids(table);
+}
+
+int tq_fit_codebook(const float* vectors, size_t n, const int8_t* signs, int bits, float* centroids,
+                    float* boundaries) {
+  if (bits < 1 || bits > 8) return fail(TQ_ERR_UNSUPPORTED, "bits must be in 1..8 (got %d)", bits);
+  if (!vectors || !signs || !centroids || !boundaries) return fail(TQ_ERR_INVALID_ARG, "null pointer");
+  for (int j = 0; j < TQ_HEAD_DIM; ++j)
+    if (signs[j] != 1 && signs[j] != -1) return fail(TQ_ERR_INVALID_ARG, "sign %d is not +-1", j);
+  const std::vector<double> u = sample_magnitudes(vectors, n, signs);
+  if (u.empty()) return fail(TQ_ERR_INVALID_ARG, "no nonzero sample vector");
+  int st = fit_levels(u, bits, centroids, boundaries);
+  return st != TQ_OK ? st : ok();
+}
+
+int tq_calibrated_table(const float* vectors, size_t n, const int8_t* signs, float* table) {
+  if (!table) return fail(TQ_ERR_INVALID_ARG, "null table");
+  if (!vectors || !signs) return fail(TQ_ERR_INVALID_ARG, "null pointer");
+  for (int j = 0; j < TQ_HEAD_DIM; ++j)
+    if (signs[j] != 1 && signs[j] != -1) return fail(TQ_ERR_INVALID_ARG, "sign %d is not +-1", j);
+  const std::vector<double> u = sample_magnitudes(vectors, n, signs);
+  if (u.empty()) return fail(TQ_ERR_INVALID_ARG, "no nonzero sample vector");
+  memset(table, 0, sizeof(float) * TQ_CODEBOOK_TABLE_FLOATS);
+  for (int b = 1; b <= 8; ++b) {
+    int st = fit_levels(u, b, table + centroid_offset(b), table + boundary_offset(b));
+    if (st != TQ_OK) return st;
+  }
+  return build_grids(table);
 }
 
 static uint64_t splitmix64_at(uint64_t seed, uint64_t index) {
@@ -415,9 +529,9 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 int check_layer(const tq_layer* L) {
   if (!L) return fail(TQ_ERR_INVALID_ARG, "null layer descriptor");
   if (L->head_dim != TQ_HEAD_DIM) return fail(TQ_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", L->head_dim);
-  if (L->k_codebook < TQ_CODEBOOK_LLOYD_MAX || L->k_codebook > TQ_CODEBOOK_BETA)
+  if (L->k_codebook < TQ_CODEBOOK_LLOYD_MAX || L->k_codebook > TQ_CODEBOOK_FITTED)
     return fail(TQ_ERR_INVALID_ARG, "unknown k_codebook %d", L->k_codebook);
-  if (L->v_codebook < TQ_CODEBOOK_LLOYD_MAX || L->v_codebook > TQ_CODEBOOK_BETA)
+  if (L->v_codebook < TQ_CODEBOOK_LLOYD_MAX || L->v_codebook > TQ_CODEBOOK_FITTED)
     return fail(TQ_ERR_INVALID_ARG, "unknown v_codebook %d", L->v_codebook);
   if (!L->sign_mask || !L->k_table || !L->v_table) return fail(TQ_ERR_INVALID_ARG, "null layer table");
   if (!aligned16(L->sign_mask) || !aligned16(L->k_table) || !aligned16(L->v_table))

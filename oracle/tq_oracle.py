@@ -327,8 +327,65 @@ def uniform_step(bits: int) -> float:
     return _UNIFORM_DELTA[bits]
 
 
+# Codebooks fitted to sample data ("TurboMOQ", Quick Start: calibrate codebooks
+# from sample data; Architecture: Lloyd-Max codebook (k-means)).
+class FittedCodebook:
+    """Fitted codebooks for every width: pass one wherever a codebook kind goes."""
+
+    def __init__(self, tables: Dict[int, Tuple[np.ndarray, np.ndarray]]):
+        self.tables = tables
+
+
+def sample_magnitudes(X: np.ndarray, signs) -> np.ndarray:
+    """|u| for every coordinate of u = sqrt(d) R x / ||x|| of the nonzero rows
+    of X, sorted (the samples and their mirror images -u share them)."""
+    X = np.asarray(X, dtype=np.float64).reshape(-1, HEAD_DIM)
+    n = np.sqrt(np.sum(X * X, axis=1))
+    X = X[n > 0]
+    n = n[n > 0]
+    R = rotation_matrix(signs)
+    U = math.sqrt(HEAD_DIM) * (X @ R.T) / n[:, None]
+    return np.sort(np.abs(U).ravel())
+
+
+def fit_levels(mags: np.ndarray, bits: int, sweeps: int = 200) -> Tuple[np.ndarray, np.ndarray]:
+    """Lloyd's iteration (k-means in one dimension) for a symmetric codebook.
+
+    The positive levels c_0 < ... < c_{h-1} start at the Gaussian Lloyd-Max
+    ones.  A sweep puts each magnitude in the cell between the midpoints of its
+    neighbouring levels (the first cell starts at 0, the last is open) and moves
+    every level to the mean of its cell; an empty cell keeps its level.  Stops
+    when no magnitude changes cell, or after `sweeps` sweeps.  Returns float32
+    (centroids, boundaries): the levels mirrored, and the midpoints taken in
+    float64.
+    """
+    L = 1 << bits
+    h = L // 2
+    c = codebook(bits, LLOYD_MAX)[0][h:].astype(np.float64)
+    prev = None
+    for _ in range(sweeps):
+        t = 0.5 * (c[:-1] + c[1:])
+        pos = np.concatenate(([0], np.searchsorted(mags, t, side="left"), [mags.size]))
+        if prev is not None and np.array_equal(pos, prev):
+            break
+        for k in range(h):
+            if pos[k + 1] > pos[k]:
+                c[k] = mags[pos[k]:pos[k + 1]].mean()
+        prev = pos
+    full = np.concatenate((-c[::-1], c))
+    return full.astype(np.float32), (0.5 * (full[:-1] + full[1:])).astype(np.float32)
+
+
+def fit_codebooks(X: np.ndarray, signs) -> FittedCodebook:
+    """Fitted codebooks of every width 1..8 from the sample vectors X [n, 128]."""
+    mags = sample_magnitudes(X, signs)
+    return FittedCodebook({b: fit_levels(mags, b) for b in range(1, 9)})
+
+
 def codebook(bits: int, kind: int = LLOYD_MAX) -> Tuple[np.ndarray, np.ndarray]:
     """(centroids, boundaries) as float32 arrays, the values both sides compare with."""
+    if isinstance(kind, FittedCodebook):
+        return kind.tables[bits]
     if kind == LLOYD_MAX:
         lloyd_max_gaussian(bits)
     elif kind == UNIFORM:

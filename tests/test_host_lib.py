@@ -39,9 +39,47 @@ def test_codebook_bit_equal_to_oracle(L, bits, kind):
     assert np.array_equal(t.view(np.uint32), ot.view(np.uint32))
 
 
-@pytest.mark.parametrize("kind", [tq.LLOYD_MAX, tq.UNIFORM, tq.BETA])
-def test_codebook_table_layout(L, kind):
-    tab = tq.codebook_table(kind)
+@pytest.fixture(scope="module")
+def fit_samples():
+    """Keys (with outlier channels) and values of a small workload, and the
+    oracle's fitted codebooks of each."""
+    w = W.make_workload(2, {"n_tokens": 128})
+    k, v = W.make_kv(w, 0)
+    signs = W.rotation_signs(42, 0)
+    out = []
+    for x in (k, v):
+        X = x.float().numpy().reshape(-1, 128)
+        out.append((X, O.fit_codebooks(X, signs)))
+    return signs, out
+
+
+@pytest.mark.parametrize("which", [0, 1])
+def test_fitted_codebooks_bit_equal_to_oracle(L, fit_samples, which):
+    signs, samples = fit_samples
+    X, fc = samples[which]
+    tab = tq.calibrated_table(X, signs)
+    for b in range(1, 9):
+        c, t = tq.fit_codebook(X, signs, b)
+        oc, ot = fc.tables[b]
+        assert np.array_equal(c.view(np.uint32), oc.view(np.uint32)), b
+        assert np.array_equal(t.view(np.uint32), ot.view(np.uint32)), b
+        co, to = (1 << b) - 2, 510 + (1 << b) - b - 1
+        assert np.array_equal(tab[co:co + (1 << b)], c) and np.array_equal(tab[to:to + (1 << b) - 1], t)
+    # zero vectors are skipped; all-zero samples are refused
+    Xz = np.concatenate([X, np.zeros((5, 128), np.float32)])
+    assert np.array_equal(tq.fit_codebook(Xz, signs, 3)[0], fc.tables[3][0])
+    with pytest.raises(tq.TQError):
+        tq.fit_codebook(np.zeros((4, 128), np.float32), signs, 2)
+
+
+@pytest.mark.parametrize("kind", [tq.LLOYD_MAX, tq.UNIFORM, tq.BETA, "fitted"])
+def test_codebook_table_layout(L, kind, fit_samples):
+    if kind == "fitted":
+        signs, samples = fit_samples
+        X, kind = samples[0]
+        tab = tq.calibrated_table(X, signs)
+    else:
+        tab = tq.codebook_table(kind)
     for b in range(1, 9):
         c, t = O.codebook(b, kind)
         co, to = (1 << b) - 2, 510 + (1 << b) - b - 1
@@ -140,7 +178,7 @@ def _encode(L, layer, cache, **kw):
 def test_encode_validation(L):
     bad = [
         (dict(layer=_fake_layer(head_dim=64)), -2),
-        (dict(layer=_fake_layer(k_codebook=3)), -1),
+        (dict(layer=_fake_layer(k_codebook=4)), -1),
         (dict(layer=_fake_layer(sign_mask=0x1004)), -3),
         (dict(layer=_fake_layer(qjl_s=0x6000, jl_dim=64)), -2),
         (dict(cache=_fake_cache(n_sessions=0)), -1),

@@ -611,3 +611,61 @@ def test_beta_codebook_law_matches_random_directions():
         p = integrate.quad(_sphere_density, t, math.sqrt(128), epsabs=1e-14)[0]
         emp = np.mean(u >= t)
         assert abs(emp - p) < 5 * math.sqrt(p * (1 - p) / u.size)
+
+
+# -------------------------------------------------------- fitted codebooks
+def test_fit_levels_hand_example():
+    mags = np.array([0.1, 0.2, 0.3, 2.0, 2.2])
+    c, t = O.fit_levels(mags, 2)
+    assert np.allclose(c, [-2.1, -0.2, 0.2, 2.1], atol=1e-7) and np.allclose(t, [-1.15, 0.0, 1.15], atol=1e-7)
+    c1, t1 = O.fit_levels(mags, 1)
+    assert np.allclose(c1, [-mags.mean(), mags.mean()]) and t1[0] == 0
+    # symmetric at every width, and exactly so in float32
+    for b in range(1, 6):
+        c, t = O.fit_levels(np.sort(np.random.default_rng(b).exponential(size=3000)), b)
+        assert np.array_equal(c, -c[::-1]) and np.array_equal(t, -t[::-1])
+
+
+def test_sample_magnitudes_rotate_and_normalise():
+    signs = W.rotation_signs(42, 3)
+    R = O.rotation_matrix(signs)
+    Y = np.zeros((3, 128))
+    Y[0, :2] = [3.0, 4.0]
+    Y[2, 5] = -2.0            # row 1 is zero: skipped
+    X = Y @ R                  # R is symmetric and its own inverse, so R x = y
+    m = O.sample_magnitudes(X, signs)
+    want = np.sort(np.concatenate(([0.6 * math.sqrt(128), 0.8 * math.sqrt(128)], np.zeros(126),
+                                   [math.sqrt(128)], np.zeros(127))))
+    assert m.size == 256 and np.allclose(m, want, atol=1e-9)
+
+
+def test_fit_levels_is_a_fixed_point_of_k_means():
+    rng = np.random.default_rng(24)
+    mags = np.sort(np.abs(rng.standard_t(5, size=4000)))
+    for bits in (2, 3):
+        c, t = O.fit_levels(mags, bits, sweeps=10000)
+        h = c.size // 2
+        # brute force: each positive level is the mean of the magnitudes closer
+        # to it than to its neighbours
+        for k in range(h):
+            lo = 0.0 if k == 0 else (float(c[h + k - 1]) + float(c[h + k])) / 2
+            hi = math.inf if k == h - 1 else (float(c[h + k]) + float(c[h + k + 1])) / 2
+            cell = [x for x in mags if lo <= x < hi]
+            assert abs(sum(cell) / len(cell) - float(c[h + k])) < 1e-6
+        # k-means never raises its objective: below the Gaussian start's
+        def obj(levels):
+            pos = levels[levels.size // 2:].astype(np.float64)
+            return np.min((mags[:, None] - pos[None, :]) ** 2, axis=1).sum()
+        assert obj(c) <= obj(O.codebook(bits, O.LLOYD_MAX)[0])
+
+
+def test_fitted_codebooks_approach_the_laws_they_sample():
+    """Fitted to many samples of a law, the codebook approaches that law's
+    Lloyd-Max codebook: Gaussian magnitudes give the Gaussian one; rotated,
+    normalised Gaussian vectors (random directions) give the Beta one."""
+    rng = np.random.default_rng(25)
+    g = np.sort(np.abs(rng.standard_normal(2_000_000)))
+    m = O.sample_magnitudes(rng.standard_normal((20000, 128)), W.rotation_signs(42, 0))
+    for b in (1, 2, 3):
+        assert np.allclose(O.fit_levels(g, b)[0], O.codebook(b, O.LLOYD_MAX)[0], atol=0.005)
+        assert np.allclose(O.fit_levels(m, b)[0], O.codebook(b, O.BETA)[0], atol=0.005)
