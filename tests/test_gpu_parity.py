@@ -27,7 +27,7 @@ def _np(x):
 
 
 def run_case(w, layers, dev, units=None, n_tokens=None, dequant=True, chunks=None, tally=None,
-             query_dtype=None):
+             query_dtype=None, layer_kw=None):
     """Encode + decode every listed layer of workload w on the GPU; compare the
     listed units (all by default) with the oracle."""
     import kv_cache_vector_srht_amd as tq
@@ -38,7 +38,10 @@ def run_case(w, layers, dev, units=None, n_tokens=None, dequant=True, chunks=Non
         has_qjl = any(f[2] for row in fm for r in row for f in r)
         signs = W.rotation_signs(W.ROTATION_SEED, l)
         S = W.qjl_matrix(W.ROTATION_SEED, l) if has_qjl else None
-        layer = tq.Layer(signs, dev, S, w.k_codebook, w.v_codebook)
+        if layer_kw is None:
+            layer = tq.Layer(signs, dev, S, w.k_codebook, w.v_codebook)
+        else:
+            layer = tq.Layer(signs, dev, S, **layer_kw)
         ntoks = n_tokens or [w.n_tokens] * w.batch
         cache = tq.Cache(fm, ntoks, dev)
         k, v = W.make_kv(w, l, device=dev)
@@ -247,3 +250,22 @@ def test_beta_keys_lloyd_max_values_with_qjl(dev):
     w = _all_bits_workload(pages=24, qjl=True)
     w.k_codebook, w.v_codebook = O.BETA, O.LLOYD_MAX
     run_case(w, [0], dev)
+
+
+def test_fitted_codebooks(dev):
+    """Codebooks fitted to a sample of another layer's keys and values (in this
+    layer's rotation), the library's tables on the GPU, the oracle's own fit
+    on the CPU; every width pair, QJL on half the heads."""
+    import kv_cache_vector_srht_amd as tq
+    w = _all_bits_workload(pages=34)
+    w.formats = [[[[f if (h == 0 or f[0] == 0) else (f[0], f[1], True) for f in row]
+                   for h, row in enumerate(w.formats[0][0])]]]
+    cal = W.make_workload(2, {"n_tokens": 256})
+    kc, vc = W.make_kv(cal, 1)
+    signs = W.rotation_signs(42, 0)
+    Xk = kc.float().numpy().reshape(-1, 128)
+    Xv = vc.float().numpy().reshape(-1, 128)
+    w.k_codebook, w.v_codebook = O.fit_codebooks(Xk, signs), O.fit_codebooks(Xv, signs)
+    layer_kw = dict(k_codebook=tq.FITTED, v_codebook=tq.FITTED,
+                    k_table=tq.calibrated_table(Xk, signs), v_table=tq.calibrated_table(Xv, signs))
+    run_case(w, [0], dev, layer_kw=layer_kw)
