@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--workload", type=int, default=3, help="workload index 1..5 (default 3)")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tiering", type=int, default=1,
+                    help="measure page-mass export and page re-tiering (1, default) or skip (0)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
     ap.add_argument("--loop-steps", type=int, default=64,
                     help="decode-loop steps (append one token per session + decode attention, "
@@ -212,6 +214,83 @@ def decode_loop(w, layers, inputs, queries, outs, wss, steps, dev):
             "context": f"{w.n_tokens} + 1..{steps} tokens, every layer, one new token per session per step"}
 
 
+def tiering(w, layers, inputs, queries, outs, wss, dev):
+    """The mechanisms attention-weighted tier demotion runs on: decode with the
+    page attention mass exported (every layer, against plain decode), and
+    tq_retier_pages calls that each demote every packed page of a layer by one
+    bit in K and in V (floor 1) in place."""
+    import numpy as np
+    import torch
+    import kv_cache_vector_srht_amd as tq
+    stream = torch.cuda.current_stream(dev)
+    caches = []
+    for l in range(w.n_layers):
+        c = tq.Cache(w.formats[l], [w.n_tokens] * w.batch, dev)
+        k, v = inputs[l]
+        tq.encode_kv(layers[l], c, k, v, tok0=0)
+        caches.append(c)
+    masses = [torch.empty((w.batch, w.n_q_heads, c.max_pages), dtype=torch.float32, device=dev) for c in caches]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    t_plain = t_mass = 0.0
+    reps = 3
+    for r in range(reps + 1):
+        ev[0].record(stream)
+        for l in range(w.n_layers):
+            tq.decode_attention(layers[l], caches[l], queries[l], out=outs[l], workspace=wss[l])
+        ev[1].record(stream)
+        for l in range(w.n_layers):
+            tq.decode_attention(layers[l], caches[l], queries[l], out=outs[l], workspace=wss[l],
+                                page_mass=masses[l])
+        ev[2].record(stream)
+        ev[2].synchronize()
+        if r:   # the first round warms up
+            t_plain += ev[0].elapsed_time(ev[1])
+            t_mass += ev[1].elapsed_time(ev[2])
+    # one-bit demotion of every packed page of a layer, in place: a warm-up
+    # call on the last layer, then one timed call on each of the first eight
+    # (the median is reported)
+    def demotions(c):
+        pages, fmts, moved = [], [], 0
+        for b in range(c.n_sessions):
+            for h in range(c.n_kv_heads):
+                for p, f in enumerate(c.formats[b][h]):
+                    if f[0] >= 1 and not f[2]:
+                        nf = (max(1, f[0] - 1), max(1, f[1] - 1), False)
+                        pages.append((b, h, p))
+                        fmts.append(nf)
+                        moved += tq.page_bytes(f) + tq.page_bytes(nf)
+        return pages, fmts, moved
+    import ctypes
+    L = tq.lib()
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    runs = []
+    for l in [w.n_layers - 1] + list(range(min(8, w.n_layers - 1))):
+        c = caches[l]
+        pages, fmts, moved = demotions(c)
+        H, P = c.n_kv_heads, c.max_pages
+        # the page list is built and copied before the timed region
+        idx = torch.tensor([(b * H + h) * P + p for b, h, p in pages], dtype=torch.int64, device=dev)
+        desc = torch.from_numpy(np.array([L.tq_page_descriptor(int(c.offsets[pg]), f[0], f[1], 0)
+                                          for pg, f in zip(pages, fmts)], dtype=np.uint64).view(np.int64)).to(dev)
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        tq.check(L.tq_retier_pages(ctypes.byref(layers[l].struct), ctypes.byref(c.struct), idx.data_ptr(),
+                                   desc.data_ptr(), len(pages), tq.RETIER_FROM_PACKED, flags.data_ptr(),
+                                   ctypes.c_void_p(stream.cuda_stream)), "tq_retier_pages")
+        ev[1].record(stream)
+        ev[1].synchronize()
+        if l != w.n_layers - 1:
+            runs.append((ev[0].elapsed_time(ev[1]), len(pages), moved))
+    assert int(flags.item()) == 0
+    rt_ms, n_pages, moved = sorted(runs)[len(runs) // 2]
+    return {"decode_us_per_layer": round(t_plain / reps / w.n_layers * 1e3, 2),
+            "decode_with_mass_us_per_layer": round(t_mass / reps / w.n_layers * 1e3, 2),
+            "retier_pages": n_pages, "retier_us": round(rt_ms * 1e3, 2),
+            "retier_gbs": round(moved / (rt_ms / 1e3) / 1e9, 1),
+            "retier": "every packed page of a layer demoted by one bit in K and V, in place; "
+                      "median of the first eight layers, one call each"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -328,6 +407,8 @@ def main():
     }
     if args.loop_steps > 0:
         line["decode_loop"] = decode_loop(w, layers, inputs, queries, outs, wss, args.loop_steps, dev)
+    if args.tiering:
+        line["tiering"] = tiering(w, layers, inputs, queries, outs, wss, dev)
     if not args.no_cpu_baseline:
         kv_host = {}
 

@@ -111,6 +111,8 @@ enum { TQ_QJL_SCORE_UNBIASED = 0, TQ_QJL_SCORE_SIGN = 1 };
 #define TQ_PAGE_QJL (1ull << 56)
 #define TQ_PAGE_PENDING (1ull << 57)
 #define TQ_PAGE_OFFSET_MASK ((1ull << 48) - 1)
+#define TQ_RETIER_FROM_PACKED 1
+#define TQ_RETIER_FROM_FP16 2
 
 /* Bytes of one page: k_bits = 0 (and v_bits = 0, qjl = 0) for an fp16 page.
  * Returns 0 for an invalid combination. */
@@ -331,17 +333,22 @@ int tq_append_kv(const tq_layer* layer, const tq_cache* cache, const tq_token_in
  * no position may be listed twice.  page_index and new_desc are device
  * arrays (8-byte aligned) of n entries; the call writes the pool and the page
  * table.  Decode after the call needs tq_cache.page_classes to cover the new
- * formats.  Errors found on the device are OR-ed into error_flags (device int
- * or NULL), and the page is left untouched:
+ * formats.  sources says which source kinds the list holds, as the caller
+ * knows: TQ_RETIER_FROM_PACKED | TQ_RETIER_FROM_FP16, 0 = unknown (both); the
+ * work of a kind left out is not launched, and a listed page of that kind is
+ * refused (flag 64).  Errors found on the device are OR-ed into error_flags
+ * (device int or NULL), and the page is left untouched:
  *   2 = the old or new descriptor is not present,
  *   4 = invalid format, a slot outside the pool, or overlapping old and new
  *       slots,
  *   8 = a QJL target and layer->qjl_s is NULL,
  *   16 = page_index[i] outside the page table,
  *   64 = an unsupported change: a pending page, a QJL page as the source or
- *       (from a packed page) as the target, or a packed width that grows.  */
+ *       (from a packed page) as the target, a packed width that grows, or a
+ *       source kind that `sources` leaves out.  */
 int tq_retier_pages(const tq_layer* layer, const tq_cache* cache, const int64_t* page_index,
-                    const uint64_t* new_desc, int n, int32_t* error_flags, void* stream);
+                    const uint64_t* new_desc, int n, int sources, int32_t* error_flags,
+                    void* stream);
 
 /* out[b][h][0..127] (device float32, row stride 128, B x H_q rows) =
  * softmax_t(scale * q_bh . k_t) . v_t over t in [0, n_tokens[b]), where k_t,

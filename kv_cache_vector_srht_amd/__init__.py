@@ -116,7 +116,8 @@ def lib() -> ctypes.CDLL:
         L.tq_append_kv.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
                                    ctypes.POINTER(tq_token_input), ctypes.c_void_p]
         L.tq_retier_pages.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache), ctypes.c_void_p,
-                                      ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+                                      ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                      ctypes.c_void_p]
         L.tq_dequantize.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache), ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                     ctypes.c_void_p]
@@ -199,6 +200,8 @@ def sign_mask(signs):
 
 
 PAGE_PENDING = 1 << 57
+RETIER_FROM_PACKED = 1
+RETIER_FROM_FP16 = 2
 
 
 def is_pending(fmt) -> bool:
@@ -450,8 +453,12 @@ def retier_pages(layer: Layer, cache: Cache, pages, new_formats, new_offsets=Non
         return
     idx_t = torch.from_numpy(idx).to(cache.device)
     desc_t = torch.from_numpy(desc.view(np.int64)).to(cache.device)
+    # the source kinds present, from the record of formats
+    sources = 0
+    for b, h, p in pages:
+        sources |= RETIER_FROM_FP16 if cache.formats[b][h][p][0] == 0 else RETIER_FROM_PACKED
     check(L.tq_retier_pages(ctypes.byref(layer.struct), ctypes.byref(cache.struct), idx_t.data_ptr(),
-                            desc_t.data_ptr(), len(pages),
+                            desc_t.data_ptr(), len(pages), sources,
                             error_flags.data_ptr() if error_flags is not None else None,
                             _stream(cache.device)), "tq_retier_pages")
     for (b, h, p), fmt, d, off in zip(pages, new_formats, desc, new_offsets):

@@ -797,9 +797,16 @@ __global__ __launch_bounds__(256) void advance_kernel(int32_t* n_tokens, int n) 
 }
 
 // ------------------------------------------------------------- re-tiering
+// Workgroups of the re-tiering launches (one wave each, striding over the
+// list): eight per CU of MI355X, as many as the packed instance's LDS allows.
+constexpr int kRetierBlocks = 2048;
+
 struct RetierArgs {
   const int64_t* index;
   const uint64_t* new_desc;
+  int n;
+  int sources;        // TQ_RETIER_FROM_* bits of the launched instances
+  int raise_errors;   // this launch raises the error flags
   int32_t* err;
   uint64_t* pages;
   int64_t n_entries;
@@ -825,6 +832,13 @@ __device__ __forceinline__ void unpack_mapped(const uint4* __restrict__ blk, int
     s[4 * i + 2] = w.z;
     s[4 * i + 3] = w.w;
   }
+  // up to 4 bits the map fits one 64-bit word as nibbles: a shift instead of
+  // an LDS read per code
+  uint64_t mw = 0;
+  if constexpr (B <= 4) {
+#pragma clang loop unroll(full)
+    for (int c = 0; c < (1 << B); ++c) mw |= (uint64_t)map[c] << (4 * c);
+  }
 #pragma clang loop unroll(full)
   for (int i = 0; i < D / 16; ++i) {
     uint32_t o[4];
@@ -832,7 +846,11 @@ __device__ __forceinline__ void unpack_mapped(const uint4* __restrict__ blk, int
     for (int k = 0; k < 4; ++k) {
       uint32_t v = 0;
 #pragma clang loop unroll(full)
-      for (int e = 0; e < 4; ++e) v |= (uint32_t)map[bits_at(s, (16 * i + 4 * k + e) * B, B)] << (8 * e);
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t c = bits_at(s, (16 * i + 4 * k + e) * B, B);
+        const uint32_t m = B <= 4 ? (uint32_t)(mw >> (4 * c)) & 15u : (uint32_t)map[c];
+        v |= m << (8 * e);
+      }
       o[k] = v;
     }
     row[i] = make_uint4(o[0], o[1], o[2], o[3]);
@@ -922,14 +940,15 @@ __device__ __forceinline__ int retier_check(const RetierArgs& a, int64_t idx, ui
   return 0;
 }
 
-// One wavefront per listed page; FROM_FP16 selects the pages of one source
-// kind, the other instance handles the rest.  The packed instance runs first
-// and raises the error flags of every listed page (the fp16 instance then
-// finds the same errors on the unchanged descriptors and skips them
-// silently).  A packed page (no QJL) is re-coded stream by stream to narrower
-// widths, keeping its norms; an fp16 page is encoded with the per-token
-// encoder.  Every lane loads the whole of its part of the old page before any
-// lane stores, so the new page may take the old slot.
+// One wavefront per workgroup, striding over the listed pages; FROM_FP16
+// selects the pages of one source kind, the other instance handles the rest.
+// The first instance launched raises the error flags of every listed page
+// (the second finds the same errors on the unchanged descriptors and skips
+// them silently); a page of a source kind the launch leaves out counts as an
+// unsupported change.  A packed page (no QJL) is re-coded stream by stream to
+// narrower widths, keeping its norms; an fp16 page is encoded with the
+// per-token encoder.  Every lane loads the whole of its part of the old page
+// before any lane stores, so the new page may take the old slot.
 template <bool FROM_FP16>
 __global__ __launch_bounds__(64) void retier_kernel(RetierArgs a) {
   __shared__ float lds_thr[FROM_FP16 ? 256 : 1];
@@ -938,19 +957,21 @@ __global__ __launch_bounds__(64) void retier_kernel(RetierArgs a) {
   __shared__ uint8_t lds_map[2][256];
   __shared__ float lds_norm[2][FROM_FP16 ? 1 : PT];
   const int lane = threadIdx.x;
-  const int64_t idx = a.index[blockIdx.x];
+  for (int item = blockIdx.x; item < a.n; item += gridDim.x) {
+  const int64_t idx = a.index[item];
   const bool in_table = idx >= 0 && idx < a.n_entries;
   uint64_t* dp = a.pages + (in_table ? idx : 0);
-  const uint64_t od = in_table ? *dp : 0, nd = a.new_desc[blockIdx.x];
-  const int e = retier_check(a, idx, od, nd);
-  if (e) {
-    if (!FROM_FP16 && lane == 0) raise_flag(a.err, e);
-    return;
-  }
+  const uint64_t od = in_table ? *dp : 0, nd = a.new_desc[item];
+  int e = retier_check(a, idx, od, nd);
   const int kb = (int)((od >> 48) & 15), vb = (int)((od >> 52) & 15);
+  if (!e && !(a.sources & (kb == 0 ? TQ_RETIER_FROM_FP16 : TQ_RETIER_FROM_PACKED))) e = 64;
+  if (e) {
+    if (a.raise_errors && lane == 0) raise_flag(a.err, e);
+    continue;
+  }
   const int nkb = (int)((nd >> 48) & 15), nvb = (int)((nd >> 52) & 15);
   const bool nq = (nd & TQ_PAGE_QJL) != 0;
-  if ((kb == 0) != FROM_FP16) return;
+  if ((kb == 0) != FROM_FP16) continue;
   const char* src = a.pool + (od & TQ_PAGE_OFFSET_MASK);
   char* dst = a.pool + (nd & TQ_PAGE_OFFSET_MASK);
   if constexpr (FROM_FP16) {
@@ -1019,6 +1040,8 @@ __global__ __launch_bounds__(64) void retier_kernel(RetierArgs a) {
     reinterpret_cast<float*>(nv + 1024 * nvb)[lane] = lds_norm[1][lane];
   }
   if (lane == 0) *dp = nd;
+  __syncthreads();   // LDS is reused by the next page
+  }
 }
 
 }  // namespace
@@ -1128,11 +1151,13 @@ int tq_append_kv(const tq_layer* layer, const tq_cache* cache, const tq_token_in
 }
 
 int tq_retier_pages(const tq_layer* layer, const tq_cache* cache, const int64_t* page_index,
-                    const uint64_t* new_desc, int n, int32_t* error_flags, void* stream) {
+                    const uint64_t* new_desc, int n, int sources, int32_t* error_flags, void* stream) {
   int st = check_layer(layer);
   if (st) return st;
   if ((st = check_cache(cache))) return st;
   if (n < 0) return fail(TQ_ERR_INVALID_ARG, "negative page count");
+  if (sources & ~(TQ_RETIER_FROM_PACKED | TQ_RETIER_FROM_FP16))
+    return fail(TQ_ERR_INVALID_ARG, "unknown source bits %#x", sources);
   if (n == 0) return TQ_OK;
   if (!page_index || !new_desc) return fail(TQ_ERR_INVALID_ARG, "null page list");
   if (((uintptr_t)page_index & 7) || ((uintptr_t)new_desc & 7))
@@ -1141,6 +1166,8 @@ int tq_retier_pages(const tq_layer* layer, const tq_cache* cache, const int64_t*
   RetierArgs a;
   a.index = page_index;
   a.new_desc = new_desc;
+  a.n = n;
+  a.sources = sources == 0 ? (TQ_RETIER_FROM_PACKED | TQ_RETIER_FROM_FP16) : sources;
   a.err = error_flags;
   a.pages = const_cast<uint64_t*>(cache->pages);
   a.n_entries = (int64_t)cache->n_sessions * cache->n_kv_heads * cache->max_pages;
@@ -1150,12 +1177,20 @@ int tq_retier_pages(const tq_layer* layer, const tq_cache* cache, const int64_t*
   a.k_table = layer->k_table;
   a.v_table = layer->v_table;
   a.qjl_s = layer->qjl_s;
-  // packed sources first: that instance raises the error flags, and the pages
-  // it re-tiers no longer look like fp16 pages to the second launch
-  hipLaunchKernelGGL(retier_kernel<false>, dim3(n), dim3(64), 0, (hipStream_t)stream, a);
-  if ((st = launch_status("retier packed pages"))) return st;
-  hipLaunchKernelGGL(retier_kernel<true>, dim3(n), dim3(64), 0, (hipStream_t)stream, a);
-  return launch_status("retier fp16 pages");
+  // packed sources first: the pages it re-tiers no longer look like fp16
+  // pages to the second launch.  The first launch raises the error flags.
+  const dim3 grid(std::min(n, kRetierBlocks));
+  a.raise_errors = 1;
+  if (a.sources & TQ_RETIER_FROM_PACKED) {
+    hipLaunchKernelGGL(retier_kernel<false>, grid, dim3(64), 0, (hipStream_t)stream, a);
+    if ((st = launch_status("retier packed pages"))) return st;
+    a.raise_errors = 0;
+  }
+  if (a.sources & TQ_RETIER_FROM_FP16) {
+    hipLaunchKernelGGL(retier_kernel<true>, grid, dim3(64), 0, (hipStream_t)stream, a);
+    st = launch_status("retier fp16 pages");
+  }
+  return st;
 }
 
 }  // extern "C"

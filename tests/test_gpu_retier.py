@@ -158,12 +158,12 @@ def test_retier_pages_parity(dev, kinds):
     t.check()
 
 
-def _raw_retier(cache, layer, idx, descs, flags):
+def _raw_retier(cache, layer, idx, descs, flags, sources=0):
     import kv_cache_vector_srht_amd as tq
     i = torch.tensor(idx, dtype=torch.int64, device=cache.device)
     d = torch.from_numpy(np.array(descs, dtype=np.uint64).view(np.int64)).to(cache.device)
     st = tq.lib().tq_retier_pages(ctypes.byref(layer.struct), ctypes.byref(cache.struct), i.data_ptr(),
-                                  d.data_ptr(), len(idx), flags.data_ptr(), None)
+                                  d.data_ptr(), len(idx), sources, flags.data_ptr(), None)
     tq.check(st, "tq_retier_pages")
     torch.cuda.synchronize()
 
@@ -207,6 +207,13 @@ def test_retier_rejects_unsupported_changes(dev):
         print(f"case {idx} -> flag {want}", flush=True)
         _raw_retier(cache, layer, idx, ds, flags)
         assert int(flags.item()) == want, (idx, int(flags.item()), want)
+        assert np.array_equal(_np(cache.pool), pool0) and np.array_equal(_np(cache.pages), pages0)
+    # a source kind the hint leaves out is refused (page 1 is packed, page 0 fp16)
+    for idx, ds, src in (([1], [desc(1, 2, 2)], 2), ([0], [desc(0, 2, 2)], 1)):
+        pool0, pages0 = _np(cache.pool).copy(), _np(cache.pages).copy()
+        flags.zero_()
+        _raw_retier(cache, layer, idx, ds, flags, sources=src)
+        assert int(flags.item()) == 64
         assert np.array_equal(_np(cache.pool), pool0) and np.array_equal(_np(cache.pages), pages0)
     # a good entry next to a refused one still goes through
     flags.zero_()

@@ -276,10 +276,12 @@ def test_retier_validation(L):
     lay, cac = _fake_layer(), _fake_cache()
     idx, desc = ctypes.c_void_p(0x70000), ctypes.c_void_p(0x71000)
 
-    def call(layer=lay, cache=cac, i=idx, d=desc, n=4, err=None):
+    def call(layer=lay, cache=cac, i=idx, d=desc, n=4, err=None, sources=0):
         return L.tq_retier_pages(ctypes.byref(layer) if layer is not None else None,
-                                 ctypes.byref(cache) if cache is not None else None, i, d, n, err, None)
+                                 ctypes.byref(cache) if cache is not None else None, i, d, n, sources,
+                                 err, None)
     assert call(n=-1) == -1
+    assert call(sources=4) == -1
     assert call(n=0) == 0                      # nothing to do, nothing launched
     assert call(i=None) == -1 and call(d=None) == -1
     assert call(i=ctypes.c_void_p(0x70004)) == -3
