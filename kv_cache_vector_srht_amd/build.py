@@ -23,7 +23,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-SOURCES = ("tq_encode.hip", "tq_decode.hip", "tq_dequant.hip", "tq_host.cpp")
+SOURCES = ("tq_encode.hip", "tq_pages.hip", "tq_decode.hip", "tq_dequant.hip", "tq_host.cpp")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-command-line-argument"]
 

@@ -1,0 +1,191 @@
+// The per-token encoder of libtq's device code (one lane per head vector):
+// rotation, norm, scalar quantisation and packing of one page part, plus the
+// QJL sign sketch of keys ("TurboMOQ", QJL residual correction).  Used by the
+// QJL key encoder, the decode-loop packing of a full tail page and the
+// re-tiering of fp16 pages.
+#ifndef TQ_TOKEN_ENCODER_H_
+#define TQ_TOKEN_ENCODER_H_
+
+#include "tq_device.h"
+
+namespace tq {
+namespace dev {
+
+__device__ __forceinline__ void raise_flag(int32_t* err, int bit) {
+  if (err) atomicOr(err, bit);
+}
+
+// Loads one head vector (128 values) as float.
+__device__ __forceinline__ void load_row(const void* base, int dtype, size_t elem_off, float (&x)[D]) {
+  if (dtype == TQ_DTYPE_F16) {
+    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const __half*>(base) + elem_off);
+#pragma clang loop unroll(full)
+    for (int c = 0; c < D / 8; ++c) {
+      uint4 w = p[c];
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma clang loop unroll(full)
+      for (int e = 0; e < 4; ++e) {
+        __half2 h2 = *reinterpret_cast<const __half2*>(&ww[e]);
+        float2 f = __half22float2(h2);
+        x[8 * c + 2 * e] = f.x;
+        x[8 * c + 2 * e + 1] = f.y;
+      }
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + elem_off);
+#pragma clang loop unroll(full)
+    for (int c = 0; c < D / 4; ++c) {
+      float4 f = p[c];
+      x[4 * c] = f.x;
+      x[4 * c + 1] = f.y;
+      x[4 * c + 2] = f.z;
+      x[4 * c + 3] = f.w;
+    }
+  }
+}
+
+// Walsh-Hadamard transform of each 64-value half (stages 1..32); the last
+// stage (pairs j, j+64) is left to the caller so that it can consume outputs
+// as they are produced.
+__device__ __forceinline__ void fwht_halves(float (&x)[D]) {
+#pragma clang loop unroll(full)
+  for (int h = 1; h < D / 2; h <<= 1) {
+#pragma clang loop unroll(full)
+    for (int i = 0; i < D; i += 2 * h) {
+#pragma clang loop unroll(full)
+      for (int j = i; j < i + h; ++j) {
+        const float a = x[j], b = x[j + h];
+        x[j] = a + b;
+        x[j + h] = a - b;
+      }
+    }
+  }
+}
+
+template <int B>
+__device__ __forceinline__ uint32_t quantize(float u, const float* thr) {
+  uint32_t c = 0;
+#pragma clang loop unroll(full)
+  for (int s = 1 << (B - 1); s >= 1; s >>= 1) c += (u >= thr[c + s - 1]) ? (uint32_t)s : 0u;
+  return c;
+}
+
+// Norm, rotation and quantisation of one vector held by this lane:
+// u = D H D x / ||x||, code_j = #{k : t_k <= u_j} (binary search over the
+// boundaries in LDS).  Codes go to `emit(j, code)`; on return x holds the
+// rotated-domain residual u - c[code] (used by QJL).
+template <int B, class Emit>
+__device__ __forceinline__ float rotate_quantize(float (&x)[D], const uint32_t (&m)[4],
+                                                 const float* thr, const float* cent, Emit emit) {
+  float ss = 0.f;
+#pragma clang loop unroll(full)
+  for (int j = 0; j < D; ++j) ss = fmaf(x[j], x[j], ss);
+  const float n = sqrtf(ss);
+#pragma clang loop unroll(full)
+  for (int j = 0; j < D; ++j) x[j] = flip_if(x[j], dsign(m, j));
+  fwht_halves(x);
+  const float inv = n > 0.f ? 1.0f / n : 0.f;
+#pragma clang loop unroll(full)
+  for (int j = 0; j < D / 2; ++j) {
+    const float a = x[j], b = x[j + D / 2];
+    const float u0 = flip_if(a + b, dsign(m, j)) * inv;
+    const float u1 = flip_if(a - b, dsign(m, j + D / 2)) * inv;
+    const uint32_t c0 = quantize<B>(u0, thr);
+    const uint32_t c1 = quantize<B>(u1, thr);
+    emit(j, c0);
+    emit(j + D / 2, c1);
+    x[j] = u0 - cent[c0];
+    x[j + D / 2] = u1 - cent[c1];
+  }
+  return n;
+}
+
+template <int PART, int B>
+__device__ __forceinline__ void encode_packed(const float* __restrict__ qjl_s, char* page, bool qjl, int lane,
+                              float (&x)[D], const uint32_t (&m)[4], float* lds_thr,
+                              float* lds_cent, uint32_t* lds_rows) {
+  constexpr int kb = B;
+  if constexpr (PART == 0) {
+    uint32_t sw[4 * B];
+#pragma clang loop unroll(full)
+    for (int i = 0; i < 4 * B; ++i) sw[i] = 0;
+    const float n = rotate_quantize<B>(x, m, lds_thr, lds_cent, [&](int j, uint32_t c) {
+      const int pos = j * B, wi = pos >> 5, sh = pos & 31;
+      sw[wi] |= c << sh;
+      if (sh + B > 32) sw[wi + 1] |= c >> (32 - sh);
+    });
+    uint4* dst = reinterpret_cast<uint4*>(page);
+#pragma clang loop unroll(full)
+    for (int w = 0; w < B; ++w)
+      dst[w * 64 + lane] = make_uint4(sw[4 * w], sw[4 * w + 1], sw[4 * w + 2], sw[4 * w + 3]);
+    reinterpret_cast<float*>(page + 1024 * kb)[lane] = n;
+    if (qjl) {
+      // r = x - xhat = (n / d) D H D (u - c): one more butterfly in registers.
+      float e2 = 0.f;
+#pragma clang loop unroll(full)
+      for (int j = 0; j < D; ++j) {
+        e2 = fmaf(x[j], x[j], e2);
+        x[j] = flip_if(x[j], dsign(m, j));
+      }
+      fwht128(x);
+      const float sc = n * (1.0f / D);
+#pragma clang loop unroll(full)
+      for (int j = 0; j < D; ++j) x[j] = flip_if(x[j], dsign(m, j)) * sc;
+      const float gamma = n * sqrtf(e2) * 0.08838834764831845f;  // n ||u - c|| / sqrt(d)
+      uint32_t zw[4];
+#pragma clang loop unroll(full)
+      for (int w = 0; w < 4; ++w) {
+        uint32_t bitsw = 0;
+        for (int ii = 0; ii < 32; ++ii) {
+          const float* srow = qjl_s + (size_t)(32 * w + ii) * D;
+          float p = 0.f;
+#pragma clang loop unroll(full)
+          for (int j = 0; j < D; ++j) p = fmaf(srow[j], x[j], p);
+          bitsw |= (p >= 0.f ? 1u : 0u) << ii;
+        }
+        zw[w] = bitsw;
+      }
+      char* qbase = page + 1024 * kb + 256;
+      reinterpret_cast<uint4*>(qbase)[lane] = make_uint4(zw[0], zw[1], zw[2], zw[3]);
+      reinterpret_cast<float*>(qbase + 1024)[lane] = gamma;
+    }
+  } else {
+    // Codes as bytes into this lane's LDS row, then transpose into V streams.
+    uint32_t cb[D / 4];
+#pragma clang loop unroll(full)
+    for (int i = 0; i < D / 4; ++i) cb[i] = 0;
+    const float n = rotate_quantize<B>(x, m, lds_thr, lds_cent, [&](int j, uint32_t c) {
+      cb[j >> 2] |= c << (8 * (j & 3));
+    });
+    uint4* row = reinterpret_cast<uint4*>(reinterpret_cast<char*>(lds_rows) + lane * kEncodeRowBytes);
+#pragma clang loop unroll(full)
+    for (int i = 0; i < D / 16; ++i) row[i] = make_uint4(cb[4 * i], cb[4 * i + 1], cb[4 * i + 2], cb[4 * i + 3]);
+    __syncthreads();
+    const int q = lane >> 4, ii = lane & 15;
+    uint32_t sw[4 * B];
+#pragma clang loop unroll(full)
+    for (int i = 0; i < 4 * B; ++i) sw[i] = 0;
+#pragma clang loop unroll(full)
+    for (int k = 0; k < 16; ++k) {
+      const uint2 b8 = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(lds_rows) +
+                                                        (4 * k + q) * kEncodeRowBytes + 8 * ii);
+#pragma clang loop unroll(full)
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t c = ((e < 4 ? b8.x : b8.y) >> (8 * (e & 3))) & 0xffu;
+        const int pos = (8 * k + e) * B, wi = pos >> 5, sh = pos & 31;
+        sw[wi] |= c << sh;
+        if (sh + B > 32) sw[wi + 1] |= c >> (32 - sh);
+      }
+    }
+    uint4* dst = reinterpret_cast<uint4*>(page);
+#pragma clang loop unroll(full)
+    for (int w = 0; w < B; ++w)
+      dst[w * 64 + lane] = make_uint4(sw[4 * w], sw[4 * w + 1], sw[4 * w + 2], sw[4 * w + 3]);
+    reinterpret_cast<float*>(page + 1024 * B)[lane] = n;
+  }
+}
+
+}  // namespace dev
+}  // namespace tq
+
+#endif  // TQ_TOKEN_ENCODER_H_
