@@ -54,6 +54,7 @@ STREAM_CODES = 128
 LLOYD_MAX = 0
 UNIFORM = 1
 BETA = 2
+POLAR = 4      # PolarQuant: coordinate pairs as (radius, angle)
 
 
 # ----------------------------------------------------------------------------
@@ -327,6 +328,100 @@ def uniform_step(bits: int) -> float:
     return _UNIFORM_DELTA[bits]
 
 
+# PolarQuant ("TurboQuant-MLX v2.0", How It Works > Pipeline and Architecture
+# Notes; the cache's r_bits / theta_bits, Quick Start): after the rotation each
+# coordinate pair (u_2i, u_2i+1) becomes a radius and an angle, quantised
+# independently, with no per-block constants.  Readings: the pair of a
+# rotated, normalised vector is close to a standard 2-D Gaussian pair, whose
+# radius is Rayleigh(1) and angle uniform; the radius takes the Lloyd-Max
+# quantiser of Rayleigh(1) and the angle the uniform grid of L = 2^b sectors
+# [-pi + 2 pi k / L, -pi + 2 pi (k+1) / L) with level at the sector's middle;
+# r_bits = theta_bits = the page width b, so a polar page has the size and
+# stream layout of a scalar one: stream position 2i holds pair i's radius
+# code, position 2i+1 its angle code.
+def _rayleigh_lloyd_map(c: np.ndarray) -> np.ndarray:
+    """One Lloyd-Max update for Rayleigh(1): cells between midpoints, from 0 to inf."""
+    e = np.concatenate(([0.0], 0.5 * (c[:-1] + c[1:]), [np.inf]))
+    tail = np.exp(-0.5 * e * e)                                       # P(R >= x)
+    mom = np.where(np.isinf(e), 0.0, np.nan_to_num(e) * tail) + math.sqrt(2 * math.pi) * ndtr(-e)
+    return (mom[:-1] - mom[1:]) / (tail[:-1] - tail[1:])
+
+
+@lru_cache(maxsize=None)
+def lloyd_max_rayleigh(bits: int) -> Tuple[np.ndarray, np.ndarray]:
+    """MSE-optimal 2^bits-level quantiser of the Rayleigh(1) radius.
+
+    f(r) = r exp(-r^2/2), P(R >= x) = exp(-x^2/2), and
+    E[R; R >= x] = x exp(-x^2/2) + sqrt(2 pi) Q(x) with Q the Gaussian upper
+    tail.  Lloyd iterations, a float64 root finder, then Newton steps in
+    40-digit arithmetic with the tridiagonal Jacobian of the conditions
+    c_k = E[R | t_k <= R < t_k+1] (t the midpoints; the first cell starts at 0).
+    Returns (levels, boundaries) in float64.
+    """
+    import mpmath as mp
+    L = 1 << bits
+    c = np.sqrt(-2.0 * np.log(1.0 - (np.arange(L) + 0.5) / L))      # equal-probability start
+    for _ in range(300):
+        c = _rayleigh_lloyd_map(c)
+    sol = optimize.root(lambda x: x - _rayleigh_lloyd_map(x), c, method="hybr", tol=1e-15)
+    c = np.sort(sol.x)
+    with mp.workdps(40):
+        dens = lambda x: x * mp.exp(-x * x / 2)
+        tail = lambda x: mp.exp(-x * x / 2)
+        mom = lambda x: x * mp.exp(-x * x / 2) + mp.sqrt(2 * mp.pi) * mp.ncdf(-x)
+        cm = [mp.mpf(float(v)) for v in c]
+        for _ in range(30):
+            a = [mp.mpf(0)] + [(cm[i - 1] + cm[i]) / 2 for i in range(1, L)]
+            ta = [tail(x) for x in a] + [mp.mpf(0)]
+            ma = [mom(x) for x in a] + [mp.mpf(0)]
+            P = [ta[i] - ta[i + 1] for i in range(L)]
+            mean = [(ma[i] - ma[i + 1]) / P[i] for i in range(L)]
+            da = [dens(a[i]) * (mean[i] - a[i]) / P[i] if i > 0 else mp.mpf(0) for i in range(L)]
+            db = [dens(a[i + 1]) * (a[i + 1] - mean[i]) / P[i] if i < L - 1 else mp.mpf(0) for i in range(L)]
+            rhs = [-(cm[i] - mean[i]) for i in range(L)]
+            diag = [1 - da[i] / 2 - db[i] / 2 for i in range(L)]
+            low = [-da[i] / 2 for i in range(L)]
+            up = [-db[i] / 2 for i in range(L)]
+            for i in range(1, L):
+                w = low[i] / diag[i - 1]
+                diag[i] -= w * up[i - 1]
+                rhs[i] -= w * rhs[i - 1]
+            step = [mp.mpf(0)] * L
+            step[L - 1] = rhs[L - 1] / diag[L - 1]
+            for i in range(L - 2, -1, -1):
+                step[i] = (rhs[i] - up[i] * step[i + 1]) / diag[i]
+            cm = [cm[i] + step[i] for i in range(L)]
+            if max(abs(x) for x in step) < mp.mpf(10) ** -34:
+                break
+        tm = [(cm[i] + cm[i + 1]) / 2 for i in range(L - 1)]
+        _F32_TABLES[(bits, POLAR)] = (np.array([_round_f32(x) for x in cm], dtype=np.float32),
+                                      np.array([_round_f32(x) for x in tm], dtype=np.float32))
+        # pair values (r_k cos a_j, r_k sin a_j), a_j the sector middles
+        pair = np.zeros((L, L, 2), dtype=np.float32)
+        for k in range(L):
+            for j in range(L):
+                ang = -mp.pi + (2 * j + 1) * mp.pi / L
+                pair[k, j, 0] = _round_f32(cm[k] * mp.cos(ang))
+                pair[k, j, 1] = _round_f32(cm[k] * mp.sin(ang))
+        _POLAR_PAIRS[bits] = pair
+        return np.array([float(x) for x in cm]), np.array([float(x) for x in tm])
+
+
+_POLAR_PAIRS: Dict[int, np.ndarray] = {}
+
+
+def polar_pairs(bits: int) -> np.ndarray:
+    """[L, L, 2] float32: the reconstructed pair of radius code k, angle code j."""
+    lloyd_max_rayleigh(bits)
+    return _POLAR_PAIRS[bits]
+
+
+def polar_angle_code(theta: np.ndarray, bits: int) -> np.ndarray:
+    """Sector index of angles in [-pi, pi] (pi is the direction of -pi: sector 0)."""
+    L = 1 << bits
+    return np.floor((np.asarray(theta, dtype=np.float64) + math.pi) * L / (2 * math.pi)).astype(np.int64) % L
+
+
 # Codebooks fitted to sample data ("TurboMOQ", Quick Start: calibrate codebooks
 # from sample data; Architecture: Lloyd-Max codebook (k-means)).
 class FittedCodebook:
@@ -392,6 +487,8 @@ def codebook(bits: int, kind: int = LLOYD_MAX) -> Tuple[np.ndarray, np.ndarray]:
         uniform_gaussian(bits)
     elif kind == BETA:
         lloyd_max_sphere(bits)
+    elif kind == POLAR:
+        lloyd_max_rayleigh(bits)
     else:
         raise ValueError(kind)
     return _F32_TABLES[(bits, kind)]
@@ -435,21 +532,45 @@ def encode(X: np.ndarray, signs, bits: int, kind: int = LLOYD_MAX,
     safe = np.where(n > 0, n, 1.0)
     U = np.where(n[:, None] > 0, math.sqrt(d) * Y / safe[:, None], 0.0)
     c32, t32 = codebook(bits, kind)
-    U32 = U.astype(np.float32)
-    # the number of boundaries <= u (t32 is ascending)
-    codes = np.searchsorted(t32, U32, side="right").astype(np.int64)
     t64 = t32.astype(np.float64)
-    below = np.abs(U - t64[np.clip(codes - 1, 0, t64.size - 1)])
-    above = np.abs(U - t64[np.clip(codes, 0, t64.size - 1)])
-    near = np.minimum(below, above) < boundary_eps
+    L = 1 << bits
+    if kind == POLAR:
+        # radius and angle of each coordinate pair; the radius decision in
+        # float32 like the scalar codes, the angle sector from float64 (the
+        # device's float32 angle may differ within ANGLE_EPS of a sector edge)
+        r = np.hypot(U[:, 0::2], U[:, 1::2])
+        th = np.arctan2(U[:, 1::2], U[:, 0::2])
+        rc = np.searchsorted(t32, r.astype(np.float32), side="right").astype(np.int64)
+        near_r = np.minimum(np.abs(r - t64[np.clip(rc - 1, 0, t64.size - 1)]),
+                            np.abs(r - t64[np.clip(rc, 0, t64.size - 1)])) < boundary_eps
+        tc = polar_angle_code(th, bits)
+        edge = (th + math.pi) * L / (2 * math.pi)
+        near_t = np.abs(edge - np.rint(edge)) * (2 * math.pi / L) < ANGLE_EPS
+        codes = np.empty(U.shape, dtype=np.int64)
+        near = np.empty(U.shape, dtype=bool)
+        codes[:, 0::2], codes[:, 1::2] = rc, tc
+        near[:, 0::2], near[:, 1::2] = near_r, near_t
+    else:
+        U32 = U.astype(np.float32)
+        # the number of boundaries <= u (t32 is ascending)
+        codes = np.searchsorted(t32, U32, side="right").astype(np.int64)
+        below = np.abs(U - t64[np.clip(codes - 1, 0, t64.size - 1)])
+        above = np.abs(U - t64[np.clip(codes, 0, t64.size - 1)])
+        near = np.minimum(below, above) < boundary_eps
     if overrides is not None:
         rows, cols, alt = (np.asarray(v, dtype=np.int64) for v in overrides)
         if rows.size:
-            if not np.all(near[rows, cols]) or not np.all(np.abs(alt - codes[rows, cols]) == 1):
+            step = np.abs(alt - codes[rows, cols])
+            if kind == POLAR:   # angle codes are cyclic
+                step = np.where(cols % 2 == 1, np.minimum(step, L - step), step)
+            if not np.all(near[rows, cols]) or not np.all(step == 1):
                 raise ValueError("override outside the boundary allowance")
             codes = codes.copy()
             codes[rows, cols] = alt
     return {"norm": n.astype(np.float32), "u": U, "codes": codes, "near": near}
+
+
+ANGLE_EPS = 1e-5   # radians: the angle-sector allowance of polar codes
 
 
 def dequantize(norm32: np.ndarray, codes: np.ndarray, signs, bits: int,
@@ -458,7 +579,14 @@ def dequantize(norm32: np.ndarray, codes: np.ndarray, signs, bits: int,
     c32, _ = codebook(bits, kind)
     R = rotation_matrix(signs)
     d = R.shape[0]
-    C = c32.astype(np.float64)[codes]
+    codes = np.asarray(codes, dtype=np.int64)
+    if kind == POLAR:
+        P = polar_pairs(bits).astype(np.float64)
+        C = np.empty(codes.shape)
+        C[:, 0::2] = P[codes[:, 0::2], codes[:, 1::2], 0]
+        C[:, 1::2] = P[codes[:, 0::2], codes[:, 1::2], 1]
+    else:
+        C = c32.astype(np.float64)[codes]
     return (np.asarray(norm32, dtype=np.float64)[:, None] / math.sqrt(d)) * (C @ R)
 
 
@@ -657,6 +785,8 @@ def decode_page(raw: bytes, fmt, signs, S=None, k_kind: int = LLOYD_MAX,
 # ----------------------------------------------------------------------------
 def requantize_codes(codes: np.ndarray, bits: int, new_bits: int, kind: int = LLOYD_MAX) -> np.ndarray:
     """Codes of width `bits` mapped to width `new_bits` through their centroids."""
+    if kind == POLAR:
+        raise ValueError("polar pages are not re-coded by a scalar map")
     c_old, _ = codebook(bits, kind)
     _, t_new = codebook(new_bits, kind)
     return np.searchsorted(t_new, c_old[np.asarray(codes, dtype=np.int64)], side="right").astype(np.int64)

@@ -669,3 +669,93 @@ def test_fitted_codebooks_approach_the_laws_they_sample():
     for b in (1, 2, 3):
         assert np.allclose(O.fit_levels(g, b)[0], O.codebook(b, O.LLOYD_MAX)[0], atol=0.005)
         assert np.allclose(O.fit_levels(m, b)[0], O.codebook(b, O.BETA)[0], atol=0.005)
+
+
+# ------------------------------------------------------------- PolarQuant
+def test_rayleigh_radius_codebook_pins():
+    from scipy import integrate
+    f = lambda r: r * math.exp(-r * r / 2)
+    for bits in (1, 2, 3, 4):
+        c, t = O.codebook(bits, O.POLAR)
+        assert np.all(np.diff(c) > 0) and c[0] > 0 and np.allclose(t, (c[:-1] + c[1:]) / 2, rtol=1e-6)
+        edges = np.concatenate(([0.0], t.astype(np.float64), [np.inf]))
+        for k in range(c.size):
+            P = integrate.quad(f, edges[k], edges[k + 1], epsabs=1e-14)[0]
+            M = integrate.quad(lambda r: r * f(r), edges[k], edges[k + 1], epsabs=1e-14)[0]
+            assert abs(M / P - c[k]) < 2e-6 * c[k], (bits, k)
+    # the pair table is radius level times the sector middle's direction
+    for bits in (1, 2, 3):
+        L = 1 << bits
+        c, _ = O.codebook(bits, O.POLAR)
+        P = O.polar_pairs(bits)
+        for j in range(L):
+            a = -math.pi + (2 * j + 1) * math.pi / L
+            assert np.allclose(P[:, j, 0], c * math.cos(a), rtol=1e-6, atol=1e-7)
+            assert np.allclose(P[:, j, 1], c * math.sin(a), rtol=1e-6, atol=1e-7)
+
+
+def _vectors_with_rotated(U, signs):
+    """Rows x with sqrt(d) R x / ||x|| = U for rows U of squared norm d."""
+    return U @ O.rotation_matrix(signs) / math.sqrt(U.shape[1])
+
+
+def test_polar_encode_hand_example():
+    signs = W.rotation_signs(42, 2)
+    r = math.sqrt(2.0)                    # every pair at radius sqrt(2): ||u||^2 = 128
+    th = np.array([0.1, 1.7, -2.0, 3.0, -0.4] + [0.5] * 59)
+    U = np.zeros((1, 128))
+    U[0, 0::2], U[0, 1::2] = r * np.cos(th), r * np.sin(th)
+    X = _vectors_with_rotated(U, signs)
+    e = O.encode(X, signs, 2, O.POLAR)
+    assert np.allclose(e["u"], U, atol=1e-12)
+    # 2 bits: radius boundaries ~ (0.822, 1.420, 2.127): sqrt(2) is level 1;
+    # angle sectors of pi/2 from -pi: 0.1 -> 2, 1.7 -> 3, -2.0 -> 0, 3.0 -> 3, -0.4 -> 1
+    assert np.all(e["codes"][0, 0::2] == 1)
+    assert e["codes"][0, 1::2][:5].tolist() == [2, 3, 0, 3, 1]
+    # reconstruction: the norm times the pair levels, rotated back
+    xh = O.dequantize(e["norm"], e["codes"], signs, 2, O.POLAR)
+    P = O.polar_pairs(2)
+    uh = np.empty(128)
+    uh[0::2] = P[1, e["codes"][0, 1::2], 0]
+    uh[1::2] = P[1, e["codes"][0, 1::2], 1]
+    assert np.allclose(math.sqrt(128) * (xh @ O.rotation_matrix(signs).T) / float(e["norm"][0]), uh, atol=1e-9)
+
+
+def test_polar_angle_wraps_and_flags_sector_edges():
+    assert O.polar_angle_code(np.array([math.pi, -math.pi, 0.0, -1e-12]), 3).tolist() == [0, 0, 4, 3]
+    signs = W.rotation_signs(42, 2)
+    L = 8
+    th = np.array([-math.pi + 2 * math.pi * 3 / L + 1e-7, 0.3] + [0.7] * 62)
+    U = np.zeros((1, 128))
+    U[0, 0::2], U[0, 1::2] = math.sqrt(2) * np.cos(th), math.sqrt(2) * np.sin(th)
+    e = O.encode(_vectors_with_rotated(U, signs), signs, 3, O.POLAR)
+    assert e["near"][0, 1] and not e["near"][0, 3]
+    # a cyclic neighbour is an admissible override at a flagged angle; 2 steps are not
+    O.encode(_vectors_with_rotated(U, signs), signs, 3, O.POLAR, overrides=([0], [1], [2]))
+    with pytest.raises(ValueError):
+        O.encode(_vectors_with_rotated(U, signs), signs, 3, O.POLAR, overrides=([0], [1], [5]))
+
+
+def test_polar_distortion_matches_closed_form():
+    """For Gaussian pairs the mean squared pair error of independent radius
+    (Lloyd-Max) and angle (uniform) quantisers is
+    2 + (1 - 2 sinc(pi/L)) sum_k P_k c_k^2, sinc x = sin x / x (the Lloyd-Max
+    centroid condition gives E[R; cell k] = c_k P_k).  Checked against the
+    oracle's encode and dequantise of vectors whose rotated coordinates are
+    Gaussian up to the normalisation (d = 128, so within a few per cent)."""
+    rng = np.random.default_rng(26)
+    signs = W.rotation_signs(42, 0)
+    R = O.rotation_matrix(signs)
+    X = rng.standard_normal((3000, 128))
+    for bits in (2, 3, 4):
+        L = 1 << bits
+        c, t = O.codebook(bits, O.POLAR)
+        e = np.concatenate(([0.0], t.astype(np.float64), [np.inf]))
+        Pk = np.exp(-0.5 * e[:-1] ** 2) - np.exp(-0.5 * np.where(np.isinf(e[1:]), np.inf, e[1:]) ** 2)
+        x = math.pi / L
+        D = 2 + (1 - 2 * math.sin(x) / x) * np.sum(Pk * c.astype(np.float64) ** 2)
+        enc = O.encode(X, signs, bits, O.POLAR)
+        xh = O.dequantize(enc["norm"], enc["codes"], signs, bits, O.POLAR)
+        uh = math.sqrt(128) * (xh @ R.T) / enc["norm"][:, None].astype(np.float64)
+        mse_pair = np.mean(np.sum((enc["u"] - uh) ** 2, axis=1)) / 64
+        assert abs(mse_pair / D - 1) < 0.03, (bits, mse_pair, D)
