@@ -66,7 +66,8 @@ enum {
 };
 
 enum { TQ_CODEBOOK_LLOYD_MAX = 0, TQ_CODEBOOK_UNIFORM = 1, TQ_CODEBOOK_BETA = 2,
-       TQ_CODEBOOK_FITTED = 3 /* a table from tq_calibrated_table */ };
+       TQ_CODEBOOK_FITTED = 3 /* a table from tq_calibrated_table */,
+       TQ_CODEBOOK_POLAR = 4 /* PolarQuant, see tq_build_codebook */ };
 enum { TQ_DTYPE_F32 = 0, TQ_DTYPE_F16 = 1 };
 enum { TQ_QJL_SCORE_UNBIASED = 0, TQ_QJL_SCORE_SIGN = 1 };
 
@@ -74,7 +75,7 @@ enum { TQ_QJL_SCORE_UNBIASED = 0, TQ_QJL_SCORE_SIGN = 1 };
 #define TQ_PAGE_TOKENS 64
 #define TQ_JL_DIM 128
 /* floats in one codebook table (all bit widths of one kind), see tq_codebook_table */
-#define TQ_CODEBOOK_TABLE_FLOATS 8192
+#define TQ_CODEBOOK_TABLE_FLOATS 12288
 
 /* ------------------------------------------------------- page descriptors
  * A cache is a caller-owned byte pool plus a page table of uint64
@@ -223,7 +224,17 @@ typedef struct tq_query {
  *   proportional to (1 - u^2/128)^(125/2); u^2/128 ~ Beta(1/2, 127/2)), the
  *   exact law of a rotated, normalised coordinate when the direction is random
  *   ("TurboMOQ", Head-to-Head Comparison and Project Structure: Beta-CDF,
- *   Beta-distribution codebooks).
+ *   Beta-distribution codebooks);
+ * kind = TQ_CODEBOOK_POLAR: PolarQuant ("TurboQuant-MLX v2.0", How It Works >
+ *   Pipeline: each rotated coordinate pair as a radius and an angle, quantised
+ *   independently).  A part coded at width b holds, for pair i, the radius code
+ *   at stream position 2i and the angle code at 2i+1, so a polar page has the
+ *   scalar layout and size.  This call gives the radius quantiser: the 2^bits
+ *   Lloyd-Max levels of Rayleigh(1) (the radius of a standard 2-D Gaussian
+ *   pair) and their midpoints.  The angle theta = atan2(u_2i+1, u_2i) takes
+ *   sector floor((theta + pi) 2^bits / (2 pi)) mod 2^bits, reconstructed at the
+ *   sector's middle.  Widths 1..4 only (pages of a polar part wider than 4
+ *   bits are refused by the kernels).
  * Writes 2^bits ascending centroids and 2^bits - 1 boundaries (caller-owned
  * host arrays), each the float32 nearest the exact value.  Pure, deterministic
  * and thread-safe; bits in 1..8. */
@@ -232,7 +243,11 @@ int tq_build_codebook(int bits, int kind, float* centroids, float* boundaries);
 /* The table kernels read, for every bits = 1..8: the centroids at float offset
  * 2^bits - 2 and the boundaries at 510 + 2^bits - bits - 1; then, for the
  * encoder, a lookup grid per width (header {S, O, n_bins, offset} at
- * 1024 + 4 (bits - 1); n_bins entries {count of boundaries below the bin
+ * 1024 + 4 (bits - 1); pair tables of widths 1..4 at float offset 1056 (width
+ * b at float2 entry 0, 4, 20, 84 for b = 1, 2, 3, 4; entry lo | hi << b holds
+ * the two values of a coordinate pair coded (lo, hi): (c[lo], c[hi]) for a
+ * scalar codebook, radius level lo in sector hi's middle direction for
+ * PolarQuant); the grids' n_bins entries {count of boundaries below the bin
  * (u32), the one boundary inside the bin widened by a quarter bin each side
  * (f32, or 3e38)} at `offset`), so that code(u) = count + [u >= boundary] at
  * bin floor(u S + O) clamped to [0, n_bins); a grid of n_bins = 256 is instead

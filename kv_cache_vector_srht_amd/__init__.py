@@ -18,11 +18,12 @@ from typing import List, Optional, Sequence, Tuple
 HEAD_DIM = 128
 PAGE_TOKENS = 64
 JL_DIM = 128
-CODEBOOK_TABLE_FLOATS = 8192
+CODEBOOK_TABLE_FLOATS = 12288
 LLOYD_MAX = 0
 UNIFORM = 1
 BETA = 2
 FITTED = 3
+POLAR = 4
 DTYPE_F32 = 0
 DTYPE_F16 = 1
 QJL_SCORE_UNBIASED = 0

@@ -25,6 +25,7 @@ struct DecodeArgs {
   int n_q_heads, group;
   float scale2;  // softmax scale * log2(e)
   int qjl_sign;  // TQ_QJL_SCORE_SIGN: the query side of the QJL term is sign(S q)
+  int k_polar, v_polar;   // PolarQuant parts: pages wider than 4 bits are skipped
   const int32_t* n_tokens;
   int n_sessions, n_kv_heads, max_pages;
   const char* pool;
@@ -84,6 +85,7 @@ __global__ __launch_bounds__(128) void qprep_kernel(DecodeArgs a) {
       // sign agreement scaled by pi/2 ||q|| / m (every thread sums the same
       // squares in the same order)
       float qq = 0.f;
+#pragma clang loop unroll(disable)
       for (int i = 0; i < D; ++i) qq = fmaf(qs[i], qs[i], qq);
       w[2 * D * G + slot] = (p >= 0.f ? 1.f : -1.f) * sqrtf(qq) * (a.scale2 * kHalfPi / TQ_JL_DIM);
     } else {
@@ -524,19 +526,21 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
     sm.vcent[i] = a.v_table[i];
   }
   __syncthreads();
+  // pair tables come with the codebook table (a scalar codebook's (c[lo],
+  // c[hi]), or PolarQuant's radius-angle pairs); a quad entry is two pairs
+  const float2* kpt = reinterpret_cast<const float2*>(a.k_table + kPairOffset);
+  const float2* vpt = reinterpret_cast<const float2*>(a.v_table + kPairOffset);
   for (int i = tid; i < 340; i += blockDim.x) {
-    const int bb = i < 4 ? 1 : i < 20 ? 2 : i < 84 ? 3 : 4;
-    const int idx = i - pair_offset(bb), L = 1 << bb;
-    const int lo = idx & (L - 1), hi = idx >> bb;
-    sm.kpair[i] = make_float2(sm.kcent[centroid_offset(bb) + lo], sm.kcent[centroid_offset(bb) + hi]);
-    sm.vpair[i] = make_float2(sm.vcent[centroid_offset(bb) + lo], sm.vcent[centroid_offset(bb) + hi]);
+    sm.kpair[i] = kpt[i];
+    sm.vpair[i] = vpt[i];
   }
   for (int i = tid; i < 272; i += blockDim.x) {
     const int bb = i < 16 ? 1 : 2;
-    const int idx = i - quad_offset(bb), msk = (1 << bb) - 1, c0 = centroid_offset(bb);
-    const int q0 = idx & msk, q1 = (idx >> bb) & msk, q2 = (idx >> (2 * bb)) & msk, q3 = idx >> (3 * bb);
-    sm.kquad[i] = make_float4(sm.kcent[c0 + q0], sm.kcent[c0 + q1], sm.kcent[c0 + q2], sm.kcent[c0 + q3]);
-    sm.vquad[i] = make_float4(sm.vcent[c0 + q0], sm.vcent[c0 + q1], sm.vcent[c0 + q2], sm.vcent[c0 + q3]);
+    const int idx = i - quad_offset(bb), sh = 2 * bb, po = pair_offset(bb);
+    const int p0 = po + (idx & ((1 << sh) - 1)), p1 = po + (idx >> sh);
+    const float2 k0 = kpt[p0], k1 = kpt[p1], v0 = vpt[p0], v1 = vpt[p1];
+    sm.kquad[i] = make_float4(k0.x, k0.y, k1.x, k1.y);
+    sm.vquad[i] = make_float4(v0.x, v0.y, v1.x, v1.y);
   }
   __syncthreads();
   // keep the scheduler from moving table work into the page loop (it otherwise
@@ -565,6 +569,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
     if (kb == 0 ? (vb != 0 || qjl) : (kb > 8 || vb < 1 || vb > 8)) continue;
     if (qjl && a.qjl_s == nullptr) continue;
     if (page_class(kb, vb, qjl) != CLASS) continue;
+    if (CLASS != 0 && ((a.k_polar && kb > 4) || (a.v_polar && vb > 4))) continue;   // no polar pair table
     const char* page = a.pool + off;
     const int valid = min(PT, ntok - p * PT);
     float s[G], alpha[G];
@@ -918,6 +923,8 @@ int decode_impl(const tq_layer* layer, const tq_cache* cache, const tq_query* qu
   const float scale = query->softmax_scale > 0.f ? query->softmax_scale : 0.08838834764831845f;
   a.scale2 = scale * kLog2e;
   a.qjl_sign = query->qjl_scoring == TQ_QJL_SCORE_SIGN;
+  a.k_polar = layer->k_codebook == TQ_CODEBOOK_POLAR;
+  a.v_polar = layer->v_codebook == TQ_CODEBOOK_POLAR;
   a.n_tokens = cache->n_tokens;
   a.n_sessions = cache->n_sessions;
   a.n_kv_heads = cache->n_kv_heads;

@@ -17,6 +17,7 @@ struct DequantArgs {
   const float* table;
   const float* qjl_s;
   int which, add_qjl, tok0, ntok, page0;
+  int polar;   // the part is PolarQuant-coded: code pairs (radius, angle)
   float* out;
 };
 
@@ -32,6 +33,7 @@ __device__ __forceinline__ uint32_t stream_code(const uint32_t* blk, int b, int 
 __global__ __launch_bounds__(64) void dequant_kernel(DequantArgs a, const float* __restrict__ qjl_s) {
   __shared__ uint32_t blk[2048];  // up to an 8-bit block (8 KB)
   __shared__ float cent[256];
+  __shared__ float2 pair[256];
   const int lane = threadIdx.x;
   const int pg = a.page0 + blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const uint64_t desc = a.pages[((size_t)b * a.n_kv_heads + h) * a.max_pages + pg];
@@ -43,7 +45,8 @@ __global__ __launch_bounds__(64) void dequant_kernel(DequantArgs a, const float*
   const bool qjl = pd.qjl;
   const uint64_t off = pd.off;
   const bool bad = !pd.present || off + page_size_dev(kb, vb, qjl) > a.pool_bytes ||
-                   (kb == 0 && (vb != 0 || qjl)) || kb > 8 || (kb > 0 && (vb < 1 || vb > 8));
+                   (kb == 0 && (vb != 0 || qjl)) || kb > 8 || (kb > 0 && (vb < 1 || vb > 8)) ||
+                   (a.polar && (a.which == 0 ? kb : vb) > 4);
   if (bad) {
     if (in_range)
       for (int j = 0; j < D; ++j) dst[j] = __builtin_nanf("");
@@ -61,18 +64,32 @@ __global__ __launch_bounds__(64) void dequant_kernel(DequantArgs a, const float*
   const float norm = reinterpret_cast<const float*>(blk_src + 1024 * B)[lane];
   for (int i = lane; i < 256 * B; i += 64) blk[i] = reinterpret_cast<const uint32_t*>(blk_src)[i];
   for (int i = lane; i < (1 << B); i += 64) cent[i] = a.table[centroid_offset(B) + i];
+  if (a.polar) {
+    const float2* pt = reinterpret_cast<const float2*>(a.table + kPairOffset) + pair_offset_host(B);
+    for (int i = lane; i < (1 << (2 * B)); i += 64) pair[i] = pt[i];
+  }
   __syncthreads();
   if (!in_range) return;
   uint32_t m[4];
   for (int w = 0; w < 4; ++w) m[w] = a.sign_mask[w];
   float x[D];
-  if (a.which == 0) {
-#pragma clang loop unroll(full)
-    for (int j = 0; j < D; ++j) x[j] = cent[stream_code(blk, B, lane, j)];
-  } else {
+  // code of coordinate j of this lane's token
+  auto code_of = [&](int j) {
+    if (a.which == 0) return stream_code(blk, B, lane, j);
     const int q = lane & 3, k = lane >> 2;
+    return stream_code(blk, B, 16 * q + (j >> 3), 8 * k + (j & 7));
+  };
+  if (a.polar) {
+    // pair i: radius code at coordinate 2i, angle code at 2i + 1
 #pragma clang loop unroll(full)
-    for (int j = 0; j < D; ++j) x[j] = cent[stream_code(blk, B, 16 * q + (j >> 3), 8 * k + (j & 7))];
+    for (int i = 0; i < D / 2; ++i) {
+      const float2 v = pair[code_of(2 * i) | (code_of(2 * i + 1) << B)];
+      x[2 * i] = v.x;
+      x[2 * i + 1] = v.y;
+    }
+  } else {
+#pragma clang loop unroll(full)
+    for (int j = 0; j < D; ++j) x[j] = cent[code_of(j)];
   }
   // xhat = (n / sqrt(d)) R c = (n / d) D H D c
 #pragma clang loop unroll(full)
@@ -133,6 +150,7 @@ int tq_dequantize(const tq_layer* layer, const tq_cache* cache, int which, int a
   a.tok0 = tok0;
   a.ntok = ntok;
   a.page0 = tok0 / TQ_PAGE_TOKENS;
+  a.polar = (which == 0 ? layer->k_codebook : layer->v_codebook) == TQ_CODEBOOK_POLAR;
   a.out = out;
   const int last_page = (tok0 + ntok - 1) / TQ_PAGE_TOKENS;
   dim3 grid(last_page - a.page0 + 1, cache->n_kv_heads, cache->n_sessions);

@@ -30,6 +30,7 @@ struct EncodeArgs {
   const float* k_table;
   const float* v_table;
   const float* qjl_s;
+  int k_polar, v_polar;   // PolarQuant parts: coded by encode_kernel, not encode_pages_kernel
 };
 
 // One wavefront per (page, KV head, session); PART 0 encodes keys, 1 values.
@@ -38,6 +39,7 @@ __global__ __launch_bounds__(64) void encode_kernel(EncodeArgs a, const uint64_t
                                                     const float* __restrict__ qjl_s) {
   __shared__ float lds_thr[256];
   __shared__ float lds_cent[256];
+  __shared__ float2 lds_pair[256];
   __shared__ uint32_t lds_rows[PT * kEncodeRowBytes / 4];
   const int lane = threadIdx.x;
   const int pg = a.page0 + blockIdx.x;
@@ -64,27 +66,7 @@ __global__ __launch_bounds__(64) void encode_kernel(EncodeArgs a, const uint64_t
   const void* src = part == 0 ? a.k : a.v;
   const size_t base = (size_t)b * a.sb + (size_t)h * a.sh;
 
-  if (kb == 0) {
-    // fp16 page: copy the covered rows of this part, 4 rows per pass.
-    __half* dst = reinterpret_cast<__half*>(page + part * PT * D * 2);
-    const int r = lane >> 4, c8 = (lane & 15) * 8;
-    for (int t = lo + r; t < hi; t += 4) {
-      const size_t e = base + (size_t)(t - a.tok0) * a.st + c8;
-      uint4 out;
-      if (a.dtype == TQ_DTYPE_F16) {
-        out = *reinterpret_cast<const uint4*>(reinterpret_cast<const __half*>(src) + e);
-      } else {
-        const float4 f0 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(src) + e);
-        const float4 f1 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(src) + e + 4);
-        __half2 h0 = __floats2half2_rn(f0.x, f0.y), h1 = __floats2half2_rn(f0.z, f0.w);
-        __half2 h2 = __floats2half2_rn(f1.x, f1.y), h3 = __floats2half2_rn(f1.z, f1.w);
-        out = make_uint4(*reinterpret_cast<uint32_t*>(&h0), *reinterpret_cast<uint32_t*>(&h1),
-                         *reinterpret_cast<uint32_t*>(&h2), *reinterpret_cast<uint32_t*>(&h3));
-      }
-      *reinterpret_cast<uint4*>(dst + (size_t)(t - t_first) * D + c8) = out;
-    }
-    return;
-  }
+  if (kb == 0) return;   // fp16 pages are copied by encode_pages_kernel
   if (lo != t_first || hi != t_first + PT) {
     if (lane == 0) raise_flag(a.err, 1);
     return;
@@ -93,13 +75,23 @@ __global__ __launch_bounds__(64) void encode_kernel(EncodeArgs a, const uint64_t
     if (lane == 0) raise_flag(a.err, 8);
     return;
   }
-  if (part == 0 && !qjl) return;   // non-QJL key pages are written by encode_pages_kernel
+  const bool polar = part == 0 ? a.k_polar : a.v_polar;
+  // scalar parts without a QJL sketch are written by encode_pages_kernel
+  if (!polar && (part == 1 || !qjl)) return;
   const int B = part == 0 ? kb : vb;
+  if (polar && B > 4) {
+    if (lane == 0) raise_flag(a.err, 4);
+    return;
+  }
   const float* table = part == 0 ? a.k_table : a.v_table;
   const int L = 1 << B;
   for (int i = lane; i < L; i += 64) {
     lds_cent[i] = table[centroid_offset(B) + i];
     if (i < L - 1) lds_thr[i] = table[boundary_offset(B) + i];
+  }
+  if (polar) {
+    const float2* pt = reinterpret_cast<const float2*>(table + kPairOffset) + pair_offset_host(B);
+    for (int i = lane; i < L * L; i += 64) lds_pair[i] = pt[i];
   }
   uint32_t m[4];
 #pragma clang loop unroll(full)
@@ -109,10 +101,10 @@ __global__ __launch_bounds__(64) void encode_kernel(EncodeArgs a, const uint64_t
   __syncthreads();
   char* part_base = part == 0 ? page : page + 1024 * kb + 256 + (qjl ? 1280 : 0);
   switch (B) {
-    case 1: encode_packed<PART, 1>(qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-    case 2: encode_packed<PART, 2>(qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-    case 3: encode_packed<PART, 3>(qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-    case 4: encode_packed<PART, 4>(qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+    case 1: encode_packed<PART, 1>(qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+    case 2: encode_packed<PART, 2>(qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+    case 3: encode_packed<PART, 3>(qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+    case 4: encode_packed<PART, 4>(qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
     case 5: encode_packed<PART, 5>(qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
     case 6: encode_packed<PART, 6>(qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
     case 7: encode_packed<PART, 7>(qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
@@ -458,9 +450,10 @@ __global__ __launch_bounds__(kEncodeBlock) void encode_pages_kernel(EncodeArgs a
     const size_t row_off = base + (size_t)(t_first + t - a.tok0) * a.st;
     uint32_t* rowk = matk + t * (kRowStride / 4);
     uint32_t* rowv = matv + t * (kRowStride / 4);
-    // QJL key pages are written by the per-token kernel (codes + sketch)
-    const float nk = qjl ? 0.f : encode_quarter<DT>(a.k, row_off, e, el, kb, lk, entk, rowk);
-    const float nv = encode_quarter<DT>(a.v, row_off, e, el, vb, lv, entv, rowv);
+    // QJL key pages and PolarQuant parts are written by the per-token kernel
+    const bool skip_k = qjl || a.k_polar, skip_v = a.v_polar;
+    const float nk = skip_k ? 0.f : encode_quarter<DT>(a.k, row_off, e, el, kb, lk, entk, rowk);
+    const float nv = skip_v ? 0.f : encode_quarter<DT>(a.v, row_off, e, el, vb, lv, entv, rowv);
     if (e == 0) {
       normk[t] = nk;
       normv[t] = nv;
@@ -469,7 +462,7 @@ __global__ __launch_bounds__(kEncodeBlock) void encode_pages_kernel(EncodeArgs a
     // pack: lane (stream s, part e) writes dwords [e*B, e*B+B) of stream s
     char* vblk = page + 1024 * kb + 256 + (qjl ? 1280 : 0);
     const int s = t;
-    if (!qjl) {
+    if (!skip_k) {
       // K stream s = token s: codes 32e..32e+31 are bytes 32e.. of row s
       const char* r = reinterpret_cast<const char*>(matk + s * (kRowStride / 4)) + 32 * e;
       const uint4 c0 = *reinterpret_cast<const uint4*>(r);
@@ -477,7 +470,7 @@ __global__ __launch_bounds__(kEncodeBlock) void encode_pages_kernel(EncodeArgs a
       const uint32_t c8[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
       store_stream_part(kb, page, s, e, c8);
     }
-    {
+    if (!skip_v) {
       // V stream s = 16q + i: positions 8k + j (k = 4e..4e+3) = token 4k+q, coordinate 8i+j
       const int q = s >> 4, i = s & 15;
       uint32_t c8[8];
@@ -491,8 +484,8 @@ __global__ __launch_bounds__(kEncodeBlock) void encode_pages_kernel(EncodeArgs a
       store_stream_part(vb, vblk, s, e, c8);
     }
     if (e == 0) {
-      if (!qjl) reinterpret_cast<float*>(page + 1024 * kb)[s] = normk[s];
-      reinterpret_cast<float*>(vblk + 1024 * vb)[s] = normv[s];
+      if (!skip_k) reinterpret_cast<float*>(page + 1024 * kb)[s] = normk[s];
+      if (!skip_v) reinterpret_cast<float*>(vblk + 1024 * vb)[s] = normv[s];
     }
     __syncthreads();
   }
@@ -546,6 +539,8 @@ int tq_encode_kv(const tq_layer* layer, const tq_cache* cache, const tq_kv_input
   a.k_table = layer->k_table;
   a.v_table = layer->v_table;
   a.qjl_s = layer->qjl_s;
+  a.k_polar = layer->k_codebook == TQ_CODEBOOK_POLAR;
+  a.v_polar = layer->v_codebook == TQ_CODEBOOK_POLAR;
   const int last_page = (in->tok0 + in->ntok - 1) / TQ_PAGE_TOKENS;
   const int n_pages = last_page - a.page0 + 1;
   dim3 grid((n_pages + kEncodePagesPerBlock - 1) / kEncodePagesPerBlock, cache->n_kv_heads,
@@ -558,12 +553,18 @@ int tq_encode_kv(const tq_layer* layer, const tq_cache* cache, const tq_kv_input
                        (hipStream_t)stream, a, cache->pages);
   int st2 = launch_status("encode");
   if (st2) return st2;
-  if (layer->qjl_s) {
-    // keys of QJL pages: codes, norm and sign sketch, one wavefront per page
-    dim3 qgrid(n_pages, cache->n_kv_heads, cache->n_sessions);
+  dim3 qgrid(n_pages, cache->n_kv_heads, cache->n_sessions);
+  if (layer->qjl_s || a.k_polar) {
+    // keys of QJL pages (codes, norm and sign sketch) and PolarQuant keys,
+    // one wavefront per page
     hipLaunchKernelGGL(encode_kernel<0>, qgrid, dim3(64), 0, (hipStream_t)stream, a, cache->pages,
                        layer->qjl_s);
-    st2 = launch_status("encode QJL keys");
+    if ((st2 = launch_status("encode QJL or polar keys"))) return st2;
+  }
+  if (a.v_polar) {
+    hipLaunchKernelGGL(encode_kernel<1>, qgrid, dim3(64), 0, (hipStream_t)stream, a, cache->pages,
+                       layer->qjl_s);
+    st2 = launch_status("encode polar values");
   }
   return st2;
 }

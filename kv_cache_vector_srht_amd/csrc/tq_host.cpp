@@ -106,6 +106,18 @@ struct SphereModel {
   }
 };
 
+// The Rayleigh(1) law of the radius of a standard 2-D Gaussian pair:
+// f(r) = r exp(-r^2/2), P(R >= x) = exp(-x^2/2),
+// E[R; R >= x] = x exp(-x^2/2) + sqrt(2 pi) P(Z >= x).
+struct RayleighModel {
+  ld end() const { return INFINITY; }
+  ld density(ld x) const { return isinf(x) ? 0.0L : x * expl(-0.5L * x * x); }
+  ld tail(ld x) const { return isinf(x) ? 0.0L : expl(-0.5L * x * x); }
+  ld moment(ld x) const {
+    return isinf(x) ? 0.0L : x * expl(-0.5L * x * x) + 2.50662827463100050241576528481104525L * upper(x);
+  }
+};
+
 // Lloyd-Max quantiser of a symmetric density with L = 2^bits levels.  By
 // symmetry only the positive centroids c[0..h-1] (h = L/2) are unknowns; cell i
 // of the positive half is [a_i, b_i) with a_0 = 0, a_i = (c[i-1] + c[i]) / 2,
@@ -259,6 +271,11 @@ int tq_build_codebook(int bits, int kind, float* centroids, float* boundaries) {
   } else if (kind == TQ_CODEBOOK_UNIFORM) {
     ld delta = uniform_step(bits);
     for (int k = 0; k < L; ++k) c[k] = ((ld)k - 0.5L * (ld)(L - 1)) * delta;
+  } else if (kind == TQ_CODEBOOK_POLAR) {
+    // the positive-half solver with 2^bits cells from 0 is the one-sided one
+    std::vector<ld> cpos;
+    lloyd_max(bits + 1, RayleighModel(), cpos);
+    for (int k = 0; k < L; ++k) c[k] = cpos[k];
   } else {
     return fail(TQ_ERR_INVALID_ARG, "unknown codebook kind %d", kind);
   }
@@ -271,12 +288,45 @@ int tq_build_codebook(int bits, int kind, float* centroids, float* boundaries) {
 
 namespace tq {
 
+// Pair section of a table (widths 1..4): entry lo | hi << b of width b holds
+// the values of a coordinate pair whose codes are lo (first coordinate) and hi
+// (second).  A scalar codebook's pair is (c[lo], c[hi]).
+static void build_scalar_pairs(float* table) {
+  for (int b = 1; b <= 4; ++b) {
+    const int L = 1 << b;
+    const float* c = table + centroid_offset(b);
+    float* p = table + kPairOffset + 2 * pair_offset_host(b);
+    for (int i = 0; i < L * L; ++i) {
+      p[2 * i] = c[i & (L - 1)];
+      p[2 * i + 1] = c[i >> b];
+    }
+  }
+}
+
+// PolarQuant's pair: radius level lo (the table's centroids) in the direction
+// of angle sector hi's middle, -pi + (2 hi + 1) pi / L.  The levels are solved
+// again in long double for the products.
+static void build_polar_pairs(float* table) {
+  const ld pi = 3.14159265358979323846264338327950288L;
+  for (int b = 1; b <= 4; ++b) {
+    const int L = 1 << b;
+    std::vector<ld> r;
+    lloyd_max(b + 1, RayleighModel(), r);
+    float* p = table + kPairOffset + 2 * pair_offset_host(b);
+    for (int i = 0; i < L * L; ++i) {
+      const ld a = -pi + (ld)(2 * (i >> b) + 1) * pi / (ld)L;
+      p[2 * i] = (float)(r[i & (L - 1)] * cosl(a));
+      p[2 * i + 1] = (float)(r[i & (L - 1)] * sinl(a));
+    }
+  }
+}
+
 // The encoder's lookup grids of a table whose centroids and boundaries are in
 // place (layout in tq_codebook_table's description).
-static int build_grids(float* table) {
+static int build_grids(float* table, int max_bits = 8) {
   uint32_t* words = reinterpret_cast<uint32_t*>(table);
   int next = kLutEntriesOffset;
-  for (int b = 1; b <= 8; ++b) {
+  for (int b = 1; b <= max_bits; ++b) {
     float* t = table + boundary_offset(b);
     // Quantiser lookup grid: bins of width h over [-T, T) with
     // idx = floor(u * S + O), S = 1/h, O = T/h.  Bin i, widened by h/4 on each
@@ -296,6 +346,8 @@ static int build_grids(float* table) {
     int nb = (int)ceil(2.0 * T / h) + 1;
     const bool byte_grid = nb <= kLutByteBins;
     if (byte_grid) nb = kLutByteBins;
+    if (nb > kLutMaxBins)   // the encoder stages at most this many bins in LDS
+      return fail(TQ_ERR_UNSUPPORTED, "boundaries of width %d too close for the lookup grid", b);
     if (next + 2 * nb > TQ_CODEBOOK_TABLE_FLOATS)
       return fail(TQ_ERR_UNSUPPORTED, "codebook lookup grid does not fit the table");
     float* hdr = table + kLutHeaderOffset + 4 * (b - 1);
@@ -402,6 +454,13 @@ int tq_codebook_table(int kind, float* table) {
     int st = tq_build_codebook(b, kind, table + centroid_offset(b), table + boundary_offset(b));
     if (st != TQ_OK) return st;
   }
+  if (kind == TQ_CODEBOOK_POLAR) {
+    // polar parts are at most 4 bits wide; their radius grids serve nothing
+    // wider
+    build_polar_pairs(table);
+    return build_grids(table, 4);
+  }
+  build_scalar_pairs(table);
   return build_grids(table);
 }
 
@@ -429,6 +488,7 @@ int tq_calibrated_table(const float* vectors, size_t n, const int8_t* signs, flo
     int st = fit_levels(u, b, table + centroid_offset(b), table + boundary_offset(b));
     if (st != TQ_OK) return st;
   }
+  build_scalar_pairs(table);
   return build_grids(table);
 }
 
@@ -529,9 +589,9 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 int check_layer(const tq_layer* L) {
   if (!L) return fail(TQ_ERR_INVALID_ARG, "null layer descriptor");
   if (L->head_dim != TQ_HEAD_DIM) return fail(TQ_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", L->head_dim);
-  if (L->k_codebook < TQ_CODEBOOK_LLOYD_MAX || L->k_codebook > TQ_CODEBOOK_FITTED)
+  if (L->k_codebook < TQ_CODEBOOK_LLOYD_MAX || L->k_codebook > TQ_CODEBOOK_POLAR)
     return fail(TQ_ERR_INVALID_ARG, "unknown k_codebook %d", L->k_codebook);
-  if (L->v_codebook < TQ_CODEBOOK_LLOYD_MAX || L->v_codebook > TQ_CODEBOOK_FITTED)
+  if (L->v_codebook < TQ_CODEBOOK_LLOYD_MAX || L->v_codebook > TQ_CODEBOOK_POLAR)
     return fail(TQ_ERR_INVALID_ARG, "unknown v_codebook %d", L->v_codebook);
   if (!L->sign_mask || !L->k_table || !L->v_table) return fail(TQ_ERR_INVALID_ARG, "null layer table");
   if (!aligned16(L->sign_mask) || !aligned16(L->k_table) || !aligned16(L->v_table))

@@ -19,7 +19,11 @@ constexpr int boundary_offset(int bits) { return 510 + (1 << bits) - bits - 1; }
 // Quantiser lookup grids: per bit width a header {S, O, n_bins, entry offset}
 // at kLutHeaderOffset + 4 (bits - 1); entries {base (u32), boundary (f32)}.
 constexpr int kLutHeaderOffset = 1024;
-constexpr int kLutEntriesOffset = 1056;
+// Pair tables of widths 1..4 (float2 entries; width b starts at entry
+// pair_offset_host(b) = 0, 4, 20, 84), then the lookup grids' entries.
+constexpr int kPairOffset = 1056;
+constexpr int pair_offset_host(int b) { return b == 1 ? 0 : b == 2 ? 4 : b == 3 ? 20 : 84; }
+constexpr int kLutEntriesOffset = kPairOffset + 2 * 340;
 constexpr int kLutMaxBins = 1400;
 constexpr int kLutByteBins = 256;   // grids this small are indexed by a saturating byte conversion
 

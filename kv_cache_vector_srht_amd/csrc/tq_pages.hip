@@ -17,6 +17,7 @@ namespace {
 
 // ------------------------------------------------------- decode-loop append
 struct AppendArgs {
+  int k_polar, v_polar;   // PolarQuant parts (at most 4 bits wide)
   const void* k;
   const void* v;
   int dtype;
@@ -41,6 +42,7 @@ struct AppendArgs {
 __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
   __shared__ float lds_thr[256];
   __shared__ float lds_cent[256];
+  __shared__ float2 lds_pair[256];
   __shared__ uint32_t lds_rows[PT * kEncodeRowBytes / 4];
   const int lane = threadIdx.x, h = blockIdx.x, b = blockIdx.y;
   const int t = a.n_tokens[b];
@@ -63,7 +65,8 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
     if (lane == 0) raise_flag(a.err, 32);
     return;
   }
-  const bool bad_target = pending && (kb < 1 || kb > 8 || vb < 1 || vb > 8 || (qjl && !a.qjl_s));
+  const bool bad_target = pending && (kb < 1 || kb > 8 || vb < 1 || vb > 8 || (qjl && !a.qjl_s) ||
+                                      (a.k_polar && kb > 4) || (a.v_polar && vb > 4));
   if (bad_target || off + page_size_dev(0, 0, false) > a.pool_bytes) {
     if (lane == 0) raise_flag(a.err, 4);
     return;
@@ -101,31 +104,36 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
       lds_cent[i] = table[centroid_offset(B) + i];
       if (i < L - 1) lds_thr[i] = table[boundary_offset(B) + i];
     }
+    const bool polar = part == 0 ? a.k_polar : a.v_polar;
+    if (polar) {
+      const float2* pt = reinterpret_cast<const float2*>(table + kPairOffset) + pair_offset_host(B);
+      for (int i = lane; i < L * L; i += 64) lds_pair[i] = pt[i];
+    }
     float x[D];
     load_row(page + part * PT * D * 2, TQ_DTYPE_F16, (size_t)lane * D, x);
     __syncthreads();
     char* part_base = part == 0 ? page : page + 1024 * kb + 256 + (qjl ? 1280 : 0);
     if (part == 0) {
       switch (B) {
-        case 1: encode_packed<0, 1>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-        case 2: encode_packed<0, 2>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-        case 3: encode_packed<0, 3>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-        case 4: encode_packed<0, 4>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-        case 5: encode_packed<0, 5>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-        case 6: encode_packed<0, 6>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-        case 7: encode_packed<0, 7>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-        default: encode_packed<0, 8>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+        case 1: encode_packed<0, 1>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        case 2: encode_packed<0, 2>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        case 3: encode_packed<0, 3>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        case 4: encode_packed<0, 4>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        case 5: encode_packed<0, 5>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        case 6: encode_packed<0, 6>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        case 7: encode_packed<0, 7>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        default: encode_packed<0, 8>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
       }
     } else {
       switch (B) {
-        case 1: encode_packed<1, 1>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-        case 2: encode_packed<1, 2>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-        case 3: encode_packed<1, 3>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-        case 4: encode_packed<1, 4>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-        case 5: encode_packed<1, 5>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-        case 6: encode_packed<1, 6>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-        case 7: encode_packed<1, 7>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-        default: encode_packed<1, 8>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+        case 1: encode_packed<1, 1>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        case 2: encode_packed<1, 2>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        case 3: encode_packed<1, 3>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        case 4: encode_packed<1, 4>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        case 5: encode_packed<1, 5>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        case 6: encode_packed<1, 6>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        case 7: encode_packed<1, 7>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        default: encode_packed<1, 8>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
       }
     }
     __syncthreads();
@@ -145,6 +153,7 @@ __global__ __launch_bounds__(256) void advance_kernel(int32_t* n_tokens, int n) 
 constexpr int kRetierBlocks = 2048;
 
 struct RetierArgs {
+  int k_polar, v_polar;   // PolarQuant parts (at most 4 bits wide)
   const int64_t* index;
   const uint64_t* new_desc;
   int n;
@@ -279,6 +288,10 @@ __device__ __forceinline__ int retier_check(const RetierArgs& a, int64_t idx, ui
       (noff != ooff && noff < ooff + osz && ooff < noff + nsz))
     return 4;
   if (((od | nd) & TQ_PAGE_PENDING) || (kb != 0 && (oq || nq || nkb > kb || nvb > vb))) return 64;
+  // PolarQuant: no code-to-code map (pairs of codes); fp16 sources encode at
+  // most 4 bits wide
+  if (kb != 0 && (a.k_polar || a.v_polar)) return 64;
+  if ((a.k_polar && nkb > 4) || (a.v_polar && nvb > 4)) return 4;
   if (nq && !a.qjl_s) return 8;
   return 0;
 }
@@ -296,6 +309,7 @@ template <bool FROM_FP16>
 __global__ __launch_bounds__(64) void retier_kernel(RetierArgs a) {
   __shared__ float lds_thr[FROM_FP16 ? 256 : 1];
   __shared__ float lds_cent[FROM_FP16 ? 256 : 1];
+  __shared__ float2 lds_pair[FROM_FP16 ? 256 : 1];
   __shared__ uint32_t lds_rows[(FROM_FP16 ? 1 : 2) * PT * kEncodeRowBytes / 4];
   __shared__ uint8_t lds_map[2][256];
   __shared__ float lds_norm[2][FROM_FP16 ? 1 : PT];
@@ -329,6 +343,11 @@ __global__ __launch_bounds__(64) void retier_kernel(RetierArgs a) {
         lds_cent[i] = table[centroid_offset(B) + i];
         if (i < L - 1) lds_thr[i] = table[boundary_offset(B) + i];
       }
+      const bool polar = part == 0 ? a.k_polar : a.v_polar;
+      if (polar) {
+        const float2* pt = reinterpret_cast<const float2*>(table + kPairOffset) + pair_offset_host(B);
+        for (int i = lane; i < L * L; i += 64) lds_pair[i] = pt[i];
+      }
       float x[D];
       load_row(src + part * PT * D * 2, TQ_DTYPE_F16, (size_t)lane * D, x);
       // the key part ends below the value rows, so in place the values are
@@ -337,25 +356,25 @@ __global__ __launch_bounds__(64) void retier_kernel(RetierArgs a) {
       char* part_base = part == 0 ? dst : dst + 1024 * nkb + 256 + (nq ? 1280 : 0);
       if (part == 0) {
         switch (B) {
-          case 1: encode_packed<0, 1>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-          case 2: encode_packed<0, 2>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-          case 3: encode_packed<0, 3>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-          case 4: encode_packed<0, 4>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-          case 5: encode_packed<0, 5>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-          case 6: encode_packed<0, 6>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-          case 7: encode_packed<0, 7>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-          default: encode_packed<0, 8>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+          case 1: encode_packed<0, 1>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+          case 2: encode_packed<0, 2>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+          case 3: encode_packed<0, 3>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+          case 4: encode_packed<0, 4>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+          case 5: encode_packed<0, 5>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+          case 6: encode_packed<0, 6>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+          case 7: encode_packed<0, 7>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+          default: encode_packed<0, 8>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
         }
       } else {
         switch (B) {
-          case 1: encode_packed<1, 1>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-          case 2: encode_packed<1, 2>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-          case 3: encode_packed<1, 3>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-          case 4: encode_packed<1, 4>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-          case 5: encode_packed<1, 5>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-          case 6: encode_packed<1, 6>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-          case 7: encode_packed<1, 7>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-          default: encode_packed<1, 8>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+          case 1: encode_packed<1, 1>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+          case 2: encode_packed<1, 2>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+          case 3: encode_packed<1, 3>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+          case 4: encode_packed<1, 4>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+          case 5: encode_packed<1, 5>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+          case 6: encode_packed<1, 6>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+          case 7: encode_packed<1, 7>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+          default: encode_packed<1, 8>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
         }
       }
       __syncthreads();
@@ -425,6 +444,8 @@ int tq_append_kv(const tq_layer* layer, const tq_cache* cache, const tq_token_in
   a.k_table = layer->k_table;
   a.v_table = layer->v_table;
   a.qjl_s = layer->qjl_s;
+  a.k_polar = layer->k_codebook == TQ_CODEBOOK_POLAR;
+  a.v_polar = layer->v_codebook == TQ_CODEBOOK_POLAR;
   hipStream_t s = (hipStream_t)stream;
   hipLaunchKernelGGL(append_kernel, dim3(cache->n_kv_heads, cache->n_sessions), dim3(64), 0, s, a);
   if ((st = launch_status("append"))) return st;
@@ -460,6 +481,8 @@ int tq_retier_pages(const tq_layer* layer, const tq_cache* cache, const int64_t*
   a.k_table = layer->k_table;
   a.v_table = layer->v_table;
   a.qjl_s = layer->qjl_s;
+  a.k_polar = layer->k_codebook == TQ_CODEBOOK_POLAR;
+  a.v_polar = layer->v_codebook == TQ_CODEBOOK_POLAR;
   // packed sources first: the pages it re-tiers no longer look like fp16
   // pages to the second launch.  The first launch raises the error flags.
   const dim3 grid(std::min(n, kRetierBlocks));

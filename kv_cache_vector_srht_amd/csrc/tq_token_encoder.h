@@ -100,20 +100,71 @@ __device__ __forceinline__ float rotate_quantize(float (&x)[D], const uint32_t (
   return n;
 }
 
+// PolarQuant of one vector held by this lane: u as above, then for each
+// coordinate pair i the radius r = |(u_2i, u_2i+1)| against the radius
+// boundaries in `thr` and the angle sector floor((atan2(u_2i+1, u_2i) + pi)
+// 2^B / (2 pi)) mod 2^B; codes go to emit(2i, radius) and emit(2i+1, angle).
+// On return x holds u minus the pair's reconstruction from `pair`.
+template <int B, class Emit>
+__device__ __forceinline__ float rotate_quantize_polar(float (&x)[D], const uint32_t (&m)[4],
+                                                       const float* thr, const float2* pair, Emit emit) {
+  constexpr int L = 1 << B;
+  constexpr float kPi = 3.14159265358979323846f;
+  constexpr float kSectors = (float)L / (2.0f * 3.14159265358979323846f);
+  float ss = 0.f;
+#pragma clang loop unroll(full)
+  for (int j = 0; j < D; ++j) ss = fmaf(x[j], x[j], ss);
+  const float n = sqrtf(ss);
+#pragma clang loop unroll(full)
+  for (int j = 0; j < D; ++j) x[j] = flip_if(x[j], dsign(m, j));
+  fwht_halves(x);
+  const float inv = n > 0.f ? 1.0f / n : 0.f;
+#pragma clang loop unroll(full)
+  for (int j = 0; j < D / 2; ++j) {
+    const float a = x[j], b = x[j + D / 2];
+    x[j] = flip_if(a + b, dsign(m, j)) * inv;
+    x[j + D / 2] = flip_if(a - b, dsign(m, j + D / 2)) * inv;
+  }
+#pragma clang loop unroll(full)
+  for (int i = 0; i < D / 2; ++i) {
+    const float u0 = x[2 * i], u1 = x[2 * i + 1];
+    const float r = sqrtf(fmaf(u0, u0, u1 * u1));
+    const float th = atan2f(u1, u0);
+    const uint32_t rc = quantize<B>(r, thr);
+    const uint32_t tc = (uint32_t)(int)floorf((th + kPi) * kSectors) & (uint32_t)(L - 1);
+    emit(2 * i, rc);
+    emit(2 * i + 1, tc);
+    const float2 p = pair[rc | (tc << B)];
+    x[2 * i] = u0 - p.x;
+    x[2 * i + 1] = u1 - p.y;
+  }
+  return n;
+}
+
+// One part (PART 0 keys, 1 values) of a page: this lane's vector encoded at
+// width B, scalar or (polar, B <= 4) PolarQuant with the pair table in LDS.
 template <int PART, int B>
 __device__ __forceinline__ void encode_packed(const float* __restrict__ qjl_s, char* page, bool qjl, int lane,
                               float (&x)[D], const uint32_t (&m)[4], float* lds_thr,
-                              float* lds_cent, uint32_t* lds_rows) {
+                              float* lds_cent, uint32_t* lds_rows, bool polar = false,
+                              const float2* lds_pair = nullptr) {
   constexpr int kb = B;
   if constexpr (PART == 0) {
     uint32_t sw[4 * B];
 #pragma clang loop unroll(full)
     for (int i = 0; i < 4 * B; ++i) sw[i] = 0;
-    const float n = rotate_quantize<B>(x, m, lds_thr, lds_cent, [&](int j, uint32_t c) {
+    auto emit = [&](int j, uint32_t c) {
       const int pos = j * B, wi = pos >> 5, sh = pos & 31;
       sw[wi] |= c << sh;
       if (sh + B > 32) sw[wi + 1] |= c >> (32 - sh);
-    });
+    };
+    float n;
+    if constexpr (B <= 4) {
+      n = polar ? rotate_quantize_polar<B>(x, m, lds_thr, lds_pair, emit)
+                : rotate_quantize<B>(x, m, lds_thr, lds_cent, emit);
+    } else {
+      n = rotate_quantize<B>(x, m, lds_thr, lds_cent, emit);
+    }
     uint4* dst = reinterpret_cast<uint4*>(page);
 #pragma clang loop unroll(full)
     for (int w = 0; w < B; ++w)
@@ -154,9 +205,14 @@ __device__ __forceinline__ void encode_packed(const float* __restrict__ qjl_s, c
     uint32_t cb[D / 4];
 #pragma clang loop unroll(full)
     for (int i = 0; i < D / 4; ++i) cb[i] = 0;
-    const float n = rotate_quantize<B>(x, m, lds_thr, lds_cent, [&](int j, uint32_t c) {
-      cb[j >> 2] |= c << (8 * (j & 3));
-    });
+    auto emit = [&](int j, uint32_t c) { cb[j >> 2] |= c << (8 * (j & 3)); };
+    float n;
+    if constexpr (B <= 4) {
+      n = polar ? rotate_quantize_polar<B>(x, m, lds_thr, lds_pair, emit)
+                : rotate_quantize<B>(x, m, lds_thr, lds_cent, emit);
+    } else {
+      n = rotate_quantize<B>(x, m, lds_thr, lds_cent, emit);
+    }
     uint4* row = reinterpret_cast<uint4*>(reinterpret_cast<char*>(lds_rows) + lane * kEncodeRowBytes);
 #pragma clang loop unroll(full)
     for (int i = 0; i < D / 16; ++i) row[i] = make_uint4(cb[4 * i], cb[4 * i + 1], cb[4 * i + 2], cb[4 * i + 3]);

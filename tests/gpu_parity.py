@@ -51,11 +51,15 @@ class Tally:
 
 
 def _cmp_codes(got: np.ndarray, exp: np.ndarray, near: np.ndarray, t: Tally, what: str, lo: int,
-               alt: list):
+               alt: list, kind=O.LLOYD_MAX, bits: int = 0):
     diff = got != exp
     t.coords += got.size
     if diff.any():
-        bad = diff & ~(near & (np.abs(got - exp) == 1))
+        step = np.abs(got - exp)
+        if kind == O.POLAR:   # angle codes (odd coordinates) are cyclic
+            L = 1 << bits
+            step[:, 1::2] = np.minimum(step[:, 1::2], L - step[:, 1::2])
+        bad = diff & ~(near & (step == 1))
         assert not bad.any(), f"{what}: {int(bad.sum())} code mismatches away from a boundary " \
                               f"(first at {np.argwhere(bad)[0].tolist()}, got {got[bad][:4]}, want {exp[bad][:4]})"
         t.mismatches += int(diff.sum())
@@ -105,10 +109,10 @@ def compare_unit_pages(cache, b: int, h: int, K: np.ndarray, V: np.ndarray, form
             return raw[o:o + n]
         kc = O.unpack_block(part("k_codes"), kb)
         ok_rows = _cmp_codes(kc, enc["k"]["codes"], enc["k"]["near"], t, f"K page ({b},{h},{p}) fmt {fmt}",
-                             lo, k_alt)
+                             lo, k_alt, k_kind, kb)
         vc = O.v_codes_from_streams(O.unpack_block(part("v_codes"), vb))
         v_rows = _cmp_codes(vc, enc["v"]["codes"], enc["v"]["near"], t, f"V page ({b},{h},{p}) fmt {fmt}",
-                            lo, v_alt)
+                            lo, v_alt, v_kind, vb)
         k_ok[lo:hi] = ok_rows
         v_ok[lo:hi] = v_rows
         for name, ref in (("k_norm", enc["k"]["norm"]), ("v_norm", enc["v"]["norm"])):
@@ -207,8 +211,8 @@ def compare_unit_full(pool_host: np.ndarray, offsets: np.ndarray, b: int, h: int
             got = np.frombuffer(b"".join(part(name)), dtype="<f4")
             assert np.allclose(got, e["norm"], rtol=NORM_RTOL, atol=0), f"{name} {what}"
         k_alt, v_alt = [], []
-        _cmp_codes(gk, ek["codes"], ek["near"], t, "K " + what, 0, k_alt)
-        _cmp_codes(gv, ev["codes"], ev["near"], t, "V " + what, 0, v_alt)
+        _cmp_codes(gk, ek["codes"], ek["near"], t, "K " + what, 0, k_alt, k_kind, kb)
+        _cmp_codes(gv, ev["codes"], ev["near"], t, "V " + what, 0, v_alt, v_kind, vb)
         kc, vc = ek["codes"].copy(), ev["codes"].copy()
         for codes, alt in ((kc, k_alt), (vc, v_alt)):
             for r, c, code in alt:

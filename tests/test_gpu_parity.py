@@ -269,3 +269,45 @@ def test_fitted_codebooks(dev):
     layer_kw = dict(k_codebook=tq.FITTED, v_codebook=tq.FITTED,
                     k_table=tq.calibrated_table(Xk, signs), v_table=tq.calibrated_table(Xv, signs))
     run_case(w, [0], dev, layer_kw=layer_kw)
+
+
+def _narrow_workload(pages=24, qjl=False, G=4):
+    """Every (K, V) width pair within 1..4 bits, an fp16 first page."""
+    w = W.make_workload(2, {"n_tokens": 64 * pages, "batch": 1, "n_kv_heads": 2,
+                            "n_q_heads": 2 * G, "sink_tokens": 0, "dtype": "float16"})
+    combos = [(kb, vb) for kb in range(1, 5) for vb in range(1, 5)]
+    w.formats = [[[[W.packed(*combos[(p + 5 * h) % 16], qjl) if p > 0 else W.FP16
+                    for p in range(pages)] for h in range(2)]]]
+    return w
+
+
+def test_polar_every_narrow_width_pair(dev):
+    """PolarQuant keys and values at every width pair up to 4 bits."""
+    w = _narrow_workload(pages=34)
+    w.k_codebook = w.v_codebook = O.POLAR
+    run_case(w, [0], dev)
+
+
+def test_polar_keys_with_qjl_and_scalar_values(dev):
+    w = _narrow_workload(pages=18, qjl=True)
+    w.k_codebook, w.v_codebook = O.POLAR, O.LLOYD_MAX
+    run_case(w, [0], dev)
+
+
+def test_polar_refuses_wide_pages(dev):
+    """A PolarQuant part wider than 4 bits is refused by encode (flag 4, page
+    untouched) and skipped by decode and dequantise."""
+    import kv_cache_vector_srht_amd as tq
+    w = W.make_workload(2, {"n_tokens": 128, "batch": 1, "n_kv_heads": 1, "n_q_heads": 4,
+                            "sink_tokens": 0})
+    fm = [[[W.packed(3, 2), W.packed(6, 2)]]]
+    layer = tq.Layer(W.rotation_signs(42, 0), dev, None, tq.POLAR, tq.LLOYD_MAX)
+    cache = tq.Cache(fm, [128], dev)
+    k, v = W.make_kv(w, 0, device=dev)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    tq.encode_kv(layer, cache, k, v, error_flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 4
+    # the K part of the refused page stays zero
+    kpart = cache.page_view(0, 0, 1)[:1024 * 6 + 256]
+    assert int(kpart.to(torch.int32).abs().sum()) == 0

@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol(L):
         assert hasattr(L, name)
 
 
-@pytest.mark.parametrize("kind", [tq.LLOYD_MAX, tq.UNIFORM, tq.BETA])
+@pytest.mark.parametrize("kind", [tq.LLOYD_MAX, tq.UNIFORM, tq.BETA, tq.POLAR])
 @pytest.mark.parametrize("bits", range(1, 9))
 def test_codebook_bit_equal_to_oracle(L, bits, kind):
     c, t = tq.build_codebook(bits, kind)
@@ -72,7 +72,7 @@ def test_fitted_codebooks_bit_equal_to_oracle(L, fit_samples, which):
         tq.fit_codebook(np.zeros((4, 128), np.float32), signs, 2)
 
 
-@pytest.mark.parametrize("kind", [tq.LLOYD_MAX, tq.UNIFORM, tq.BETA, "fitted"])
+@pytest.mark.parametrize("kind", [tq.LLOYD_MAX, tq.UNIFORM, tq.BETA, tq.POLAR, "fitted"])
 def test_codebook_table_layout(L, kind, fit_samples):
     if kind == "fitted":
         signs, samples = fit_samples
@@ -85,11 +85,23 @@ def test_codebook_table_layout(L, kind, fit_samples):
         co, to = (1 << b) - 2, 510 + (1 << b) - b - 1
         assert np.array_equal(tab[co:co + (1 << b)], c) and np.array_equal(tab[to:to + (1 << b) - 1], t)
     assert np.all(tab[1012:1024] == 0)
+    # pair tables of widths 1..4: (c[lo], c[hi]), or PolarQuant's pair levels
+    for b, first in ((1, 0), (2, 4), (3, 20), (4, 84)):
+        Lb = 1 << b
+        pt = tab[1056 + 2 * first:1056 + 2 * (first + Lb * Lb)].reshape(Lb * Lb, 2)
+        lo, hi = np.arange(Lb * Lb) % Lb, np.arange(Lb * Lb) >> b
+        if kind is tq.POLAR or (isinstance(kind, int) and kind == tq.POLAR):
+            want = O.polar_pairs(b)[lo, hi]
+            ulp = np.abs(pt.view(np.int32).astype(np.int64) - want.astype(np.float32).view(np.int32))
+            assert np.all((ulp <= 1) | (np.abs(pt - want) < 1e-12)), b
+        else:
+            c = O.codebook(b, kind)[0]
+            assert np.array_equal(pt[:, 0], c[lo]) and np.array_equal(pt[:, 1], c[hi]), b
     # lookup grids: code(u) = base + [u >= boundary] at bin floor(u S + O), or
     # at the nearest integer for 256-bin grids (their O carries the -1/2)
     words = tab.view(np.uint32)
     rng = np.random.default_rng(0)
-    for b in range(1, 9):
+    for b in range(1, 5 if kind is tq.POLAR or (isinstance(kind, int) and kind == tq.POLAR) else 9):
         gS, gO = tab[1024 + 4 * (b - 1)], tab[1024 + 4 * (b - 1) + 1]
         nb, off = int(words[1024 + 4 * (b - 1) + 2]), int(words[1024 + 4 * (b - 1) + 3])
         ent = words[off:off + 2 * nb].reshape(nb, 2)
@@ -178,7 +190,7 @@ def _encode(L, layer, cache, **kw):
 def test_encode_validation(L):
     bad = [
         (dict(layer=_fake_layer(head_dim=64)), -2),
-        (dict(layer=_fake_layer(k_codebook=4)), -1),
+        (dict(layer=_fake_layer(k_codebook=5)), -1),
         (dict(layer=_fake_layer(sign_mask=0x1004)), -3),
         (dict(layer=_fake_layer(qjl_s=0x6000, jl_dim=64)), -2),
         (dict(cache=_fake_cache(n_sessions=0)), -1),
