@@ -37,8 +37,10 @@ def _effective(targets, n):
     return out
 
 
-@pytest.mark.parametrize("dtype", ["float16", "float32"])
-def test_decode_loop_append_and_pack(dev, dtype):
+@pytest.mark.parametrize("dtype,kinds", [("float16", (O.LLOYD_MAX, O.LLOYD_MAX)),
+                                         ("float32", (O.LLOYD_MAX, O.LLOYD_MAX)),
+                                         ("float16", (O.POLAR, O.POLAR))])
+def test_decode_loop_append_and_pack(dev, dtype, kinds):
     import kv_cache_vector_srht_amd as tq
     B, H, G, T = 2, 2, 4, 64 * 5 + 20
     w = W.make_workload(2, {"n_tokens": T, "batch": B, "n_kv_heads": H, "n_q_heads": H * G,
@@ -49,7 +51,7 @@ def test_decode_loop_append_and_pack(dev, dtype):
            for h in range(H)] for _ in range(B)]
     signs = W.rotation_signs(42, 0)
     S = W.qjl_matrix(42, 0)
-    layer = tq.Layer(signs, dev, S)
+    layer = tq.Layer(signs, dev, S, kinds[0], kinds[1])
     k, v = W.make_kv(w, 0, device=dev)          # [B, H, T, 128], the tokens in order
     q = W.make_query(w, 0, device=dev)
     start = [100, 90]                            # ragged sessions
@@ -85,7 +87,7 @@ def test_decode_loop_append_and_pack(dev, dtype):
                     pending = bool(int(desc[b, h, p]) >> 57 & 1)
                     assert pending == (eff[p] == W.FP16), (step, b, h, p)
                 Kh, Vh = compare_unit_full(pool, cache.offsets, b, h, kh[b, h, :n1[b]], vh[b, h, :n1[b]],
-                                           eff, signs, S, t)
+                                           eff, signs, S, t, kinds[0], kinds[1])
                 compare_attention(out[b, h * G:(h + 1) * G], qh[b, h * G:(h + 1) * G], Kh, Vh, t)
     assert int(flags.item()) == 0
     t.check()

@@ -224,3 +224,45 @@ def test_retier_rejects_unsupported_changes(dev):
 
 def tq_present():
     return 1 << 63
+
+
+def test_retier_fp16_into_polar_and_refuse_polar_demotion(dev):
+    """With PolarQuant parts an fp16 page is encoded into a polar format of at
+    most 4 bits; a packed polar page is not re-coded (flag 64) and a polar
+    target wider than 4 bits is refused (flag 4)."""
+    import kv_cache_vector_srht_amd as tq
+    B, H, G, P = 1, 2, 4, 4
+    T = P * 64
+    w = W.make_workload(2, {"n_tokens": T, "batch": B, "n_kv_heads": H, "n_q_heads": H * G,
+                            "sink_tokens": 0, "dtype": "float16"})
+    fm = [[[W.FP16, W.FP16, W.packed(3, 2), W.FP16] for _ in range(H)]]
+    signs, S = W.rotation_signs(42, 0), W.qjl_matrix(42, 0)
+    layer = tq.Layer(signs, dev, S, tq.POLAR, tq.POLAR)
+    cache = tq.Cache(fm, [T], dev)
+    k, v = W.make_kv(w, 0, device=dev)
+    q = W.make_query(w, 0, device=dev)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    tq.encode_kv(layer, cache, k, v, error_flags=flags)
+    tq.retier_pages(layer, cache, [(0, 0, 0), (0, 1, 1), (0, 1, 0)],
+                    [(4, 4, False), (2, 1, True), (3, 3, False)], error_flags=flags)
+    out = _np(tq.decode_attention(layer, cache, q))
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 0
+    pool = _np(cache.pool)
+    kh, vh, qh = _np(k).astype(np.float64), _np(v).astype(np.float64), _np(q).astype(np.float64)
+    t = Tally()
+    for h in range(H):
+        Keff, Veff = kh[0, h].copy(), vh[0, h].copy()
+        Kh, Vh = compare_unit_full(pool, cache.offsets, 0, h, Keff, Veff, cache.formats[0][h], signs, S, t,
+                                   O.POLAR, O.POLAR)
+        compare_attention(out[0, h * G:(h + 1) * G], qh[0, h * G:(h + 1) * G], Kh, Vh, t)
+    t.check()
+    L = tq.lib()
+    off = cache.offsets[0, 0]
+    for idx, d, want in (([2], [L.tq_page_descriptor(int(off[2]), 2, 1, 0)], 64),
+                         ([3], [L.tq_page_descriptor(int(off[3]), 6, 2, 0)], 4)):
+        pool0 = _np(cache.pool).copy()
+        flags.zero_()
+        _raw_retier(cache, layer, idx, d, flags)
+        assert int(flags.item()) == want
+        assert np.array_equal(_np(cache.pool), pool0)
