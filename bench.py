@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--workload", type=int, default=3, help="workload index 1..5 (default 3)")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--codecs", type=int, default=1,
+                    help="compare the scalar codec with PolarQuant on one layer (1, default) or skip (0)")
     ap.add_argument("--tiering", type=int, default=1,
                     help="measure page-mass export and page re-tiering (1, default) or skip (0)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
@@ -291,6 +293,49 @@ def tiering(w, layers, inputs, queries, outs, wss, dev):
                       "median of the first eight layers, one call each"}
 
 
+def codecs(w, inputs, queries, dev, reps=5):
+    """Scalar Lloyd-Max against PolarQuant on one layer of the workload's shape
+    with every page at 4 + 4 bits (the pages' default of 4-bit radius and
+    4-bit angle): encode and decode attention time per layer (median of
+    `reps` after a warm-up) and the effective GB/s of each."""
+    import numpy as np
+    import torch
+    import kv_cache_vector_srht_amd as tq
+    import workloads as W
+    stream = torch.cuda.current_stream(dev)
+    k, v = inputs[0]
+    q = queries[0]
+    fm = [[[W.packed(4, 4)] * w.n_pages for _ in range(w.n_kv_heads)] for _ in range(w.batch)]
+    page = tq.page_bytes(W.packed(4, 4))
+    n_pages = w.batch * w.n_kv_heads * w.n_pages
+    enc_bytes = k.numel() * k.element_size() * 2 + n_pages * page
+    dec_bytes = n_pages * page + q.numel() * q.element_size() + w.batch * w.n_q_heads * 128 * 4
+    res = {}
+    for name, kind in (("lloyd_max", tq.LLOYD_MAX), ("polar", tq.POLAR)):
+        layer = tq.Layer(W.rotation_signs(W.ROTATION_SEED, 0), dev, None, kind, kind)
+        c = tq.Cache(fm, [w.n_tokens] * w.batch, dev)
+        out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
+        ws = torch.empty(tq.workspace_bytes(c, w.n_q_heads), dtype=torch.uint8, device=dev)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        te, td = [], []
+        for r in range(reps + 1):
+            ev[0].record(stream)
+            tq.encode_kv(layer, c, k, v, tok0=0)
+            ev[1].record(stream)
+            tq.decode_attention(layer, c, q, out=out, workspace=ws)
+            ev[2].record(stream)
+            ev[2].synchronize()
+            if r:
+                te.append(ev[0].elapsed_time(ev[1]))
+                td.append(ev[1].elapsed_time(ev[2]))
+        e_ms, d_ms = float(np.median(te)), float(np.median(td))
+        res[name] = {"encode_us": round(e_ms * 1e3, 2), "encode_gbs": round(enc_bytes / e_ms / 1e6, 1),
+                     "decode_us": round(d_ms * 1e3, 2), "decode_gbs": round(dec_bytes / d_ms / 1e6, 1)}
+    res["shape"] = (f"one layer, {w.batch} sessions x {w.n_kv_heads} KV heads x {w.n_tokens} tokens, "
+                    f"every page K4/V4")
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -409,6 +454,8 @@ def main():
         line["decode_loop"] = decode_loop(w, layers, inputs, queries, outs, wss, args.loop_steps, dev)
     if args.tiering:
         line["tiering"] = tiering(w, layers, inputs, queries, outs, wss, dev)
+    if args.codecs:
+        line["codecs"] = codecs(w, inputs, queries, dev)
     if not args.no_cpu_baseline:
         kv_host = {}
 
