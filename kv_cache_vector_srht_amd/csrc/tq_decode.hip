@@ -397,23 +397,20 @@ __device__ __forceinline__ void value_accum_wide(const char* blk, int lane, cons
 // Value accumulation of an fp16 page into the rotated-domain sums: each token's
 // row is rotated with the unnormalised D H D (the 16 lanes of a quarter hold
 // its 128 values, 8 each), so that D H D acc / d at the end returns sum p v.
+// Value sums of an fp16 page: acc (rotated domain) += D H D sum_t w_t v_t.
+// Lane (quarter q, 16 lanes i) sums coordinates 8i..8i+7 of tokens 4k+q in
+// the original domain; then, once per page and query head, the quarter's sum
+// is rotated (the transform is linear), in-lane for coordinate bits 0..2 and
+// across the 16 lanes of the quarter for bits 3..6.  Up to G = 4; wider groups
+// rotate each token's row (fewer registers).
 template <int G>
 __device__ __forceinline__ void value_accum_fp16(const char* page, int lane, const float* wv,
                                                  const uint32_t (&dm)[8], float (&acc)[G][8]) {
   const __half* vbase = reinterpret_cast<const __half*>(page + PT * D * 2);
   const int q = lane >> 4, i = lane & 15;
-  for (int k = 0; k < 16; ++k) {
-    const int t = 4 * k + q;
-    const uint4 vv = reinterpret_cast<const uint4*>(vbase + (size_t)t * D + 8 * i)[0];
-    const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
-    float x[8];
+  auto rotate = [&](float (&x)[8]) {
 #pragma clang loop unroll(full)
-    for (int e = 0; e < 4; ++e) {
-      const float2 f = __half22float2(*reinterpret_cast<const __half2*>(&vw[e]));
-      x[2 * e] = flip_if(f.x, dm[2 * e]);
-      x[2 * e + 1] = flip_if(f.y, dm[2 * e + 1]);
-    }
-    // coordinate bits 0..2: within the lane
+    for (int e = 0; e < 8; ++e) x[e] = flip_if(x[e], dm[e]);
 #pragma clang loop unroll(full)
     for (int hh = 1; hh < 8; hh <<= 1)
 #pragma clang loop unroll(full)
@@ -423,7 +420,6 @@ __device__ __forceinline__ void value_accum_fp16(const char* page, int lane, con
           x[e] = a0 + b0;
           x[e + hh] = a0 - b0;
         }
-    // coordinate bits 3..6: across the 16 lanes of the quarter
 #pragma clang loop unroll(full)
     for (int m = 1; m < 16; m <<= 1) {
       const float sg = (i & m) ? -1.f : 1.f;
@@ -433,14 +429,55 @@ __device__ __forceinline__ void value_accum_fp16(const char* page, int lane, con
         x[e] = fmaf(sg, x[e], other);
       }
     }
-    float wt[G];
 #pragma clang loop unroll(full)
-    for (int h = 0; h < G; ++h) wt[h] = wv[t * G + h];
+    for (int e = 0; e < 8; ++e) x[e] = flip_if(x[e], dm[e]);
+  };
+  auto row = [&](int t, float (&x)[8]) {
+    const uint4 vv = reinterpret_cast<const uint4*>(vbase + (size_t)t * D + 8 * i)[0];
+    const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma clang loop unroll(full)
-    for (int e = 0; e < 8; ++e) {
-      const float y = flip_if(x[e], dm[e]);
+    for (int e = 0; e < 4; ++e) {
+      const float2 f = __half22float2(*reinterpret_cast<const __half2*>(&vw[e]));
+      x[2 * e] = f.x;
+      x[2 * e + 1] = f.y;
+    }
+  };
+  if constexpr (G <= 4) {
+    float y[G][8];
 #pragma clang loop unroll(full)
-      for (int h = 0; h < G; ++h) acc[h][e] = fmaf(wt[h], y, acc[h][e]);
+    for (int h = 0; h < G; ++h)
+#pragma clang loop unroll(full)
+      for (int e = 0; e < 8; ++e) y[h][e] = 0.f;
+#pragma clang loop unroll_count(4)
+    for (int k = 0; k < 16; ++k) {
+      const int t = 4 * k + q;
+      float x[8];
+      row(t, x);
+#pragma clang loop unroll(full)
+      for (int h = 0; h < G; ++h) {
+        const float wt = wv[t * G + h];
+#pragma clang loop unroll(full)
+        for (int e = 0; e < 8; ++e) y[h][e] = fmaf(wt, x[e], y[h][e]);
+      }
+    }
+#pragma clang loop unroll(full)
+    for (int h = 0; h < G; ++h) {
+      rotate(y[h]);
+#pragma clang loop unroll(full)
+      for (int e = 0; e < 8; ++e) acc[h][e] += y[h][e];
+    }
+  } else {
+    for (int k = 0; k < 16; ++k) {
+      const int t = 4 * k + q;
+      float x[8];
+      row(t, x);
+      rotate(x);
+#pragma clang loop unroll(full)
+      for (int h = 0; h < G; ++h) {
+        const float wt = wv[t * G + h];
+#pragma clang loop unroll(full)
+        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(wt, x[e], acc[h][e]);
+      }
     }
   }
 }
@@ -489,7 +526,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
                                                                   float* __restrict__ wsp) {
   __shared__ SplitLds<G> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+  // the other class runs its ranges last page first: a decode loop's fp16
+  // tail page is then in the first workgroups dispatched, not behind the
+  // rounds of workgroups that find nothing of the class
+  const int split = CLASS == 2 ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
+  const int hkv = blockIdx.y, b = blockIdx.z;
   const int hq0 = hkv * G;
   // partials [B][H_q][n_partials]: the classes that run, in class order
   const size_t head_stride = (size_t)a.n_partials * kPartialFloats;
@@ -502,14 +543,18 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
   const int p_begin = split * pps;
   const int p_end = min(npages, p_begin + pps);
   const uint64_t* ptab = pages + ((size_t)b * a.n_kv_heads + hkv) * a.max_pages;
+  bool need_tables;
   {
     // nothing of this class in the range: an empty partial, no setup (the
     // descriptors are read in parallel, one per thread)
-    bool mine = false;
+    bool mine = false, coded = false;
     for (int p = p_begin + tid; p < p_end; p += blockDim.x) {
       const PageDesc pd = read_desc(ptab[p]);
-      mine |= page_class(pd.kb, pd.vb, pd.qjl) == CLASS;
+      const bool m = page_class(pd.kb, pd.vb, pd.qjl) == CLASS;
+      mine |= m;
+      coded |= m && pd.kb != 0;
     }
+    need_tables = CLASS != 2 || __syncthreads_or(coded);
     if (!__syncthreads_or(mine)) {
       if (tid < G) {
         part[tid * head_stride] = -INFINITY;
@@ -520,29 +565,31 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
   }
 
   // Stage codebooks: pair tables for 1..4 bits, quad tables for 1..2 bits and
-  // all centroid lists.
-  for (int i = tid; i < 510; i += blockDim.x) {
-    sm.kcent[i] = a.k_table[i];
-    sm.vcent[i] = a.v_table[i];
+  // all centroid lists (not needed when the range's pages of this class are
+  // all fp16, as a decode loop's tail pages are).
+  if (need_tables) {
+    for (int i = tid; i < 510; i += blockDim.x) {
+      sm.kcent[i] = a.k_table[i];
+      sm.vcent[i] = a.v_table[i];
+    }
+    // pair tables come with the codebook table (a scalar codebook's (c[lo],
+    // c[hi]), or PolarQuant's radius-angle pairs); a quad entry is two pairs
+    const float2* kpt = reinterpret_cast<const float2*>(a.k_table + kPairOffset);
+    const float2* vpt = reinterpret_cast<const float2*>(a.v_table + kPairOffset);
+    for (int i = tid; i < 340; i += blockDim.x) {
+      sm.kpair[i] = kpt[i];
+      sm.vpair[i] = vpt[i];
+    }
+    for (int i = tid; i < 272; i += blockDim.x) {
+      const int bb = i < 16 ? 1 : 2;
+      const int idx = i - quad_offset(bb), sh = 2 * bb, po = pair_offset(bb);
+      const int p0 = po + (idx & ((1 << sh) - 1)), p1 = po + (idx >> sh);
+      const float2 k0 = kpt[p0], k1 = kpt[p1], v0 = vpt[p0], v1 = vpt[p1];
+      sm.kquad[i] = make_float4(k0.x, k0.y, k1.x, k1.y);
+      sm.vquad[i] = make_float4(v0.x, v0.y, v1.x, v1.y);
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  // pair tables come with the codebook table (a scalar codebook's (c[lo],
-  // c[hi]), or PolarQuant's radius-angle pairs); a quad entry is two pairs
-  const float2* kpt = reinterpret_cast<const float2*>(a.k_table + kPairOffset);
-  const float2* vpt = reinterpret_cast<const float2*>(a.v_table + kPairOffset);
-  for (int i = tid; i < 340; i += blockDim.x) {
-    sm.kpair[i] = kpt[i];
-    sm.vpair[i] = vpt[i];
-  }
-  for (int i = tid; i < 272; i += blockDim.x) {
-    const int bb = i < 16 ? 1 : 2;
-    const int idx = i - quad_offset(bb), sh = 2 * bb, po = pair_offset(bb);
-    const int p0 = po + (idx & ((1 << sh) - 1)), p1 = po + (idx >> sh);
-    const float2 k0 = kpt[p0], k1 = kpt[p1], v0 = vpt[p0], v1 = vpt[p1];
-    sm.kquad[i] = make_float4(k0.x, k0.y, k1.x, k1.y);
-    sm.vquad[i] = make_float4(v0.x, v0.y, v1.x, v1.y);
-  }
-  __syncthreads();
   // keep the scheduler from moving table work into the page loop (it otherwise
   // inflates the loop's register use)
   __builtin_amdgcn_sched_barrier(0);
