@@ -315,94 +315,94 @@ __global__ __launch_bounds__(64) void retier_kernel(RetierArgs a) {
   __shared__ float lds_norm[2][FROM_FP16 ? 1 : PT];
   const int lane = threadIdx.x;
   for (int item = blockIdx.x; item < a.n; item += gridDim.x) {
-  const int64_t idx = a.index[item];
-  const bool in_table = idx >= 0 && idx < a.n_entries;
-  uint64_t* dp = a.pages + (in_table ? idx : 0);
-  const uint64_t od = in_table ? *dp : 0, nd = a.new_desc[item];
-  int e = retier_check(a, idx, od, nd);
-  const int kb = (int)((od >> 48) & 15), vb = (int)((od >> 52) & 15);
-  if (!e && !(a.sources & (kb == 0 ? TQ_RETIER_FROM_FP16 : TQ_RETIER_FROM_PACKED))) e = 64;
-  if (e) {
-    if (a.raise_errors && lane == 0) raise_flag(a.err, e);
-    continue;
-  }
-  const int nkb = (int)((nd >> 48) & 15), nvb = (int)((nd >> 52) & 15);
-  const bool nq = (nd & TQ_PAGE_QJL) != 0;
-  if ((kb == 0) != FROM_FP16) continue;
-  const char* src = a.pool + (od & TQ_PAGE_OFFSET_MASK);
-  char* dst = a.pool + (nd & TQ_PAGE_OFFSET_MASK);
-  if constexpr (FROM_FP16) {
-    uint32_t m[4];
-#pragma clang loop unroll(full)
-    for (int w = 0; w < 4; ++w) m[w] = a.sign_mask[w];
-    for (int part = 0; part < 2; ++part) {
-      const int B = part == 0 ? nkb : nvb;
-      const float* table = part == 0 ? a.k_table : a.v_table;
-      const int L = 1 << B;
-      for (int i = lane; i < L; i += 64) {
-        lds_cent[i] = table[centroid_offset(B) + i];
-        if (i < L - 1) lds_thr[i] = table[boundary_offset(B) + i];
-      }
-      const bool polar = part == 0 ? a.k_polar : a.v_polar;
-      if (polar) {
-        const float2* pt = reinterpret_cast<const float2*>(table + kPairOffset) + pair_offset_host(B);
-        for (int i = lane; i < L * L; i += 64) lds_pair[i] = pt[i];
-      }
-      float x[D];
-      load_row(src + part * PT * D * 2, TQ_DTYPE_F16, (size_t)lane * D, x);
-      // the key part ends below the value rows, so in place the values are
-      // still intact when they are loaded here
-      __syncthreads();
-      char* part_base = part == 0 ? dst : dst + 1024 * nkb + 256 + (nq ? 1280 : 0);
-      if (part == 0) {
-        switch (B) {
-          case 1: encode_packed<0, 1>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-          case 2: encode_packed<0, 2>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-          case 3: encode_packed<0, 3>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-          case 4: encode_packed<0, 4>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-          case 5: encode_packed<0, 5>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-          case 6: encode_packed<0, 6>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-          case 7: encode_packed<0, 7>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-          default: encode_packed<0, 8>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        }
-      } else {
-        switch (B) {
-          case 1: encode_packed<1, 1>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-          case 2: encode_packed<1, 2>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-          case 3: encode_packed<1, 3>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-          case 4: encode_packed<1, 4>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-          case 5: encode_packed<1, 5>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-          case 6: encode_packed<1, 6>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-          case 7: encode_packed<1, 7>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-          default: encode_packed<1, 8>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        }
-      }
-      __syncthreads();
+    const int64_t idx = a.index[item];
+    const bool in_table = idx >= 0 && idx < a.n_entries;
+    uint64_t* dp = a.pages + (in_table ? idx : 0);
+    const uint64_t od = in_table ? *dp : 0, nd = a.new_desc[item];
+    int e = retier_check(a, idx, od, nd);
+    const int kb = (int)((od >> 48) & 15), vb = (int)((od >> 52) & 15);
+    if (!e && !(a.sources & (kb == 0 ? TQ_RETIER_FROM_FP16 : TQ_RETIER_FROM_PACKED))) e = 64;
+    if (e) {
+      if (a.raise_errors && lane == 0) raise_flag(a.err, e);
+      continue;
     }
-  } else {
-    build_code_map(a.k_table, kb, nkb, lds_map[0], lane);
-    build_code_map(a.v_table, vb, nvb, lds_map[1], lane);
-    __syncthreads();
-    // every load of the old page, then (after the barrier) every store
-    uint4* krow = reinterpret_cast<uint4*>(reinterpret_cast<char*>(lds_rows) + lane * kEncodeRowBytes);
-    uint4* vrow = reinterpret_cast<uint4*>(reinterpret_cast<char*>(lds_rows) + (PT + lane) * kEncodeRowBytes);
-    const char* ov = src + 1024 * kb + 256;
-    unpack_mapped_any(kb, reinterpret_cast<const uint4*>(src), lane, lds_map[0], krow);
-    unpack_mapped_any(vb, reinterpret_cast<const uint4*>(ov), lane, lds_map[1], vrow);
-    // the norms pass through LDS too, so that every load of the old page has
-    // returned before the first store (the barrier of a one-wave block does
-    // not wait for vector memory)
-    lds_norm[0][lane] = reinterpret_cast<const float*>(src + 1024 * kb)[lane];
-    lds_norm[1][lane] = reinterpret_cast<const float*>(ov + 1024 * vb)[lane];
-    __syncthreads();
-    char* nv = dst + 1024 * nkb + 256;
-    pack_row_any(nkb, krow, lane, reinterpret_cast<uint4*>(dst));
-    pack_row_any(nvb, vrow, lane, reinterpret_cast<uint4*>(nv));
-    reinterpret_cast<float*>(dst + 1024 * nkb)[lane] = lds_norm[0][lane];
-    reinterpret_cast<float*>(nv + 1024 * nvb)[lane] = lds_norm[1][lane];
-  }
-  if (lane == 0) *dp = nd;
-  __syncthreads();   // LDS is reused by the next page
+    const int nkb = (int)((nd >> 48) & 15), nvb = (int)((nd >> 52) & 15);
+    const bool nq = (nd & TQ_PAGE_QJL) != 0;
+    if ((kb == 0) != FROM_FP16) continue;
+    const char* src = a.pool + (od & TQ_PAGE_OFFSET_MASK);
+    char* dst = a.pool + (nd & TQ_PAGE_OFFSET_MASK);
+    if constexpr (FROM_FP16) {
+      uint32_t m[4];
+#pragma clang loop unroll(full)
+      for (int w = 0; w < 4; ++w) m[w] = a.sign_mask[w];
+      for (int part = 0; part < 2; ++part) {
+        const int B = part == 0 ? nkb : nvb;
+        const float* table = part == 0 ? a.k_table : a.v_table;
+        const int L = 1 << B;
+        for (int i = lane; i < L; i += 64) {
+          lds_cent[i] = table[centroid_offset(B) + i];
+          if (i < L - 1) lds_thr[i] = table[boundary_offset(B) + i];
+        }
+        const bool polar = part == 0 ? a.k_polar : a.v_polar;
+        if (polar) {
+          const float2* pt = reinterpret_cast<const float2*>(table + kPairOffset) + pair_offset_host(B);
+          for (int i = lane; i < L * L; i += 64) lds_pair[i] = pt[i];
+        }
+        float x[D];
+        load_row(src + part * PT * D * 2, TQ_DTYPE_F16, (size_t)lane * D, x);
+        // the key part ends below the value rows, so in place the values are
+        // still intact when they are loaded here
+        __syncthreads();
+        char* part_base = part == 0 ? dst : dst + 1024 * nkb + 256 + (nq ? 1280 : 0);
+        if (part == 0) {
+          switch (B) {
+            case 1: encode_packed<0, 1>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            case 2: encode_packed<0, 2>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            case 3: encode_packed<0, 3>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            case 4: encode_packed<0, 4>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            case 5: encode_packed<0, 5>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            case 6: encode_packed<0, 6>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            case 7: encode_packed<0, 7>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            default: encode_packed<0, 8>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+          }
+        } else {
+          switch (B) {
+            case 1: encode_packed<1, 1>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            case 2: encode_packed<1, 2>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            case 3: encode_packed<1, 3>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            case 4: encode_packed<1, 4>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            case 5: encode_packed<1, 5>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            case 6: encode_packed<1, 6>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            case 7: encode_packed<1, 7>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            default: encode_packed<1, 8>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+          }
+        }
+        __syncthreads();
+      }
+    } else {
+      build_code_map(a.k_table, kb, nkb, lds_map[0], lane);
+      build_code_map(a.v_table, vb, nvb, lds_map[1], lane);
+      __syncthreads();
+      // every load of the old page, then (after the barrier) every store
+      uint4* krow = reinterpret_cast<uint4*>(reinterpret_cast<char*>(lds_rows) + lane * kEncodeRowBytes);
+      uint4* vrow = reinterpret_cast<uint4*>(reinterpret_cast<char*>(lds_rows) + (PT + lane) * kEncodeRowBytes);
+      const char* ov = src + 1024 * kb + 256;
+      unpack_mapped_any(kb, reinterpret_cast<const uint4*>(src), lane, lds_map[0], krow);
+      unpack_mapped_any(vb, reinterpret_cast<const uint4*>(ov), lane, lds_map[1], vrow);
+      // the norms pass through LDS too, so that every load of the old page has
+      // returned before the first store (the barrier of a one-wave block does
+      // not wait for vector memory)
+      lds_norm[0][lane] = reinterpret_cast<const float*>(src + 1024 * kb)[lane];
+      lds_norm[1][lane] = reinterpret_cast<const float*>(ov + 1024 * vb)[lane];
+      __syncthreads();
+      char* nv = dst + 1024 * nkb + 256;
+      pack_row_any(nkb, krow, lane, reinterpret_cast<uint4*>(dst));
+      pack_row_any(nvb, vrow, lane, reinterpret_cast<uint4*>(nv));
+      reinterpret_cast<float*>(dst + 1024 * nkb)[lane] = lds_norm[0][lane];
+      reinterpret_cast<float*>(nv + 1024 * nvb)[lane] = lds_norm[1][lane];
+    }
+    if (lane == 0) *dp = nd;
+    __syncthreads();   // LDS is reused by the next page
   }
 }
 
