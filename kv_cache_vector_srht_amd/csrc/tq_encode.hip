@@ -76,13 +76,13 @@ __global__ __launch_bounds__(64) void encode_kernel(EncodeArgs a, const uint64_t
     return;
   }
   const bool polar = part == 0 ? a.k_polar : a.v_polar;
-  // scalar parts without a QJL sketch are written by encode_pages_kernel
-  if (!polar && (part == 1 || !qjl)) return;
   const int B = part == 0 ? kb : vb;
-  if (polar && B > 4) {
+  if (polar && B > 4) {   // no pair table that wide: refused, the part untouched
     if (lane == 0) raise_flag(a.err, 4);
     return;
   }
+  // everything but the keys of QJL pages is written by encode_pages_kernel
+  if (part == 1 || !qjl) return;
   const float* table = part == 0 ? a.k_table : a.v_table;
   const int L = 1 << B;
   for (int i = lane; i < L; i += 64) {
@@ -194,7 +194,7 @@ struct EncodeLane {
 
 // Encodes this lane's quarter of one token into code bytes of its LDS matrix
 // row; returns the vector norm (the same in the four lanes of the quad).
-template <int DT>
+template <int DT, bool POLAR = false>
 __device__ __forceinline__ float encode_quarter(const void* src, size_t row_off, int e,
                                                 const EncodeLane& el, int B, const Lut& lut,
                                                 const uint2* ent, uint32_t* mat_row) {
@@ -266,6 +266,38 @@ __device__ __forceinline__ float encode_quarter(const void* src, size_t row_off,
   uint32_t cb[8];
 #pragma clang loop unroll(full)
   for (int i = 0; i < 8; ++i) cb[i] = 0;
+  if constexpr (POLAR) {
+    // PolarQuant: slots 2m, 2m+1 are a coordinate pair.  Undo the outer D and
+    // the lane's sign to get u, then the radius code from the lookup grid
+    // (built on the radius boundaries) and the angle sector from atan2.  The
+    // codes are final: no flip below.
+    constexpr float kPi = 3.14159265358979323846f;
+    const uint32_t lsign = (e == 1 || e == 2) ? 1u : 0u;
+    const int L = 1 << B;
+    const float sectors = (float)L * (1.0f / (2.0f * kPi));
+#pragma clang loop unroll(full)
+    for (int m = 0; m < 16; ++m) {
+      const int s0 = 2 * m, s1 = 2 * m + 1;
+      const float u0 = flip_if(x[s0], ((el.dl >> s0) & 1u) ^ lsign) * inv;
+      const float u1 = flip_if(x[s1], ((el.dl >> s1) & 1u) ^ lsign) * inv;
+      const float r = sqrtf(fmaf(u0, u0, u1 * u1));
+      uint32_t bin;
+      if (lut.nb == kLutByteBins)
+        bin = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(r, lut.S, lut.O), 0, 0u);
+      else
+        bin = (uint32_t)(int)__builtin_amdgcn_fmed3f(fmaf(r, lut.S, lut.O), 0.f, lut.fmax);
+      const uint2 en = ent[bin];
+      const uint32_t rc = en.x + (r >= __uint_as_float(en.y) ? 1u : 0u);
+      const uint32_t tc = (uint32_t)(int)floorf((atan2f(u1, u0) + kPi) * sectors) & (uint32_t)(L - 1);
+      cb[s0 >> 2] |= rc << (8 * (s0 & 3));
+      cb[s1 >> 2] |= tc << (8 * (s1 & 3));
+    }
+#pragma clang loop unroll(full)
+    for (int c = 0; c < 4; ++c)
+      *reinterpret_cast<uint2*>(reinterpret_cast<char*>(mat_row) + 32 * c + 8 * e) =
+          make_uint2(cb[2 * c], cb[2 * c + 1]);
+    return n;
+  }
   if (lut.nb == kLutByteBins) {
     // 256-bin grid: the bin is u S + O (O carries the -1/2) rounded and
     // saturated to a byte by one conversion
@@ -348,7 +380,9 @@ __device__ __forceinline__ void store_stream_part(int B, char* blk, int s, int e
   }
 }
 
-template <int DT>
+// POLAR: the instantiation for layers with PolarQuant parts (K and/or V, as
+// a.k_polar / a.v_polar say); the plain one has no polar code at all.
+template <int DT, bool POLAR>
 __global__ __launch_bounds__(kEncodeBlock) void encode_pages_kernel(EncodeArgs a,
                                                                     const uint64_t* __restrict__ pages) {
   __shared__ uint2 entk[kLutMaxBins], entv[kLutMaxBins];
@@ -450,10 +484,17 @@ __global__ __launch_bounds__(kEncodeBlock) void encode_pages_kernel(EncodeArgs a
     const size_t row_off = base + (size_t)(t_first + t - a.tok0) * a.st;
     uint32_t* rowk = matk + t * (kRowStride / 4);
     uint32_t* rowv = matv + t * (kRowStride / 4);
-    // QJL key pages and PolarQuant parts are written by the per-token kernel
-    const bool skip_k = qjl || a.k_polar, skip_v = a.v_polar;
-    const float nk = skip_k ? 0.f : encode_quarter<DT>(a.k, row_off, e, el, kb, lk, entk, rowk);
-    const float nv = skip_v ? 0.f : encode_quarter<DT>(a.v, row_off, e, el, vb, lv, entv, rowv);
+    // QJL key pages are written by the per-token kernel (codes + sketch), as
+    // are PolarQuant parts wider than 4 bits (which it refuses)
+    const bool kp = POLAR && a.k_polar, vp = POLAR && a.v_polar;
+    const bool skip_k = qjl || (kp && kb > 4), skip_v = vp && vb > 4;
+    float nk = 0.f, nv = 0.f;
+    if (!skip_k)
+      nk = kp ? encode_quarter<DT, POLAR>(a.k, row_off, e, el, kb, lk, entk, rowk)
+              : encode_quarter<DT>(a.k, row_off, e, el, kb, lk, entk, rowk);
+    if (!skip_v)
+      nv = vp ? encode_quarter<DT, POLAR>(a.v, row_off, e, el, vb, lv, entv, rowv)
+              : encode_quarter<DT>(a.v, row_off, e, el, vb, lv, entv, rowv);
     if (e == 0) {
       normk[t] = nk;
       normv[t] = nv;
@@ -545,26 +586,37 @@ int tq_encode_kv(const tq_layer* layer, const tq_cache* cache, const tq_kv_input
   const int n_pages = last_page - a.page0 + 1;
   dim3 grid((n_pages + kEncodePagesPerBlock - 1) / kEncodePagesPerBlock, cache->n_kv_heads,
             cache->n_sessions);
-  if (a.dtype == TQ_DTYPE_F16)
-    hipLaunchKernelGGL(encode_pages_kernel<TQ_DTYPE_F16>, grid, dim3(kEncodeBlock), 0,
-                       (hipStream_t)stream, a, cache->pages);
-  else
-    hipLaunchKernelGGL(encode_pages_kernel<TQ_DTYPE_F32>, grid, dim3(kEncodeBlock), 0,
-                       (hipStream_t)stream, a, cache->pages);
+  const bool polar = a.k_polar || a.v_polar;
+  if (a.dtype == TQ_DTYPE_F16) {
+    if (polar)
+      hipLaunchKernelGGL((encode_pages_kernel<TQ_DTYPE_F16, true>), grid, dim3(kEncodeBlock), 0,
+                         (hipStream_t)stream, a, cache->pages);
+    else
+      hipLaunchKernelGGL((encode_pages_kernel<TQ_DTYPE_F16, false>), grid, dim3(kEncodeBlock), 0,
+                         (hipStream_t)stream, a, cache->pages);
+  } else {
+    if (polar)
+      hipLaunchKernelGGL((encode_pages_kernel<TQ_DTYPE_F32, true>), grid, dim3(kEncodeBlock), 0,
+                         (hipStream_t)stream, a, cache->pages);
+    else
+      hipLaunchKernelGGL((encode_pages_kernel<TQ_DTYPE_F32, false>), grid, dim3(kEncodeBlock), 0,
+                         (hipStream_t)stream, a, cache->pages);
+  }
   int st2 = launch_status("encode");
   if (st2) return st2;
   dim3 qgrid(n_pages, cache->n_kv_heads, cache->n_sessions);
   if (layer->qjl_s || a.k_polar) {
-    // keys of QJL pages (codes, norm and sign sketch) and PolarQuant keys,
-    // one wavefront per page
+    // keys of QJL pages (codes, norm and sign sketch), one wavefront per page;
+    // it also flags PolarQuant keys wider than 4 bits
     hipLaunchKernelGGL(encode_kernel<0>, qgrid, dim3(64), 0, (hipStream_t)stream, a, cache->pages,
                        layer->qjl_s);
-    if ((st2 = launch_status("encode QJL or polar keys"))) return st2;
+    if ((st2 = launch_status("encode QJL keys"))) return st2;
   }
   if (a.v_polar) {
+    // flags PolarQuant values wider than 4 bits (nothing else to write)
     hipLaunchKernelGGL(encode_kernel<1>, qgrid, dim3(64), 0, (hipStream_t)stream, a, cache->pages,
                        layer->qjl_s);
-    st2 = launch_status("encode polar values");
+    st2 = launch_status("check polar values");
   }
   return st2;
 }
