@@ -77,12 +77,9 @@ __global__ __launch_bounds__(64) void encode_kernel(EncodeArgs a, const uint64_t
   }
   const bool polar = part == 0 ? a.k_polar : a.v_polar;
   const int B = part == 0 ? kb : vb;
-  if (polar && B > 4) {   // no pair table that wide: refused, the part untouched
-    if (lane == 0) raise_flag(a.err, 4);
-    return;
-  }
-  // everything but the keys of QJL pages is written by encode_pages_kernel
-  if (part == 1 || !qjl) return;
+  // everything but the keys of QJL pages is written by encode_pages_kernel,
+  // which also flags PolarQuant parts wider than 4 bits
+  if (part == 1 || !qjl || (polar && B > 4)) return;
   const float* table = part == 0 ? a.k_table : a.v_table;
   const int L = 1 << B;
   for (int i = lane; i < L; i += 64) {
@@ -269,12 +266,15 @@ __device__ __forceinline__ float encode_quarter(const void* src, size_t row_off,
   if constexpr (POLAR) {
     // PolarQuant: slots 2m, 2m+1 are a coordinate pair.  Undo the outer D and
     // the lane's sign to get u, then the radius code from the lookup grid
-    // (built on the radius boundaries) and the angle sector from atan2.  The
-    // codes are final: no flip below.
-    constexpr float kPi = 3.14159265358979323846f;
+    // (built on the radius boundaries) and the angle sector
+    // floor((theta + pi) L / (2 pi)) mod L without an arctangent: the signs
+    // give the quadrant (sectors of L/4 each from -pi), and inside it the
+    // angle psi from the quadrant's start has tan psi = a / b with (a, b) =
+    // (|u1|, |u0|) in quadrants 0 and 2, (|u0|, |u1|) in 1 and 3, so the
+    // sector's offset counts the edges 2 pi j / L with a >= tan(2 pi j / L) b.
+    // The codes are final: no flip below.
     const uint32_t lsign = (e == 1 || e == 2) ? 1u : 0u;
     const int L = 1 << B;
-    const float sectors = (float)L * (1.0f / (2.0f * kPi));
 #pragma clang loop unroll(full)
     for (int m = 0; m < 16; ++m) {
       const int s0 = 2 * m, s1 = 2 * m + 1;
@@ -288,7 +288,24 @@ __device__ __forceinline__ float encode_quarter(const void* src, size_t row_off,
         bin = (uint32_t)(int)__builtin_amdgcn_fmed3f(fmaf(r, lut.S, lut.O), 0.f, lut.fmax);
       const uint2 en = ent[bin];
       const uint32_t rc = en.x + (r >= __uint_as_float(en.y) ? 1u : 0u);
-      const uint32_t tc = (uint32_t)(int)floorf((atan2f(u1, u0) + kPi) * sectors) & (uint32_t)(L - 1);
+      uint32_t tc;
+      if (L == 2) {
+        tc = u1 >= 0.f ? 1u : 0u;
+      } else {
+        const bool n0 = u0 < 0.f, n1 = u1 < 0.f;
+        const uint32_t qd = n1 ? (n0 ? 0u : 1u) : (n0 ? 3u : 2u);
+        const float a0 = fabsf(u0), a1 = fabsf(u1);
+        const float pa = (qd & 1u) ? a0 : a1, pb = (qd & 1u) ? a1 : a0;
+        uint32_t sub = 0;
+        if (L == 8) {
+          sub = pa >= pb ? 1u : 0u;                                   // tan(pi/4)
+        } else if (L == 16) {
+          sub = (pa >= 0.41421356237309503f * pb ? 1u : 0u) +        // tan(pi/8)
+                (pa >= pb ? 1u : 0u) +                                // tan(pi/4)
+                (pa >= 2.41421356237309503f * pb ? 1u : 0u);          // tan(3 pi/8)
+        }
+        tc = qd * (uint32_t)(L >> 2) + sub;
+      }
       cb[s0 >> 2] |= rc << (8 * (s0 & 3));
       cb[s1 >> 2] |= tc << (8 * (s1 & 3));
     }
@@ -488,6 +505,8 @@ __global__ __launch_bounds__(kEncodeBlock) void encode_pages_kernel(EncodeArgs a
     // are PolarQuant parts wider than 4 bits (which it refuses)
     const bool kp = POLAR && a.k_polar, vp = POLAR && a.v_polar;
     const bool skip_k = qjl || (kp && kb > 4), skip_v = vp && vb > 4;
+    // a PolarQuant part wider than 4 bits has no pair table: refused, untouched
+    if (tid == 0 && ((kp && kb > 4) || (vp && vb > 4))) raise_flag(a.err, 4);
     float nk = 0.f, nv = 0.f;
     if (!skip_k)
       nk = kp ? encode_quarter<DT, POLAR>(a.k, row_off, e, el, kb, lk, entk, rowk)
@@ -604,19 +623,12 @@ int tq_encode_kv(const tq_layer* layer, const tq_cache* cache, const tq_kv_input
   }
   int st2 = launch_status("encode");
   if (st2) return st2;
-  dim3 qgrid(n_pages, cache->n_kv_heads, cache->n_sessions);
-  if (layer->qjl_s || a.k_polar) {
-    // keys of QJL pages (codes, norm and sign sketch), one wavefront per page;
-    // it also flags PolarQuant keys wider than 4 bits
+  if (layer->qjl_s) {
+    // keys of QJL pages: codes, norm and sign sketch, one wavefront per page
+    dim3 qgrid(n_pages, cache->n_kv_heads, cache->n_sessions);
     hipLaunchKernelGGL(encode_kernel<0>, qgrid, dim3(64), 0, (hipStream_t)stream, a, cache->pages,
                        layer->qjl_s);
-    if ((st2 = launch_status("encode QJL keys"))) return st2;
-  }
-  if (a.v_polar) {
-    // flags PolarQuant values wider than 4 bits (nothing else to write)
-    hipLaunchKernelGGL(encode_kernel<1>, qgrid, dim3(64), 0, (hipStream_t)stream, a, cache->pages,
-                       layer->qjl_s);
-    st2 = launch_status("check polar values");
+    st2 = launch_status("encode QJL keys");
   }
   return st2;
 }
