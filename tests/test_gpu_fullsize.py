@@ -112,3 +112,85 @@ def test_fullsize_tiers_256k(dev):
     # oldest tier, the K4/V4 tier, and the boundary into the fp16 tier
     run_full(w, [0], lambda fm: [(0, 0), (3, 5), (w.batch - 1, w.n_kv_heads - 2)],
              [(0, 256), (T - 4096, 256), (T - 1024 - 128, 256)], dev)
+
+
+@pytest.mark.timeout(300)
+def test_fullsize_tiers_256k_reached_by_retiering(dev):
+    """The 256K tiered workload built the way the pages' tiering runs: every
+    packed page encoded at its head's warm tier (K4/V4 plus the head's offset),
+    then one tq_retier_pages call demotes the older and the masked pages to
+    their tiers in place.  Sampled units against the oracle: demoted pages hold
+    the oracle's warm-tier codes requantised to the target widths with the
+    warm-tier norms; attention over the re-tiered cache."""
+    import math
+    import kv_cache_vector_srht_amd as tq
+    w = W.make_workload(5)
+    fm = w.formats[0]
+    B, H, T = w.batch, w.n_kv_heads, w.n_tokens
+    offs = [int(math.floor(5 * s)) - 2 for s in W._score_rng(5, 0, 11).random(H)]
+    warm = [W.packed(min(8, max(1, 4 + o)), min(8, max(1, 4 + o))) for o in offs]
+    init = [[[f if f[0] == 0 else warm[h] for f in fm[b][h]] for h in range(H)] for b in range(B)]
+    signs = W.rotation_signs(W.ROTATION_SEED, 0)
+    layer = tq.Layer(signs, dev)
+    cache = tq.Cache(init, [T] * B, dev)
+    k, v = W.make_kv(w, 0, device=dev)
+    q = W.make_query(w, 0, device=dev)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    tq.encode_kv(layer, cache, k, v, error_flags=flags)
+    pages = [(b, h, p) for b in range(B) for h in range(H) for p in range(len(fm[b][h]))
+             if tuple(fm[b][h][p]) != tuple(init[b][h][p])]
+    print(f"demoting {len(pages)} of {B * H * len(fm[0][0])} pages", flush=True)
+    tq.retier_pages(layer, cache, pages, [fm[b][h][p] for b, h, p in pages], error_flags=flags)
+    out = _np(tq.decode_attention(layer, cache, q))
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 0
+    assert cache.page_classes == tq.page_classes(fm)
+    assert np.array_equal(_np(cache.pages).view(np.uint64), cache.host_pages)
+    pool = _np(cache.pool)
+    qh = _np(q).astype(np.float64)
+    G = w.n_q_heads // H
+    t = Tally()
+    for (b, h) in [(0, 0), (3, 5), (B - 1, H - 2)]:
+        kh = _np(k[b, h]).astype(np.float64)
+        vh = _np(v[b, h]).astype(np.float64)
+        demoted = {p for (bb, hh, p) in pages if (bb, hh) == (b, h)}
+        Kh, Vh = compare_unit_full(pool, cache.offsets, b, h, kh, vh, fm[b][h], signs, None, t,
+                                   skip=demoted)
+        # demoted pages, one oracle pass per (warm, target) group
+        groups = {}
+        for p in sorted(demoted):
+            groups.setdefault(tuple(fm[b][h][p]), []).append(p)
+        (kb, vb, _) = warm[h]
+        for (nkb, nvb, _), plist in groups.items():
+            rows = np.concatenate([np.arange(64 * p, 64 * p + 64) for p in plist])
+            sec = O.page_sections((nkb, nvb, False))
+            raws = [pool[int(cache.offsets[b, h, p]):int(cache.offsets[b, h, p]) + O.page_bytes((nkb, nvb, False))]
+                    for p in plist]
+
+            def part(name):
+                o, n = sec[name]
+                return b"".join(r[o:o + n].tobytes() for r in raws)
+            recon = {}
+            for which, X, ob, nb in (("k", kh, kb, nkb), ("v", vh, vb, nvb)):
+                e = O.encode(X[rows], signs, ob)
+                exp = O.requantize_codes(e["codes"], ob, nb)
+                if which == "k":
+                    g = np.concatenate([O.unpack_block(r[sec["k_codes"][0]:sec["k_codes"][0] + sec["k_codes"][1]]
+                                                       .tobytes(), nb) for r in raws])
+                else:
+                    g = np.concatenate([O.v_codes_from_streams(O.unpack_block(
+                        r[sec["v_codes"][0]:sec["v_codes"][0] + sec["v_codes"][1]].tobytes(), nb)) for r in raws])
+                diff = g != exp
+                t.coords += g.size
+                if diff.any():
+                    c = e["codes"][diff]
+                    lo = O.requantize_codes(np.maximum(c - 1, 0), ob, nb)
+                    hi = O.requantize_codes(np.minimum(c + 1, (1 << ob) - 1), ob, nb)
+                    assert np.all(e["near"][diff] & ((g[diff] == lo) | (g[diff] == hi)))
+                    t.mismatches += int(diff.sum())
+                norm = np.frombuffer(part(f"{which}_norm"), dtype="<f4")
+                assert np.allclose(norm, e["norm"], rtol=1e-5, atol=0)
+                recon[which] = O.dequantize(e["norm"], g, signs, nb)
+            Kh[rows], Vh[rows] = recon["k"], recon["v"]
+        compare_attention(out[b, h * G:(h + 1) * G], qh[b, h * G:(h + 1) * G], Kh, Vh, t)
+    t.check()
