@@ -97,16 +97,18 @@ __global__ __launch_bounds__(64) void encode_kernel(EncodeArgs a, const uint64_t
   load_row(src, a.dtype, base + (size_t)(t_first + lane - a.tok0) * a.st, x);
   __syncthreads();
   char* part_base = part == 0 ? page : page + 1024 * kb + 256 + (qjl ? 1280 : 0);
+  float n = 0.f;
   switch (B) {
-    case 1: encode_packed<PART, 1>(qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-    case 2: encode_packed<PART, 2>(qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-    case 3: encode_packed<PART, 3>(qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-    case 4: encode_packed<PART, 4>(qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-    case 5: encode_packed<PART, 5>(qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-    case 6: encode_packed<PART, 6>(qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-    case 7: encode_packed<PART, 7>(qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-    default: encode_packed<PART, 8>(qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+    case 1: n = encode_packed<PART, 1>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+    case 2: n = encode_packed<PART, 2>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+    case 3: n = encode_packed<PART, 3>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+    case 4: n = encode_packed<PART, 4>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+    case 5: n = encode_packed<PART, 5>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+    case 6: n = encode_packed<PART, 6>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+    case 7: n = encode_packed<PART, 7>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+    default: n = encode_packed<PART, 8>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows); break;
   }
+  if (PART == 0 && qjl) qjl_sketch(qjl_s, part_base + 1024 * B + 256, lane, x, m, n);
 }
 
 // ------------------------------------------------------- encode (quad lanes)

@@ -113,27 +113,29 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
     load_row(page + part * PT * D * 2, TQ_DTYPE_F16, (size_t)lane * D, x);
     __syncthreads();
     char* part_base = part == 0 ? page : page + 1024 * kb + 256 + (qjl ? 1280 : 0);
+    float n = 0.f;
     if (part == 0) {
       switch (B) {
-        case 1: encode_packed<0, 1>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        case 2: encode_packed<0, 2>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        case 3: encode_packed<0, 3>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        case 4: encode_packed<0, 4>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        case 5: encode_packed<0, 5>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        case 6: encode_packed<0, 6>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        case 7: encode_packed<0, 7>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        default: encode_packed<0, 8>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        case 1: n = encode_packed<0, 1>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        case 2: n = encode_packed<0, 2>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        case 3: n = encode_packed<0, 3>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        case 4: n = encode_packed<0, 4>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        case 5: n = encode_packed<0, 5>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        case 6: n = encode_packed<0, 6>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        case 7: n = encode_packed<0, 7>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        default: n = encode_packed<0, 8>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
       }
+      if (qjl) qjl_sketch(a.qjl_s, part_base + 1024 * B + 256, lane, x, m, n);
     } else {
       switch (B) {
-        case 1: encode_packed<1, 1>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        case 2: encode_packed<1, 2>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        case 3: encode_packed<1, 3>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        case 4: encode_packed<1, 4>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        case 5: encode_packed<1, 5>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        case 6: encode_packed<1, 6>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        case 7: encode_packed<1, 7>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        default: encode_packed<1, 8>(a.qjl_s, part_base, qjl, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        case 1: n = encode_packed<1, 1>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        case 2: n = encode_packed<1, 2>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        case 3: n = encode_packed<1, 3>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        case 4: n = encode_packed<1, 4>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        case 5: n = encode_packed<1, 5>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        case 6: n = encode_packed<1, 6>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        case 7: n = encode_packed<1, 7>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        default: n = encode_packed<1, 8>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
       }
     }
     __syncthreads();
@@ -354,27 +356,29 @@ __global__ __launch_bounds__(64) void retier_kernel(RetierArgs a) {
         // still intact when they are loaded here
         __syncthreads();
         char* part_base = part == 0 ? dst : dst + 1024 * nkb + 256 + (nq ? 1280 : 0);
+        float n = 0.f;
         if (part == 0) {
           switch (B) {
-            case 1: encode_packed<0, 1>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-            case 2: encode_packed<0, 2>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-            case 3: encode_packed<0, 3>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-            case 4: encode_packed<0, 4>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-            case 5: encode_packed<0, 5>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-            case 6: encode_packed<0, 6>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-            case 7: encode_packed<0, 7>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-            default: encode_packed<0, 8>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            case 1: n = encode_packed<0, 1>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            case 2: n = encode_packed<0, 2>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            case 3: n = encode_packed<0, 3>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            case 4: n = encode_packed<0, 4>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            case 5: n = encode_packed<0, 5>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            case 6: n = encode_packed<0, 6>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            case 7: n = encode_packed<0, 7>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            default: n = encode_packed<0, 8>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
           }
+          if (nq) qjl_sketch(a.qjl_s, part_base + 1024 * B + 256, lane, x, m, n);
         } else {
           switch (B) {
-            case 1: encode_packed<1, 1>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-            case 2: encode_packed<1, 2>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-            case 3: encode_packed<1, 3>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-            case 4: encode_packed<1, 4>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-            case 5: encode_packed<1, 5>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-            case 6: encode_packed<1, 6>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-            case 7: encode_packed<1, 7>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-            default: encode_packed<1, 8>(a.qjl_s, part_base, nq, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            case 1: n = encode_packed<1, 1>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            case 2: n = encode_packed<1, 2>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            case 3: n = encode_packed<1, 3>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            case 4: n = encode_packed<1, 4>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            case 5: n = encode_packed<1, 5>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            case 6: n = encode_packed<1, 6>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            case 7: n = encode_packed<1, 7>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            default: n = encode_packed<1, 8>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
           }
         }
         __syncthreads();

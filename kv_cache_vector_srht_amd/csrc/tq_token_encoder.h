@@ -143,11 +143,12 @@ __device__ __forceinline__ float rotate_quantize_polar(float (&x)[D], const uint
 
 // One part (PART 0 keys, 1 values) of a page: this lane's vector encoded at
 // width B, scalar or (polar, B <= 4) PolarQuant with the pair table in LDS.
+// Returns the vector's norm; for keys x is left holding the rotated-domain
+// residual u - c[code] (qjl_sketch's input).
 template <int PART, int B>
-__device__ __forceinline__ void encode_packed(const float* __restrict__ qjl_s, char* page, bool qjl, int lane,
-                              float (&x)[D], const uint32_t (&m)[4], float* lds_thr,
-                              float* lds_cent, uint32_t* lds_rows, bool polar = false,
-                              const float2* lds_pair = nullptr) {
+__device__ __forceinline__ float encode_packed(char* page, int lane, float (&x)[D], const uint32_t (&m)[4],
+                                               float* lds_thr, float* lds_cent, uint32_t* lds_rows,
+                                               bool polar = false, const float2* lds_pair = nullptr) {
   constexpr int kb = B;
   if constexpr (PART == 0) {
     uint32_t sw[4 * B];
@@ -170,36 +171,7 @@ __device__ __forceinline__ void encode_packed(const float* __restrict__ qjl_s, c
     for (int w = 0; w < B; ++w)
       dst[w * 64 + lane] = make_uint4(sw[4 * w], sw[4 * w + 1], sw[4 * w + 2], sw[4 * w + 3]);
     reinterpret_cast<float*>(page + 1024 * kb)[lane] = n;
-    if (qjl) {
-      // r = x - xhat = (n / d) D H D (u - c): one more butterfly in registers.
-      float e2 = 0.f;
-#pragma clang loop unroll(full)
-      for (int j = 0; j < D; ++j) {
-        e2 = fmaf(x[j], x[j], e2);
-        x[j] = flip_if(x[j], dsign(m, j));
-      }
-      fwht128(x);
-      const float sc = n * (1.0f / D);
-#pragma clang loop unroll(full)
-      for (int j = 0; j < D; ++j) x[j] = flip_if(x[j], dsign(m, j)) * sc;
-      const float gamma = n * sqrtf(e2) * 0.08838834764831845f;  // n ||u - c|| / sqrt(d)
-      uint32_t zw[4];
-#pragma clang loop unroll(full)
-      for (int w = 0; w < 4; ++w) {
-        uint32_t bitsw = 0;
-        for (int ii = 0; ii < 32; ++ii) {
-          const float* srow = qjl_s + (size_t)(32 * w + ii) * D;
-          float p = 0.f;
-#pragma clang loop unroll(full)
-          for (int j = 0; j < D; ++j) p = fmaf(srow[j], x[j], p);
-          bitsw |= (p >= 0.f ? 1u : 0u) << ii;
-        }
-        zw[w] = bitsw;
-      }
-      char* qbase = page + 1024 * kb + 256;
-      reinterpret_cast<uint4*>(qbase)[lane] = make_uint4(zw[0], zw[1], zw[2], zw[3]);
-      reinterpret_cast<float*>(qbase + 1024)[lane] = gamma;
-    }
+    return n;
   } else {
     // Codes as bytes into this lane's LDS row, then transpose into V streams.
     uint32_t cb[D / 4];
@@ -238,7 +210,44 @@ __device__ __forceinline__ void encode_packed(const float* __restrict__ qjl_s, c
     for (int w = 0; w < B; ++w)
       dst[w * 64 + lane] = make_uint4(sw[4 * w], sw[4 * w + 1], sw[4 * w + 2], sw[4 * w + 3]);
     reinterpret_cast<float*>(page + 1024 * B)[lane] = n;
+    return n;
   }
+}
+
+// The QJL sign sketch of a key ("TurboMOQ", QJL residual correction) from the
+// rotated-domain residual u - c that encode_packed leaves in x:
+// r = x - xhat = (n / d) D H D (u - c) (one more butterfly in registers),
+// z = sign(S r) (bit i of the lane's 128-bit word), gamma = ||r||, stored at
+// qbase (64 x 16 B signs) and qbase + 1024 (64 x float32).  One copy serves
+// every width.
+__device__ __forceinline__ void qjl_sketch(const float* __restrict__ qjl_s, char* qbase, int lane,
+                                           float (&x)[D], const uint32_t (&m)[4], float n) {
+  float e2 = 0.f;
+#pragma clang loop unroll(full)
+  for (int j = 0; j < D; ++j) {
+    e2 = fmaf(x[j], x[j], e2);
+    x[j] = flip_if(x[j], dsign(m, j));
+  }
+  fwht128(x);
+  const float sc = n * (1.0f / D);
+#pragma clang loop unroll(full)
+  for (int j = 0; j < D; ++j) x[j] = flip_if(x[j], dsign(m, j)) * sc;
+  const float gamma = n * sqrtf(e2) * 0.08838834764831845f;  // n ||u - c|| / sqrt(d)
+  uint32_t zw[4];
+#pragma clang loop unroll(full)
+  for (int w = 0; w < 4; ++w) {
+    uint32_t bitsw = 0;
+    for (int ii = 0; ii < 32; ++ii) {
+      const float* srow = qjl_s + (size_t)(32 * w + ii) * D;
+      float p = 0.f;
+#pragma clang loop unroll(full)
+      for (int j = 0; j < D; ++j) p = fmaf(srow[j], x[j], p);
+      bitsw |= (p >= 0.f ? 1u : 0u) << ii;
+    }
+    zw[w] = bitsw;
+  }
+  reinterpret_cast<uint4*>(qbase)[lane] = make_uint4(zw[0], zw[1], zw[2], zw[3]);
+  reinterpret_cast<float*>(qbase + 1024)[lane] = gamma;
 }
 
 }  // namespace dev
