@@ -44,6 +44,28 @@ struct DecodeArgs {
   float* mass;  // [B][H_q][max_pages] page attention mass, or null
 };
 
+// In-place Walsh-Hadamard transform (Sylvester order, unnormalised) of 128
+// values held one per thread by the block's first two waves (thread j holds
+// value j, active = j < 128): stages 1..32 inside the wave through lane
+// shuffles, stage 64 across the two waves through `xch` (128 floats of LDS).
+// Every thread of the block calls it: it holds one barrier.
+__device__ __forceinline__ float fwht128_two_waves(float v, int j, bool active, float* xch) {
+  if (active) {
+#pragma clang loop unroll(full)
+    for (int hh = 1; hh < 64; hh <<= 1) {
+      const float other = __shfl_xor(v, hh, 64);
+      v = (j & hh) ? other - v : v + other;
+    }
+    xch[j] = v;
+  }
+  __syncthreads();
+  if (active) {
+    const float other = xch[j ^ 64];
+    v = (j & 64) ? other - v : v + other;
+  }
+  return v;
+}
+
 // (1) query prep: one 128-thread block per (session, query head).
 __global__ __launch_bounds__(128) void qprep_kernel(DecodeArgs a) {
   __shared__ float buf[D];
@@ -59,15 +81,7 @@ __global__ __launch_bounds__(128) void qprep_kernel(DecodeArgs a) {
   }
   const uint32_t neg = (a.sign_mask[j >> 5] >> (j & 31)) & 1u;
   qs[j] = qj;
-  buf[j] = flip_if(qj, neg);
-  __syncthreads();
-#pragma clang loop unroll(full)
-  for (int hh = 1; hh < D; hh <<= 1) {
-    const float mine = buf[j], other = buf[j ^ hh];
-    __syncthreads();
-    buf[j] = (j & hh) ? other - mine : mine + other;
-    __syncthreads();
-  }
+  const float hq = fwht128_two_waves(flip_if(qj, neg), j, true, buf);   // H D q
   // Layout per (session, KV head): three sections of 128 x G floats (rotated q,
   // plain q, S q), each ordered [coordinate / 4][query head in group][coordinate % 4]
   // so that one 16-dword scalar load brings 4 coordinates of 4 heads.
@@ -75,7 +89,7 @@ __global__ __launch_bounds__(128) void qprep_kernel(DecodeArgs a) {
   float* w = a.wsq + ((size_t)b * a.n_kv_heads + g) * kQPrepFloats * G;
   const size_t slot = ((size_t)(j >> 2) * G + hg) * 4 + (j & 3);
   // R q = D H D q / sqrt(d); packed-page scores use (R q) * scale2 / sqrt(d).
-  w[slot] = flip_if(buf[j], neg) * (a.scale2 * (1.0f / D));
+  w[slot] = flip_if(hq, neg) * (a.scale2 * (1.0f / D));
   w[D * G + slot] = qj * a.scale2;
   if (a.qjl_s) {
     const float* srow = a.qjl_s + (size_t)j * D;
@@ -876,30 +890,17 @@ __global__ __launch_bounds__(128 * kCombineGroups) void combine_kernel(DecodeArg
   }
   gsum[g][j] = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
   __syncthreads();
-  // o = D H D acc / d / L, the FWHT in place on gsum[0]
-  // (thread j alone reads column j of gsum and writes buf[j] = gsum[0][j])
-  float* buf = gsum[0];
+  // o = D H D acc / d / L; the transform exchanges through gsum[0] (thread j
+  // alone reads column j of gsum, before it writes gsum[0][j])
   uint32_t neg = 0;
+  float ar = 0.f;
   if (tid < D) {
-    float ar = 0.f;
 #pragma clang loop unroll(full)
     for (int q = 0; q < kCombineGroups; ++q) ar += gsum[q][j];
     neg = (a.sign_mask[j >> 5] >> (j & 31)) & 1u;
-    buf[j] = flip_if(ar, neg);
   }
-  __syncthreads();
-#pragma clang loop unroll(full)
-  for (int hh = 1; hh < D; hh <<= 1) {
-    float mine = 0.f, other = 0.f;
-    if (tid < D) {
-      mine = buf[j];
-      other = buf[j ^ hh];
-    }
-    __syncthreads();
-    if (tid < D) buf[j] = (j & hh) ? other - mine : mine + other;
-    __syncthreads();
-  }
-  if (tid < D) o[j] = flip_if(buf[j], neg) * (1.0f / D) / L;
+  const float hv = fwht128_two_waves(flip_if(ar, neg), j, tid < D, gsum[0]);
+  if (tid < D) o[j] = flip_if(hv, neg) * (1.0f / D) / L;
 }
 
 
