@@ -176,31 +176,62 @@ def cpu_baseline(w, layers_data, seconds: float):
     }
 
 
-def decode_loop(w, layers, inputs, queries, outs, wss, steps, dev):
+def decode_loop(w, layers, inputs, queries, outs, wss, steps, dev, graph=False):
     """The decode loop the cache serves: every step appends one token per
     session to every layer (tq_append_kv into a pending fp16 tail page, packed
     in place when its 64th token arrives) and runs decode attention over every
     layer.  Each layer's cache is the workload's, prefilled by encode, plus one
-    pending tail page per (session, KV head) in the format of its last page."""
+    pending tail page per (session, KV head) in the format of its last page.
+
+    With ``graph``, one step (append + decode over every layer, reading the new
+    tokens from a fixed staging buffer) is captured once in a HIP graph and
+    replayed every step after one copy of that step's tokens into the buffer;
+    the copy is inside the timed region."""
     import torch
     import kv_cache_vector_srht_amd as tq
-    caches, news = [], []
+    caches = []
     for l in range(w.n_layers):
         fm = [[list(r) + [tuple(r[-1][:3]) + (True,)] for r in row] for row in w.formats[l]]
         c = tq.Cache(fm, [w.n_tokens] * w.batch, dev)
         k, v = inputs[l]
         tq.encode_kv(layers[l], c, k, v, tok0=0)
         caches.append(c)
-        g = torch.Generator(device=dev).manual_seed(7 + l)
-        news.append(torch.randn((steps, w.batch, w.n_kv_heads, 2, 128), generator=g, device=dev).to(k.dtype))
+    g = torch.Generator(device=dev).manual_seed(7)
+    dtype = inputs[0][0].dtype
+    news = torch.randn((steps, w.n_layers, w.batch, w.n_kv_heads, 2, 128), generator=g,
+                       device=dev).to(dtype)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     t_append = t_decode = 0.0
+    if graph:
+        stage = torch.empty_like(news[0])
+        cap = torch.cuda.Stream(dev)
+        cap.wait_stream(stream)
+        hg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(hg, stream=cap):
+            for l in range(w.n_layers):
+                tq.append_kv(layers[l], caches[l], stage[l, :, :, 0], stage[l, :, :, 1])
+            for l in range(w.n_layers):
+                tq.decode_attention(layers[l], caches[l], queries[l], out=outs[l], workspace=wss[l])
+        torch.cuda.synchronize()
+        for i in range(steps):
+            ev[0].record(stream)
+            stage.copy_(news[i])
+            hg.replay()
+            ev[2].record(stream)
+            ev[2].synchronize()
+            t_decode += ev[0].elapsed_time(ev[2])
+        ms = t_decode / steps
+        del hg
+        return {"steps": steps, "ms_per_step": round(ms, 3),
+                "us_per_layer": round(ms / w.n_layers * 1e3, 2),
+                "tokens_per_s": round(w.batch / (ms / 1e3), 1),
+                "context": f"{w.n_tokens} + 1..{steps} tokens, every layer, one HIP graph per step"}
     for i in range(steps):
         ev[0].record(stream)
         for l in range(w.n_layers):
-            tq.append_kv(layers[l], caches[l], news[l][i, :, :, 0], news[l][i, :, :, 1])
+            tq.append_kv(layers[l], caches[l], news[i, l, :, :, 0], news[i, l, :, :, 1])
         ev[1].record(stream)
         for l in range(w.n_layers):
             tq.decode_attention(layers[l], caches[l], queries[l], out=outs[l], workspace=wss[l])
@@ -452,6 +483,8 @@ def main():
     }
     if args.loop_steps > 0:
         line["decode_loop"] = decode_loop(w, layers, inputs, queries, outs, wss, args.loop_steps, dev)
+        line["decode_loop_graph"] = decode_loop(w, layers, inputs, queries, outs, wss, args.loop_steps,
+                                                dev, graph=True)
     if args.tiering:
         line["tiering"] = tiering(w, layers, inputs, queries, outs, wss, dev)
     if args.codecs:
