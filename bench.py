@@ -17,6 +17,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -165,8 +166,18 @@ def cpu_baseline(w, layers_data, seconds: float):
             if b == w.batch:
                 b, l = 0, (l + 1) % w.n_layers
     unit_count = w.n_layers * w.batch * w.n_kv_heads
+    cpu_model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    cpu_model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": dec_bytes / dec_t / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+        "cpu_model": cpu_model, "affinity_cpus": len(os.sched_getaffinity(0)),
         "sample": (f"{units} of {unit_count} (layer, session, KV head) units, "
                    f"{w.n_tokens} tokens each: encode then decode attention for the "
                    f"{G} query heads; numpy float64"),
@@ -174,6 +185,75 @@ def cpu_baseline(w, layers_data, seconds: float):
         "encode_mtokens_per_s": tokens / (w.n_layers * w.n_kv_heads) / enc_t / 1e6,
         "seconds": enc_t + dec_t,
     }
+
+
+def hbm_stream(dev, mib: int = 4096, reps: int = 20):
+    """Plain streaming references on the same GPU, each over buffers far larger
+    than the 256 MB last-level cache: a device-to-device copy (bytes read plus
+    bytes written) and a float32 sum (bytes read).  Median of ``reps`` HIP-event
+    timed repetitions after two untimed ones."""
+    import numpy as np
+    import torch
+    n = (mib << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    acc = torch.empty((), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) / 1e3)
+        return float(np.median(ts))
+
+    t_copy = timed(lambda: dst.copy_(src))
+    t_read = timed(lambda: torch.sum(src, dim=0, out=acc))
+    nbytes = n * 4
+    del src, dst
+    torch.cuda.synchronize()
+    return {"copy_gbs": round(2 * nbytes / t_copy / 1e9, 1), "read_gbs": round(nbytes / t_read / 1e9, 1),
+            "buffer_bytes": nbytes, "reps": reps,
+            "what": "device copy (read + write bytes) and float32 sum (read bytes), median"}
+
+
+def decode_graph(w, layers, caches, queries, outs, wss, dec_bytes, dev, reps: int = 50):
+    """The decode step of every layer captured once in a HIP graph and replayed
+    ``reps`` times (after three untimed replays); median step time.  The layers'
+    pages together far exceed the last-level cache, so every replay streams HBM."""
+    import numpy as np
+    import torch
+    import kv_cache_vector_srht_amd as tq
+    stream = torch.cuda.current_stream(dev)
+    cap = torch.cuda.Stream(dev)
+    cap.wait_stream(stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        for l in range(w.n_layers):
+            tq.decode_attention(layers[l], caches[l], queries[l], out=outs[l], workspace=wss[l])
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) / 1e3)
+    del g
+    med = float(np.median(ts))
+    return {"reps": reps, "median_ms": round(med * 1e3, 4), "min_ms": round(min(ts) * 1e3, 4),
+            "gbs": round(dec_bytes / med / 1e9, 1),
+            "frac_of_peak": round(dec_bytes / med / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def decode_loop(w, layers, inputs, queries, outs, wss, steps, dev, graph=False):
@@ -481,6 +561,12 @@ def main():
         "decode_bytes_per_step": int(dec_bytes), "encode_bytes_per_step": int(enc_bytes),
         "roofline": roof,
     }
+    line["decode_graph"] = decode_graph(w, layers, caches, queries, outs, wss, dec_bytes, dev)
+    hs = hbm_stream(dev)
+    best = max(hs["copy_gbs"], hs["read_gbs"])
+    hs["decode_frac_of_stream"] = round(dec_gbs / best, 4)
+    hs["encode_frac_of_copy"] = round(achieved / hs["copy_gbs"], 4)
+    line["hbm_stream"] = hs
     if args.loop_steps > 0:
         line["decode_loop"] = decode_loop(w, layers, inputs, queries, outs, wss, args.loop_steps, dev)
         line["decode_loop_graph"] = decode_loop(w, layers, inputs, queries, outs, wss, args.loop_steps,
