@@ -158,7 +158,22 @@ typedef struct tq_cache {
   const uint64_t* pages;     /* device [B][H_kv][max_pages] descriptors          */
   void* pool;                /* device byte pool, 256-byte aligned               */
   uint64_t pool_bytes;       /* pool size; pages outside it are never touched    */
+  const uint8_t* unit_classes; /* host [B][H_kv] or NULL: the page classes each
+                                (session, KV head) holds, in the bits of
+                                page_classes.  Decode attention then launches a
+                                class's workgroups only for the units whose bit
+                                is set (and that page_classes admits), so a
+                                class held by a few heads costs no workgroups
+                                on the others; a unit whose bit is clear has its
+                                pages of that class ignored, as with
+                                page_classes.  Read on the host during the call
+                                only (a captured graph keeps the lists of its
+                                capture).  NULL, or more than
+                                TQ_MAX_LISTED_UNITS units, launches every unit
+                                of every admitted class.                        */
 } tq_cache;
+
+#define TQ_MAX_LISTED_UNITS 512
 
 typedef struct tq_kv_input {
   const void* k;             /* device: element (b, h, t, j) of the call's keys at

@@ -54,7 +54,8 @@ class tq_cache(ctypes.Structure):
     _fields_ = [("n_sessions", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("max_pages", ctypes.c_int32), ("page_classes", ctypes.c_int32),
                 ("n_tokens", ctypes.c_void_p), ("pages", ctypes.c_void_p),
-                ("pool", ctypes.c_void_p), ("pool_bytes", ctypes.c_uint64)]
+                ("pool", ctypes.c_void_p), ("pool_bytes", ctypes.c_uint64),
+                ("unit_classes", ctypes.c_void_p)]
 
 
 class tq_kv_input(ctypes.Structure):
@@ -272,6 +273,34 @@ CACHE_OTHER_PAGES = 2
 CACHE_WIDE_PAGES = 4
 
 
+def _format_classes(f) -> int:
+    kb, vb, q = f[:3]
+    if 1 <= kb <= 4 and 1 <= vb <= 4 and not q:
+        bits = CACHE_COMMON_PAGES
+    elif kb >= 5 and vb >= 5 and not q:
+        bits = CACHE_WIDE_PAGES
+    else:
+        bits = CACHE_OTHER_PAGES
+    if is_pending(f):
+        bits |= CACHE_OTHER_PAGES   # fp16 until it is packed
+    return bits
+
+
+def unit_classes(formats):
+    """The tq_cache.unit_classes array ([B][H_kv] uint8) of a page table with
+    these formats: per (session, KV head), the page classes its pages hold."""
+    import numpy as np
+    B, H = len(formats), len(formats[0])
+    out = np.zeros((B, H), dtype=np.uint8)
+    for b in range(B):
+        for h in range(H):
+            bits = 0
+            for f in formats[b][h]:
+                bits |= _format_classes(f)
+            out[b, h] = bits
+    return out
+
+
 def page_classes(formats) -> int:
     """The tq_cache.page_classes bits of a page table with these formats:
     common = 1-4 bit K and V without QJL; wide = 5-8 bit K and V without QJL;
@@ -281,15 +310,7 @@ def page_classes(formats) -> int:
     for row in formats:
         for fm in row:
             for f in fm:
-                kb, vb, q = f[:3]
-                if 1 <= kb <= 4 and 1 <= vb <= 4 and not q:
-                    bits |= CACHE_COMMON_PAGES
-                elif kb >= 5 and vb >= 5 and not q:
-                    bits |= CACHE_WIDE_PAGES
-                else:
-                    bits |= CACHE_OTHER_PAGES
-                if is_pending(f):
-                    bits |= CACHE_OTHER_PAGES   # fp16 until it is packed
+                bits |= _format_classes(f)
     return bits
 
 
@@ -336,8 +357,10 @@ class Cache:
         self.pages = torch.from_numpy(desc.view(np.int64)).to(self.device)
         self.n_tokens = torch.tensor(list(n_tokens), dtype=torch.int32, device=self.device)
         self.page_classes = page_classes(formats)
+        self.unit_classes = np.ascontiguousarray(unit_classes(formats))
         self.struct = tq_cache(B, H, P, self.page_classes, self.n_tokens.data_ptr(),
-                               self.pages.data_ptr(), self.pool.data_ptr(), self.pool_bytes)
+                               self.pages.data_ptr(), self.pool.data_ptr(), self.pool_bytes,
+                               self.unit_classes.ctypes.data)
 
     def set_n_tokens(self, n_tokens: Sequence[int]) -> None:
         self.n_tokens.copy_(self.n_tokens.new_tensor(list(n_tokens)))
@@ -468,6 +491,7 @@ def retier_pages(layer: Layer, cache: Cache, pages, new_formats, new_offsets=Non
         cache.offsets[b, h, p] = int(off)
     cache.page_classes = page_classes(cache.formats)
     cache.struct.page_classes = cache.page_classes
+    cache.unit_classes[...] = unit_classes(cache.formats)
 
 
 def dequantize(layer: Layer, cache: Cache, which: int, tok0: int, ntok: int, add_qjl: bool = True,

@@ -11,6 +11,8 @@
 // rotation per query head (the Walsh-Hadamard transform factored out of the
 // value sum, as the MLX TurboQuant skill page reports for its Metal kernels,
 // Path A > Optimisations Metal).
+#include <cstring>
+
 #include "tq_device.h"
 
 namespace tq {
@@ -42,6 +44,16 @@ struct DecodeArgs {
   float* wsp;   // [B][H_q][n_splits][kPartialFloats]: m, l, -, -, acc[128]
   float* out;
   float* mass;  // [B][H_q][max_pages] page attention mass, or null
+  // bit u of unit_skip[c]: class c was not launched for unit u = b * H_kv + h
+  // (its partials of that class hold nothing; the combine passes over them)
+  uint32_t unit_skip[3][TQ_MAX_LISTED_UNITS / 32];
+};
+
+// The units (b * H_kv + h) one class's split launch covers, one per grid row;
+// n == 0: the grid is (ranges, H_kv, B) and covers every unit.
+struct UnitList {
+  int32_t n;
+  uint16_t unit[TQ_MAX_LISTED_UNITS];
 };
 
 // In-place Walsh-Hadamard transform (Sylvester order, unnormalised) of 128
@@ -537,14 +549,20 @@ template <int G, int CLASS, bool MASS>
 __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
                                                                   const float* __restrict__ wsq,
                                                                   const uint64_t* __restrict__ pages,
-                                                                  float* __restrict__ wsp) {
+                                                                  float* __restrict__ wsp,
+                                                                  const UnitList list) {
   __shared__ SplitLds<G> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // the other class runs its ranges last page first: a decode loop's fp16
   // tail page is then in the first workgroups dispatched, not behind the
   // rounds of workgroups that find nothing of the class
   const int split = CLASS == 2 ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
-  const int hkv = blockIdx.y, b = blockIdx.z;
+  int hkv = blockIdx.y, b = blockIdx.z;
+  if (list.n > 0) {
+    const int u = list.unit[blockIdx.y];
+    b = u / a.n_kv_heads;
+    hkv = u - b * a.n_kv_heads;
+  }
   const int hq0 = hkv * G;
   // partials [B][H_q][n_partials]: the classes that run, in class order
   const size_t head_stride = (size_t)a.n_partials * kPartialFloats;
@@ -812,9 +830,21 @@ __global__ __launch_bounds__(128 * kCombineGroups) void combine_kernel(DecodeArg
   const int ns = a.n_partials;   // every class that ran
   const float* part = a.wsp + (size_t)row * ns * kPartialFloats;
   float* o = a.out + (size_t)row * D;
+  // the classes whose split launch left this row's unit out: their partials
+  // were never written and count as empty
+  const int unit = b * a.n_kv_heads + (row - b * a.n_q_heads) / a.group;
+  int skip = 0;
+  if (unit < TQ_MAX_LISTED_UNITS) {
+#pragma clang loop unroll(full)
+    for (int c = 0; c < 3; ++c) skip |= (int)((a.unit_skip[c][unit >> 5] >> (unit & 31)) & 1u) << c;
+  }
+  auto m_of = [&](int s) {
+    const int c = s < a.part_base[1] ? 0 : s < a.part_base[2] ? 1 : 2;
+    return (skip >> c) & 1 ? -INFINITY : part[(size_t)s * kPartialFloats];
+  };
   // global max over partials
   float mloc = -INFINITY;
-  for (int s = tid; s < ns; s += nthr) mloc = fmaxf(mloc, part[(size_t)s * kPartialFloats]);
+  for (int s = tid; s < ns; s += nthr) mloc = fmaxf(mloc, m_of(s));
   mloc = wave_max(mloc);
   if (lane == 0) red[wave] = mloc;
   __syncthreads();
@@ -834,7 +864,7 @@ __global__ __launch_bounds__(128 * kCombineGroups) void combine_kernel(DecodeArg
     const int s = base + tid;
     float f = 0.f;
     if (s < ns) {
-      const float ms = part[(size_t)s * kPartialFloats];
+      const float ms = m_of(s);
       f = ms == -INFINITY ? 0.f : exp2f(ms - M);
       wgt[s] = f;
     }
@@ -914,22 +944,23 @@ using namespace tq::dev;
 namespace {
 
 template <int CLASS, bool MASS>
-void launch_split(int G, dim3 grid, dim3 blk, hipStream_t s, const DecodeArgs& a, const uint64_t* pages) {
+void launch_split(int G, dim3 grid, dim3 blk, hipStream_t s, const DecodeArgs& a, const uint64_t* pages,
+                  const UnitList& l) {
   switch (G) {
-    case 1: hipLaunchKernelGGL((split_kernel<1, CLASS, MASS>), grid, blk, 0, s, a, a.wsq, pages, a.wsp); break;
-    case 2: hipLaunchKernelGGL((split_kernel<2, CLASS, MASS>), grid, blk, 0, s, a, a.wsq, pages, a.wsp); break;
-    case 4: hipLaunchKernelGGL((split_kernel<4, CLASS, MASS>), grid, blk, 0, s, a, a.wsq, pages, a.wsp); break;
-    default: hipLaunchKernelGGL((split_kernel<8, CLASS, MASS>), grid, blk, 0, s, a, a.wsq, pages, a.wsp); break;
+    case 1: hipLaunchKernelGGL((split_kernel<1, CLASS, MASS>), grid, blk, 0, s, a, a.wsq, pages, a.wsp, l); break;
+    case 2: hipLaunchKernelGGL((split_kernel<2, CLASS, MASS>), grid, blk, 0, s, a, a.wsq, pages, a.wsp, l); break;
+    case 4: hipLaunchKernelGGL((split_kernel<4, CLASS, MASS>), grid, blk, 0, s, a, a.wsq, pages, a.wsp, l); break;
+    default: hipLaunchKernelGGL((split_kernel<8, CLASS, MASS>), grid, blk, 0, s, a, a.wsq, pages, a.wsp, l); break;
   }
 }
 
 template <int CLASS>
 void launch_split_any(bool mass, int G, dim3 grid, dim3 blk, hipStream_t s, const DecodeArgs& a,
-                      const uint64_t* pages) {
+                      const uint64_t* pages, const UnitList& l) {
   if (mass)
-    launch_split<CLASS, true>(G, grid, blk, s, a, pages);
+    launch_split<CLASS, true>(G, grid, blk, s, a, pages, l);
   else
-    launch_split<CLASS, false>(G, grid, blk, s, a, pages);
+    launch_split<CLASS, false>(G, grid, blk, s, a, pages, l);
 }
 
 int decode_impl(const tq_layer* layer, const tq_cache* cache, const tq_query* query, float* out,
@@ -1003,6 +1034,23 @@ int decode_impl(const tq_layer* layer, const tq_cache* cache, const tq_query* qu
   a.pages_per_split_general = sp.pages_per_split_general;
   a.n_splits_wide = sp.n_splits_wide;
   a.pages_per_split_wide = sp.pages_per_split_wide;
+  // Per-class unit lists from the host's per-unit record: a class's launch
+  // covers only the units that hold it.  Class 0 = common, 1 = wide, 2 = other.
+  UnitList lists[3];
+  const int class_bit[3] = {TQ_CACHE_COMMON_PAGES, TQ_CACHE_WIDE_PAGES, TQ_CACHE_OTHER_PAGES};
+  const int64_t units = (int64_t)cache->n_sessions * cache->n_kv_heads;
+  const bool listed = cache->unit_classes != nullptr && units <= TQ_MAX_LISTED_UNITS;
+  std::memset(a.unit_skip, 0, sizeof(a.unit_skip));
+  for (int c = 0; c < 3; ++c) {
+    lists[c].n = 0;
+    if (!listed) continue;
+    for (int u = 0; u < (int)units; ++u) {
+      if (cache->unit_classes[u] & class_bit[c])
+        lists[c].unit[lists[c].n++] = (uint16_t)u;
+      else
+        a.unit_skip[c][u >> 5] |= 1u << (u & 31);
+    }
+  }
   a.wsq = reinterpret_cast<float*>(workspace);
   a.wsp = a.wsq + (size_t)cache->n_sessions * query->n_q_heads * kQPrepFloats;
   a.out = out;
@@ -1012,20 +1060,21 @@ int decode_impl(const tq_layer* layer, const tq_cache* cache, const tq_query* qu
   const int rows = cache->n_sessions * query->n_q_heads;
   hipLaunchKernelGGL(qprep_kernel, dim3(rows), dim3(128), 0, s, a);
   if ((st = launch_status("query prep"))) return st;
-  const dim3 grid(sp.n_splits, cache->n_kv_heads, cache->n_sessions);
-  const dim3 ggrid(sp.n_splits_general, cache->n_kv_heads, cache->n_sessions);
-  const dim3 wgrid(sp.n_splits_wide, cache->n_kv_heads, cache->n_sessions);
+  // one grid row per listed unit, else (H_kv, B) over every unit
+  auto grid_of = [&](int n_splits, const UnitList& l) {
+    return listed ? dim3(n_splits, l.n, 1) : dim3(n_splits, cache->n_kv_heads, cache->n_sessions);
+  };
   const dim3 blk(64 * kDecodeWaves);
-  if (run_common) {
-    launch_split_any<0>(mass, G, grid, blk, s, a, cache->pages);
+  if (run_common && (!listed || lists[0].n > 0)) {
+    launch_split_any<0>(mass, G, grid_of(sp.n_splits, lists[0]), blk, s, a, cache->pages, lists[0]);
     if ((st = launch_status("split (common pages)"))) return st;
   }
-  if (run_wide) {
-    launch_split_any<1>(mass, G, wgrid, blk, s, a, cache->pages);
+  if (run_wide && (!listed || lists[1].n > 0)) {
+    launch_split_any<1>(mass, G, grid_of(sp.n_splits_wide, lists[1]), blk, s, a, cache->pages, lists[1]);
     if ((st = launch_status("split (wide pages)"))) return st;
   }
-  if (run_other) {
-    launch_split_any<2>(mass, G, ggrid, blk, s, a, cache->pages);
+  if (run_other && (!listed || lists[2].n > 0)) {
+    launch_split_any<2>(mass, G, grid_of(sp.n_splits_general, lists[2]), blk, s, a, cache->pages, lists[2]);
     if ((st = launch_status("split (other pages)"))) return st;
   }
   hipLaunchKernelGGL(combine_kernel, dim3(rows), dim3(128 * kCombineGroups), 0, s, a);

@@ -617,6 +617,13 @@ int check_cache(const tq_cache* C) {
   if (C->pool_bytes == 0) return fail(TQ_ERR_INVALID_ARG, "empty pool");
   if (C->page_classes & ~(TQ_CACHE_COMMON_PAGES | TQ_CACHE_OTHER_PAGES | TQ_CACHE_WIDE_PAGES))
     return fail(TQ_ERR_INVALID_ARG, "unknown page_classes bits 0x%x", C->page_classes);
+  if (C->unit_classes) {
+    const int64_t units = (int64_t)C->n_sessions * C->n_kv_heads;
+    for (int64_t u = 0; u < units; ++u)
+      if (C->unit_classes[u] & ~(TQ_CACHE_COMMON_PAGES | TQ_CACHE_OTHER_PAGES | TQ_CACHE_WIDE_PAGES))
+        return fail(TQ_ERR_INVALID_ARG, "unknown unit_classes bits 0x%x at unit %lld",
+                    (unsigned)C->unit_classes[u], (long long)u);
+  }
   return TQ_OK;
 }
 

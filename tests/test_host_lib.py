@@ -235,10 +235,14 @@ def test_decode_validation(L):
         (dict(layer=_fake_layer(head_dim=256)), -2),
         (dict(cache=_fake_cache(page_classes=8)), -1),
     ]
+    # a per-unit class record with an unknown bit (unit 7 of 8)
+    bad_units = (ctypes.c_uint8 * 8)(1, 1, 2, 4, 7, 0, 1, 8)
+    cases.append((dict(cache=_fake_cache(unit_classes=ctypes.addressof(bad_units))), -1))
     for case, want in cases:
         st = _decode(L, case.get("layer", _fake_layer()), case.get("cache", _fake_cache()),
                      case.get("ws", 1 << 30), **case.get("kw", {}))
         assert st == want, (case, st, L.tq_last_error())
+    assert b"unit 7" in L.tq_last_error()
 
 
 def test_decode_mass_validation(L):
@@ -338,3 +342,21 @@ def test_page_classes_bits():
     w3 = W.make_workload(3, {"n_tokens": 128, "batch": 1})
     assert tq.page_classes(w3.formats[0]) == tq.CACHE_COMMON_PAGES
     assert tq.page_classes(w3.formats[2]) == tq.CACHE_COMMON_PAGES | tq.CACHE_WIDE_PAGES
+
+
+def test_unit_classes_record():
+    """Per (session, KV head) classes; their union is the cache's page classes."""
+    import numpy as np
+    import kv_cache_vector_srht_amd as tq
+    fm = [[[W.packed(3, 2)], [W.packed(8, 6), W.FP16], [W.packed(2, 2, True)], [(3, 2, False, True)]]]
+    got = tq.unit_classes(fm)
+    assert got.dtype == np.uint8 and got.shape == (1, 4)
+    assert got.tolist() == [[tq.CACHE_COMMON_PAGES, tq.CACHE_WIDE_PAGES | tq.CACHE_OTHER_PAGES,
+                             tq.CACHE_OTHER_PAGES, tq.CACHE_COMMON_PAGES | tq.CACHE_OTHER_PAGES]]
+    w3 = W.make_workload(3, {"n_tokens": 128, "batch": 2})
+    for l in range(w3.n_layers):
+        u = tq.unit_classes(w3.formats[l])
+        assert int(np.bitwise_or.reduce(u.reshape(-1))) == tq.page_classes(w3.formats[l])
+        # the hub heads hold the wide pages, the same heads in every session
+        assert (u[0] == u[1]).all()
+
