@@ -134,6 +134,7 @@ struct SplitLds {
   float w[kDecodeWaves][PT * G];           // softmax weights of the current page
   float red[kDecodeWaves][G * D];          // workgroup reduction
   float stat[kDecodeWaves][2][G];          // m, l per wave
+  uint64_t desc[kMaxPagesPerSplit];        // the range's page descriptors, read once
 };
 
 __device__ __forceinline__ int pair_offset(int b) {
@@ -510,20 +511,31 @@ __device__ __forceinline__ void value_accum_fp16(const char* page, int lane, con
 
 // Online-softmax update of one page for G heads.  s: log2-domain scores of
 // this lane's token (-inf when masked); on return s holds p = 2^(s - m) and
-// alpha the rescale of the running sums.
+// alpha the rescale of the running sums.  m is a wave-uniform reference, not
+// necessarily the running maximum: it moves (to the exact maximum, with a
+// rescale) only when a score exceeds it by more than kSoftmaxSlack, so most
+// pages skip the 64-lane maximum reduction.  Every weight stays below
+// 2^kSoftmaxSlack, far from float32 overflow even summed over 2^31 tokens;
+// the partials carry their reference, and the log-sum-exp merges are exact
+// for any reference, so only rounding differs from the running-maximum form.
+constexpr float kSoftmaxSlack = 32.f;
+
 template <int G>
 __device__ __forceinline__ void softmax_update(float (&s)[G], float (&m)[G], float (&l)[G],
                                                float (&alpha)[G]) {
 #pragma clang loop unroll(full)
   for (int h = 0; h < G; ++h) {
-    const float mx = wave_max(s[h]);
-    const float mn = fmaxf(m[h], mx);
+    // m = -inf (nothing seen yet): any unmasked lane moves it
+    const bool up = __ballot(s[h] > m[h] + kSoftmaxSlack) != 0ull;
+    const float mn = up ? fmaxf(m[h], wave_max(s[h])) : m[h];
+    // the hardware exponential: a weight below 2^-126 of the reference (which
+    // some token reached at weight 1) flushes to zero, far below any effect
     if (mn == -INFINITY) {
       alpha[h] = 1.f;
       s[h] = 0.f;
     } else {
-      alpha[h] = exp2f(m[h] - mn);
-      s[h] = exp2f(s[h] - mn);
+      alpha[h] = up ? __builtin_amdgcn_exp2f(m[h] - mn) : 1.f;
+      s[h] = __builtin_amdgcn_exp2f(s[h] - mn);
     }
     m[h] = mn;
     l[h] = fmaf(l[h], alpha[h], s[h]);
@@ -581,11 +593,14 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
     // descriptors are read in parallel, one per thread)
     bool mine = false, coded = false;
     for (int p = p_begin + tid; p < p_end; p += blockDim.x) {
-      const PageDesc pd = read_desc(ptab[p]);
+      const uint64_t raw = ptab[p];
+      sm.desc[p - p_begin] = raw;   // the page loop reads it from LDS
+      const PageDesc pd = read_desc(raw);
       const bool m = page_class(pd.kb, pd.vb, pd.qjl) == CLASS;
       mine |= m;
       coded |= m && pd.kb != 0;
     }
+    __syncthreads();   // the cached descriptors are visible to every wave
     need_tables = CLASS != 2 || __syncthreads_or(coded);
     if (!__syncthreads_or(mine)) {
       if (tid < G) {
@@ -640,7 +655,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
   const int q4 = lane >> 4, i16 = lane & 15;
 
   for (int p = p_begin + wave; p < p_end; p += kDecodeWaves) {
-    const PageDesc pd = read_desc(ptab[p]);
+    const PageDesc pd = read_desc(sm.desc[p - p_begin]);
     const int kb = pd.kb, vb = pd.vb;
     const bool qjl = pd.qjl;
     const uint64_t off = pd.off;

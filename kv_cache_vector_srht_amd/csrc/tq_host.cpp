@@ -566,6 +566,7 @@ SplitPlan split_plan(int n_sessions, int n_kv_heads, int max_pages) {
   int64_t total_pages = units * max_pages;
   int64_t pps = (total_pages + kTargetSplitGroups - 1) / kTargetSplitGroups;
   if (pps < kDecodeWaves) pps = kDecodeWaves;
+  if (pps > kMaxPagesPerSplit) pps = kMaxPagesPerSplit;
   if (pps > max_pages) pps = max_pages;
   SplitPlan sp;
   sp.pages_per_split = (int)pps;

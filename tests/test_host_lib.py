@@ -161,6 +161,11 @@ def test_cache_bytes_and_workspace(L):
     n = L.tq_decode_workspace_bytes(ctypes.byref(c), 32)
     # 32 units x 512 pages over ~1024 groups: 16 pages per split, 32 splits
     assert n == 4 * (4 * 32 * 384 + 4 * 32 * (32 + 128 + 64) * 132)
+    # one unit of 300000 pages: ranges are capped at 256 pages (the split
+    # kernel keeps a range's descriptors in LDS): 1172 common, 4688 wide
+    # (64-page) and 2344 other (128-page) ranges
+    big = tq.tq_cache(1, 1, 300000, 0, None, None, None, 0)
+    assert L.tq_decode_workspace_bytes(ctypes.byref(big), 1) == 4 * (384 + (1172 + 4688 + 2344) * 132)
     c0 = tq.tq_cache(0, 8, 512, 0, None, None, None, 0)
     assert L.tq_decode_workspace_bytes(ctypes.byref(c0), 32) == 0
 
