@@ -12,6 +12,7 @@
 // value sum, as the MLX TurboQuant skill page reports for its Metal kernels,
 // Path A > Optimisations Metal).
 #include <cstring>
+#include <type_traits>
 
 #include "tq_device.h"
 
@@ -49,11 +50,13 @@ struct DecodeArgs {
   uint32_t unit_skip[3][TQ_MAX_LISTED_UNITS / 32];
 };
 
-// The units (b * H_kv + h) one class's split launch covers, one per grid row;
-// n == 0: the grid is (ranges, H_kv, B) and covers every unit.
+// The units (b * H_kv + h) one split launch covers.  A single-class launch
+// takes one unit per grid row; the merged common + wide launch (CLASS 3) takes
+// the wide units unit[0, n_first) and then the common units unit[n_first, n).
+// n == 0: every unit, in (B, H_kv) order.
 struct UnitList {
-  int32_t n;
-  uint16_t unit[TQ_MAX_LISTED_UNITS];
+  int32_t n, n_first;
+  uint16_t unit[2 * TQ_MAX_LISTED_UNITS];
 };
 
 // In-place Walsh-Hadamard transform (Sylvester order, unnormalised) of 128
@@ -547,7 +550,9 @@ __device__ __forceinline__ void softmax_update(float (&s)[G], float (&m)[G], flo
 //   0 common: k_bits, v_bits <= 4, no QJL;
 //   1 wide:   k_bits, v_bits >= 5, no QJL (the few important heads);
 //   2 other:  fp16 pages, QJL keys and mixed widths.
-// Each writes its own partials; the combine merges them.
+// Each writes its own partials; the combine merges them.  When a layer holds
+// both common and wide pages, one launch (CLASS 3) runs the two classes' blocks
+// side by side, so that the wide pages' latency hides behind common work.
 __device__ __forceinline__ int page_class(int kb, int vb, bool qjl) {
   if (kb >= 1 && kb <= 4 && vb >= 1 && vb <= 4 && !qjl) return 0;
   if (kb >= 5 && vb >= 5 && !qjl) return 1;
@@ -558,7 +563,8 @@ __device__ __forceinline__ int page_class(int kb, int vb, bool qjl) {
 // softmax numerator (m + log2 of the page's sum of 2^(s - m)); the combine
 // turns it into the page's attention mass.
 template <int G, int CLASS, bool MASS>
-__global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
+__global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(CLASS == 3 ? 4 : 1)))
+void split_kernel(DecodeArgs a,
                                                                   const float* __restrict__ wsq,
                                                                   const uint64_t* __restrict__ pages,
                                                                   float* __restrict__ wsp,
@@ -568,19 +574,42 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
   // the other class runs its ranges last page first: a decode loop's fp16
   // tail page is then in the first workgroups dispatched, not behind the
   // rounds of workgroups that find nothing of the class
-  const int split = CLASS == 2 ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
-  int hkv = blockIdx.y, b = blockIdx.z;
-  if (list.n > 0) {
-    const int u = list.unit[blockIdx.y];
+  int split, hkv, b, cls = CLASS;
+  if constexpr (CLASS == 3) {
+    // merged common + wide launch, one block per (unit, range), the wide
+    // class's blocks first so that its few long pages start early
+    const int wide_blocks = (list.n > 0 ? list.n_first : a.n_sessions * a.n_kv_heads) * a.n_splits_wide;
+    int i = blockIdx.x, ui;
+    if (i < wide_blocks) {
+      cls = 1;
+      ui = i / a.n_splits_wide;
+      split = i - ui * a.n_splits_wide;
+    } else {
+      cls = 0;
+      i -= wide_blocks;
+      ui = i / a.n_splits;
+      split = i - ui * a.n_splits;
+      if (list.n > 0) ui += list.n_first;
+    }
+    const int u = list.n > 0 ? list.unit[ui] : ui;
     b = u / a.n_kv_heads;
     hkv = u - b * a.n_kv_heads;
+  } else {
+    split = CLASS == 2 ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
+    hkv = blockIdx.y;
+    b = blockIdx.z;
+    if (list.n > 0) {
+      const int u = list.unit[blockIdx.y];
+      b = u / a.n_kv_heads;
+      hkv = u - b * a.n_kv_heads;
+    }
   }
   const int hq0 = hkv * G;
   // partials [B][H_q][n_partials]: the classes that run, in class order
   const size_t head_stride = (size_t)a.n_partials * kPartialFloats;
   float* part = wsp + ((size_t)b * a.n_q_heads + hq0) * head_stride +
-                ((size_t)a.part_base[CLASS] + split) * kPartialFloats;
-  const int pps = CLASS == 0 ? a.pages_per_split : CLASS == 1 ? a.pages_per_split_wide : a.pages_per_split_general;
+                ((size_t)a.part_base[cls] + split) * kPartialFloats;
+  const int pps = cls == 0 ? a.pages_per_split : cls == 1 ? a.pages_per_split_wide : a.pages_per_split_general;
 
   const int ntok = max(0, a.n_tokens[b]);
   const int npages = min(a.max_pages, (ntok + PT - 1) / PT);   // never past the table row
@@ -596,7 +625,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
       const uint64_t raw = ptab[p];
       sm.desc[p - p_begin] = raw;   // the page loop reads it from LDS
       const PageDesc pd = read_desc(raw);
-      const bool m = page_class(pd.kb, pd.vb, pd.qjl) == CLASS;
+      const bool m = page_class(pd.kb, pd.vb, pd.qjl) == cls;
       mine |= m;
       coded |= m && pd.kb != 0;
     }
@@ -654,127 +683,143 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void split_kernel(DecodeArgs a,
   float* wv = sm.w[wave];
   const int q4 = lane >> 4, i16 = lane & 15;
 
-  for (int p = p_begin + wave; p < p_end; p += kDecodeWaves) {
-    const PageDesc pd = read_desc(sm.desc[p - p_begin]);
-    const int kb = pd.kb, vb = pd.vb;
-    const bool qjl = pd.qjl;
-    const uint64_t off = pd.off;
-    if (!pd.present || off + page_size_dev(kb, vb, qjl) > a.pool_bytes) continue;
-    if (kb == 0 ? (vb != 0 || qjl) : (kb > 8 || vb < 1 || vb > 8)) continue;
-    if (qjl && a.qjl_s == nullptr) continue;
-    if (page_class(kb, vb, qjl) != CLASS) continue;
-    if (CLASS != 0 && ((a.k_polar && kb > 4) || (a.v_polar && vb > 4))) continue;   // no polar pair table
-    const char* page = a.pool + off;
-    const int valid = min(PT, ntok - p * PT);
-    float s[G], alpha[G];
-    const char* vblk = page + 1024 * kb + 256;
-    // the norms (and the QJL scale) are loaded with the codes, not after them
-    float nk = 1.f, nv = 1.f, gq = 0.f;
-    if (kb != 0) {
-      nk = reinterpret_cast<const float*>(page + 1024 * kb)[lane];
-      const char* vb0 = vblk + (qjl ? 1280 : 0);
-      nv = reinterpret_cast<const float*>(vb0 + 1024 * vb)[lane];
-      if (CLASS == 2 && qjl) gq = reinterpret_cast<const float*>(vblk + 1024)[lane];
-    }
-    if (CLASS == 2 && kb == 0) {
-      key_scores_fp16<G>(page, lane, qrow + D * G, s);
-    } else {
-      if constexpr (CLASS == 0) {
-        switch (kb) {
-          case 1: key_scores<1, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
-          case 2: key_scores<2, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
-          case 3: key_scores<3, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
-          default: key_scores<4, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
+  // The page loop, compiled for page class PC.  The merged launch runs a
+  // common-class and a wide-class copy side by side (a uniform branch), each
+  // with its own code; it is held to 4 waves per SIMD (a few spills in the
+  // wide copy, cheaper than a fourth of the waves).
+  auto page_loop = [&](auto pc_tag) {
+    constexpr int PC = decltype(pc_tag)::value;
+    for (int p = p_begin + wave; p < p_end; p += kDecodeWaves) {
+      const PageDesc pd = read_desc(sm.desc[p - p_begin]);
+      const int kb = pd.kb, vb = pd.vb;
+      const bool qjl = pd.qjl;
+      const uint64_t off = pd.off;
+      if (!pd.present || off + page_size_dev(kb, vb, qjl) > a.pool_bytes) continue;
+      if (kb == 0 ? (vb != 0 || qjl) : (kb > 8 || vb < 1 || vb > 8)) continue;
+      if (qjl && a.qjl_s == nullptr) continue;
+      if (page_class(kb, vb, qjl) != PC) continue;
+      if (PC != 0 && ((a.k_polar && kb > 4) || (a.v_polar && vb > 4))) continue;   // no polar pair table
+      const char* page = a.pool + off;
+      const int valid = min(PT, ntok - p * PT);
+      float s[G], alpha[G];
+      const char* vblk = page + 1024 * kb + 256;
+      // the norms (and the QJL scale) are loaded with the codes, not after them
+      float nk = 1.f, nv = 1.f, gq = 0.f;
+      if (kb != 0) {
+        nk = reinterpret_cast<const float*>(page + 1024 * kb)[lane];
+        const char* vb0 = vblk + (qjl ? 1280 : 0);
+        nv = reinterpret_cast<const float*>(vb0 + 1024 * vb)[lane];
+        if (PC == 2 && qjl) gq = reinterpret_cast<const float*>(vblk + 1024)[lane];
+      }
+      if (PC == 2 && kb == 0) {
+        key_scores_fp16<G>(page, lane, qrow + D * G, s);
+      } else {
+        if constexpr (PC == 0) {
+          switch (kb) {
+            case 1: key_scores<1, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
+            case 2: key_scores<2, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
+            case 3: key_scores<3, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
+            default: key_scores<4, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
+          }
+        } else if constexpr (PC == 1) {
+          switch (kb) {
+            case 5: key_scores_wide<5, G>(page, lane, qrow, sm.kcent, s); break;
+            case 6: key_scores_wide<6, G>(page, lane, qrow, sm.kcent, s); break;
+            case 7: key_scores_wide<7, G>(page, lane, qrow, sm.kcent, s); break;
+            default: key_scores_wide<8, G>(page, lane, qrow, sm.kcent, s); break;
+          }
+        } else {
+          switch (kb) {
+            case 1: key_scores<1, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
+            case 2: key_scores<2, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
+            case 3: key_scores<3, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
+            case 4: key_scores<4, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
+            case 5: key_scores_wide<5, G>(page, lane, qrow, sm.kcent, s); break;
+            case 6: key_scores_wide<6, G>(page, lane, qrow, sm.kcent, s); break;
+            case 7: key_scores_wide<7, G>(page, lane, qrow, sm.kcent, s); break;
+            default: key_scores_wide<8, G>(page, lane, qrow, sm.kcent, s); break;
+          }
         }
-      } else if constexpr (CLASS == 1) {
-        switch (kb) {
-          case 5: key_scores_wide<5, G>(page, lane, qrow, sm.kcent, s); break;
-          case 6: key_scores_wide<6, G>(page, lane, qrow, sm.kcent, s); break;
-          case 7: key_scores_wide<7, G>(page, lane, qrow, sm.kcent, s); break;
-          default: key_scores_wide<8, G>(page, lane, qrow, sm.kcent, s); break;
+  #pragma clang loop unroll(full)
+        for (int h = 0; h < G; ++h) s[h] *= nk;
+        if (PC == 2 && qjl) {
+          float t[G];
+          qjl_scores<G>(vblk, lane, qrow + 2 * D * G, t);
+  #pragma clang loop unroll(full)
+          for (int h = 0; h < G; ++h) s[h] = fmaf(gq, t[h], s[h]);
+          vblk += 1280;
+        }
+      }
+  #pragma clang loop unroll(full)
+      for (int h = 0; h < G; ++h)
+        if (lane >= valid) s[h] = -INFINITY;
+      softmax_update<G>(s, m, l, alpha);
+      if constexpr (MASS) {
+        float* mrow = a.mass + ((size_t)b * a.n_q_heads + hq0) * a.max_pages + p;
+  #pragma clang loop unroll(full)
+        for (int h = 0; h < G; ++h) {
+          const float ps = wave_sum(s[h]);
+          if (lane == 0) mrow[(size_t)h * a.max_pages] = ps > 0.f ? m[h] + log2f(ps) : -INFINITY;
+        }
+      }
+      // the running sums need rescaling only when some head's maximum moved
+      // (alpha is wave-uniform, so is the branch)
+      bool moved = false;
+  #pragma clang loop unroll(full)
+      for (int h = 0; h < G; ++h) moved |= alpha[h] != 1.f;
+      if (moved) {
+  #pragma clang loop unroll(full)
+        for (int h = 0; h < G; ++h)
+  #pragma clang loop unroll(full)
+          for (int e = 0; e < 8; ++e) acc[h][e] *= alpha[h];
+      }
+  #pragma clang loop unroll(full)
+      for (int h = 0; h < G; ++h) wv[lane * G + h] = s[h] * nv;
+      wave_lds_sync();
+      if (PC == 2 && kb == 0) {
+        uint32_t dm[8];
+        const uint32_t dword = a.sign_mask[i16 >> 2];
+  #pragma clang loop unroll(full)
+        for (int e = 0; e < 8; ++e) dm[e] = (dword >> (8 * (i16 & 3) + e)) & 1u;
+        value_accum_fp16<G>(page, lane, wv, dm, acc);
+      } else if constexpr (PC == 0) {
+        switch (vb) {
+          case 1: value_accum<1, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
+          case 2: value_accum<2, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
+          case 3: value_accum<3, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
+          default: value_accum<4, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
+        }
+      } else if constexpr (PC == 1) {
+        switch (vb) {
+          case 5: value_accum_wide<5, G>(vblk, lane, wv, sm.vcent, acc); break;
+          case 6: value_accum_wide<6, G>(vblk, lane, wv, sm.vcent, acc); break;
+          case 7: value_accum_wide<7, G>(vblk, lane, wv, sm.vcent, acc); break;
+          default: value_accum_wide<8, G>(vblk, lane, wv, sm.vcent, acc); break;
         }
       } else {
-        switch (kb) {
-          case 1: key_scores<1, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
-          case 2: key_scores<2, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
-          case 3: key_scores<3, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
-          case 4: key_scores<4, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
-          case 5: key_scores_wide<5, G>(page, lane, qrow, sm.kcent, s); break;
-          case 6: key_scores_wide<6, G>(page, lane, qrow, sm.kcent, s); break;
-          case 7: key_scores_wide<7, G>(page, lane, qrow, sm.kcent, s); break;
-          default: key_scores_wide<8, G>(page, lane, qrow, sm.kcent, s); break;
+        switch (vb) {
+          case 1: value_accum<1, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
+          case 2: value_accum<2, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
+          case 3: value_accum<3, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
+          case 4: value_accum<4, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
+          case 5: value_accum_wide<5, G>(vblk, lane, wv, sm.vcent, acc); break;
+          case 6: value_accum_wide<6, G>(vblk, lane, wv, sm.vcent, acc); break;
+          case 7: value_accum_wide<7, G>(vblk, lane, wv, sm.vcent, acc); break;
+          default: value_accum_wide<8, G>(vblk, lane, wv, sm.vcent, acc); break;
         }
       }
-#pragma clang loop unroll(full)
-      for (int h = 0; h < G; ++h) s[h] *= nk;
-      if (CLASS == 2 && qjl) {
-        float t[G];
-        qjl_scores<G>(vblk, lane, qrow + 2 * D * G, t);
-#pragma clang loop unroll(full)
-        for (int h = 0; h < G; ++h) s[h] = fmaf(gq, t[h], s[h]);
-        vblk += 1280;
-      }
+      wave_lds_sync();
     }
-#pragma clang loop unroll(full)
-    for (int h = 0; h < G; ++h)
-      if (lane >= valid) s[h] = -INFINITY;
-    softmax_update<G>(s, m, l, alpha);
-    if constexpr (MASS) {
-      float* mrow = a.mass + ((size_t)b * a.n_q_heads + hq0) * a.max_pages + p;
-#pragma clang loop unroll(full)
-      for (int h = 0; h < G; ++h) {
-        const float ps = wave_sum(s[h]);
-        if (lane == 0) mrow[(size_t)h * a.max_pages] = ps > 0.f ? m[h] + log2f(ps) : -INFINITY;
-      }
-    }
-    // the running sums need rescaling only when some head's maximum moved
-    // (alpha is wave-uniform, so is the branch)
-    bool moved = false;
-#pragma clang loop unroll(full)
-    for (int h = 0; h < G; ++h) moved |= alpha[h] != 1.f;
-    if (moved) {
-#pragma clang loop unroll(full)
-      for (int h = 0; h < G; ++h)
-#pragma clang loop unroll(full)
-        for (int e = 0; e < 8; ++e) acc[h][e] *= alpha[h];
-    }
-#pragma clang loop unroll(full)
-    for (int h = 0; h < G; ++h) wv[lane * G + h] = s[h] * nv;
-    wave_lds_sync();
-    if (CLASS == 2 && kb == 0) {
-      uint32_t dm[8];
-      const uint32_t dword = a.sign_mask[i16 >> 2];
-#pragma clang loop unroll(full)
-      for (int e = 0; e < 8; ++e) dm[e] = (dword >> (8 * (i16 & 3) + e)) & 1u;
-      value_accum_fp16<G>(page, lane, wv, dm, acc);
-    } else if constexpr (CLASS == 0) {
-      switch (vb) {
-        case 1: value_accum<1, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
-        case 2: value_accum<2, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
-        case 3: value_accum<3, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
-        default: value_accum<4, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
-      }
-    } else if constexpr (CLASS == 1) {
-      switch (vb) {
-        case 5: value_accum_wide<5, G>(vblk, lane, wv, sm.vcent, acc); break;
-        case 6: value_accum_wide<6, G>(vblk, lane, wv, sm.vcent, acc); break;
-        case 7: value_accum_wide<7, G>(vblk, lane, wv, sm.vcent, acc); break;
-        default: value_accum_wide<8, G>(vblk, lane, wv, sm.vcent, acc); break;
-      }
-    } else {
-      switch (vb) {
-        case 1: value_accum<1, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
-        case 2: value_accum<2, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
-        case 3: value_accum<3, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
-        case 4: value_accum<4, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
-        case 5: value_accum_wide<5, G>(vblk, lane, wv, sm.vcent, acc); break;
-        case 6: value_accum_wide<6, G>(vblk, lane, wv, sm.vcent, acc); break;
-        case 7: value_accum_wide<7, G>(vblk, lane, wv, sm.vcent, acc); break;
-        default: value_accum_wide<8, G>(vblk, lane, wv, sm.vcent, acc); break;
-      }
-    }
-    wave_lds_sync();
+  };
+  if constexpr (CLASS == 3) {
+    if (cls == 0)
+      page_loop(std::integral_constant<int, 0>{});
+    else
+      page_loop(std::integral_constant<int, 1>{});
+  } else {
+    page_loop(std::integral_constant<int, CLASS>{});
   }
+
 
   // ---- workgroup reduction: waves, then token quarters.
 #pragma clang loop unroll(full)
@@ -1051,13 +1096,13 @@ int decode_impl(const tq_layer* layer, const tq_cache* cache, const tq_query* qu
   a.pages_per_split_wide = sp.pages_per_split_wide;
   // Per-class unit lists from the host's per-unit record: a class's launch
   // covers only the units that hold it.  Class 0 = common, 1 = wide, 2 = other.
-  UnitList lists[3];
+  UnitList lists[3];   // n_first unused by single-class launches
   const int class_bit[3] = {TQ_CACHE_COMMON_PAGES, TQ_CACHE_WIDE_PAGES, TQ_CACHE_OTHER_PAGES};
   const int64_t units = (int64_t)cache->n_sessions * cache->n_kv_heads;
   const bool listed = cache->unit_classes != nullptr && units <= TQ_MAX_LISTED_UNITS;
   std::memset(a.unit_skip, 0, sizeof(a.unit_skip));
   for (int c = 0; c < 3; ++c) {
-    lists[c].n = 0;
+    lists[c].n = lists[c].n_first = 0;
     if (!listed) continue;
     for (int u = 0; u < (int)units; ++u) {
       if (cache->unit_classes[u] & class_bit[c])
@@ -1080,11 +1125,25 @@ int decode_impl(const tq_layer* layer, const tq_cache* cache, const tq_query* qu
     return listed ? dim3(n_splits, l.n, 1) : dim3(n_splits, cache->n_kv_heads, cache->n_sessions);
   };
   const dim3 blk(64 * kDecodeWaves);
-  if (run_common && (!listed || lists[0].n > 0)) {
+  const bool go_common = run_common && (!listed || lists[0].n > 0);
+  const bool go_wide = run_wide && (!listed || lists[1].n > 0);
+  if (go_common && go_wide) {
+    // one launch: the wide units' blocks, then the common units' blocks
+    UnitList merged;
+    merged.n = merged.n_first = 0;
+    int64_t blocks = units * ((int64_t)sp.n_splits + sp.n_splits_wide);
+    if (listed) {
+      for (int i = 0; i < lists[1].n; ++i) merged.unit[merged.n++] = lists[1].unit[i];
+      merged.n_first = merged.n;
+      for (int i = 0; i < lists[0].n; ++i) merged.unit[merged.n++] = lists[0].unit[i];
+      blocks = (int64_t)lists[1].n * sp.n_splits_wide + (int64_t)lists[0].n * sp.n_splits;
+    }
+    launch_split_any<3>(mass, G, dim3((unsigned)blocks), blk, s, a, cache->pages, merged);
+    if ((st = launch_status("split (common and wide pages)"))) return st;
+  } else if (go_common) {
     launch_split_any<0>(mass, G, grid_of(sp.n_splits, lists[0]), blk, s, a, cache->pages, lists[0]);
     if ((st = launch_status("split (common pages)"))) return st;
-  }
-  if (run_wide && (!listed || lists[1].n > 0)) {
+  } else if (go_wide) {
     launch_split_any<1>(mass, G, grid_of(sp.n_splits_wide, lists[1]), blk, s, a, cache->pages, lists[1]);
     if ((st = launch_status("split (wide pages)"))) return st;
   }

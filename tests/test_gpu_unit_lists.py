@@ -146,3 +146,37 @@ def test_admitted_class_held_by_no_unit(dev):
     out7, mass7 = _decode(tq, layer, cache, q)
     assert np.array_equal(out1, out7) and np.array_equal(mass1, mass7)
 
+
+
+def test_more_units_than_listed(dev):
+    """528 (session, KV head) units, above the 512 a launch can list: the
+    record is ignored and every class's grid covers every unit; sampled units
+    against the oracle."""
+    import kv_cache_vector_srht_amd as tq
+    B, H, G = 66, 8, 1
+    plans = [[C3, W6], [Q2, C1], [W8, W.FP16], [C1, C3]]
+    fm = [[list(plans[(b * H + h) % 4]) for h in range(H)] for b in range(B)]
+    n_tokens = [128 if b % 3 else 100 for b in range(B)]
+    for b in range(B):
+        if n_tokens[b] % 64:
+            for h in range(H):
+                fm[b][h][1] = W.FP16
+    w = W.make_workload(2, {"n_tokens": 128, "batch": B, "n_kv_heads": H, "n_q_heads": H * G,
+                            "sink_tokens": 0, "dtype": "float16"})
+    signs, S = W.rotation_signs(42, 0), W.qjl_matrix(42, 0)
+    layer = tq.Layer(signs, dev, S)
+    cache = tq.Cache(fm, n_tokens, dev)
+    k, v = W.make_kv(w, 0, device=dev)
+    q = W.make_query(w, 0, device=dev)
+    tq.encode_kv(layer, cache, k, v)
+    print("decode over 528 units", flush=True)
+    out = _np(tq.decode_attention(layer, cache, q))
+    torch.cuda.synchronize()
+    pool = _np(cache.pool)
+    kh, vh, qh = _np(k).astype(np.float64), _np(v).astype(np.float64), _np(q).astype(np.float64)
+    t = Tally()
+    for b, h in [(0, 0), (0, 1), (1, 2), (33, 7), (64, 5), (65, 3), (65, 6)]:
+        n = n_tokens[b]
+        Kh, Vh = compare_unit_full(pool, cache.offsets, b, h, kh[b, h, :n], vh[b, h, :n], fm[b][h], signs, S, t)
+        compare_attention(out[b, h:h + 1], qh[b, h:h + 1], Kh, Vh, t)
+    t.check()
