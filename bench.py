@@ -269,13 +269,16 @@ def decode_loop(w, layers, inputs, queries, outs, wss, steps, dev, graph=False):
     the copy is inside the timed region."""
     import torch
     import kv_cache_vector_srht_amd as tq
-    caches = []
+    caches, wss = [], []
     for l in range(w.n_layers):
         fm = [[list(r) + [tuple(r[-1][:3]) + (True,)] for r in row] for row in w.formats[l]]
         c = tq.Cache(fm, [w.n_tokens] * w.batch, dev)
         k, v = inputs[l]
         tq.encode_kv(layers[l], c, k, v, tok0=0)
         caches.append(c)
+        # the tail page adds a page to every row: the split plan, and so the
+        # workspace, is this cache's own
+        wss.append(torch.empty(tq.workspace_bytes(c, w.n_q_heads), dtype=torch.uint8, device=dev))
     g = torch.Generator(device=dev).manual_seed(7)
     dtype = inputs[0][0].dtype
     news = torch.randn((steps, w.n_layers, w.batch, w.n_kv_heads, 2, 128), generator=g,
