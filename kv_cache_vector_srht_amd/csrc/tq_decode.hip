@@ -51,11 +51,14 @@ struct DecodeArgs {
 };
 
 // The units (b * H_kv + h) one split launch covers.  A single-class launch
-// takes one unit per grid row; the merged common + wide launch (CLASS 3) takes
-// the wide units unit[0, n_first) and then the common units unit[n_first, n).
-// n == 0: every unit, in (B, H_kv) order.
+// takes one unit per grid row.  The merged launch (CLASS 3) runs up to three
+// groups of units: group[2] units of the other class, then group[1] of the
+// wide class, then group[0] of the common class, listed in that order in
+// unit[] (a class absent from the launch has an empty group).  n == 0: no
+// list, unit index = position in the group (single-class: the grid's rows).
 struct UnitList {
-  int32_t n, n_first;
+  int32_t n;
+  int32_t group[3];
   uint16_t unit[2 * TQ_MAX_LISTED_UNITS];
 };
 
@@ -550,7 +553,10 @@ __device__ __forceinline__ void softmax_update(float (&s)[G], float (&m)[G], flo
 //   0 common: k_bits, v_bits <= 4, no QJL;
 //   1 wide:   k_bits, v_bits >= 5, no QJL (the few important heads);
 //   2 other:  fp16 pages, QJL keys and mixed widths.
-// Each writes its own partials; the combine merges them.  When a layer holds
+// Each writes its own partials; the combine merges them.  Beside common pages,
+// the wide class (CLASS 3: common + wide) and also the other class (CLASS 4:
+// all three) run in one merged launch, each block taking its class's copy of
+// the page loop.  When a layer holds
 // both common and wide pages, one launch (CLASS 3) runs the two classes' blocks
 // side by side, so that the wide pages' latency hides behind common work.
 __device__ __forceinline__ int page_class(int kb, int vb, bool qjl) {
@@ -563,7 +569,7 @@ __device__ __forceinline__ int page_class(int kb, int vb, bool qjl) {
 // softmax numerator (m + log2 of the page's sum of 2^(s - m)); the combine
 // turns it into the page's attention mass.
 template <int G, int CLASS, bool MASS>
-__global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(CLASS == 3 ? 4 : 1)))
+__global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(CLASS >= 3 ? 4 : 1)))
 void split_kernel(DecodeArgs a,
                                                                   const float* __restrict__ wsq,
                                                                   const uint64_t* __restrict__ pages,
@@ -575,23 +581,35 @@ void split_kernel(DecodeArgs a,
   // tail page is then in the first workgroups dispatched, not behind the
   // rounds of workgroups that find nothing of the class
   int split, hkv, b, cls = CLASS;
-  if constexpr (CLASS == 3) {
-    // merged common + wide launch, one block per (unit, range), the wide
-    // class's blocks first so that its few long pages start early
-    const int wide_blocks = (list.n > 0 ? list.n_first : a.n_sessions * a.n_kv_heads) * a.n_splits_wide;
-    int i = blockIdx.x, ui;
-    if (i < wide_blocks) {
+  if constexpr (CLASS >= 3) {
+    // merged launch, one block per (unit, range): the other class's blocks
+    // first, range-major from each unit's last range (where a decode loop's
+    // fp16 tail page sits, so every unit's tail starts at once), then the wide
+    // class's and the common class's blocks, unit-major
+    const int other_blocks = list.group[2] * a.n_splits_general;
+    const int wide_blocks = list.group[1] * a.n_splits_wide;
+    int i = blockIdx.x, pos, off;   // position in the class's group, its list offset
+    if (i < other_blocks) {
+      cls = 2;
+      const int r = i / list.group[2];
+      pos = i - r * list.group[2];
+      split = a.n_splits_general - 1 - r;
+      off = 0;
+    } else if (i < other_blocks + wide_blocks) {
       cls = 1;
-      ui = i / a.n_splits_wide;
-      split = i - ui * a.n_splits_wide;
+      i -= other_blocks;
+      pos = i / a.n_splits_wide;
+      split = i - pos * a.n_splits_wide;
+      off = list.group[2];
     } else {
       cls = 0;
-      i -= wide_blocks;
-      ui = i / a.n_splits;
-      split = i - ui * a.n_splits;
-      if (list.n > 0) ui += list.n_first;
+      i -= other_blocks + wide_blocks;
+      pos = i / a.n_splits;
+      split = i - pos * a.n_splits;
+      off = list.group[2] + list.group[1];
     }
-    const int u = list.n > 0 ? list.unit[ui] : ui;
+    // without a list every group is every unit, in (B, H_kv) order
+    const int u = list.n > 0 ? list.unit[off + pos] : pos;
     b = u / a.n_kv_heads;
     hkv = u - b * a.n_kv_heads;
   } else {
@@ -630,7 +648,7 @@ void split_kernel(DecodeArgs a,
       coded |= m && pd.kb != 0;
     }
     __syncthreads();   // the cached descriptors are visible to every wave
-    need_tables = CLASS != 2 || __syncthreads_or(coded);
+    need_tables = cls != 2 || __syncthreads_or(coded);
     if (!__syncthreads_or(mine)) {
       if (tid < G) {
         part[tid * head_stride] = -INFINITY;
@@ -816,6 +834,13 @@ void split_kernel(DecodeArgs a,
       page_loop(std::integral_constant<int, 0>{});
     else
       page_loop(std::integral_constant<int, 1>{});
+  } else if constexpr (CLASS == 4) {
+    if (cls == 0)
+      page_loop(std::integral_constant<int, 0>{});
+    else if (cls == 1)
+      page_loop(std::integral_constant<int, 1>{});
+    else
+      page_loop(std::integral_constant<int, 2>{});
   } else {
     page_loop(std::integral_constant<int, CLASS>{});
   }
@@ -1096,13 +1121,14 @@ int decode_impl(const tq_layer* layer, const tq_cache* cache, const tq_query* qu
   a.pages_per_split_wide = sp.pages_per_split_wide;
   // Per-class unit lists from the host's per-unit record: a class's launch
   // covers only the units that hold it.  Class 0 = common, 1 = wide, 2 = other.
-  UnitList lists[3];   // n_first unused by single-class launches
+  UnitList lists[3];
   const int class_bit[3] = {TQ_CACHE_COMMON_PAGES, TQ_CACHE_WIDE_PAGES, TQ_CACHE_OTHER_PAGES};
   const int64_t units = (int64_t)cache->n_sessions * cache->n_kv_heads;
   const bool listed = cache->unit_classes != nullptr && units <= TQ_MAX_LISTED_UNITS;
   std::memset(a.unit_skip, 0, sizeof(a.unit_skip));
   for (int c = 0; c < 3; ++c) {
-    lists[c].n = lists[c].n_first = 0;
+    lists[c].n = 0;
+    lists[c].group[0] = lists[c].group[1] = lists[c].group[2] = 0;
     if (!listed) continue;
     for (int u = 0; u < (int)units; ++u) {
       if (cache->unit_classes[u] & class_bit[c])
@@ -1127,19 +1153,34 @@ int decode_impl(const tq_layer* layer, const tq_cache* cache, const tq_query* qu
   const dim3 blk(64 * kDecodeWaves);
   const bool go_common = run_common && (!listed || lists[0].n > 0);
   const bool go_wide = run_wide && (!listed || lists[1].n > 0);
-  if (go_common && go_wide) {
-    // one launch: the wide units' blocks, then the common units' blocks
+  const bool go_other = run_other && (!listed || lists[2].n > 0);
+  // Beside common pages, the wide class and the other class (sink and tail
+  // pages, a minority there) join one merged launch; a layer without common
+  // pages (QJL or fp16 alone, say) keeps each class's own kernel.
+  const int cnt[3] = {listed ? lists[0].n : (int)units, listed ? lists[1].n : (int)units,
+                      listed ? lists[2].n : (int)units};
+  // (groups of 8 query heads keep separate launches: the merged kernel does
+  // not fit 4 waves per SIMD at that width)
+  const bool merge = G <= 4 && go_common;
+  const bool merge_other = merge && go_other &&
+                           (!listed || cnt[0] + (go_wide ? cnt[1] : 0) + cnt[2] <= 2 * TQ_MAX_LISTED_UNITS);
+  if (merge && (go_wide || merge_other)) {
     UnitList merged;
-    merged.n = merged.n_first = 0;
-    int64_t blocks = units * ((int64_t)sp.n_splits + sp.n_splits_wide);
+    merged.n = 0;
+    merged.group[2] = merge_other ? cnt[2] : 0;
+    merged.group[1] = go_wide ? cnt[1] : 0;
+    merged.group[0] = cnt[0];
     if (listed) {
-      for (int i = 0; i < lists[1].n; ++i) merged.unit[merged.n++] = lists[1].unit[i];
-      merged.n_first = merged.n;
-      for (int i = 0; i < lists[0].n; ++i) merged.unit[merged.n++] = lists[0].unit[i];
-      blocks = (int64_t)lists[1].n * sp.n_splits_wide + (int64_t)lists[0].n * sp.n_splits;
+      for (int c = 2; c >= 0; --c)
+        for (int i = 0; i < merged.group[c]; ++i) merged.unit[merged.n++] = lists[c].unit[i];
     }
-    launch_split_any<3>(mass, G, dim3((unsigned)blocks), blk, s, a, cache->pages, merged);
-    if ((st = launch_status("split (common and wide pages)"))) return st;
+    const int64_t blocks = (int64_t)merged.group[2] * sp.n_splits_general +
+                           (int64_t)merged.group[1] * sp.n_splits_wide + (int64_t)merged.group[0] * sp.n_splits;
+    if (merge_other)
+      launch_split_any<4>(mass, G, dim3((unsigned)blocks), blk, s, a, cache->pages, merged);
+    else
+      launch_split_any<3>(mass, G, dim3((unsigned)blocks), blk, s, a, cache->pages, merged);
+    if ((st = launch_status("split (merged classes)"))) return st;
   } else if (go_common) {
     launch_split_any<0>(mass, G, grid_of(sp.n_splits, lists[0]), blk, s, a, cache->pages, lists[0]);
     if ((st = launch_status("split (common pages)"))) return st;
@@ -1147,7 +1188,7 @@ int decode_impl(const tq_layer* layer, const tq_cache* cache, const tq_query* qu
     launch_split_any<1>(mass, G, grid_of(sp.n_splits_wide, lists[1]), blk, s, a, cache->pages, lists[1]);
     if ((st = launch_status("split (wide pages)"))) return st;
   }
-  if (run_other && (!listed || lists[2].n > 0)) {
+  if (go_other && !merge_other) {
     launch_split_any<2>(mass, G, grid_of(sp.n_splits_general, lists[2]), blk, s, a, cache->pages, lists[2]);
     if ((st = launch_status("split (other pages)"))) return st;
   }
