@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--codecs", type=int, default=1,
                     help="compare the scalar codec with PolarQuant on one layer (1, default) or skip (0)")
+    ap.add_argument("--qjl", type=int, default=1,
+                    help="also time one layer of the QJL workload's encode (1 = yes)")
     ap.add_argument("--tiering", type=int, default=1,
                     help="measure page-mass export and page re-tiering (1, default) or skip (0)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
@@ -87,13 +89,16 @@ def encode_bytes(w, formats):
     return inp + out
 
 
-def traffic_record(kernel: str):
-    """Measured HBM traffic of `kernel` from profiles/, if taken on the current source."""
+def traffic_record(kernel: str, workload: str):
+    """Measured HBM traffic of `kernel` from profiles/, if taken on this workload
+    and on the current source."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
+    if rec.get("workload") != workload:
+        return None
     sha = hashlib.sha256()
     for f in rec.get("sources", []):
         sha.update(open(os.path.join(ROOT, f), "rb").read())
@@ -254,6 +259,44 @@ def decode_graph(w, layers, caches, queries, outs, wss, dec_bytes, dev, reps: in
     return {"reps": reps, "median_ms": round(med * 1e3, 4), "min_ms": round(min(ts) * 1e3, 4),
             "gbs": round(dec_bytes / med / 1e9, 1),
             "frac_of_peak": round(dec_bytes / med / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def qjl_encode(dev, sessions: int = 4, reps: int = 3):
+    """Encode of one layer of the 128K QJL workload's shape at ``sessions`` of
+    its 16 sessions (keys K2 + QJL sketch, values V2, 128-token fp16 sink):
+    HIP-event time of tq_encode_kv, median of ``reps`` after one untimed call.
+    The sketch (2 x 128 x 128 flops per key, on the float32 matrix cores) is
+    the dominant part; its rate is bounded below by sketch flops / call time."""
+    import numpy as np
+    import torch
+    import kv_cache_vector_srht_amd as tq
+    import workloads as W
+    w = W.make_workload(4, {"batch": sessions})
+    S = W.qjl_matrix(W.ROTATION_SEED, 0)
+    layer = tq.Layer(W.rotation_signs(W.ROTATION_SEED, 0), dev, S, w.k_codebook, w.v_codebook)
+    cache = tq.Cache(w.formats[0], [w.n_tokens] * w.batch, dev)
+    k, v = W.make_kv(w, 0, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    tq.encode_kv(layer, cache, k, v)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        tq.encode_kv(layer, cache, k, v)
+        e1.record(stream)
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) / 1e3)
+    t = float(np.median(ts))
+    qjl_keys = sum(64 for row in w.formats[0] for r in row for f in r if f[2])
+    flops = qjl_keys * 2.0 * 128 * 128
+    out = {"workload": w.name, "sessions": sessions, "encode_ms": round(t * 1e3, 3),
+           "mtokens_per_s": round(w.batch * w.n_tokens / t / 1e6, 2),
+           "qjl_keys": qjl_keys, "sketch_tflops_lower_bound": round(flops / t / 1e12, 2),
+           "fp32_mfma_peak_tflops": 157.3}
+    del cache, k, v
+    torch.cuda.synchronize()
+    return out
 
 
 def decode_loop(w, layers, inputs, queries, outs, wss, steps, dev, graph=False):
@@ -545,7 +588,7 @@ def main():
                                                 dec_s / w.n_layers)
     achieved = per_launch_bytes / per_launch_s / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_record(name),
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_record(name, w.name),
             "kernel": name, "bytes_per_launch": int(per_launch_bytes),
             "launch_us": round(per_launch_s * 1e6, 2)}
     line = {
@@ -574,6 +617,8 @@ def main():
         line["decode_loop"] = decode_loop(w, layers, inputs, queries, outs, wss, args.loop_steps, dev)
         line["decode_loop_graph"] = decode_loop(w, layers, inputs, queries, outs, wss, args.loop_steps,
                                                 dev, graph=True)
+    if args.qjl:
+        line["qjl_encode"] = qjl_encode(dev)
     if args.tiering:
         line["tiering"] = tiering(w, layers, inputs, queries, outs, wss, dev)
     if args.codecs:

@@ -1035,7 +1035,11 @@ void launch_split(int G, dim3 grid, dim3 blk, hipStream_t s, const DecodeArgs& a
     case 1: hipLaunchKernelGGL((split_kernel<1, CLASS, MASS>), grid, blk, 0, s, a, a.wsq, pages, a.wsp, l); break;
     case 2: hipLaunchKernelGGL((split_kernel<2, CLASS, MASS>), grid, blk, 0, s, a, a.wsq, pages, a.wsp, l); break;
     case 4: hipLaunchKernelGGL((split_kernel<4, CLASS, MASS>), grid, blk, 0, s, a, a.wsq, pages, a.wsp, l); break;
-    default: hipLaunchKernelGGL((split_kernel<8, CLASS, MASS>), grid, blk, 0, s, a, a.wsq, pages, a.wsp, l); break;
+    default:
+      // the merged launches (CLASS 3, 4) are not used for groups of 8
+      if constexpr (CLASS < 3)
+        hipLaunchKernelGGL((split_kernel<8, CLASS, MASS>), grid, blk, 0, s, a, a.wsq, pages, a.wsp, l);
+      break;
   }
 }
 

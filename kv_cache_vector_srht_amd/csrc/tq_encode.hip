@@ -4,9 +4,12 @@
 // Architecture): every 128-value head vector x is rotated by D H D, its norm is
 // stored, and each coordinate of u = D H D x / ||x|| is quantised and packed.
 // encode_pages_kernel (four lanes per vector, below) writes fp16 pages and the
-// packed keys and values of every page without a QJL residual.  encode_kernel
-// (one lane per vector) writes the keys of QJL pages: codes, norm, and the
-// signs of S r for r = x - xhat ("TurboMOQ", QJL residual correction).
+// packed keys and values of every page without a QJL residual.
+// qjl_keys_kernel (one lane per vector) writes the keys of QJL pages: codes,
+// norm, and the signs of S r for r = x - xhat ("TurboMOQ", QJL residual
+// correction), the sketch on the matrix cores.
+#include <algorithm>
+
 #include "tq_device.h"
 #include "tq_token_encoder.h"
 
@@ -23,92 +26,136 @@ struct EncodeArgs {
   int64_t sb, sh, st;
   int32_t* err;
   const uint64_t* pages;
-  int n_kv_heads, max_pages;
+  int n_sessions, n_kv_heads, max_pages;
   char* pool;
   uint64_t pool_bytes;
   const uint32_t* sign_mask;
   const float* k_table;
   const float* v_table;
   const float* qjl_s;
-  int k_polar, v_polar;   // PolarQuant parts: coded by encode_kernel, not encode_pages_kernel
+  int k_polar, v_polar;   // PolarQuant parts (at most 4 bits wide)
 };
 
-// One wavefront per (page, KV head, session); PART 0 encodes keys, 1 values.
-template <int PART>
-__global__ __launch_bounds__(64) void encode_kernel(EncodeArgs a, const uint64_t* __restrict__ pages,
-                                                    const float* __restrict__ qjl_s) {
-  __shared__ float lds_thr[256];
-  __shared__ float lds_cent[256];
-  __shared__ float2 lds_pair[256];
-  __shared__ uint32_t lds_rows[PT * kEncodeRowBytes / 4];
-  const int lane = threadIdx.x;
-  const int pg = a.page0 + blockIdx.x;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
-  constexpr int part = PART;
-  const uint64_t desc = pages[((size_t)b * a.n_kv_heads + h) * a.max_pages + pg];
-  if (!(desc & TQ_PAGE_PRESENT)) {
-    if (lane == 0) raise_flag(a.err, 2);
-    return;
-  }
-  const PageDesc pd = read_desc(desc);
-  const int kb = pd.kb, vb = pd.vb;
-  const bool qjl = pd.qjl;
-  const uint64_t off = pd.off;
-  const bool bad_fmt = kb == 0 ? (vb != 0 || qjl) : (kb > 8 || vb < 1 || vb > 8);
-  if (bad_fmt || off + page_size_dev(kb, vb, qjl) > a.pool_bytes) {
-    if (lane == 0) raise_flag(a.err, 4);
-    return;
-  }
-  char* page = a.pool + off;
-  const int t_first = pg * PT;
-  const int lo = max(t_first, a.tok0), hi = min(t_first + PT, a.tok0 + a.ntok);
-  const void* src = part == 0 ? a.k : a.v;
-  const size_t base = (size_t)b * a.sb + (size_t)h * a.sh;
+// Keys of QJL pages: the per-token encoder (lane = token) writes codes and norm
+// and leaves the residual r in registers; the sign sketch z = sign(S r) of the
+// page's 64 keys is then one product [64 tokens x 128] . [128 x 128] on the
+// float32 matrix cores (v_mfma_f32_32x32x2f32, exact float32 products).
+// Persistent: kQjlBlocks workgroups of kQjlWaves waves stride over the call's
+// (page, KV head, session) items, one page per wave at a time; S sits in LDS
+// once per workgroup, laid out for the B operand:
+//   S[i][j] at ((j / 4 * 2 + j % 2) * 128 + i) * 2 + (j / 2) % 2,
+// so that lane (h = lane / 32, n = lane % 32) of column block c reads the B
+// values of K-steps 2kk and 2kk + 1 (coordinates 4kk + h and 4kk + 2 + h of
+// sketch row 32c + n) as one float2.  A operands come from the lanes' own
+// residuals: permlane32_swap of (r[2k], r[2k + 1]) gives tile 0's operand
+// (tokens 0-31: lane l < 32 holds r[l][2k], lane l >= 32 r[l - 32][2k + 1]) and
+// tile 1's (tokens 32-63).  Accumulator v of lane l holds row
+// 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32, so the ballot of its sign is
+// the sketch dword c of two tokens (low half: that row; high half: row + 4).
+constexpr int kQjlWaves = 4;
+constexpr int kQjlBlocksPerCU = 2;   // 80 KB of LDS each
+typedef float mfma_acc16 __attribute__((ext_vector_type(16)));
 
-  if (kb == 0) return;   // fp16 pages are copied by encode_pages_kernel
-  if (lo != t_first || hi != t_first + PT) {
-    if (lane == 0) raise_flag(a.err, 1);
-    return;
+__global__ __launch_bounds__(64 * kQjlWaves) void qjl_keys_kernel(EncodeArgs a, const uint64_t* __restrict__ pages,
+                                                                 int n_pages) {
+  __shared__ float st[D * D];
+  __shared__ float lds_thr[kQjlWaves][256];
+  __shared__ float lds_cent[kQjlWaves][256];
+  __shared__ float2 lds_pair[kQjlWaves][256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < D * D; e += blockDim.x) {
+    const int i = e >> 7, j = e & (D - 1);
+    st[(((j >> 2) * 2 + (j & 1)) * D + i) * 2 + ((j >> 1) & 1)] = a.qjl_s[e];
   }
-  if (part == 0 && qjl && a.qjl_s == nullptr) {
-    if (lane == 0) raise_flag(a.err, 8);
-    return;
-  }
-  const bool polar = part == 0 ? a.k_polar : a.v_polar;
-  const int B = part == 0 ? kb : vb;
-  // everything but the keys of QJL pages is written by encode_pages_kernel,
-  // which also flags PolarQuant parts wider than 4 bits
-  if (part == 1 || !qjl || (polar && B > 4)) return;
-  const float* table = part == 0 ? a.k_table : a.v_table;
-  const int L = 1 << B;
-  for (int i = lane; i < L; i += 64) {
-    lds_cent[i] = table[centroid_offset(B) + i];
-    if (i < L - 1) lds_thr[i] = table[boundary_offset(B) + i];
-  }
-  if (polar) {
-    const float2* pt = reinterpret_cast<const float2*>(table + kPairOffset) + pair_offset_host(B);
-    for (int i = lane; i < L * L; i += 64) lds_pair[i] = pt[i];
-  }
+  __syncthreads();
   uint32_t m[4];
 #pragma clang loop unroll(full)
   for (int w = 0; w < 4; ++w) m[w] = a.sign_mask[w];
-  float x[D];
-  load_row(src, a.dtype, base + (size_t)(t_first + lane - a.tok0) * a.st, x);
-  __syncthreads();
-  char* part_base = part == 0 ? page : page + 1024 * kb + 256 + (qjl ? 1280 : 0);
-  float n = 0.f;
-  switch (B) {
-    case 1: n = encode_packed<PART, 1>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-    case 2: n = encode_packed<PART, 2>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-    case 3: n = encode_packed<PART, 3>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-    case 4: n = encode_packed<PART, 4>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-    case 5: n = encode_packed<PART, 5>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-    case 6: n = encode_packed<PART, 6>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-    case 7: n = encode_packed<PART, 7>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows); break;
-    default: n = encode_packed<PART, 8>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows); break;
+  const int h_half = lane >> 5, n_col = lane & 31;
+  // which accumulator and ballot half hold this lane's token (lane = token)
+  const int tt = lane & 31;
+  const int my_v = 4 * (tt >> 3) + (tt & 3), my_half = (tt >> 2) & 1, my_tile = lane >> 5;
+
+  const int total = n_pages * a.n_kv_heads * a.n_sessions;
+  for (int item = blockIdx.x * kQjlWaves + wave; item < total; item += gridDim.x * kQjlWaves) {
+    const int pgi = item % n_pages, rest = item / n_pages;
+    const int h = rest % a.n_kv_heads, b = rest / a.n_kv_heads;
+    const int pg = a.page0 + pgi;
+    const uint64_t desc = pages[((size_t)b * a.n_kv_heads + h) * a.max_pages + pg];
+    if (!(desc & TQ_PAGE_PRESENT)) continue;    // flagged by encode_pages_kernel
+    const PageDesc pd = read_desc(desc);
+    const int kb = pd.kb, vb = pd.vb;
+    const bool qjl = pd.qjl;
+    const bool bad_fmt = kb == 0 ? (vb != 0 || qjl) : (kb > 8 || vb < 1 || vb > 8);
+    if (!qjl || bad_fmt || pd.off + page_size_dev(kb, vb, qjl) > a.pool_bytes) continue;
+    const int t_first = pg * PT;
+    if (max(t_first, a.tok0) != t_first || min(t_first + PT, a.tok0 + a.ntok) != t_first + PT) continue;
+    const bool polar = a.k_polar;
+    if (polar && kb > 4) continue;               // refused (and flagged) by encode_pages_kernel
+    char* page = a.pool + pd.off;
+    // this wave's quantiser tables for the key width
+    wave_lds_sync();
+    const int L = 1 << kb;
+    for (int i = lane; i < L; i += 64) {
+      lds_cent[wave][i] = a.k_table[centroid_offset(kb) + i];
+      if (i < L - 1) lds_thr[wave][i] = a.k_table[boundary_offset(kb) + i];
+    }
+    if (polar) {
+      const float2* pt = reinterpret_cast<const float2*>(a.k_table + kPairOffset) + pair_offset_host(kb);
+      for (int i = lane; i < L * L; i += 64) lds_pair[wave][i] = pt[i];
+    }
+    float x[D];
+    const size_t base = (size_t)b * a.sb + (size_t)h * a.sh;
+    load_row(a.k, a.dtype, base + (size_t)(t_first + lane - a.tok0) * a.st, x);
+    wave_lds_sync();
+    float n;
+    float* thr = lds_thr[wave];
+    float* cent = lds_cent[wave];
+    float2* pair = lds_pair[wave];
+    switch (kb) {
+      case 1: n = encode_packed<0, 1>(page, lane, x, m, thr, cent, nullptr, polar, pair); break;
+      case 2: n = encode_packed<0, 2>(page, lane, x, m, thr, cent, nullptr, polar, pair); break;
+      case 3: n = encode_packed<0, 3>(page, lane, x, m, thr, cent, nullptr, polar, pair); break;
+      case 4: n = encode_packed<0, 4>(page, lane, x, m, thr, cent, nullptr, polar, pair); break;
+      case 5: n = encode_packed<0, 5>(page, lane, x, m, thr, cent, nullptr); break;
+      case 6: n = encode_packed<0, 6>(page, lane, x, m, thr, cent, nullptr); break;
+      case 7: n = encode_packed<0, 7>(page, lane, x, m, thr, cent, nullptr); break;
+      default: n = encode_packed<0, 8>(page, lane, x, m, thr, cent, nullptr); break;
+    }
+    const float gamma = qjl_residual(x, m, n);
+    // A operands in place: x[2k] <- tile 0's, x[2k + 1] <- tile 1's
+#pragma clang loop unroll(full)
+    for (int k = 0; k < D / 2; ++k) {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[2 * k]), __float_as_uint(x[2 * k + 1]),
+                                                      false, false);
+      x[2 * k] = __uint_as_float(r[0]);
+      x[2 * k + 1] = __uint_as_float(r[1]);
+    }
+    char* qbase = page + 1024 * kb + 256;
+    // one column block (sketch dword c of every token) at a time
+#pragma clang loop unroll(disable)
+    for (int c = 0; c < 4; ++c) {
+      mfma_acc16 acc0 = {}, acc1 = {};
+      const float2* bsrc = reinterpret_cast<const float2*>(st) + h_half * D + 32 * c + n_col;
+#pragma clang loop unroll(full)
+      for (int kk = 0; kk < D / 4; ++kk) {
+        const float2 bb = bsrc[kk * 2 * D];
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(x[4 * kk], bb.x, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(x[4 * kk + 1], bb.x, acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(x[4 * kk + 2], bb.y, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(x[4 * kk + 3], bb.y, acc1, 0, 0, 0);
+      }
+      uint32_t word = 0;
+#pragma clang loop unroll(full)
+      for (int v = 0; v < 16; ++v) {
+        const uint64_t b0 = __ballot(acc0[v] >= 0.f), b1 = __ballot(acc1[v] >= 0.f);
+        const uint64_t bt = my_tile ? b1 : b0;
+        if (my_v == v) word = (uint32_t)(bt >> (32 * my_half));
+      }
+      reinterpret_cast<uint32_t*>(qbase)[4 * lane + c] = word;
+    }
+    reinterpret_cast<float*>(qbase + 1024)[lane] = gamma;
   }
-  if (PART == 0 && qjl) qjl_sketch(qjl_s, part_base + 1024 * B + 256, lane, x, m, n);
 }
 
 // ------------------------------------------------------- encode (quad lanes)
@@ -593,6 +640,7 @@ int tq_encode_kv(const tq_layer* layer, const tq_cache* cache, const tq_kv_input
   a.st = in->stride_t;
   a.err = in->error_flags;
   a.pages = cache->pages;
+  a.n_sessions = cache->n_sessions;
   a.n_kv_heads = cache->n_kv_heads;
   a.max_pages = cache->max_pages;
   a.pool = reinterpret_cast<char*>(cache->pool);
@@ -626,10 +674,21 @@ int tq_encode_kv(const tq_layer* layer, const tq_cache* cache, const tq_kv_input
   int st2 = launch_status("encode");
   if (st2) return st2;
   if (layer->qjl_s) {
-    // keys of QJL pages: codes, norm and sign sketch, one wavefront per page
-    dim3 qgrid(n_pages, cache->n_kv_heads, cache->n_sessions);
-    hipLaunchKernelGGL(encode_kernel<0>, qgrid, dim3(64), 0, (hipStream_t)stream, a, cache->pages,
-                       layer->qjl_s);
+    // keys of QJL pages: codes, norm and sign sketch, a page per wave on
+    // persistent workgroups (as many as the items need, at most two per CU)
+    static int cu_count[64] = {};   // per device, read once (a benign race: same value)
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+      if (cu_count[dev] < 1 &&
+          hipDeviceGetAttribute(&cu_count[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cu_count[dev] = 0;
+      if (cu_count[dev] >= 1) cus = cu_count[dev];
+    }
+    const int64_t items = (int64_t)n_pages * cache->n_kv_heads * cache->n_sessions;
+    const int64_t want = (items + kQjlWaves - 1) / kQjlWaves;
+    const int blocks = (int)std::min<int64_t>(want, (int64_t)cus * kQjlBlocksPerCU);
+    hipLaunchKernelGGL(qjl_keys_kernel, dim3(blocks), dim3(64 * kQjlWaves), 0, (hipStream_t)stream, a,
+                       cache->pages, n_pages);
     st2 = launch_status("encode QJL keys");
   }
   return st2;

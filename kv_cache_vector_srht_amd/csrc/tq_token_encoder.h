@@ -214,14 +214,11 @@ __device__ __forceinline__ float encode_packed(char* page, int lane, float (&x)[
   }
 }
 
-// The QJL sign sketch of a key ("TurboMOQ", QJL residual correction) from the
-// rotated-domain residual u - c that encode_packed leaves in x:
-// r = x - xhat = (n / d) D H D (u - c) (one more butterfly in registers),
-// z = sign(S r) (bit i of the lane's 128-bit word), gamma = ||r||, stored at
-// qbase (64 x 16 B signs) and qbase + 1024 (64 x float32).  One copy serves
-// every width.
-__device__ __forceinline__ void qjl_sketch(const float* __restrict__ qjl_s, char* qbase, int lane,
-                                           float (&x)[D], const uint32_t (&m)[4], float n) {
+// The residual of a QJL key ("TurboMOQ", QJL residual correction) from the
+// rotated-domain residual u - c that encode_packed leaves in x: on return x
+// holds r = x - xhat = (n / d) D H D (u - c) (one more butterfly in
+// registers); returns gamma = ||r||.
+__device__ __forceinline__ float qjl_residual(float (&x)[D], const uint32_t (&m)[4], float n) {
   float e2 = 0.f;
 #pragma clang loop unroll(full)
   for (int j = 0; j < D; ++j) {
@@ -232,7 +229,16 @@ __device__ __forceinline__ void qjl_sketch(const float* __restrict__ qjl_s, char
   const float sc = n * (1.0f / D);
 #pragma clang loop unroll(full)
   for (int j = 0; j < D; ++j) x[j] = flip_if(x[j], dsign(m, j)) * sc;
-  const float gamma = n * sqrtf(e2) * 0.08838834764831845f;  // n ||u - c|| / sqrt(d)
+  return n * sqrtf(e2) * 0.08838834764831845f;  // n ||u - c|| / sqrt(d)
+}
+
+// The QJL sign sketch of one key, lane = token: z = sign(S r) (bit i of the
+// lane's 128-bit word) and gamma, stored at qbase (64 x 16 B signs) and
+// qbase + 1024 (64 x float32).  One copy serves every width; the bulk encode
+// computes the same sketch a page at a time on the matrix cores.
+__device__ __forceinline__ void qjl_sketch(const float* __restrict__ qjl_s, char* qbase, int lane,
+                                           float (&x)[D], const uint32_t (&m)[4], float n) {
+  const float gamma = qjl_residual(x, m, n);
   uint32_t zw[4];
 #pragma clang loop unroll(full)
   for (int w = 0; w < 4; ++w) {
