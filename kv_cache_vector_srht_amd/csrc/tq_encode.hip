@@ -176,7 +176,7 @@ __global__ __launch_bounds__(64 * kQjlWaves) void qjl_keys_kernel(EncodeArgs a, 
 // streaming accumulator whose flush points are uniform.
 constexpr int kRowStride = 144;            // LDS byte-matrix row: 128 codes + pad
 constexpr int kEncodeBlock = 256;
-constexpr int kEncodePagesPerBlock = 8;
+constexpr int kEncodePagesPerBlock = 4;
 
 __device__ __forceinline__ float quad_swap(float v, int m) {
   // partner lane = lane ^ m inside the quad; m is a compile-time 1 or 2 after unrolling
