@@ -108,6 +108,25 @@ def traffic_record(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
+def valu_record(workload: str):
+    """VALU issue per kernel (fraction of SIMD cycles issuing VALU) from the
+    committed SQ counter record, if taken on this workload and on the current
+    kernel sources; None otherwise."""
+    path = os.path.join(ROOT, "profiles", f"valu_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("workload") != workload:
+        return None
+    sha = hashlib.sha256()
+    for f in rec.get("sources", []):
+        sha.update(open(os.path.join(ROOT, f), "rb").read())
+    if rec.get("source_sha256") != sha.hexdigest():
+        return None
+    return rec.get("valu_issue")
+
+
 def cpu_baseline(w, layers_data, seconds: float):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     whole (layer, session, KV head) units, encode then decode attention."""
@@ -606,6 +625,8 @@ def main():
         "encode_ms_per_step": round(enc_s * 1e3, 3),
         "decode_bytes_per_step": int(dec_bytes), "encode_bytes_per_step": int(enc_bytes),
         "roofline": roof,
+        # from profiles/ (rocprofv3 SQ counters), when taken on these sources
+        "valu_issue": valu_record(w.name),
     }
     line["decode_graph"] = decode_graph(w, layers, caches, queries, outs, wss, dec_bytes, dev)
     hs = hbm_stream(dev)
