@@ -569,7 +569,7 @@ __device__ __forceinline__ int page_class(int kb, int vb, bool qjl) {
 // softmax numerator (m + log2 of the page's sum of 2^(s - m)); the combine
 // turns it into the page's attention mass.
 template <int G, int CLASS, bool MASS>
-__global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(CLASS >= 3 ? 4 : 1)))
+__global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(CLASS >= 3 ? 4 : (CLASS == 2 && G <= 4) ? 3 : 1)))
 void split_kernel(DecodeArgs a,
                                                                   const float* __restrict__ wsq,
                                                                   const uint64_t* __restrict__ pages,
