@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attn effective HBM GB/s (% of peak) + encode Mtokens/s at 32K ctx"
 HBM_PEAK_GBS = 8000.0
+FP32_MFMA_PEAK_TFLOPS = 157.3   # dense float32 matrix-core peak
 
 
 def parse():
@@ -312,7 +313,7 @@ def qjl_encode(dev, sessions: int = 4, reps: int = 3):
     out = {"workload": w.name, "sessions": sessions, "encode_ms": round(t * 1e3, 3),
            "mtokens_per_s": round(w.batch * w.n_tokens / t / 1e6, 2),
            "qjl_keys": qjl_keys, "sketch_tflops_lower_bound": round(flops / t / 1e12, 2),
-           "fp32_mfma_peak_tflops": 157.3}
+           "fp32_mfma_peak_tflops": FP32_MFMA_PEAK_TFLOPS}
     del cache, k, v
     torch.cuda.synchronize()
     return out
@@ -597,8 +598,9 @@ def main():
     enc_mtok = w.batch * w.n_tokens / enc_s / 1e6
 
     # the kernel that dominates the step
-    # (encode is one encode_pages_kernel launch per layer unless a layer has
-    # QJL keys; decode is four launches per layer, reported as one call)
+    # (encode is one encode_pages_kernel launch per layer, plus qjl_keys_kernel
+    # when a layer has QJL keys; decode is four launches per layer, reported as
+    # one call)
     if enc_s >= dec_s:
         name, per_launch_bytes, per_launch_s = ("encode_pages_kernel", enc_bytes / w.n_layers,
                                                 enc_s / w.n_layers)
@@ -610,6 +612,21 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_record(name, w.name),
             "kernel": name, "bytes_per_launch": int(per_launch_bytes),
             "launch_us": round(per_launch_s * 1e6, 2)}
+    qjl_keys = sum(64 for fm in w.formats for row in fm for r in row for f in r if f[2])
+    if qjl_keys and enc_s >= dec_s:
+        # With QJL key pages the encode call is dominated by qjl_keys_kernel, the
+        # sketch z = sign(S r) as a float32 matrix-core product (2 x 128 x 128
+        # flops per key).  Its own duration is not separable from the call's
+        # encode_pages_kernel with events around the call, so the rate is a
+        # lower bound: sketch flops / whole call time.
+        flops = qjl_keys * 2.0 * 128 * 128 / w.n_layers
+        tflops = flops / per_launch_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": FP32_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "qjl_keys_kernel", "flops_per_launch": int(flops),
+                "launch_us": round(per_launch_s * 1e6, 2),
+                "timed": "whole tq_encode_kv call (qjl_keys_kernel + encode_pages_kernel): lower bound",
+                "hbm_gbs_of_call": round(achieved, 1)}
     line = {
         "metric": METRIC, "value": round(dec_gbs, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
