@@ -242,20 +242,35 @@ __device__ __forceinline__ void key_scores_fp16(const char* page, int lane, cons
   }
 }
 
-// QJL term: sum_i qs[h][i] (2 z_i - 1) for lane = token.
+// QJL term: sum_i qs[h][i] (2 z_i - 1) for lane = token, taken as
+// 2 sum_i z_i qs[h][i] - qsum[h] with z_i in {0, 1} (qsum[h] = sum_i qs[h][i]).
+// Four consecutive sign bits x are spread into the four bytes of a register by
+// one multiply, x * (1 + 2^7 + 2^14 + 2^21): bit b of x lands at b + 7m for the
+// m-th term, positions that are all distinct (no carries), and only m = b hits
+// bit 8b; each byte is then converted to float on its own.  That is 1.75
+// instructions per coordinate for the signs, not the 3 of a per-bit select.
 template <int G>
 __device__ __forceinline__ void qjl_scores(const char* qb, int lane, const float* __restrict__ qsv,
-                                           float (&t)[G]) {
+                                           const float (&qsum)[G], float (&t)[G]) {
   const uint4 z4 = reinterpret_cast<const uint4*>(qb)[lane];
   const uint32_t zw[4] = {z4.x, z4.y, z4.z, z4.w};
 #pragma clang loop unroll(full)
   for (int h = 0; h < G; ++h) t[h] = 0.f;
 #pragma clang loop unroll(full)
-  for (int i = 0; i < TQ_JL_DIM; ++i) {
-    const float z = ((zw[i >> 5] >> (i & 31)) & 1u) ? 1.f : -1.f;
+  for (int n = 0; n < TQ_JL_DIM / 4; ++n) {
+    uint32_t by = ((zw[n >> 3] >> (4 * (n & 7))) & 0xFu) * 0x204081u & 0x01010101u;
+    // opaque to the optimiser, which would otherwise extract every bit on its
+    // own before converting it
+    asm("" : "+v"(by));
 #pragma clang loop unroll(full)
-    for (int h = 0; h < G; ++h) t[h] = fmaf(qsv[((i >> 2) * G + h) * 4 + (i & 3)], z, t[h]);
+    for (int e = 0; e < 4; ++e) {
+      const float z = (float)((by >> (8 * e)) & 0xFFu);   // sign bit 4 n + e
+#pragma clang loop unroll(full)
+      for (int h = 0; h < G; ++h) t[h] = fmaf(qsv[(n * G + h) * 4 + e], z, t[h]);
+    }
   }
+#pragma clang loop unroll(full)
+  for (int h = 0; h < G; ++h) t[h] = fmaf(2.f, t[h], -qsum[h]);
 }
 
 // Value accumulation of one packed page: lane (q, i) owns coordinates
@@ -707,6 +722,20 @@ void split_kernel(DecodeArgs a,
   // wide copy, cheaper than a fourth of the waves).
   auto page_loop = [&](auto pc_tag) {
     constexpr int PC = decltype(pc_tag)::value;
+    // sum over coordinates of the QJL query term, per head (lane l adds
+    // coordinates 2l and 2l + 1, then a wavefront sum)
+    float qsum[G];
+#pragma clang loop unroll(full)
+    for (int h = 0; h < G; ++h) qsum[h] = 0.f;
+    if (PC == 2 && a.qjl_s != nullptr) {
+      const float* qsv = qrow + 2 * D * G;
+      const int i0 = 2 * lane;
+#pragma clang loop unroll(full)
+      for (int h = 0; h < G; ++h) {
+        const float* c = qsv + ((i0 >> 2) * G + h) * 4 + (i0 & 3);
+        qsum[h] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_sum(c[0] + c[1]))));
+      }
+    }
     for (int p = p_begin + wave; p < p_end; p += kDecodeWaves) {
       const PageDesc pd = read_desc(sm.desc[p - p_begin]);
       const int kb = pd.kb, vb = pd.vb;
@@ -762,7 +791,7 @@ void split_kernel(DecodeArgs a,
         for (int h = 0; h < G; ++h) s[h] *= nk;
         if (PC == 2 && qjl) {
           float t[G];
-          qjl_scores<G>(vblk, lane, qrow + 2 * D * G, t);
+          qjl_scores<G>(vblk, lane, qrow + 2 * D * G, qsum, t);
   #pragma clang loop unroll(full)
           for (int h = 0; h < G; ++h) s[h] = fmaf(gq, t[h], s[h]);
           vblk += 1280;
