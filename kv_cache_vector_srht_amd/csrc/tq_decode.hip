@@ -273,6 +273,38 @@ __device__ __forceinline__ void qjl_scores(const char* qb, int lane, const float
   for (int h = 0; h < G; ++h) t[h] = fmaf(2.f, t[h], -qsum[h]);
 }
 
+// The same term from a table of signed sums per group of four sign bits:
+// lut[(n * 16 + v) * G + h] = sum_{e < 4} (2 bit_e(v) - 1) qs[h][4 n + e], so a
+// key's term is 32 reads (all G heads of one group at once) and their sums.
+template <int G>
+__device__ __forceinline__ void qjl_scores_lut(const char* qb, int lane, const float* lut, float (&t)[G]) {
+  const uint4 z4 = reinterpret_cast<const uint4*>(qb)[lane];
+  const uint32_t zw[4] = {z4.x, z4.y, z4.z, z4.w};
+#pragma clang loop unroll(full)
+  for (int h = 0; h < G; ++h) t[h] = 0.f;
+#pragma clang loop unroll(full)
+  for (int n = 0; n < TQ_JL_DIM / 4; ++n) {
+    const uint32_t v = (zw[n >> 3] >> (4 * (n & 7))) & 0xFu;
+    const float* e = lut + (n * 16 + (int)v) * G;
+    if constexpr (G % 4 == 0) {
+#pragma clang loop unroll(full)
+      for (int h = 0; h < G; h += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(e + h);
+        t[h] += x.x;
+        t[h + 1] += x.y;
+        t[h + 2] += x.z;
+        t[h + 3] += x.w;
+      }
+    } else if constexpr (G == 2) {
+      const float2 x = *reinterpret_cast<const float2*>(e);
+      t[0] += x.x;
+      t[1] += x.y;
+    } else {
+      t[0] += e[0];
+    }
+  }
+}
+
 // Value accumulation of one packed page: lane (q, i) owns coordinates
 // 8i..8i+7 of tokens 4k+q; acc[h][e] += w[token][h] c[code].
 template <int B, int G>
@@ -705,6 +737,29 @@ void split_kernel(DecodeArgs a,
 
   const float* __restrict__ qrow = wsq + ((size_t)b * a.n_kv_heads + hkv) * kQPrepFloats * G;
 
+  // The other class's own launch keeps the QJL term's table (qjl_scores_lut):
+  // 32 x 16 x G floats built once per workgroup from the prepared S q.  The
+  // merged launches, whose LDS is sized for 4 waves per SIMD, keep the
+  // per-coordinate form (qjl_scores).
+  float* qlut = nullptr;
+  if constexpr (CLASS == 2) {
+    constexpr int kLut = TQ_JL_DIM / 4 * 16 * G;
+    __shared__ __align__(16) float lut[kLut];
+    qlut = lut;
+    if (a.qjl_s != nullptr) {
+      const float* qsv = qrow + 2 * D * G;
+      for (int idx = tid; idx < kLut; idx += blockDim.x) {
+        const int h = idx % G, v = (idx / G) & 15, n = idx / (16 * G);
+        const float* c = qsv + (n * G + h) * 4;
+        float sum = 0.f;
+#pragma clang loop unroll(full)
+        for (int e = 0; e < 4; ++e) sum += ((v >> e) & 1) ? c[e] : -c[e];
+        lut[idx] = sum;
+      }
+    }
+    __syncthreads();
+  }
+
   float m[G], l[G], acc[G][8];
 #pragma clang loop unroll(full)
   for (int h = 0; h < G; ++h) {
@@ -727,7 +782,7 @@ void split_kernel(DecodeArgs a,
     float qsum[G];
 #pragma clang loop unroll(full)
     for (int h = 0; h < G; ++h) qsum[h] = 0.f;
-    if (PC == 2 && a.qjl_s != nullptr) {
+    if (PC == 2 && CLASS != 2 && a.qjl_s != nullptr) {
       const float* qsv = qrow + 2 * D * G;
       const int i0 = 2 * lane;
 #pragma clang loop unroll(full)
@@ -791,7 +846,10 @@ void split_kernel(DecodeArgs a,
         for (int h = 0; h < G; ++h) s[h] *= nk;
         if (PC == 2 && qjl) {
           float t[G];
-          qjl_scores<G>(vblk, lane, qrow + 2 * D * G, qsum, t);
+          if constexpr (CLASS == 2)
+            qjl_scores_lut<G>(vblk, lane, qlut, t);
+          else
+            qjl_scores<G>(vblk, lane, qrow + 2 * D * G, qsum, t);
   #pragma clang loop unroll(full)
           for (int h = 0; h < G; ++h) s[h] = fmaf(gq, t[h], s[h]);
           vblk += 1280;

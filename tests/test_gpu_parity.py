@@ -135,6 +135,13 @@ def test_gqa_groups(dev, G):
     run_case(_all_bits_workload(G=G, pages=12), [0], dev, dequant=False)
 
 
+@pytest.mark.parametrize("G", [1, 2, 8])
+def test_gqa_groups_qjl(dev, G):
+    # every packed page carries the QJL sketch: the layer runs the other
+    # class's own launch, whose QJL term reads the per-workgroup sign table
+    run_case(_all_bits_workload(G=G, pages=12, qjl=True), [0], dev, dequant=False)
+
+
 def test_fp32_inputs_and_fp32_query(dev):
     run_case(_all_bits_workload(dtype="float32", pages=10), [0], dev, query_dtype=torch.float32)
 
