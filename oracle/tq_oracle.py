@@ -74,6 +74,14 @@ def rotation_matrix(signs: Sequence[int]) -> np.ndarray:
     return _rotation_cached(tuple(int(v) for v in np.asarray(signs).ravel())).copy()
 
 
+def signed_hadamard(signs: Sequence[int]) -> np.ndarray:
+    """D H D with D = diag(signs), the unnormalised rotation: entries +-1
+    (float64, exact).  u = sqrt(d) R x / n = (D H D x) / n, since the sqrt(d)
+    of R = D H D / sqrt(d) cancels."""
+    s = np.asarray(signs, dtype=np.float64).ravel()
+    return s[:, None] * sylvester_hadamard(s.shape[0]).astype(np.float64) * s[None, :]
+
+
 @lru_cache(maxsize=64)
 def _rotation_cached(signs: Tuple[int, ...]) -> np.ndarray:
     s = np.asarray(signs, dtype=np.float64)
@@ -525,12 +533,13 @@ def encode(X: np.ndarray, signs, bits: int, kind: int = LLOYD_MAX,
     flagged coordinates (any other override raises ValueError).
     """
     X = np.asarray(X, dtype=np.float64)
-    d = X.shape[-1]
-    R = rotation_matrix(signs)
     n = np.sqrt(np.sum(X * X, axis=-1))
-    Y = X @ R.T
+    # D H D x with the integer matrix: the products are exact and, for fp16
+    # inputs, so are the sums, so a coordinate that cancels is exactly 0 (a
+    # tie at the middle boundary) rather than a rounding residue of either sign
+    Y = X @ signed_hadamard(signs).T
     safe = np.where(n > 0, n, 1.0)
-    U = np.where(n[:, None] > 0, math.sqrt(d) * Y / safe[:, None], 0.0)
+    U = np.where(n[:, None] > 0, Y / safe[:, None], 0.0)
     c32, t32 = codebook(bits, kind)
     t64 = t32.astype(np.float64)
     L = 1 << bits

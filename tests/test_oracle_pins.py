@@ -310,6 +310,60 @@ def test_qjl_estimator_unbiased_with_closed_form_variance():
     assert abs(est.var() / var - 1) < 0.15
 
 
+def test_qjl_key_estimate_unbiased_through_encode_and_reconstruct():
+    """The whole QJL key path of the oracle, composed: x_hat from the codec,
+    (z, gamma) = qjl_encode(x, x_hat, S), r_hat = qjl_reconstruct(z, gamma, S).
+    Over Gaussian S the attended key x_hat + r_hat is an unbiased estimate of
+    x along any q ("TurboMOQ", QJL residual correction: the sign sketch
+    corrects the residual), with variance ((pi/2) |q|^2 |r|^2 - (q.r)^2) / m
+    for r = x - x_hat (the sign of a Gaussian projection: E[sign(s.r) s] =
+    sqrt(2/pi) r/|r|).  A residual taken the other way round (x_hat - x) would
+    centre the estimate on 2 q.x_hat - q.x instead."""
+    rng = np.random.default_rng(41)
+    signs = W.rotation_signs(42, 3)
+    x = rng.standard_normal((1, 128))
+    e = O.encode(x, signs, 2)
+    xh = O.dequantize(e["norm"], e["codes"], signs, 2)
+    r = (x - xh)[0]
+    q = rng.standard_normal(128)
+    m, trials = 128, 4000
+    est = np.empty(trials)
+    for k in range(trials):
+        S = rng.standard_normal((m, 128))
+        qj = O.qjl_encode(x, xh, S)
+        est[k] = q @ (xh[0] + O.qjl_reconstruct(qj["z"], qj["gamma"], S)[0])
+    g32 = float(np.float32(np.linalg.norm(r)))
+    scale = g32 / np.linalg.norm(r)          # gamma is stored in float32
+    mean = q @ xh[0] + scale * (q @ r)
+    var = ((math.pi / 2) * (q @ q) * g32 ** 2 - (scale * (q @ r)) ** 2) / m
+    assert abs(mean - q @ x[0]) < 1e-6 * abs(q @ x[0]) + 1e-9
+    assert abs(est.mean() - mean) < 4 * math.sqrt(var / trials)
+    assert abs(est.var() / var - 1) < 0.15
+    wrong = 2 * (q @ xh[0]) - q @ x[0]
+    assert abs(est.mean() - wrong) > 8 * math.sqrt(var / trials)
+
+
+def test_qjl_orientation_with_a_permutation_sketch():
+    """S a permutation matrix (row i selects coordinate pi(i)): the sketch is
+    z_i = [r_pi(i) >= 0] and the reconstruction sqrt(pi/2)/m gamma S^T (2z - 1)
+    is sqrt(pi/2)/m gamma sign(r), coordinate by coordinate.  S^T in place of
+    S would select pi^-1(i) instead."""
+    rng = np.random.default_rng(43)
+    perm = rng.permutation(128)
+    assert np.any(perm[perm] != np.arange(128))      # not an involution: S != S^T
+    S = np.zeros((128, 128))
+    S[np.arange(128), perm] = 1.0
+    x = rng.standard_normal((3, 128))
+    xh = 0.7 * x + 0.2 * rng.standard_normal((3, 128))
+    r = x - xh
+    qj = O.qjl_encode(x, xh, S)
+    assert np.array_equal(qj["z"], r[:, perm] >= 0)
+    assert np.array_equal(qj["gamma"], np.linalg.norm(r, axis=1).astype(np.float32))
+    rh = O.qjl_reconstruct(qj["z"], qj["gamma"], S)
+    expect = math.sqrt(math.pi / 2) / 128 * qj["gamma"].astype(np.float64)[:, None] * np.where(r >= 0, 1.0, -1.0)
+    assert np.allclose(rh, expect, rtol=1e-14, atol=0)
+
+
 def test_qjl_encode_scale_and_signs():
     rng = np.random.default_rng(5)
     x = rng.standard_normal((8, 128))
