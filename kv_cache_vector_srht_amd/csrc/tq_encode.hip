@@ -9,6 +9,7 @@
 // norm, and the signs of S r for r = x - xhat ("TurboMOQ", QJL residual
 // correction), the sketch on the matrix cores.
 #include <algorithm>
+#include <atomic>
 
 #include "tq_device.h"
 #include "tq_token_encoder.h"
@@ -168,10 +169,9 @@ __global__ __launch_bounds__(64 * kQjlWaves) void qjl_keys_kernel(EncodeArgs a, 
 //
 // Codes of u = H D x / ||x|| come from the width's lookup grid in LDS
 // (code = count below the bin + [u >= the bin's boundary]), so one code path
-// serves every width.  The outer D is applied afterwards as a code flip:
-// exact, because the float32 boundary sets are symmetric
-// (code(-u) = L-1-code(u) except at exact ties, which lie inside the boundary
-// allowance).  Codes go to an LDS byte matrix [token][coordinate]; each lane
+// serves every width.  The outer D (times the lane's sign, below) is applied
+// to u before the lookup, so exact ties round up on every coordinate.  Codes
+// go to an LDS byte matrix [token][coordinate]; each lane
 // then packs 32 consecutive codes of one stream (exactly b dwords) with a
 // streaming accumulator whose flush points are uniform.
 constexpr int kRowStride = 144;            // LDS byte-matrix row: 128 codes + pad
@@ -234,7 +234,7 @@ struct Lut {
 
 struct EncodeLane {
   uint32_t hmask[16];   // D sign bits of the lane's value pairs, placed for an fp16x2 xor
-  uint32_t fmask[8];    // per code byte: 0xff when the code is flipped (outer D times the lane's sign)
+  uint32_t fl;          // bit s: slot s's transform is negated (outer D times the lane's sign)
   uint32_t dl;          // D bits of the lane's 32 slots
 };
 
@@ -304,7 +304,7 @@ __device__ __forceinline__ float encode_quarter(const void* src, size_t row_off,
   // lane computes mine + sg * partner (one multiply-add with the partner read
   // through DPP), so an upper lane keeps the negated butterfly output; after
   // both stages lane e holds rho_e times the transform, rho_e = -1 for e = 1, 2,
-  // which the code flip below undoes (the flip mask carries it).
+  // which the sign applied before quantising undoes (EncodeLane::fl carries it).
   quad_butterfly<0xB1>(x, (e & 1) ? -1.f : 1.f);
   quad_butterfly<0x4E>(x, (e & 2) ? -1.f : 1.f);
   const float n = sqrtf(ss);
@@ -353,6 +353,9 @@ __device__ __forceinline__ float encode_quarter(const void* src, size_t row_off,
                 (pa >= pb ? 1u : 0u) +                                // tan(pi/4)
                 (pa >= 2.41421356237309503f * pb ? 1u : 0u);          // tan(3 pi/8)
         }
+        // a zero pair takes the angle atan2(+0, +0) = 0 (quadrant 2, no edge
+        // passed), whatever the signs of its zeros; pa = 0 < pb gives 0 anyway
+        if (pa == 0.f) sub = 0;
         tc = qd * (uint32_t)(L >> 2) + sub;
       }
       cb[s0 >> 2] |= rc << (8 * (s0 & 3));
@@ -364,12 +367,16 @@ __device__ __forceinline__ float encode_quarter(const void* src, size_t row_off,
           make_uint2(cb[2 * c], cb[2 * c + 1]);
     return n;
   }
+  // u carries its sign (outer D times the lane's sign) before the lookup, so
+  // that an exact tie u = t_k counts t_k on every coordinate (#{t_k <= u}),
+  // as for unflipped ones: a code flip after quantising would count it on
+  // flipped coordinates only (L - 1 - #{t_k <= -u} = #{t_k < u}).
   if (lut.nb == kLutByteBins) {
     // 256-bin grid: the bin is u S + O (O carries the -1/2) rounded and
     // saturated to a byte by one conversion
 #pragma clang loop unroll(full)
     for (int s = 0; s < 32; ++s) {
-      const float u = x[s] * inv;
+      const float u = flip_if(x[s] * inv, (el.fl >> s) & 1u);
       const uint32_t bin = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(u, lut.S, lut.O), 0, 0u);
       const uint2 en = ent[bin];
       const uint32_t c = en.x + (u >= __uint_as_float(en.y) ? 1u : 0u);
@@ -378,7 +385,7 @@ __device__ __forceinline__ float encode_quarter(const void* src, size_t row_off,
   } else {
 #pragma clang loop unroll(full)
     for (int s = 0; s < 32; ++s) {
-      const float u = x[s] * inv;
+      const float u = flip_if(x[s] * inv, (el.fl >> s) & 1u);
       // bin = clamp(floor(u S + O), 0, nb - 1), clamped in float (one med3)
       const int bin = (int)__builtin_amdgcn_fmed3f(fmaf(u, lut.S, lut.O), 0.f, lut.fmax);
       const uint2 en = ent[bin];
@@ -386,13 +393,10 @@ __device__ __forceinline__ float encode_quarter(const void* src, size_t row_off,
       cb[s >> 2] |= c << (8 * (s & 3));
     }
   }
-  const uint32_t flip = ((1u << B) - 1u) * 0x01010101u;
   // chunk c holds coordinates 32c + 8e .. +7: row bytes 32c + 8e
 #pragma clang loop unroll(full)
-  for (int c = 0; c < 4; ++c) {
-    const uint2 v = make_uint2(cb[2 * c] ^ (el.fmask[2 * c] & flip), cb[2 * c + 1] ^ (el.fmask[2 * c + 1] & flip));
-    *reinterpret_cast<uint2*>(reinterpret_cast<char*>(mat_row) + 32 * c + 8 * e) = v;
-  }
+  for (int c = 0; c < 4; ++c)
+    *reinterpret_cast<uint2*>(reinterpret_cast<char*>(mat_row) + 32 * c + 8 * e) = make_uint2(cb[2 * c], cb[2 * c + 1]);
   return n;
 }
 
@@ -471,14 +475,8 @@ __global__ __launch_bounds__(kEncodeBlock) void encode_pages_kernel(EncodeArgs a
 #pragma clang loop unroll(full)
     for (int i = 0; i < 16; ++i)
       el.hmask[i] = (((el.dl >> (2 * i)) & 1u) << 15) | (((el.dl >> (2 * i + 1)) & 1u) << 31);
-#pragma clang loop unroll(full)
-    for (int i = 0; i < 8; ++i) {
-      uint32_t f = 0;
-#pragma clang loop unroll(full)
-      for (int k = 0; k < 4; ++k) f |= ((el.dl >> (4 * i + k)) & 1u) ? (0xffu << (8 * k)) : 0u;
-      // lanes 1 and 2 of the quad hold the negated transform (see encode_quarter)
-      el.fmask[i] = (e == 1 || e == 2) ? ~f : f;
-    }
+    // lanes 1 and 2 of the quad hold the negated transform (see encode_quarter)
+    el.fl = (e == 1 || e == 2) ? ~el.dl : el.dl;
   }
   int cur_kb = -1, cur_vb = -1;
   Lut lk{0.f, 0.f, 1, 0.f}, lv{0.f, 0.f, 1, 0.f};
@@ -608,6 +606,22 @@ __global__ __launch_bounds__(kEncodeBlock) void encode_pages_kernel(EncodeArgs a
 using namespace tq;
 using namespace tq::dev;
 
+namespace {
+
+// Compute units of device `dev`, queried once per device and cached in an
+// atomic (calls from several host threads may race to store the same value).
+int compute_units(int dev) {
+  static std::atomic<int> cached[64];
+  if (dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n >= 1) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) return 256;
+  cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+}  // namespace
+
 extern "C" {
 
 int tq_encode_kv(const tq_layer* layer, const tq_cache* cache, const tq_kv_input* in, void* stream) {
@@ -676,14 +690,8 @@ int tq_encode_kv(const tq_layer* layer, const tq_cache* cache, const tq_kv_input
   if (layer->qjl_s) {
     // keys of QJL pages: codes, norm and sign sketch, a page per wave on
     // persistent workgroups (as many as the items need, at most two per CU)
-    static int cu_count[64] = {};   // per device, read once (a benign race: same value)
     int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
-      if (cu_count[dev] < 1 &&
-          hipDeviceGetAttribute(&cu_count[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cu_count[dev] = 0;
-      if (cu_count[dev] >= 1) cus = cu_count[dev];
-    }
+    if (hipGetDevice(&dev) == hipSuccess) cus = compute_units(dev);
     const int64_t items = (int64_t)n_pages * cache->n_kv_heads * cache->n_sessions;
     const int64_t want = (items + kQjlWaves - 1) / kQjlWaves;
     const int blocks = (int)std::min<int64_t>(want, (int64_t)cus * kQjlBlocksPerCU);

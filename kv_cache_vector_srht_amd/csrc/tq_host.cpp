@@ -55,6 +55,14 @@ struct GaussianModel {
 //   d(2m+1) = -(a+m)(a+b+m) x / ((a+2m)(a+2m+1)),  d(2m) = m(b-m) x / ((a+2m-1)(a+2m)),
 // evaluated front to back with the modified Lentz method, on the side of the
 // symmetry I_x(a, b) = 1 - I_{1-x}(b, a) where the fraction converges fast.
+// log Gamma(x) for x > 0.  lgammal also stores the sign of Gamma in the
+// process-wide signgam, a data race between host threads; lgammal_r returns
+// it through an argument instead.
+static ld log_gamma(ld x) {
+  int sign = 0;
+  return lgammal_r(x, &sign);
+}
+
 static ld incomplete_beta(ld a, ld b, ld x) {
   if (x <= 0.0L) return 0.0L;
   if (x >= 1.0L) return 1.0L;
@@ -77,7 +85,7 @@ static ld incomplete_beta(ld a, ld b, ld x) {
     value *= step;
     if (fabsl(step - 1.0L) < 1e-21L) break;
   }
-  const ld lfront = a * logl(x) + b * log1pl(-x) - (lgammal(a) + lgammal(b) - lgammal(a + b)) - logl(a);
+  const ld lfront = a * logl(x) + b * log1pl(-x) - (log_gamma(a) + log_gamma(b) - log_gamma(a + b)) - logl(a);
   return expl(lfront) * value;
 }
 
@@ -88,7 +96,7 @@ static ld incomplete_beta(ld a, ld b, ld x) {
 struct SphereModel {
   ld d, c;
   explicit SphereModel(int dim) : d((ld)dim) {
-    c = expl(lgammal(0.5L * d) - lgammal(0.5L * (d - 1.0L))) / sqrtl(3.14159265358979323846264338327950288L * d);
+    c = expl(log_gamma(0.5L * d) - log_gamma(0.5L * (d - 1.0L))) / sqrtl(3.14159265358979323846264338327950288L * d);
   }
   ld end() const { return sqrtl(d); }
   ld density(ld x) const {

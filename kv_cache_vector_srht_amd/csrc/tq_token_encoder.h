@@ -129,7 +129,8 @@ __device__ __forceinline__ float rotate_quantize_polar(float (&x)[D], const uint
   for (int i = 0; i < D / 2; ++i) {
     const float u0 = x[2 * i], u1 = x[2 * i + 1];
     const float r = sqrtf(fmaf(u0, u0, u1 * u1));
-    const float th = atan2f(u1, u0);
+    // a zero pair takes the angle atan2(+0, +0) = 0, whatever its zeros' signs
+    const float th = (u0 == 0.f && u1 == 0.f) ? 0.f : atan2f(u1, u0);
     const uint32_t rc = quantize<B>(r, thr);
     const uint32_t tc = (uint32_t)(int)floorf((th + kPi) * kSectors) & (uint32_t)(L - 1);
     emit(2 * i, rc);

@@ -12,7 +12,7 @@ import pytest
 
 import workloads as W
 from oracle import tq_oracle as O
-from tests.gpu_parity import NORM_RTOL, Tally, compare_attention, compare_unit_full
+from tests.gpu_parity import NORM_ULPS, Tally, compare_attention, compare_unit_full, ulps32
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -88,7 +88,7 @@ def compare_demoted(raw, old, new, K, V, signs, t, k_kind, v_kind, what):
             assert ok.all(), f"{what} {which}: {int((~ok).sum())} requantised codes differ away from a boundary"
             t.mismatches += int(diff.sum())
         norm = np.frombuffer(part(f"{which}_norm"), dtype="<f4")
-        assert np.allclose(norm, e["norm"], rtol=NORM_RTOL, atol=0), f"{what} {which} norms"
+        assert ulps32(norm, e["norm"]) <= NORM_ULPS, f"{what} {which} norms"
         recon[which] = O.dequantize(e["norm"], g, signs, nb, kind)
     return recon["k"], recon["v"]
 

@@ -305,3 +305,28 @@ def make_query(w: Workload, layer: int, device="cpu"):
 def gaussian_rows(seed: int, n: int, dim: int = HEAD_DIM) -> np.ndarray:
     """Plain N(0,1) float64 rows for small statistical checks."""
     return np.random.Generator(np.random.PCG64(seed)).standard_normal((n, dim))
+
+
+def degenerate_rows(signs) -> np.ndarray:
+    """Eight head vectors [8, 128] (float64, exactly representable in fp16)
+    for the degenerate cases of the codec: exact ties and the zero vector.
+
+    Row 0 is the zero vector and row 1 the zero vector of negative zeros
+    (their norm is 0).  Rows 2-4 are sums and differences of two or four basis
+    vectors and row 5 a scaled basis vector: under a Walsh-Hadamard rotation
+    with any sign diagonal their coordinates are sums of a few +-1 terms, many
+    of which cancel exactly, so those coordinates sit exactly on the middle
+    decision boundary 0 of every even number of levels.  Row 6 is the sign
+    vector itself scaled, x = c D: D H D x = c D H 1 is zero outside its first
+    coordinate.  Row 7 is a basis vector scaled by -2.
+    """
+    s = np.asarray(signs, dtype=np.float64)
+    X = np.zeros((8, HEAD_DIM))
+    X[1] = -0.0
+    X[2, [0, 1]] = 1.0
+    X[3, 5], X[3, 77] = 3.5, -3.5
+    X[4, [9, 10, 40, 100]] = 0.75
+    X[5, 64] = 0.5
+    X[6] = 0.25 * s
+    X[7, 127] = -2.0
+    return X
