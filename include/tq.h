@@ -405,6 +405,23 @@ int tq_decode_attention_mass(const tq_layer* layer, const tq_cache* cache,
                              const tq_query* query, float* out, float* page_mass,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* tq_decode_attention without a caller's workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The query-prep rows and split partials
+ * live in a file-scope device array of the library, TQ_NOALLOC_SCRATCH_BYTES
+ * bytes per GPU, allocated with the library's code object and held until the
+ * process ends; its device address is looked up once per device on the first
+ * call there.  The call itself allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine) and needs nothing cleared.  Every call on one
+ * GPU shares that GPU's array: calls that overlap on one GPU (other streams,
+ * other host threads) race and give wrong results; serialise them.  Returns
+ * TQ_ERR_WORKSPACE when tq_decode_workspace_bytes(cache, n_q_heads) exceeds
+ * TQ_NOALLOC_SCRATCH_BYTES (then nothing is launched); otherwise as
+ * tq_decode_attention, with the same results bit for bit. */
+#define TQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+int tq_decode_attention_noalloc(const tq_layer* layer, const tq_cache* cache,
+                                const tq_query* query, float* out, void* stream);
+
 /* Dense reconstruction of tokens [tok0, tok0 + ntok) of every (session,
  * KV head): out[b][h][t][0..127] float32 (device, contiguous).  which = 0 keys,
  * 1 values; add_qjl adds the QJL residual on keys of QJL pages.  fp16 pages

@@ -35,7 +35,8 @@ EXPORTS = ("tq_page_bytes", "tq_page_descriptor", "tq_build_codebook", "tq_codeb
            "tq_layer_params", "tq_sign_mask", "tq_decode_workspace_bytes", "tq_cache_bytes",
            "tq_status_string", "tq_last_error", "tq_encode_kv", "tq_decode_attention",
            "tq_dequantize", "tq_append_kv", "tq_retier_pages", "tq_decode_attention_mass",
-           "tq_fit_codebook", "tq_calibrated_table")
+           "tq_fit_codebook", "tq_calibrated_table", "tq_decode_attention_noalloc")
+NOALLOC_SCRATCH_BYTES = 32 << 20     # TQ_NOALLOC_SCRATCH_BYTES
 
 
 class TQError(RuntimeError):
@@ -115,6 +116,8 @@ def lib() -> ctypes.CDLL:
         L.tq_decode_attention_mass.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
                                                ctypes.POINTER(tq_query), ctypes.c_void_p, ctypes.c_void_p,
                                                ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.tq_decode_attention_noalloc.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
+                                                  ctypes.POINTER(tq_query), ctypes.c_void_p, ctypes.c_void_p]
         L.tq_append_kv.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
                                    ctypes.POINTER(tq_token_input), ctypes.c_void_p]
         L.tq_retier_pages.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache), ctypes.c_void_p,
@@ -425,6 +428,23 @@ def decode_attention(layer: Layer, cache: Cache, q, out=None, workspace=None,
                                          ctypes.byref(qs), out.data_ptr(), page_mass.data_ptr(),
                                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                          _stream(q.device)), "tq_decode_attention_mass")
+    return out
+
+
+def decode_attention_noalloc(layer: Layer, cache: Cache, q, out, softmax_scale: float = 0.0,
+                             qjl_scoring: int = 0):
+    """tq_decode_attention_noalloc: decode attention into a caller's ``out``
+    [B, H_q, 128] float32 with the library's built-in device scratch in place
+    of a workspace; allocates nothing.  Calls that overlap on one GPU race."""
+    import torch
+    if q.dim() != 3 or q.shape[0] != cache.n_sessions or q.shape[-1] != HEAD_DIM or q.stride(-1) != 1:
+        raise TQError(f"q must be [B, H_q, 128] with unit innermost stride, got {tuple(q.shape)}")
+    if out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != (q.shape[0], q.shape[1], HEAD_DIM):
+        raise TQError("out must be a contiguous float32 [B, H_q, 128] tensor")
+    qs = tq_query(q.data_ptr(), _dtype_code(q), q.shape[1], q.stride(0), q.stride(1), softmax_scale, qjl_scoring)
+    check(lib().tq_decode_attention_noalloc(ctypes.byref(layer.struct), ctypes.byref(cache.struct),
+                                            ctypes.byref(qs), out.data_ptr(), _stream(q.device)),
+          "tq_decode_attention_noalloc")
     return out
 
 

@@ -11,6 +11,7 @@
 // rotation per query head (the Walsh-Hadamard transform factored out of the
 // value sum, as the MLX TurboQuant skill page reports for its Metal kernels,
 // Path A > Optimisations Metal).
+#include <atomic>
 #include <cstring>
 #include <type_traits>
 
@@ -1287,9 +1288,50 @@ int decode_impl(const tq_layer* layer, const tq_cache* cache, const tq_query* qu
   return launch_status("combine");
 }
 
+// Device scratch of tq_decode_attention_noalloc: the query-prep rows and the
+// split partials, in a file-scope device array (one copy per GPU, allocated
+// with the code object and held until the process ends) in place of a caller's
+// workspace.
+constexpr size_t kScratchBytes = TQ_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) char scratch[kScratchBytes];
+
+// The device address of `scratch` on the current device, looked up once per
+// device.  In host code the array's name is only a host-side stand-in, never a
+// device address.
+int scratch_address(void** out) {
+  static std::atomic<void*> cached[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TQ_ERR_DEVICE, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(TQ_ERR_UNSUPPORTED, "device %d: at most 64 devices", dev);
+  void* p = cached[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(TQ_ERR_DEVICE, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    cached[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
+
+int tq_decode_attention_noalloc(const tq_layer* layer, const tq_cache* cache, const tq_query* query,
+                                float* out, void* stream) {
+  if (!cache || !query) return fail(TQ_ERR_INVALID_ARG, "null cache or query");
+  const size_t need = tq_decode_workspace_bytes(cache, query->n_q_heads);
+  if (need == 0) return fail(TQ_ERR_INVALID_ARG, "invalid cache or query-head count");
+  if (need > kScratchBytes)
+    return fail(TQ_ERR_WORKSPACE, "decode needs %zu bytes of scratch; the built-in scratch holds %zu",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  const int st = scratch_address(&ws);
+  if (st) return st;
+  return decode_impl(layer, cache, query, out, nullptr, ws, kScratchBytes, stream);
+}
 
 int tq_decode_attention(const tq_layer* layer, const tq_cache* cache, const tq_query* query,
                         float* out, void* workspace, size_t workspace_bytes, void* stream) {
