@@ -98,9 +98,11 @@ enum { TQ_QJL_SCORE_UNBIASED = 0, TQ_QJL_SCORE_SIGN = 1 };
  *   K norms   64 x float32
  *   [QJL]     64 x 16 B sign words (bit i of token t's word = z_i), then
  *             64 x float32 gamma
- *   V codes   1024*v_bits : 64 streams as above, but stream s = 16q+i holds,
- *             for k = 0..15 and e = 0..7, the code of token 4k+q,
- *             coordinate 8i+e at stream position 8k+e
+ *   V codes   1024*v_bits : 64 streams as above, but stream s = n + 32P
+ *             (n < 32, P in {0, 1}) holds one coordinate pair over the
+ *             page: token t's codes of coordinates c0 and c0 + 1 at stream
+ *             positions 2t and 2t+1, where c0 = 64*((n >> 2) & 1) + 32P +
+ *             8*(n >> 3) + 2*(n & 3)
  *   V norms   64 x float32
  * fp16 page: 64 rows of K then 64 rows of V, fp16, 128 values per row.
  * These layouts are a convention of this library (the pages name bit packing

@@ -138,7 +138,8 @@ struct SplitLds {
   float4 vquad[272];
   float kcent[512];           // centroid lists for every bit width (table layout)
   float vcent[512];
-  float w[kDecodeWaves][PT * G];           // softmax weights of the current page
+  float w[kDecodeWaves][(G < 4 ? 4 : G) * PT];   // weights of the current page, [head][token]
+                                                 // (rows G..3 stay zero)
   float red[kDecodeWaves][G * D];          // workgroup reduction
   float stat[kDecodeWaves][2][G];          // m, l per wave
   uint64_t desc[kMaxPagesPerSplit];        // the range's page descriptors, read once
@@ -157,18 +158,13 @@ __device__ __forceinline__ int quad_offset(int b) { return b == 1 ? 0 : 16; }
 // the LDS codebook lookups and return out of order, so the loop is pipelined by
 // hand: for chunk n the first FMA waits for chunk n's data only, then chunk
 // n+1's scalar loads and lookups are issued, then the rest of chunk n runs.
-template <int B, int G>
-__device__ __forceinline__ void key_scores(const char* blk, int lane, const float* __restrict__ qr,
-                                           const float2* pair, const float4* quad, const float* cent,
-                                           float (&s)[G]) {
+// The stream's words come in `sw` (its first 4B dwords are used).
+template <int B, int G, int N>
+__device__ __forceinline__ void key_scores_w(const uint32_t (&sw)[N], const float* __restrict__ qr,
+                                             const float2* pair, const float4* quad, const float* cent,
+                                             float (&s)[G]) {
+  static_assert(N >= 4 * B, "the stream's words");
   constexpr int CH = 4;                       // coordinates per chunk
-  uint32_t sw[4 * B];
-  const uint4* src = reinterpret_cast<const uint4*>(blk);
-#pragma clang loop unroll(full)
-  for (int w = 0; w < B; ++w) {
-    const uint4 v = src[w * 64 + lane];
-    sw[4 * w] = v.x; sw[4 * w + 1] = v.y; sw[4 * w + 2] = v.z; sw[4 * w + 3] = v.w;
-  }
 #pragma clang loop unroll(full)
   for (int h = 0; h < G; ++h) s[h] = 0.f;
   float qa[G][CH], qb[G][CH], ca[CH], cb[CH];
@@ -217,6 +213,20 @@ __device__ __forceinline__ void key_scores(const char* blk, int lane, const floa
     __builtin_amdgcn_sched_barrier(0);
     fmas(qb, cb, 1, CH);
   }
+}
+
+template <int B, int G>
+__device__ __forceinline__ void key_scores(const char* blk, int lane, const float* __restrict__ qr,
+                                           const float2* pair, const float4* quad, const float* cent,
+                                           float (&s)[G]) {
+  uint32_t sw[4 * B];
+  const uint4* src = reinterpret_cast<const uint4*>(blk);
+#pragma clang loop unroll(full)
+  for (int w = 0; w < B; ++w) {
+    const uint4 v = src[w * 64 + lane];
+    sw[4 * w] = v.x; sw[4 * w + 1] = v.y; sw[4 * w + 2] = v.z; sw[4 * w + 3] = v.w;
+  }
+  key_scores_w<B, G>(sw, qr, pair, quad, cent, s);
 }
 
 // Key scores of an fp16 page, lane = token, with the unrotated query.
@@ -306,55 +316,47 @@ __device__ __forceinline__ void qjl_scores_lut(const char* qb, int lane, const f
   }
 }
 
-// Value accumulation of one packed page: lane (q, i) owns coordinates
-// 8i..8i+7 of tokens 4k+q; acc[h][e] += w[token][h] c[code].
-template <int B, int G>
-__device__ __forceinline__ void value_accum(const char* blk, int lane, const float* wv,
-                                            const float2* pair, const float4* quad, const float* cent,
-                                            float (&acc)[G][8]) {
-  uint32_t sw[4 * B];
-  const uint4* src = reinterpret_cast<const uint4*>(blk);
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Value sums of one packed page on the matrix cores (v_mfma_f32_4x4x1f32, 16
+// independent 4 x 4 outer products per instruction, exact float32 products).
+// Per token t: lane L (block L / 4, column L % 4) brings the value of its V
+// stream's first coordinate (then its second) as the B operand, and the A
+// operand p'[4 g + L % 4][t], the weight (times the token's norm) of query head
+// 4 g + L % 4, from the wave's weight rows in LDS (rows past the group are
+// zero); register i of acc[g][k] of lane L then accumulates head 4 g + i,
+// coordinate v_stream_coord(L, k).  Codes of stream L: positions 2t, 2t + 1.
+template <int B, int NG, int N>
+__device__ __forceinline__ void value_mfma_w(const uint32_t (&sw)[N], int lane, const float* wv,
+                                             const float2* pair, const float4* quad,
+                                             v4f (&acc)[NG][2]) {
+  static_assert(N >= 4 * B, "the stream's words");
+  const float* wl = wv + (lane & 3) * PT;
 #pragma clang loop unroll(full)
-  for (int w = 0; w < B; ++w) {
-    const uint4 v = src[w * 64 + lane];
-    sw[4 * w] = v.x; sw[4 * w + 1] = v.y; sw[4 * w + 2] = v.z; sw[4 * w + 3] = v.w;
-  }
-  const int q = lane >> 4;
+  for (int t4 = 0; t4 < PT / 4; ++t4) {
+    float4 a[NG];
 #pragma clang loop unroll(full)
-  for (int k = 0; k < 16; ++k) {
-    float wt[G];
+    for (int g = 0; g < NG; ++g) a[g] = *reinterpret_cast<const float4*>(wl + 4 * g * PT + 4 * t4);
 #pragma clang loop unroll(full)
-    for (int h = 0; h < G; ++h) wt[h] = wv[(4 * k + q) * G + h];
-    if constexpr (B <= 2) {
-#pragma clang loop unroll(full)
-      for (int e = 0; e < 8; e += 4) {
-        const float4 c = quad[quad_offset(B) + bits_at(sw, (8 * k + e) * B, 4 * B)];
-#pragma clang loop unroll(full)
-        for (int h = 0; h < G; ++h) {
-          acc[h][e] = fmaf(wt[h], c.x, acc[h][e]);
-          acc[h][e + 1] = fmaf(wt[h], c.y, acc[h][e + 1]);
-          acc[h][e + 2] = fmaf(wt[h], c.z, acc[h][e + 2]);
-          acc[h][e + 3] = fmaf(wt[h], c.w, acc[h][e + 3]);
-        }
+    for (int e = 0; e < 4; e += 2) {
+      const int t = 4 * t4 + e;
+      float c[4];   // (t, first), (t, second), (t + 1, first), (t + 1, second)
+      if constexpr (B <= 2) {
+        const float4 q = quad[quad_offset(B) + bits_at(sw, 2 * t * B, 4 * B)];
+        c[0] = q.x; c[1] = q.y; c[2] = q.z; c[3] = q.w;
+      } else {
+        const float2* pt = pair + pair_offset(B);
+        const float2 p0 = pt[bits_at(sw, 2 * t * B, 2 * B)];
+        const float2 p1 = pt[bits_at(sw, 2 * (t + 1) * B, 2 * B)];
+        c[0] = p0.x; c[1] = p0.y; c[2] = p1.x; c[3] = p1.y;
       }
-    } else if constexpr (B <= 4) {
-      const float2* pt = pair + pair_offset(B);
 #pragma clang loop unroll(full)
-      for (int e = 0; e < 8; e += 2) {
-        const float2 c = pt[bits_at(sw, (8 * k + e) * B, 2 * B)];
-#pragma clang loop unroll(full)
-        for (int h = 0; h < G; ++h) {
-          acc[h][e] = fmaf(wt[h], c.x, acc[h][e]);
-          acc[h][e + 1] = fmaf(wt[h], c.y, acc[h][e + 1]);
-        }
-      }
-    } else {
-      const float* ct = cent + centroid_offset(B);
-#pragma clang loop unroll(full)
-      for (int e = 0; e < 8; ++e) {
-        const float c = ct[bits_at(sw, (8 * k + e) * B, B)];
-#pragma clang loop unroll(full)
-        for (int h = 0; h < G; ++h) acc[h][e] = fmaf(wt[h], c, acc[h][e]);
+      for (int g = 0; g < NG; ++g) {
+        const float a0 = e == 0 ? a[g].x : a[g].z, a1 = e == 0 ? a[g].y : a[g].w;
+        acc[g][0] = __builtin_amdgcn_mfma_f32_4x4x1f32(a0, c[0], acc[g][0], 0, 0, 0);
+        acc[g][1] = __builtin_amdgcn_mfma_f32_4x4x1f32(a0, c[1], acc[g][1], 0, 0, 0);
+        acc[g][0] = __builtin_amdgcn_mfma_f32_4x4x1f32(a1, c[2], acc[g][0], 0, 0, 0);
+        acc[g][1] = __builtin_amdgcn_mfma_f32_4x4x1f32(a1, c[3], acc[g][1], 0, 0, 0);
       }
     }
   }
@@ -421,14 +423,29 @@ __device__ __forceinline__ void key_scores_wide(const char* blk, int lane, const
   }
 }
 
-// Value accumulation of a packed page at 5-8 bits, in the same four passes:
-// pass n holds tokens 4k + q for k = 4n .. 4n + 3.
-template <int B, int G>
-__device__ __forceinline__ void value_accum_wide(const char* blk, int lane, const float* wv,
-                                                 const float* cent, float (&acc)[G][8]) {
+template <int B, int NG>
+__device__ __forceinline__ void value_mfma(const char* blk, int lane, const float* wv,
+                                           const float2* pair, const float4* quad,
+                                           v4f (&acc)[NG][2]) {
+  uint32_t sw[4 * B];
+  const uint4* src = reinterpret_cast<const uint4*>(blk);
+#pragma clang loop unroll(full)
+  for (int w = 0; w < B; ++w) {
+    const uint4 v = src[w * 64 + lane];
+    sw[4 * w] = v.x; sw[4 * w + 1] = v.y; sw[4 * w + 2] = v.z; sw[4 * w + 3] = v.w;
+  }
+  value_mfma_w<B, NG>(sw, lane, wv, pair, quad, acc);
+}
+
+// Value sums of a packed page at 5-8 bits, as value_mfma with one centroid
+// lookup per code, in four passes of 16 tokens: a pass's 32 codes of the
+// stream are exactly B dwords (B n .. B n + B - 1), loaded one pass ahead.
+template <int B, int NG>
+__device__ __forceinline__ void value_mfma_wide(const char* blk, int lane, const float* wv, const float* cent,
+                                                v4f (&acc)[NG][2]) {
   const uint32_t* src = reinterpret_cast<const uint32_t*>(blk);
   const float* ct = cent + centroid_offset(B);
-  const int q = lane >> 4;
+  const float* wl = wv + (lane & 3) * PT;
   uint32_t w[B], nx[B];
   auto load = [&](int n, uint32_t (&d)[B]) {
 #pragma clang loop unroll(full)
@@ -441,35 +458,23 @@ __device__ __forceinline__ void value_accum_wide(const char* blk, int lane, cons
 #pragma clang loop unroll(disable)
   for (int n = 0; n < 4; ++n) {
     load(min(n + 1, 3), nx);
-    // one token's weights and codes in flight while the previous one's FMAs run
-    float wa[G], wb[G], ca[8], cb[8];
-    auto fetch = [&](int kk, float (&wd)[G], float (&cd)[8]) {
 #pragma clang loop unroll(full)
-      for (int h = 0; h < G; ++h) wd[h] = wv[(4 * (4 * n + kk) + q) * G + h];
+    for (int t4 = 0; t4 < 4; ++t4) {
+      float4 a[NG];
 #pragma clang loop unroll(full)
-      for (int e = 0; e < 8; ++e) cd[e] = ct[bits_at(w, (8 * kk + e) * B, B)];
-    };
-    auto fmas = [&](const float (&wd)[G], const float (&cd)[8]) {
+      for (int g = 0; g < NG; ++g) a[g] = *reinterpret_cast<const float4*>(wl + 4 * g * PT + 16 * n + 4 * t4);
 #pragma clang loop unroll(full)
-      for (int e = 0; e < 8; ++e)
+      for (int e = 0; e < 4; ++e) {
+        const int tl = 4 * t4 + e;   // token 16 n + tl: codes at pass positions 2 tl, 2 tl + 1
+        const float c0 = ct[bits_at(w, 2 * tl * B, B)], c1 = ct[bits_at(w, (2 * tl + 1) * B, B)];
 #pragma clang loop unroll(full)
-        for (int h = 0; h < G; ++h) acc[h][e] = fmaf(wd[h], cd[e], acc[h][e]);
-    };
-    fetch(0, wa, ca);
-    __builtin_amdgcn_sched_barrier(0);
-    fetch(1, wb, cb);
-    __builtin_amdgcn_sched_barrier(0);
-    fmas(wa, ca);
-    __builtin_amdgcn_sched_barrier(0);
-    fetch(2, wa, ca);
-    __builtin_amdgcn_sched_barrier(0);
-    fmas(wb, cb);
-    __builtin_amdgcn_sched_barrier(0);
-    fetch(3, wb, cb);
-    __builtin_amdgcn_sched_barrier(0);
-    fmas(wa, ca);
-    __builtin_amdgcn_sched_barrier(0);
-    fmas(wb, cb);
+        for (int g = 0; g < NG; ++g) {
+          const float av = e == 0 ? a[g].x : e == 1 ? a[g].y : e == 2 ? a[g].z : a[g].w;
+          acc[g][0] = __builtin_amdgcn_mfma_f32_4x4x1f32(av, c0, acc[g][0], 0, 0, 0);
+          acc[g][1] = __builtin_amdgcn_mfma_f32_4x4x1f32(av, c1, acc[g][1], 0, 0, 0);
+        }
+      }
+    }
 #pragma clang loop unroll(full)
     for (int i = 0; i < B; ++i) w[i] = nx[i];
   }
@@ -536,7 +541,7 @@ __device__ __forceinline__ void value_accum_fp16(const char* page, int lane, con
       row(t, x);
 #pragma clang loop unroll(full)
       for (int h = 0; h < G; ++h) {
-        const float wt = wv[t * G + h];
+        const float wt = wv[h * PT + t];
 #pragma clang loop unroll(full)
         for (int e = 0; e < 8; ++e) y[h][e] = fmaf(wt, x[e], y[h][e]);
       }
@@ -555,7 +560,7 @@ __device__ __forceinline__ void value_accum_fp16(const char* page, int lane, con
       rotate(x);
 #pragma clang loop unroll(full)
       for (int h = 0; h < G; ++h) {
-        const float wt = wv[t * G + h];
+        const float wt = wv[h * PT + t];
 #pragma clang loop unroll(full)
         for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(wt, x[e], acc[h][e]);
       }
@@ -617,7 +622,7 @@ __device__ __forceinline__ int page_class(int kb, int vb, bool qjl) {
 // softmax numerator (m + log2 of the page's sum of 2^(s - m)); the combine
 // turns it into the page's attention mass.
 template <int G, int CLASS, bool MASS>
-__global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(CLASS >= 3 ? 4 : (CLASS == 2 && G <= 4) ? 3 : 1)))
+__global__ __launch_bounds__(64 * kDecodeWaves) __attribute__((amdgpu_waves_per_eu(CLASS >= 3 || (CLASS == 0 && G <= 4) ? 4 : (CLASS == 2 && G <= 4) ? 3 : 1)))
 void split_kernel(DecodeArgs a,
                                                                   const float* __restrict__ wsq,
                                                                   const uint64_t* __restrict__ pages,
@@ -761,15 +766,28 @@ void split_kernel(DecodeArgs a,
     __syncthreads();
   }
 
-  float m[G], l[G], acc[G][8];
+  // acc: packed pages' value sums on the matrix cores (value_mfma); acc16:
+  // fp16 pages' (lane = (token quarter, 8 coordinates), classes with fp16 pages)
+  constexpr int NG = G > 4 ? G / 4 : 1;
+  constexpr bool kFp16 = CLASS == 2 || CLASS == 4;
+  float m[G], l[G], acc16[kFp16 ? G : 1][8];
+  v4f acc[NG][2];
 #pragma clang loop unroll(full)
   for (int h = 0; h < G; ++h) {
     m[h] = -INFINITY;
     l[h] = 0.f;
-#pragma clang loop unroll(full)
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
   }
+#pragma clang loop unroll(full)
+  for (int h = 0; h < (kFp16 ? G : 1); ++h)
+#pragma clang loop unroll(full)
+    for (int e = 0; e < 8; ++e) acc16[h][e] = 0.f;
+#pragma clang loop unroll(full)
+  for (int g = 0; g < NG; ++g) acc[g][0] = acc[g][1] = v4f{0.f, 0.f, 0.f, 0.f};
   float* wv = sm.w[wave];
+  if constexpr (G < 4) {
+    for (int i = lane; i < 4 * PT; i += 64) wv[i] = 0.f;
+    wave_lds_sync();
+  }
   const int q4 = lane >> 4, i16 = lane & 15;
 
   // The page loop, compiled for page class PC.  The merged launch runs a
@@ -792,6 +810,125 @@ void split_kernel(DecodeArgs a,
         qsum[h] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_sum(c[0] + c[1]))));
       }
     }
+    // One page's softmax step, shared by the loops below: masks the lanes past
+    // the session's tokens, updates the running maximum and sums, writes the
+    // page mass, rescales the value sums when the reference moved, and leaves
+    // the page's weights (times the value norms) in the wave's LDS rows.
+    auto weigh = [&](int p, float (&s)[G], float nv, int valid) {
+      float alpha[G];
+  #pragma clang loop unroll(full)
+      for (int h = 0; h < G; ++h)
+        if (lane >= valid) s[h] = -INFINITY;
+      softmax_update<G>(s, m, l, alpha);
+      if constexpr (MASS) {
+        float* mrow = a.mass + ((size_t)b * a.n_q_heads + hq0) * a.max_pages + p;
+  #pragma clang loop unroll(full)
+        for (int h = 0; h < G; ++h) {
+          const float ps = wave_sum(s[h]);
+          if (lane == 0) mrow[(size_t)h * a.max_pages] = ps > 0.f ? m[h] + log2f(ps) : -INFINITY;
+        }
+      }
+      // the running sums need rescaling only when some head's maximum moved
+      // (alpha is wave-uniform, so is the branch)
+      bool moved = false;
+  #pragma clang loop unroll(full)
+      for (int h = 0; h < G; ++h) moved |= alpha[h] != 1.f;
+      if (moved) {
+  #pragma clang loop unroll(full)
+        for (int g = 0; g < NG; ++g)
+  #pragma clang loop unroll(full)
+          for (int i = 0; i < 4; ++i)
+            if (4 * g + i < G) {
+              acc[g][0][i] *= alpha[4 * g + i];
+              acc[g][1][i] *= alpha[4 * g + i];
+            }
+        if constexpr (kFp16) {
+  #pragma clang loop unroll(full)
+          for (int h = 0; h < G; ++h)
+  #pragma clang loop unroll(full)
+            for (int e = 0; e < 8; ++e) acc16[h][e] *= alpha[h];
+        }
+      }
+  #pragma clang loop unroll(full)
+      for (int h = 0; h < G; ++h) wv[h * PT + lane] = s[h] * nv;
+      wave_lds_sync();
+    };
+
+    if constexpr (PC == 0) {
+      // Common pages, one page ahead: the next page's K and V code words and
+      // norms are loaded while this page is computed.  Every lane issues the
+      // same ten loads per page (words past a width repeat its last word; a
+      // page to skip reads the codebook table, 48 KB, instead), so the waits
+      // on this page's data count loads statically.
+      uint32_t kw[16], vw[16], kn[16], vn[16];
+      float nk, nv, nkn, nvn;
+      int kb, vb, kbn, vbn;   // kb = 0: no page of the class here
+      auto fetch = [&](int p, uint32_t (&kd)[16], uint32_t (&vd)[16], float& fk, float& fv, int& fkb,
+                       int& fvb) {
+        bool ok = false;
+        int kb_ = 1, vb_ = 1;
+        uint64_t off = 0;
+        if (p < p_end) {
+          const PageDesc pd = read_desc(sm.desc[p - p_begin]);
+          ok = pd.present && !pd.qjl && pd.kb >= 1 && pd.kb <= 4 && pd.vb >= 1 && pd.vb <= 4 &&
+               pd.off + page_size_dev(pd.kb, pd.vb, false) <= a.pool_bytes;
+          if (ok) {
+            kb_ = pd.kb;
+            vb_ = pd.vb;
+            off = pd.off;
+          }
+        }
+        const char* kp = ok ? a.pool + off : reinterpret_cast<const char*>(a.k_table);
+        const char* vp = ok ? kp + 1024 * kb_ + 256 : reinterpret_cast<const char*>(a.k_table);
+        const uint4* ks = reinterpret_cast<const uint4*>(kp);
+        const uint4* vs = reinterpret_cast<const uint4*>(vp);
+  #pragma clang loop unroll(full)
+        for (int w = 0; w < 4; ++w) {
+          const uint4 x = ks[min(w, kb_ - 1) * 64 + lane];
+          const uint4 y = vs[min(w, vb_ - 1) * 64 + lane];
+          kd[4 * w] = x.x; kd[4 * w + 1] = x.y; kd[4 * w + 2] = x.z; kd[4 * w + 3] = x.w;
+          vd[4 * w] = y.x; vd[4 * w + 1] = y.y; vd[4 * w + 2] = y.z; vd[4 * w + 3] = y.w;
+        }
+        fk = reinterpret_cast<const float*>(kp + 1024 * kb_)[lane];
+        fv = reinterpret_cast<const float*>(vp + 1024 * vb_)[lane];
+        fkb = ok ? kb_ : 0;
+        fvb = vb_;
+      };
+      fetch(p_begin + wave, kw, vw, nk, nv, kb, vb);
+      for (int p = p_begin + wave; p < p_end; p += kDecodeWaves) {
+        fetch(p + kDecodeWaves, kn, vn, nkn, nvn, kbn, vbn);
+        if (kb != 0) {
+          float s[G];
+          switch (kb) {
+            case 1: key_scores_w<1, G>(kw, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
+            case 2: key_scores_w<2, G>(kw, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
+            case 3: key_scores_w<3, G>(kw, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
+            default: key_scores_w<4, G>(kw, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
+          }
+  #pragma clang loop unroll(full)
+          for (int h = 0; h < G; ++h) s[h] *= nk;
+          weigh(p, s, nv, min(PT, ntok - p * PT));
+          switch (vb) {
+            case 1: value_mfma_w<1, NG>(vw, lane, wv, sm.vpair, sm.vquad, acc); break;
+            case 2: value_mfma_w<2, NG>(vw, lane, wv, sm.vpair, sm.vquad, acc); break;
+            case 3: value_mfma_w<3, NG>(vw, lane, wv, sm.vpair, sm.vquad, acc); break;
+            default: value_mfma_w<4, NG>(vw, lane, wv, sm.vpair, sm.vquad, acc); break;
+          }
+          wave_lds_sync();
+        }
+  #pragma clang loop unroll(full)
+        for (int i = 0; i < 16; ++i) {
+          kw[i] = kn[i];
+          vw[i] = vn[i];
+        }
+        nk = nkn;
+        nv = nvn;
+        kb = kbn;
+        vb = vbn;
+      }
+      return;
+    }
+
     for (int p = p_begin + wave; p < p_end; p += kDecodeWaves) {
       const PageDesc pd = read_desc(sm.desc[p - p_begin]);
       const int kb = pd.kb, vb = pd.vb;
@@ -804,7 +941,7 @@ void split_kernel(DecodeArgs a,
       if (PC != 0 && ((a.k_polar && kb > 4) || (a.v_polar && vb > 4))) continue;   // no polar pair table
       const char* page = a.pool + off;
       const int valid = min(PT, ntok - p * PT);
-      float s[G], alpha[G];
+      float s[G];
       const char* vblk = page + 1024 * kb + 256;
       // the norms (and the QJL scale) are loaded with the codes, not after them
       float nk = 1.f, nv = 1.f, gq = 0.f;
@@ -856,62 +993,39 @@ void split_kernel(DecodeArgs a,
           vblk += 1280;
         }
       }
-  #pragma clang loop unroll(full)
-      for (int h = 0; h < G; ++h)
-        if (lane >= valid) s[h] = -INFINITY;
-      softmax_update<G>(s, m, l, alpha);
-      if constexpr (MASS) {
-        float* mrow = a.mass + ((size_t)b * a.n_q_heads + hq0) * a.max_pages + p;
-  #pragma clang loop unroll(full)
-        for (int h = 0; h < G; ++h) {
-          const float ps = wave_sum(s[h]);
-          if (lane == 0) mrow[(size_t)h * a.max_pages] = ps > 0.f ? m[h] + log2f(ps) : -INFINITY;
-        }
-      }
-      // the running sums need rescaling only when some head's maximum moved
-      // (alpha is wave-uniform, so is the branch)
-      bool moved = false;
-  #pragma clang loop unroll(full)
-      for (int h = 0; h < G; ++h) moved |= alpha[h] != 1.f;
-      if (moved) {
-  #pragma clang loop unroll(full)
-        for (int h = 0; h < G; ++h)
-  #pragma clang loop unroll(full)
-          for (int e = 0; e < 8; ++e) acc[h][e] *= alpha[h];
-      }
-  #pragma clang loop unroll(full)
-      for (int h = 0; h < G; ++h) wv[lane * G + h] = s[h] * nv;
-      wave_lds_sync();
+      weigh(p, s, nv, valid);
       if (PC == 2 && kb == 0) {
-        uint32_t dm[8];
-        const uint32_t dword = a.sign_mask[i16 >> 2];
+        if constexpr (kFp16) {
+          uint32_t dm[8];
+          const uint32_t dword = a.sign_mask[i16 >> 2];
   #pragma clang loop unroll(full)
-        for (int e = 0; e < 8; ++e) dm[e] = (dword >> (8 * (i16 & 3) + e)) & 1u;
-        value_accum_fp16<G>(page, lane, wv, dm, acc);
+          for (int e = 0; e < 8; ++e) dm[e] = (dword >> (8 * (i16 & 3) + e)) & 1u;
+          value_accum_fp16<G>(page, lane, wv, dm, acc16);
+        }
       } else if constexpr (PC == 0) {
         switch (vb) {
-          case 1: value_accum<1, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
-          case 2: value_accum<2, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
-          case 3: value_accum<3, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
-          default: value_accum<4, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
+          case 1: value_mfma<1, NG>(vblk, lane, wv, sm.vpair, sm.vquad, acc); break;
+          case 2: value_mfma<2, NG>(vblk, lane, wv, sm.vpair, sm.vquad, acc); break;
+          case 3: value_mfma<3, NG>(vblk, lane, wv, sm.vpair, sm.vquad, acc); break;
+          default: value_mfma<4, NG>(vblk, lane, wv, sm.vpair, sm.vquad, acc); break;
         }
       } else if constexpr (PC == 1) {
         switch (vb) {
-          case 5: value_accum_wide<5, G>(vblk, lane, wv, sm.vcent, acc); break;
-          case 6: value_accum_wide<6, G>(vblk, lane, wv, sm.vcent, acc); break;
-          case 7: value_accum_wide<7, G>(vblk, lane, wv, sm.vcent, acc); break;
-          default: value_accum_wide<8, G>(vblk, lane, wv, sm.vcent, acc); break;
+          case 5: value_mfma_wide<5, NG>(vblk, lane, wv, sm.vcent, acc); break;
+          case 6: value_mfma_wide<6, NG>(vblk, lane, wv, sm.vcent, acc); break;
+          case 7: value_mfma_wide<7, NG>(vblk, lane, wv, sm.vcent, acc); break;
+          default: value_mfma_wide<8, NG>(vblk, lane, wv, sm.vcent, acc); break;
         }
       } else {
         switch (vb) {
-          case 1: value_accum<1, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
-          case 2: value_accum<2, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
-          case 3: value_accum<3, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
-          case 4: value_accum<4, G>(vblk, lane, wv, sm.vpair, sm.vquad, sm.vcent, acc); break;
-          case 5: value_accum_wide<5, G>(vblk, lane, wv, sm.vcent, acc); break;
-          case 6: value_accum_wide<6, G>(vblk, lane, wv, sm.vcent, acc); break;
-          case 7: value_accum_wide<7, G>(vblk, lane, wv, sm.vcent, acc); break;
-          default: value_accum_wide<8, G>(vblk, lane, wv, sm.vcent, acc); break;
+          case 1: value_mfma<1, NG>(vblk, lane, wv, sm.vpair, sm.vquad, acc); break;
+          case 2: value_mfma<2, NG>(vblk, lane, wv, sm.vpair, sm.vquad, acc); break;
+          case 3: value_mfma<3, NG>(vblk, lane, wv, sm.vpair, sm.vquad, acc); break;
+          case 4: value_mfma<4, NG>(vblk, lane, wv, sm.vpair, sm.vquad, acc); break;
+          case 5: value_mfma_wide<5, NG>(vblk, lane, wv, sm.vcent, acc); break;
+          case 6: value_mfma_wide<6, NG>(vblk, lane, wv, sm.vcent, acc); break;
+          case 7: value_mfma_wide<7, NG>(vblk, lane, wv, sm.vcent, acc); break;
+          default: value_mfma_wide<8, NG>(vblk, lane, wv, sm.vcent, acc); break;
         }
       }
       wave_lds_sync();
@@ -960,15 +1074,34 @@ void split_kernel(DecodeArgs a,
     ph[0] = M[h];
     ph[1] = lsum;
   }
+  float fsc[G];
 #pragma clang loop unroll(full)
-  for (int h = 0; h < G; ++h) {
-    const float f = m[h] == -INFINITY ? 0.f : exp2f(m[h] - M[h]);
+  for (int h = 0; h < G; ++h) fsc[h] = m[h] == -INFINITY ? 0.f : exp2f(m[h] - M[h]);
+  // the matrix-core sums: lane L holds coordinates v_stream_coord(L, 0 / 1)
+  {
+    const int c0 = v_stream_coord(lane, 0), c1 = v_stream_coord(lane, 1);
 #pragma clang loop unroll(full)
-    for (int e = 0; e < 8; ++e) {
-      float v = acc[h][e] * f;
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      if (q4 == 0) sm.red[wave][h * D + 8 * i16 + e] = v;
+    for (int g = 0; g < NG; ++g)
+#pragma clang loop unroll(full)
+      for (int i = 0; i < 4; ++i)
+        if (4 * g + i < G) {
+          sm.red[wave][(4 * g + i) * D + c0] = acc[g][0][i] * fsc[4 * g + i];
+          sm.red[wave][(4 * g + i) * D + c1] = acc[g][1][i] * fsc[4 * g + i];
+        }
+  }
+  if constexpr (kFp16) {
+    // plus the fp16 pages' sums: lanes (quarter, 8 coordinates), reduced over
+    // the quarters
+    wave_lds_sync();
+#pragma clang loop unroll(full)
+    for (int h = 0; h < G; ++h) {
+#pragma clang loop unroll(full)
+      for (int e = 0; e < 8; ++e) {
+        float v = acc16[h][e] * fsc[h];
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        if (q4 == 0) sm.red[wave][h * D + 8 * i16 + e] += v;
+      }
     }
   }
   __syncthreads();

@@ -76,8 +76,10 @@ __global__ __launch_bounds__(64) void dequant_kernel(DequantArgs a, const float*
   // code of coordinate j of this lane's token
   auto code_of = [&](int j) {
     if (a.which == 0) return stream_code(blk, B, lane, j);
-    const int q = lane & 3, k = lane >> 2;
-    return stream_code(blk, B, 16 * q + (j >> 3), 8 * k + (j & 7));
+    // V: coordinate j is in stream n + 32 P at position 2 t + (j & 1) (the
+    // inverse of v_stream_coord)
+    const int n = ((j >> 1) & 3) | (((j >> 6) & 1) << 2) | (((j >> 3) & 3) << 3), P = (j >> 5) & 1;
+    return stream_code(blk, B, n + 32 * P, 2 * lane + (j & 1));
   };
   if (a.polar) {
     // pair i: radius code at coordinate 2i, angle code at 2i + 1

@@ -76,6 +76,17 @@ __device__ __forceinline__ uint32_t bits_at(const uint32_t (&s)[N], int pos, int
   return v & ((1u << w) - 1u);
 }
 
+// Coordinate k (0 or 1) of V stream s of a packed page: stream s = n + 32 P
+// (n < 32) holds, for every token t, the codes of the coordinate pair c0, c0 + 1
+// at stream positions 2t and 2t + 1, with
+// c0 = 64 bit2(n) + 32 P + 8 (n >> 3) + 2 (n & 3).  Each stream is one
+// coordinate pair over the page's 64 tokens (a PolarQuant pair too), the pair
+// the decode's matrix-core value sums give a lane.
+__device__ __forceinline__ int v_stream_coord(int s, int k) {
+  const int n = s & 31;
+  return 64 * ((n >> 2) & 1) + 32 * (s >> 5) + 8 * (n >> 3) + 2 * (n & 3) + k;
+}
+
 // Wavefront reductions (every lane active).  Inside each 16-lane row the
 // partner values come through DPP (quad permutations xor 1 and xor 2, then the
 // half-row and row mirrors), which keeps them in the VALU pipeline; the four

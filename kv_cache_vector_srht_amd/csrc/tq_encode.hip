@@ -578,15 +578,16 @@ __global__ __launch_bounds__(kEncodeBlock) void encode_pages_kernel(EncodeArgs a
       store_stream_part(kb, page, s, e, c8);
     }
     if (!skip_v) {
-      // V stream s = 16q + i: positions 8k + j (k = 4e..4e+3) = token 4k+q, coordinate 8i+j
-      const int q = s >> 4, i = s & 15;
+      // V stream s: positions 2t, 2t + 1 (t = 16e .. 16e + 15) = token t at
+      // coordinates v_stream_coord(s, 0) and v_stream_coord(s, 1)
+      const uint8_t* mv = reinterpret_cast<const uint8_t*>(matv);
+      const int c0 = v_stream_coord(s, 0), c1 = v_stream_coord(s, 1);
       uint32_t c8[8];
 #pragma clang loop unroll(full)
-      for (int kk = 0; kk < 4; ++kk) {
-        const uint2 v = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(matv) +
-                                                        (4 * (4 * e + kk) + q) * kRowStride + 8 * i);
-        c8[2 * kk] = v.x;
-        c8[2 * kk + 1] = v.y;
+      for (int kk = 0; kk < 8; ++kk) {
+        const int t0 = 16 * e + 2 * kk;
+        c8[kk] = (uint32_t)mv[t0 * kRowStride + c0] | ((uint32_t)mv[t0 * kRowStride + c1] << 8) |
+                 ((uint32_t)mv[(t0 + 1) * kRowStride + c0] << 16) | ((uint32_t)mv[(t0 + 1) * kRowStride + c1] << 24);
       }
       store_stream_part(vb, vblk, s, e, c8);
     }

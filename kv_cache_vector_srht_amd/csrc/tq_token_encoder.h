@@ -190,18 +190,18 @@ __device__ __forceinline__ float encode_packed(char* page, int lane, float (&x)[
 #pragma clang loop unroll(full)
     for (int i = 0; i < D / 16; ++i) row[i] = make_uint4(cb[4 * i], cb[4 * i + 1], cb[4 * i + 2], cb[4 * i + 3]);
     __syncthreads();
-    const int q = lane >> 4, ii = lane & 15;
+    // stream `lane`: positions 2t, 2t + 1 = token t at its two coordinates
+    const uint8_t* rows = reinterpret_cast<const uint8_t*>(lds_rows);
+    const int c0 = v_stream_coord(lane, 0), c1 = v_stream_coord(lane, 1);
     uint32_t sw[4 * B];
 #pragma clang loop unroll(full)
     for (int i = 0; i < 4 * B; ++i) sw[i] = 0;
 #pragma clang loop unroll(full)
-    for (int k = 0; k < 16; ++k) {
-      const uint2 b8 = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(lds_rows) +
-                                                        (4 * k + q) * kEncodeRowBytes + 8 * ii);
+    for (int t = 0; t < PT; ++t) {
 #pragma clang loop unroll(full)
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t c = ((e < 4 ? b8.x : b8.y) >> (8 * (e & 3))) & 0xffu;
-        const int pos = (8 * k + e) * B, wi = pos >> 5, sh = pos & 31;
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t c = rows[t * kEncodeRowBytes + (k ? c1 : c0)];
+        const int pos = (2 * t + k) * B, wi = pos >> 5, sh = pos & 31;
         sw[wi] |= c << sh;
         if (sh + B > 32) sw[wi + 1] |= c >> (32 - sh);
       }

@@ -633,8 +633,10 @@ def qjl_reconstruct(z: np.ndarray, gamma32: np.ndarray, S: np.ndarray) -> np.nda
 # n*b .. n*b+b-1), i.e. b little-endian 128-bit words, and word w of stream s
 # sits at byte (w*64 + s)*16 of the block.
 #   K block: stream t = token t, codes of coordinates 0..127 in order.
-#   V block: stream s = 16q + i holds, for k = 0..15 and e = 0..7, the code of
-#            token 4k+q, coordinate 8i+e at stream position 8k+e.
+#   V block: stream s = n + 32 P (n < 32, P in {0, 1}) holds, for every token
+#            t, the codes of coordinates c0 and c0 + 1 at stream positions 2t
+#            and 2t + 1, c0 = 64 bit2(n) + 32 P + 8 (n >> 3) + 2 (n & 3) (so one
+#            stream is one coordinate pair over the page).
 # Page = K block (1024 bK B) | K norms (64 x f32) | [QJL signs 64 x 16 B,
 #        bit i of token t's 128-bit word = z_i, | QJL gamma 64 x f32] |
 #        V block (1024 bV B) | V norms (64 x f32).
@@ -646,19 +648,31 @@ def k_stream_codes(codes: np.ndarray) -> np.ndarray:
     return np.array(codes, copy=True)
 
 
-def v_stream_codes(codes: np.ndarray) -> np.ndarray:
-    """[64 tokens][128 coords] -> [64 streams][128 codes] for a V block.
+def v_stream_coord(s: int, k: int) -> int:
+    """Coordinate k (0 or 1) of V stream s (layout above)."""
+    n = s & 31
+    return 64 * ((n >> 2) & 1) + 32 * (s >> 5) + 8 * (n >> 3) + 2 * (n & 3) + k
 
-    Token 4k+q, coordinate 8i+e goes to stream 16q+i, position 8k+e: view the
-    codes as [k][q][i][e] and reorder the axes to [q][i][k][e].
-    """
+
+# token and coordinate of every (stream, position) of a V block
+_V_TOKEN = np.array([[p >> 1 for p in range(STREAM_CODES)] for _ in range(64)])
+_V_COORD = np.array([[v_stream_coord(s, p & 1) for p in range(STREAM_CODES)] for s in range(64)])
+
+
+def v_stream_codes(codes: np.ndarray) -> np.ndarray:
+    """[64 tokens][128 coords] -> [64 streams][128 codes] for a V block:
+    stream s, position p holds token p >> 1, coordinate v_stream_coord(s, p & 1)."""
+    codes = np.asarray(codes)
     assert codes.shape == (PAGE_TOKENS, HEAD_DIM)
-    return np.asarray(codes).reshape(16, 4, 16, 8).transpose(1, 2, 0, 3).reshape(64, 128)
+    return codes[_V_TOKEN, _V_COORD]
 
 
 def v_codes_from_streams(streams: np.ndarray) -> np.ndarray:
     """Inverse of v_stream_codes."""
-    return np.asarray(streams).reshape(4, 16, 16, 8).transpose(2, 0, 1, 3).reshape(64, 128)
+    streams = np.asarray(streams)
+    out = np.empty((PAGE_TOKENS, HEAD_DIM), dtype=streams.dtype)
+    out[_V_TOKEN, _V_COORD] = streams
+    return out
 
 
 def pack_block(streams: np.ndarray, bits: int) -> bytes:

@@ -258,9 +258,17 @@ def test_v_stream_order_is_a_permutation():
     st = O.v_stream_codes(codes)
     assert sorted(st.ravel().tolist()) == list(range(64 * 128))
     assert np.array_equal(O.v_codes_from_streams(st), codes)
-    # stream 16q+i, position 8k+e holds token 4k+q, coordinate 8i+e
-    q, i, k, e = 2, 5, 7, 3
-    assert st[16 * q + i, 8 * k + e] == codes[4 * k + q, 8 * i + e]
+    # stream s holds one coordinate pair (c0, c0 + 1) over the 64 tokens:
+    # position 2t (2t + 1) is token t, coordinate c0 (c0 + 1); hand-worked:
+    # stream 0: coordinates 0, 1; stream 5 (n = 5: bit 2 set, n & 3 = 1):
+    # 64 + 2 = 66, 67; stream 43 (n = 11: n >> 3 = 1, n & 3 = 3; P = 1):
+    # 32 + 8 + 6 = 46, 47
+    for s_, c0 in ((0, 0), (5, 66), (43, 46)):
+        for t in (0, 17, 63):
+            assert st[s_, 2 * t] == codes[t, c0] and st[s_, 2 * t + 1] == codes[t, c0 + 1]
+    pairs = {(O.v_stream_coord(s_, 0), O.v_stream_coord(s_, 1)) for s_ in range(64)}
+    assert sorted(c for pr in pairs for c in pr) == list(range(128))
+    assert all(b == a + 1 and a % 2 == 0 for a, b in pairs)
 
 
 def test_sign_words_round_trip():
