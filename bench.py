@@ -9,7 +9,13 @@ widths 1-8.  Inputs are synthetic, seeded, and resident in HBM before timing.
 Prints one JSON line.  ``value`` is decode-attention effective bandwidth
 (algorithmic bytes per decode step / decode time); the encode rate is in
 ``encode_mtokens_per_s``.  The ``roofline`` object describes the kernel that
-dominates the step, timed with HIP events on the stream it runs on.
+dominates the step and ``decode_roofline`` the decode-attention call, both
+timed with HIP events on the stream they run on.  Beside the step the line
+carries: the small single-head and Llama-3-8B-layer configurations as
+latency (``latency``), one full-size layer of the 128K QJL and 256K tier
+workloads (``one_layer``), the decode loop, the tiering mechanisms, a codec
+comparison, plain HBM stream rates, and the CPU oracle on a bounded sample
+(``cpu_baseline``: one core and a process pool over every core).
 """
 from __future__ import annotations
 
@@ -39,8 +45,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--codecs", type=int, default=1,
                     help="compare the scalar codec with PolarQuant on one layer (1, default) or skip (0)")
-    ap.add_argument("--qjl", type=int, default=1,
-                    help="also time one layer of the QJL workload's encode (1 = yes)")
+    ap.add_argument("--subworkloads", type=int, default=1,
+                    help="also time one full-size layer of the 128K QJL and 256K tier workloads (1 = yes)")
+    ap.add_argument("--latency", type=int, default=1,
+                    help="also time the single-head and Llama-3-8B-layer configurations as latency (1 = yes)")
     ap.add_argument("--tiering", type=int, default=1,
                     help="measure page-mass export and page re-tiering (1, default) or skip (0)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget")
@@ -128,69 +136,122 @@ def valu_record(workload: str):
     return rec.get("valu_issue")
 
 
-def cpu_baseline(w, layers_data, seconds: float):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    whole (layer, session, KV head) units, encode then decode attention."""
+def _oracle_unit(job):
+    """One (layer, session, KV head) unit through the CPU oracle: encode every
+    packed page group, rebuild K and V (fp16 pages as stored), then decode
+    attention for the unit's query heads.  Returns (encode s, decode s)."""
     import numpy as np
     from oracle import tq_oracle as O
-    import workloads as W
+    fm, k, v, q, signs, S, k_codebook, v_codebook = job
+    k, v, q = k.astype(np.float64), v.astype(np.float64), q.astype(np.float64)
+    t0 = time.perf_counter()
+    groups = {}
+    for p, f in enumerate(fm):
+        if f[0]:
+            groups.setdefault(tuple(f), []).append(p)
+    encs = {}
+    for f, plist in groups.items():
+        rows = np.concatenate([np.arange(64 * p, 64 * p + 64) for p in plist])
+        ek = O.encode(k[rows], signs, f[0], k_codebook)
+        ev = O.encode(v[rows], signs, f[1], v_codebook)
+        qj = None
+        if f[2]:
+            kh0 = O.dequantize(ek["norm"], ek["codes"], signs, f[0], k_codebook)
+            qj = O.qjl_encode(k[rows], kh0, S)
+        encs[f] = (rows, ek, ev, qj)
+    t1 = time.perf_counter()
+    Kh = np.zeros_like(k)
+    Vh = np.zeros_like(v)
+    for p, f in enumerate(fm):
+        if f[0] == 0:
+            Kh[64 * p:64 * p + 64] = k[64 * p:64 * p + 64].astype(np.float16)
+            Vh[64 * p:64 * p + 64] = v[64 * p:64 * p + 64].astype(np.float16)
+    for f, (rows, ek, ev, qj) in encs.items():
+        kh = O.dequantize(ek["norm"], ek["codes"], signs, f[0], k_codebook)
+        if qj is not None:
+            kh = kh + O.qjl_reconstruct(qj["z"], qj["gamma"], S)
+        Kh[rows] = kh
+        Vh[rows] = O.dequantize(ev["norm"], ev["codes"], signs, f[1], v_codebook)
+    O.decode_attention_unit(q, Kh, Vh)
+    return t1 - t0, time.perf_counter() - t1
+
+
+_ONE_THREAD = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS")
+
+
+def _one_thread_pool(n):
+    """A pool of ``n`` fresh interpreters (spawned, so nothing of this
+    process's GPU state is inherited), each with single-threaded BLAS."""
+    import multiprocessing as mp
+    saved = {k: os.environ.get(k) for k in _ONE_THREAD}
+    os.environ.update({k: "1" for k in _ONE_THREAD})
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = int(os.environ.get("OMP_NUM_THREADS", "1"))
+        pool = mp.get_context("spawn").Pool(n)
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    return pool
+
+
+def cpu_baseline(w, unit_job, seconds: float):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    whole (layer, session, KV head) units, encode then decode attention, each
+    unit in one single-threaded process.  Two legs: one core (units one after
+    another, ``seconds / 2`` of work) and every core of this process's CPU
+    share (capped at 16) running units side by side in a process pool, for
+    about ``seconds / 2`` of wall time.  ``value`` is the all-core leg."""
+    import numpy as np
     G = w.n_q_heads // w.n_kv_heads
-    enc_t = dec_t = 0.0
-    tokens = dec_bytes = 0
-    units = 0
-    t_start = time.perf_counter()
-    l = b = h = 0
-    while time.perf_counter() - t_start < seconds and units < 64:
-        k, v, q, signs, S = layers_data(l, b, h)
-        fm = w.formats[l][b][h]
-        t0 = time.perf_counter()
-        groups = {}
-        for p, f in enumerate(fm):
-            if f[0]:
-                groups.setdefault(tuple(f), []).append(p)
-        encs = {}
-        for f, plist in groups.items():
-            rows = np.concatenate([np.arange(64 * p, 64 * p + 64) for p in plist])
-            ek = O.encode(k[rows], signs, f[0], w.k_codebook)
-            ev = O.encode(v[rows], signs, f[1], w.v_codebook)
-            qj = None
-            if f[2]:
-                kh0 = O.dequantize(ek["norm"], ek["codes"], signs, f[0], w.k_codebook)
-                qj = O.qjl_encode(k[rows], kh0, S)
-            encs[f] = (rows, ek, ev, qj)
-        t1 = time.perf_counter()
-        Kh = np.zeros_like(k)
-        Vh = np.zeros_like(v)
-        for p, f in enumerate(fm):
-            if f[0] == 0:
-                Kh[64 * p:64 * p + 64] = k[64 * p:64 * p + 64].astype(np.float16)
-                Vh[64 * p:64 * p + 64] = v[64 * p:64 * p + 64].astype(np.float16)
-        for f, (rows, ek, ev, qj) in encs.items():
-            kh = O.dequantize(ek["norm"], ek["codes"], signs, f[0], w.k_codebook)
-            if qj is not None:
-                kh = kh + O.qjl_reconstruct(qj["z"], qj["gamma"], S)
-            Kh[rows] = kh
-            Vh[rows] = O.dequantize(ev["norm"], ev["codes"], signs, f[1], w.v_codebook)
-        O.decode_attention_unit(q[h * G:(h + 1) * G], Kh, Vh)
-        t2 = time.perf_counter()
-        enc_t += t1 - t0
-        dec_t += t2 - t1
-        tokens += w.n_tokens
-        one = type(w)(**{**w.__dict__})
-        one.batch, one.n_kv_heads, one.n_q_heads = 1, 1, G
-        dec_bytes += decode_bytes(one, [[fm]], G)
-        units += 1
-        h += 1
-        if h == w.n_kv_heads:
-            h, b = 0, b + 1
-            if b == w.batch:
-                b, l = 0, (l + 1) % w.n_layers
     unit_count = w.n_layers * w.batch * w.n_kv_heads
+    units = [(l, b, h) for l in range(w.n_layers) for b in range(w.batch) for h in range(w.n_kv_heads)]
+    one = type(w)(**{**w.__dict__})
+    one.batch, one.n_kv_heads, one.n_q_heads = 1, 1, G
+
+    def unit_bytes(u):
+        l, b, h = u
+        return decode_bytes(one, [[w.formats[l][b][h]]], G)
+
+    affinity = len(os.sched_getaffinity(0))
+    cores = max(1, min(affinity, 16))
+    # one core
+    pool = _one_thread_pool(1)
+    done, enc_t, dec_t, nbytes = 0, 0.0, 0.0, 0
+    try:
+        while enc_t + dec_t < seconds / 2 and done < len(units):
+            e, d = pool.apply(_oracle_unit, (unit_job(*units[done]),))
+            enc_t, dec_t, nbytes = enc_t + e, dec_t + d, nbytes + unit_bytes(units[done])
+            done += 1
+    finally:
+        pool.terminate()
+        pool.join()
+    single = {"value": nbytes / dec_t / 1e9, "unit": "GB/s", "cores": 1, "units": done,
+              "encode_mtokens_per_s": done * w.n_tokens / (w.n_layers * w.n_kv_heads) / enc_t / 1e6,
+              "seconds": enc_t + dec_t}
+    # every core: rounds of `cores` units side by side until the budget is used;
+    # the rate is bytes over wall time, process start-up excluded
+    pool = _one_thread_pool(cores)
+    n_all, p_bytes, p_enc, p_dec = 0, 0, 0.0, 0.0
+    try:
+        pool.map(abs, range(cores))          # the workers are up
+        t_start = time.perf_counter()
+        nxt = done
+        while time.perf_counter() - t_start < seconds / 2:
+            batch = [units[(nxt + i) % len(units)] for i in range(cores)]
+            nxt += cores
+            res = pool.map(_oracle_unit, [unit_job(*u) for u in batch], chunksize=1)
+            for u, (e, d) in zip(batch, res):
+                p_enc, p_dec, p_bytes = p_enc + e, p_dec + d, p_bytes + unit_bytes(u)
+            n_all += len(batch)
+        wall = time.perf_counter() - t_start
+    finally:
+        pool.terminate()
+        pool.join()
+    # the pool's wall time holds encode and decode; split it as their CPU time splits
+    dec_wall = wall * p_dec / (p_enc + p_dec)
+    enc_wall = wall - dec_wall
     cpu_model = platform.processor() or platform.machine()
     try:
         with open("/proc/cpuinfo") as f:
@@ -201,14 +262,15 @@ def cpu_baseline(w, layers_data, seconds: float):
     except OSError:
         pass
     return {
-        "value": dec_bytes / dec_t / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
-        "cpu_model": cpu_model, "affinity_cpus": len(os.sched_getaffinity(0)),
-        "sample": (f"{units} of {unit_count} (layer, session, KV head) units, "
-                   f"{w.n_tokens} tokens each: encode then decode attention for the "
-                   f"{G} query heads; numpy float64"),
+        "value": p_bytes / dec_wall / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+        "cpu_model": cpu_model, "affinity_cpus": affinity,
+        "sample": (f"{n_all} (all cores) and {done} (one core) of {unit_count} (layer, session, "
+                   f"KV head) units, {w.n_tokens} tokens each: encode then decode attention for "
+                   f"the {G} query heads; numpy float64, one BLAS thread per process"),
         # one whole-stack session-token = one vector per (layer, KV head)
-        "encode_mtokens_per_s": tokens / (w.n_layers * w.n_kv_heads) / enc_t / 1e6,
-        "seconds": enc_t + dec_t,
+        "encode_mtokens_per_s": n_all * w.n_tokens / (w.n_layers * w.n_kv_heads) / enc_wall / 1e6,
+        "seconds": wall,
+        "single_core": single,
     }
 
 
@@ -281,42 +343,143 @@ def decode_graph(w, layers, caches, queries, outs, wss, dec_bytes, dev, reps: in
             "frac_of_peak": round(dec_bytes / med / 1e9 / HBM_PEAK_GBS, 4)}
 
 
-def qjl_encode(dev, sessions: int = 4, reps: int = 3):
-    """Encode of one layer of the 128K QJL workload's shape at ``sessions`` of
-    its 16 sessions (keys K2 + QJL sketch, values V2, 128-token fp16 sink):
-    HIP-event time of tq_encode_kv, median of ``reps`` after one untimed call.
-    The sketch (2 x 128 x 128 flops per key, on the float32 matrix cores) is
-    the dominant part; its rate is bounded below by sketch flops / call time."""
+def _median_us(ts):
+    import numpy as np
+    return round(float(np.median(ts)) * 1e6, 2)
+
+
+def latency(dev, reps: int = 60):
+    """The two small configurations as latency, each figure a median of
+    ``reps`` calls after warm-up calls: device time between HIP events around
+    the call on its stream, and host time from the call's start to the end of a
+    stream synchronize after it (argument marshalling and launches included).
+
+    single-head-4k-fp32: one tq_encode_kv of all 4096 tokens, then one
+    tq_decode_attention.  llama3-8b-layer-4k: the 4096-token prefill as 64
+    tq_encode_kv calls of 64 tokens each (every chunk call is one sample; the
+    first two chunks are the fp16 sink), the whole chunked prefill, and one
+    tq_decode_attention for the 32 query heads."""
     import numpy as np
     import torch
     import kv_cache_vector_srht_amd as tq
     import workloads as W
-    w = W.make_workload(4, {"batch": sessions})
-    S = W.qjl_matrix(W.ROTATION_SEED, 0)
-    layer = tq.Layer(W.rotation_signs(W.ROTATION_SEED, 0), dev, S, w.k_codebook, w.v_codebook)
-    cache = tq.Cache(w.formats[0], [w.n_tokens] * w.batch, dev)
-    k, v = W.make_kv(w, 0, device=dev)
     stream = torch.cuda.current_stream(dev)
-    tq.encode_kv(layer, cache, k, v)
-    torch.cuda.synchronize()
-    ts = []
-    for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        t0 = time.perf_counter()
         e0.record(stream)
-        tq.encode_kv(layer, cache, k, v)
+        fn()
         e1.record(stream)
         e1.synchronize()
-        ts.append(e0.elapsed_time(e1) / 1e3)
-    t = float(np.median(ts))
-    qjl_keys = sum(64 for row in w.formats[0] for r in row for f in r if f[2])
-    flops = qjl_keys * 2.0 * 128 * 128
-    out = {"workload": w.name, "sessions": sessions, "encode_ms": round(t * 1e3, 3),
-           "mtokens_per_s": round(w.batch * w.n_tokens / t / 1e6, 2),
-           "qjl_keys": qjl_keys, "sketch_tflops_lower_bound": round(flops / t / 1e12, 2),
-           "fp32_mfma_peak_tflops": FP32_MFMA_PEAK_TFLOPS}
-    del cache, k, v
+        return e0.elapsed_time(e1) / 1e3, time.perf_counter() - t0
+
+    out = {"reps": reps}
+    for idx in (1, 2):
+        w = W.make_workload(idx)
+        fm = w.formats[0]
+        layer = tq.Layer(W.rotation_signs(W.ROTATION_SEED, 0), dev, None, w.k_codebook, w.v_codebook)
+        cache = tq.Cache(fm, [w.n_tokens] * w.batch, dev)
+        k, v = W.make_kv(w, 0, device=dev)
+        q = W.make_query(w, 0, device=dev)
+        o = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
+        ws = torch.empty(tq.workspace_bytes(cache, w.n_q_heads), dtype=torch.uint8, device=dev)
+        rec = {"tokens": w.n_tokens, "kv_heads": w.n_kv_heads, "q_heads": w.n_q_heads,
+               "input_dtype": w.dtype}
+        if w.chunked_encode:
+            chunks = w.n_tokens // 64
+
+            def prefill():
+                for c in range(chunks):
+                    tq.encode_kv(layer, cache, k[:, :, 64 * c:64 * c + 64], v[:, :, 64 * c:64 * c + 64],
+                                 tok0=64 * c)
+            prefill()
+            torch.cuda.synchronize()
+            dev_t, host_t = [], []
+            for r in range(max(1, reps // chunks) + 1):
+                for c in range(chunks):
+                    d, h = timed(lambda: tq.encode_kv(layer, cache, k[:, :, 64 * c:64 * c + 64],
+                                                      v[:, :, 64 * c:64 * c + 64], tok0=64 * c))
+                    dev_t.append(d)
+                    host_t.append(h)
+            rec["chunk_encode_us"] = {"device": _median_us(dev_t), "host": _median_us(host_t),
+                                      "samples": len(dev_t), "tokens_per_call": 64}
+            pre = [timed(prefill) for _ in range(max(3, reps // 10))]
+            rec["chunked_prefill_us"] = {"device": _median_us([a for a, _ in pre]),
+                                         "host": _median_us([b for _, b in pre]), "calls": chunks,
+                                         "samples": len(pre)}
+        else:
+            enc = lambda: tq.encode_kv(layer, cache, k, v, tok0=0)
+            for _ in range(3):
+                enc()
+            ts = [timed(enc) for _ in range(reps)]
+            rec["encode_us"] = {"device": _median_us([a for a, _ in ts]),
+                                "host": _median_us([b for _, b in ts]), "tokens_per_call": w.n_tokens}
+        dec = lambda: tq.decode_attention(layer, cache, q, out=o, workspace=ws)
+        for _ in range(3):
+            dec()
+        ts = [timed(dec) for _ in range(reps)]
+        rec["decode_us"] = {"device": _median_us([a for a, _ in ts]), "host": _median_us([b for _, b in ts])}
+        rec["decode_bytes"] = decode_bytes(w, fm, w.n_q_heads)
+        out[w.name] = rec
+        del cache, k, v, q, o, ws
     torch.cuda.synchronize()
     return out
+
+
+def one_layer(idx, dev, enc_reps: int = 5, dec_reps: int = 30):
+    """One layer of a long-context workload at its full size (every session,
+    every KV head, the whole context): encode then decode attention, each
+    timed with HIP events on the launch stream, median of ``enc_reps`` /
+    ``dec_reps`` calls after warm-up calls, as effective GB/s of the
+    algorithmic bytes.  For the QJL workload the call's sketch rate, sketch
+    flops (2 x 128 x 128 per key) over the whole encode call, is a lower bound
+    of qjl_keys_kernel's."""
+    import numpy as np
+    import torch
+    import kv_cache_vector_srht_amd as tq
+    import workloads as W
+    w = W.make_workload(idx)
+    fm = w.formats[0]
+    has_qjl = any(f[2] for row in fm for r in row for f in r)
+    S = W.qjl_matrix(W.ROTATION_SEED, 0) if has_qjl else None
+    layer = tq.Layer(W.rotation_signs(W.ROTATION_SEED, 0), dev, S, w.k_codebook, w.v_codebook)
+    cache = tq.Cache(fm, [w.n_tokens] * w.batch, dev)
+    k, v = W.make_kv(w, 0, device=dev)
+    q = W.make_query(w, 0, device=dev)
+    o = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
+    ws = torch.empty(tq.workspace_bytes(cache, w.n_q_heads), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def times(fn, warm, reps):
+        for _ in range(warm):
+            fn()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) / 1e3)
+        return float(np.median(ts))
+
+    t_enc = times(lambda: tq.encode_kv(layer, cache, k, v, tok0=0), 1, enc_reps)
+    t_dec = times(lambda: tq.decode_attention(layer, cache, q, out=o, workspace=ws), 3, dec_reps)
+    eb, db = encode_bytes(w, fm), decode_bytes(w, fm, w.n_q_heads)
+    rec = {"workload": w.name, "layers": 1, "batch": w.batch, "context": w.n_tokens,
+           "decode_us": round(t_dec * 1e6, 2), "decode_bytes": db,
+           "decode_gbs": round(db / t_dec / 1e9, 1), "decode_frac_of_peak": round(db / t_dec / 1e9 / HBM_PEAK_GBS, 4),
+           "encode_us": round(t_enc * 1e6, 2), "encode_bytes": eb, "encode_gbs": round(eb / t_enc / 1e9, 1),
+           "encode_mtokens_per_s": round(w.batch * w.n_tokens / t_enc / 1e6, 2)}
+    if has_qjl:
+        keys = sum(64 for row in fm for r in row for f in r if f[2])
+        tf = keys * 2.0 * 128 * 128 / t_enc / 1e12
+        rec["qjl_sketch_tflops_lower_bound"] = round(tf, 2)
+        rec["qjl_sketch_frac_lower_bound"] = round(tf / FP32_MFMA_PEAK_TFLOPS, 4)
+    del cache, k, v, q, o, ws
+    torch.cuda.synchronize()
+    return rec
 
 
 def decode_loop(w, layers, inputs, queries, outs, wss, steps, dev, graph=False):
@@ -612,6 +775,15 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_record(name, w.name),
             "kernel": name, "bytes_per_launch": int(per_launch_bytes),
             "launch_us": round(per_launch_s * 1e6, 2)}
+    # the headline kernel: the decode-attention call of one layer (qprep_kernel,
+    # the split kernel(s) of the layer's page classes, combine_kernel), timed
+    # with HIP events around each step's decode calls on the launch stream
+    dec_roof = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                "traffic": traffic_record("decode_attention", w.name),
+                "kernel": "decode_attention (qprep_kernel + split_kernel + combine_kernel)",
+                "bytes_per_launch": int(dec_bytes / w.n_layers),
+                "launch_us": round(dec_s / w.n_layers * 1e6, 2)}
     qjl_keys = sum(64 for fm in w.formats for row in fm for r in row for f in r if f[2])
     if qjl_keys and enc_s >= dec_s:
         # With QJL key pages the encode call is dominated by qjl_keys_kernel, the
@@ -642,6 +814,7 @@ def main():
         "encode_ms_per_step": round(enc_s * 1e3, 3),
         "decode_bytes_per_step": int(dec_bytes), "encode_bytes_per_step": int(enc_bytes),
         "roofline": roof,
+        "decode_roofline": dec_roof,
         # from profiles/ (rocprofv3 SQ counters), when taken on these sources
         "valu_issue": valu_record(w.name),
     }
@@ -655,8 +828,10 @@ def main():
         line["decode_loop"] = decode_loop(w, layers, inputs, queries, outs, wss, args.loop_steps, dev)
         line["decode_loop_graph"] = decode_loop(w, layers, inputs, queries, outs, wss, args.loop_steps,
                                                 dev, graph=True)
-    if args.qjl:
-        line["qjl_encode"] = qjl_encode(dev)
+    if args.latency:
+        line["latency"] = latency(dev)
+    if args.subworkloads:
+        line["one_layer"] = {W.make_workload(i).name: one_layer(i, dev) for i in (4, 5)}
     if args.tiering:
         line["tiering"] = tiering(w, layers, inputs, queries, outs, wss, dev)
     if args.codecs:
@@ -664,18 +839,20 @@ def main():
     if not args.no_cpu_baseline:
         kv_host = {}
 
-        def layer_unit(l, b, h):
+        def unit_job(l, b, h):
             if l not in kv_host:
                 k, v = inputs[l]
                 kv_host[l] = (k.cpu().numpy(), v.cpu().numpy(), queries[l].cpu().numpy())
             k, v, q = kv_host[l]
             signs = W.rotation_signs(W.ROTATION_SEED, l)
             S = W.qjl_matrix(W.ROTATION_SEED, l) if any(f[2] for f in w.formats[l][b][h]) else None
-            return (k[b, h].astype(np.float64), v[b, h].astype(np.float64),
-                    q[b].astype(np.float64), signs, S)
-        cb = cpu_baseline(w, layer_unit, args.cpu_seconds)
-        line["cpu_baseline"] = {k2: (round(v2, 4) if isinstance(v2, float) else v2)
-                                for k2, v2 in cb.items()}
+            return (w.formats[l][b][h], k[b, h], v[b, h], q[b, h * G:(h + 1) * G], signs, S,
+                    w.k_codebook, w.v_codebook)
+
+        def rounded(d):
+            return {k2: (round(v2, 4) if isinstance(v2, float) else rounded(v2) if isinstance(v2, dict)
+                         else v2) for k2, v2 in d.items()}
+        line["cpu_baseline"] = rounded(cpu_baseline(w, unit_job, args.cpu_seconds))
     print(json.dumps(line), flush=True)
 
 
