@@ -129,6 +129,11 @@ __global__ __launch_bounds__(128) void qprep_kernel(DecodeArgs a) {
   }
 }
 
+// Row stride (floats) of a wave's page weights in LDS, [head][token]: four
+// floats past a page, so that the four head rows a matrix-core step reads
+// at once (lane % 4 picks the row) fall in different LDS banks.
+constexpr int kWRow = PT + 4;
+
 // Per-workgroup LDS of the split kernel.
 template <int G>
 struct SplitLds {
@@ -138,7 +143,7 @@ struct SplitLds {
   float4 vquad[272];
   float kcent[512];           // centroid lists for every bit width (table layout)
   float vcent[512];
-  float w[kDecodeWaves][(G < 4 ? 4 : G) * PT];   // weights of the current page, [head][token]
+  float w[kDecodeWaves][(G < 4 ? 4 : G) * kWRow];   // weights of the current page, [head][token]
                                                  // (rows G..3 stay zero)
   float red[kDecodeWaves][G * D];          // workgroup reduction
   float stat[kDecodeWaves][2][G];          // m, l per wave
@@ -164,21 +169,25 @@ __device__ __forceinline__ void key_scores_w(const uint32_t (&sw)[N], const floa
                                              const float2* pair, const float4* quad, const float* cent,
                                              float (&s)[G]) {
   static_assert(N >= 4 * B, "the stream's words");
-  constexpr int CH = 4;                       // coordinates per chunk
+  constexpr int CH = 8;                       // coordinates per chunk
 #pragma clang loop unroll(full)
   for (int h = 0; h < G; ++h) s[h] = 0.f;
   float qa[G][CH], qb[G][CH], ca[CH], cb[CH];
   auto fetch = [&](int n, float (&qd)[G][CH], float (&cd)[CH]) {
+    // prepared query: groups of four coordinates, all heads of a group together
 #pragma clang loop unroll(full)
     for (int h = 0; h < G; ++h)
 #pragma clang loop unroll(full)
-      for (int e = 0; e < CH; ++e) qd[h][e] = qr[(n * G + h) * CH + e];
+      for (int e = 0; e < CH; ++e) qd[h][e] = qr[((n * CH / 4 + (e >> 2)) * G + h) * 4 + (e & 3)];
     if constexpr (B <= 2) {
-      const float4 c = quad[quad_offset(B) + bits_at(sw, n * CH * B, 4 * B)];
-      cd[0] = c.x;
-      cd[1] = c.y;
-      cd[2] = c.z;
-      cd[3] = c.w;
+#pragma clang loop unroll(full)
+      for (int e = 0; e < CH; e += 4) {
+        const float4 c = quad[quad_offset(B) + bits_at(sw, (n * CH + e) * B, 4 * B)];
+        cd[e] = c.x;
+        cd[e + 1] = c.y;
+        cd[e + 2] = c.z;
+        cd[e + 3] = c.w;
+      }
     } else if constexpr (B <= 4) {
       const float2* pt = pair + pair_offset(B);
 #pragma clang loop unroll(full)
@@ -331,34 +340,52 @@ __device__ __forceinline__ void value_mfma_w(const uint32_t (&sw)[N], int lane, 
                                              const float2* pair, const float4* quad,
                                              v4f (&acc)[NG][2]) {
   static_assert(N >= 4 * B, "the stream's words");
-  const float* wl = wv + (lane & 3) * PT;
+  const float* wl = wv + (lane & 3) * kWRow;
+  // four tokens per step; step u + 1's weights and centroids are read from LDS
+  // while step u's products run (LDS reads complete in order, so the wait
+  // before step u's products leaves step u + 1's reads in flight)
+  float4 wa[NG], wb[NG];
+  float ca[8], cb[8];   // per token pair: (t, first), (t, second), (t + 1, first), (t + 1, second)
+  auto fetch = [&](int t4, float4 (&wd)[NG], float (&cd)[8]) {
 #pragma clang loop unroll(full)
-  for (int t4 = 0; t4 < PT / 4; ++t4) {
-    float4 a[NG];
-#pragma clang loop unroll(full)
-    for (int g = 0; g < NG; ++g) a[g] = *reinterpret_cast<const float4*>(wl + 4 * g * PT + 4 * t4);
+    for (int g = 0; g < NG; ++g) wd[g] = *reinterpret_cast<const float4*>(wl + 4 * g * kWRow + 4 * t4);
 #pragma clang loop unroll(full)
     for (int e = 0; e < 4; e += 2) {
       const int t = 4 * t4 + e;
-      float c[4];   // (t, first), (t, second), (t + 1, first), (t + 1, second)
       if constexpr (B <= 2) {
         const float4 q = quad[quad_offset(B) + bits_at(sw, 2 * t * B, 4 * B)];
-        c[0] = q.x; c[1] = q.y; c[2] = q.z; c[3] = q.w;
+        cd[2 * e] = q.x; cd[2 * e + 1] = q.y; cd[2 * e + 2] = q.z; cd[2 * e + 3] = q.w;
       } else {
         const float2* pt = pair + pair_offset(B);
         const float2 p0 = pt[bits_at(sw, 2 * t * B, 2 * B)];
         const float2 p1 = pt[bits_at(sw, 2 * (t + 1) * B, 2 * B)];
-        c[0] = p0.x; c[1] = p0.y; c[2] = p1.x; c[3] = p1.y;
-      }
-#pragma clang loop unroll(full)
-      for (int g = 0; g < NG; ++g) {
-        const float a0 = e == 0 ? a[g].x : a[g].z, a1 = e == 0 ? a[g].y : a[g].w;
-        acc[g][0] = __builtin_amdgcn_mfma_f32_4x4x1f32(a0, c[0], acc[g][0], 0, 0, 0);
-        acc[g][1] = __builtin_amdgcn_mfma_f32_4x4x1f32(a0, c[1], acc[g][1], 0, 0, 0);
-        acc[g][0] = __builtin_amdgcn_mfma_f32_4x4x1f32(a1, c[2], acc[g][0], 0, 0, 0);
-        acc[g][1] = __builtin_amdgcn_mfma_f32_4x4x1f32(a1, c[3], acc[g][1], 0, 0, 0);
+        cd[2 * e] = p0.x; cd[2 * e + 1] = p0.y; cd[2 * e + 2] = p1.x; cd[2 * e + 3] = p1.y;
       }
     }
+  };
+  auto products = [&](const float4 (&wd)[NG], const float (&cd)[8]) {
+#pragma clang loop unroll(full)
+    for (int e = 0; e < 4; e += 2)
+#pragma clang loop unroll(full)
+      for (int g = 0; g < NG; ++g) {
+        const float a0 = e == 0 ? wd[g].x : wd[g].z, a1 = e == 0 ? wd[g].y : wd[g].w;
+        acc[g][0] = __builtin_amdgcn_mfma_f32_4x4x1f32(a0, cd[2 * e], acc[g][0], 0, 0, 0);
+        acc[g][1] = __builtin_amdgcn_mfma_f32_4x4x1f32(a0, cd[2 * e + 1], acc[g][1], 0, 0, 0);
+        acc[g][0] = __builtin_amdgcn_mfma_f32_4x4x1f32(a1, cd[2 * e + 2], acc[g][0], 0, 0, 0);
+        acc[g][1] = __builtin_amdgcn_mfma_f32_4x4x1f32(a1, cd[2 * e + 3], acc[g][1], 0, 0, 0);
+      }
+  };
+  fetch(0, wa, ca);
+#pragma clang loop unroll(full)
+  for (int t4 = 0; t4 < PT / 4; t4 += 2) {
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(t4 + 1, wb, cb);
+    __builtin_amdgcn_sched_barrier(0);
+    products(wa, ca);
+    __builtin_amdgcn_sched_barrier(0);
+    if (t4 + 2 < PT / 4) fetch(t4 + 2, wa, ca);
+    __builtin_amdgcn_sched_barrier(0);
+    products(wb, cb);
   }
 }
 
@@ -445,7 +472,7 @@ __device__ __forceinline__ void value_mfma_wide(const char* blk, int lane, const
                                                 v4f (&acc)[NG][2]) {
   const uint32_t* src = reinterpret_cast<const uint32_t*>(blk);
   const float* ct = cent + centroid_offset(B);
-  const float* wl = wv + (lane & 3) * PT;
+  const float* wl = wv + (lane & 3) * kWRow;
   uint32_t w[B], nx[B];
   auto load = [&](int n, uint32_t (&d)[B]) {
 #pragma clang loop unroll(full)
@@ -462,7 +489,7 @@ __device__ __forceinline__ void value_mfma_wide(const char* blk, int lane, const
     for (int t4 = 0; t4 < 4; ++t4) {
       float4 a[NG];
 #pragma clang loop unroll(full)
-      for (int g = 0; g < NG; ++g) a[g] = *reinterpret_cast<const float4*>(wl + 4 * g * PT + 16 * n + 4 * t4);
+      for (int g = 0; g < NG; ++g) a[g] = *reinterpret_cast<const float4*>(wl + 4 * g * kWRow + 16 * n + 4 * t4);
 #pragma clang loop unroll(full)
       for (int e = 0; e < 4; ++e) {
         const int tl = 4 * t4 + e;   // token 16 n + tl: codes at pass positions 2 tl, 2 tl + 1
@@ -541,7 +568,7 @@ __device__ __forceinline__ void value_accum_fp16(const char* page, int lane, con
       row(t, x);
 #pragma clang loop unroll(full)
       for (int h = 0; h < G; ++h) {
-        const float wt = wv[h * PT + t];
+        const float wt = wv[h * kWRow + t];
 #pragma clang loop unroll(full)
         for (int e = 0; e < 8; ++e) y[h][e] = fmaf(wt, x[e], y[h][e]);
       }
@@ -560,7 +587,7 @@ __device__ __forceinline__ void value_accum_fp16(const char* page, int lane, con
       rotate(x);
 #pragma clang loop unroll(full)
       for (int h = 0; h < G; ++h) {
-        const float wt = wv[h * PT + t];
+        const float wt = wv[h * kWRow + t];
 #pragma clang loop unroll(full)
         for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(wt, x[e], acc[h][e]);
       }
@@ -785,7 +812,7 @@ void split_kernel(DecodeArgs a,
   for (int g = 0; g < NG; ++g) acc[g][0] = acc[g][1] = v4f{0.f, 0.f, 0.f, 0.f};
   float* wv = sm.w[wave];
   if constexpr (G < 4) {
-    for (int i = lane; i < 4 * PT; i += 64) wv[i] = 0.f;
+    for (int i = lane; i < 4 * kWRow; i += 64) wv[i] = 0.f;
     wave_lds_sync();
   }
   const int q4 = lane >> 4, i16 = lane & 15;
@@ -850,7 +877,7 @@ void split_kernel(DecodeArgs a,
         }
       }
   #pragma clang loop unroll(full)
-      for (int h = 0; h < G; ++h) wv[h * PT + lane] = s[h] * nv;
+      for (int h = 0; h < G; ++h) wv[h * kWRow + lane] = s[h] * nv;
       wave_lds_sync();
     };
 
