@@ -135,17 +135,24 @@ __global__ __launch_bounds__(128) void qprep_kernel(DecodeArgs a) {
 constexpr int kWRow = PT + 4;
 
 // Per-workgroup LDS of the split kernel.
-template <int G>
-struct SplitLds {
+struct SplitTables {
   float2 kpair[340];          // pair tables for bits 1..4 (4 + 16 + 64 + 256 entries)
   float2 vpair[340];
   float4 kquad[272];          // quad tables for bits 1..2 (16 + 256 entries)
   float4 vquad[272];
   float kcent[512];           // centroid lists for every bit width (table layout)
   float vcent[512];
+};
+template <int G>
+struct SplitLds {
+  // the codebook tables serve the page loop; the workgroup reduction reuses
+  // their space once every wave has left the loop (after a barrier)
+  union {
+    SplitTables t;
+    float red[kDecodeWaves][G * D];
+  };
   float w[kDecodeWaves][(G < 4 ? 4 : G) * kWRow];   // weights of the current page, [head][token]
                                                  // (rows G..3 stay zero)
-  float red[kDecodeWaves][G * D];          // workgroup reduction
   float stat[kDecodeWaves][2][G];          // m, l per wave
   uint64_t desc[kMaxPagesPerSplit];        // the range's page descriptors, read once
 };
@@ -743,24 +750,24 @@ void split_kernel(DecodeArgs a,
   // all fp16, as a decode loop's tail pages are).
   if (need_tables) {
     for (int i = tid; i < 510; i += blockDim.x) {
-      sm.kcent[i] = a.k_table[i];
-      sm.vcent[i] = a.v_table[i];
+      sm.t.kcent[i] = a.k_table[i];
+      sm.t.vcent[i] = a.v_table[i];
     }
     // pair tables come with the codebook table (a scalar codebook's (c[lo],
     // c[hi]), or PolarQuant's radius-angle pairs); a quad entry is two pairs
     const float2* kpt = reinterpret_cast<const float2*>(a.k_table + kPairOffset);
     const float2* vpt = reinterpret_cast<const float2*>(a.v_table + kPairOffset);
     for (int i = tid; i < 340; i += blockDim.x) {
-      sm.kpair[i] = kpt[i];
-      sm.vpair[i] = vpt[i];
+      sm.t.kpair[i] = kpt[i];
+      sm.t.vpair[i] = vpt[i];
     }
     for (int i = tid; i < 272; i += blockDim.x) {
       const int bb = i < 16 ? 1 : 2;
       const int idx = i - quad_offset(bb), sh = 2 * bb, po = pair_offset(bb);
       const int p0 = po + (idx & ((1 << sh) - 1)), p1 = po + (idx >> sh);
       const float2 k0 = kpt[p0], k1 = kpt[p1], v0 = vpt[p0], v1 = vpt[p1];
-      sm.kquad[i] = make_float4(k0.x, k0.y, k1.x, k1.y);
-      sm.vquad[i] = make_float4(v0.x, v0.y, v1.x, v1.y);
+      sm.t.kquad[i] = make_float4(k0.x, k0.y, k1.x, k1.y);
+      sm.t.vquad[i] = make_float4(v0.x, v0.y, v1.x, v1.y);
     }
     __syncthreads();
   }
@@ -882,76 +889,50 @@ void split_kernel(DecodeArgs a,
     };
 
     if constexpr (PC == 0) {
-      // Common pages, one page ahead: the next page's K and V code words and
-      // norms are loaded while this page is computed.  Every lane issues the
-      // same ten loads per page (words past a width repeat its last word; a
-      // page to skip reads the codebook table, 48 KB, instead), so the waits
-      // on this page's data count loads statically.
-      uint32_t kw[16], vw[16], kn[16], vn[16];
-      float nk, nv, nkn, nvn;
-      int kb, vb, kbn, vbn;   // kb = 0: no page of the class here
-      auto fetch = [&](int p, uint32_t (&kd)[16], uint32_t (&vd)[16], float& fk, float& fv, int& fkb,
-                       int& fvb) {
-        bool ok = false;
-        int kb_ = 1, vb_ = 1;
-        uint64_t off = 0;
-        if (p < p_end) {
-          const PageDesc pd = read_desc(sm.desc[p - p_begin]);
-          ok = pd.present && !pd.qjl && pd.kb >= 1 && pd.kb <= 4 && pd.vb >= 1 && pd.vb <= 4 &&
-               pd.off + page_size_dev(pd.kb, pd.vb, false) <= a.pool_bytes;
-          if (ok) {
-            kb_ = pd.kb;
-            vb_ = pd.vb;
-            off = pd.off;
-          }
-        }
-        const char* kp = ok ? a.pool + off : reinterpret_cast<const char*>(a.k_table);
-        const char* vp = ok ? kp + 1024 * kb_ + 256 : reinterpret_cast<const char*>(a.k_table);
+      // Common pages.  Every lane issues the same ten loads per page (words
+      // past a width repeat its last word), K and V together at the page's
+      // start, so the V words arrive while the scores are computed; the other
+      // waves of the SIMD cover the wait for the K words.
+      for (int p = p_begin + wave; p < p_end; p += kDecodeWaves) {
+        const PageDesc pd = read_desc(sm.desc[p - p_begin]);
+        const bool ok = pd.present && !pd.qjl && pd.kb >= 1 && pd.kb <= 4 && pd.vb >= 1 && pd.vb <= 4 &&
+                        pd.off + page_size_dev(pd.kb, pd.vb, false) <= a.pool_bytes;
+        if (!__builtin_amdgcn_readfirstlane(ok)) continue;
+        const int kb = __builtin_amdgcn_readfirstlane(pd.kb), vb = __builtin_amdgcn_readfirstlane(pd.vb);
+        const char* kp = a.pool + pd.off;
+        const char* vp = kp + 1024 * kb + 256;
         const uint4* ks = reinterpret_cast<const uint4*>(kp);
         const uint4* vs = reinterpret_cast<const uint4*>(vp);
+        uint32_t kw[16], vw[16];
   #pragma clang loop unroll(full)
         for (int w = 0; w < 4; ++w) {
-          const uint4 x = ks[min(w, kb_ - 1) * 64 + lane];
-          const uint4 y = vs[min(w, vb_ - 1) * 64 + lane];
-          kd[4 * w] = x.x; kd[4 * w + 1] = x.y; kd[4 * w + 2] = x.z; kd[4 * w + 3] = x.w;
-          vd[4 * w] = y.x; vd[4 * w + 1] = y.y; vd[4 * w + 2] = y.z; vd[4 * w + 3] = y.w;
+          const uint4 x = ks[min(w, kb - 1) * 64 + lane];
+          kw[4 * w] = x.x; kw[4 * w + 1] = x.y; kw[4 * w + 2] = x.z; kw[4 * w + 3] = x.w;
         }
-        fk = reinterpret_cast<const float*>(kp + 1024 * kb_)[lane];
-        fv = reinterpret_cast<const float*>(vp + 1024 * vb_)[lane];
-        fkb = ok ? kb_ : 0;
-        fvb = vb_;
-      };
-      fetch(p_begin + wave, kw, vw, nk, nv, kb, vb);
-      for (int p = p_begin + wave; p < p_end; p += kDecodeWaves) {
-        fetch(p + kDecodeWaves, kn, vn, nkn, nvn, kbn, vbn);
-        if (kb != 0) {
-          float s[G];
-          switch (kb) {
-            case 1: key_scores_w<1, G>(kw, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
-            case 2: key_scores_w<2, G>(kw, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
-            case 3: key_scores_w<3, G>(kw, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
-            default: key_scores_w<4, G>(kw, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
-          }
+        const float nk = reinterpret_cast<const float*>(kp + 1024 * kb)[lane];
   #pragma clang loop unroll(full)
-          for (int h = 0; h < G; ++h) s[h] *= nk;
-          weigh(p, s, nv, min(PT, ntok - p * PT));
-          switch (vb) {
-            case 1: value_mfma_w<1, NG>(vw, lane, wv, sm.vpair, sm.vquad, acc); break;
-            case 2: value_mfma_w<2, NG>(vw, lane, wv, sm.vpair, sm.vquad, acc); break;
-            case 3: value_mfma_w<3, NG>(vw, lane, wv, sm.vpair, sm.vquad, acc); break;
-            default: value_mfma_w<4, NG>(vw, lane, wv, sm.vpair, sm.vquad, acc); break;
-          }
-          wave_lds_sync();
+        for (int w = 0; w < 4; ++w) {
+          const uint4 y = vs[min(w, vb - 1) * 64 + lane];
+          vw[4 * w] = y.x; vw[4 * w + 1] = y.y; vw[4 * w + 2] = y.z; vw[4 * w + 3] = y.w;
+        }
+        const float nv = reinterpret_cast<const float*>(vp + 1024 * vb)[lane];
+        float s[G];
+        switch (kb) {
+          case 1: key_scores_w<1, G>(kw, qrow, sm.t.kpair, sm.t.kquad, sm.t.kcent, s); break;
+          case 2: key_scores_w<2, G>(kw, qrow, sm.t.kpair, sm.t.kquad, sm.t.kcent, s); break;
+          case 3: key_scores_w<3, G>(kw, qrow, sm.t.kpair, sm.t.kquad, sm.t.kcent, s); break;
+          default: key_scores_w<4, G>(kw, qrow, sm.t.kpair, sm.t.kquad, sm.t.kcent, s); break;
         }
   #pragma clang loop unroll(full)
-        for (int i = 0; i < 16; ++i) {
-          kw[i] = kn[i];
-          vw[i] = vn[i];
+        for (int h = 0; h < G; ++h) s[h] *= nk;
+        weigh(p, s, nv, min(PT, ntok - p * PT));
+        switch (vb) {
+          case 1: value_mfma_w<1, NG>(vw, lane, wv, sm.t.vpair, sm.t.vquad, acc); break;
+          case 2: value_mfma_w<2, NG>(vw, lane, wv, sm.t.vpair, sm.t.vquad, acc); break;
+          case 3: value_mfma_w<3, NG>(vw, lane, wv, sm.t.vpair, sm.t.vquad, acc); break;
+          default: value_mfma_w<4, NG>(vw, lane, wv, sm.t.vpair, sm.t.vquad, acc); break;
         }
-        nk = nkn;
-        nv = nvn;
-        kb = kbn;
-        vb = vbn;
+        wave_lds_sync();
       }
       return;
     }
@@ -983,28 +964,28 @@ void split_kernel(DecodeArgs a,
       } else {
         if constexpr (PC == 0) {
           switch (kb) {
-            case 1: key_scores<1, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
-            case 2: key_scores<2, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
-            case 3: key_scores<3, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
-            default: key_scores<4, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
+            case 1: key_scores<1, G>(page, lane, qrow, sm.t.kpair, sm.t.kquad, sm.t.kcent, s); break;
+            case 2: key_scores<2, G>(page, lane, qrow, sm.t.kpair, sm.t.kquad, sm.t.kcent, s); break;
+            case 3: key_scores<3, G>(page, lane, qrow, sm.t.kpair, sm.t.kquad, sm.t.kcent, s); break;
+            default: key_scores<4, G>(page, lane, qrow, sm.t.kpair, sm.t.kquad, sm.t.kcent, s); break;
           }
         } else if constexpr (PC == 1) {
           switch (kb) {
-            case 5: key_scores_wide<5, G>(page, lane, qrow, sm.kcent, s); break;
-            case 6: key_scores_wide<6, G>(page, lane, qrow, sm.kcent, s); break;
-            case 7: key_scores_wide<7, G>(page, lane, qrow, sm.kcent, s); break;
-            default: key_scores_wide<8, G>(page, lane, qrow, sm.kcent, s); break;
+            case 5: key_scores_wide<5, G>(page, lane, qrow, sm.t.kcent, s); break;
+            case 6: key_scores_wide<6, G>(page, lane, qrow, sm.t.kcent, s); break;
+            case 7: key_scores_wide<7, G>(page, lane, qrow, sm.t.kcent, s); break;
+            default: key_scores_wide<8, G>(page, lane, qrow, sm.t.kcent, s); break;
           }
         } else {
           switch (kb) {
-            case 1: key_scores<1, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
-            case 2: key_scores<2, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
-            case 3: key_scores<3, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
-            case 4: key_scores<4, G>(page, lane, qrow, sm.kpair, sm.kquad, sm.kcent, s); break;
-            case 5: key_scores_wide<5, G>(page, lane, qrow, sm.kcent, s); break;
-            case 6: key_scores_wide<6, G>(page, lane, qrow, sm.kcent, s); break;
-            case 7: key_scores_wide<7, G>(page, lane, qrow, sm.kcent, s); break;
-            default: key_scores_wide<8, G>(page, lane, qrow, sm.kcent, s); break;
+            case 1: key_scores<1, G>(page, lane, qrow, sm.t.kpair, sm.t.kquad, sm.t.kcent, s); break;
+            case 2: key_scores<2, G>(page, lane, qrow, sm.t.kpair, sm.t.kquad, sm.t.kcent, s); break;
+            case 3: key_scores<3, G>(page, lane, qrow, sm.t.kpair, sm.t.kquad, sm.t.kcent, s); break;
+            case 4: key_scores<4, G>(page, lane, qrow, sm.t.kpair, sm.t.kquad, sm.t.kcent, s); break;
+            case 5: key_scores_wide<5, G>(page, lane, qrow, sm.t.kcent, s); break;
+            case 6: key_scores_wide<6, G>(page, lane, qrow, sm.t.kcent, s); break;
+            case 7: key_scores_wide<7, G>(page, lane, qrow, sm.t.kcent, s); break;
+            default: key_scores_wide<8, G>(page, lane, qrow, sm.t.kcent, s); break;
           }
         }
   #pragma clang loop unroll(full)
@@ -1031,28 +1012,28 @@ void split_kernel(DecodeArgs a,
         }
       } else if constexpr (PC == 0) {
         switch (vb) {
-          case 1: value_mfma<1, NG>(vblk, lane, wv, sm.vpair, sm.vquad, acc); break;
-          case 2: value_mfma<2, NG>(vblk, lane, wv, sm.vpair, sm.vquad, acc); break;
-          case 3: value_mfma<3, NG>(vblk, lane, wv, sm.vpair, sm.vquad, acc); break;
-          default: value_mfma<4, NG>(vblk, lane, wv, sm.vpair, sm.vquad, acc); break;
+          case 1: value_mfma<1, NG>(vblk, lane, wv, sm.t.vpair, sm.t.vquad, acc); break;
+          case 2: value_mfma<2, NG>(vblk, lane, wv, sm.t.vpair, sm.t.vquad, acc); break;
+          case 3: value_mfma<3, NG>(vblk, lane, wv, sm.t.vpair, sm.t.vquad, acc); break;
+          default: value_mfma<4, NG>(vblk, lane, wv, sm.t.vpair, sm.t.vquad, acc); break;
         }
       } else if constexpr (PC == 1) {
         switch (vb) {
-          case 5: value_mfma_wide<5, NG>(vblk, lane, wv, sm.vcent, acc); break;
-          case 6: value_mfma_wide<6, NG>(vblk, lane, wv, sm.vcent, acc); break;
-          case 7: value_mfma_wide<7, NG>(vblk, lane, wv, sm.vcent, acc); break;
-          default: value_mfma_wide<8, NG>(vblk, lane, wv, sm.vcent, acc); break;
+          case 5: value_mfma_wide<5, NG>(vblk, lane, wv, sm.t.vcent, acc); break;
+          case 6: value_mfma_wide<6, NG>(vblk, lane, wv, sm.t.vcent, acc); break;
+          case 7: value_mfma_wide<7, NG>(vblk, lane, wv, sm.t.vcent, acc); break;
+          default: value_mfma_wide<8, NG>(vblk, lane, wv, sm.t.vcent, acc); break;
         }
       } else {
         switch (vb) {
-          case 1: value_mfma<1, NG>(vblk, lane, wv, sm.vpair, sm.vquad, acc); break;
-          case 2: value_mfma<2, NG>(vblk, lane, wv, sm.vpair, sm.vquad, acc); break;
-          case 3: value_mfma<3, NG>(vblk, lane, wv, sm.vpair, sm.vquad, acc); break;
-          case 4: value_mfma<4, NG>(vblk, lane, wv, sm.vpair, sm.vquad, acc); break;
-          case 5: value_mfma_wide<5, NG>(vblk, lane, wv, sm.vcent, acc); break;
-          case 6: value_mfma_wide<6, NG>(vblk, lane, wv, sm.vcent, acc); break;
-          case 7: value_mfma_wide<7, NG>(vblk, lane, wv, sm.vcent, acc); break;
-          default: value_mfma_wide<8, NG>(vblk, lane, wv, sm.vcent, acc); break;
+          case 1: value_mfma<1, NG>(vblk, lane, wv, sm.t.vpair, sm.t.vquad, acc); break;
+          case 2: value_mfma<2, NG>(vblk, lane, wv, sm.t.vpair, sm.t.vquad, acc); break;
+          case 3: value_mfma<3, NG>(vblk, lane, wv, sm.t.vpair, sm.t.vquad, acc); break;
+          case 4: value_mfma<4, NG>(vblk, lane, wv, sm.t.vpair, sm.t.vquad, acc); break;
+          case 5: value_mfma_wide<5, NG>(vblk, lane, wv, sm.t.vcent, acc); break;
+          case 6: value_mfma_wide<6, NG>(vblk, lane, wv, sm.t.vcent, acc); break;
+          case 7: value_mfma_wide<7, NG>(vblk, lane, wv, sm.t.vcent, acc); break;
+          default: value_mfma_wide<8, NG>(vblk, lane, wv, sm.t.vcent, acc); break;
         }
       }
       wave_lds_sync();
