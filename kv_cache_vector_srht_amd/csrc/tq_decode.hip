@@ -154,6 +154,7 @@ struct SplitLds {
   float w[kDecodeWaves][(G < 4 ? 4 : G) * kWRow];   // weights of the current page, [head][token]
                                                  // (rows G..3 stay zero)
   float stat[kDecodeWaves][2][G];          // m, l per wave
+  int widths[kDecodeWaves];                // page widths each wave's descriptors hold
   uint64_t desc[kMaxPagesPerSplit];        // the range's page descriptors, read once
 };
 
@@ -176,7 +177,8 @@ __device__ __forceinline__ void key_scores_w(const uint32_t (&sw)[N], const floa
                                              const float2* pair, const float4* quad, const float* cent,
                                              float (&s)[G]) {
   static_assert(N >= 4 * B, "the stream's words");
-  constexpr int CH = 8;                       // coordinates per chunk
+  constexpr int CH = G >= 8 ? 4 : 8;          // coordinates per chunk (its query values
+                                              // take 2 x G x CH scalar registers)
 #pragma clang loop unroll(full)
   for (int h = 0; h < G; ++h) s[h] = 0.f;
   float qa[G][CH], qb[G][CH], ca[CH], cb[CH];
@@ -514,92 +516,60 @@ __device__ __forceinline__ void value_mfma_wide(const char* blk, int lane, const
   }
 }
 
-// Value accumulation of an fp16 page into the rotated-domain sums: each token's
-// row is rotated with the unnormalised D H D (the 16 lanes of a quarter hold
-// its 128 values, 8 each), so that D H D acc / d at the end returns sum p v.
-// Value sums of an fp16 page: acc (rotated domain) += D H D sum_t w_t v_t.
-// Lane (quarter q, 16 lanes i) sums coordinates 8i..8i+7 of tokens 4k+q in
-// the original domain; then, once per page and query head, the quarter's sum
-// is rotated (the transform is linear), in-lane for coordinate bits 0..2 and
-// across the 16 lanes of the quarter for bits 3..6.  Up to G = 4; wider groups
-// rotate each token's row (fewer registers).
-template <int G>
-__device__ __forceinline__ void value_accum_fp16(const char* page, int lane, const float* wv,
-                                                 const uint32_t (&dm)[8], float (&acc)[G][8]) {
-  const __half* vbase = reinterpret_cast<const __half*>(page + PT * D * 2);
-  const int q = lane >> 4, i = lane & 15;
-  auto rotate = [&](float (&x)[8]) {
-#pragma clang loop unroll(full)
-    for (int e = 0; e < 8; ++e) x[e] = flip_if(x[e], dm[e]);
-#pragma clang loop unroll(full)
-    for (int hh = 1; hh < 8; hh <<= 1)
-#pragma clang loop unroll(full)
-      for (int e = 0; e < 8; ++e)
-        if (!(e & hh)) {
-          const float a0 = x[e], b0 = x[e + hh];
-          x[e] = a0 + b0;
-          x[e + hh] = a0 - b0;
-        }
-#pragma clang loop unroll(full)
-    for (int m = 1; m < 16; m <<= 1) {
-      const float sg = (i & m) ? -1.f : 1.f;
-#pragma clang loop unroll(full)
-      for (int e = 0; e < 8; ++e) {
-        const float other = __shfl_xor(x[e], m, 64);
-        x[e] = fmaf(sg, x[e], other);
-      }
-    }
-#pragma clang loop unroll(full)
-    for (int e = 0; e < 8; ++e) x[e] = flip_if(x[e], dm[e]);
-  };
-  auto row = [&](int t, float (&x)[8]) {
-    const uint4 vv = reinterpret_cast<const uint4*>(vbase + (size_t)t * D + 8 * i)[0];
-    const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma clang loop unroll(full)
-    for (int e = 0; e < 4; ++e) {
-      const float2 f = __half22float2(*reinterpret_cast<const __half2*>(&vw[e]));
-      x[2 * e] = f.x;
-      x[2 * e + 1] = f.y;
-    }
-  };
-  if constexpr (G <= 4) {
-    float y[G][8];
-#pragma clang loop unroll(full)
-    for (int h = 0; h < G; ++h)
-#pragma clang loop unroll(full)
-      for (int e = 0; e < 8; ++e) y[h][e] = 0.f;
+// Value sums of an fp16 page on the matrix cores, as value_mfma_w but in the
+// original domain (the caller rotates the sums once, after the last page): the
+// B operand of token t is its value at the lane's coordinates
+// v_stream_coord(L, 0) and v_stream_coord(L, 0) + 1, one 4-byte load per token.
+template <int NG>
+__device__ __forceinline__ void value_mfma_fp16(const char* page, int lane, const float* wv,
+                                                v4f (&acc)[NG][2]) {
+  const __half2* vcol = reinterpret_cast<const __half2*>(page + PT * D * 2) + v_stream_coord(lane, 0) / 2;
+  const float* wl = wv + (lane & 3) * kWRow;
 #pragma clang loop unroll_count(4)
-    for (int k = 0; k < 16; ++k) {
-      const int t = 4 * k + q;
-      float x[8];
-      row(t, x);
+  for (int t4 = 0; t4 < PT / 4; ++t4) {
+    float2 v[4];
 #pragma clang loop unroll(full)
-      for (int h = 0; h < G; ++h) {
-        const float wt = wv[h * kWRow + t];
+    for (int e = 0; e < 4; ++e) v[e] = __half22float2(vcol[(4 * t4 + e) * (D / 2)]);
 #pragma clang loop unroll(full)
-        for (int e = 0; e < 8; ++e) y[h][e] = fmaf(wt, x[e], y[h][e]);
-      }
-    }
+    for (int g = 0; g < NG; ++g) {
+      const float4 wd = *reinterpret_cast<const float4*>(wl + 4 * g * kWRow + 4 * t4);
+      const float w4[4] = {wd.x, wd.y, wd.z, wd.w};
 #pragma clang loop unroll(full)
-    for (int h = 0; h < G; ++h) {
-      rotate(y[h]);
-#pragma clang loop unroll(full)
-      for (int e = 0; e < 8; ++e) acc[h][e] += y[h][e];
-    }
-  } else {
-    for (int k = 0; k < 16; ++k) {
-      const int t = 4 * k + q;
-      float x[8];
-      row(t, x);
-      rotate(x);
-#pragma clang loop unroll(full)
-      for (int h = 0; h < G; ++h) {
-        const float wt = wv[h * kWRow + t];
-#pragma clang loop unroll(full)
-        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(wt, x[e], acc[h][e]);
+      for (int e = 0; e < 4; ++e) {
+        acc[g][0] = __builtin_amdgcn_mfma_f32_4x4x1f32(w4[e], v[e].x, acc[g][0], 0, 0, 0);
+        acc[g][1] = __builtin_amdgcn_mfma_f32_4x4x1f32(w4[e], v[e].y, acc[g][1], 0, 0, 0);
       }
     }
   }
+}
+
+// acc += D H D x for sums x held as the matrix-core value sums hold them (lane
+// L: coordinates c = v_stream_coord(L, k), k = 0, 1): coordinate bit 0 is the
+// register pair, and bits 1, 2, 3, 4, 5, 6 are lane bits 0, 1, 3, 4, 5, 2, so
+// the unnormalised transform is one in-lane butterfly and six lane exchanges.
+template <int NG>
+__device__ __forceinline__ void add_rotated(const v4f (&x)[NG][2], int lane, const uint32_t* sign_mask,
+                                            v4f (&acc)[NG][2]) {
+  const int c0 = v_stream_coord(lane, 0);
+  const uint32_t n0 = (sign_mask[c0 >> 5] >> (c0 & 31)) & 1u, n1 = (sign_mask[c0 >> 5] >> ((c0 + 1) & 31)) & 1u;
+  constexpr int kLaneBit[6] = {0, 1, 3, 4, 5, 2};
+#pragma clang loop unroll(full)
+  for (int g = 0; g < NG; ++g)
+#pragma clang loop unroll(full)
+    for (int i = 0; i < 4; ++i) {
+      const float y0 = flip_if(x[g][0][i], n0), y1 = flip_if(x[g][1][i], n1);
+      float u0 = y0 + y1, u1 = y0 - y1;
+#pragma clang loop unroll(full)
+      for (int st = 0; st < 6; ++st) {
+        const int m = 1 << kLaneBit[st];
+        const float o0 = __shfl_xor(u0, m, 64), o1 = __shfl_xor(u1, m, 64);
+        const float sg = (lane & m) ? -1.f : 1.f;
+        u0 = fmaf(sg, u0, o0);
+        u1 = fmaf(sg, u1, o1);
+      }
+      acc[g][0][i] += flip_if(u0, n0);
+      acc[g][1][i] += flip_if(u1, n1);
+    }
 }
 
 // Online-softmax update of one page for G heads.  s: log2-domain scores of
@@ -726,6 +696,7 @@ void split_kernel(DecodeArgs a,
     // nothing of this class in the range: an empty partial, no setup (the
     // descriptors are read in parallel, one per thread)
     bool mine = false, coded = false;
+    int widths = 0;   // bit b: a packed page of the class with K width b; bit 9 + b: V width b
     for (int p = p_begin + tid; p < p_end; p += blockDim.x) {
       const uint64_t raw = ptab[p];
       sm.desc[p - p_begin] = raw;   // the page loop reads it from LDS
@@ -733,10 +704,14 @@ void split_kernel(DecodeArgs a,
       const bool m = page_class(pd.kb, pd.vb, pd.qjl) == cls;
       mine |= m;
       coded |= m && pd.kb != 0;
+      if (m && pd.kb != 0 && pd.kb <= 8 && pd.vb <= 8) widths |= (1 << pd.kb) | (1 << (9 + pd.vb));
     }
+#pragma clang loop unroll(full)
+    for (int o = 1; o < 64; o <<= 1) widths |= __shfl_xor(widths, o, 64);
     __syncthreads();   // the cached descriptors are visible to every wave
+    if (lane == 0) sm.widths[wave] = widths;
     need_tables = cls != 2 || __syncthreads_or(coded);
-    if (!__syncthreads_or(mine)) {
+    if (!__syncthreads_or(mine)) {   // (also makes sm.widths visible)
       if (tid < G) {
         part[tid * head_stride] = -INFINITY;
         part[tid * head_stride + 1] = 0.f;
@@ -745,35 +720,45 @@ void split_kernel(DecodeArgs a,
     }
   }
 
-  // Stage codebooks: pair tables for 1..4 bits, quad tables for 1..2 bits and
-  // all centroid lists (not needed when the range's pages of this class are
-  // all fp16, as a decode loop's tail pages are).
-  if (need_tables) {
-    for (int i = tid; i < 510; i += blockDim.x) {
-      sm.t.kcent[i] = a.k_table[i];
-      sm.t.vcent[i] = a.v_table[i];
-    }
+  // Stage the codebook tables the range's pages of this class use: pair
+  // tables at 3-4 bits, quad tables at 1-2 bits, centroid lists at 5-8 bits
+  // (nothing when those pages are all fp16, as a decode loop's tail pages are).
+  auto stage_tables = [&]() {
+    if (!need_tables) return;
+    int widths = 0;
+#pragma clang loop unroll(full)
+    for (int w = 0; w < kDecodeWaves; ++w) widths |= sm.widths[w];
     // pair tables come with the codebook table (a scalar codebook's (c[lo],
     // c[hi]), or PolarQuant's radius-angle pairs); a quad entry is two pairs
-    const float2* kpt = reinterpret_cast<const float2*>(a.k_table + kPairOffset);
-    const float2* vpt = reinterpret_cast<const float2*>(a.v_table + kPairOffset);
-    for (int i = tid; i < 340; i += blockDim.x) {
-      sm.t.kpair[i] = kpt[i];
-      sm.t.vpair[i] = vpt[i];
-    }
-    for (int i = tid; i < 272; i += blockDim.x) {
-      const int bb = i < 16 ? 1 : 2;
-      const int idx = i - quad_offset(bb), sh = 2 * bb, po = pair_offset(bb);
-      const int p0 = po + (idx & ((1 << sh) - 1)), p1 = po + (idx >> sh);
-      const float2 k0 = kpt[p0], k1 = kpt[p1], v0 = vpt[p0], v1 = vpt[p1];
-      sm.t.kquad[i] = make_float4(k0.x, k0.y, k1.x, k1.y);
-      sm.t.vquad[i] = make_float4(v0.x, v0.y, v1.x, v1.y);
-    }
+    auto stage = [&](int wm, const float* tab, float2* pair, float4* quad, float* cent) {
+      const float2* pt = reinterpret_cast<const float2*>(tab + kPairOffset);
+      for (int bb = 3; bb <= 4; ++bb) {
+        if (!((wm >> bb) & 1)) continue;
+        const int o = pair_offset(bb), n = 1 << (2 * bb);
+        for (int i = tid; i < n; i += blockDim.x) pair[o + i] = pt[o + i];
+      }
+      for (int bb = 1; bb <= 2; ++bb) {
+        if (!((wm >> bb) & 1)) continue;
+        const int sh = 2 * bb, po = pair_offset(bb), n = 1 << (2 * sh);
+        for (int i = tid; i < n; i += blockDim.x) {
+          const float2 c0 = pt[po + (i & ((1 << sh) - 1))], c1 = pt[po + (i >> sh)];
+          quad[quad_offset(bb) + i] = make_float4(c0.x, c0.y, c1.x, c1.y);
+        }
+      }
+      for (int bb = 5; bb <= 8; ++bb) {
+        if (!((wm >> bb) & 1)) continue;
+        const int o = centroid_offset(bb), n = 1 << bb;
+        for (int i = tid; i < n; i += blockDim.x) cent[o + i] = tab[o + i];
+      }
+    };
+    stage(widths & 0x1FF, a.k_table, sm.t.kpair, sm.t.kquad, sm.t.kcent);
+    stage(widths >> 9, a.v_table, sm.t.vpair, sm.t.vquad, sm.t.vcent);
     __syncthreads();
-  }
-  // keep the scheduler from moving table work into the page loop (it otherwise
-  // inflates the loop's register use)
-  __builtin_amdgcn_sched_barrier(0);
+    // keep the scheduler from moving table work into the page loop (it
+    // otherwise inflates the loop's register use)
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  stage_tables();
 
   const float* __restrict__ qrow = wsq + ((size_t)b * a.n_kv_heads + hkv) * kQPrepFloats * G;
 
@@ -800,29 +785,27 @@ void split_kernel(DecodeArgs a,
     __syncthreads();
   }
 
-  // acc: packed pages' value sums on the matrix cores (value_mfma); acc16:
-  // fp16 pages' (lane = (token quarter, 8 coordinates), classes with fp16 pages)
+  // acc: packed pages' value sums on the matrix cores (value_mfma), in the
+  // rotated domain; acco: fp16 pages' (classes with fp16 pages), in the
+  // original domain until the end
   constexpr int NG = G > 4 ? G / 4 : 1;
   constexpr bool kFp16 = CLASS == 2 || CLASS == 4;
-  float m[G], l[G], acc16[kFp16 ? G : 1][8];
-  v4f acc[NG][2];
+  float m[G], l[G];
+  v4f acc[NG][2], acco[kFp16 ? NG : 1][2];
 #pragma clang loop unroll(full)
   for (int h = 0; h < G; ++h) {
     m[h] = -INFINITY;
     l[h] = 0.f;
   }
 #pragma clang loop unroll(full)
-  for (int h = 0; h < (kFp16 ? G : 1); ++h)
-#pragma clang loop unroll(full)
-    for (int e = 0; e < 8; ++e) acc16[h][e] = 0.f;
-#pragma clang loop unroll(full)
   for (int g = 0; g < NG; ++g) acc[g][0] = acc[g][1] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma clang loop unroll(full)
+  for (int g = 0; g < (kFp16 ? NG : 1); ++g) acco[g][0] = acco[g][1] = v4f{0.f, 0.f, 0.f, 0.f};
   float* wv = sm.w[wave];
   if constexpr (G < 4) {
     for (int i = lane; i < 4 * kWRow; i += 64) wv[i] = 0.f;
     wave_lds_sync();
   }
-  const int q4 = lane >> 4, i16 = lane & 15;
 
   // The page loop, compiled for page class PC.  The merged launch runs a
   // common-class and a wide-class copy side by side (a uniform branch), each
@@ -878,9 +861,13 @@ void split_kernel(DecodeArgs a,
             }
         if constexpr (kFp16) {
   #pragma clang loop unroll(full)
-          for (int h = 0; h < G; ++h)
+          for (int g = 0; g < NG; ++g)
   #pragma clang loop unroll(full)
-            for (int e = 0; e < 8; ++e) acc16[h][e] *= alpha[h];
+            for (int i = 0; i < 4; ++i)
+              if (4 * g + i < G) {
+                acco[g][0][i] *= alpha[4 * g + i];
+                acco[g][1][i] *= alpha[4 * g + i];
+              }
         }
       }
   #pragma clang loop unroll(full)
@@ -1003,13 +990,7 @@ void split_kernel(DecodeArgs a,
       }
       weigh(p, s, nv, valid);
       if (PC == 2 && kb == 0) {
-        if constexpr (kFp16) {
-          uint32_t dm[8];
-          const uint32_t dword = a.sign_mask[i16 >> 2];
-  #pragma clang loop unroll(full)
-          for (int e = 0; e < 8; ++e) dm[e] = (dword >> (8 * (i16 & 3) + e)) & 1u;
-          value_accum_fp16<G>(page, lane, wv, dm, acc16);
-        }
+        if constexpr (kFp16) value_mfma_fp16<NG>(page, lane, wv, acco);
       } else if constexpr (PC == 0) {
         switch (vb) {
           case 1: value_mfma<1, NG>(vblk, lane, wv, sm.t.vpair, sm.t.vquad, acc); break;
@@ -1085,6 +1066,8 @@ void split_kernel(DecodeArgs a,
   float fsc[G];
 #pragma clang loop unroll(full)
   for (int h = 0; h < G; ++h) fsc[h] = m[h] == -INFINITY ? 0.f : exp2f(m[h] - M[h]);
+  // the fp16 pages' sums join the rotated-domain sums
+  if constexpr (kFp16) add_rotated<NG>(acco, lane, a.sign_mask, acc);
   // the matrix-core sums: lane L holds coordinates v_stream_coord(L, 0 / 1)
   {
     const int c0 = v_stream_coord(lane, 0), c1 = v_stream_coord(lane, 1);
@@ -1096,21 +1079,6 @@ void split_kernel(DecodeArgs a,
           sm.red[wave][(4 * g + i) * D + c0] = acc[g][0][i] * fsc[4 * g + i];
           sm.red[wave][(4 * g + i) * D + c1] = acc[g][1][i] * fsc[4 * g + i];
         }
-  }
-  if constexpr (kFp16) {
-    // plus the fp16 pages' sums: lanes (quarter, 8 coordinates), reduced over
-    // the quarters
-    wave_lds_sync();
-#pragma clang loop unroll(full)
-    for (int h = 0; h < G; ++h) {
-#pragma clang loop unroll(full)
-      for (int e = 0; e < 8; ++e) {
-        float v = acc16[h][e] * fsc[h];
-        v += __shfl_xor(v, 16, 64);
-        v += __shfl_xor(v, 32, 64);
-        if (q4 == 0) sm.red[wave][h * D + 8 * i16 + e] += v;
-      }
-    }
   }
   __syncthreads();
   for (int idx = tid; idx < G * D; idx += blockDim.x) {
