@@ -407,6 +407,21 @@ int tq_decode_attention_mass(const tq_layer* layer, const tq_cache* cache,
                              const tq_query* query, float* out, float* page_mass,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* tq_decode_attention, also returning the attention weight of every token
+ * ("TurboMOQ", Attention-weighted tier demotion: the policy tracks importance
+ * per position, {position: tier}).  token_mass[b][hq][t] (device float32,
+ * B x H_q x (max_pages x 64), contiguous, 16-byte aligned; every entry is
+ * written) = the softmax weight query head hq gives token t of session b; 0
+ * for t >= n_tokens[b] and for the tokens of pages decode skips (absent,
+ * outside the pool, or of a class page_classes leaves out).  A row sums to 1
+ * up to rounding, and the tokens of a page sum to its tq_decode_attention_mass
+ * entry.  Same workspace and errors as tq_decode_attention, plus
+ * TQ_ERR_INVALID_ARG for a null token_mass and TQ_ERR_ALIGNMENT for one not
+ * 16-byte aligned. */
+int tq_decode_attention_token_mass(const tq_layer* layer, const tq_cache* cache,
+                                   const tq_query* query, float* out, float* token_mass,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* tq_decode_attention without a caller's workspace, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  The query-prep rows and split partials

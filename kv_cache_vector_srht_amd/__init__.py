@@ -35,7 +35,8 @@ EXPORTS = ("tq_page_bytes", "tq_page_descriptor", "tq_build_codebook", "tq_codeb
            "tq_layer_params", "tq_sign_mask", "tq_decode_workspace_bytes", "tq_cache_bytes",
            "tq_status_string", "tq_last_error", "tq_encode_kv", "tq_decode_attention",
            "tq_dequantize", "tq_append_kv", "tq_retier_pages", "tq_decode_attention_mass",
-           "tq_fit_codebook", "tq_calibrated_table", "tq_decode_attention_noalloc")
+           "tq_fit_codebook", "tq_calibrated_table", "tq_decode_attention_noalloc",
+           "tq_decode_attention_token_mass")
 NOALLOC_SCRATCH_BYTES = 32 << 20     # TQ_NOALLOC_SCRATCH_BYTES
 
 
@@ -116,6 +117,9 @@ def lib() -> ctypes.CDLL:
         L.tq_decode_attention_mass.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
                                                ctypes.POINTER(tq_query), ctypes.c_void_p, ctypes.c_void_p,
                                                ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.tq_decode_attention_token_mass.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
+                                                     ctypes.POINTER(tq_query), ctypes.c_void_p, ctypes.c_void_p,
+                                                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.tq_decode_attention_noalloc.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
                                                   ctypes.POINTER(tq_query), ctypes.c_void_p, ctypes.c_void_p]
         L.tq_append_kv.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
@@ -401,10 +405,13 @@ def workspace_bytes(cache: Cache, n_q_heads: int) -> int:
 
 
 def decode_attention(layer: Layer, cache: Cache, q, out=None, workspace=None,
-                     softmax_scale: float = 0.0, page_mass=None, qjl_scoring: int = 0):
+                     softmax_scale: float = 0.0, page_mass=None, qjl_scoring: int = 0,
+                     token_mass=None):
     """tq_decode_attention for q [B, H_q, 128]; returns out [B, H_q, 128] float32.
     With ``page_mass`` (float32 [B, H_q, max_pages]), tq_decode_attention_mass
-    also fills it with each page's attention mass."""
+    also fills it with each page's attention mass; with ``token_mass`` (float32
+    [B, H_q, 64 max_pages]), tq_decode_attention_token_mass fills it with each
+    token's attention weight (one of the two at a time)."""
     import torch
     if q.dim() != 3 or q.shape[0] != cache.n_sessions or q.shape[-1] != HEAD_DIM or q.stride(-1) != 1:
         raise TQError(f"q must be [B, H_q, 128] with unit innermost stride, got {tuple(q.shape)}")
@@ -415,6 +422,18 @@ def decode_attention(layer: Layer, cache: Cache, q, out=None, workspace=None,
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     qs = tq_query(q.data_ptr(), _dtype_code(q), Hq, q.stride(0), q.stride(1), softmax_scale, qjl_scoring)
+    if token_mass is not None:
+        if page_mass is not None:
+            raise TQError("page_mass and token_mass are separate calls")
+        if (token_mass.dtype != torch.float32 or not token_mass.is_contiguous()
+                or tuple(token_mass.shape) != (cache.n_sessions, Hq, cache.max_pages * PAGE_TOKENS)):
+            raise TQError("token_mass must be a contiguous float32 [B, H_q, 64 max_pages] tensor")
+        check(lib().tq_decode_attention_token_mass(ctypes.byref(layer.struct), ctypes.byref(cache.struct),
+                                                   ctypes.byref(qs), out.data_ptr(), token_mass.data_ptr(),
+                                                   workspace.data_ptr(),
+                                                   workspace.numel() * workspace.element_size(),
+                                                   _stream(q.device)), "tq_decode_attention_token_mass")
+        return out
     if page_mass is None:
         check(lib().tq_decode_attention(ctypes.byref(layer.struct), ctypes.byref(cache.struct),
                                         ctypes.byref(qs), out.data_ptr(), workspace.data_ptr(),

@@ -46,6 +46,7 @@ struct DecodeArgs {
   float* wsp;   // [B][H_q][n_splits][kPartialFloats]: m, l, -, -, acc[128]
   float* out;
   float* mass;  // [B][H_q][max_pages] page attention mass, or null
+  float* tmass; // [B][H_q][max_pages * 64] token attention weights, or null (then mass is null)
   // bit u of unit_skip[c]: class c was not launched for unit u = b * H_kv + h
   // (its partials of that class hold nothing; the combine passes over them)
   uint32_t unit_skip[3][TQ_MAX_LISTED_UNITS / 32];
@@ -97,6 +98,11 @@ __global__ __launch_bounds__(128) void qprep_kernel(DecodeArgs a) {
     // pages no split kernel visits keep -inf (mass 0 after the combine)
     float* mrow = a.mass + (size_t)row * a.max_pages;
     for (int p = j; p < a.max_pages; p += 128) mrow[p] = -INFINITY;
+  }
+  if (a.tmass) {
+    // so do the tokens of such pages
+    float4* trow = reinterpret_cast<float4*>(a.tmass + (size_t)row * a.max_pages * PT);
+    for (int i = j; i < a.max_pages * PT / 4; i += 128) trow[i] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
   }
   const uint32_t neg = (a.sign_mask[j >> 5] >> (j & 31)) & 1u;
   qs[j] = qj;
@@ -836,13 +842,24 @@ void split_kernel(DecodeArgs a,
   #pragma clang loop unroll(full)
       for (int h = 0; h < G; ++h)
         if (lane >= valid) s[h] = -INFINITY;
+      // token weights: the scores (log2 units); the combine normalises them
+      if constexpr (MASS) {
+        if (a.tmass) {
+          const size_t ts = (size_t)a.max_pages * PT;
+          float* trow = a.tmass + ((size_t)b * a.n_q_heads + hq0) * ts + (size_t)p * PT + lane;
+  #pragma clang loop unroll(full)
+          for (int h = 0; h < G; ++h) trow[h * ts] = s[h];
+        }
+      }
       softmax_update<G>(s, m, l, alpha);
       if constexpr (MASS) {
-        float* mrow = a.mass + ((size_t)b * a.n_q_heads + hq0) * a.max_pages + p;
+        if (a.mass) {
+          float* mrow = a.mass + ((size_t)b * a.n_q_heads + hq0) * a.max_pages + p;
   #pragma clang loop unroll(full)
-        for (int h = 0; h < G; ++h) {
-          const float ps = wave_sum(s[h]);
-          if (lane == 0) mrow[(size_t)h * a.max_pages] = ps > 0.f ? m[h] + log2f(ps) : -INFINITY;
+          for (int h = 0; h < G; ++h) {
+            const float ps = wave_sum(s[h]);
+            if (lane == 0) mrow[(size_t)h * a.max_pages] = ps > 0.f ? m[h] + log2f(ps) : -INFINITY;
+          }
         }
       }
       // the running sums need rescaling only when some head's maximum moved
@@ -1134,10 +1151,13 @@ __global__ __launch_bounds__(128 * kCombineGroups) void combine_kernel(DecodeArg
 #pragma clang loop unroll(full)
   for (int w = 1; w < kCombineWaves; ++w) M = fmaxf(M, red[w]);
   float* mrow = a.mass ? a.mass + (size_t)row * a.max_pages : nullptr;
+  float* trow = a.tmass ? a.tmass + (size_t)row * a.max_pages * PT : nullptr;
   if (M == -INFINITY || a.n_tokens[b] <= 0) {
     if (tid < D) o[tid] = 0.f;
     if (mrow)
       for (int p = tid; p < a.max_pages; p += nthr) mrow[p] = 0.f;
+    if (trow)
+      for (int t = tid; t < a.max_pages * PT; t += nthr) trow[t] = 0.f;
     return;
   }
   // weights, the denominator and the list of non-empty partials
@@ -1183,6 +1203,18 @@ __global__ __launch_bounds__(128 * kCombineGroups) void combine_kernel(DecodeArg
     for (int p = tid; p < a.max_pages; p += nthr) {
       const float v = mrow[p];
       mrow[p] = v == -INFINITY ? 0.f : exp2f(v - M) * invL;
+    }
+  }
+  if (trow) {
+    const float invL = 1.0f / L;
+    float4* t4 = reinterpret_cast<float4*>(trow);
+    for (int i = tid; i < a.max_pages * PT / 4; i += nthr) {
+      float4 v = t4[i];
+      v.x = v.x == -INFINITY ? 0.f : exp2f(v.x - M) * invL;
+      v.y = v.y == -INFINITY ? 0.f : exp2f(v.y - M) * invL;
+      v.z = v.z == -INFINITY ? 0.f : exp2f(v.z - M) * invL;
+      v.w = v.w == -INFINITY ? 0.f : exp2f(v.w - M) * invL;
+      t4[i] = v;
     }
   }
   // value sums: group g takes list entries g, g + 4, ...; four loads in flight
@@ -1250,7 +1282,7 @@ void launch_split_any(bool mass, int G, dim3 grid, dim3 blk, hipStream_t s, cons
 }
 
 int decode_impl(const tq_layer* layer, const tq_cache* cache, const tq_query* query, float* out,
-                float* page_mass, void* workspace, size_t workspace_bytes, void* stream) {
+                float* page_mass, float* token_mass, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_layer(layer);
   if (st) return st;
   if ((st = check_cache(cache))) return st;
@@ -1267,6 +1299,7 @@ int decode_impl(const tq_layer* layer, const tq_cache* cache, const tq_query* qu
   if (!out || !workspace) return fail(TQ_ERR_INVALID_ARG, "null output or workspace");
   if (!aligned16(out) || !aligned16(workspace)) return fail(TQ_ERR_ALIGNMENT, "out/workspace misaligned");
   if (((uintptr_t)page_mass & 3) != 0) return fail(TQ_ERR_ALIGNMENT, "page_mass misaligned");
+  if (((uintptr_t)token_mass & 15) != 0) return fail(TQ_ERR_ALIGNMENT, "token_mass misaligned");
   if (!(query->softmax_scale >= 0.f) || isinf(query->softmax_scale))
     return fail(TQ_ERR_INVALID_ARG, "bad softmax scale");
   if (query->qjl_scoring != TQ_QJL_SCORE_UNBIASED && query->qjl_scoring != TQ_QJL_SCORE_SIGN)
@@ -1342,7 +1375,8 @@ int decode_impl(const tq_layer* layer, const tq_cache* cache, const tq_query* qu
   a.wsp = a.wsq + (size_t)cache->n_sessions * query->n_q_heads * kQPrepFloats;
   a.out = out;
   a.mass = page_mass;
-  const bool mass = page_mass != nullptr;
+  a.tmass = token_mass;
+  const bool mass = page_mass != nullptr || token_mass != nullptr;
   hipStream_t s = (hipStream_t)stream;
   const int rows = cache->n_sessions * query->n_q_heads;
   hipLaunchKernelGGL(qprep_kernel, dim3(rows), dim3(128), 0, s, a);
@@ -1439,19 +1473,26 @@ int tq_decode_attention_noalloc(const tq_layer* layer, const tq_cache* cache, co
   void* ws = nullptr;
   const int st = scratch_address(&ws);
   if (st) return st;
-  return decode_impl(layer, cache, query, out, nullptr, ws, kScratchBytes, stream);
+  return decode_impl(layer, cache, query, out, nullptr, nullptr, ws, kScratchBytes, stream);
 }
 
 int tq_decode_attention(const tq_layer* layer, const tq_cache* cache, const tq_query* query,
                         float* out, void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_impl(layer, cache, query, out, nullptr, workspace, workspace_bytes, stream);
+  return decode_impl(layer, cache, query, out, nullptr, nullptr, workspace, workspace_bytes, stream);
 }
 
 int tq_decode_attention_mass(const tq_layer* layer, const tq_cache* cache, const tq_query* query,
                              float* out, float* page_mass, void* workspace, size_t workspace_bytes,
                              void* stream) {
   if (!page_mass) return fail(TQ_ERR_INVALID_ARG, "null page_mass");
-  return decode_impl(layer, cache, query, out, page_mass, workspace, workspace_bytes, stream);
+  return decode_impl(layer, cache, query, out, page_mass, nullptr, workspace, workspace_bytes, stream);
+}
+
+int tq_decode_attention_token_mass(const tq_layer* layer, const tq_cache* cache, const tq_query* query,
+                                   float* out, float* token_mass, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  if (!token_mass) return fail(TQ_ERR_INVALID_ARG, "null token_mass");
+  return decode_impl(layer, cache, query, out, nullptr, token_mass, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -983,6 +983,22 @@ def page_attention_mass(q_heads: np.ndarray, Kh: np.ndarray, scale: float | None
     return out
 
 
+def token_attention_weights(q_heads: np.ndarray, Kh: np.ndarray, scale: float | None = None) -> np.ndarray:
+    """[G, T]: for each query head, the softmax weight of every key of Kh, the
+    per-position importance an attention-weighted tier policy reads
+    ("TurboMOQ", Attention-weighted tier demotion: tiers are kept per
+    position).  Computed on its own from the scores (not from
+    page_attention_mass), so that the two can be checked against each other."""
+    Kh = np.asarray(Kh, dtype=np.float64)
+    out = np.zeros((len(q_heads), Kh.shape[0]))
+    for g, q in enumerate(np.asarray(q_heads, dtype=np.float64)):
+        sc = 1.0 / math.sqrt(q.shape[-1]) if scale is None else scale
+        s = np.array([float(np.dot(k, q)) for k in Kh]) * sc
+        e = np.exp(s - s.max())
+        out[g] = e / e.sum()
+    return out
+
+
 # ----------------------------------------------------------------------------
 # Footprint.
 # ----------------------------------------------------------------------------

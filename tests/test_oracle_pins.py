@@ -551,6 +551,34 @@ def test_page_attention_mass_pins():
     assert O.page_attention_mass(qs[:1], K3)[0, 2] > 1 - 1e-12
 
 
+def test_token_attention_weights_pins():
+    rng = np.random.default_rng(5)
+    T = 150
+    K = rng.standard_normal((T, 128)) * 2
+    qs = rng.standard_normal((3, 128))
+    w = O.token_attention_weights(qs, K)
+    assert w.shape == (3, T) and np.all(w >= 0)
+    assert np.allclose(w.sum(axis=1), 1.0, atol=1e-12)
+    # the weights are attention over one-hot values: value t picks token t
+    for g in range(3):
+        assert np.allclose(w[g], O.attention(qs[g], K, np.eye(T)), atol=1e-12)
+    # a page's tokens sum to its page mass
+    pm = O.page_attention_mass(qs, K)
+    for p in range(3):
+        assert np.allclose(w[:, 64 * p:64 * p + 64].sum(axis=1), pm[:, p], atol=1e-12)
+    # closed form: two scores 0 and c
+    q = np.zeros(128)
+    q[0] = 1.0
+    K2 = np.zeros((2, 128))
+    K2[1, 0] = 3.0
+    c = 3.0 / math.sqrt(128)
+    assert np.allclose(O.token_attention_weights(q[None], K2)[0], [1 / (1 + math.exp(c)), 1 / (1 + math.exp(-c))],
+                       atol=1e-12)
+    # a softmax scale multiplies every score
+    assert np.allclose(O.token_attention_weights(q[None], K2, scale=0.5)[0],
+                       [1 / (1 + math.exp(1.5)), 1 / (1 + math.exp(-1.5))], atol=1e-12)
+
+
 def test_requantize_decisions_are_far_from_ties():
     """Every centroid sits at least 1e-4 from every boundary of a narrower or
     equal width, so the map is the same whether it is decided in float32 or
