@@ -402,6 +402,7 @@ def lloyd_max_rayleigh(bits: int) -> Tuple[np.ndarray, np.ndarray]:
             if max(abs(x) for x in step) < mp.mpf(10) ** -34:
                 break
         tm = [(cm[i] + cm[i + 1]) / 2 for i in range(L - 1)]
+        _RAYLEIGH_LEVELS[bits] = list(cm)
         _F32_TABLES[(bits, POLAR)] = (np.array([_round_f32(x) for x in cm], dtype=np.float32),
                                       np.array([_round_f32(x) for x in tm], dtype=np.float32))
         # pair values (r_k cos a_j, r_k sin a_j), a_j the sector middles
@@ -416,12 +417,72 @@ def lloyd_max_rayleigh(bits: int) -> Tuple[np.ndarray, np.ndarray]:
 
 
 _POLAR_PAIRS: Dict[int, np.ndarray] = {}
+_RAYLEIGH_LEVELS: Dict[int, list] = {}   # 40-digit levels of lloyd_max_rayleigh
 
 
 def polar_pairs(bits: int) -> np.ndarray:
     """[L, L, 2] float32: the reconstructed pair of radius code k, angle code j."""
     lloyd_max_rayleigh(bits)
     return _POLAR_PAIRS[bits]
+
+
+class PolarSplit:
+    """PolarQuant with the radius and the angle at widths of their own
+    ("TurboQuant-MLX v2.0", Quick Start: r_bits and theta_bits are separate
+    settings; "turboquant-mlx" README, apply_turboquant_cache: k/v_theta_bits
+    and k/v_radius_bits).  Reading: a part keeps the page width b of the
+    scalar layout (a pair has 2b bits); ``shift`` t moves bits from the
+    radius to the angle, r = b - t and theta = b + t (both 1..8), and the
+    pair's 2b-bit field F = radius code | angle code << r is stored as two
+    b-bit codes, F's low bits at stream position 2i and its high bits at
+    2i + 1.  Shift 0 is POLAR itself.  Pass one wherever a codebook kind goes."""
+
+    def __init__(self, shift: int):
+        self.shift = int(shift)
+
+    def __eq__(self, other):
+        return isinstance(other, PolarSplit) and other.shift == self.shift
+
+    def __hash__(self):
+        return hash(("polar", self.shift))
+
+    def __repr__(self):
+        return f"PolarSplit({self.shift})"
+
+
+def polar_shift(kind):
+    """The angle shift of a PolarQuant kind (0 for POLAR), None for others."""
+    if isinstance(kind, PolarSplit):
+        return kind.shift
+    if isinstance(kind, (int, np.integer)) and not isinstance(kind, bool) and kind == POLAR:
+        return 0
+    return None
+
+
+def polar_widths(bits: int, shift: int) -> Tuple[int, int]:
+    """(radius bits, angle bits) of a page width under an angle shift."""
+    r, a = bits - shift, bits + shift
+    if not (1 <= r <= 8 and 1 <= a <= 8):
+        raise ValueError(f"width {bits} cannot carry an angle shift of {shift}")
+    return r, a
+
+
+def polar_pair_table(bits: int, shift: int = 0) -> np.ndarray:
+    """[2^(2 bits), 2] float32: entry F = rc | tc << r is the pair of radius
+    level rc (Lloyd-Max of Rayleigh(1) at r bits) in the middle direction of
+    angle sector tc of 2^theta, each value the float32 nearest the exact one."""
+    import mpmath as mp
+    r, a = polar_widths(bits, shift)
+    lloyd_max_rayleigh(r)
+    lv = _RAYLEIGH_LEVELS[r]
+    out = np.zeros((1 << (2 * bits), 2), dtype=np.float32)
+    with mp.workdps(40):
+        for tc in range(1 << a):
+            ang = -mp.pi + (2 * tc + 1) * mp.pi / (1 << a)
+            cs, sn = mp.cos(ang), mp.sin(ang)
+            for rc in range(1 << r):
+                out[rc | (tc << r)] = (_round_f32(lv[rc] * cs), _round_f32(lv[rc] * sn))
+    return out
 
 
 def polar_angle_code(theta: np.ndarray, bits: int) -> np.ndarray:
@@ -489,6 +550,8 @@ def codebook(bits: int, kind: int = LLOYD_MAX) -> Tuple[np.ndarray, np.ndarray]:
     """(centroids, boundaries) as float32 arrays, the values both sides compare with."""
     if isinstance(kind, FittedCodebook):
         return kind.tables[bits]
+    if isinstance(kind, PolarSplit):
+        return codebook(polar_widths(bits, kind.shift)[0], POLAR)
     if kind == LLOYD_MAX:
         lloyd_max_gaussian(bits)
     elif kind == UNIFORM:
@@ -543,21 +606,28 @@ def encode(X: np.ndarray, signs, bits: int, kind: int = LLOYD_MAX,
     c32, t32 = codebook(bits, kind)
     t64 = t32.astype(np.float64)
     L = 1 << bits
-    if kind == POLAR:
+    ps = polar_shift(kind)
+    if ps is not None:
         # radius and angle of each coordinate pair; the radius decision in
         # float32 like the scalar codes, the angle sector from float64 (the
-        # device's float32 angle may differ within ANGLE_EPS of a sector edge)
+        # device's float32 angle may differ within ANGLE_EPS of a sector edge).
+        # The radius takes rb bits and the angle ab (rb = ab = bits unless the
+        # kind is a PolarSplit); the pair field rc | tc << rb is stored as two
+        # bits-wide codes, low half at the even position.
+        rb, ab = polar_widths(bits, ps)
+        LA = 1 << ab
         r = np.hypot(U[:, 0::2], U[:, 1::2])
         th = np.arctan2(U[:, 1::2], U[:, 0::2])
         rc = np.searchsorted(t32, r.astype(np.float32), side="right").astype(np.int64)
         near_r = np.minimum(np.abs(r - t64[np.clip(rc - 1, 0, t64.size - 1)]),
                             np.abs(r - t64[np.clip(rc, 0, t64.size - 1)])) < boundary_eps
-        tc = polar_angle_code(th, bits)
-        edge = (th + math.pi) * L / (2 * math.pi)
-        near_t = np.abs(edge - np.rint(edge)) * (2 * math.pi / L) < ANGLE_EPS
+        tc = polar_angle_code(th, ab)
+        edge = (th + math.pi) * LA / (2 * math.pi)
+        near_t = np.abs(edge - np.rint(edge)) * (2 * math.pi / LA) < ANGLE_EPS
+        F = rc | (tc << rb)
         codes = np.empty(U.shape, dtype=np.int64)
         near = np.empty(U.shape, dtype=bool)
-        codes[:, 0::2], codes[:, 1::2] = rc, tc
+        codes[:, 0::2], codes[:, 1::2] = F & (L - 1), F >> bits
         near[:, 0::2], near[:, 1::2] = near_r, near_t
     else:
         U32 = U.astype(np.float32)
@@ -569,13 +639,28 @@ def encode(X: np.ndarray, signs, bits: int, kind: int = LLOYD_MAX,
     if overrides is not None:
         rows, cols, alt = (np.asarray(v, dtype=np.int64) for v in overrides)
         if rows.size:
-            step = np.abs(alt - codes[rows, cols])
-            if kind == POLAR:   # angle codes are cyclic
-                step = np.where(cols % 2 == 1, np.minimum(step, L - step), step)
-            if not np.all(near[rows, cols]) or not np.all(step == 1):
-                raise ValueError("override outside the boundary allowance")
-            codes = codes.copy()
-            codes[rows, cols] = alt
+            if ps is None:
+                step = np.abs(alt - codes[rows, cols])
+                if not np.all(near[rows, cols]) or not np.all(step == 1):
+                    raise ValueError("override outside the boundary allowance")
+                codes = codes.copy()
+                codes[rows, cols] = alt
+            else:
+                # a pair may move one radius level (near a radius boundary)
+                # and one angle sector, cyclically (near a sector edge)
+                new = codes.copy()
+                new[rows, cols] = alt
+                pr, pc = np.unique(np.stack([rows, cols // 2]), axis=1)
+                F0 = codes[pr, 2 * pc] | (codes[pr, 2 * pc + 1] << bits)
+                F1 = new[pr, 2 * pc] | (new[pr, 2 * pc + 1] << bits)
+                m = (1 << rb) - 1
+                dr = np.abs((F1 & m) - (F0 & m))
+                dt = np.abs((F1 >> rb) - (F0 >> rb))
+                dt = np.minimum(dt, LA - dt)
+                ok = ((dr == 0) | ((dr == 1) & near[pr, 2 * pc])) & ((dt == 0) | ((dt == 1) & near[pr, 2 * pc + 1]))
+                if not np.all(ok) or not np.all((F1 >> rb) < LA):
+                    raise ValueError("override outside the boundary allowance")
+                codes = new
     return {"norm": n.astype(np.float32), "u": U, "codes": codes, "near": near}
 
 
@@ -589,11 +674,13 @@ def dequantize(norm32: np.ndarray, codes: np.ndarray, signs, bits: int,
     R = rotation_matrix(signs)
     d = R.shape[0]
     codes = np.asarray(codes, dtype=np.int64)
-    if kind == POLAR:
-        P = polar_pairs(bits).astype(np.float64)
+    ps = polar_shift(kind)
+    if ps is not None:
+        P = polar_pair_table(bits, ps).astype(np.float64)
+        F = codes[:, 0::2] | (codes[:, 1::2] << bits)
         C = np.empty(codes.shape)
-        C[:, 0::2] = P[codes[:, 0::2], codes[:, 1::2], 0]
-        C[:, 1::2] = P[codes[:, 0::2], codes[:, 1::2], 1]
+        C[:, 0::2] = P[F, 0]
+        C[:, 1::2] = P[F, 1]
     else:
         C = c32.astype(np.float64)[codes]
     return (np.asarray(norm32, dtype=np.float64)[:, None] / math.sqrt(d)) * (C @ R)
@@ -808,7 +895,7 @@ def decode_page(raw: bytes, fmt, signs, S=None, k_kind: int = LLOYD_MAX,
 # ----------------------------------------------------------------------------
 def requantize_codes(codes: np.ndarray, bits: int, new_bits: int, kind: int = LLOYD_MAX) -> np.ndarray:
     """Codes of width `bits` mapped to width `new_bits` through their centroids."""
-    if kind == POLAR:
+    if polar_shift(kind) is not None:
         raise ValueError("polar pages are not re-coded by a scalar map")
     c_old, _ = codebook(bits, kind)
     _, t_new = codebook(new_bits, kind)

@@ -849,3 +849,88 @@ def test_polar_distortion_matches_closed_form():
         uh = math.sqrt(128) * (xh @ R.T) / enc["norm"][:, None].astype(np.float64)
         mse_pair = np.mean(np.sum((enc["u"] - uh) ** 2, axis=1)) / 64
         assert abs(mse_pair / D - 1) < 0.03, (bits, mse_pair, D)
+
+
+def test_polar_split_shift0_is_polar():
+    rng = np.random.default_rng(31)
+    signs = W.rotation_signs(42, 1)
+    X = rng.standard_normal((40, 128))
+    for bits in (1, 2, 3, 4):
+        a = O.encode(X, signs, bits, O.POLAR)
+        b = O.encode(X, signs, bits, O.PolarSplit(0))
+        assert np.array_equal(a["codes"], b["codes"]) and np.array_equal(a["near"], b["near"])
+        assert np.array_equal(O.dequantize(a["norm"], a["codes"], signs, bits, O.POLAR),
+                              O.dequantize(b["norm"], b["codes"], signs, bits, O.PolarSplit(0)))
+        P, T = O.polar_pairs(bits), O.polar_pair_table(bits, 0)
+        L = 1 << bits
+        for rc in range(L):
+            for tc in range(L):
+                assert np.array_equal(P[rc, tc], T[rc | (tc << bits)])
+
+
+def test_polar_split_packing_hand_example():
+    """Width 3 with shift 2: a 1-bit radius and a 5-bit angle.  Pairs at radius
+    sqrt(2) and angles 0.1 and -2.0: sectors of 2 pi / 32 from -pi give
+    floor((0.1 + pi) 32 / (2 pi)) = 16 and floor((-2.0 + pi) 32 / (2 pi)) = 5;
+    the field F = rc | tc << 1 is stored as F & 7 (even position) and F >> 3."""
+    signs = W.rotation_signs(42, 2)
+    th = np.array([0.1, -2.0] + [0.5] * 62)
+    U = np.zeros((1, 128))
+    U[0, 0::2], U[0, 1::2] = math.sqrt(2) * np.cos(th), math.sqrt(2) * np.sin(th)
+    e = O.encode(_vectors_with_rotated(U, signs), signs, 3, O.PolarSplit(2))
+    _, t1 = O.codebook(1, O.POLAR)
+    rc = int(math.sqrt(2) >= float(t1[0]))
+    for i, tc in ((0, 16), (1, 5)):
+        F = rc | (tc << 1)
+        assert e["codes"][0, 2 * i] == F & 7 and e["codes"][0, 2 * i + 1] == F >> 3
+    assert np.all(e["codes"] < 8)
+    # the reconstruction is radius level rc in the middle of the sector
+    xh = O.dequantize(e["norm"], e["codes"], signs, 3, O.PolarSplit(2))
+    uh = math.sqrt(128) * (xh @ O.rotation_matrix(signs).T) / float(e["norm"][0])
+    c1, _ = O.codebook(1, O.POLAR)
+    for i, tc in ((0, 16), (1, 5)):
+        mid = -math.pi + (2 * tc + 1) * math.pi / 32
+        assert np.allclose(uh[0, 2 * i:2 * i + 2], [c1[rc] * math.cos(mid), c1[rc] * math.sin(mid)], atol=1e-6)
+
+
+def test_polar_split_overrides_move_one_level_or_sector():
+    signs = W.rotation_signs(42, 2)
+    L = 32                                  # width 3, shift 2: 5 angle bits
+    th = np.array([-math.pi + 2 * math.pi * 7 / L + 1e-7, 0.3] + [0.7] * 62)
+    U = np.zeros((1, 128))
+    U[0, 0::2], U[0, 1::2] = math.sqrt(2) * np.cos(th), math.sqrt(2) * np.sin(th)
+    X = _vectors_with_rotated(U, signs)
+    kind = O.PolarSplit(2)
+    e = O.encode(X, signs, 3, kind)
+    assert e["near"][0, 1] and not e["near"][0, 3]
+    F = e["codes"][0, 0] | (e["codes"][0, 1] << 3)
+    assert F >> 1 == 7
+    G = (F & 1) | (6 << 1)                  # one sector down: admissible at the flagged edge
+    O.encode(X, signs, 3, kind, overrides=([0, 0], [0, 1], [G & 7, G >> 3]))
+    H = (F & 1) | (5 << 1)                  # two sectors: not
+    with pytest.raises(ValueError):
+        O.encode(X, signs, 3, kind, overrides=([0, 0], [0, 1], [H & 7, H >> 3]))
+    with pytest.raises(ValueError):
+        O.polar_widths(2, 2)                # no radius bit left
+
+
+def test_polar_split_distortion_matches_closed_form():
+    """The closed form of the polar distortion above, with the radius levels of
+    r = b - t bits and 2^(b + t) angle sectors, for shifts of either sign."""
+    rng = np.random.default_rng(27)
+    signs = W.rotation_signs(42, 0)
+    R = O.rotation_matrix(signs)
+    X = rng.standard_normal((3000, 128))
+    for bits, shift in ((2, 1), (3, 1), (3, -1), (4, 2), (4, -2)):
+        rb, ab = O.polar_widths(bits, shift)
+        c, t = O.codebook(rb, O.POLAR)
+        e = np.concatenate(([0.0], t.astype(np.float64), [np.inf]))
+        Pk = np.exp(-0.5 * e[:-1] ** 2) - np.exp(-0.5 * np.where(np.isinf(e[1:]), np.inf, e[1:]) ** 2)
+        x = math.pi / (1 << ab)
+        D = 2 + (1 - 2 * math.sin(x) / x) * np.sum(Pk * c.astype(np.float64) ** 2)
+        kind = O.PolarSplit(shift)
+        enc = O.encode(X, signs, bits, kind)
+        xh = O.dequantize(enc["norm"], enc["codes"], signs, bits, kind)
+        uh = math.sqrt(128) * (xh @ R.T) / enc["norm"][:, None].astype(np.float64)
+        mse_pair = np.mean(np.sum((enc["u"] - uh) ** 2, axis=1)) / 64
+        assert abs(mse_pair / D - 1) < 0.03, (bits, shift, mse_pair, D)
