@@ -274,6 +274,22 @@ int tq_build_codebook(int bits, int kind, float* centroids, float* boundaries);
  * tq_layer). */
 int tq_codebook_table(int kind, float* table);
 
+/* The table of a PolarQuant part whose radius and angle take widths of their
+ * own ("TurboQuant-MLX v2.0", Quick Start: r_bits and theta_bits are separate;
+ * "turboquant-mlx" README, apply_turboquant_cache: k/v_theta_bits,
+ * k/v_radius_bits).  A page of width b keeps the scalar layout and size (2b
+ * bits per coordinate pair); angle_shift t (-3..3) gives the radius r = b - t
+ * bits (the Lloyd-Max levels of Rayleigh(1) at r bits) and the angle a = b + t
+ * bits (2^a sectors), and the pair field F = radius code | angle code << r is
+ * stored as two b-bit codes, F's low b bits at stream position 2i and its high
+ * b bits at 2i + 1.  The pair table of width b is indexed by F; the shift is
+ * kept in the table's last entry, where the encoders read it.  Use with
+ * k_codebook / v_codebook = TQ_CODEBOOK_POLAR; tq_codebook_table(POLAR) is
+ * shift 0.  Pages wider than 4 bits, or whose width cannot carry the shift
+ * (r or a below 1), are refused by the encoders (error flag 4) and must not be
+ * decoded.  TQ_ERR_UNSUPPORTED for a shift outside -3..3. */
+int tq_polar_table(int angle_shift, float* table);
+
 /* Codebook fitted to sample head vectors ("TurboMOQ", Quick Start: calibrate
  * codebooks from sample data; Architecture: Lloyd-Max codebook (k-means);
  * Limitations: Lloyd-Max codebooks need sample data).  The samples are the

@@ -36,7 +36,7 @@ EXPORTS = ("tq_page_bytes", "tq_page_descriptor", "tq_build_codebook", "tq_codeb
            "tq_status_string", "tq_last_error", "tq_encode_kv", "tq_decode_attention",
            "tq_dequantize", "tq_append_kv", "tq_retier_pages", "tq_decode_attention_mass",
            "tq_fit_codebook", "tq_calibrated_table", "tq_decode_attention_noalloc",
-           "tq_decode_attention_token_mass")
+           "tq_decode_attention_token_mass", "tq_polar_table")
 NOALLOC_SCRATCH_BYTES = 32 << 20     # TQ_NOALLOC_SCRATCH_BYTES
 
 
@@ -96,6 +96,7 @@ def lib() -> ctypes.CDLL:
         L.tq_page_descriptor.argtypes = [ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
         L.tq_build_codebook.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
         L.tq_codebook_table.argtypes = [ctypes.c_int, ctypes.c_void_p]
+        L.tq_polar_table.argtypes = [ctypes.c_int, ctypes.c_void_p]
         L.tq_fit_codebook.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
                                       ctypes.c_void_p, ctypes.c_void_p]
         L.tq_calibrated_table.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
@@ -156,6 +157,16 @@ def codebook_table(kind: int = LLOYD_MAX):
     import numpy as np
     tab = np.zeros(CODEBOOK_TABLE_FLOATS, np.float32)
     check(lib().tq_codebook_table(kind, tab.ctypes.data), "tq_codebook_table")
+    return tab
+
+
+def polar_table(angle_shift: int = 0):
+    """tq_polar_table: the table of a PolarQuant part whose page width b gives
+    b - angle_shift radius bits and b + angle_shift angle bits (use with kind
+    POLAR as Layer's k_table / v_table)."""
+    import numpy as np
+    tab = np.zeros(CODEBOOK_TABLE_FLOATS, np.float32)
+    check(lib().tq_polar_table(int(angle_shift), tab.ctypes.data), "tq_polar_table")
     return tab
 
 
@@ -252,15 +263,17 @@ class Layer:
 
     def __init__(self, signs, device, qjl_s=None, k_codebook: int = LLOYD_MAX,
                  v_codebook: int = LLOYD_MAX, k_table=None, v_table=None):
-        """k_table / v_table: a table from calibrated_table (kind FITTED) in
-        place of the built-in codebook of that kind."""
+        """k_table / v_table: a table from calibrated_table (kind FITTED) or
+        from polar_table (kind POLAR) in place of the built-in codebook of
+        that kind."""
         import numpy as np
         import torch
         self.device = torch.device(device)
         self.signs = np.asarray(signs, dtype=np.int8)
         self.mask = torch.from_numpy(sign_mask(self.signs).view(np.int32).copy()).to(self.device)
-        if (k_table is None) == (k_codebook == FITTED) or (v_table is None) == (v_codebook == FITTED):
-            raise TQError("a FITTED codebook comes with its table, and only a FITTED one does")
+        for kind, tab in ((k_codebook, k_table), (v_codebook, v_table)):
+            if (kind == FITTED and tab is None) or (tab is not None and kind not in (FITTED, POLAR)):
+                raise TQError("a FITTED codebook comes with its table; only FITTED and POLAR take one")
         kt = codebook_table(k_codebook) if k_table is None else np.asarray(k_table, dtype=np.float32)
         vt = codebook_table(v_codebook) if v_table is None else np.asarray(v_table, dtype=np.float32)
         self.k_table = torch.from_numpy(np.ascontiguousarray(kt)).to(self.device)

@@ -92,19 +92,12 @@ __global__ __launch_bounds__(64 * kQjlWaves) void qjl_keys_kernel(EncodeArgs a, 
     const int t_first = pg * PT;
     if (max(t_first, a.tok0) != t_first || min(t_first + PT, a.tok0 + a.ntok) != t_first + PT) continue;
     const bool polar = a.k_polar;
-    if (polar && kb > 4) continue;               // refused (and flagged) by encode_pages_kernel
+    const int shift = polar ? polar_shift_of(a.k_table) : 0;
+    if (polar && !polar_width_ok(kb, shift)) continue;   // refused (and flagged) by encode_pages_kernel
     char* page = a.pool + pd.off;
     // this wave's quantiser tables for the key width
     wave_lds_sync();
-    const int L = 1 << kb;
-    for (int i = lane; i < L; i += 64) {
-      lds_cent[wave][i] = a.k_table[centroid_offset(kb) + i];
-      if (i < L - 1) lds_thr[wave][i] = a.k_table[boundary_offset(kb) + i];
-    }
-    if (polar) {
-      const float2* pt = reinterpret_cast<const float2*>(a.k_table + kPairOffset) + pair_offset_host(kb);
-      for (int i = lane; i < L * L; i += 64) lds_pair[wave][i] = pt[i];
-    }
+    stage_token_tables(a.k_table, kb, polar, shift, lane, 64, lds_thr[wave], lds_cent[wave], lds_pair[wave]);
     float x[D];
     const size_t base = (size_t)b * a.sb + (size_t)h * a.sh;
     load_row(a.k, a.dtype, base + (size_t)(t_first + lane - a.tok0) * a.st, x);
@@ -114,10 +107,10 @@ __global__ __launch_bounds__(64 * kQjlWaves) void qjl_keys_kernel(EncodeArgs a, 
     float* cent = lds_cent[wave];
     float2* pair = lds_pair[wave];
     switch (kb) {
-      case 1: n = encode_packed<0, 1>(page, lane, x, m, thr, cent, nullptr, polar, pair); break;
-      case 2: n = encode_packed<0, 2>(page, lane, x, m, thr, cent, nullptr, polar, pair); break;
-      case 3: n = encode_packed<0, 3>(page, lane, x, m, thr, cent, nullptr, polar, pair); break;
-      case 4: n = encode_packed<0, 4>(page, lane, x, m, thr, cent, nullptr, polar, pair); break;
+      case 1: n = encode_packed<0, 1>(page, lane, x, m, thr, cent, nullptr, polar, pair, shift); break;
+      case 2: n = encode_packed<0, 2>(page, lane, x, m, thr, cent, nullptr, polar, pair, shift); break;
+      case 3: n = encode_packed<0, 3>(page, lane, x, m, thr, cent, nullptr, polar, pair, shift); break;
+      case 4: n = encode_packed<0, 4>(page, lane, x, m, thr, cent, nullptr, polar, pair, shift); break;
       case 5: n = encode_packed<0, 5>(page, lane, x, m, thr, cent, nullptr); break;
       case 6: n = encode_packed<0, 6>(page, lane, x, m, thr, cent, nullptr); break;
       case 7: n = encode_packed<0, 7>(page, lane, x, m, thr, cent, nullptr); break;
@@ -243,7 +236,7 @@ struct EncodeLane {
 template <int DT, bool POLAR = false>
 __device__ __forceinline__ float encode_quarter(const void* src, size_t row_off, int e,
                                                 const EncodeLane& el, int B, const Lut& lut,
-                                                const uint2* ent, uint32_t* mat_row) {
+                                                const uint2* ent, uint32_t* mat_row, int shift = 0) {
   float x[32];
   float ss = 0.f;
   if constexpr (DT == TQ_DTYPE_F16) {
@@ -315,15 +308,17 @@ __device__ __forceinline__ float encode_quarter(const void* src, size_t row_off,
   if constexpr (POLAR) {
     // PolarQuant: slots 2m, 2m+1 are a coordinate pair.  Undo the outer D and
     // the lane's sign to get u, then the radius code from the lookup grid
-    // (built on the radius boundaries) and the angle sector
-    // floor((theta + pi) L / (2 pi)) mod L without an arctangent: the signs
-    // give the quadrant (sectors of L/4 each from -pi), and inside it the
-    // angle psi from the quadrant's start has tan psi = a / b with (a, b) =
-    // (|u1|, |u0|) in quadrants 0 and 2, (|u0|, |u1|) in 1 and 3, so the
-    // sector's offset counts the edges 2 pi j / L with a >= tan(2 pi j / L) b.
-    // The codes are final: no flip below.
+    // (built on the radius boundaries of B - shift bits) and the angle sector
+    // floor((theta + pi) L / (2 pi)) mod L, L = 2^(B + shift), without an
+    // arctangent up to 16 sectors: the signs give the quadrant (sectors of
+    // L/4 each from -pi), and inside it the angle psi from the quadrant's
+    // start has tan psi = a / b with (a, b) = (|u1|, |u0|) in quadrants 0 and
+    // 2, (|u0|, |u1|) in 1 and 3, so the sector's offset counts the edges
+    // 2 pi j / L with a >= tan(2 pi j / L) b (finer grids take psi from an
+    // arctangent).  The pair field F = radius | angle << (B - shift) goes to
+    // the two slots, low B bits first.  The codes are final: no flip below.
     const uint32_t lsign = (e == 1 || e == 2) ? 1u : 0u;
-    const int L = 1 << B;
+    const int L = 1 << (B + shift), RB = B - shift;
 #pragma clang loop unroll(full)
     for (int m = 0; m < 16; ++m) {
       const int s0 = 2 * m, s1 = 2 * m + 1;
@@ -352,14 +347,17 @@ __device__ __forceinline__ float encode_quarter(const void* src, size_t row_off,
           sub = (pa >= 0.41421356237309503f * pb ? 1u : 0u) +        // tan(pi/8)
                 (pa >= pb ? 1u : 0u) +                                // tan(pi/4)
                 (pa >= 2.41421356237309503f * pb ? 1u : 0u);          // tan(3 pi/8)
+        } else if (L > 16) {
+          sub = min((uint32_t)(atan2f(pa, pb) * ((float)L / 6.28318530717958648f)), (uint32_t)(L / 4 - 1));
         }
         // a zero pair takes the angle atan2(+0, +0) = 0 (quadrant 2, no edge
         // passed), whatever the signs of its zeros; pa = 0 < pb gives 0 anyway
         if (pa == 0.f) sub = 0;
         tc = qd * (uint32_t)(L >> 2) + sub;
       }
-      cb[s0 >> 2] |= rc << (8 * (s0 & 3));
-      cb[s1 >> 2] |= tc << (8 * (s1 & 3));
+      const uint32_t F = rc | (tc << RB);
+      cb[s0 >> 2] |= (F & ((1u << B) - 1u)) << (8 * (s0 & 3));
+      cb[s1 >> 2] |= (F >> B) << (8 * (s1 & 3));
     }
 #pragma clang loop unroll(full)
     for (int c = 0; c < 4; ++c)
@@ -480,6 +478,10 @@ __global__ __launch_bounds__(kEncodeBlock) void encode_pages_kernel(EncodeArgs a
   }
   int cur_kb = -1, cur_vb = -1;
   Lut lk{0.f, 0.f, 1, 0.f}, lv{0.f, 0.f, 1, 0.f};
+  // PolarQuant parts: the angle shift (radius width = page width - shift)
+  const int tk = POLAR && a.k_polar ? polar_shift_of(a.k_table) : 0;
+  const int tv = POLAR && a.v_polar ? polar_shift_of(a.v_table) : 0;
+
   const size_t base = (size_t)b * a.sb + (size_t)h * a.sh;
   const uint64_t* prow = pages + ((size_t)b * a.n_kv_heads + h) * a.max_pages;
 
@@ -531,8 +533,12 @@ __global__ __launch_bounds__(kEncodeBlock) void encode_pages_kernel(EncodeArgs a
     // stage the lookup grids when the widths change (uniform branch)
     if (kb != cur_kb || vb != cur_vb) {
       __syncthreads();
-      const float* hk = a.k_table + kLutHeaderOffset + 4 * (kb - 1);
-      const float* hv = a.v_table + kLutHeaderOffset + 4 * (vb - 1);
+      // a polar part quantises the radius at its own width (clamped into the
+      // table for widths it refuses below)
+      const int rk = POLAR && a.k_polar ? min(8, max(1, kb - tk)) : kb;
+      const int rv = POLAR && a.v_polar ? min(8, max(1, vb - tv)) : vb;
+      const float* hk = a.k_table + kLutHeaderOffset + 4 * (rk - 1);
+      const float* hv = a.v_table + kLutHeaderOffset + 4 * (rv - 1);
       const int nbk = min((int)__float_as_uint(hk[2]), kLutMaxBins);
       const int nbv = min((int)__float_as_uint(hv[2]), kLutMaxBins);
       lk = Lut{hk[0], hk[1], nbk, (float)(nbk - 1)};
@@ -549,17 +555,19 @@ __global__ __launch_bounds__(kEncodeBlock) void encode_pages_kernel(EncodeArgs a
     uint32_t* rowk = matk + t * (kRowStride / 4);
     uint32_t* rowv = matv + t * (kRowStride / 4);
     // QJL key pages are written by the per-token kernel (codes + sketch), as
-    // are PolarQuant parts wider than 4 bits (which it refuses)
+    // are PolarQuant parts it refuses
     const bool kp = POLAR && a.k_polar, vp = POLAR && a.v_polar;
-    const bool skip_k = qjl || (kp && kb > 4), skip_v = vp && vb > 4;
-    // a PolarQuant part wider than 4 bits has no pair table: refused, untouched
-    if (tid == 0 && ((kp && kb > 4) || (vp && vb > 4))) raise_flag(a.err, 4);
+    const bool k_bad = kp && !polar_width_ok(kb, tk), v_bad = vp && !polar_width_ok(vb, tv);
+    const bool skip_k = qjl || k_bad, skip_v = v_bad;
+    // a PolarQuant part wider than 4 bits has no pair table, and one whose
+    // width cannot carry the angle shift has no split: refused, untouched
+    if (tid == 0 && (k_bad || v_bad)) raise_flag(a.err, 4);
     float nk = 0.f, nv = 0.f;
     if (!skip_k)
-      nk = kp ? encode_quarter<DT, POLAR>(a.k, row_off, e, el, kb, lk, entk, rowk)
+      nk = kp ? encode_quarter<DT, POLAR>(a.k, row_off, e, el, kb, lk, entk, rowk, tk)
               : encode_quarter<DT>(a.k, row_off, e, el, kb, lk, entk, rowk);
     if (!skip_v)
-      nv = vp ? encode_quarter<DT, POLAR>(a.v, row_off, e, el, vb, lv, entv, rowv)
+      nv = vp ? encode_quarter<DT, POLAR>(a.v, row_off, e, el, vb, lv, entv, rowv, tv)
               : encode_quarter<DT>(a.v, row_off, e, el, vb, lv, entv, rowv);
     if (e == 0) {
       normk[t] = nk;

@@ -311,20 +311,24 @@ static void build_scalar_pairs(float* table) {
   }
 }
 
-// PolarQuant's pair: radius level lo (the table's centroids) in the direction
-// of angle sector hi's middle, -pi + (2 hi + 1) pi / L.  The levels are solved
-// again in long double for the products.
-static void build_polar_pairs(float* table) {
+// PolarQuant's pair at width b with angle shift t: the pair field
+// F = rc | tc << r (r = b - t radius bits, a = b + t angle bits) holds radius
+// level rc (Lloyd-Max of Rayleigh(1) at r bits) in the direction of angle
+// sector tc's middle, -pi + (2 tc + 1) pi / 2^a.  The levels are solved again
+// in long double for the products.  A width that cannot carry the shift (r or
+// a outside 1..8) keeps a zero table; the encoders refuse its pages.
+static void build_polar_pairs(float* table, int shift) {
   const ld pi = 3.14159265358979323846264338327950288L;
   for (int b = 1; b <= 4; ++b) {
-    const int L = 1 << b;
+    const int rb = b - shift, ab = b + shift;
+    if (rb < 1 || rb > 8 || ab < 1 || ab > 8) continue;
     std::vector<ld> r;
-    lloyd_max(b + 1, RayleighModel(), r);
+    lloyd_max(rb + 1, RayleighModel(), r);
     float* p = table + kPairOffset + 2 * pair_offset_host(b);
-    for (int i = 0; i < L * L; ++i) {
-      const ld a = -pi + (ld)(2 * (i >> b) + 1) * pi / (ld)L;
-      p[2 * i] = (float)(r[i & (L - 1)] * cosl(a));
-      p[2 * i + 1] = (float)(r[i & (L - 1)] * sinl(a));
+    for (int i = 0; i < (1 << (2 * b)); ++i) {
+      const ld a = -pi + (ld)(2 * (i >> rb) + 1) * pi / (ld)(1 << ab);
+      p[2 * i] = (float)(r[i & ((1 << rb) - 1)] * cosl(a));
+      p[2 * i + 1] = (float)(r[i & ((1 << rb) - 1)] * sinl(a));
     }
   }
 }
@@ -462,14 +466,24 @@ int tq_codebook_table(int kind, float* table) {
     int st = tq_build_codebook(b, kind, table + centroid_offset(b), table + boundary_offset(b));
     if (st != TQ_OK) return st;
   }
-  if (kind == TQ_CODEBOOK_POLAR) {
-    // polar parts are at most 4 bits wide; their radius grids serve nothing
-    // wider
-    build_polar_pairs(table);
-    return build_grids(table, 4);
-  }
+  if (kind == TQ_CODEBOOK_POLAR) return tq_polar_table(0, table);
   build_scalar_pairs(table);
   return build_grids(table);
+}
+
+int tq_polar_table(int angle_shift, float* table) {
+  if (!table) return fail(TQ_ERR_INVALID_ARG, "null table");
+  if (angle_shift < -3 || angle_shift > 3)
+    return fail(TQ_ERR_UNSUPPORTED, "angle shift %d outside -3..3", angle_shift);
+  memset(table, 0, sizeof(float) * TQ_CODEBOOK_TABLE_FLOATS);
+  for (int b = 1; b <= 8; ++b) {
+    int st = tq_build_codebook(b, TQ_CODEBOOK_POLAR, table + centroid_offset(b), table + boundary_offset(b));
+    if (st != TQ_OK) return st;
+  }
+  // pages are at most 4 bits wide; their radius grids go up to 4 - shift bits
+  build_polar_pairs(table, angle_shift);
+  table[kPolarShiftSlot] = (float)angle_shift;
+  return build_grids(table, std::min(8, 4 - std::min(angle_shift, 0)));
 }
 
 int tq_fit_codebook(const float* vectors, size_t n, const int8_t* signs, int bits, float* centroids,

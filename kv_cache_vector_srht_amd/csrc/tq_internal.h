@@ -25,6 +25,9 @@ constexpr int kPairOffset = 1056;
 constexpr int pair_offset_host(int b) { return b == 1 ? 0 : b == 2 ? 4 : b == 3 ? 20 : 84; }
 constexpr int kLutEntriesOffset = kPairOffset + 2 * 340;
 constexpr int kLutMaxBins = 1400;
+// PolarQuant tables: the angle shift t (radius b - t bits, angle b + t bits at
+// page width b) as a float in the table's last entry (0 for an even split).
+constexpr int kPolarShiftSlot = TQ_CODEBOOK_TABLE_FLOATS - 1;
 constexpr int kLutByteBins = 256;   // grids this small are indexed by a saturating byte conversion
 
 // Decode split-K geometry.

@@ -65,8 +65,10 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
     if (lane == 0) raise_flag(a.err, 32);
     return;
   }
+  const int tk = a.k_polar ? polar_shift_of(a.k_table) : 0, tv = a.v_polar ? polar_shift_of(a.v_table) : 0;
   const bool bad_target = pending && (kb < 1 || kb > 8 || vb < 1 || vb > 8 || (qjl && !a.qjl_s) ||
-                                      (a.k_polar && kb > 4) || (a.v_polar && vb > 4));
+                                      (a.k_polar && !polar_width_ok(kb, tk)) ||
+                                      (a.v_polar && !polar_width_ok(vb, tv)));
   if (bad_target || off + page_size_dev(0, 0, false) > a.pool_bytes) {
     if (lane == 0) raise_flag(a.err, 4);
     return;
@@ -99,16 +101,9 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
   for (int part = 0; part < 2; ++part) {
     const int B = part == 0 ? kb : vb;
     const float* table = part == 0 ? a.k_table : a.v_table;
-    const int L = 1 << B;
-    for (int i = lane; i < L; i += 64) {
-      lds_cent[i] = table[centroid_offset(B) + i];
-      if (i < L - 1) lds_thr[i] = table[boundary_offset(B) + i];
-    }
     const bool polar = part == 0 ? a.k_polar : a.v_polar;
-    if (polar) {
-      const float2* pt = reinterpret_cast<const float2*>(table + kPairOffset) + pair_offset_host(B);
-      for (int i = lane; i < L * L; i += 64) lds_pair[i] = pt[i];
-    }
+    const int shift = part == 0 ? tk : tv;
+    stage_token_tables(table, B, polar, shift, lane, 64, lds_thr, lds_cent, lds_pair);
     float x[D];
     load_row(page + part * PT * D * 2, TQ_DTYPE_F16, (size_t)lane * D, x);
     __syncthreads();
@@ -116,26 +111,26 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
     float n = 0.f;
     if (part == 0) {
       switch (B) {
-        case 1: n = encode_packed<0, 1>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        case 2: n = encode_packed<0, 2>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        case 3: n = encode_packed<0, 3>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        case 4: n = encode_packed<0, 4>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        case 5: n = encode_packed<0, 5>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        case 6: n = encode_packed<0, 6>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        case 7: n = encode_packed<0, 7>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        default: n = encode_packed<0, 8>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        case 1: n = encode_packed<0, 1>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
+        case 2: n = encode_packed<0, 2>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
+        case 3: n = encode_packed<0, 3>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
+        case 4: n = encode_packed<0, 4>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
+        case 5: n = encode_packed<0, 5>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
+        case 6: n = encode_packed<0, 6>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
+        case 7: n = encode_packed<0, 7>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
+        default: n = encode_packed<0, 8>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
       }
       if (qjl) qjl_sketch(a.qjl_s, part_base + 1024 * B + 256, lane, x, m, n);
     } else {
       switch (B) {
-        case 1: n = encode_packed<1, 1>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        case 2: n = encode_packed<1, 2>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        case 3: n = encode_packed<1, 3>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        case 4: n = encode_packed<1, 4>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        case 5: n = encode_packed<1, 5>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        case 6: n = encode_packed<1, 6>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        case 7: n = encode_packed<1, 7>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-        default: n = encode_packed<1, 8>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+        case 1: n = encode_packed<1, 1>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
+        case 2: n = encode_packed<1, 2>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
+        case 3: n = encode_packed<1, 3>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
+        case 4: n = encode_packed<1, 4>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
+        case 5: n = encode_packed<1, 5>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
+        case 6: n = encode_packed<1, 6>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
+        case 7: n = encode_packed<1, 7>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
+        default: n = encode_packed<1, 8>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
       }
     }
     __syncthreads();
@@ -293,7 +288,9 @@ __device__ __forceinline__ int retier_check(const RetierArgs& a, int64_t idx, ui
   // PolarQuant: no code-to-code map (pairs of codes); fp16 sources encode at
   // most 4 bits wide
   if (kb != 0 && (a.k_polar || a.v_polar)) return 64;
-  if ((a.k_polar && nkb > 4) || (a.v_polar && nvb > 4)) return 4;
+  if ((a.k_polar && !polar_width_ok(nkb, polar_shift_of(a.k_table))) ||
+      (a.v_polar && !polar_width_ok(nvb, polar_shift_of(a.v_table))))
+    return 4;
   if (nq && !a.qjl_s) return 8;
   return 0;
 }
@@ -340,16 +337,9 @@ __global__ __launch_bounds__(64) void retier_kernel(RetierArgs a) {
       for (int part = 0; part < 2; ++part) {
         const int B = part == 0 ? nkb : nvb;
         const float* table = part == 0 ? a.k_table : a.v_table;
-        const int L = 1 << B;
-        for (int i = lane; i < L; i += 64) {
-          lds_cent[i] = table[centroid_offset(B) + i];
-          if (i < L - 1) lds_thr[i] = table[boundary_offset(B) + i];
-        }
         const bool polar = part == 0 ? a.k_polar : a.v_polar;
-        if (polar) {
-          const float2* pt = reinterpret_cast<const float2*>(table + kPairOffset) + pair_offset_host(B);
-          for (int i = lane; i < L * L; i += 64) lds_pair[i] = pt[i];
-        }
+        const int shift = polar ? polar_shift_of(table) : 0;
+        stage_token_tables(table, B, polar, shift, lane, 64, lds_thr, lds_cent, lds_pair);
         float x[D];
         load_row(src + part * PT * D * 2, TQ_DTYPE_F16, (size_t)lane * D, x);
         // the key part ends below the value rows, so in place the values are
@@ -359,26 +349,26 @@ __global__ __launch_bounds__(64) void retier_kernel(RetierArgs a) {
         float n = 0.f;
         if (part == 0) {
           switch (B) {
-            case 1: n = encode_packed<0, 1>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-            case 2: n = encode_packed<0, 2>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-            case 3: n = encode_packed<0, 3>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-            case 4: n = encode_packed<0, 4>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-            case 5: n = encode_packed<0, 5>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-            case 6: n = encode_packed<0, 6>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-            case 7: n = encode_packed<0, 7>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-            default: n = encode_packed<0, 8>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            case 1: n = encode_packed<0, 1>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
+            case 2: n = encode_packed<0, 2>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
+            case 3: n = encode_packed<0, 3>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
+            case 4: n = encode_packed<0, 4>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
+            case 5: n = encode_packed<0, 5>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
+            case 6: n = encode_packed<0, 6>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
+            case 7: n = encode_packed<0, 7>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
+            default: n = encode_packed<0, 8>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
           }
           if (nq) qjl_sketch(a.qjl_s, part_base + 1024 * B + 256, lane, x, m, n);
         } else {
           switch (B) {
-            case 1: n = encode_packed<1, 1>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-            case 2: n = encode_packed<1, 2>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-            case 3: n = encode_packed<1, 3>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-            case 4: n = encode_packed<1, 4>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-            case 5: n = encode_packed<1, 5>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-            case 6: n = encode_packed<1, 6>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-            case 7: n = encode_packed<1, 7>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
-            default: n = encode_packed<1, 8>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair); break;
+            case 1: n = encode_packed<1, 1>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
+            case 2: n = encode_packed<1, 2>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
+            case 3: n = encode_packed<1, 3>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
+            case 4: n = encode_packed<1, 4>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
+            case 5: n = encode_packed<1, 5>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
+            case 6: n = encode_packed<1, 6>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
+            case 7: n = encode_packed<1, 7>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
+            default: n = encode_packed<1, 8>(part_base, lane, x, m, lds_thr, lds_cent, lds_rows, polar, lds_pair, shift); break;
           }
         }
         __syncthreads();

@@ -100,17 +100,43 @@ __device__ __forceinline__ float rotate_quantize(float (&x)[D], const uint32_t (
   return n;
 }
 
+// PolarQuant tables carry their angle shift t in the last entry; a page of
+// width bw has a pair table (bw <= 4) and a split (radius bw - t and angle
+// bw + t bits in 1..8) only for some shifts.
+__device__ __forceinline__ int polar_shift_of(const float* table) { return (int)table[kPolarShiftSlot]; }
+__device__ __forceinline__ bool polar_width_ok(int bw, int t) {
+  return bw >= 1 && bw <= 4 && bw - t >= 1 && bw + t >= 1 && bw + t <= 8;
+}
+// Stage, for encode_packed, the quantiser of width B of `table` (PolarQuant:
+// the radius boundaries of B - shift bits and the pair table of width B).
+__device__ __forceinline__ void stage_token_tables(const float* table, int B, bool polar, int shift, int lane,
+                                                   int nthreads, float* lds_thr, float* lds_cent,
+                                                   float2* lds_pair) {
+  const int W = polar ? B - shift : B, L = 1 << W;
+  for (int i = lane; i < L; i += nthreads) {
+    lds_cent[i] = table[centroid_offset(W) + i];
+    if (i < L - 1) lds_thr[i] = table[boundary_offset(W) + i];
+  }
+  if (polar) {
+    const float2* pt = reinterpret_cast<const float2*>(table + kPairOffset) + pair_offset_host(B);
+    for (int i = lane; i < (1 << (2 * B)); i += nthreads) lds_pair[i] = pt[i];
+  }
+}
+
 // PolarQuant of one vector held by this lane: u as above, then for each
-// coordinate pair i the radius r = |(u_2i, u_2i+1)| against the radius
-// boundaries in `thr` and the angle sector floor((atan2(u_2i+1, u_2i) + pi)
-// 2^B / (2 pi)) mod 2^B; codes go to emit(2i, radius) and emit(2i+1, angle).
-// On return x holds u minus the pair's reconstruction from `pair`.
+// coordinate pair i the radius r = |(u_2i, u_2i+1)| against the 2^RB - 1
+// radius boundaries in `thr` (RB = B - shift bits) and the angle sector
+// floor((atan2(u_2i+1, u_2i) + pi) 2^AB / (2 pi)) mod 2^AB (AB = B + shift
+// bits); the pair field F = radius | angle << RB goes to emit(2i, F's low B
+// bits) and emit(2i+1, its high B bits).  On return x holds u minus the
+// pair's reconstruction pair[F].
 template <int B, class Emit>
 __device__ __forceinline__ float rotate_quantize_polar(float (&x)[D], const uint32_t (&m)[4],
-                                                       const float* thr, const float2* pair, Emit emit) {
-  constexpr int L = 1 << B;
+                                                       const float* thr, const float2* pair, Emit emit,
+                                                       int shift) {
+  const int RB = B - shift, L = 1 << (B + shift);
   constexpr float kPi = 3.14159265358979323846f;
-  constexpr float kSectors = (float)L / (2.0f * 3.14159265358979323846f);
+  const float kSectors = (float)L / (2.0f * 3.14159265358979323846f);
   float ss = 0.f;
 #pragma clang loop unroll(full)
   for (int j = 0; j < D; ++j) ss = fmaf(x[j], x[j], ss);
@@ -131,11 +157,13 @@ __device__ __forceinline__ float rotate_quantize_polar(float (&x)[D], const uint
     const float r = sqrtf(fmaf(u0, u0, u1 * u1));
     // a zero pair takes the angle atan2(+0, +0) = 0, whatever its zeros' signs
     const float th = (u0 == 0.f && u1 == 0.f) ? 0.f : atan2f(u1, u0);
-    const uint32_t rc = quantize<B>(r, thr);
+    uint32_t rc = 0;   // #{boundaries <= r}, a binary search over 2^RB - 1 of them
+    for (int st = 1 << (RB - 1); st >= 1; st >>= 1) rc += (r >= thr[rc + st - 1]) ? (uint32_t)st : 0u;
     const uint32_t tc = (uint32_t)(int)floorf((th + kPi) * kSectors) & (uint32_t)(L - 1);
-    emit(2 * i, rc);
-    emit(2 * i + 1, tc);
-    const float2 p = pair[rc | (tc << B)];
+    const uint32_t F = rc | (tc << RB);
+    emit(2 * i, F & ((1u << B) - 1u));
+    emit(2 * i + 1, F >> B);
+    const float2 p = pair[F];
     x[2 * i] = u0 - p.x;
     x[2 * i + 1] = u1 - p.y;
   }
@@ -143,13 +171,15 @@ __device__ __forceinline__ float rotate_quantize_polar(float (&x)[D], const uint
 }
 
 // One part (PART 0 keys, 1 values) of a page: this lane's vector encoded at
-// width B, scalar or (polar, B <= 4) PolarQuant with the pair table in LDS.
+// width B, scalar or (polar, B <= 4) PolarQuant with the pair table in LDS
+// and, in lds_thr, the radius boundaries of B - polar_shift bits.
 // Returns the vector's norm; for keys x is left holding the rotated-domain
 // residual u - c[code] (qjl_sketch's input).
 template <int PART, int B>
 __device__ __forceinline__ float encode_packed(char* page, int lane, float (&x)[D], const uint32_t (&m)[4],
                                                float* lds_thr, float* lds_cent, uint32_t* lds_rows,
-                                               bool polar = false, const float2* lds_pair = nullptr) {
+                                               bool polar = false, const float2* lds_pair = nullptr,
+                                               int polar_shift = 0) {
   constexpr int kb = B;
   if constexpr (PART == 0) {
     uint32_t sw[4 * B];
@@ -162,7 +192,7 @@ __device__ __forceinline__ float encode_packed(char* page, int lane, float (&x)[
     };
     float n;
     if constexpr (B <= 4) {
-      n = polar ? rotate_quantize_polar<B>(x, m, lds_thr, lds_pair, emit)
+      n = polar ? rotate_quantize_polar<B>(x, m, lds_thr, lds_pair, emit, polar_shift)
                 : rotate_quantize<B>(x, m, lds_thr, lds_cent, emit);
     } else {
       n = rotate_quantize<B>(x, m, lds_thr, lds_cent, emit);
@@ -181,7 +211,7 @@ __device__ __forceinline__ float encode_packed(char* page, int lane, float (&x)[
     auto emit = [&](int j, uint32_t c) { cb[j >> 2] |= c << (8 * (j & 3)); };
     float n;
     if constexpr (B <= 4) {
-      n = polar ? rotate_quantize_polar<B>(x, m, lds_thr, lds_pair, emit)
+      n = polar ? rotate_quantize_polar<B>(x, m, lds_thr, lds_pair, emit, polar_shift)
                 : rotate_quantize<B>(x, m, lds_thr, lds_cent, emit);
     } else {
       n = rotate_quantize<B>(x, m, lds_thr, lds_cent, emit);

@@ -81,16 +81,41 @@ class Tally:
         assert self.worst_cos >= COS_MIN, f"dequantised cosine {self.worst_cos:.9f}"
 
 
+def layer_args(k_kind, v_kind) -> dict:
+    """tq.Layer codebook arguments for the oracle's kinds: a PolarSplit is kind
+    POLAR with the library's table for its shift."""
+    import kv_cache_vector_srht_amd as tq
+    kw = {}
+    for part, kind in (("k", k_kind), ("v", v_kind)):
+        if isinstance(kind, O.PolarSplit):
+            kw[part + "_codebook"] = tq.POLAR
+            kw[part + "_table"] = tq.polar_table(kind.shift)
+        else:
+            kw[part + "_codebook"] = kind
+    return kw
+
+
 def _cmp_codes(got: np.ndarray, exp: np.ndarray, near: np.ndarray, t: Tally, what: str, lo: int,
                alt: list, kind=O.LLOYD_MAX, bits: int = 0):
     diff = got != exp
     t.coords += got.size
     if diff.any():
-        step = np.abs(got - exp)
-        if kind == O.POLAR:   # angle codes (odd coordinates) are cyclic
-            L = 1 << bits
-            step[:, 1::2] = np.minimum(step[:, 1::2], L - step[:, 1::2])
-        bad = diff & ~(near & (step == 1))
+        shift = O.polar_shift(kind)
+        if shift is None:
+            step = np.abs(got - exp)
+            bad = diff & ~(near & (step == 1))
+        else:
+            # PolarQuant: a pair's radius may move one level near a radius
+            # boundary and its angle one sector, cyclically, near a sector edge
+            rb, ab = O.polar_widths(bits, shift)
+            Fg = got[:, 0::2] | (got[:, 1::2] << bits)
+            Fe = exp[:, 0::2] | (exp[:, 1::2] << bits)
+            m = (1 << rb) - 1
+            dr = np.abs((Fg & m) - (Fe & m))
+            dt = np.abs((Fg >> rb) - (Fe >> rb))
+            dt = np.minimum(dt, (1 << ab) - dt)
+            ok = ((dr == 0) | ((dr == 1) & near[:, 0::2])) & ((dt == 0) | ((dt == 1) & near[:, 1::2]))
+            bad = diff & ~np.repeat(ok, 2, axis=1)
         assert not bad.any(), f"{what}: {int(bad.sum())} code mismatches away from a boundary " \
                               f"(first at {np.argwhere(bad)[0].tolist()}, got {got[bad][:4]}, want {exp[bad][:4]})"
         t.mismatches += int(diff.sum())

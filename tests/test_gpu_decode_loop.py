@@ -8,7 +8,7 @@ import pytest
 
 import workloads as W
 from oracle import tq_oracle as O
-from tests.gpu_parity import Tally, compare_attention, compare_unit_full
+from tests.gpu_parity import Tally, compare_attention, compare_unit_full, layer_args
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -39,7 +39,8 @@ def _effective(targets, n):
 
 @pytest.mark.parametrize("dtype,kinds", [("float16", (O.LLOYD_MAX, O.LLOYD_MAX)),
                                          ("float32", (O.LLOYD_MAX, O.LLOYD_MAX)),
-                                         ("float16", (O.POLAR, O.POLAR))])
+                                         ("float16", (O.POLAR, O.POLAR)),
+                                         ("float16", (O.PolarSplit(1), O.PolarSplit(-1)))])
 def test_decode_loop_append_and_pack(dev, dtype, kinds):
     import kv_cache_vector_srht_amd as tq
     B, H, G, T = 2, 2, 4, 64 * 5 + 20
@@ -51,7 +52,7 @@ def test_decode_loop_append_and_pack(dev, dtype, kinds):
            for h in range(H)] for _ in range(B)]
     signs = W.rotation_signs(42, 0)
     S = W.qjl_matrix(42, 0)
-    layer = tq.Layer(signs, dev, S, kinds[0], kinds[1])
+    layer = tq.Layer(signs, dev, S, **layer_args(kinds[0], kinds[1]))
     k, v = W.make_kv(w, 0, device=dev)          # [B, H, T, 128], the tokens in order
     q = W.make_query(w, 0, device=dev)
     start = [100, 90]                            # ragged sessions

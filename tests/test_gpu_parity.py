@@ -7,7 +7,8 @@ import pytest
 
 import workloads as W
 from oracle import tq_oracle as O
-from tests.gpu_parity import Tally, compare_attention, compare_dequant, compare_unit_full, compare_unit_pages
+from tests.gpu_parity import (Tally, compare_attention, compare_dequant, compare_unit_full, compare_unit_pages,
+                               layer_args)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -39,7 +40,7 @@ def run_case(w, layers, dev, units=None, n_tokens=None, dequant=True, chunks=Non
         signs = W.rotation_signs(W.ROTATION_SEED, l)
         S = W.qjl_matrix(W.ROTATION_SEED, l) if has_qjl else None
         if layer_kw is None:
-            layer = tq.Layer(signs, dev, S, w.k_codebook, w.v_codebook)
+            layer = tq.Layer(signs, dev, S, **layer_args(w.k_codebook, w.v_codebook))
         else:
             layer = tq.Layer(signs, dev, S, **layer_kw)
         ntoks = n_tokens or [w.n_tokens] * w.batch
@@ -299,6 +300,43 @@ def test_polar_keys_with_qjl_and_scalar_values(dev):
     w = _narrow_workload(pages=18, qjl=True)
     w.k_codebook, w.v_codebook = O.POLAR, O.LLOYD_MAX
     run_case(w, [0], dev)
+
+
+@pytest.mark.parametrize("k_shift,v_shift", [(1, -1), (2, 3), (-2, -3)])
+def test_polar_split_widths(dev, k_shift, v_shift):
+    """PolarQuant with radius and angle widths of their own: every width pair
+    whose widths can carry the shifts (radius b - t, angle b + t bits),
+    encoded by the bulk encoder, decoded and dequantised, against the oracle's
+    PolarSplit (2-bit and 3-bit angles take the tangent tests, wider ones the
+    arctangent)."""
+    ks = [b for b in range(1, 5) if 1 <= b - k_shift and 1 <= b + k_shift <= 8]
+    vs = [b for b in range(1, 5) if 1 <= b - v_shift and 1 <= b + v_shift <= 8]
+    combos = [(kb, vb) for kb in ks for vb in vs]
+    pages = 1 + 2 * len(combos)
+    w = W.make_workload(2, {"n_tokens": 64 * pages, "batch": 1, "n_kv_heads": 2, "n_q_heads": 8,
+                            "sink_tokens": 64})
+    w.formats = [[[[W.packed(*combos[(p + 3 * h) % len(combos)]) if p > 0 else W.FP16
+                    for p in range(pages)] for h in range(2)]]]
+    w.k_codebook, w.v_codebook = O.PolarSplit(k_shift), O.PolarSplit(v_shift)
+    run_case(w, [0], dev)
+
+
+def test_polar_split_refuses_widths_without_a_split(dev):
+    """A page too narrow for the angle shift (no radius bit left) is refused by
+    encode (flag 4, page untouched)."""
+    import kv_cache_vector_srht_amd as tq
+    w = W.make_workload(2, {"n_tokens": 128, "batch": 1, "n_kv_heads": 1, "n_q_heads": 4,
+                            "sink_tokens": 0})
+    fm = [[[W.packed(3, 2), W.packed(2, 2)]]]
+    layer = tq.Layer(W.rotation_signs(42, 0), dev, None, **layer_args(O.PolarSplit(2), O.LLOYD_MAX))
+    cache = tq.Cache(fm, [128], dev)
+    k, v = W.make_kv(w, 0, device=dev)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    tq.encode_kv(layer, cache, k, v, error_flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 4
+    kpart = cache.page_view(0, 0, 1)[:1024 * 2 + 256]
+    assert int(kpart.to(torch.int32).abs().sum()) == 0
 
 
 def test_polar_refuses_wide_pages(dev):

@@ -122,6 +122,37 @@ def test_codebook_table_layout(L, kind, fit_samples):
         assert np.array_equal(got, want), b
 
 
+@pytest.mark.parametrize("shift", [-3, -1, 0, 1, 2, 3])
+def test_polar_table_with_angle_shift(L, shift):
+    """tq_polar_table: Rayleigh levels at every width, pair tables of widths
+    1..4 indexed by the pair field rc | tc << (b - shift) equal to the oracle's
+    (to 1 ulp: both round the exact product), the shift in the last entry, and
+    radius lookup grids at the widths the pages use."""
+    tab = tq.polar_table(shift)
+    assert tab[-1] == shift
+    if shift == 0:
+        assert np.array_equal(tab, tq.codebook_table(tq.POLAR))
+    for b in range(1, 9):
+        c, t = O.codebook(b, O.POLAR)
+        co, to = (1 << b) - 2, 510 + (1 << b) - b - 1
+        assert np.array_equal(tab[co:co + (1 << b)], c) and np.array_equal(tab[to:to + (1 << b) - 1], t)
+    for b, first in ((1, 0), (2, 4), (3, 20), (4, 84)):
+        n = 1 << (2 * b)
+        pt = tab[1056 + 2 * first:1056 + 2 * (first + n)].reshape(n, 2)
+        try:
+            want = O.polar_pair_table(b, shift)
+        except ValueError:          # this width cannot carry the shift: no table
+            assert np.all(pt == 0)
+            continue
+        ulp = np.abs(pt.view(np.int32).astype(np.int64) - want.view(np.int32))
+        assert np.all((ulp <= 1) | (np.abs(pt - want) < 1e-12)), b
+    words = tab.view(np.uint32)
+    for r in range(1, 5 - min(shift, 0)):
+        assert int(words[1024 + 4 * (r - 1) + 2]) > 0, r       # a radius grid at width r
+    with pytest.raises(tq.TQError):
+        tq.polar_table(4)
+
+
 @pytest.mark.parametrize("layer", [0, 1, 35])
 def test_layer_params_match_generator(L, layer):
     s, S = tq.layer_params(42, layer)
