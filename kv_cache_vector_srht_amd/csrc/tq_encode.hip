@@ -57,6 +57,9 @@ constexpr int kQjlWaves = 4;
 constexpr int kQjlBlocksPerCU = 2;   // 80 KB of LDS each
 typedef float mfma_acc16 __attribute__((ext_vector_type(16)));
 
+// POLAR: the instantiation for PolarQuant keys (the plain one has no polar
+// code, which keeps its registers).
+template <bool POLAR>
 __global__ __launch_bounds__(64 * kQjlWaves) void qjl_keys_kernel(EncodeArgs a, const uint64_t* __restrict__ pages,
                                                                  int n_pages) {
   __shared__ float st[D * D];
@@ -91,7 +94,7 @@ __global__ __launch_bounds__(64 * kQjlWaves) void qjl_keys_kernel(EncodeArgs a, 
     if (!qjl || bad_fmt || pd.off + page_size_dev(kb, vb, qjl) > a.pool_bytes) continue;
     const int t_first = pg * PT;
     if (max(t_first, a.tok0) != t_first || min(t_first + PT, a.tok0 + a.ntok) != t_first + PT) continue;
-    const bool polar = a.k_polar;
+    const bool polar = POLAR && a.k_polar;
     const int shift = polar ? polar_shift_of(a.k_table) : 0;
     if (polar && !polar_width_ok(kb, shift)) continue;   // refused (and flagged) by encode_pages_kernel
     char* page = a.pool + pd.off;
@@ -704,7 +707,11 @@ int tq_encode_kv(const tq_layer* layer, const tq_cache* cache, const tq_kv_input
     const int64_t items = (int64_t)n_pages * cache->n_kv_heads * cache->n_sessions;
     const int64_t want = (items + kQjlWaves - 1) / kQjlWaves;
     const int blocks = (int)std::min<int64_t>(want, (int64_t)cus * kQjlBlocksPerCU);
-    hipLaunchKernelGGL(qjl_keys_kernel, dim3(blocks), dim3(64 * kQjlWaves), 0, (hipStream_t)stream, a,
+    if (a.k_polar)
+      hipLaunchKernelGGL(qjl_keys_kernel<true>, dim3(blocks), dim3(64 * kQjlWaves), 0, (hipStream_t)stream, a,
+                         cache->pages, n_pages);
+    else
+      hipLaunchKernelGGL(qjl_keys_kernel<false>, dim3(blocks), dim3(64 * kQjlWaves), 0, (hipStream_t)stream, a,
                        cache->pages, n_pages);
     st2 = launch_status("encode QJL keys");
   }

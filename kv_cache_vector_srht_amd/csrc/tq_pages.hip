@@ -39,6 +39,9 @@ struct AppendArgs {
 // the page in place with the per-token encoder (keys, then values; every lane
 // loads its row before any lane stores, and the key part ends below the value
 // rows) and clears the pending bit.
+// POLAR: the instantiation for layers with PolarQuant parts (the plain one has
+// no polar code, which keeps its registers).
+template <bool POLAR>
 __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
   __shared__ float lds_thr[256];
   __shared__ float lds_cent[256];
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
   for (int part = 0; part < 2; ++part) {
     const int B = part == 0 ? kb : vb;
     const float* table = part == 0 ? a.k_table : a.v_table;
-    const bool polar = part == 0 ? a.k_polar : a.v_polar;
+    const bool polar = POLAR && (part == 0 ? a.k_polar : a.v_polar);
     const int shift = part == 0 ? tk : tv;
     stage_token_tables(table, B, polar, shift, lane, 64, lds_thr, lds_cent, lds_pair);
     float x[D];
@@ -304,7 +307,7 @@ __device__ __forceinline__ int retier_check(const RetierArgs& a, int64_t idx, ui
 // narrower widths, keeping its norms; an fp16 page is encoded with the
 // per-token encoder.  Every lane loads the whole of its part of the old page
 // before any lane stores, so the new page may take the old slot.
-template <bool FROM_FP16>
+template <bool FROM_FP16, bool POLAR>
 __global__ __launch_bounds__(64) void retier_kernel(RetierArgs a) {
   __shared__ float lds_thr[FROM_FP16 ? 256 : 1];
   __shared__ float lds_cent[FROM_FP16 ? 256 : 1];
@@ -337,7 +340,7 @@ __global__ __launch_bounds__(64) void retier_kernel(RetierArgs a) {
       for (int part = 0; part < 2; ++part) {
         const int B = part == 0 ? nkb : nvb;
         const float* table = part == 0 ? a.k_table : a.v_table;
-        const bool polar = part == 0 ? a.k_polar : a.v_polar;
+        const bool polar = POLAR && (part == 0 ? a.k_polar : a.v_polar);
         const int shift = polar ? polar_shift_of(table) : 0;
         stage_token_tables(table, B, polar, shift, lane, 64, lds_thr, lds_cent, lds_pair);
         float x[D];
@@ -441,7 +444,10 @@ int tq_append_kv(const tq_layer* layer, const tq_cache* cache, const tq_token_in
   a.k_polar = layer->k_codebook == TQ_CODEBOOK_POLAR;
   a.v_polar = layer->v_codebook == TQ_CODEBOOK_POLAR;
   hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL(append_kernel, dim3(cache->n_kv_heads, cache->n_sessions), dim3(64), 0, s, a);
+  if (a.k_polar || a.v_polar)
+    hipLaunchKernelGGL(append_kernel<true>, dim3(cache->n_kv_heads, cache->n_sessions), dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL(append_kernel<false>, dim3(cache->n_kv_heads, cache->n_sessions), dim3(64), 0, s, a);
   if ((st = launch_status("append"))) return st;
   hipLaunchKernelGGL(advance_kernel, dim3((cache->n_sessions + 255) / 256), dim3(256), 0, s,
                      const_cast<int32_t*>(cache->n_tokens), cache->n_sessions);
@@ -482,12 +488,15 @@ int tq_retier_pages(const tq_layer* layer, const tq_cache* cache, const int64_t*
   const dim3 grid(std::min(n, kRetierBlocks));
   a.raise_errors = 1;
   if (a.sources & TQ_RETIER_FROM_PACKED) {
-    hipLaunchKernelGGL(retier_kernel<false>, grid, dim3(64), 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL((retier_kernel<false, false>), grid, dim3(64), 0, (hipStream_t)stream, a);
     if ((st = launch_status("retier packed pages"))) return st;
     a.raise_errors = 0;
   }
   if (a.sources & TQ_RETIER_FROM_FP16) {
-    hipLaunchKernelGGL(retier_kernel<true>, grid, dim3(64), 0, (hipStream_t)stream, a);
+    if (a.k_polar || a.v_polar)
+      hipLaunchKernelGGL((retier_kernel<true, true>), grid, dim3(64), 0, (hipStream_t)stream, a);
+    else
+      hipLaunchKernelGGL((retier_kernel<true, false>), grid, dim3(64), 0, (hipStream_t)stream, a);
     st = launch_status("retier fp16 pages");
   }
   return st;

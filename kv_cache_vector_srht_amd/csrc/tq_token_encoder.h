@@ -108,7 +108,9 @@ __device__ __forceinline__ bool polar_width_ok(int bw, int t) {
   return bw >= 1 && bw <= 4 && bw - t >= 1 && bw + t >= 1 && bw + t <= 8;
 }
 // Stage, for encode_packed, the quantiser of width B of `table` (PolarQuant:
-// the radius boundaries of B - shift bits and the pair table of width B).
+// the radius boundaries of B - shift bits, padded with +inf to 255 entries so
+// that the radius search takes a fixed number of steps, and the pair table of
+// width B).  lds_thr holds 256 floats.
 __device__ __forceinline__ void stage_token_tables(const float* table, int B, bool polar, int shift, int lane,
                                                    int nthreads, float* lds_thr, float* lds_cent,
                                                    float2* lds_pair) {
@@ -118,6 +120,7 @@ __device__ __forceinline__ void stage_token_tables(const float* table, int B, bo
     if (i < L - 1) lds_thr[i] = table[boundary_offset(W) + i];
   }
   if (polar) {
+    for (int i = L - 1 + lane; i < 255; i += nthreads) lds_thr[i] = __builtin_inff();
     const float2* pt = reinterpret_cast<const float2*>(table + kPairOffset) + pair_offset_host(B);
     for (int i = lane; i < (1 << (2 * B)); i += nthreads) lds_pair[i] = pt[i];
   }
@@ -135,6 +138,7 @@ __device__ __forceinline__ float rotate_quantize_polar(float (&x)[D], const uint
                                                        const float* thr, const float2* pair, Emit emit,
                                                        int shift) {
   const int RB = B - shift, L = 1 << (B + shift);
+  constexpr int kMaxRB = B + 3 < 8 ? B + 3 : 8;   // the radius width at shift -3
   constexpr float kPi = 3.14159265358979323846f;
   const float kSectors = (float)L / (2.0f * 3.14159265358979323846f);
   float ss = 0.f;
@@ -157,8 +161,14 @@ __device__ __forceinline__ float rotate_quantize_polar(float (&x)[D], const uint
     const float r = sqrtf(fmaf(u0, u0, u1 * u1));
     // a zero pair takes the angle atan2(+0, +0) = 0, whatever its zeros' signs
     const float th = (u0 == 0.f && u1 == 0.f) ? 0.f : atan2f(u1, u0);
-    uint32_t rc = 0;   // #{boundaries <= r}, a binary search over 2^RB - 1 of them
-    for (int st = 1 << (RB - 1); st >= 1; st >>= 1) rc += (r >= thr[rc + st - 1]) ? (uint32_t)st : 0u;
+    // #{boundaries <= r}: a binary search of kMaxRB steps over the 2^RB - 1 of
+    // them and the +inf padding behind them (the same steps at every shift, so
+    // that the pair loop unrolls and x stays in registers); the clamp keeps an
+    // r of +inf at the top level
+    uint32_t rc = 0;
+#pragma clang loop unroll(full)
+    for (int st = 1 << (kMaxRB - 1); st >= 1; st >>= 1) rc += (r >= thr[rc + st - 1]) ? (uint32_t)st : 0u;
+    rc = min(rc, (uint32_t)((1 << RB) - 1));
     const uint32_t tc = (uint32_t)(int)floorf((th + kPi) * kSectors) & (uint32_t)(L - 1);
     const uint32_t F = rc | (tc << RB);
     emit(2 * i, F & ((1u << B) - 1u));
