@@ -998,7 +998,7 @@ def attention(q: np.ndarray, keys: np.ndarray, values: np.ndarray,
 
 def reconstruct_unit(K: np.ndarray, V: np.ndarray, formats, signs, S=None,
                      k_kind: int = LLOYD_MAX, v_kind: int = LLOYD_MAX,
-                     k_overrides=None, v_overrides=None):
+                     k_overrides=None, v_overrides=None, sign_overrides=None):
     """Keys/values as decode attention sees them for one (session, KV head).
 
     K, V: the stored input rows [T, 128] of this unit; formats: page formats.
@@ -1006,7 +1006,9 @@ def reconstruct_unit(K: np.ndarray, V: np.ndarray, formats, signs, S=None,
     (keys plus the QJL residual when the page carries one).  Pages of one
     format are encoded together (rows are independent).  ``k_overrides`` /
     ``v_overrides`` = (tokens, cols, codes) pick the other admissible level at
-    boundary coordinates (see ``encode``).
+    boundary coordinates (see ``encode``); ``sign_overrides`` = (tokens, rows
+    of S, signs) the other admissible QJL sign where (S r)_i is within
+    rounding of zero (``qjl_encode``'s ``near``).
     """
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
@@ -1041,7 +1043,12 @@ def reconstruct_unit(K: np.ndarray, V: np.ndarray, formats, signs, S=None,
         kh = dequantize(ek["norm"], ek["codes"], signs, kb, k_kind)
         if qjl:
             qj = qjl_encode(K[rows], kh, S)
-            kh = kh + qjl_reconstruct(qj["z"], qj["gamma"], S)
+            z = qj["z"].copy()
+            so = local(sign_overrides, rows)
+            if so is not None:
+                assert np.all(qj["near"][so[0], so[1]]), "a sign override away from zero"
+                z[so[0], so[1]] = so[2].astype(bool)
+            kh = kh + qjl_reconstruct(z, qj["gamma"], S)
         Kh[rows] = kh
         Vh[rows] = dequantize(ev["norm"], ev["codes"], signs, vb, v_kind)
     return Kh, Vh

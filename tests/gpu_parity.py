@@ -135,14 +135,16 @@ def compare_unit_pages(cache, b: int, h: int, K: np.ndarray, V: np.ndarray, form
                        pool_host: Optional[np.ndarray] = None):
     """Compare every page of unit (b, h) with the oracle's encoding of K, V.
 
-    Returns (k_ok, v_ok, k_alt, v_alt): boolean arrays [T] marking tokens whose
-    K (resp. V) codes all match, and the admissible boundary tie-breaks the GPU
-    took, as (tokens, coordinates, codes) for ``reconstruct_unit``.
+    Returns (k_ok, v_ok, k_alt, v_alt, z_alt): boolean arrays [T] marking
+    tokens whose K (resp. V) codes all match, the admissible boundary
+    tie-breaks the GPU took, as (tokens, coordinates, codes), and its
+    admissible near-zero QJL signs, as (tokens, rows of S, signs), for
+    ``reconstruct_unit``.
     """
     T = K.shape[0] if n_tokens is None else n_tokens
     k_ok = np.ones(T, dtype=bool)
     v_ok = np.ones(T, dtype=bool)
-    k_alt, v_alt = [], []
+    k_alt, v_alt, z_alt = [], [], []
     for p, fmt in enumerate(formats):
         lo, hi = p * 64, min(T, (p + 1) * 64)
         if lo >= T:
@@ -184,12 +186,15 @@ def compare_unit_pages(cache, b: int, h: int, K: np.ndarray, V: np.ndarray, form
             assert not (dz & ~qj["near"][rows]).any(), f"QJL signs page ({b},{h},{p})"
             t.sign_bits += dz.size
             t.sign_mismatches += int(dz.sum())
+            if dz.any():
+                r, c = np.nonzero(dz)
+                z_alt.append((lo + rows[r], c, z[rows[r], c]))
             assert np.allclose(g[rows], qj["gamma"][rows], rtol=NORM_RTOL, atol=1e-30), \
                 f"QJL gamma page ({b},{h},{p})"
             gr = np.abs(g[rows] - qj["gamma"][rows]) / np.maximum(qj["gamma"][rows], 1e-30)
             t.worst_gamma_rel = max(t.worst_gamma_rel, float(gr.max()) if gr.size else 0.0)
             k_ok[lo + rows[dz.any(axis=1)]] = False
-    return k_ok, v_ok, _stack(k_alt), _stack(v_alt)
+    return k_ok, v_ok, _stack(k_alt), _stack(v_alt), _stack(z_alt)
 
 
 def compare_attention(out_rows: np.ndarray, q_rows: np.ndarray, Kh: np.ndarray, Vh: np.ndarray,
@@ -216,7 +221,7 @@ def compare_unit_full(pool_host: np.ndarray, offsets: np.ndarray, b: int, h: int
     """Compare every page of unit (b, h) with the oracle, encoding the pages of
     one format together (one oracle pass over the unit), and return the
     oracle's reconstruction (Kh, Vh) under the admissible boundary tie-breaks
-    the GPU took: the same composition of oracle steps as
+    and near-zero QJL signs the GPU took: the same composition of oracle steps as
     ``O.reconstruct_unit`` with overrides, without encoding twice.  Pages in
     ``skip`` are left to the caller (their rows of Kh, Vh stay zero).  With a
     ``parts`` dict, also returns there the keys without their QJL term
@@ -294,9 +299,11 @@ def compare_unit_full(pool_host: np.ndarray, offsets: np.ndarray, b: int, h: int
             assert np.all(dg <= NORM_RTOL * qj["gamma"] + GAMMA_ULPS_OF_X * 2.0 ** -24 * xn + 1e-30), \
                 (f"QJL gamma {what}: max rel {np.max(dg / np.maximum(qj['gamma'], 1e-30)):.3e}, "
                  f"max |dgamma| / ||x|| {np.max(dg / np.maximum(xn, 1e-30)):.3e}")
-            kh = kh + O.qjl_reconstruct(qj["z"], qj["gamma"], S)
+            # the GPU's sign where it is admissible (every difference is, above)
+            za = np.where(dz, z, qj["z"])
+            kh = kh + O.qjl_reconstruct(za, qj["gamma"], S)
             if parts is not None:
-                parts["z"][rows] = qj["z"]
+                parts["z"][rows] = za
                 parts["gamma"][rows] = qj["gamma"]
         Kh[rows] = kh
         Vh[rows] = O.dequantize(ev["norm"], vc, signs, vb, v_kind)

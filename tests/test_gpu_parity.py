@@ -64,12 +64,13 @@ def run_case(w, layers, dev, units=None, n_tokens=None, dequant=True, chunks=Non
         pool = _np(cache.pool)
         for (b, h) in (units or [(b, h) for b in range(w.batch) for h in range(w.n_kv_heads)]):
             T = ntoks[b]
-            k_ok, v_ok, k_alt, v_alt = compare_unit_pages(cache, b, h, kh[b, h], vh[b, h], fm[b][h],
+            k_ok, v_ok, k_alt, v_alt, z_alt = compare_unit_pages(cache, b, h, kh[b, h], vh[b, h], fm[b][h],
                                                           signs, S, t, w.k_codebook, w.v_codebook,
                                                           n_tokens=w.n_tokens, pool_host=pool)
-            # the oracle's encoding under the admissible boundary tie-breaks taken above
+            # the oracle's encoding under the admissible boundary tie-breaks and
+            # near-zero QJL signs taken above
             Kh, Vh = O.reconstruct_unit(kh[b, h, :T], vh[b, h, :T], fm[b][h], signs, S,
-                                        w.k_codebook, w.v_codebook, k_alt, v_alt)
+                                        w.k_codebook, w.v_codebook, k_alt, v_alt, z_alt)
             rows = out[b, h * G:(h + 1) * G]
             if T == 0:
                 assert np.all(rows == 0)
@@ -77,7 +78,7 @@ def run_case(w, layers, dev, units=None, n_tokens=None, dequant=True, chunks=Non
                 compare_attention(rows, qh[b, h * G:(h + 1) * G], Kh, Vh, t)
             if dequant and T > 0:
                 Kf, Vf = O.reconstruct_unit(kh[b, h], vh[b, h], fm[b][h], signs, S,
-                                            w.k_codebook, w.v_codebook, k_alt, v_alt)
+                                            w.k_codebook, w.v_codebook, k_alt, v_alt, z_alt)
                 compare_dequant(dk[b, h], Kf, t)
                 compare_dequant(dv[b, h], Vf, t)
     t.check()
