@@ -5,9 +5,10 @@
 // stored, and each coordinate of u = D H D x / ||x|| is quantised and packed.
 // encode_pages_kernel (four lanes per vector, below) writes fp16 pages and the
 // packed keys and values of every page without a QJL residual.
-// qjl_keys_kernel (one lane per vector) writes the keys of QJL pages: codes,
-// norm, and the signs of S r for r = x - xhat ("TurboMOQ", QJL residual
-// correction), the sketch on the matrix cores.
+// The keys of QJL pages (codes, norm, and the signs of S r for r = x - xhat,
+// "TurboMOQ", QJL residual correction, the sketch on the matrix cores) come
+// from qjl_quad_kernel (four lanes per vector) for scalar codebooks and from
+// qjl_keys_kernel (one lane per vector) for PolarQuant keys.
 #include <algorithm>
 #include <atomic>
 
@@ -37,7 +38,7 @@ struct EncodeArgs {
   int k_polar, v_polar;   // PolarQuant parts (at most 4 bits wide)
 };
 
-// Keys of QJL pages: the per-token encoder (lane = token) writes codes and norm
+// PolarQuant keys of QJL pages: the per-token encoder (lane = token) writes codes and norm
 // and leaves the residual r in registers; the sign sketch z = sign(S r) of the
 // page's 64 keys is then one product [64 tokens x 128] . [128 x 128] on the
 // float32 matrix cores (v_mfma_f32_32x32x2f32, exact float32 products).
@@ -57,9 +58,7 @@ constexpr int kQjlWaves = 4;
 constexpr int kQjlBlocksPerCU = 2;   // 80 KB of LDS each
 typedef float mfma_acc16 __attribute__((ext_vector_type(16)));
 
-// POLAR: the instantiation for PolarQuant keys (the plain one has no polar
-// code, which keeps its registers).
-template <bool POLAR>
+// Launched for PolarQuant keys; scalar keys take qjl_quad_kernel (below).
 __global__ __launch_bounds__(64 * kQjlWaves) void qjl_keys_kernel(EncodeArgs a, const uint64_t* __restrict__ pages,
                                                                  int n_pages) {
   __shared__ float st[D * D];
@@ -94,7 +93,7 @@ __global__ __launch_bounds__(64 * kQjlWaves) void qjl_keys_kernel(EncodeArgs a, 
     if (!qjl || bad_fmt || pd.off + page_size_dev(kb, vb, qjl) > a.pool_bytes) continue;
     const int t_first = pg * PT;
     if (max(t_first, a.tok0) != t_first || min(t_first + PT, a.tok0 + a.ntok) != t_first + PT) continue;
-    const bool polar = POLAR && a.k_polar;
+    const bool polar = a.k_polar;
     const int shift = polar ? polar_shift_of(a.k_table) : 0;
     if (polar && !polar_width_ok(kb, shift)) continue;   // refused (and flagged) by encode_pages_kernel
     char* page = a.pool + pd.off;
@@ -222,6 +221,28 @@ __device__ __forceinline__ void quad_butterfly(float (&x)[32], float sg) {
 #undef TQ_FMAC_DPP
 }
 
+// The rest of the 128-point transform of a quad's vector once slot bit 0's
+// butterflies are done: in-lane butterflies over slot bits 1..4 (coordinate
+// bits 1,2,5,6), then across the quad coordinate bits 3 (lane bit 0) and 4
+// (lane bit 1).  Each lane computes mine + sg * partner (one multiply-add with
+// the partner read through DPP), so an upper lane keeps the negated butterfly
+// output; afterwards lane e holds rho_e times the transform, rho_e = -1 for
+// e = 1, 2, which the sign applied before quantising undoes (EncodeLane::fl
+// carries it).
+__device__ __forceinline__ void quarter_butterflies(float (&x)[32], int e) {
+#pragma clang loop unroll(full)
+  for (int h = 2; h < 32; h <<= 1)
+#pragma clang loop unroll(full)
+    for (int s = 0; s < 32; ++s)
+      if (!(s & h)) {
+        const float a0 = x[s], b0 = x[s + h];
+        x[s] = a0 + b0;
+        x[s + h] = a0 - b0;
+      }
+  quad_butterfly<0xB1>(x, (e & 1) ? -1.f : 1.f);
+  quad_butterfly<0x4E>(x, (e & 2) ? -1.f : 1.f);
+}
+
 struct Lut {
   float S, O;
   int nb;
@@ -234,23 +255,62 @@ struct EncodeLane {
   uint32_t dl;          // D bits of the lane's 32 slots
 };
 
+// Quad lane e's sign words: the D signs of its coordinates 32c + 8e + k.
+__device__ __forceinline__ EncodeLane encode_lane(const uint32_t* sign_mask, int e) {
+  EncodeLane el;
+  uint32_t m[4];
+#pragma clang loop unroll(full)
+  for (int w = 0; w < 4; ++w) m[w] = sign_mask[w];
+  el.dl = 0;
+#pragma clang loop unroll(full)
+  for (int c = 0; c < 4; ++c) el.dl |= ((m[c] >> (8 * e)) & 0xffu) << (8 * c);
+#pragma clang loop unroll(full)
+  for (int i = 0; i < 16; ++i)
+    el.hmask[i] = (((el.dl >> (2 * i)) & 1u) << 15) | (((el.dl >> (2 * i + 1)) & 1u) << 31);
+  // lanes 1 and 2 of the quad hold the negated transform (quarter_butterflies)
+  el.fl = (e == 1 || e == 2) ? ~el.dl : el.dl;
+  return el;
+}
+
 // Encodes this lane's quarter of one token into code bytes of its LDS matrix
 // row; returns the vector norm (the same in the four lanes of the quad).
-template <int DT, bool POLAR = false>
-__device__ __forceinline__ float encode_quarter(const void* src, size_t row_off, int e,
-                                                const EncodeLane& el, int B, const Lut& lut,
-                                                const uint2* ent, uint32_t* mat_row, int shift = 0) {
-  float x[32];
+// This lane's quarter of one token as loaded: chunk c (coordinates
+// 32c + 8e .. + 7) is w[c] in fp16, w[2c], w[2c + 1] in float32.
+template <int DT>
+struct Quarter {
+  uint4 w[DT == TQ_DTYPE_F16 ? 4 : 8];
+};
+
+template <int DT>
+__device__ __forceinline__ void load_quarter(Quarter<DT>& qv, const void* src, size_t row_off, int e) {
+  if constexpr (DT == TQ_DTYPE_F16) {
+    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const __half*>(src) + row_off);
+#pragma clang loop unroll(full)
+    for (int c = 0; c < 4; ++c) qv.w[c] = p[4 * c + e];
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(src) + row_off);
+#pragma clang loop unroll(full)
+    for (int c = 0; c < 4; ++c) {
+      qv.w[2 * c] = p[2 * (4 * c + e)];
+      qv.w[2 * c + 1] = p[2 * (4 * c + e) + 1];
+    }
+  }
+}
+
+// Leaves in x this lane's share of rho_e H D x (slot 8c + k = coordinate
+// 32c + 8e + k) for the loaded quarter; returns ||x|| (the same in the four
+// lanes of the quad).
+template <int DT>
+__device__ __forceinline__ float rotate_loaded(const Quarter<DT>& qv, int e, const EncodeLane& el, float (&x)[32]) {
   float ss = 0.f;
   if constexpr (DT == TQ_DTYPE_F16) {
     // slots 2i, 2i+1 are the two halves of one fp16 pair: the first butterfly
     // (slot bit 0) reads them straight from the pair with mixed-precision
     // multiply-adds (lo + 1.0 * hi, lo - 1.0 * hi), so no conversion is issued;
     // the norm's squares are mixed-precision too
-    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const __half*>(src) + row_off);
 #pragma clang loop unroll(full)
     for (int c = 0; c < 4; ++c) {
-      const uint4 w = p[4 * c + e];
+      const uint4 w = qv.w[c];
       const uint32_t ww[4] = {w.x ^ el.hmask[4 * c], w.y ^ el.hmask[4 * c + 1],
                               w.z ^ el.hmask[4 * c + 2], w.w ^ el.hmask[4 * c + 3]};
 #pragma clang loop unroll(full)
@@ -267,11 +327,11 @@ __device__ __forceinline__ float encode_quarter(const void* src, size_t row_off,
       }
     }
   } else {
-    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(src) + row_off);
 #pragma clang loop unroll(full)
     for (int c = 0; c < 4; ++c) {
-      const float4 f0 = p[2 * (4 * c + e)], f1 = p[2 * (4 * c + e) + 1];
-      const float v[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+      const uint4 f0 = qv.w[2 * c], f1 = qv.w[2 * c + 1];
+      const float v[8] = {__uint_as_float(f0.x), __uint_as_float(f0.y), __uint_as_float(f0.z), __uint_as_float(f0.w),
+                          __uint_as_float(f1.x), __uint_as_float(f1.y), __uint_as_float(f1.z), __uint_as_float(f1.w)};
 #pragma clang loop unroll(full)
       for (int k = 0; k < 8; ++k) x[8 * c + k] = flip_if(v[k], (el.dl >> (8 * c + k)) & 1u);
     }
@@ -286,24 +346,24 @@ __device__ __forceinline__ float encode_quarter(const void* src, size_t row_off,
   }
   ss += quad_swap(ss, 1);
   ss += quad_swap(ss, 2);
-  // in-lane butterflies over slot bits 1..4 (coordinate bits 1,2,5,6); bit 0 is done
-#pragma clang loop unroll(full)
-  for (int h = 2; h < 32; h <<= 1)
-#pragma clang loop unroll(full)
-    for (int s = 0; s < 32; ++s)
-      if (!(s & h)) {
-        const float a0 = x[s], b0 = x[s + h];
-        x[s] = a0 + b0;
-        x[s + h] = a0 - b0;
-      }
-  // across the quad: coordinate bits 3 (lane bit 0) and 4 (lane bit 1).  Each
-  // lane computes mine + sg * partner (one multiply-add with the partner read
-  // through DPP), so an upper lane keeps the negated butterfly output; after
-  // both stages lane e holds rho_e times the transform, rho_e = -1 for e = 1, 2,
-  // which the sign applied before quantising undoes (EncodeLane::fl carries it).
-  quad_butterfly<0xB1>(x, (e & 1) ? -1.f : 1.f);
-  quad_butterfly<0x4E>(x, (e & 2) ? -1.f : 1.f);
-  const float n = sqrtf(ss);
+  quarter_butterflies(x, e);
+  return sqrtf(ss);
+}
+
+template <int DT>
+__device__ __forceinline__ float rotate_quarter(const void* src, size_t row_off, int e, const EncodeLane& el,
+                                                float (&x)[32]) {
+  Quarter<DT> qv;
+  load_quarter<DT>(qv, src, row_off, e);
+  return rotate_loaded<DT>(qv, e, el, x);
+}
+
+template <int DT, bool POLAR = false>
+__device__ __forceinline__ float encode_quarter(const void* src, size_t row_off, int e,
+                                                const EncodeLane& el, int B, const Lut& lut,
+                                                const uint2* ent, uint32_t* mat_row, int shift = 0) {
+  float x[32];
+  const float n = rotate_quarter<DT>(src, row_off, e, el, x);
   const float inv = n > 0.f ? 1.0f / n : 0.f;
   uint32_t cb[8];
 #pragma clang loop unroll(full)
@@ -465,20 +525,7 @@ __global__ __launch_bounds__(kEncodeBlock) void encode_pages_kernel(EncodeArgs a
   const int pg0 = a.page0 + blockIdx.x * kEncodePagesPerBlock;
   const int pg_last = (a.tok0 + a.ntok - 1) / PT;
 
-  EncodeLane el;
-  {
-    uint32_t m[4];
-#pragma clang loop unroll(full)
-    for (int w = 0; w < 4; ++w) m[w] = a.sign_mask[w];
-    el.dl = 0;
-#pragma clang loop unroll(full)
-    for (int c = 0; c < 4; ++c) el.dl |= ((m[c] >> (8 * e)) & 0xffu) << (8 * c);
-#pragma clang loop unroll(full)
-    for (int i = 0; i < 16; ++i)
-      el.hmask[i] = (((el.dl >> (2 * i)) & 1u) << 15) | (((el.dl >> (2 * i + 1)) & 1u) << 31);
-    // lanes 1 and 2 of the quad hold the negated transform (see encode_quarter)
-    el.fl = (e == 1 || e == 2) ? ~el.dl : el.dl;
-  }
+  const EncodeLane el = encode_lane(a.sign_mask, e);
   int cur_kb = -1, cur_vb = -1;
   Lut lk{0.f, 0.f, 1, 0.f}, lv{0.f, 0.f, 1, 0.f};
   // PolarQuant parts: the angle shift (radius width = page width - shift)
@@ -611,6 +658,239 @@ __global__ __launch_bounds__(kEncodeBlock) void encode_pages_kernel(EncodeArgs a
 }
 
 
+// ------------------------------------------------- QJL keys (quad lanes)
+// Keys of QJL pages with scalar codebooks: the four-lanes-per-vector encoder
+// of encode_pages_kernel (16 tokens per wave and pass, four passes per page),
+// and the sign sketch in the rotated domain on the matrix cores.  The
+// residual r = x - xhat = (||x|| / d) D H D (u - c) ("TurboMOQ", QJL residual
+// correction), so S r = (||x|| / d) S' (u - c) with S' = S D H D: the signs
+// of S r are those of S' v for v = f (u - c), any f > 0, when ||x|| > 0, and
+// all + for a zero row (r = 0).  f scales each token's v to norm sqrt(d), and
+// each row of S' is scaled to a largest magnitude of 8 (neither changes a
+// sign), which keeps both operands well inside float16's range.
+//
+// The products run as float16 pairs: every float32 operand y is hi + lo with
+// hi = fp16(y) and lo = fp16(y - hi) (both rounded to nearest), and
+// S' v = S'hi vhi + S'hi vlo + S'lo vhi on v_mfma_f32_16x16x32_f16 (fp16
+// products are exact in the float32 accumulator).  The dropped S'lo vlo and
+// the rounding of the lo parts leave at most 2^-21 |S'_ij v_j| per term, far
+// inside the rounding band of a QJL sign (1e-5 ||S'_i|| ||v||), where float32
+// evaluation already decides nothing.
+//
+// Each pass multiplies the 16 tokens' v by S'^T, [16 x 128] . [128 x 128]:
+// 8 column blocks x 4 K steps x 3 products.  MFMA lane l = 16 kq + i holds
+// A row i (token) and K elements 8 kq .. 8 kq + 7 of a 32-wide step t; K
+// element (t, kq, j) is coordinate 32 t + 8 kq + j, which quad lane kq of
+// token i holds in slot 8 t + j, so the A operands are one lane permutation of
+// the encoder's registers.  B lane l holds sketch row 16 nb + l % 16 at the
+// same 8 K elements; D lane l, register v: token 4 (l / 16) + v.  S' is built
+// once per workgroup in LDS (each row rotated by a quad, as a token is), hi
+// and lo as 16-byte lane vectors:
+//   S'[n][32 t + 8 kq + j] at vector ((n / 16) 4 + t) 64 + 16 kq + n % 16, half j.
+// One 8-wave workgroup per CU (S' takes 64 KiB of LDS), persistent over the
+// call's pages.
+constexpr int kQjlQuadWaves = 8;
+typedef float mfma_acc4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+
+// u = the lane's slots, outer D and lane sign applied, times inv; code =
+// #{t_k <= u} (binary search over the width's boundaries), into cb's bytes;
+// x[s] <- u - c[code]; e2 += the squares of those residuals.
+template <int B>
+__device__ __forceinline__ void quantize_residual(float (&x)[32], float inv, uint32_t fl, const float* thr,
+                                                  const float* cent, uint32_t (&cb)[8], float& e2) {
+#pragma clang loop unroll(full)
+  for (int s = 0; s < 32; ++s) {
+    const float u = flip_if(x[s] * inv, (fl >> s) & 1u);
+    const uint32_t c = quantize<B>(u, thr);
+    cb[s >> 2] |= c << (8 * (s & 3));
+    const float r = u - cent[c];
+    e2 = fmaf(r, r, e2);
+    x[s] = r;
+  }
+}
+
+// y = hi + lo in float16 (both rounded to nearest); two values per dword,
+// the lower slot in the low half.
+__device__ __forceinline__ void split_pair(float y0, float y1, uint32_t& hi, uint32_t& lo) {
+  const _Float16 h0 = (_Float16)y0, h1 = (_Float16)y1;
+  const _Float16 l0 = (_Float16)(y0 - (float)h0), l1 = (_Float16)(y1 - (float)h1);
+  hi = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+  lo = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+}
+
+__device__ __forceinline__ half8 as_half8(uint4 v) { return __builtin_bit_cast(half8, v); }
+
+template <int DT>
+__global__ __launch_bounds__(64 * kQjlQuadWaves) void qjl_quad_kernel(EncodeArgs a, const uint64_t* __restrict__ pages,
+                                                                      int n_pages) {
+  __shared__ uint4 sph[D * D / 8];
+  __shared__ uint4 spl[D * D / 8];
+  __shared__ uint32_t rows[kQjlQuadWaves][16 * kRowStride / 4];
+  __shared__ float lds_thr[kQjlQuadWaves][256];
+  __shared__ float lds_cent[kQjlQuadWaves][256];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, e = lane & 3, mq = lane >> 2;
+  const EncodeLane el = encode_lane(a.sign_mask, e);
+  // S' rows: quad i / 4 rotates row i of S (all four lanes of a quad take the
+  // same trip count, as the DPP butterflies need)
+  for (int i = tid >> 2; i < D; i += blockDim.x >> 2) {
+    const float* srow = a.qjl_s + (size_t)i * D;
+    float x[32];
+#pragma clang loop unroll(full)
+    for (int c = 0; c < 4; ++c)
+#pragma clang loop unroll(full)
+      for (int k = 0; k < 8; ++k) x[8 * c + k] = flip_if(srow[32 * c + 8 * e + k], (el.dl >> (8 * c + k)) & 1u);
+#pragma clang loop unroll(full)
+    for (int s = 0; s < 32; s += 2) {
+      const float a0 = x[s], b0 = x[s + 1];
+      x[s] = a0 + b0;
+      x[s + 1] = a0 - b0;
+    }
+    quarter_butterflies(x, e);
+    float mx = 0.f;
+#pragma clang loop unroll(full)
+    for (int s = 0; s < 32; ++s) mx = fmaxf(mx, fabsf(x[s]));
+    mx = fmaxf(mx, quad_swap(mx, 1));
+    mx = fmaxf(mx, quad_swap(mx, 2));
+    const float g = mx > 0.f ? 8.0f / mx : 0.f;
+#pragma clang loop unroll(full)
+    for (int c = 0; c < 4; ++c) {
+      uint32_t hi[4], lo[4];
+#pragma clang loop unroll(full)
+      for (int m = 0; m < 4; ++m) {
+        const int s0 = 8 * c + 2 * m;
+        split_pair(flip_if(x[s0] * g, (el.fl >> s0) & 1u), flip_if(x[s0 + 1] * g, (el.fl >> (s0 + 1)) & 1u), hi[m],
+                   lo[m]);
+      }
+      const int at = ((i >> 4) * 4 + c) * 64 + 16 * e + (i & 15);
+      sph[at] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      spl[at] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    }
+  }
+  __syncthreads();
+
+  float* thr = lds_thr[wave];
+  float* cent = lds_cent[wave];
+  uint32_t* rw = rows[wave];
+  const int src = 4 * (lane & 15) + (lane >> 4);     // the encoder lane of this lane's A operands
+  const int vsel = lane & 3, gsh = 16 * ((lane >> 2) & 3);   // lanes 0-15: token = 4 (gsh / 16) + vsel
+  int cur_kb = -1;
+  const int total = n_pages * a.n_kv_heads * a.n_sessions;
+  for (int item = blockIdx.x * kQjlQuadWaves + wave; item < total; item += gridDim.x * kQjlQuadWaves) {
+    const int pgi = item % n_pages, rest = item / n_pages;
+    const int h = rest % a.n_kv_heads, b = rest / a.n_kv_heads;
+    const int pg = a.page0 + pgi;
+    const uint64_t desc = pages[((size_t)b * a.n_kv_heads + h) * a.max_pages + pg];
+    if (!(desc & TQ_PAGE_PRESENT)) continue;    // flagged by encode_pages_kernel
+    const PageDesc pd = read_desc(desc);
+    const int kb = pd.kb, vb = pd.vb;
+    const bool bad_fmt = kb == 0 ? (vb != 0 || pd.qjl) : (kb > 8 || vb < 1 || vb > 8);
+    if (!pd.qjl || bad_fmt || pd.off + page_size_dev(kb, vb, true) > a.pool_bytes) continue;
+    const int t_first = pg * PT;
+    if (max(t_first, a.tok0) != t_first || min(t_first + PT, a.tok0 + a.ntok) != t_first + PT) continue;
+    if (kb != cur_kb) {
+      wave_lds_sync();
+      stage_token_tables(a.k_table, kb, false, 0, lane, 64, thr, cent, nullptr);
+      wave_lds_sync();
+      cur_kb = kb;
+    }
+    char* page = a.pool + pd.off;
+    char* qbase = page + 1024 * kb + 256;
+    const size_t base = (size_t)b * a.sb + (size_t)h * a.sh;
+    const size_t row0 = base + (size_t)(t_first + mq - a.tok0) * a.st;
+    Quarter<DT> qv;
+    load_quarter<DT>(qv, a.k, row0, e);
+#pragma clang loop unroll(disable)
+    for (int q = 0; q < 4; ++q) {
+      const int tok = 16 * q + mq;
+      float x[32];
+      const float n = rotate_loaded<DT>(qv, e, el, x);
+      // the next pass's rows load during this pass's quantiser and products
+      if (q < 3) load_quarter<DT>(qv, a.k, row0 + (size_t)(16 * (q + 1)) * a.st, e);
+      const float inv = n > 0.f ? 1.0f / n : 0.f;
+      uint32_t cb[8];
+#pragma clang loop unroll(full)
+      for (int i = 0; i < 8; ++i) cb[i] = 0;
+      float e2 = 0.f;
+      switch (kb) {
+        case 1: quantize_residual<1>(x, inv, el.fl, thr, cent, cb, e2); break;
+        case 2: quantize_residual<2>(x, inv, el.fl, thr, cent, cb, e2); break;
+        case 3: quantize_residual<3>(x, inv, el.fl, thr, cent, cb, e2); break;
+        case 4: quantize_residual<4>(x, inv, el.fl, thr, cent, cb, e2); break;
+        case 5: quantize_residual<5>(x, inv, el.fl, thr, cent, cb, e2); break;
+        case 6: quantize_residual<6>(x, inv, el.fl, thr, cent, cb, e2); break;
+        case 7: quantize_residual<7>(x, inv, el.fl, thr, cent, cb, e2); break;
+        default: quantize_residual<8>(x, inv, el.fl, thr, cent, cb, e2); break;
+      }
+      e2 += quad_swap(e2, 1);
+      e2 += quad_swap(e2, 2);
+      // codes: row mq holds token tok's 128 code bytes (coordinate order)
+      char* row = reinterpret_cast<char*>(rw + mq * (kRowStride / 4));
+#pragma clang loop unroll(full)
+      for (int c = 0; c < 4; ++c) *reinterpret_cast<uint2*>(row + 32 * c + 8 * e) = make_uint2(cb[2 * c], cb[2 * c + 1]);
+      // A operands: v = f (u - c) as float16 hi + lo; slots 8t .. 8t + 7 of
+      // quad lane kq of token i go to lane 16 kq + i as step t's
+      const float f = e2 > 0.f ? 11.313708498984761f * __builtin_amdgcn_rsqf(fmaxf(e2, 1e-30f)) : 0.f;
+      uint4 ah[4], al[4];
+#pragma clang loop unroll(full)
+      for (int t = 0; t < 4; ++t) {
+        uint32_t hi[4], lo[4];
+#pragma clang loop unroll(full)
+        for (int m = 0; m < 4; ++m) split_pair(x[8 * t + 2 * m] * f, x[8 * t + 2 * m + 1] * f, hi[m], lo[m]);
+        ah[t] = make_uint4(__shfl(hi[0], src), __shfl(hi[1], src), __shfl(hi[2], src), __shfl(hi[3], src));
+        al[t] = make_uint4(__shfl(lo[0], src), __shfl(lo[1], src), __shfl(lo[2], src), __shfl(lo[3], src));
+      }
+      const float ntok = __shfl(n, 4 * (lane & 15));
+      wave_lds_sync();
+      {
+        // K stream tok: quad lane e packs codes 32e .. 32e + 31
+        const uint4 c0 = *reinterpret_cast<const uint4*>(row + 32 * e);
+        const uint4 c1 = *reinterpret_cast<const uint4*>(row + 32 * e + 16);
+        const uint32_t c8[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        store_stream_part(kb, page, tok, e, c8);
+      }
+      if (e == 0) {
+        reinterpret_cast<float*>(page + 1024 * kb)[tok] = n;
+        reinterpret_cast<float*>(qbase + 1024)[tok] = n * sqrtf(e2) * 0.08838834764831845f;   // n ||u - c|| / sqrt(d)
+      }
+      // sketch dword c of the 16 tokens: sketch rows 32c .. 32c + 31 as the
+      // column blocks 2c (low half) and 2c + 1
+      uint32_t w[4];
+#pragma clang loop unroll(full)
+      for (int c = 0; c < 4; ++c) {
+        mfma_acc4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma clang loop unroll(full)
+        for (int t = 0; t < 4; ++t) {
+          const int b0 = ((2 * c) * 4 + t) * 64 + lane, b1 = ((2 * c + 1) * 4 + t) * 64 + lane;
+          const half8 h0 = as_half8(sph[b0]), l0 = as_half8(spl[b0]);
+          const half8 h1 = as_half8(sph[b1]), l1 = as_half8(spl[b1]);
+          const half8 xa = as_half8(ah[t]), xl = as_half8(al[t]);
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl, h0, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl, h1, acc1, 0, 0, 0);
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, l0, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, l1, acc1, 0, 0, 0);
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, h0, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, h1, acc1, 0, 0, 0);
+        }
+        // ballot bit l of register v: token 4 (l / 16) + v, sketch row 16 nb + l % 16
+        uint64_t l0 = 0, l1 = 0;
+#pragma clang loop unroll(full)
+        for (int v = 0; v < 4; ++v) {
+          const uint64_t p0 = __ballot(acc0[v] >= 0.f), p1 = __ballot(acc1[v] >= 0.f);
+          if (vsel == v) {
+            l0 = p0;
+            l1 = p1;
+          }
+        }
+        w[c] = (uint32_t)((l0 >> gsh) & 0xffffu) | ((uint32_t)((l1 >> gsh) & 0xffffu) << 16);
+      }
+      if (lane < 16)
+        reinterpret_cast<uint4*>(qbase)[16 * q + lane] =
+            ntok > 0.f ? make_uint4(w[0], w[1], w[2], w[3]) : make_uint4(~0u, ~0u, ~0u, ~0u);
+      wave_lds_sync();   // the next pass rewrites the rows
+    }
+  }
+}
 }  // namespace
 }  // namespace dev
 }  // namespace tq
@@ -701,18 +981,26 @@ int tq_encode_kv(const tq_layer* layer, const tq_cache* cache, const tq_kv_input
   if (st2) return st2;
   if (layer->qjl_s) {
     // keys of QJL pages: codes, norm and sign sketch, a page per wave on
-    // persistent workgroups (as many as the items need, at most two per CU)
+    // persistent workgroups (as many as the items need: scalar keys one
+    // 8-wave workgroup per CU, PolarQuant keys at most two 4-wave ones)
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) cus = compute_units(dev);
     const int64_t items = (int64_t)n_pages * cache->n_kv_heads * cache->n_sessions;
-    const int64_t want = (items + kQjlWaves - 1) / kQjlWaves;
-    const int blocks = (int)std::min<int64_t>(want, (int64_t)cus * kQjlBlocksPerCU);
-    if (a.k_polar)
-      hipLaunchKernelGGL(qjl_keys_kernel<true>, dim3(blocks), dim3(64 * kQjlWaves), 0, (hipStream_t)stream, a,
+    if (a.k_polar) {
+      const int64_t want = (items + kQjlWaves - 1) / kQjlWaves;
+      const int blocks = (int)std::min<int64_t>(want, (int64_t)cus * kQjlBlocksPerCU);
+      hipLaunchKernelGGL(qjl_keys_kernel, dim3(blocks), dim3(64 * kQjlWaves), 0, (hipStream_t)stream, a,
                          cache->pages, n_pages);
-    else
-      hipLaunchKernelGGL(qjl_keys_kernel<false>, dim3(blocks), dim3(64 * kQjlWaves), 0, (hipStream_t)stream, a,
-                       cache->pages, n_pages);
+    } else {
+      const int64_t want = (items + kQjlQuadWaves - 1) / kQjlQuadWaves;
+      const int blocks = (int)std::min<int64_t>(want, (int64_t)cus);
+      if (a.dtype == TQ_DTYPE_F16)
+        hipLaunchKernelGGL(qjl_quad_kernel<TQ_DTYPE_F16>, dim3(blocks), dim3(64 * kQjlQuadWaves), 0,
+                           (hipStream_t)stream, a, cache->pages, n_pages);
+      else
+        hipLaunchKernelGGL(qjl_quad_kernel<TQ_DTYPE_F32>, dim3(blocks), dim3(64 * kQjlQuadWaves), 0,
+                           (hipStream_t)stream, a, cache->pages, n_pages);
+    }
     st2 = launch_status("encode QJL keys");
   }
   return st2;
