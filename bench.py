@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "decode-attn effective HBM GB/s (% of peak) + encode Mtokens/s at 32K ctx"
 HBM_PEAK_GBS = 8000.0
 FP32_MFMA_PEAK_TFLOPS = 157.3   # dense float32 matrix-core peak
+FP16_MFMA_PEAK_TFLOPS = 2500.0  # dense float16 matrix-core peak
 
 
 def parse():
@@ -434,7 +435,7 @@ def one_layer(idx, dev, enc_reps: int = 5, dec_reps: int = 30):
     ``dec_reps`` calls after warm-up calls, as effective GB/s of the
     algorithmic bytes.  For the QJL workload the call's sketch rate, sketch
     flops (2 x 128 x 128 per key) over the whole encode call, is a lower bound
-    of qjl_keys_kernel's."""
+    of qjl_quad_kernel's."""
     import numpy as np
     import torch
     import kv_cache_vector_srht_amd as tq
@@ -761,7 +762,7 @@ def main():
     enc_mtok = w.batch * w.n_tokens / enc_s / 1e6
 
     # the kernel that dominates the step
-    # (encode is one encode_pages_kernel launch per layer, plus qjl_keys_kernel
+    # (encode is one encode_pages_kernel launch per layer, plus qjl_quad_kernel
     # when a layer has QJL keys; decode is four launches per layer, reported as
     # one call)
     if enc_s >= dec_s:
@@ -786,18 +787,25 @@ def main():
                 "launch_us": round(dec_s / w.n_layers * 1e6, 2)}
     qjl_keys = sum(64 for fm in w.formats for row in fm for r in row for f in r if f[2])
     if qjl_keys and enc_s >= dec_s:
-        # With QJL key pages the encode call is dominated by qjl_keys_kernel, the
-        # sketch z = sign(S r) as a float32 matrix-core product (2 x 128 x 128
-        # flops per key).  Its own duration is not separable from the call's
-        # encode_pages_kernel with events around the call, so the rate is a
-        # lower bound: sketch flops / whole call time.
+        # With QJL key pages the encode call is dominated by qjl_quad_kernel,
+        # whose contraction is the sketch z = sign(S r), 2 x 128 x 128 flops per
+        # key at float32 accuracy, executed as three float16 products (hi/lo
+        # split of both operands) on the matrix cores.  achieved/peak take the
+        # float32 flops against the float32 matrix peak; the executed float16
+        # flops (3x) against the float16 peak are given beside them.  Its own
+        # duration is not separable from the call's encode_pages_kernel with
+        # events around the call, so the rates are lower bounds: flops / whole
+        # call time.
         flops = qjl_keys * 2.0 * 128 * 128 / w.n_layers
         tflops = flops / per_launch_s / 1e12
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": FP32_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": None,
-                "kernel": "qjl_keys_kernel", "flops_per_launch": int(flops),
+                "kernel": "qjl_quad_kernel", "flops_per_launch": int(flops),
                 "launch_us": round(per_launch_s * 1e6, 2),
-                "timed": "whole tq_encode_kv call (qjl_keys_kernel + encode_pages_kernel): lower bound",
+                "executed": "3 float16 products per float32 product (v_mfma_f32_16x16x32_f16)",
+                "fp16_executed_tflops": round(3 * tflops, 2), "fp16_peak": FP16_MFMA_PEAK_TFLOPS,
+                "fp16_frac": round(3 * tflops / FP16_MFMA_PEAK_TFLOPS, 4),
+                "timed": "whole tq_encode_kv call (qjl_quad_kernel + encode_pages_kernel): lower bound",
                 "hbm_gbs_of_call": round(achieved, 1)}
     line = {
         "metric": METRIC, "value": round(dec_gbs, 1), "unit": "GB/s", "n_gpus": 1,
