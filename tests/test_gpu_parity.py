@@ -28,9 +28,10 @@ def _np(x):
 
 
 def run_case(w, layers, dev, units=None, n_tokens=None, dequant=True, chunks=None, tally=None,
-             query_dtype=None, layer_kw=None):
+             query_dtype=None, layer_kw=None, qjl_s=None):
     """Encode + decode every listed layer of workload w on the GPU; compare the
-    listed units (all by default) with the oracle."""
+    listed units (all by default) with the oracle.  ``qjl_s`` replaces the
+    seeded QJL matrix of layers with QJL pages."""
     import kv_cache_vector_srht_amd as tq
     t = tally or Tally()
     G = w.n_q_heads // w.n_kv_heads
@@ -38,7 +39,7 @@ def run_case(w, layers, dev, units=None, n_tokens=None, dequant=True, chunks=Non
         fm = w.formats[l]
         has_qjl = any(f[2] for row in fm for r in row for f in r)
         signs = W.rotation_signs(W.ROTATION_SEED, l)
-        S = W.qjl_matrix(W.ROTATION_SEED, l) if has_qjl else None
+        S = (qjl_s if qjl_s is not None else W.qjl_matrix(W.ROTATION_SEED, l)) if has_qjl else None
         if layer_kw is None:
             layer = tq.Layer(signs, dev, S, **layer_args(w.k_codebook, w.v_codebook))
         else:
@@ -146,6 +147,25 @@ def test_gqa_groups_qjl(dev, G):
 
 def test_fp32_inputs_and_fp32_query(dev):
     run_case(_all_bits_workload(dtype="float32", pages=10), [0], dev, query_dtype=torch.float32)
+
+
+def test_fp32_inputs_with_qjl(dev):
+    # float32 rows into the QJL key kernel (its second input instantiation)
+    run_case(_all_bits_workload(dtype="float32", pages=10, qjl=True), [0], dev, query_dtype=torch.float32)
+
+
+def test_qjl_matrix_rows_of_any_scale(dev):
+    # the sketch's signs do not depend on the scale of S's rows; the key kernel
+    # rescales each row of S D H D before splitting it into float16 parts, so
+    # rows far outside float16's range, tiny rows and a zero row (every sign +)
+    # must all match the oracle
+    S = W.qjl_matrix(W.ROTATION_SEED, 0).astype(np.float64)
+    scale = np.ones(S.shape[0])
+    scale[0::16] = 4e3      # S D H D entries past float16's largest value
+    scale[3::7] = 1e-6      # entries in float16's subnormal range
+    scale[9] = 0.0
+    S = (S * scale[:, None]).astype(np.float32)
+    run_case(_all_bits_workload(pages=8, qjl=True), [0], dev, qjl_s=S)
 
 
 def test_short_and_empty_sessions(dev):
