@@ -7,8 +7,7 @@
 // packed keys and values of every page without a QJL residual.
 // The keys of QJL pages (codes, norm, and the signs of S r for r = x - xhat,
 // "TurboMOQ", QJL residual correction, the sketch on the matrix cores) come
-// from qjl_quad_kernel (four lanes per vector) for scalar codebooks and from
-// qjl_keys_kernel (one lane per vector) for PolarQuant keys.
+// from qjl_quad_kernel (four lanes per vector).
 #include <algorithm>
 #include <atomic>
 
@@ -37,122 +36,6 @@ struct EncodeArgs {
   const float* qjl_s;
   int k_polar, v_polar;   // PolarQuant parts (at most 4 bits wide)
 };
-
-// PolarQuant keys of QJL pages: the per-token encoder (lane = token) writes codes and norm
-// and leaves the residual r in registers; the sign sketch z = sign(S r) of the
-// page's 64 keys is then one product [64 tokens x 128] . [128 x 128] on the
-// float32 matrix cores (v_mfma_f32_32x32x2f32, exact float32 products).
-// Persistent: kQjlBlocks workgroups of kQjlWaves waves stride over the call's
-// (page, KV head, session) items, one page per wave at a time; S sits in LDS
-// once per workgroup, laid out for the B operand:
-//   S[i][j] at ((j / 4 * 2 + j % 2) * 128 + i) * 2 + (j / 2) % 2,
-// so that lane (h = lane / 32, n = lane % 32) of column block c reads the B
-// values of K-steps 2kk and 2kk + 1 (coordinates 4kk + h and 4kk + 2 + h of
-// sketch row 32c + n) as one float2.  A operands come from the lanes' own
-// residuals: permlane32_swap of (r[2k], r[2k + 1]) gives tile 0's operand
-// (tokens 0-31: lane l < 32 holds r[l][2k], lane l >= 32 r[l - 32][2k + 1]) and
-// tile 1's (tokens 32-63).  Accumulator v of lane l holds row
-// 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32, so the ballot of its sign is
-// the sketch dword c of two tokens (low half: that row; high half: row + 4).
-constexpr int kQjlWaves = 4;
-constexpr int kQjlBlocksPerCU = 2;   // 80 KB of LDS each
-typedef float mfma_acc16 __attribute__((ext_vector_type(16)));
-
-// Launched for PolarQuant keys; scalar keys take qjl_quad_kernel (below).
-__global__ __launch_bounds__(64 * kQjlWaves) void qjl_keys_kernel(EncodeArgs a, const uint64_t* __restrict__ pages,
-                                                                 int n_pages) {
-  __shared__ float st[D * D];
-  __shared__ float lds_thr[kQjlWaves][256];
-  __shared__ float lds_cent[kQjlWaves][256];
-  __shared__ float2 lds_pair[kQjlWaves][256];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < D * D; e += blockDim.x) {
-    const int i = e >> 7, j = e & (D - 1);
-    st[(((j >> 2) * 2 + (j & 1)) * D + i) * 2 + ((j >> 1) & 1)] = a.qjl_s[e];
-  }
-  __syncthreads();
-  uint32_t m[4];
-#pragma clang loop unroll(full)
-  for (int w = 0; w < 4; ++w) m[w] = a.sign_mask[w];
-  const int h_half = lane >> 5, n_col = lane & 31;
-  // which accumulator and ballot half hold this lane's token (lane = token)
-  const int tt = lane & 31;
-  const int my_v = 4 * (tt >> 3) + (tt & 3), my_half = (tt >> 2) & 1, my_tile = lane >> 5;
-
-  const int total = n_pages * a.n_kv_heads * a.n_sessions;
-  for (int item = blockIdx.x * kQjlWaves + wave; item < total; item += gridDim.x * kQjlWaves) {
-    const int pgi = item % n_pages, rest = item / n_pages;
-    const int h = rest % a.n_kv_heads, b = rest / a.n_kv_heads;
-    const int pg = a.page0 + pgi;
-    const uint64_t desc = pages[((size_t)b * a.n_kv_heads + h) * a.max_pages + pg];
-    if (!(desc & TQ_PAGE_PRESENT)) continue;    // flagged by encode_pages_kernel
-    const PageDesc pd = read_desc(desc);
-    const int kb = pd.kb, vb = pd.vb;
-    const bool qjl = pd.qjl;
-    const bool bad_fmt = kb == 0 ? (vb != 0 || qjl) : (kb > 8 || vb < 1 || vb > 8);
-    if (!qjl || bad_fmt || pd.off + page_size_dev(kb, vb, qjl) > a.pool_bytes) continue;
-    const int t_first = pg * PT;
-    if (max(t_first, a.tok0) != t_first || min(t_first + PT, a.tok0 + a.ntok) != t_first + PT) continue;
-    const bool polar = a.k_polar;
-    const int shift = polar ? polar_shift_of(a.k_table) : 0;
-    if (polar && !polar_width_ok(kb, shift)) continue;   // refused (and flagged) by encode_pages_kernel
-    char* page = a.pool + pd.off;
-    // this wave's quantiser tables for the key width
-    wave_lds_sync();
-    stage_token_tables(a.k_table, kb, polar, shift, lane, 64, lds_thr[wave], lds_cent[wave], lds_pair[wave]);
-    float x[D];
-    const size_t base = (size_t)b * a.sb + (size_t)h * a.sh;
-    load_row(a.k, a.dtype, base + (size_t)(t_first + lane - a.tok0) * a.st, x);
-    wave_lds_sync();
-    float n;
-    float* thr = lds_thr[wave];
-    float* cent = lds_cent[wave];
-    float2* pair = lds_pair[wave];
-    switch (kb) {
-      case 1: n = encode_packed<0, 1>(page, lane, x, m, thr, cent, nullptr, polar, pair, shift); break;
-      case 2: n = encode_packed<0, 2>(page, lane, x, m, thr, cent, nullptr, polar, pair, shift); break;
-      case 3: n = encode_packed<0, 3>(page, lane, x, m, thr, cent, nullptr, polar, pair, shift); break;
-      case 4: n = encode_packed<0, 4>(page, lane, x, m, thr, cent, nullptr, polar, pair, shift); break;
-      case 5: n = encode_packed<0, 5>(page, lane, x, m, thr, cent, nullptr); break;
-      case 6: n = encode_packed<0, 6>(page, lane, x, m, thr, cent, nullptr); break;
-      case 7: n = encode_packed<0, 7>(page, lane, x, m, thr, cent, nullptr); break;
-      default: n = encode_packed<0, 8>(page, lane, x, m, thr, cent, nullptr); break;
-    }
-    const float gamma = qjl_residual(x, m, n);
-    // A operands in place: x[2k] <- tile 0's, x[2k + 1] <- tile 1's
-#pragma clang loop unroll(full)
-    for (int k = 0; k < D / 2; ++k) {
-      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[2 * k]), __float_as_uint(x[2 * k + 1]),
-                                                      false, false);
-      x[2 * k] = __uint_as_float(r[0]);
-      x[2 * k + 1] = __uint_as_float(r[1]);
-    }
-    char* qbase = page + 1024 * kb + 256;
-    // one column block (sketch dword c of every token) at a time
-#pragma clang loop unroll(disable)
-    for (int c = 0; c < 4; ++c) {
-      mfma_acc16 acc0 = {}, acc1 = {};
-      const float2* bsrc = reinterpret_cast<const float2*>(st) + h_half * D + 32 * c + n_col;
-#pragma clang loop unroll(full)
-      for (int kk = 0; kk < D / 4; ++kk) {
-        const float2 bb = bsrc[kk * 2 * D];
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(x[4 * kk], bb.x, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(x[4 * kk + 1], bb.x, acc1, 0, 0, 0);
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(x[4 * kk + 2], bb.y, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(x[4 * kk + 3], bb.y, acc1, 0, 0, 0);
-      }
-      uint32_t word = 0;
-#pragma clang loop unroll(full)
-      for (int v = 0; v < 16; ++v) {
-        const uint64_t b0 = __ballot(acc0[v] >= 0.f), b1 = __ballot(acc1[v] >= 0.f);
-        const uint64_t bt = my_tile ? b1 : b0;
-        if (my_v == v) word = (uint32_t)(bt >> (32 * my_half));
-      }
-      reinterpret_cast<uint32_t*>(qbase)[4 * lane + c] = word;
-    }
-    reinterpret_cast<float*>(qbase + 1024)[lane] = gamma;
-  }
-}
 
 // ------------------------------------------------------- encode (quad lanes)
 // One 256-thread block per (range of pages, KV head, session), keys and values.
@@ -659,9 +542,10 @@ __global__ __launch_bounds__(kEncodeBlock) void encode_pages_kernel(EncodeArgs a
 
 
 // ------------------------------------------------- QJL keys (quad lanes)
-// Keys of QJL pages with scalar codebooks: the four-lanes-per-vector encoder
-// of encode_pages_kernel (16 tokens per wave and pass, four passes per page),
-// and the sign sketch in the rotated domain on the matrix cores.  The
+// Keys of QJL pages: the four-lanes-per-vector encoder of encode_pages_kernel
+// (16 tokens per wave and pass, four passes per page; PolarQuant keys in their
+// own instantiation), and the sign sketch in the rotated domain on the matrix
+// cores.  The
 // residual r = x - xhat = (||x|| / d) D H D (u - c) ("TurboMOQ", QJL residual
 // correction), so S r = (||x|| / d) S' (u - c) with S' = S D H D: the signs
 // of S r are those of S' v for v = f (u - c), any f > 0, when ||x|| > 0, and
@@ -710,6 +594,29 @@ __device__ __forceinline__ void quantize_residual(float (&x)[32], float inv, uin
   }
 }
 
+// PolarQuant (B <= 4): slots 2m, 2m + 1 hold a coordinate pair; its pair field
+// F (polar_pair_field) goes to the two code bytes, low B bits first, and x
+// keeps u minus the pair's reconstruction pair[F].
+template <int B>
+__device__ __forceinline__ void quantize_residual_polar(float (&x)[32], float inv, uint32_t fl, const float* thr,
+                                                        const float2* pair, int shift, uint32_t (&cb)[8],
+                                                        float& e2) {
+#pragma clang loop unroll(full)
+  for (int m = 0; m < 16; ++m) {
+    const int s0 = 2 * m, s1 = 2 * m + 1;
+    const float u0 = flip_if(x[s0] * inv, (fl >> s0) & 1u), u1 = flip_if(x[s1] * inv, (fl >> s1) & 1u);
+    const uint32_t F = polar_pair_field<B>(u0, u1, thr, shift);
+    cb[s0 >> 2] |= (F & ((1u << B) - 1u)) << (8 * (s0 & 3));
+    cb[s1 >> 2] |= (F >> B) << (8 * (s1 & 3));
+    const float2 p = pair[F];
+    const float r0 = u0 - p.x, r1 = u1 - p.y;
+    e2 = fmaf(r0, r0, e2);
+    e2 = fmaf(r1, r1, e2);
+    x[s0] = r0;
+    x[s1] = r1;
+  }
+}
+
 // y = hi + lo in float16 (both rounded to nearest); two values per dword,
 // the lower slot in the low half.
 __device__ __forceinline__ void split_pair(float y0, float y1, uint32_t& hi, uint32_t& lo) {
@@ -721,7 +628,9 @@ __device__ __forceinline__ void split_pair(float y0, float y1, uint32_t& hi, uin
 
 __device__ __forceinline__ half8 as_half8(uint4 v) { return __builtin_bit_cast(half8, v); }
 
-template <int DT>
+// POLAR: the instantiation for PolarQuant keys (widths up to 4 bits, the pair
+// table in LDS as well).
+template <int DT, bool POLAR>
 __global__ __launch_bounds__(64 * kQjlQuadWaves) void qjl_quad_kernel(EncodeArgs a, const uint64_t* __restrict__ pages,
                                                                       int n_pages) {
   __shared__ uint4 sph[D * D / 8];
@@ -729,6 +638,7 @@ __global__ __launch_bounds__(64 * kQjlQuadWaves) void qjl_quad_kernel(EncodeArgs
   __shared__ uint32_t rows[kQjlQuadWaves][16 * kRowStride / 4];
   __shared__ float lds_thr[kQjlQuadWaves][256];
   __shared__ float lds_cent[kQjlQuadWaves][256];
+  __shared__ float2 lds_pair[kQjlQuadWaves][POLAR ? 256 : 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, e = lane & 3, mq = lane >> 2;
   const EncodeLane el = encode_lane(a.sign_mask, e);
   // S' rows: quad i / 4 rotates row i of S (all four lanes of a quad take the
@@ -771,7 +681,9 @@ __global__ __launch_bounds__(64 * kQjlQuadWaves) void qjl_quad_kernel(EncodeArgs
 
   float* thr = lds_thr[wave];
   float* cent = lds_cent[wave];
+  float2* pair = lds_pair[wave];
   uint32_t* rw = rows[wave];
+  const int shift = POLAR ? polar_shift_of(a.k_table) : 0;
   const int src = 4 * (lane & 15) + (lane >> 4);     // the encoder lane of this lane's A operands
   const int vsel = lane & 3, gsh = 16 * ((lane >> 2) & 3);   // lanes 0-15: token = 4 (gsh / 16) + vsel
   int cur_kb = -1;
@@ -788,9 +700,10 @@ __global__ __launch_bounds__(64 * kQjlQuadWaves) void qjl_quad_kernel(EncodeArgs
     if (!pd.qjl || bad_fmt || pd.off + page_size_dev(kb, vb, true) > a.pool_bytes) continue;
     const int t_first = pg * PT;
     if (max(t_first, a.tok0) != t_first || min(t_first + PT, a.tok0 + a.ntok) != t_first + PT) continue;
+    if (POLAR && !polar_width_ok(kb, shift)) continue;   // refused (and flagged) by encode_pages_kernel
     if (kb != cur_kb) {
       wave_lds_sync();
-      stage_token_tables(a.k_table, kb, false, 0, lane, 64, thr, cent, nullptr);
+      stage_token_tables(a.k_table, kb, POLAR, shift, lane, 64, thr, cent, POLAR ? pair : nullptr);
       wave_lds_sync();
       cur_kb = kb;
     }
@@ -812,15 +725,24 @@ __global__ __launch_bounds__(64 * kQjlQuadWaves) void qjl_quad_kernel(EncodeArgs
 #pragma clang loop unroll(full)
       for (int i = 0; i < 8; ++i) cb[i] = 0;
       float e2 = 0.f;
-      switch (kb) {
-        case 1: quantize_residual<1>(x, inv, el.fl, thr, cent, cb, e2); break;
-        case 2: quantize_residual<2>(x, inv, el.fl, thr, cent, cb, e2); break;
-        case 3: quantize_residual<3>(x, inv, el.fl, thr, cent, cb, e2); break;
-        case 4: quantize_residual<4>(x, inv, el.fl, thr, cent, cb, e2); break;
-        case 5: quantize_residual<5>(x, inv, el.fl, thr, cent, cb, e2); break;
-        case 6: quantize_residual<6>(x, inv, el.fl, thr, cent, cb, e2); break;
-        case 7: quantize_residual<7>(x, inv, el.fl, thr, cent, cb, e2); break;
-        default: quantize_residual<8>(x, inv, el.fl, thr, cent, cb, e2); break;
+      if constexpr (POLAR) {
+        switch (kb) {
+          case 1: quantize_residual_polar<1>(x, inv, el.fl, thr, pair, shift, cb, e2); break;
+          case 2: quantize_residual_polar<2>(x, inv, el.fl, thr, pair, shift, cb, e2); break;
+          case 3: quantize_residual_polar<3>(x, inv, el.fl, thr, pair, shift, cb, e2); break;
+          default: quantize_residual_polar<4>(x, inv, el.fl, thr, pair, shift, cb, e2); break;
+        }
+      } else {
+        switch (kb) {
+          case 1: quantize_residual<1>(x, inv, el.fl, thr, cent, cb, e2); break;
+          case 2: quantize_residual<2>(x, inv, el.fl, thr, cent, cb, e2); break;
+          case 3: quantize_residual<3>(x, inv, el.fl, thr, cent, cb, e2); break;
+          case 4: quantize_residual<4>(x, inv, el.fl, thr, cent, cb, e2); break;
+          case 5: quantize_residual<5>(x, inv, el.fl, thr, cent, cb, e2); break;
+          case 6: quantize_residual<6>(x, inv, el.fl, thr, cent, cb, e2); break;
+          case 7: quantize_residual<7>(x, inv, el.fl, thr, cent, cb, e2); break;
+          default: quantize_residual<8>(x, inv, el.fl, thr, cent, cb, e2); break;
+        }
       }
       e2 += quad_swap(e2, 1);
       e2 += quad_swap(e2, 2);
@@ -981,25 +903,24 @@ int tq_encode_kv(const tq_layer* layer, const tq_cache* cache, const tq_kv_input
   if (st2) return st2;
   if (layer->qjl_s) {
     // keys of QJL pages: codes, norm and sign sketch, a page per wave on
-    // persistent workgroups (as many as the items need: scalar keys one
-    // 8-wave workgroup per CU, PolarQuant keys at most two 4-wave ones)
+    // persistent workgroups (as many as the items need, one 8-wave workgroup
+    // per CU)
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) cus = compute_units(dev);
     const int64_t items = (int64_t)n_pages * cache->n_kv_heads * cache->n_sessions;
-    if (a.k_polar) {
-      const int64_t want = (items + kQjlWaves - 1) / kQjlWaves;
-      const int blocks = (int)std::min<int64_t>(want, (int64_t)cus * kQjlBlocksPerCU);
-      hipLaunchKernelGGL(qjl_keys_kernel, dim3(blocks), dim3(64 * kQjlWaves), 0, (hipStream_t)stream, a,
-                         cache->pages, n_pages);
-    } else {
-      const int64_t want = (items + kQjlQuadWaves - 1) / kQjlQuadWaves;
-      const int blocks = (int)std::min<int64_t>(want, (int64_t)cus);
-      if (a.dtype == TQ_DTYPE_F16)
-        hipLaunchKernelGGL(qjl_quad_kernel<TQ_DTYPE_F16>, dim3(blocks), dim3(64 * kQjlQuadWaves), 0,
-                           (hipStream_t)stream, a, cache->pages, n_pages);
+    const int64_t want = (items + kQjlQuadWaves - 1) / kQjlQuadWaves;
+    const dim3 grid_q((unsigned)std::min<int64_t>(want, (int64_t)cus)), block_q(64 * kQjlQuadWaves);
+    const hipStream_t sq = (hipStream_t)stream;
+    if (a.dtype == TQ_DTYPE_F16) {
+      if (a.k_polar)
+        hipLaunchKernelGGL((qjl_quad_kernel<TQ_DTYPE_F16, true>), grid_q, block_q, 0, sq, a, cache->pages, n_pages);
       else
-        hipLaunchKernelGGL(qjl_quad_kernel<TQ_DTYPE_F32>, dim3(blocks), dim3(64 * kQjlQuadWaves), 0,
-                           (hipStream_t)stream, a, cache->pages, n_pages);
+        hipLaunchKernelGGL((qjl_quad_kernel<TQ_DTYPE_F16, false>), grid_q, block_q, 0, sq, a, cache->pages, n_pages);
+    } else {
+      if (a.k_polar)
+        hipLaunchKernelGGL((qjl_quad_kernel<TQ_DTYPE_F32, true>), grid_q, block_q, 0, sq, a, cache->pages, n_pages);
+      else
+        hipLaunchKernelGGL((qjl_quad_kernel<TQ_DTYPE_F32, false>), grid_q, block_q, 0, sq, a, cache->pages, n_pages);
     }
     st2 = launch_status("encode QJL keys");
   }

@@ -133,14 +133,34 @@ __device__ __forceinline__ void stage_token_tables(const float* table, int B, bo
 // bits); the pair field F = radius | angle << RB goes to emit(2i, F's low B
 // bits) and emit(2i+1, its high B bits).  On return x holds u minus the
 // pair's reconstruction pair[F].
-template <int B, class Emit>
-__device__ __forceinline__ float rotate_quantize_polar(float (&x)[D], const uint32_t (&m)[4],
-                                                       const float* thr, const float2* pair, Emit emit,
-                                                       int shift) {
+// The pair field of one coordinate pair u = (u0, u1) at page width B and
+// angle shift `shift`: F = radius | angle << (B - shift) as above, the radius
+// boundaries in `thr` padded with +inf to 255 entries.
+template <int B>
+__device__ __forceinline__ uint32_t polar_pair_field(float u0, float u1, const float* thr, int shift) {
   const int RB = B - shift, L = 1 << (B + shift);
   constexpr int kMaxRB = B + 3 < 8 ? B + 3 : 8;   // the radius width at shift -3
   constexpr float kPi = 3.14159265358979323846f;
   const float kSectors = (float)L / (2.0f * 3.14159265358979323846f);
+  const float r = sqrtf(fmaf(u0, u0, u1 * u1));
+  // a zero pair takes the angle atan2(+0, +0) = 0, whatever its zeros' signs
+  const float th = (u0 == 0.f && u1 == 0.f) ? 0.f : atan2f(u1, u0);
+  // #{boundaries <= r}: a binary search of kMaxRB steps over the 2^RB - 1 of
+  // them and the +inf padding behind them (the same steps at every shift, so
+  // that the pair loop unrolls and x stays in registers); the clamp keeps an
+  // r of +inf at the top level
+  uint32_t rc = 0;
+#pragma clang loop unroll(full)
+  for (int st = 1 << (kMaxRB - 1); st >= 1; st >>= 1) rc += (r >= thr[rc + st - 1]) ? (uint32_t)st : 0u;
+  rc = min(rc, (uint32_t)((1 << RB) - 1));
+  const uint32_t tc = (uint32_t)(int)floorf((th + kPi) * kSectors) & (uint32_t)(L - 1);
+  return rc | (tc << RB);
+}
+
+template <int B, class Emit>
+__device__ __forceinline__ float rotate_quantize_polar(float (&x)[D], const uint32_t (&m)[4],
+                                                       const float* thr, const float2* pair, Emit emit,
+                                                       int shift) {
   float ss = 0.f;
 #pragma clang loop unroll(full)
   for (int j = 0; j < D; ++j) ss = fmaf(x[j], x[j], ss);
@@ -158,19 +178,7 @@ __device__ __forceinline__ float rotate_quantize_polar(float (&x)[D], const uint
 #pragma clang loop unroll(full)
   for (int i = 0; i < D / 2; ++i) {
     const float u0 = x[2 * i], u1 = x[2 * i + 1];
-    const float r = sqrtf(fmaf(u0, u0, u1 * u1));
-    // a zero pair takes the angle atan2(+0, +0) = 0, whatever its zeros' signs
-    const float th = (u0 == 0.f && u1 == 0.f) ? 0.f : atan2f(u1, u0);
-    // #{boundaries <= r}: a binary search of kMaxRB steps over the 2^RB - 1 of
-    // them and the +inf padding behind them (the same steps at every shift, so
-    // that the pair loop unrolls and x stays in registers); the clamp keeps an
-    // r of +inf at the top level
-    uint32_t rc = 0;
-#pragma clang loop unroll(full)
-    for (int st = 1 << (kMaxRB - 1); st >= 1; st >>= 1) rc += (r >= thr[rc + st - 1]) ? (uint32_t)st : 0u;
-    rc = min(rc, (uint32_t)((1 << RB) - 1));
-    const uint32_t tc = (uint32_t)(int)floorf((th + kPi) * kSectors) & (uint32_t)(L - 1);
-    const uint32_t F = rc | (tc << RB);
+    const uint32_t F = polar_pair_field<B>(u0, u1, thr, shift);
     emit(2 * i, F & ((1u << B) - 1u));
     emit(2 * i + 1, F >> B);
     const float2 p = pair[F];
