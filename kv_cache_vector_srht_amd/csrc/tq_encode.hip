@@ -190,7 +190,8 @@ __device__ __forceinline__ float rotate_loaded(const Quarter<DT>& qv, int e, con
     // slots 2i, 2i+1 are the two halves of one fp16 pair: the first butterfly
     // (slot bit 0) reads them straight from the pair with mixed-precision
     // multiply-adds (lo + 1.0 * hi, lo - 1.0 * hi), so no conversion is issued;
-    // the norm's squares are mixed-precision too
+    // the pair's two squares enter the norm as one fp16 dot product with a
+    // float32 accumulator (fp16 products are exact in float32)
 #pragma clang loop unroll(full)
     for (int c = 0; c < 4; ++c) {
       const uint4 w = qv.w[c];
@@ -198,9 +199,9 @@ __device__ __forceinline__ float rotate_loaded(const Quarter<DT>& qv, int e, con
                               w.z ^ el.hmask[4 * c + 2], w.w ^ el.hmask[4 * c + 3]};
 #pragma clang loop unroll(full)
       for (int kk = 0; kk < 4; ++kk) {
-        const float2 f = __half22float2(*reinterpret_cast<const __half2*>(&ww[kk]));
-        ss = fmaf(f.x, f.x, ss);
-        ss = fmaf(f.y, f.y, ss);
+        typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+        const h2v hv = __builtin_bit_cast(h2v, ww[kk]);
+        ss = __builtin_amdgcn_fdot2(hv, hv, ss, false);
         float sum, dif;
         asm("v_fma_mix_f32 %0, %1, 1.0, %1 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(sum) : "v"(ww[kk]));
         asm("v_fma_mix_f32 %0, %1, 1.0, -%1 op_sel:[0,0,1] op_sel_hi:[1,0,1]"

@@ -282,3 +282,36 @@ def test_decode_zero_query(dev):
         t.worst_attn = max(t.worst_attn, float(err.max()))
         compare_attention(rows, np.zeros((G, 128)), Kh, Vh, t)
     t.check()
+
+
+@pytest.mark.parametrize("qjl", [False, True])
+def test_subnormal_rows_bulk_encoder(dev, qjl):
+    """Rows whose fp16 values all lie in fp16's subnormal range (multiples of
+    2^-24 below 2^-14): their norms and codes follow the oracle under the usual
+    allowance, so no step of the encoders (the norm's products included)
+    flushes them to zero."""
+    import kv_cache_vector_srht_amd as tq
+    fm = _formats_all_widths(qjl)
+    P = len(fm[0][0])
+    w = W.make_workload(2, {"n_tokens": 64 * P, "batch": 1, "n_kv_heads": 2, "n_q_heads": 8, "sink_tokens": 0})
+    signs, S = W.rotation_signs(42, 0), W.qjl_matrix(42, 0)
+    layer = tq.Layer(signs, dev, S if qjl else None)
+    cache = tq.Cache(fm, [w.n_tokens], dev)
+    k, v = W.make_kv(w, 0, device=dev)
+    rng = np.random.default_rng(7)
+    for p in range(P):
+        for x in (k, v):
+            sub = rng.integers(-1000, 1001, size=(1, 2, N_SPECIAL, 128)).astype(np.float64) * 2.0 ** -24
+            x[:, :, 64 * p:64 * p + N_SPECIAL] = torch.as_tensor(sub, dtype=x.dtype, device=dev)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    print(f"bulk encode of subnormal rows, qjl {qjl}: {P} pages x 2 heads", flush=True)
+    tq.encode_kv(layer, cache, k, v, error_flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 0
+    kh, vh = _np(k).astype(np.float64), _np(v).astype(np.float64)
+    assert np.all(np.abs(kh[0, :, :N_SPECIAL]) < 2.0 ** -14) and np.any(kh[0, :, :N_SPECIAL] != 0)
+    pool = _np(cache.pool)
+    t = Tally()
+    for h in range(2):
+        compare_unit_full(pool, cache.offsets, 0, h, kh[0, h], vh[0, h], fm[0][h], signs, S if qjl else None, t)
+    t.check()
