@@ -272,13 +272,15 @@ __device__ __forceinline__ float encode_quarter(const void* src, size_t row_off,
       const float u0 = flip_if(x[s0], ((el.dl >> s0) & 1u) ^ lsign) * inv;
       const float u1 = flip_if(x[s1], ((el.dl >> s1) & 1u) ^ lsign) * inv;
       const float r = sqrtf(fmaf(u0, u0, u1 * u1));
+      // the radius in the grid's coordinate, compared there with the boundary
+      const float tr = fmaf(r, lut.S, lut.O);
       uint32_t bin;
       if (lut.nb == kLutByteBins)
-        bin = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(r, lut.S, lut.O), 0, 0u);
+        bin = __builtin_amdgcn_cvt_pk_u8_f32(tr, 0, 0u);
       else
-        bin = (uint32_t)(int)__builtin_amdgcn_fmed3f(fmaf(r, lut.S, lut.O), 0.f, lut.fmax);
+        bin = (uint32_t)(int)__builtin_amdgcn_fmed3f(tr, 0.f, lut.fmax);
       const uint2 en = ent[bin];
-      const uint32_t rc = en.x + (r >= __uint_as_float(en.y) ? 1u : 0u);
+      const uint32_t rc = en.x + (tr >= __uint_as_float(en.y) ? 1u : 0u);
       uint32_t tc;
       if (L == 2) {
         tc = u1 >= 0.f ? 1u : 0u;
@@ -315,26 +317,30 @@ __device__ __forceinline__ float encode_quarter(const void* src, size_t row_off,
   // u carries its sign (outer D times the lane's sign) before the lookup, so
   // that an exact tie u = t_k counts t_k on every coordinate (#{t_k <= u}),
   // as for unflipped ones: a code flip after quantising would count it on
-  // flipped coordinates only (L - 1 - #{t_k <= -u} = #{t_k < u}).
+  // flipped coordinates only (L - 1 - #{t_k <= -u} = #{t_k < u}).  The value
+  // goes to the grid's coordinate g = u S + O as one fma of the signed slot
+  // with S / ||x||, and the grid's boundaries are stored in that coordinate;
+  // a zero row (every g = O) ties with the boundary 0 exactly.
+  const float sinv = lut.S * inv;
   if (lut.nb == kLutByteBins) {
-    // 256-bin grid: the bin is u S + O (O carries the -1/2) rounded and
-    // saturated to a byte by one conversion
+    // 256-bin grid: the bin is g (O carries the -1/2) rounded and saturated
+    // to a byte by one conversion
 #pragma clang loop unroll(full)
     for (int s = 0; s < 32; ++s) {
-      const float u = flip_if(x[s] * inv, (el.fl >> s) & 1u);
-      const uint32_t bin = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(u, lut.S, lut.O), 0, 0u);
+      const float g = fmaf(flip_if(x[s], (el.fl >> s) & 1u), sinv, lut.O);
+      const uint32_t bin = __builtin_amdgcn_cvt_pk_u8_f32(g, 0, 0u);
       const uint2 en = ent[bin];
-      const uint32_t c = en.x + (u >= __uint_as_float(en.y) ? 1u : 0u);
+      const uint32_t c = en.x + (g >= __uint_as_float(en.y) ? 1u : 0u);
       cb[s >> 2] |= c << (8 * (s & 3));
     }
   } else {
 #pragma clang loop unroll(full)
     for (int s = 0; s < 32; ++s) {
-      const float u = flip_if(x[s] * inv, (el.fl >> s) & 1u);
-      // bin = clamp(floor(u S + O), 0, nb - 1), clamped in float (one med3)
-      const int bin = (int)__builtin_amdgcn_fmed3f(fmaf(u, lut.S, lut.O), 0.f, lut.fmax);
+      const float g = fmaf(flip_if(x[s], (el.fl >> s) & 1u), sinv, lut.O);
+      // bin = clamp(floor(g), 0, nb - 1), clamped in float (one med3)
+      const int bin = (int)__builtin_amdgcn_fmed3f(g, 0.f, lut.fmax);
       const uint2 en = ent[bin];
-      const uint32_t c = en.x + (u >= __uint_as_float(en.y) ? 1u : 0u);
+      const uint32_t c = en.x + (g >= __uint_as_float(en.y) ? 1u : 0u);
       cb[s >> 2] |= c << (8 * (s & 3));
     }
   }

@@ -343,7 +343,10 @@ static int build_grids(float* table, int max_bits = 8) {
     // Quantiser lookup grid: bins of width h over [-T, T) with
     // idx = floor(u * S + O), S = 1/h, O = T/h.  Bin i, widened by h/4 on each
     // side, holds at most one boundary; base = boundaries below the widened bin.
-    // (The widening makes an index off by one at a bin edge harmless.)
+    // (The widening makes an index off by one at a bin edge harmless.)  The
+    // boundary is stored in the grid's own coordinate, fma(t, S, O) rounded
+    // once to float32, so that the encoder compares its fma(u, S, O) with it
+    // (an exact tie u = t stays a tie: both sides round the same expression).
     const int nt = (1 << b) - 1;
     double gap = 2.0, tmax = 0.0;
     for (int k = 0; k + 1 < nt; ++k) gap = std::min(gap, (double)t[k + 1] - (double)t[k]);
@@ -367,6 +370,7 @@ static int build_grids(float* table, int max_bits = 8) {
     hdr[1] = byte_grid ? O - 0.5f : O;
     reinterpret_cast<uint32_t*>(hdr)[2] = (uint32_t)nb;
     reinterpret_cast<uint32_t*>(hdr)[3] = (uint32_t)next;
+    const float Oh = hdr[1];
     for (int i = 0; i < nb; ++i) {
       const long double lo = ((long double)i - (long double)O) / (long double)S - 0.25L / (long double)S;
       const long double hi = ((long double)i + 1.0L - (long double)O) / (long double)S + 0.25L / (long double)S;
@@ -375,7 +379,7 @@ static int build_grids(float* table, int max_bits = 8) {
       int inside = 0;
       for (int k = 0; k < nt; ++k) {
         if ((long double)t[k] < lo) ++base;
-        else if ((long double)t[k] < hi) { thr = t[k]; ++inside; }
+        else if ((long double)t[k] < hi) { thr = fmaf(t[k], S, Oh); ++inside; }
       }
       if (inside > 1) return fail(TQ_ERR_UNSUPPORTED, "lookup bin with two boundaries (bits %d)", b);
       words[next + 2 * i] = base;

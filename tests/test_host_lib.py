@@ -97,8 +97,9 @@ def test_codebook_table_layout(L, kind, fit_samples):
         else:
             c = O.codebook(b, kind)[0]
             assert np.array_equal(pt[:, 0], c[lo]) and np.array_equal(pt[:, 1], c[hi]), b
-    # lookup grids: code(u) = base + [u >= boundary] at bin floor(u S + O), or
-    # at the nearest integer for 256-bin grids (their O carries the -1/2)
+    # lookup grids: with g = fl32(u S + O) (one fma), code(u) = base + [g >=
+    # boundary] at bin floor(g), or at the nearest integer for 256-bin grids
+    # (their O carries the -1/2); the boundary is stored as fl32(t S + O)
     words = tab.view(np.uint32)
     rng = np.random.default_rng(0)
     for b in range(1, 5 if kind is tq.POLAR or (isinstance(kind, int) and kind == tq.POLAR) else 9):
@@ -112,14 +113,26 @@ def test_codebook_table_layout(L, kind, fit_samples):
                             t, np.nextafter(t, np.float32(-np.inf)), np.nextafter(t, np.float32(np.inf)),
                             edges, np.nextafter(edges, np.float32(-np.inf)), np.nextafter(edges, np.float32(np.inf)),
                             np.float32([-50, 50, 0, -0.0, -11.32, 11.32])]).astype(np.float32)
-        x = (u.astype(np.float64) * np.float64(gS) + np.float64(gO)).astype(np.float32).astype(np.float64)
+        # one rounding of the exact u S + O, as the device's fma
+        x = (u.astype(np.longdouble) * np.longdouble(gS) + np.longdouble(gO)).astype(np.float32)
+        xb = x.astype(np.float64)
         if nb == 256:   # byte grid: round half to even, saturate to [0, 255]
-            bins = np.clip(np.rint(x), 0, 255).astype(np.int64)
+            bins = np.clip(np.rint(xb), 0, 255).astype(np.int64)
         else:
-            bins = np.clip(np.trunc(x).astype(np.int64), 0, nb - 1)
-        got = ent[bins, 0] + (u >= ent[bins, 1].view(np.float32))
+            bins = np.clip(np.trunc(xb).astype(np.int64), 0, nb - 1)
+        got = ent[bins, 0] + (x >= ent[bins, 1].view(np.float32))
         want = np.searchsorted(t, u, side="right")
-        assert np.array_equal(got, want), b
+        # the stored boundary is the grid coordinate of t rounded the same way
+        nz = ent[:, 1].view(np.float32) < 1e38
+        tw = (t.astype(np.longdouble) * np.longdouble(gS) + np.longdouble(gO)).astype(np.float32)
+        assert np.all(np.isin(ent[nz, 1].view(np.float32), tw)), b
+        # exact on the boundaries themselves (a tie is a tie) and away from
+        # them; within 1e-6 of a boundary (the parity allowance) the rounding
+        # of g may take the neighbouring level
+        diff = got != want
+        assert not diff[np.isin(u, t)].any(), b
+        dist = np.min(np.abs(u[:, None].astype(np.float64) - t[None, :].astype(np.float64)), axis=1)
+        assert np.all(~diff | ((dist <= 1e-6) & (np.abs(got.astype(np.int64) - want) == 1))), b
 
 
 @pytest.mark.parametrize("shift", [-3, -1, 0, 1, 2, 3])
