@@ -323,6 +323,19 @@ def test_polar_keys_with_qjl_and_scalar_values(dev):
     run_case(w, [0], dev)
 
 
+def test_split_polar_keys_with_qjl_fp32_inputs(dev):
+    # float32 rows into the PolarQuant instantiation of the QJL key kernel, at
+    # an angle shift (key widths 2-4, the ones that carry it), scalar values
+    combos = [(kb, vb) for kb in range(2, 5) for vb in range(1, 5)]
+    pages = 1 + len(combos)
+    w = W.make_workload(2, {"n_tokens": 64 * pages, "batch": 1, "n_kv_heads": 2, "n_q_heads": 8,
+                            "sink_tokens": 0, "dtype": "float32"})
+    w.formats = [[[[W.packed(*combos[(p + 5 * h) % len(combos)], True) if p > 0 else W.FP16
+                    for p in range(pages)] for h in range(2)]]]
+    w.k_codebook, w.v_codebook = O.PolarSplit(-1), O.LLOYD_MAX
+    run_case(w, [0], dev, query_dtype=torch.float32)
+
+
 @pytest.mark.parametrize("k_shift,v_shift", [(1, -1), (2, 3), (-2, -3)])
 def test_polar_split_widths(dev, k_shift, v_shift):
     """PolarQuant with radius and angle widths of their own: every width pair
