@@ -336,6 +336,18 @@ size_t tq_cache_bytes(const uint64_t* host_pages, size_t n);
 const char* tq_status_string(int status);
 const char* tq_last_error(void);
 
+/* The device checks of a checked build (the library compiled with
+ * TQ_DEVICE_CHECKS=1, libtq_checked.so): the kernels verify their index
+ * invariants as they run, record a violated one as a bit, and clamp the index
+ * so that the access stays in bounds.  *flags receives the bits recorded since
+ * the last reset (1 encode lookup grid, 2 encode streams and code rows, 4 QJL
+ * key encoder LDS, 8 decode tables and weight rows, 16 decode descriptor and
+ * partial slots, 32 combine lists, 64 append and re-tier); reset != 0 clears
+ * them.  Synchronous: waits for the device's work.  A release build sets
+ * *flags = 0 and returns TQ_ERR_UNSUPPORTED; TQ_ERR_INVALID_ARG for a null
+ * flags. */
+int tq_device_checks(uint32_t* flags, int reset);
+
 /* ----------------------------------------------------------- device calls */
 
 /* Encodes tokens [tok0, tok0 + ntok) of every (session, KV head) into the
@@ -347,6 +359,17 @@ const char* tq_last_error(void);
  * order.  Keys of QJL pages also get their sign sketch and gamma. */
 int tq_encode_kv(const tq_layer* layer, const tq_cache* cache,
                  const tq_kv_input* in, void* stream);
+
+/* tq_encode_kv with its launch shape chosen by the caller, for checking that
+ * the result does not depend on it (the kernels' LDS reuse and barriers):
+ * pages_per_block = pages each workgroup of the bulk encoder takes in turn
+ * (1..16, 0 = the default 4), qjl_workgroups = the persistent workgroups of
+ * the QJL key encoder (0 = one per compute unit; more than the work needs are
+ * not launched).  The pages written are byte-identical for every shape.
+ * TQ_ERR_INVALID_ARG for a shape outside those ranges, else as tq_encode_kv. */
+int tq_encode_kv_shaped(const tq_layer* layer, const tq_cache* cache,
+                        const tq_kv_input* in, int pages_per_block,
+                        int qjl_workgroups, void* stream);
 
 /* One step of a decode loop ("TurboQuant-MLX v2.0", What's New > FP16
  * Attention Sinks and Dynamic Chunk Buffering: recent tokens stay fp16 until a

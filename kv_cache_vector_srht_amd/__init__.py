@@ -31,13 +31,17 @@ QJL_SCORE_SIGN = 1
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "lib", "libtq.so")
+# the same library built with TQ_DEVICE_CHECKS=1 (device index checks)
+CHECKED_LIB_PATH = os.path.join(_PKG, "lib", "libtq_checked.so")
 EXPORTS = ("tq_page_bytes", "tq_page_descriptor", "tq_build_codebook", "tq_codebook_table",
            "tq_layer_params", "tq_sign_mask", "tq_decode_workspace_bytes", "tq_cache_bytes",
            "tq_status_string", "tq_last_error", "tq_encode_kv", "tq_decode_attention",
            "tq_dequantize", "tq_append_kv", "tq_retier_pages", "tq_decode_attention_mass",
            "tq_fit_codebook", "tq_calibrated_table", "tq_decode_attention_noalloc",
-           "tq_decode_attention_token_mass", "tq_polar_table")
+           "tq_decode_attention_token_mass", "tq_polar_table", "tq_encode_kv_shaped",
+           "tq_device_checks")
 NOALLOC_SCRATCH_BYTES = 32 << 20     # TQ_NOALLOC_SCRATCH_BYTES
+ERR_UNSUPPORTED = -2                 # TQ_ERR_UNSUPPORTED
 
 
 class TQError(RuntimeError):
@@ -82,57 +86,97 @@ class tq_query(ctypes.Structure):
 _lib = None
 
 
+def _open(path: str) -> ctypes.CDLL:
+    """Loads a build of libtq and declares its calls' argument types."""
+    if not os.path.exists(path):
+        raise TQError(f"{path} is missing: build it with __graft_entry__.build() "
+                      "or python kv_cache_vector_srht_amd/build.py")
+    L = ctypes.CDLL(path)
+    L.tq_page_bytes.restype = ctypes.c_size_t
+    L.tq_page_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    L.tq_page_descriptor.restype = ctypes.c_uint64
+    L.tq_page_descriptor.argtypes = [ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    L.tq_build_codebook.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.tq_codebook_table.argtypes = [ctypes.c_int, ctypes.c_void_p]
+    L.tq_polar_table.argtypes = [ctypes.c_int, ctypes.c_void_p]
+    L.tq_fit_codebook.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                  ctypes.c_void_p, ctypes.c_void_p]
+    L.tq_calibrated_table.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    L.tq_layer_params.argtypes = [ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p, ctypes.c_void_p]
+    L.tq_sign_mask.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    L.tq_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.tq_decode_workspace_bytes.argtypes = [ctypes.POINTER(tq_cache), ctypes.c_int]
+    L.tq_cache_bytes.restype = ctypes.c_size_t
+    L.tq_cache_bytes.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    L.tq_status_string.restype = ctypes.c_char_p
+    L.tq_status_string.argtypes = [ctypes.c_int]
+    L.tq_last_error.restype = ctypes.c_char_p
+    L.tq_encode_kv.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
+                               ctypes.POINTER(tq_kv_input), ctypes.c_void_p]
+    L.tq_encode_kv_shaped.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
+                                      ctypes.POINTER(tq_kv_input), ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_void_p]
+    L.tq_device_checks.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    L.tq_decode_attention.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
+                                      ctypes.POINTER(tq_query), ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    L.tq_decode_attention_mass.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
+                                           ctypes.POINTER(tq_query), ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    L.tq_decode_attention_token_mass.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
+                                                 ctypes.POINTER(tq_query), ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    L.tq_decode_attention_noalloc.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
+                                              ctypes.POINTER(tq_query), ctypes.c_void_p, ctypes.c_void_p]
+    L.tq_append_kv.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
+                               ctypes.POINTER(tq_token_input), ctypes.c_void_p]
+    L.tq_retier_pages.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache), ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                  ctypes.c_void_p]
+    L.tq_dequantize.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache), ctypes.c_int,
+                                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                ctypes.c_void_p]
+    return L
+
+
 def lib() -> ctypes.CDLL:
     """The loaded libtq (raises TQError when it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise TQError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
-                          "or python kv_cache_vector_srht_amd/build.py")
-        L = ctypes.CDLL(LIB_PATH)
-        L.tq_page_bytes.restype = ctypes.c_size_t
-        L.tq_page_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
-        L.tq_page_descriptor.restype = ctypes.c_uint64
-        L.tq_page_descriptor.argtypes = [ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
-        L.tq_build_codebook.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-        L.tq_codebook_table.argtypes = [ctypes.c_int, ctypes.c_void_p]
-        L.tq_polar_table.argtypes = [ctypes.c_int, ctypes.c_void_p]
-        L.tq_fit_codebook.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
-                                      ctypes.c_void_p, ctypes.c_void_p]
-        L.tq_calibrated_table.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
-        L.tq_layer_params.argtypes = [ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                      ctypes.c_void_p, ctypes.c_void_p]
-        L.tq_sign_mask.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
-        L.tq_decode_workspace_bytes.restype = ctypes.c_size_t
-        L.tq_decode_workspace_bytes.argtypes = [ctypes.POINTER(tq_cache), ctypes.c_int]
-        L.tq_cache_bytes.restype = ctypes.c_size_t
-        L.tq_cache_bytes.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
-        L.tq_status_string.restype = ctypes.c_char_p
-        L.tq_status_string.argtypes = [ctypes.c_int]
-        L.tq_last_error.restype = ctypes.c_char_p
-        L.tq_encode_kv.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
-                                   ctypes.POINTER(tq_kv_input), ctypes.c_void_p]
-        L.tq_decode_attention.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
-                                          ctypes.POINTER(tq_query), ctypes.c_void_p,
-                                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
-        L.tq_decode_attention_mass.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
-                                               ctypes.POINTER(tq_query), ctypes.c_void_p, ctypes.c_void_p,
-                                               ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
-        L.tq_decode_attention_token_mass.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
-                                                     ctypes.POINTER(tq_query), ctypes.c_void_p, ctypes.c_void_p,
-                                                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
-        L.tq_decode_attention_noalloc.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
-                                                  ctypes.POINTER(tq_query), ctypes.c_void_p, ctypes.c_void_p]
-        L.tq_append_kv.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache),
-                                   ctypes.POINTER(tq_token_input), ctypes.c_void_p]
-        L.tq_retier_pages.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache), ctypes.c_void_p,
-                                      ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
-                                      ctypes.c_void_p]
-        L.tq_dequantize.argtypes = [ctypes.POINTER(tq_layer), ctypes.POINTER(tq_cache), ctypes.c_int,
-                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
-                                    ctypes.c_void_p]
-        _lib = L
+        _lib = _open(LIB_PATH)
     return _lib
+
+
+class library:
+    """Context manager: every call of this module inside the block goes to the
+    build of libtq at ``path`` (the checked build, by default), loaded beside
+    the release one; device memory and streams are shared."""
+
+    def __init__(self, path: str = None):
+        self.path = path or CHECKED_LIB_PATH
+
+    def __enter__(self):
+        global _lib
+        self.saved = lib()
+        _lib = _open(self.path)
+        return _lib
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
+
+
+def device_checks(reset: bool = True):
+    """tq_device_checks: the check bits the kernels recorded (a checked build),
+    or None for a release build."""
+    flags = ctypes.c_uint32(0)
+    st = lib().tq_device_checks(ctypes.byref(flags), 1 if reset else 0)
+    if st == ERR_UNSUPPORTED:
+        return None
+    check(st, "tq_device_checks")
+    return int(flags.value)
 
 
 def check(status: int, what: str) -> None:
@@ -398,8 +442,10 @@ class Cache:
 
 
 # ------------------------------------------------------------- device calls
-def encode_kv(layer: Layer, cache: Cache, k, v, tok0: int = 0, error_flags=None) -> None:
-    """tq_encode_kv over k, v of shape [B, H_kv, ntok, 128] (fp16 or fp32)."""
+def encode_kv(layer: Layer, cache: Cache, k, v, tok0: int = 0, error_flags=None,
+              pages_per_block: int = 0, qjl_workgroups: int = 0) -> None:
+    """tq_encode_kv over k, v of shape [B, H_kv, ntok, 128] (fp16 or fp32);
+    with a launch shape (pages_per_block, qjl_workgroups), tq_encode_kv_shaped."""
     if k.shape != v.shape or k.dim() != 4 or k.shape[-1] != HEAD_DIM or k.dtype != v.dtype:
         raise TQError(f"k and v must both be [B, H_kv, T, 128] of one dtype, got {tuple(k.shape)}, {tuple(v.shape)}")
     if k.stride() != v.stride() or k.stride(-1) != 1:
@@ -409,8 +455,12 @@ def encode_kv(layer: Layer, cache: Cache, k, v, tok0: int = 0, error_flags=None)
     inp = tq_kv_input(k.data_ptr(), v.data_ptr(), _dtype_code(k), tok0, k.shape[2], 0,
                       k.stride(0), k.stride(1), k.stride(2),
                       error_flags.data_ptr() if error_flags is not None else None)
-    check(lib().tq_encode_kv(ctypes.byref(layer.struct), ctypes.byref(cache.struct),
-                             ctypes.byref(inp), _stream(k.device)), "tq_encode_kv")
+    if pages_per_block or qjl_workgroups:
+        check(lib().tq_encode_kv_shaped(ctypes.byref(layer.struct), ctypes.byref(cache.struct), ctypes.byref(inp),
+                                        pages_per_block, qjl_workgroups, _stream(k.device)), "tq_encode_kv_shaped")
+    else:
+        check(lib().tq_encode_kv(ctypes.byref(layer.struct), ctypes.byref(cache.struct),
+                                 ctypes.byref(inp), _stream(k.device)), "tq_encode_kv")
 
 
 def workspace_bytes(cache: Cache, n_q_heads: int) -> int:

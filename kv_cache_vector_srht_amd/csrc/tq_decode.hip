@@ -197,7 +197,7 @@ __device__ __forceinline__ void key_scores_w(const uint32_t (&sw)[N], const floa
     if constexpr (B <= 2) {
 #pragma clang loop unroll(full)
       for (int e = 0; e < CH; e += 4) {
-        const float4 c = quad[quad_offset(B) + bits_at(sw, (n * CH + e) * B, 4 * B)];
+        const float4 c = quad[quad_offset(B) + checked(bits_at(sw, (n * CH + e) * B, 4 * B), 1 << (4 * B), kCheckDecodeTable)];
         cd[e] = c.x;
         cd[e + 1] = c.y;
         cd[e + 2] = c.z;
@@ -207,14 +207,14 @@ __device__ __forceinline__ void key_scores_w(const uint32_t (&sw)[N], const floa
       const float2* pt = pair + pair_offset(B);
 #pragma clang loop unroll(full)
       for (int e = 0; e < CH; e += 2) {
-        const float2 c = pt[bits_at(sw, (n * CH + e) * B, 2 * B)];
+        const float2 c = pt[checked(bits_at(sw, (n * CH + e) * B, 2 * B), 1 << (2 * B), kCheckDecodeTable)];
         cd[e] = c.x;
         cd[e + 1] = c.y;
       }
     } else {
       const float* ct = cent + centroid_offset(B);
 #pragma clang loop unroll(full)
-      for (int e = 0; e < CH; ++e) cd[e] = ct[bits_at(sw, (n * CH + e) * B, B)];
+      for (int e = 0; e < CH; ++e) cd[e] = ct[checked(bits_at(sw, (n * CH + e) * B, B), 1 << B, kCheckDecodeTable)];
     }
   };
   auto fmas = [&](const float (&qd)[G][CH], const float (&cd)[CH], int e0, int e1) {
@@ -368,12 +368,12 @@ __device__ __forceinline__ void value_mfma_w(const uint32_t (&sw)[N], int lane, 
     for (int e = 0; e < 4; e += 2) {
       const int t = 4 * t4 + e;
       if constexpr (B <= 2) {
-        const float4 q = quad[quad_offset(B) + bits_at(sw, 2 * t * B, 4 * B)];
+        const float4 q = quad[quad_offset(B) + checked(bits_at(sw, 2 * t * B, 4 * B), 1 << (4 * B), kCheckDecodeTable)];
         cd[2 * e] = q.x; cd[2 * e + 1] = q.y; cd[2 * e + 2] = q.z; cd[2 * e + 3] = q.w;
       } else {
         const float2* pt = pair + pair_offset(B);
-        const float2 p0 = pt[bits_at(sw, 2 * t * B, 2 * B)];
-        const float2 p1 = pt[bits_at(sw, 2 * (t + 1) * B, 2 * B)];
+        const float2 p0 = pt[checked(bits_at(sw, 2 * t * B, 2 * B), 1 << (2 * B), kCheckDecodeTable)];
+        const float2 p1 = pt[checked(bits_at(sw, 2 * (t + 1) * B, 2 * B), 1 << (2 * B), kCheckDecodeTable)];
         cd[2 * e] = p0.x; cd[2 * e + 1] = p0.y; cd[2 * e + 2] = p1.x; cd[2 * e + 3] = p1.y;
       }
     }
@@ -438,7 +438,7 @@ __device__ __forceinline__ void key_scores_wide(const char* blk, int lane, const
 #pragma clang loop unroll(full)
         for (int e = 0; e < CH; ++e) qd[h][e] = qn[(c * G + h) * CH + e];
 #pragma clang loop unroll(full)
-      for (int e = 0; e < CH; ++e) cd[e] = ct[bits_at(w, (c * CH + e) * B, B)];
+      for (int e = 0; e < CH; ++e) cd[e] = ct[checked(bits_at(w, (c * CH + e) * B, B), 1 << B, kCheckDecodeTable)];
     };
     auto fmas = [&](const float (&qd)[G][CH], const float (&cd)[CH], int e0, int e1) {
 #pragma clang loop unroll(full)
@@ -508,7 +508,8 @@ __device__ __forceinline__ void value_mfma_wide(const char* blk, int lane, const
 #pragma clang loop unroll(full)
       for (int e = 0; e < 4; ++e) {
         const int tl = 4 * t4 + e;   // token 16 n + tl: codes at pass positions 2 tl, 2 tl + 1
-        const float c0 = ct[bits_at(w, 2 * tl * B, B)], c1 = ct[bits_at(w, (2 * tl + 1) * B, B)];
+        const float c0 = ct[checked(bits_at(w, 2 * tl * B, B), 1 << B, kCheckDecodeTable)];
+        const float c1 = ct[checked(bits_at(w, (2 * tl + 1) * B, B), 1 << B, kCheckDecodeTable)];
 #pragma clang loop unroll(full)
         for (int g = 0; g < NG; ++g) {
           const float av = e == 0 ? a[g].x : e == 1 ? a[g].y : e == 2 ? a[g].z : a[g].w;
@@ -689,7 +690,7 @@ void split_kernel(DecodeArgs a,
   // partials [B][H_q][n_partials]: the classes that run, in class order
   const size_t head_stride = (size_t)a.n_partials * kPartialFloats;
   float* part = wsp + ((size_t)b * a.n_q_heads + hq0) * head_stride +
-                ((size_t)a.part_base[cls] + split) * kPartialFloats;
+                (size_t)checked(a.part_base[cls] + split, a.n_partials, kCheckDecodeIndex) * kPartialFloats;
   const int pps = cls == 0 ? a.pages_per_split : cls == 1 ? a.pages_per_split_wide : a.pages_per_split_general;
 
   const int ntok = max(0, a.n_tokens[b]);
@@ -705,7 +706,7 @@ void split_kernel(DecodeArgs a,
     int widths = 0;   // bit b: a packed page of the class with K width b; bit 9 + b: V width b
     for (int p = p_begin + tid; p < p_end; p += blockDim.x) {
       const uint64_t raw = ptab[p];
-      sm.desc[p - p_begin] = raw;   // the page loop reads it from LDS
+      sm.desc[checked(p - p_begin, kMaxPagesPerSplit, kCheckDecodeIndex)] = raw;   // the page loop reads it from LDS
       const PageDesc pd = read_desc(raw);
       const bool m = page_class(pd.kb, pd.vb, pd.qjl) == cls;
       mine |= m;
@@ -898,7 +899,7 @@ void split_kernel(DecodeArgs a,
       // start, so the V words arrive while the scores are computed; the other
       // waves of the SIMD cover the wait for the K words.
       for (int p = p_begin + wave; p < p_end; p += kDecodeWaves) {
-        const PageDesc pd = read_desc(sm.desc[p - p_begin]);
+        const PageDesc pd = read_desc(sm.desc[checked(p - p_begin, kMaxPagesPerSplit, kCheckDecodeIndex)]);
         const bool ok = pd.present && !pd.qjl && pd.kb >= 1 && pd.kb <= 4 && pd.vb >= 1 && pd.vb <= 4 &&
                         pd.off + page_size_dev(pd.kb, pd.vb, false) <= a.pool_bytes;
         if (!__builtin_amdgcn_readfirstlane(ok)) continue;
@@ -942,7 +943,7 @@ void split_kernel(DecodeArgs a,
     }
 
     for (int p = p_begin + wave; p < p_end; p += kDecodeWaves) {
-      const PageDesc pd = read_desc(sm.desc[p - p_begin]);
+      const PageDesc pd = read_desc(sm.desc[checked(p - p_begin, kMaxPagesPerSplit, kCheckDecodeIndex)]);
       const int kb = pd.kb, vb = pd.vb;
       const bool qjl = pd.qjl;
       const uint64_t off = pd.off;
@@ -1180,7 +1181,7 @@ __global__ __launch_bounds__(128 * kCombineGroups) void combine_kernel(DecodeArg
       off += w < wave ? cnt[w] : 0;
       all += cnt[w];
     }
-    if (f != 0.f) list[off + __popcll(bal & ((1ull << lane) - 1ull))] = s;
+    if (f != 0.f) list[checked(off + (int)__popcll(bal & ((1ull << lane) - 1ull)), kMaxPartials, kCheckCombine)] = s;
     total = all;
   }
   __syncthreads();
@@ -1188,7 +1189,7 @@ __global__ __launch_bounds__(128 * kCombineGroups) void combine_kernel(DecodeArg
   // does not depend on where the partials sit (which classes ran)
   float lloc = 0.f;
   for (int k = tid; k < total; k += nthr) {
-    const int s = list[k];
+    const int s = checked(list[k], ns, kCheckCombine);
     lloc = fmaf(part[(size_t)s * kPartialFloats + 1], wgt[s], lloc);
   }
   lloc = wave_sum(lloc);
@@ -1254,6 +1255,8 @@ __global__ __launch_bounds__(128 * kCombineGroups) void combine_kernel(DecodeArg
 
 using namespace tq;
 using namespace tq::dev;
+
+int tq::check_word_decode(uint32_t* out, bool reset) { return read_check_word(out, reset); }
 
 namespace {
 
@@ -1461,6 +1464,21 @@ int scratch_address(void** out) {
 }  // namespace
 
 extern "C" {
+
+int tq_device_checks(uint32_t* flags, int reset) {
+  if (!flags) return fail(TQ_ERR_INVALID_ARG, "null flags");
+  *flags = 0;
+#if TQ_DEVICE_CHECKS
+  int st;
+  if ((st = check_word_encode(flags, reset)) || (st = check_word_pages(flags, reset)) ||
+      (st = check_word_decode(flags, reset)) || (st = check_word_dequant(flags, reset)))
+    return fail(st, "reading the device check words failed");
+  return ok();
+#else
+  (void)reset;
+  return fail(TQ_ERR_UNSUPPORTED, "a release build has no device checks");
+#endif
+}
 
 int tq_decode_attention_noalloc(const tq_layer* layer, const tq_cache* cache, const tq_query* query,
                                 float* out, void* stream) {

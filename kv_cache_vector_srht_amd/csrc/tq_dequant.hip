@@ -85,13 +85,13 @@ __global__ __launch_bounds__(64) void dequant_kernel(DequantArgs a, const float*
     // pair i: radius code at coordinate 2i, angle code at 2i + 1
 #pragma clang loop unroll(full)
     for (int i = 0; i < D / 2; ++i) {
-      const float2 v = pair[code_of(2 * i) | (code_of(2 * i + 1) << B)];
+      const float2 v = pair[checked(code_of(2 * i) | (code_of(2 * i + 1) << B), 1 << (2 * B), kCheckDecodeTable)];
       x[2 * i] = v.x;
       x[2 * i + 1] = v.y;
     }
   } else {
 #pragma clang loop unroll(full)
-    for (int j = 0; j < D; ++j) x[j] = cent[code_of(j)];
+    for (int j = 0; j < D; ++j) x[j] = cent[checked(code_of(j), 1 << B, kCheckDecodeTable)];
   }
   // xhat = (n / sqrt(d)) R c = (n / d) D H D c
 #pragma clang loop unroll(full)
@@ -125,6 +125,8 @@ __global__ __launch_bounds__(64) void dequant_kernel(DequantArgs a, const float*
 
 using namespace tq;
 using namespace tq::dev;
+
+int tq::check_word_dequant(uint32_t* out, bool reset) { return read_check_word(out, reset); }
 
 extern "C" {
 

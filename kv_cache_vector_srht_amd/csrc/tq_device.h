@@ -18,6 +18,40 @@ constexpr float kSqrtHalfPi = 1.2533141373155003f;  // sqrt(pi / 2)
 constexpr float kHalfPi = 1.5707963267948966f;       // pi / 2
 constexpr int kEncodeRowBytes = 144;                 // LDS row of 128 code bytes + pad
 
+// ------------------------------------------------------------ checked builds
+// A build with TQ_DEVICE_CHECKS=1 verifies the kernels' index invariants as
+// they run: an index outside its array sets its check's bit in this
+// translation unit's check word (tq_device_checks reads them) and is clamped
+// into the array, so the access stays in bounds.  A release build compiles the
+// checks out (checked() returns its index).
+#ifndef TQ_DEVICE_CHECKS
+#define TQ_DEVICE_CHECKS 0
+#endif
+enum : uint32_t {
+  kCheckEncodeGrid = 1u,      // the encoder's lookup grid
+  kCheckEncodeStream = 2u,    // stream dwords and code-byte rows of a page part
+  kCheckQjlLds = 4u,          // the QJL key encoder's LDS (S' tiles, tables, rows)
+  kCheckDecodeTable = 8u,     // decode's codebook tables and weight rows
+  kCheckDecodeIndex = 16u,    // decode's descriptor slots and partial slots
+  kCheckCombine = 32u,        // the combine's partial lists
+  kCheckPages = 64u,          // the append and re-tier kernels
+};
+#if TQ_DEVICE_CHECKS
+static __device__ uint32_t g_check_word;
+#endif
+__device__ __forceinline__ int checked(int i, int n, uint32_t bit) {
+#if TQ_DEVICE_CHECKS
+  if ((unsigned)i >= (unsigned)n) {
+    atomicOr(&g_check_word, bit);
+    return i < 0 ? 0 : n - 1;
+  }
+#else
+  (void)n;
+  (void)bit;
+#endif
+  return i;
+}
+
 // ----------------------------------------------------------------- helpers
 __device__ __forceinline__ size_t page_size_dev(int kb, int vb, bool qjl) {
   return kb == 0 ? (size_t)2 * PT * D * 2 : (size_t)1024 * (kb + vb) + 512 + (qjl ? 1280 : 0);
@@ -135,6 +169,24 @@ __device__ __forceinline__ float load_elem(const void* p, int dtype, size_t i) {
 
 // Host helpers of the entry points.
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// OR-s this translation unit's check word into *out and zeroes it when reset
+// (synchronous copies; a release build has no word and leaves *out alone).
+static inline int read_check_word(uint32_t* out, bool reset) {
+#if TQ_DEVICE_CHECKS
+  uint32_t v = 0;
+  if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_check_word), sizeof v) != hipSuccess) return TQ_ERR_DEVICE;
+  *out |= v;
+  if (reset) {
+    const uint32_t z = 0;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(g_check_word), &z, sizeof z) != hipSuccess) return TQ_ERR_DEVICE;
+  }
+#else
+  (void)out;
+  (void)reset;
+#endif
+  return TQ_OK;
+}
 
 inline int launch_status(const char* what) {
   hipError_t e = hipGetLastError();

@@ -35,6 +35,7 @@ struct EncodeArgs {
   const float* v_table;
   const float* qjl_s;
   int k_polar, v_polar;   // PolarQuant parts (at most 4 bits wide)
+  int pages_per_block;    // encode_pages_kernel: pages per workgroup
 };
 
 // ------------------------------------------------------- encode (quad lanes)
@@ -54,7 +55,8 @@ struct EncodeArgs {
 // streaming accumulator whose flush points are uniform.
 constexpr int kRowStride = 144;            // LDS byte-matrix row: 128 codes + pad
 constexpr int kEncodeBlock = 256;
-constexpr int kEncodePagesPerBlock = 4;
+constexpr int kEncodePagesPerBlock = 4;   // the default launch shape
+constexpr int kEncodeMaxPagesPerBlock = 16;
 
 __device__ __forceinline__ float quad_swap(float v, int m) {
   // partner lane = lane ^ m inside the quad; m is a compile-time 1 or 2 after unrolling
@@ -279,7 +281,7 @@ __device__ __forceinline__ float encode_quarter(const void* src, size_t row_off,
         bin = __builtin_amdgcn_cvt_pk_u8_f32(tr, 0, 0u);
       else
         bin = (uint32_t)(int)__builtin_amdgcn_fmed3f(tr, 0.f, lut.fmax);
-      const uint2 en = ent[bin];
+      const uint2 en = ent[checked((int)bin, lut.nb, kCheckEncodeGrid)];
       const uint32_t rc = en.x + (tr >= __uint_as_float(en.y) ? 1u : 0u);
       uint32_t tc;
       if (L == 2) {
@@ -329,7 +331,7 @@ __device__ __forceinline__ float encode_quarter(const void* src, size_t row_off,
     for (int s = 0; s < 32; ++s) {
       const float g = fmaf(flip_if(x[s], (el.fl >> s) & 1u), sinv, lut.O);
       const uint32_t bin = __builtin_amdgcn_cvt_pk_u8_f32(g, 0, 0u);
-      const uint2 en = ent[bin];
+      const uint2 en = ent[checked((int)bin, lut.nb, kCheckEncodeGrid)];
       const uint32_t c = en.x + (g >= __uint_as_float(en.y) ? 1u : 0u);
       cb[s >> 2] |= c << (8 * (s & 3));
     }
@@ -339,7 +341,7 @@ __device__ __forceinline__ float encode_quarter(const void* src, size_t row_off,
       const float g = fmaf(flip_if(x[s], (el.fl >> s) & 1u), sinv, lut.O);
       // bin = clamp(floor(g), 0, nb - 1), clamped in float (one med3)
       const int bin = (int)__builtin_amdgcn_fmed3f(g, 0.f, lut.fmax);
-      const uint2 en = ent[bin];
+      const uint2 en = ent[checked(bin, lut.nb, kCheckEncodeGrid)];
       const uint32_t c = en.x + (g >= __uint_as_float(en.y) ? 1u : 0u);
       cb[s >> 2] |= c << (8 * (s & 3));
     }
@@ -361,7 +363,8 @@ __device__ __forceinline__ void store_stream_part(int B, char* blk, int s, int e
   uint32_t* const base = reinterpret_cast<uint32_t*>(blk + s * 16);   // dword d: base[(d >> 2) * 256 + (d & 3)]
   int d = e * B;
   auto emit = [&](uint32_t v) {
-    base[(d >> 2) * 256 + (d & 3)] = v;
+    const int dd = checked(d, 4 * B, kCheckEncodeStream);   // dwords e B .. e B + B - 1, e < 4
+    base[(dd >> 2) * 256 + (dd & 3)] = v;
     ++d;
   };
   if (B == 8) {
@@ -412,7 +415,7 @@ __global__ __launch_bounds__(kEncodeBlock) void encode_pages_kernel(EncodeArgs a
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int e = lane & 3, t = wave * 16 + (lane >> 2);
   const int h = blockIdx.y, b = blockIdx.z;
-  const int pg0 = a.page0 + blockIdx.x * kEncodePagesPerBlock;
+  const int pg0 = a.page0 + blockIdx.x * a.pages_per_block;
   const int pg_last = (a.tok0 + a.ntok - 1) / PT;
 
   const EncodeLane el = encode_lane(a.sign_mask, e);
@@ -425,7 +428,7 @@ __global__ __launch_bounds__(kEncodeBlock) void encode_pages_kernel(EncodeArgs a
   const size_t base = (size_t)b * a.sb + (size_t)h * a.sh;
   const uint64_t* prow = pages + ((size_t)b * a.n_kv_heads + h) * a.max_pages;
 
-  for (int pg = pg0; pg < pg0 + kEncodePagesPerBlock && pg <= pg_last; ++pg) {
+  for (int pg = pg0; pg < pg0 + a.pages_per_block && pg <= pg_last; ++pg) {
     const uint64_t desc = prow[pg];
     if (!(desc & TQ_PAGE_PRESENT)) {
       if (tid == 0) raise_flag(a.err, 2);
@@ -534,8 +537,9 @@ __global__ __launch_bounds__(kEncodeBlock) void encode_pages_kernel(EncodeArgs a
 #pragma clang loop unroll(full)
       for (int kk = 0; kk < 8; ++kk) {
         const int t0 = 16 * e + 2 * kk;
-        c8[kk] = (uint32_t)mv[t0 * kRowStride + c0] | ((uint32_t)mv[t0 * kRowStride + c1] << 8) |
-                 ((uint32_t)mv[(t0 + 1) * kRowStride + c0] << 16) | ((uint32_t)mv[(t0 + 1) * kRowStride + c1] << 24);
+        const int r0 = checked(t0 * kRowStride, (PT - 1) * kRowStride, kCheckEncodeStream);
+        c8[kk] = (uint32_t)mv[r0 + c0] | ((uint32_t)mv[r0 + c1] << 8) |
+                 ((uint32_t)mv[r0 + kRowStride + c0] << 16) | ((uint32_t)mv[r0 + kRowStride + c1] << 24);
       }
       store_stream_part(vb, vblk, s, e, c8);
     }
@@ -595,7 +599,7 @@ __device__ __forceinline__ void quantize_residual(float (&x)[32], float inv, uin
     const float u = flip_if(x[s] * inv, (fl >> s) & 1u);
     const uint32_t c = quantize<B>(u, thr);
     cb[s >> 2] |= c << (8 * (s & 3));
-    const float r = u - cent[c];
+    const float r = u - cent[checked((int)c, 1 << B, kCheckQjlLds)];
     e2 = fmaf(r, r, e2);
     x[s] = r;
   }
@@ -615,7 +619,7 @@ __device__ __forceinline__ void quantize_residual_polar(float (&x)[32], float in
     const uint32_t F = polar_pair_field<B>(u0, u1, thr, shift);
     cb[s0 >> 2] |= (F & ((1u << B) - 1u)) << (8 * (s0 & 3));
     cb[s1 >> 2] |= (F >> B) << (8 * (s1 & 3));
-    const float2 p = pair[F];
+    const float2 p = pair[checked((int)F, 1 << (2 * B), kCheckQjlLds)];
     const float r0 = u0 - p.x, r1 = u1 - p.y;
     e2 = fmaf(r0, r0, e2);
     e2 = fmaf(r1, r1, e2);
@@ -679,7 +683,7 @@ __global__ __launch_bounds__(64 * kQjlQuadWaves) void qjl_quad_kernel(EncodeArgs
         split_pair(flip_if(x[s0] * g, (el.fl >> s0) & 1u), flip_if(x[s0 + 1] * g, (el.fl >> (s0 + 1)) & 1u), hi[m],
                    lo[m]);
       }
-      const int at = ((i >> 4) * 4 + c) * 64 + 16 * e + (i & 15);
+      const int at = checked(((i >> 4) * 4 + c) * 64 + 16 * e + (i & 15), D * D / 8, kCheckQjlLds);
       sph[at] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
       spl[at] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     }
@@ -790,7 +794,8 @@ __global__ __launch_bounds__(64 * kQjlQuadWaves) void qjl_quad_kernel(EncodeArgs
         mfma_acc4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma clang loop unroll(full)
         for (int t = 0; t < 4; ++t) {
-          const int b0 = ((2 * c) * 4 + t) * 64 + lane, b1 = ((2 * c + 1) * 4 + t) * 64 + lane;
+          const int b0 = checked(((2 * c) * 4 + t) * 64 + lane, D * D / 8, kCheckQjlLds);
+          const int b1 = checked(((2 * c + 1) * 4 + t) * 64 + lane, D * D / 8, kCheckQjlLds);
           const half8 h0 = as_half8(sph[b0]), l0 = as_half8(spl[b0]);
           const half8 h1 = as_half8(sph[b1]), l1 = as_half8(spl[b1]);
           const half8 xa = as_half8(ah[t]), xl = as_half8(al[t]);
@@ -827,6 +832,8 @@ __global__ __launch_bounds__(64 * kQjlQuadWaves) void qjl_quad_kernel(EncodeArgs
 using namespace tq;
 using namespace tq::dev;
 
+int tq::check_word_encode(uint32_t* out, bool reset) { return read_check_word(out, reset); }
+
 namespace {
 
 // Compute units of device `dev`, queried once per device and cached in an
@@ -846,6 +853,14 @@ int compute_units(int dev) {
 extern "C" {
 
 int tq_encode_kv(const tq_layer* layer, const tq_cache* cache, const tq_kv_input* in, void* stream) {
+  return tq_encode_kv_shaped(layer, cache, in, 0, 0, stream);
+}
+
+int tq_encode_kv_shaped(const tq_layer* layer, const tq_cache* cache, const tq_kv_input* in,
+                        int pages_per_block, int qjl_workgroups, void* stream) {
+  if (pages_per_block < 0 || pages_per_block > kEncodeMaxPagesPerBlock)
+    return fail(TQ_ERR_INVALID_ARG, "pages_per_block %d outside 0..%d", pages_per_block, kEncodeMaxPagesPerBlock);
+  if (qjl_workgroups < 0) return fail(TQ_ERR_INVALID_ARG, "negative qjl_workgroups");
   int st = check_layer(layer);
   if (st) return st;
   if ((st = check_cache(cache))) return st;
@@ -886,9 +901,10 @@ int tq_encode_kv(const tq_layer* layer, const tq_cache* cache, const tq_kv_input
   a.qjl_s = layer->qjl_s;
   a.k_polar = layer->k_codebook == TQ_CODEBOOK_POLAR;
   a.v_polar = layer->v_codebook == TQ_CODEBOOK_POLAR;
+  a.pages_per_block = pages_per_block > 0 ? pages_per_block : kEncodePagesPerBlock;
   const int last_page = (in->tok0 + in->ntok - 1) / TQ_PAGE_TOKENS;
   const int n_pages = last_page - a.page0 + 1;
-  dim3 grid((n_pages + kEncodePagesPerBlock - 1) / kEncodePagesPerBlock, cache->n_kv_heads,
+  dim3 grid((n_pages + a.pages_per_block - 1) / a.pages_per_block, cache->n_kv_heads,
             cache->n_sessions);
   const bool polar = a.k_polar || a.v_polar;
   if (a.dtype == TQ_DTYPE_F16) {
@@ -916,7 +932,8 @@ int tq_encode_kv(const tq_layer* layer, const tq_cache* cache, const tq_kv_input
     if (hipGetDevice(&dev) == hipSuccess) cus = compute_units(dev);
     const int64_t items = (int64_t)n_pages * cache->n_kv_heads * cache->n_sessions;
     const int64_t want = (items + kQjlQuadWaves - 1) / kQjlQuadWaves;
-    const dim3 grid_q((unsigned)std::min<int64_t>(want, (int64_t)cus)), block_q(64 * kQjlQuadWaves);
+    const int64_t cap = qjl_workgroups > 0 ? qjl_workgroups : cus;
+    const dim3 grid_q((unsigned)std::max<int64_t>(1, std::min<int64_t>(want, cap))), block_q(64 * kQjlQuadWaves);
     const hipStream_t sq = (hipStream_t)stream;
     if (a.dtype == TQ_DTYPE_F16) {
       if (a.k_polar)

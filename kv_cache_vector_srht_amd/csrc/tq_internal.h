@@ -54,6 +54,13 @@ struct SplitPlan {
 SplitPlan split_plan(int n_sessions, int n_kv_heads, int max_pages);
 size_t decode_workspace_bytes(int n_sessions, int n_q_heads, const SplitPlan& sp);
 
+// Each HIP translation unit's device check word (checked builds): OR-ed into
+// *out, zeroed when reset.
+int check_word_encode(uint32_t* out, bool reset);
+int check_word_pages(uint32_t* out, bool reset);
+int check_word_decode(uint32_t* out, bool reset);
+int check_word_dequant(uint32_t* out, bool reset);
+
 // Validation shared by the device entry points (host only, before any HIP call).
 int check_layer(const tq_layer* layer);
 int check_cache(const tq_cache* cache);

@@ -200,7 +200,7 @@ __device__ __forceinline__ void unpack_mapped(const uint4* __restrict__ blk, int
 #pragma clang loop unroll(full)
       for (int e = 0; e < 4; ++e) {
         const uint32_t c = bits_at(s, (16 * i + 4 * k + e) * B, B);
-        const uint32_t m = B <= 4 ? (uint32_t)(mw >> (4 * c)) & 15u : (uint32_t)map[c];
+        const uint32_t m = B <= 4 ? (uint32_t)(mw >> (4 * c)) & 15u : (uint32_t)map[checked((int)c, 1 << B, kCheckPages)];
         v |= m << (8 * e);
       }
       o[k] = v;
@@ -409,6 +409,8 @@ __global__ __launch_bounds__(64) void retier_kernel(RetierArgs a) {
 
 using namespace tq;
 using namespace tq::dev;
+
+int tq::check_word_pages(uint32_t* out, bool reset) { return read_check_word(out, reset); }
 
 extern "C" {
 

@@ -30,6 +30,28 @@ def test_exports_every_declared_symbol(L):
         assert hasattr(L, name)
 
 
+def test_checked_build_exports_every_declared_symbol(L):
+    # the checked build (device index checks) is the same library
+    import ctypes
+    C = ctypes.CDLL(tq.CHECKED_LIB_PATH)
+    for name in tq.EXPORTS:
+        assert hasattr(C, name)
+
+
+def test_release_build_has_no_device_checks(L):
+    # no HIP call: a release build answers TQ_ERR_UNSUPPORTED and zero flags
+    assert tq.device_checks() is None
+    assert L.tq_device_checks(None, 0) == -1   # TQ_ERR_INVALID_ARG: null flags
+
+
+def test_shaped_encode_rejects_bad_shapes(L):
+    # launch shapes are checked on the host before anything else
+    for ppb, qw in ((17, 0), (-1, 0), (0, -1)):
+        st = L.tq_encode_kv_shaped(None, None, None, ppb, qw, None)
+        assert st == -1, (ppb, qw, st)   # TQ_ERR_INVALID_ARG
+        assert b"pages_per_block" in tq.lib().tq_last_error() or b"qjl_workgroups" in tq.lib().tq_last_error()
+
+
 @pytest.mark.parametrize("kind", [tq.LLOYD_MAX, tq.UNIFORM, tq.BETA, tq.POLAR])
 @pytest.mark.parametrize("bits", range(1, 9))
 def test_codebook_bit_equal_to_oracle(L, bits, kind):
