@@ -140,11 +140,20 @@ __global__ __launch_bounds__(128) void qprep_kernel(DecodeArgs a) {
 // at once (lane % 4 picks the row) fall in different LDS banks.
 constexpr int kWRow = PT + 4;
 
+// The query's key table for 1- and 2-bit keys of the common class (up to 4
+// query heads): a stream nibble covers four 1-bit or two 2-bit codes, and
+// entry 16 g + m holds, per head, the score of nibble value m at nibble
+// position g (coordinates 4g .. 4g + 3, resp. 2g, 2g + 1).
+constexpr int kKeyLutEntries = 64 * 16;
+
 // Per-workgroup LDS of the split kernel.
 struct SplitTables {
   float2 kpair[340];          // pair tables for bits 1..4 (4 + 16 + 64 + 256 entries)
   float2 vpair[340];
-  float4 kquad[272];          // quad tables for bits 1..2 (16 + 256 entries)
+  union {
+    float4 kquad[272];        // quad tables for bits 1..2 (16 + 256 entries)
+    float4 klut[kKeyLutEntries];   // or the query's key table of 1- or 2-bit pages
+  };
   float4 vquad[272];
   float kcent[512];           // centroid lists for every bit width (table layout)
   float vcent[512];
@@ -251,6 +260,26 @@ __device__ __forceinline__ void key_scores(const char* blk, int lane, const floa
     sw[4 * w] = v.x; sw[4 * w + 1] = v.y; sw[4 * w + 2] = v.z; sw[4 * w + 3] = v.w;
   }
   key_scores_w<B, G>(sw, qr, pair, quad, cent, s);
+}
+
+// Key scores of a 1- or 2-bit packed page from the query's key table, lane =
+// token: s[h] = sum over the stream's nibbles g of klut[16 g + nibble].h (one
+// lookup of four heads and G additions per nibble, against 4 (B = 1) or 2
+// (B = 2) coordinates' decode and G multiply-adds each).
+template <int B, int G, int N>
+__device__ __forceinline__ void key_scores_table(const uint32_t (&sw)[N], const float4* klut, float (&s)[G]) {
+  static_assert(B == 1 || B == 2, "a nibble holds whole codes");
+  static_assert(N >= 4 * B, "the stream's words");
+  constexpr int kGroups = 32 * B;
+#pragma clang loop unroll(full)
+  for (int h = 0; h < G; ++h) s[h] = 0.f;
+#pragma clang loop unroll(full)
+  for (int g = 0; g < kGroups; ++g) {
+    const float4 v = klut[checked(16 * g + (int)((sw[g >> 3] >> (4 * (g & 7))) & 0xFu), kKeyLutEntries, kCheckDecodeTable)];
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma clang loop unroll(full)
+    for (int h = 0; h < G; ++h) s[h] += vv[h];
+  }
 }
 
 // Key scores of an fp16 page, lane = token, with the unrotated query.
@@ -727,14 +756,52 @@ void split_kernel(DecodeArgs a,
     }
   }
 
+  const float* __restrict__ qrow = wsq + ((size_t)b * a.n_kv_heads + hkv) * kQPrepFloats * G;
+
   // Stage the codebook tables the range's pages of this class use: pair
   // tables at 3-4 bits, quad tables at 1-2 bits, centroid lists at 5-8 bits
   // (nothing when those pages are all fp16, as a decode loop's tail pages are).
+  // A common-class range whose keys are 1 or 2 bits wide (one of the two, up
+  // to 4 query heads, scalar codebooks) builds the query's key table for that
+  // width instead of the key quad table (key_table_bits).
+  int key_table_bits = 0;
   auto stage_tables = [&]() {
     if (!need_tables) return;
     int widths = 0;
 #pragma clang loop unroll(full)
     for (int w = 0; w < kDecodeWaves; ++w) widths |= sm.widths[w];
+    if (G <= 4 && cls == 0 && !a.k_polar && (CLASS == 0 || CLASS >= 3)) {
+      const int k12 = widths & 6;
+      key_table_bits = k12 == 2 ? 1 : k12 == 4 ? 2 : 0;
+    }
+    if (key_table_bits) {
+      // entry 16 g + m: sum over the nibble's codes of q[h][coordinate] c[code],
+      // the prepared query (scale included) at qrow[((j / 4) G + h) 4 + j % 4]
+      const float* cb = a.k_table + centroid_offset(key_table_bits);
+      const int n = 16 * 32 * key_table_bits;
+      for (int i = tid; i < n; i += blockDim.x) {
+        const int g = i >> 4, mm = i & 15;
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma clang loop unroll(full)
+        for (int h = 0; h < G; ++h) {
+          if (key_table_bits == 1) {
+#pragma clang loop unroll(full)
+            for (int e = 0; e < 4; ++e) {
+              const int j = 4 * g + e;
+              v[h] = fmaf(qrow[((j >> 2) * G + h) * 4 + (j & 3)], cb[(mm >> e) & 1], v[h]);
+            }
+          } else {
+#pragma clang loop unroll(full)
+            for (int e = 0; e < 2; ++e) {
+              const int j = 2 * g + e;
+              v[h] = fmaf(qrow[((j >> 2) * G + h) * 4 + (j & 3)], cb[(mm >> (2 * e)) & 3], v[h]);
+            }
+          }
+        }
+        sm.t.klut[i] = make_float4(v[0], v[1], v[2], v[3]);
+      }
+      widths &= ~6;   // no key quad table
+    }
     // pair tables come with the codebook table (a scalar codebook's (c[lo],
     // c[hi]), or PolarQuant's radius-angle pairs); a quad entry is two pairs
     auto stage = [&](int wm, const float* tab, float2* pair, float4* quad, float* cent) {
@@ -766,8 +833,6 @@ void split_kernel(DecodeArgs a,
     __builtin_amdgcn_sched_barrier(0);
   };
   stage_tables();
-
-  const float* __restrict__ qrow = wsq + ((size_t)b * a.n_kv_heads + hkv) * kQPrepFloats * G;
 
   // The other class's own launch keeps the QJL term's table (qjl_scores_lut):
   // 32 x 16 x G floats built once per workgroup from the prepared S q.  The
@@ -923,8 +988,14 @@ void split_kernel(DecodeArgs a,
         const float nv = reinterpret_cast<const float*>(vp + 1024 * vb)[lane];
         float s[G];
         switch (kb) {
-          case 1: key_scores_w<1, G>(kw, qrow, sm.t.kpair, sm.t.kquad, sm.t.kcent, s); break;
-          case 2: key_scores_w<2, G>(kw, qrow, sm.t.kpair, sm.t.kquad, sm.t.kcent, s); break;
+          case 1:
+            if (key_table_bits == 1) key_scores_table<1, G>(kw, sm.t.klut, s);
+            else key_scores_w<1, G>(kw, qrow, sm.t.kpair, sm.t.kquad, sm.t.kcent, s);
+            break;
+          case 2:
+            if (key_table_bits == 2) key_scores_table<2, G>(kw, sm.t.klut, s);
+            else key_scores_w<2, G>(kw, qrow, sm.t.kpair, sm.t.kquad, sm.t.kcent, s);
+            break;
           case 3: key_scores_w<3, G>(kw, qrow, sm.t.kpair, sm.t.kquad, sm.t.kcent, s); break;
           default: key_scores_w<4, G>(kw, qrow, sm.t.kpair, sm.t.kquad, sm.t.kcent, s); break;
         }
