@@ -587,17 +587,28 @@ namespace tq {
 
 SplitPlan split_plan(int n_sessions, int n_kv_heads, int max_pages) {
   // Enough workgroups to fill the GPU several times over, each with at least
-  // one page per wave.
+  // one page per wave: ranges of total / kTargetSplitGroups pages.  The other
+  // class (half as long) keeps that length.  The common and wide classes cut
+  // ranges longer than kLongRangePages to about 3 kTargetSplitGroups of them
+  // (not below kLongRangePages): with long contexts their ranges, all
+  // resident at once, would otherwise wait for the slowest (tiers mix cheap
+  // and dear pages), while several rounds of shorter ones balance.
   const int64_t units = (int64_t)n_sessions * n_kv_heads;
-  int64_t total_pages = units * max_pages;
-  int64_t pps = (total_pages + kTargetSplitGroups - 1) / kTargetSplitGroups;
-  if (pps < kDecodeWaves) pps = kDecodeWaves;
-  if (pps > kMaxPagesPerSplit) pps = kMaxPagesPerSplit;
-  if (pps > max_pages) pps = max_pages;
+  const int64_t total_pages = units * max_pages;
+  auto clamp_len = [&](int64_t p) {
+    p = std::max<int64_t>(p, kDecodeWaves);
+    p = std::min<int64_t>(p, kMaxPagesPerSplit);
+    return std::min<int64_t>(p, max_pages);
+  };
+  const int64_t pps = clamp_len((total_pages + kTargetSplitGroups - 1) / kTargetSplitGroups);
+  const int64_t short_len = (total_pages + 3 * kTargetSplitGroups - 1) / (3 * kTargetSplitGroups);
+  int64_t ppc = std::max<int64_t>(std::min<int64_t>(pps, kLongRangePages), short_len);
+  // at most kTargetSplitGroups ranges per unit (the partials' slots)
+  ppc = clamp_len(std::max<int64_t>(ppc, (max_pages + kTargetSplitGroups - 1) / kTargetSplitGroups));
   SplitPlan sp;
-  sp.pages_per_split = (int)pps;
-  sp.n_splits = (int)((max_pages + pps - 1) / pps);
-  sp.pages_per_split_general = (sp.pages_per_split + 1) / 2;
+  sp.pages_per_split = (int)ppc;
+  sp.n_splits = (int)((max_pages + ppc - 1) / ppc);
+  sp.pages_per_split_general = (int)((pps + 1) / 2);
   sp.n_splits_general = (max_pages + sp.pages_per_split_general - 1) / sp.pages_per_split_general;
   sp.pages_per_split_wide = (sp.pages_per_split + 3) / 4;
   sp.n_splits_wide = (max_pages + sp.pages_per_split_wide - 1) / sp.pages_per_split_wide;

@@ -33,6 +33,7 @@ constexpr int kLutByteBins = 256;   // grids this small are indexed by a saturat
 // Decode split-K geometry.
 constexpr int kDecodeWaves = 4;             // waves per split workgroup
 constexpr int kTargetSplitGroups = 1024;    // workgroups the split grid aims for
+constexpr int kLongRangePages = 64;         // common ranges longer than this are cut further
 constexpr int kMaxPagesPerSplit = 256;      // a range's descriptors fit the workgroup's LDS copy
 constexpr int kQPrepFloats = 3 * 128;       // rotated q, plain q, S q (all pre-scaled)
 constexpr int kPartialFloats = 4 + 128;     // m, l, (pad), acc[128]
