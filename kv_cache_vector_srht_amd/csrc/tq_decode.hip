@@ -146,24 +146,32 @@ constexpr int kWRow = PT + 4;
 // position g (coordinates 4g .. 4g + 3, resp. 2g, 2g + 1).
 constexpr int kKeyLutEntries = 64 * 16;
 
-// Per-workgroup LDS of the split kernel.
+// Per-workgroup LDS of the split kernel (KLUT: the launch may build the key
+// table; the others leave its space out).
+template <bool KLUT>
 struct SplitTables {
   float2 kpair[340];          // pair tables for bits 1..4 (4 + 16 + 64 + 256 entries)
   float2 vpair[340];
   union {
     float4 kquad[272];        // quad tables for bits 1..2 (16 + 256 entries)
-    float4 klut[kKeyLutEntries];   // or the query's key table of 1- or 2-bit pages
+    float4 klut[KLUT ? kKeyLutEntries : 1];   // or the query's key table of 1- or 2-bit pages
   };
   float4 vquad[272];
-  float kcent[512];           // centroid lists for every bit width (table layout)
-  float vcent[512];
+  union {
+    struct {
+      float kcent[512];       // centroid lists for every bit width (table layout; 5-8 bits)
+      float vcent[512];
+    };
+    uint4 kqa[256];           // or (common class, 1-4 bits) the query as the matrix
+                              // cores' A operand (key_scores_mfma)
+  };
 };
-template <int G>
+template <int G, bool KLUT>
 struct SplitLds {
   // the codebook tables serve the page loop; the workgroup reduction reuses
   // their space once every wave has left the loop (after a barrier)
   union {
-    SplitTables t;
+    SplitTables<KLUT> t;
     float red[kDecodeWaves][G * D];
   };
   float w[kDecodeWaves][(G < 4 ? 4 : G) * kWRow];   // weights of the current page, [head][token]
@@ -433,6 +441,107 @@ __device__ __forceinline__ void value_mfma_w(const uint32_t (&sw)[N], int lane, 
   }
 }
 
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ half8 as_half8(uint4 v) { return __builtin_bit_cast(half8, v); }
+
+// Two float32 values as float16 parts: hi = fp16(y), lo = fp16(y - hi), the
+// pair's hi parts in one dword (first value in the low half), lo in another.
+// (fp16(y - hi) is y - hi rounded once: y - hi is exact in float32.)
+__device__ __forceinline__ uint2 split_half2(float y0, float y1) {
+  const _Float16 h0 = (_Float16)y0, h1 = (_Float16)y1;
+  const _Float16 l0 = (_Float16)(y0 - (float)h0), l1 = (_Float16)(y1 - (float)h1);
+  return make_uint2((uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16),
+                    (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16));
+}
+
+// Scale of the key pair table on the matrix cores: coordinates of a unit
+// vector times sqrt(d) stay below 12 in magnitude, so 2^8 keeps them well
+// inside the float16 range while their lo parts stay normal.
+constexpr float kKeyPairScale = 256.f;
+
+
+// Code words of a 3- or 4-bit key page in the layout key_scores_mfma reads:
+// lane l (k-group g = l / 16, column n = l % 16) takes the coordinate quarter
+// 32 g .. 32 g + 31 of token 16 t + n for each tile t, i.e. dwords B g ..
+// B g + B - 1 of that token's stream, into kw[B t ..].
+template <int B>
+__device__ __forceinline__ void load_keys_mfma(const char* kp, int lane, uint32_t (&kw)[16]) {
+  const int g = lane >> 4, n = lane & 15;
+  if constexpr (B == 4) {
+    const uint4* ks = reinterpret_cast<const uint4*>(kp);
+#pragma clang loop unroll(full)
+    for (int t = 0; t < 4; ++t) {
+      const uint4 x = ks[g * 64 + 16 * t + n];
+      kw[4 * t] = x.x; kw[4 * t + 1] = x.y; kw[4 * t + 2] = x.z; kw[4 * t + 3] = x.w;
+    }
+  } else {
+    // a quarter is 96 bits: dwords 3 g .. 3 g + 2, which may straddle the
+    // stream's 16-byte blocks (dword d of token u: block d / 4, lane u)
+    const uint32_t* kd = reinterpret_cast<const uint32_t*>(kp);
+#pragma clang loop unroll(full)
+    for (int t = 0; t < 4; ++t)
+#pragma clang loop unroll(full)
+      for (int i = 0; i < 3; ++i) {
+        const int d = 3 * g + i;
+        kw[3 * t + i] = kd[((d >> 2) * 64 + 16 * t + n) * 4 + (d & 3)];
+      }
+#pragma clang loop unroll(full)
+    for (int i = 12; i < 16; ++i) kw[i] = 0;
+  }
+}
+
+// Key scores of a 3- or 4-bit packed page for four query heads on the matrix
+// cores (v_mfma_f32_16x16x32_f16), lane = token on return, unscaled (times
+// the query's and the table's scales).  The page is four tiles of 16 tokens:
+// tile t is the B operand (column n = token 16 t + n) and the query the A
+// operand (row i = head i % 4, each head four times), so accumulator t holds
+// in lane l the scores of token 16 t + l % 16 for the four heads, and lane l
+// keeps accumulator l / 16, its own token's.  Float32 operands enter as
+// float16 hi and lo parts and each product as three float16 ones (hi hi,
+// hi lo, lo hi), exact in the float32 accumulator; the dropped lo lo term and
+// the lo parts' rounding are below 2^-21 of each product.  In step st (of 8)
+// k-group g = l / 16 holds coordinates c0..c3 = 32 g + 4 st + 0..3, two code
+// pairs, as B = [ch0 ch1 cl0 cl1 ch2 ch3 cl2 cl3]: each pair's (hi, lo) table
+// entry (khl, two dwords) is one lookup into its place.  The query is
+// A1 = [qh0 qh1 qh0 qh1 qh2 qh3 qh2 qh3] (qh ch + qh cl) and
+// A2 = [ql0 ql1 0 0 ql2 ql3 0 0] (ql ch), staged in kqa per (st, g, head).
+template <int B>
+__device__ __forceinline__ void key_scores_mfma(const uint32_t (&kw)[16], int lane, const uint4* kqa,
+                                                const uint2* khl, float (&s)[4]) {
+  static_assert(B == 3 || B == 4, "pair-table widths");
+  const int g = lane >> 4;
+  v4f acc[4];
+#pragma clang loop unroll(full)
+  for (int t = 0; t < 4; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma clang loop unroll(full)
+  for (int st = 0; st < 8; ++st) {
+    const uint4* qa = kqa + checked(2 * ((st * 4 + g) * 4 + (lane & 3)), 255, kCheckDecodeTable);
+    const half8 a1 = as_half8(qa[0]), a2 = as_half8(qa[1]);
+#pragma clang loop unroll(full)
+    for (int t = 0; t < 4; ++t) {
+      // the step's two code pairs (2 x 2B bits) of tile t's token: pairs
+      // 2 st, 2 st + 1 of the lane's quarter (pair m at bit 2 B m)
+      uint32_t x;
+      if constexpr (B == 4) {
+        x = kw[4 * t + (st >> 1)] >> (16 * (st & 1));
+      } else {
+        const int bit = 12 * st, d = bit >> 5, sh = bit & 31;
+        x = sh <= 20 ? kw[3 * t + d] >> sh : __builtin_amdgcn_alignbit(kw[3 * t + d + 1], kw[3 * t + d], sh);
+      }
+      constexpr uint32_t kMask = (1u << (2 * B)) - 1u;
+      const uint2 e0 = khl[checked((int)(x & kMask), 1 << (2 * B), kCheckDecodeTable)];
+      const uint2 e1 = khl[checked((int)((x >> (2 * B)) & kMask), 1 << (2 * B), kCheckDecodeTable)];
+      const half8 bv = as_half8(make_uint4(e0.x, e0.y, e1.x, e1.y));
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2, bv, acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bv, acc[t], 0, 0, 0);
+    }
+  }
+#pragma clang loop unroll(full)
+  for (int h = 0; h < 4; ++h)
+    s[h] = g == 0 ? acc[0][h] : g == 1 ? acc[1][h] : g == 2 ? acc[2][h] : acc[3][h];
+}
+
 // Key scores of a packed page at 5-8 bits.  These widths are rare (a few
 // important heads), so the code is kept short instead of fully unrolled: four
 // passes over 32 coordinates each, whose codes fill exactly B dwords of the
@@ -668,7 +777,9 @@ void split_kernel(DecodeArgs a,
                                                                   const uint64_t* __restrict__ pages,
                                                                   float* __restrict__ wsp,
                                                                   const UnitList list) {
-  __shared__ SplitLds<G> sm;
+  // the query's key table: common pages of up to four query heads
+  constexpr bool kKeyTable = G <= 4 && (CLASS == 0 || CLASS >= 3);
+  __shared__ SplitLds<G, kKeyTable> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // the other class runs its ranges last page first: a decode loop's fp16
   // tail page is then in the first workgroups dispatched, not behind the
@@ -765,16 +876,54 @@ void split_kernel(DecodeArgs a,
   // to 4 query heads, scalar codebooks) builds the query's key table for that
   // width instead of the key quad table (key_table_bits).
   int key_table_bits = 0;
+  // A common-class range of four query heads with 3- or 4-bit keys scores them
+  // on the matrix cores (key_scores_mfma): its key pair tables at those widths
+  // hold float16 hi and lo parts (times kKeyPairScale), and the query is staged
+  // as the A operand, times 2^E so that its largest magnitude is in [2^9, 2^10);
+  // the scores are then multiplied by key_unscale = 2^-(E + 8).
+  // (Not in the launch merged with the other class: its register budget is
+  // spent by the other class's copy of the page loop.)
+  constexpr bool kMfmaKeys = G == 4 && CLASS != 4;
+  bool key_mfma = false;
+  float key_unscale = 1.f;
   auto stage_tables = [&]() {
     if (!need_tables) return;
     int widths = 0;
 #pragma clang loop unroll(full)
     for (int w = 0; w < kDecodeWaves; ++w) widths |= sm.widths[w];
-    if (G <= 4 && cls == 0 && !a.k_polar && (CLASS == 0 || CLASS >= 3)) {
+    if (kKeyTable && cls == 0 && !a.k_polar) {
       const int k12 = widths & 6;
       key_table_bits = k12 == 2 ? 1 : k12 == 4 ? 2 : 0;
     }
-    if (key_table_bits) {
+    if constexpr (kMfmaKeys) {
+      key_mfma = cls == 0 && (widths & 0x18) != 0;
+      if (key_mfma) {
+        // every wave finds the same largest magnitude of the prepared query
+        float mx = 0.f;
+        for (int i = lane; i < D * G; i += 64) mx = fmaxf(mx, fabsf(qrow[i]));
+        mx = wave_max(mx);
+        int ex = 0;
+        (void)frexpf(mx, &ex);
+        const int E = (mx > 0.f && mx <= 3.0e38f) ? min(60, max(-60, 10 - ex)) : 0;
+        const float qs = ldexpf(1.f, E);
+        key_unscale = ldexpf(1.f, -(E + 8));
+        // entry (step st, k-group g, head h): coordinates c0..c3 = 32 g + 4 st
+        // + 0..3 of head h as A1 = (qh0 qh1, qh0 qh1, qh2 qh3, qh2 qh3) and
+        // A2 = (ql0 ql1, 0, ql2 ql3, 0), key_scores_mfma's operands (the
+        // prepared query's layout: coordinate j of head h at ((j / 4) G + h)
+        // 4 + j % 4, so c0..c3 are one aligned quad)
+        if (tid < 128) {
+          const int st = tid >> 4, gg = (tid >> 2) & 3, h = tid & 3;
+          const int j0 = 32 * gg + 4 * st;
+          const float* qc = qrow + ((j0 >> 2) * G + h) * 4;
+          const uint2 v01 = split_half2(qc[0] * qs, qc[1] * qs);
+          const uint2 v23 = split_half2(qc[2] * qs, qc[3] * qs);
+          sm.t.kqa[checked(2 * tid, 256, kCheckDecodeTable)] = make_uint4(v01.x, v01.x, v23.x, v23.x);
+          sm.t.kqa[checked(2 * tid + 1, 256, kCheckDecodeTable)] = make_uint4(v01.y, 0u, v23.y, 0u);
+        }
+      }
+    }
+    if (kKeyTable && key_table_bits) {
       // entry 16 g + m: sum over the nibble's codes of q[h][coordinate] c[code],
       // the prepared query (scale included) at qrow[((j / 4) G + h) 4 + j % 4]
       const float* cb = a.k_table + centroid_offset(key_table_bits);
@@ -798,18 +947,24 @@ void split_kernel(DecodeArgs a,
             }
           }
         }
-        sm.t.klut[i] = make_float4(v[0], v[1], v[2], v[3]);
+        sm.t.klut[checked(i, kKeyLutEntries, kCheckDecodeTable)] = make_float4(v[0], v[1], v[2], v[3]);
       }
       widths &= ~6;   // no key quad table
     }
     // pair tables come with the codebook table (a scalar codebook's (c[lo],
     // c[hi]), or PolarQuant's radius-angle pairs); a quad entry is two pairs
-    auto stage = [&](int wm, const float* tab, float2* pair, float4* quad, float* cent) {
+    auto stage = [&](int wm, const float* tab, float2* pair, float4* quad, float* cent, bool hilo) {
       const float2* pt = reinterpret_cast<const float2*>(tab + kPairOffset);
       for (int bb = 3; bb <= 4; ++bb) {
         if (!((wm >> bb) & 1)) continue;
         const int o = pair_offset(bb), n = 1 << (2 * bb);
-        for (int i = tid; i < n; i += blockDim.x) pair[o + i] = pt[o + i];
+        if (hilo) {
+          for (int i = tid; i < n; i += blockDim.x)
+            reinterpret_cast<uint2*>(pair)[o + i] = split_half2(pt[o + i].x * kKeyPairScale,
+                                                                pt[o + i].y * kKeyPairScale);
+        } else {
+          for (int i = tid; i < n; i += blockDim.x) pair[o + i] = pt[o + i];
+        }
       }
       for (int bb = 1; bb <= 2; ++bb) {
         if (!((wm >> bb) & 1)) continue;
@@ -825,8 +980,8 @@ void split_kernel(DecodeArgs a,
         for (int i = tid; i < n; i += blockDim.x) cent[o + i] = tab[o + i];
       }
     };
-    stage(widths & 0x1FF, a.k_table, sm.t.kpair, sm.t.kquad, sm.t.kcent);
-    stage(widths >> 9, a.v_table, sm.t.vpair, sm.t.vquad, sm.t.vcent);
+    stage(widths & 0x1FF, a.k_table, sm.t.kpair, sm.t.kquad, sm.t.kcent, key_mfma);
+    stage(widths >> 9, a.v_table, sm.t.vpair, sm.t.vquad, sm.t.vcent, false);
     __syncthreads();
     // keep the scheduler from moving table work into the page loop (it
     // otherwise inflates the loop's register use)
@@ -959,10 +1114,10 @@ void split_kernel(DecodeArgs a,
     };
 
     if constexpr (PC == 0) {
-      // Common pages.  Every lane issues the same ten loads per page (words
-      // past a width repeat its last word), K and V together at the page's
-      // start, so the V words arrive while the scores are computed; the other
-      // waves of the SIMD cover the wait for the K words.
+      // Common pages.  Every lane issues the same loads per page (words past
+      // a width repeat its last word), K and V together at the page's start,
+      // so the V words arrive while the scores are computed; the other waves
+      // of the SIMD cover the wait for the K words.
       for (int p = p_begin + wave; p < p_end; p += kDecodeWaves) {
         const PageDesc pd = read_desc(sm.desc[checked(p - p_begin, kMaxPagesPerSplit, kCheckDecodeIndex)]);
         const bool ok = pd.present && !pd.qjl && pd.kb >= 1 && pd.kb <= 4 && pd.vb >= 1 && pd.vb <= 4 &&
@@ -974,10 +1129,19 @@ void split_kernel(DecodeArgs a,
         const uint4* ks = reinterpret_cast<const uint4*>(kp);
         const uint4* vs = reinterpret_cast<const uint4*>(vp);
         uint32_t kw[16], vw[16];
+        // 3- and 4-bit keys on the matrix cores (every such page of the range
+        // set key_mfma when the tables were staged)
+        const bool mk = kMfmaKeys && kb >= 3;
+        if (mk) {
+          (void)checked((int)!key_mfma, 1, kCheckDecodeTable);
+          if (kb == 3) load_keys_mfma<3>(kp, lane, kw);
+          else load_keys_mfma<4>(kp, lane, kw);
+        } else {
   #pragma clang loop unroll(full)
-        for (int w = 0; w < 4; ++w) {
-          const uint4 x = ks[min(w, kb - 1) * 64 + lane];
-          kw[4 * w] = x.x; kw[4 * w + 1] = x.y; kw[4 * w + 2] = x.z; kw[4 * w + 3] = x.w;
+          for (int w = 0; w < 4; ++w) {
+            const uint4 x = ks[min(w, kb - 1) * 64 + lane];
+            kw[4 * w] = x.x; kw[4 * w + 1] = x.y; kw[4 * w + 2] = x.z; kw[4 * w + 3] = x.w;
+          }
         }
         const float nk = reinterpret_cast<const float*>(kp + 1024 * kb)[lane];
   #pragma clang loop unroll(full)
@@ -996,11 +1160,22 @@ void split_kernel(DecodeArgs a,
             if (key_table_bits == 2) key_scores_table<2, G>(kw, sm.t.klut, s);
             else key_scores_w<2, G>(kw, qrow, sm.t.kpair, sm.t.kquad, sm.t.kcent, s);
             break;
-          case 3: key_scores_w<3, G>(kw, qrow, sm.t.kpair, sm.t.kquad, sm.t.kcent, s); break;
-          default: key_scores_w<4, G>(kw, qrow, sm.t.kpair, sm.t.kquad, sm.t.kcent, s); break;
+          case 3:
+            if constexpr (kMfmaKeys)
+              key_scores_mfma<3>(kw, lane, sm.t.kqa, reinterpret_cast<const uint2*>(sm.t.kpair) + pair_offset(3), s);
+            else
+              key_scores_w<3, G>(kw, qrow, sm.t.kpair, sm.t.kquad, sm.t.kcent, s);
+            break;
+          default:
+            if constexpr (kMfmaKeys)
+              key_scores_mfma<4>(kw, lane, sm.t.kqa, reinterpret_cast<const uint2*>(sm.t.kpair) + pair_offset(4), s);
+            else
+              key_scores_w<4, G>(kw, qrow, sm.t.kpair, sm.t.kquad, sm.t.kcent, s);
+            break;
         }
+        const float ks_scale = mk ? nk * key_unscale : nk;
   #pragma clang loop unroll(full)
-        for (int h = 0; h < G; ++h) s[h] *= nk;
+        for (int h = 0; h < G; ++h) s[h] *= ks_scale;
         weigh(p, s, nv, min(PT, ntok - p * PT));
         switch (vb) {
           case 1: value_mfma_w<1, NG>(vw, lane, wv, sm.t.vpair, sm.t.vquad, acc); break;

@@ -28,10 +28,11 @@ def _np(x):
 
 
 def run_case(w, layers, dev, units=None, n_tokens=None, dequant=True, chunks=None, tally=None,
-             query_dtype=None, layer_kw=None, qjl_s=None):
+             query_dtype=None, layer_kw=None, qjl_s=None, query_scale=None):
     """Encode + decode every listed layer of workload w on the GPU; compare the
     listed units (all by default) with the oracle.  ``qjl_s`` replaces the
-    seeded QJL matrix of layers with QJL pages."""
+    seeded QJL matrix of layers with QJL pages; ``query_scale`` multiplies the
+    query (after its cast to ``query_dtype``)."""
     import kv_cache_vector_srht_amd as tq
     t = tally or Tally()
     G = w.n_q_heads // w.n_kv_heads
@@ -50,6 +51,8 @@ def run_case(w, layers, dev, units=None, n_tokens=None, dequant=True, chunks=Non
         q = W.make_query(w, l, device=dev)
         if query_dtype is not None:
             q = q.to(query_dtype)
+        if query_scale is not None:
+            q = q * query_scale
         flags = torch.zeros(1, dtype=torch.int32, device=dev)
         if chunks:
             for t0, t1 in chunks:
@@ -308,6 +311,33 @@ def _narrow_workload(pages=24, qjl=False, G=4):
     w.formats = [[[[W.packed(*combos[(p + 5 * h) % 16], qjl) if p > 0 else W.FP16
                     for p in range(pages)] for h in range(2)]]]
     return w
+
+
+def _packed_narrow_workload(pages=40, G=4):
+    """Every (K, V) width pair within 1..4 bits and no fp16 page, so that the
+    layer takes the common class's own launch (four query heads: 3- and 4-bit
+    keys scored on the matrix cores, 1- and 2-bit keys from the query's key
+    table, both kinds in one range)."""
+    w = W.make_workload(2, {"n_tokens": 64 * pages, "batch": 1, "n_kv_heads": 2,
+                            "n_q_heads": 2 * G, "sink_tokens": 0, "dtype": "float16"})
+    combos = [(kb, vb) for kb in range(1, 5) for vb in range(1, 5)]
+    w.formats = [[[[W.packed(*combos[(p + 5 * h) % 16], False) for p in range(pages)] for h in range(2)]]]
+    return w
+
+
+@pytest.mark.parametrize("kind", [O.LLOYD_MAX, O.UNIFORM, O.BETA, O.POLAR])
+def test_common_launch_every_narrow_width_pair(dev, kind):
+    w = _packed_narrow_workload()
+    w.k_codebook = w.v_codebook = kind
+    run_case(w, [0], dev)
+
+
+@pytest.mark.parametrize("scale", [0.0, 2.0 ** -40, 16.0])
+def test_common_launch_query_scales(dev, scale):
+    """The matrix-core key scores stage the query times a power of two that
+    puts its largest magnitude near 2^10 (and undo it): a zero query (uniform
+    weights), a tiny one and a large one."""
+    run_case(_packed_narrow_workload(pages=20), [0], dev, query_dtype=torch.float32, query_scale=scale)
 
 
 def test_polar_every_narrow_width_pair(dev):
