@@ -355,50 +355,58 @@ __device__ __forceinline__ float encode_quarter(const void* src, size_t row_off,
 
 // Writes dwords [e*B, e*B + B) of stream s of a code block from its codes
 // 32e..32e+31 (one per byte of c8, each below 2^B), LSB-first: code n at bit
-// n B.  The width is uniform, so the branches below are too.  Up to 4 bits,
-// each dword of four codes is folded in two shift-or-mask steps (pairs, then a
-// 4B-bit quad) before entering the bit accumulator; 8-bit codes are already
-// packed; 5-7 bits enter code by code.
-__device__ __forceinline__ void store_stream_part(int B, char* blk, int s, int e, const uint32_t (&c8)[8]) {
-  uint32_t* const base = reinterpret_cast<uint32_t*>(blk + s * 16);   // dword d: base[(d >> 2) * 256 + (d & 3)]
-  int d = e * B;
-  auto emit = [&](uint32_t v) {
-    const int dd = checked(d, 4 * B, kCheckEncodeStream);   // dwords e B .. e B + B - 1, e < 4
-    base[(dd >> 2) * 256 + (dd & 3)] = v;
-    ++d;
-  };
-  if (B == 8) {
+// n B.  Up to 4 bits the width is a template argument, so every shift is a
+// constant: each dword of four codes is folded in two shift-or-mask steps
+// (pairs, then a 4B-bit quad) and the eight quads are placed at bit 4B k.
+template <int B>
+__device__ __forceinline__ void store_stream_part_w(char* blk, int s, int e, const uint32_t (&c8)[8]) {
+  uint32_t out[B];
 #pragma clang loop unroll(full)
-    for (int i = 0; i < 8; ++i) emit(c8[i]);
-    return;
-  }
-  uint64_t acc = 0;
-  int nb = 0;
-  if (B <= 4) {
-    const int s1 = 8 - B, s2 = 16 - 2 * B, w4 = 4 * B;
-    const uint32_t m2 = ((1u << (2 * B)) - 1u) * 0x00010001u, m4 = (1u << w4) - 1u;
+  for (int i = 0; i < B; ++i) out[i] = 0;
+  static_assert(B >= 1 && B <= 4, "narrow widths");
+  {
+    constexpr uint32_t m2 = ((1u << (2 * B)) - 1u) * 0x00010001u, m4 = (1u << (4 * B)) - 1u;
 #pragma clang loop unroll(full)
     for (int k = 0; k < 8; ++k) {
       const uint32_t w = c8[k];
-      const uint32_t pr = (w | (w >> s1)) & m2;     // c0 | c1 << B, c2 | c3 << B
-      const uint32_t qd = (pr | (pr >> s2)) & m4;   // c0 | c1 << B | c2 << 2B | c3 << 3B
-      acc |= (uint64_t)qd << nb;
-      nb += w4;
-      if (nb >= 32) {
-        emit((uint32_t)acc);
-        acc >>= 32;
-        nb -= 32;
-      }
+      const uint32_t pr = (w | (w >> (8 - B))) & m2;             // c0 | c1 << B, c2 | c3 << B
+      const uint32_t qd = (pr | (pr >> (16 - 2 * B))) & m4;      // c0 | c1 << B | c2 << 2B | c3 << 3B
+      constexpr int kw = 4 * B;
+      const int bit = kw * k, d = bit >> 5, sh = bit & 31;
+      out[d] |= qd << sh;
+      if (sh + kw > 32) out[d + 1] |= qd >> (32 - sh);
     }
-  } else {
+  }
+  uint32_t* const base = reinterpret_cast<uint32_t*>(blk + s * 16);   // dword d: base[(d >> 2) * 256 + (d & 3)]
 #pragma clang loop unroll(full)
-    for (int n = 0; n < 32; ++n) {
-      acc |= (uint64_t)((c8[n >> 2] >> (8 * (n & 3))) & 0xffu) << nb;
-      nb += B;
-      if (nb >= 32) {
-        emit((uint32_t)acc);
-        acc >>= 32;
-        nb -= 32;
+  for (int i = 0; i < B; ++i) {
+    const int dd = checked(e * B + i, 4 * B, kCheckEncodeStream);   // dwords e B .. e B + B - 1, e < 4
+    base[(dd >> 2) * 256 + (dd & 3)] = out[i];
+  }
+}
+
+__device__ __forceinline__ void store_stream_part(int B, char* blk, int s, int e, const uint32_t (&c8)[8]) {
+  switch (B) {
+    case 1: store_stream_part_w<1>(blk, s, e, c8); break;
+    case 2: store_stream_part_w<2>(blk, s, e, c8); break;
+    case 3: store_stream_part_w<3>(blk, s, e, c8); break;
+    case 4: store_stream_part_w<4>(blk, s, e, c8); break;
+    default: {
+      // 5-8 bits (a few important heads): code by code at run-time offsets
+      uint32_t* const base = reinterpret_cast<uint32_t*>(blk + s * 16);
+      int d = e * B;
+      uint64_t acc = 0;
+      int nb = 0;
+      for (int n = 0; n < 32; ++n) {
+        acc |= (uint64_t)((c8[n >> 2] >> (8 * (n & 3))) & 0xffu) << nb;
+        nb += B;
+        if (nb >= 32) {
+          const int dd = checked(d, 4 * B, kCheckEncodeStream);
+          base[(dd >> 2) * 256 + (dd & 3)] = (uint32_t)acc;
+          ++d;
+          acc >>= 32;
+          nb -= 32;
+        }
       }
     }
   }
