@@ -592,7 +592,11 @@ SplitPlan split_plan(int n_sessions, int n_kv_heads, int max_pages) {
   // ranges longer than kLongRangePages to about 3 kTargetSplitGroups of them
   // (not below kLongRangePages): with long contexts their ranges, all
   // resident at once, would otherwise wait for the slowest (tiers mix cheap
-  // and dear pages), while several rounds of shorter ones balance.
+  // and dear pages), while several rounds of shorter ones balance.  Wide
+  // ranges are as long as common ones when those are not cut (the merged
+  // launch of a layer with hub heads then stays one round of workgroups;
+  // shorter wide ranges added a round of their own), and a quarter of that
+  // length when they are.
   const int64_t units = (int64_t)n_sessions * n_kv_heads;
   const int64_t total_pages = units * max_pages;
   auto clamp_len = [&](int64_t p) {
@@ -610,7 +614,7 @@ SplitPlan split_plan(int n_sessions, int n_kv_heads, int max_pages) {
   sp.n_splits = (int)((max_pages + ppc - 1) / ppc);
   sp.pages_per_split_general = (int)((pps + 1) / 2);
   sp.n_splits_general = (max_pages + sp.pages_per_split_general - 1) / sp.pages_per_split_general;
-  sp.pages_per_split_wide = (sp.pages_per_split + 3) / 4;
+  sp.pages_per_split_wide = pps > kLongRangePages ? (sp.pages_per_split + 3) / 4 : sp.pages_per_split;
   sp.n_splits_wide = (max_pages + sp.pages_per_split_wide - 1) / sp.pages_per_split_wide;
   return sp;
 }
