@@ -1554,7 +1554,7 @@ int decode_impl(const tq_layer* layer, const tq_cache* cache, const tq_query* qu
   if (query->qjl_scoring != TQ_QJL_SCORE_UNBIASED && query->qjl_scoring != TQ_QJL_SCORE_SIGN)
     return fail(TQ_ERR_INVALID_ARG, "unknown qjl_scoring %d", query->qjl_scoring);
   SplitPlan sp = split_plan(cache->n_sessions, cache->n_kv_heads, cache->max_pages);
-  const int max_partials = sp.n_splits + sp.n_splits_wide + sp.n_splits_general;
+  const int max_partials = sp.n_splits + sp.max_splits_wide + sp.n_splits_general;
   if (max_partials > kMaxPartials)   // the combine stages their weights in LDS
     return fail(TQ_ERR_UNSUPPORTED, "%d partials per row exceed %d", max_partials, kMaxPartials);
   const size_t need = decode_workspace_bytes(cache->n_sessions, query->n_q_heads, sp);
@@ -1589,19 +1589,6 @@ int decode_impl(const tq_layer* layer, const tq_cache* cache, const tq_query* qu
   const bool run_common = (cls & TQ_CACHE_COMMON_PAGES) != 0;
   const bool run_wide = (cls & TQ_CACHE_WIDE_PAGES) != 0;
   const bool run_other = (cls & TQ_CACHE_OTHER_PAGES) != 0;
-  const int n_common = run_common ? sp.n_splits : 0;
-  const int n_wide = run_wide ? sp.n_splits_wide : 0;
-  const int n_other = run_other ? sp.n_splits_general : 0;
-  a.part_base[0] = 0;
-  a.part_base[1] = n_common;
-  a.part_base[2] = n_common + n_wide;
-  a.n_partials = n_common + n_wide + n_other;
-  a.n_splits = sp.n_splits;
-  a.pages_per_split = sp.pages_per_split;
-  a.n_splits_general = sp.n_splits_general;
-  a.pages_per_split_general = sp.pages_per_split_general;
-  a.n_splits_wide = sp.n_splits_wide;
-  a.pages_per_split_wide = sp.pages_per_split_wide;
   // Per-class unit lists from the host's per-unit record: a class's launch
   // covers only the units that hold it.  Class 0 = common, 1 = wide, 2 = other.
   UnitList lists[3];
@@ -1620,16 +1607,6 @@ int decode_impl(const tq_layer* layer, const tq_cache* cache, const tq_query* qu
         a.unit_skip[c][u >> 5] |= 1u << (u & 31);
     }
   }
-  a.wsq = reinterpret_cast<float*>(workspace);
-  a.wsp = a.wsq + (size_t)cache->n_sessions * query->n_q_heads * kQPrepFloats;
-  a.out = out;
-  a.mass = page_mass;
-  a.tmass = token_mass;
-  const bool mass = page_mass != nullptr || token_mass != nullptr;
-  hipStream_t s = (hipStream_t)stream;
-  const int rows = cache->n_sessions * query->n_q_heads;
-  hipLaunchKernelGGL(qprep_kernel, dim3(rows), dim3(128), 0, s, a);
-  if ((st = launch_status("query prep"))) return st;
   // one grid row per listed unit, else (H_kv, B) over every unit
   auto grid_of = [&](int n_splits, const UnitList& l) {
     return listed ? dim3(n_splits, l.n, 1) : dim3(n_splits, cache->n_kv_heads, cache->n_sessions);
@@ -1648,6 +1625,46 @@ int decode_impl(const tq_layer* layer, const tq_cache* cache, const tq_query* qu
   const bool merge = G <= 4 && go_common;
   const bool merge_other = merge && go_other &&
                            (!listed || cnt[0] + (go_wide ? cnt[1] : 0) + cnt[2] <= 2 * TQ_MAX_LISTED_UNITS);
+  // The merged launch of common and wide pages (listed units, ranges not cut
+  // for a long context) balances its ranges: wide ranges shorter in proportion to a wide page's
+  // cost (whole pages per wave), common ones the shortest that keep the
+  // launch within one round of kTargetSplitGroups workgroups.
+  int lc = sp.pages_per_split, lw = sp.pages_per_split_wide;
+  if (listed && merge && go_wide && !merge_other && !sp.cut) {
+    const int M = cache->max_pages, lmax = std::min(M, kMaxPagesPerSplit);
+    for (int l = sp.pages_per_split; l <= lmax; ++l) {
+      const int per_wave = (l + kDecodeWaves - 1) / kDecodeWaves;
+      const int w = std::min(l, std::max(sp.min_pages_per_split_wide,
+                                         kDecodeWaves * std::max(1, (int)(per_wave / kWidePageCost))));
+      lc = l;
+      lw = w;
+      const int64_t groups = (int64_t)cnt[0] * ((M + l - 1) / l) + (int64_t)cnt[1] * ((M + w - 1) / w);
+      if (groups <= kTargetSplitGroups) break;
+    }
+  }
+  a.n_splits = (cache->max_pages + lc - 1) / lc;
+  a.pages_per_split = lc;
+  a.n_splits_general = sp.n_splits_general;
+  a.pages_per_split_general = sp.pages_per_split_general;
+  a.n_splits_wide = (cache->max_pages + lw - 1) / lw;
+  a.pages_per_split_wide = lw;
+  const int n_common = run_common ? a.n_splits : 0;
+  const int n_wide = run_wide ? a.n_splits_wide : 0;
+  const int n_other = run_other ? sp.n_splits_general : 0;
+  a.part_base[0] = 0;
+  a.part_base[1] = n_common;
+  a.part_base[2] = n_common + n_wide;
+  a.n_partials = n_common + n_wide + n_other;
+  a.wsq = reinterpret_cast<float*>(workspace);
+  a.wsp = a.wsq + (size_t)cache->n_sessions * query->n_q_heads * kQPrepFloats;
+  a.out = out;
+  a.mass = page_mass;
+  a.tmass = token_mass;
+  const bool mass = page_mass != nullptr || token_mass != nullptr;
+  hipStream_t s = (hipStream_t)stream;
+  const int rows = cache->n_sessions * query->n_q_heads;
+  hipLaunchKernelGGL(qprep_kernel, dim3(rows), dim3(128), 0, s, a);
+  if ((st = launch_status("query prep"))) return st;
   if (merge && (go_wide || merge_other)) {
     UnitList merged;
     merged.n = 0;
@@ -1658,22 +1675,22 @@ int decode_impl(const tq_layer* layer, const tq_cache* cache, const tq_query* qu
       for (int c = 2; c >= 0; --c)
         for (int i = 0; i < merged.group[c]; ++i) merged.unit[merged.n++] = lists[c].unit[i];
     }
-    const int64_t blocks = (int64_t)merged.group[2] * sp.n_splits_general +
-                           (int64_t)merged.group[1] * sp.n_splits_wide + (int64_t)merged.group[0] * sp.n_splits;
+    const int64_t blocks = (int64_t)merged.group[2] * a.n_splits_general +
+                           (int64_t)merged.group[1] * a.n_splits_wide + (int64_t)merged.group[0] * a.n_splits;
     if (merge_other)
       launch_split_any<4>(mass, G, dim3((unsigned)blocks), blk, s, a, cache->pages, merged);
     else
       launch_split_any<3>(mass, G, dim3((unsigned)blocks), blk, s, a, cache->pages, merged);
     if ((st = launch_status("split (merged classes)"))) return st;
   } else if (go_common) {
-    launch_split_any<0>(mass, G, grid_of(sp.n_splits, lists[0]), blk, s, a, cache->pages, lists[0]);
+    launch_split_any<0>(mass, G, grid_of(a.n_splits, lists[0]), blk, s, a, cache->pages, lists[0]);
     if ((st = launch_status("split (common pages)"))) return st;
   } else if (go_wide) {
-    launch_split_any<1>(mass, G, grid_of(sp.n_splits_wide, lists[1]), blk, s, a, cache->pages, lists[1]);
+    launch_split_any<1>(mass, G, grid_of(a.n_splits_wide, lists[1]), blk, s, a, cache->pages, lists[1]);
     if ((st = launch_status("split (wide pages)"))) return st;
   }
   if (go_other && !merge_other) {
-    launch_split_any<2>(mass, G, grid_of(sp.n_splits_general, lists[2]), blk, s, a, cache->pages, lists[2]);
+    launch_split_any<2>(mass, G, grid_of(a.n_splits_general, lists[2]), blk, s, a, cache->pages, lists[2]);
     if ((st = launch_status("split (other pages)"))) return st;
   }
   hipLaunchKernelGGL(combine_kernel, dim3(rows), dim3(128 * kCombineGroups), 0, s, a);

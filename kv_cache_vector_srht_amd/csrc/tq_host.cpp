@@ -595,8 +595,9 @@ SplitPlan split_plan(int n_sessions, int n_kv_heads, int max_pages) {
   // and dear pages), while several rounds of shorter ones balance.  Wide
   // ranges are as long as common ones when those are not cut (the merged
   // launch of a layer with hub heads then stays one round of workgroups;
-  // shorter wide ranges added a round of their own), and a quarter of that
-  // length when they are.
+  // shorter wide ranges added a round of their own; the launch may shorten
+  // them down to a quarter, balancing them against longer common ranges),
+  // and a quarter of that length when they are.
   const int64_t units = (int64_t)n_sessions * n_kv_heads;
   const int64_t total_pages = units * max_pages;
   auto clamp_len = [&](int64_t p) {
@@ -614,7 +615,10 @@ SplitPlan split_plan(int n_sessions, int n_kv_heads, int max_pages) {
   sp.n_splits = (int)((max_pages + ppc - 1) / ppc);
   sp.pages_per_split_general = (int)((pps + 1) / 2);
   sp.n_splits_general = (max_pages + sp.pages_per_split_general - 1) / sp.pages_per_split_general;
-  sp.pages_per_split_wide = pps > kLongRangePages ? (sp.pages_per_split + 3) / 4 : sp.pages_per_split;
+  sp.cut = pps > kLongRangePages;
+  sp.min_pages_per_split_wide = (sp.pages_per_split + 3) / 4;
+  sp.max_splits_wide = (max_pages + sp.min_pages_per_split_wide - 1) / sp.min_pages_per_split_wide;
+  sp.pages_per_split_wide = sp.cut ? sp.min_pages_per_split_wide : sp.pages_per_split;
   sp.n_splits_wide = (max_pages + sp.pages_per_split_wide - 1) / sp.pages_per_split_wide;
   return sp;
 }
@@ -623,7 +627,7 @@ size_t decode_workspace_bytes(int n_sessions, int n_q_heads, const SplitPlan& sp
   const size_t rows = (size_t)n_sessions * n_q_heads;
   // query prep, then the partials of the three page classes
   return sizeof(float) * rows *
-         (kQPrepFloats + (size_t)(sp.n_splits + sp.n_splits_wide + sp.n_splits_general) * kPartialFloats);
+         (kQPrepFloats + (size_t)(sp.n_splits + sp.max_splits_wide + sp.n_splits_general) * kPartialFloats);
 }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }

@@ -51,7 +51,12 @@ struct SplitPlan {
   int pages_per_split_general;
   int n_splits_wide;            // the wide class (5-8 bits)
   int pages_per_split_wide;
+  bool cut;                     // common ranges cut for a long context
+  int min_pages_per_split_wide; // the shortest wide ranges a launch may choose
+  int max_splits_wide;          // and their count (the workspace's wide partials)
 };
+// Time of a wide page in common pages, for balancing a merged launch's ranges.
+constexpr float kWidePageCost = 1.5f;
 SplitPlan split_plan(int n_sessions, int n_kv_heads, int max_pages);
 size_t decode_workspace_bytes(int n_sessions, int n_q_heads, const SplitPlan& sp);
 
