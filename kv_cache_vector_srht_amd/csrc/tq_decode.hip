@@ -838,6 +838,48 @@ void split_kernel(DecodeArgs a,
   const int p_begin = split * pps;
   const int p_end = min(npages, p_begin + pps);
   const uint64_t* ptab = pages + ((size_t)b * a.n_kv_heads + hkv) * a.max_pages;
+  const float* __restrict__ qrow = wsq + ((size_t)b * a.n_kv_heads + hkv) * kQPrepFloats * G;
+  // A common-class range of four query heads with 3- or 4-bit keys scores them
+  // on the matrix cores (key_scores_mfma): its key pair tables at those widths
+  // hold float16 hi and lo parts (times kKeyPairScale), and the query is staged
+  // as the A operand, times 2^E so that its largest magnitude is in [2^9, 2^10);
+  // the scores are then multiplied by key_unscale = 2^-(E + 8).
+  // (Not in the launch merged with the other class: its register budget is
+  // spent by the other class's copy of the page loop.)
+  constexpr bool kMfmaKeys = G == 4 && CLASS != 4;
+  bool key_mfma = false;
+  float key_unscale = 1.f;
+  // A common-class block of four query heads stages the query as the matrix
+  // cores' A operand before anything else (its loads then overlap the
+  // descriptor scan's), whether or not its range holds 3- or 4-bit keys
+  // (key_mfma, decided with the tables, says whether they are used).
+  if constexpr (kMfmaKeys) {
+    if (cls == 0) {
+      // every wave finds the same largest magnitude of the prepared query
+      float mx = 0.f;
+      for (int i = lane; i < D * G; i += 64) mx = fmaxf(mx, fabsf(qrow[i]));
+      mx = wave_max(mx);
+      int ex = 0;
+      (void)frexpf(mx, &ex);
+      const int E = (mx > 0.f && mx <= 3.0e38f) ? min(60, max(-60, 10 - ex)) : 0;
+      const float qs = ldexpf(1.f, E);
+      key_unscale = ldexpf(1.f, -(E + 8));
+      // entry (step st, k-group g, head h): coordinates c0..c3 = 32 g + 4 st
+      // + 0..3 of head h as A1 = (qh0 qh1, qh0 qh1, qh2 qh3, qh2 qh3) and
+      // A2 = (ql0 ql1, 0, ql2 ql3, 0), key_scores_mfma's operands (the
+      // prepared query's layout: coordinate j of head h at ((j / 4) G + h)
+      // 4 + j % 4, so c0..c3 are one aligned quad)
+      if (tid < 128) {
+        const int st = tid >> 4, gg = (tid >> 2) & 3, h = tid & 3;
+        const int j0 = 32 * gg + 4 * st;
+        const float* qc = qrow + ((j0 >> 2) * G + h) * 4;
+        const uint2 v01 = split_half2(qc[0] * qs, qc[1] * qs);
+        const uint2 v23 = split_half2(qc[2] * qs, qc[3] * qs);
+        sm.t.kqa[checked(2 * tid, 256, kCheckDecodeTable)] = make_uint4(v01.x, v01.x, v23.x, v23.x);
+        sm.t.kqa[checked(2 * tid + 1, 256, kCheckDecodeTable)] = make_uint4(v01.y, 0u, v23.y, 0u);
+      }
+    }
+  }
   bool need_tables;
   {
     // nothing of this class in the range: an empty partial, no setup (the
@@ -867,7 +909,6 @@ void split_kernel(DecodeArgs a,
     }
   }
 
-  const float* __restrict__ qrow = wsq + ((size_t)b * a.n_kv_heads + hkv) * kQPrepFloats * G;
 
   // Stage the codebook tables the range's pages of this class use: pair
   // tables at 3-4 bits, quad tables at 1-2 bits, centroid lists at 5-8 bits
@@ -876,16 +917,6 @@ void split_kernel(DecodeArgs a,
   // to 4 query heads, scalar codebooks) builds the query's key table for that
   // width instead of the key quad table (key_table_bits).
   int key_table_bits = 0;
-  // A common-class range of four query heads with 3- or 4-bit keys scores them
-  // on the matrix cores (key_scores_mfma): its key pair tables at those widths
-  // hold float16 hi and lo parts (times kKeyPairScale), and the query is staged
-  // as the A operand, times 2^E so that its largest magnitude is in [2^9, 2^10);
-  // the scores are then multiplied by key_unscale = 2^-(E + 8).
-  // (Not in the launch merged with the other class: its register budget is
-  // spent by the other class's copy of the page loop.)
-  constexpr bool kMfmaKeys = G == 4 && CLASS != 4;
-  bool key_mfma = false;
-  float key_unscale = 1.f;
   auto stage_tables = [&]() {
     if (!need_tables) return;
     int widths = 0;
@@ -897,31 +928,6 @@ void split_kernel(DecodeArgs a,
     }
     if constexpr (kMfmaKeys) {
       key_mfma = cls == 0 && (widths & 0x18) != 0;
-      if (key_mfma) {
-        // every wave finds the same largest magnitude of the prepared query
-        float mx = 0.f;
-        for (int i = lane; i < D * G; i += 64) mx = fmaxf(mx, fabsf(qrow[i]));
-        mx = wave_max(mx);
-        int ex = 0;
-        (void)frexpf(mx, &ex);
-        const int E = (mx > 0.f && mx <= 3.0e38f) ? min(60, max(-60, 10 - ex)) : 0;
-        const float qs = ldexpf(1.f, E);
-        key_unscale = ldexpf(1.f, -(E + 8));
-        // entry (step st, k-group g, head h): coordinates c0..c3 = 32 g + 4 st
-        // + 0..3 of head h as A1 = (qh0 qh1, qh0 qh1, qh2 qh3, qh2 qh3) and
-        // A2 = (ql0 ql1, 0, ql2 ql3, 0), key_scores_mfma's operands (the
-        // prepared query's layout: coordinate j of head h at ((j / 4) G + h)
-        // 4 + j % 4, so c0..c3 are one aligned quad)
-        if (tid < 128) {
-          const int st = tid >> 4, gg = (tid >> 2) & 3, h = tid & 3;
-          const int j0 = 32 * gg + 4 * st;
-          const float* qc = qrow + ((j0 >> 2) * G + h) * 4;
-          const uint2 v01 = split_half2(qc[0] * qs, qc[1] * qs);
-          const uint2 v23 = split_half2(qc[2] * qs, qc[3] * qs);
-          sm.t.kqa[checked(2 * tid, 256, kCheckDecodeTable)] = make_uint4(v01.x, v01.x, v23.x, v23.x);
-          sm.t.kqa[checked(2 * tid + 1, 256, kCheckDecodeTable)] = make_uint4(v01.y, 0u, v23.y, 0u);
-        }
-      }
     }
     if (kKeyTable && key_table_bits) {
       // entry 16 g + m: sum over the nibble's codes of q[h][coordinate] c[code],
