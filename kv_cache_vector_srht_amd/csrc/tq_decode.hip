@@ -880,6 +880,29 @@ void split_kernel(DecodeArgs a,
       }
     }
   }
+  // A common-class block also loads the 1-4-bit pair and quad sources of both
+  // tables before the descriptor scan (one pair of the 4-bit table per
+  // thread, the 3-bit table in the first 64, a 2-bit quad's two pairs, a
+  // 1-bit quad's in the first 16); the staging below writes those its widths
+  // use.
+  static_assert(64 * kDecodeWaves == 256, "one 4-bit pair per thread");
+  struct PairSrc {
+    float2 p3, p4, q2a, q2b, q1a, q1b;
+  };
+  PairSrc pre[2];
+  const bool prefetched = (CLASS == 0 || CLASS >= 3) && cls == 0;
+  if (prefetched) {
+#pragma clang loop unroll(full)
+    for (int kv = 0; kv < 2; ++kv) {
+      const float2* pt = reinterpret_cast<const float2*>((kv ? a.v_table : a.k_table) + kPairOffset);
+      pre[kv].p4 = pt[pair_offset(4) + tid];
+      pre[kv].p3 = pt[pair_offset(3) + (tid & 63)];
+      pre[kv].q2a = pt[pair_offset(2) + (tid & 15)];
+      pre[kv].q2b = pt[pair_offset(2) + (tid >> 4)];
+      pre[kv].q1a = pt[pair_offset(1) + (tid & 3)];
+      pre[kv].q1b = pt[pair_offset(1) + ((tid >> 2) & 3)];
+    }
+  }
   bool need_tables;
   {
     // nothing of this class in the range: an empty partial, no setup (the
@@ -959,8 +982,29 @@ void split_kernel(DecodeArgs a,
     }
     // pair tables come with the codebook table (a scalar codebook's (c[lo],
     // c[hi]), or PolarQuant's radius-angle pairs); a quad entry is two pairs
-    auto stage = [&](int wm, const float* tab, float2* pair, float4* quad, float* cent, bool hilo) {
+    auto stage = [&](int wm, const float* tab, float2* pair, float4* quad, float* cent, bool hilo, const PairSrc& pr) {
       const float2* pt = reinterpret_cast<const float2*>(tab + kPairOffset);
+      if (prefetched) {
+        // the sources loaded before the scan: every width of 1-4 bits in one
+        // pass of the block's threads
+        if ((wm >> 4) & 1) {
+          const int o = pair_offset(4);
+          if (hilo)
+            reinterpret_cast<uint2*>(pair)[o + tid] = split_half2(pr.p4.x * kKeyPairScale, pr.p4.y * kKeyPairScale);
+          else
+            pair[o + tid] = pr.p4;
+        }
+        if (((wm >> 3) & 1) && tid < 64) {
+          const int o = pair_offset(3);
+          if (hilo)
+            reinterpret_cast<uint2*>(pair)[o + tid] = split_half2(pr.p3.x * kKeyPairScale, pr.p3.y * kKeyPairScale);
+          else
+            pair[o + tid] = pr.p3;
+        }
+        if ((wm >> 2) & 1) quad[quad_offset(2) + tid] = make_float4(pr.q2a.x, pr.q2a.y, pr.q2b.x, pr.q2b.y);
+        if (((wm >> 1) & 1) && tid < 16) quad[quad_offset(1) + tid] = make_float4(pr.q1a.x, pr.q1a.y, pr.q1b.x, pr.q1b.y);
+        wm &= ~0x1E;
+      }
       for (int bb = 3; bb <= 4; ++bb) {
         if (!((wm >> bb) & 1)) continue;
         const int o = pair_offset(bb), n = 1 << (2 * bb);
@@ -986,8 +1030,8 @@ void split_kernel(DecodeArgs a,
         for (int i = tid; i < n; i += blockDim.x) cent[o + i] = tab[o + i];
       }
     };
-    stage(widths & 0x1FF, a.k_table, sm.t.kpair, sm.t.kquad, sm.t.kcent, key_mfma);
-    stage(widths >> 9, a.v_table, sm.t.vpair, sm.t.vquad, sm.t.vcent, false);
+    stage(widths & 0x1FF, a.k_table, sm.t.kpair, sm.t.kquad, sm.t.kcent, key_mfma, pre[0]);
+    stage(widths >> 9, a.v_table, sm.t.vpair, sm.t.vquad, sm.t.vcent, false, pre[1]);
     __syncthreads();
     // keep the scheduler from moving table work into the page loop (it
     // otherwise inflates the loop's register use)
