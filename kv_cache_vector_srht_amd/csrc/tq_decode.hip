@@ -1675,12 +1675,13 @@ int decode_impl(const tq_layer* layer, const tq_cache* cache, const tq_query* qu
   const bool merge = G <= 4 && go_common;
   const bool merge_other = merge && go_other &&
                            (!listed || cnt[0] + (go_wide ? cnt[1] : 0) + cnt[2] <= 2 * TQ_MAX_LISTED_UNITS);
-  // The merged launch of common and wide pages (listed units, ranges not cut
-  // for a long context) balances its ranges: wide ranges shorter in proportion to a wide page's
+  // A merged launch of common and wide pages (listed units, ranges not cut
+  // for a long context; the other class's blocks, mostly empty ranges around
+  // a decode loop's tail pages, are not counted) balances its ranges: wide ranges shorter in proportion to a wide page's
   // cost (whole pages per wave), common ones the shortest that keep the
   // launch within one round of kTargetSplitGroups workgroups.
   int lc = sp.pages_per_split, lw = sp.pages_per_split_wide;
-  if (listed && merge && go_wide && !merge_other && !sp.cut) {
+  if (listed && merge && go_wide && !sp.cut) {
     const int M = cache->max_pages, lmax = std::min(M, kMaxPagesPerSplit);
     for (int l = sp.pages_per_split; l <= lmax; ++l) {
       const int per_wave = (l + kDecodeWaves - 1) / kDecodeWaves;
