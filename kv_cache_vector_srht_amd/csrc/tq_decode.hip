@@ -42,6 +42,7 @@ struct DecodeArgs {
   int n_splits_general, pages_per_split_general;   // other class
   int n_splits_wide, pages_per_split_wide;         // wide class
   int part_base[3], n_partials;                     // first partial of each class, total
+  int other_edges_first;        // merged launch: the other class's middle ranges after the others
   float* wsq;   // [B][H_q][384]: rotated q, plain q, S q (pre-scaled)
   float* wsp;   // [B][H_q][n_splits][kPartialFloats]: m, l, -, -, acc[128]
   float* out;
@@ -789,28 +790,41 @@ void split_kernel(DecodeArgs a,
     // merged launch, one block per (unit, range): the other class's blocks
     // first, range-major from each unit's last range (where a decode loop's
     // fp16 tail page sits, so every unit's tail starts at once), then the wide
-    // class's and the common class's blocks, unit-major
+    // class's and the common class's blocks, unit-major.  With
+    // other_edges_first only the other class's last and first ranges (the tail
+    // and sink pages) come first, its middle ranges (empty around a decode
+    // loop's tail) after the common blocks, range-major from the end.
     const int other_blocks = list.group[2] * a.n_splits_general;
+    const int n_head = a.other_edges_first ? min(a.n_splits_general, 2) : a.n_splits_general;
+    const int head_blocks = list.group[2] * n_head;
     const int wide_blocks = list.group[1] * a.n_splits_wide;
+    const int common_blocks = (int)gridDim.x - other_blocks - wide_blocks;
     int i = blockIdx.x, pos, off;   // position in the class's group, its list offset
-    if (i < other_blocks) {
+    if (i < head_blocks) {
       cls = 2;
       const int r = i / list.group[2];
       pos = i - r * list.group[2];
-      split = a.n_splits_general - 1 - r;
+      split = a.other_edges_first && r == 1 ? 0 : a.n_splits_general - 1 - r;
       off = 0;
-    } else if (i < other_blocks + wide_blocks) {
+    } else if (i < head_blocks + wide_blocks) {
       cls = 1;
-      i -= other_blocks;
+      i -= head_blocks;
       pos = i / a.n_splits_wide;
       split = i - pos * a.n_splits_wide;
       off = list.group[2];
-    } else {
+    } else if (i < head_blocks + wide_blocks + common_blocks) {
       cls = 0;
-      i -= other_blocks + wide_blocks;
+      i -= head_blocks + wide_blocks;
       pos = i / a.n_splits;
       split = i - pos * a.n_splits;
       off = list.group[2] + list.group[1];
+    } else {
+      cls = 2;
+      i -= head_blocks + wide_blocks + common_blocks;
+      const int r = i / list.group[2];
+      pos = i - r * list.group[2];
+      split = a.n_splits_general - 2 - r;
+      off = 0;
     }
     // without a list every group is every unit, in (B, H_kv) order
     const int u = list.n > 0 ? list.unit[off + pos] : pos;
@@ -1693,6 +1707,8 @@ int decode_impl(const tq_layer* layer, const tq_cache* cache, const tq_query* qu
       if (groups <= kTargetSplitGroups) break;
     }
   }
+  // short contexts: the other class's middle ranges after the common ones
+  a.other_edges_first = !sp.cut;
   a.n_splits = (cache->max_pages + lc - 1) / lc;
   a.pages_per_split = lc;
   a.n_splits_general = sp.n_splits_general;
